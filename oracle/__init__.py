@@ -1,0 +1,185 @@
+"""fp64 CPU oracle for SAGA + Atop-N decode attention (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  The product
+path (the HIP library and its binding) never imports it, and it imports
+nothing from the product.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision); this module
+only builds that file with gcc and marshals numpy arrays.  Every function
+takes bf16 data as ``uint16`` bit patterns, exactly the values the device
+sees.  Citations of the pages are in ``oracle.c`` next to each function.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+# The mutation tests point a child process at a deliberately broken build.
+_LIB = os.environ.get("SAGA_ORACLE_LIBRARY", _LIB)
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (OpenMP, -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
+             "-o", tmp, _SRC, "-lm"],
+            check=True,
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        i32, i64, dbl, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+        lib.oracle_logits.argtypes = [i32, i32, i32, i32, i32, i64, i64, dbl, vp, vp, vp, i32]
+        lib.oracle_nth_largest.argtypes = [vp, i64, i64]
+        lib.oracle_nth_largest.restype = dbl
+        lib.oracle_atopn_run.argtypes = [i32, i32, i32, i32, i32, i64, i32, vp, dbl, i64, i64,
+                                         vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        lib.oracle_masked.argtypes = [i32, i32, i32, i32, i32, i64, i64, dbl, vp, vp, vp, vp,
+                                      vp, vp, i32]
+        lib.oracle_exact_topn.argtypes = [i32, i32, i32, i32, i32, i64, i64, dbl, i64, vp, vp,
+                                          vp, vp, i32]
+        lib.oracle_full.argtypes = [i32, i32, i32, i32, i32, i64, i64, dbl, vp, vp, vp, vp, i32]
+        lib.oracle_max_threads.restype = i32
+        for name in ("oracle_logits", "oracle_atopn_run", "oracle_masked",
+                     "oracle_exact_topn", "oracle_full"):
+            getattr(lib, name).restype = i32
+        _lib = lib
+    return _lib
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError(f"expected bf16 bit patterns as uint16, got {a.dtype}")
+    return a
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _cache_shape(K, V):
+    B, hk, cache_len, d = K.shape
+    B2, hv, cache_len2, d2 = V.shape
+    if (B, cache_len, d) != (B2, cache_len2, d2):
+        raise ValueError("K and V caches disagree on batch, rows or head_dim")
+    return B, hk, hv, cache_len, d
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def logits(q, K, ctx: int, scale: float = 1.0, nthreads: int = 0) -> np.ndarray:
+    """fp64 logits ``[B][hq][ctx]`` of one step; q ``[B][hq][d]``, K ``[B][hk][rows][d]``."""
+    q, K = _u16(q), _u16(K)
+    B, hk, cache_len, d = K.shape
+    hq = q.shape[1]
+    out = np.empty((B, hq, ctx), dtype=np.float64)
+    rc = _load().oracle_logits(B, hq, hk, hk, d, cache_len, ctx, scale, _ptr(q), _ptr(K),
+                               _ptr(out), nthreads)
+    if rc:
+        raise ValueError("oracle_logits rejected its arguments")
+    return out
+
+
+def nth_largest(s, N: int) -> float:
+    """Exact N-th largest of a 1-D array (sorted), ``-inf`` when ``N >= len(s)``."""
+    s = np.ascontiguousarray(s, dtype=np.float64)
+    return float(_load().oracle_nth_largest(_ptr(s), s.size, N))
+
+
+def atopn_run(q_steps, K, V, ctx_steps, top_n: int, refresh_n: int, scale: float = 1.0,
+              want_sel: bool = False, want_logits: bool = False, nthreads: int = 0):
+    """Atop-N over T steps of one layer.
+
+    ``q_steps`` is ``[T][B][hq][d]``; ``ctx_steps`` the rows attended per step.
+    Returns a dict with ``out [T][B][hq][d]``, ``tau [T][B][hq]``,
+    ``count [T][B][hq]`` and optionally ``sel``/``logits`` ``[T][B][hq][rows]``.
+    """
+    q_steps, K, V = _u16(q_steps), _u16(K), _u16(V)
+    B, hk, hv, cache_len, d = _cache_shape(K, V)
+    T, _, hq, _ = q_steps.shape
+    ctx = np.ascontiguousarray(ctx_steps, dtype=np.int64)
+    if ctx.shape != (T,):
+        raise ValueError("ctx_steps must hold one length per step")
+    out = np.empty((T, B, hq, d), dtype=np.float64)
+    tau = np.empty((T, B, hq), dtype=np.float64)
+    count = np.empty((T, B, hq), dtype=np.int64)
+    sel = np.empty((T, B, hq, cache_len), dtype=np.uint8) if want_sel else None
+    lg = np.empty((T, B, hq, cache_len), dtype=np.float64) if want_logits else None
+    rc = _load().oracle_atopn_run(
+        B, hq, hk, hv, d, cache_len, T, _ptr(ctx), scale, top_n, refresh_n,
+        _ptr(q_steps), _ptr(K), _ptr(V), _ptr(out), _ptr(tau), _ptr(count),
+        _ptr(sel) if sel is not None else None, _ptr(lg) if lg is not None else None,
+        nthreads)
+    if rc:
+        raise ValueError("oracle_atopn_run rejected its arguments")
+    res = {"out": out, "tau": tau, "count": count}
+    if sel is not None:
+        res["sel"] = sel
+    if lg is not None:
+        res["logits"] = lg
+    return res
+
+
+def masked(q, K, V, ctx: int, bitmap, scale: float = 1.0, nthreads: int = 0):
+    """One step over a caller-given selection bitmap ``[B][hq][ceil(rows/32)]`` (uint32)."""
+    q, K, V = _u16(q), _u16(K), _u16(V)
+    B, hk, hv, cache_len, d = _cache_shape(K, V)
+    hq = q.shape[1]
+    bitmap = np.ascontiguousarray(bitmap, dtype=np.uint32)
+    if bitmap.shape != (B, hq, (cache_len + 31) // 32):
+        raise ValueError("bitmap must be [B][hq][ceil(rows/32)]")
+    out = np.empty((B, hq, d), dtype=np.float64)
+    count = np.empty((B, hq), dtype=np.int64)
+    rc = _load().oracle_masked(B, hq, hk, hv, d, cache_len, ctx, scale, _ptr(q), _ptr(K),
+                               _ptr(V), _ptr(bitmap), _ptr(out), _ptr(count), nthreads)
+    if rc:
+        raise ValueError("oracle_masked rejected its arguments")
+    return out, count
+
+
+def exact_topn(q, K, V, ctx: int, top_n: int, scale: float = 1.0, nthreads: int = 0):
+    """Exact top-N attention of one step (index sort, first N, softmax)."""
+    q, K, V = _u16(q), _u16(K), _u16(V)
+    B, hk, hv, cache_len, d = _cache_shape(K, V)
+    hq = q.shape[1]
+    out = np.empty((B, hq, d), dtype=np.float64)
+    rc = _load().oracle_exact_topn(B, hq, hk, hv, d, cache_len, ctx, scale, top_n, _ptr(q),
+                                   _ptr(K), _ptr(V), _ptr(out), nthreads)
+    if rc:
+        raise ValueError("oracle_exact_topn rejected its arguments")
+    return out
+
+
+def full(q, K, V, ctx: int, scale: float = 1.0, nthreads: int = 0):
+    """Dense softmax attention of one step over all ``ctx`` rows."""
+    q, K, V = _u16(q), _u16(K), _u16(V)
+    B, hk, hv, cache_len, d = _cache_shape(K, V)
+    hq = q.shape[1]
+    out = np.empty((B, hq, d), dtype=np.float64)
+    rc = _load().oracle_full(B, hq, hk, hv, d, cache_len, ctx, scale, _ptr(q), _ptr(K),
+                             _ptr(V), _ptr(out), nthreads)
+    if rc:
+        raise ValueError("oracle_full rejected its arguments")
+    return out
