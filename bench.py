@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark of SAGA + Atop-N on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A *step* is one decode step of the whole hot path for every layer of the
+workload and every batch row: for each layer, the exact top-N threshold
+refresh when t mod n == 0 (QK logits + radix select) and the fused Atop-N
+decode (K stream, threshold mask, ballot compaction, masked online softmax,
+sparse V gather, split-sequence combine).  Step t attends ctx_t = L + t rows
+and t cycles through the workload's T = 32 decode steps, so K = 320 steps is
+the pages' protocol of 10 runs x 32 generated tokens.  Each step (all layers)
+is captured once into a HIP graph and replayed; inputs are resident in HBM
+before the timed region.
+
+Printed: one JSON line with steps/s (value), tokens/s, the roofline of the
+dominant kernel (the fused decode kernel: algorithmic bytes per launch over
+its event-timed duration), the same library's full-attention GQA baseline on
+the GQA twin of the shape (h_k = h_v), and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "llama_like_128k_b16"
+GQA_TWIN = {"llama_like_128k_b16": 8, "qwen_like_128k_b1": 2, "qwen_like_128k_b16": 2,
+            "llama_like_8k": 8, "tiny": 2}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=320)
+    p.add_argument("--warmup", type=int, default=32)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--no-gqa", action="store_true", help="skip the full-attention GQA baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--traffic", default=None,
+                   help="JSON with rocprofv3-measured HBM bytes of the decode kernel")
+    return p.parse_args()
+
+
+def layer_inputs(torch, wl, w, layer):
+    x = wl.make_layer(w, layer, device="cuda")
+    return x["K"], x["V"], x["q"]
+
+
+def decode_algorithmic_bytes(w, ctx, sel_total):
+    """Bytes the fused decode launch must move: K once per (b, key head), the
+    selected V rows, q, out and the thresholds."""
+    d = w.head_dim
+    return (w.batch * w.h_k * ctx * d * 2 + sel_total * d * 2
+            + 2 * w.batch * w.h_q * d * 2 + w.batch * w.h_q * 4)
+
+
+def full_algorithmic_bytes(w, ctx):
+    return w.batch * (w.h_k + w.h_v) * ctx * w.head_dim * 2 + 2 * w.batch * w.h_q * w.head_dim * 2
+
+
+def time_graphs(torch, graphs, steps, warmup):
+    T = len(graphs)
+    for k in range(warmup):
+        graphs[k % T].replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(steps):
+        graphs[(warmup + k) % T].replay()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / 1e3, wall
+
+
+def run_saga(torch, saga, wl, w, args):
+    T, L = w.steps, w.L
+    layers = []
+    log(f"generating {w.layers} layers of {w.name} ({w.kv_bytes() / 1e9:.1f} GB of KV cache)")
+    for layer in range(w.layers):
+        K, V, q = layer_inputs(torch, wl, w, layer)
+        layers.append(dict(K=K, V=V, q=q,
+                           tau=torch.empty(w.batch, w.h_q, dtype=torch.float32, device="cuda"),
+                           out=torch.empty(w.batch, w.h_q, w.head_dim, dtype=torch.bfloat16,
+                                           device="cuda"),
+                           cnt=torch.empty(w.batch, w.h_q, dtype=torch.int32, device="cuda")))
+    torch.cuda.synchronize()
+    d0 = saga.dims(w.batch, w.h_q, w.h_k, w.h_v, w.head_dim, L, w.rows, w.scale)
+    ws = saga.alloc_workspace(d0, w.top_n)
+
+    def step(t, events=None):
+        dm = saga.dims(w.batch, w.h_q, w.h_k, w.h_v, w.head_dim, L + t, w.rows, w.scale)
+        for li, x in enumerate(layers):
+            if t % w.refresh_n == 0:
+                saga.atopn_refresh_thresholds(dm, w.top_n, x["q"][t], x["K"], x["tau"], ws)
+            if events is not None:
+                events[li][0].record()
+            saga.saga_decode_step(dm, x["q"][t], x["K"], x["V"], x["tau"], x["out"], ws,
+                                  sel_counts=x["cnt"])
+            if events is not None:
+                events[li][1].record()
+
+    # Eager pass over one full run: per-launch timing of the decode kernel with
+    # events on the stream it runs on, and the selected counts of every launch.
+    log("eager pass (per-launch decode timing)")
+    for t in range(T):
+        step(t)
+    torch.cuda.synchronize()
+    launches = []
+    for t in range(T):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in layers]
+        step(t, ev)
+        torch.cuda.synchronize()
+        for li, x in enumerate(layers):
+            ms = ev[li][0].elapsed_time(ev[li][1])
+            sel = int(x["cnt"].sum().item())
+            launches.append((t, li, ms, decode_algorithmic_bytes(w, L + t, sel), sel))
+
+    log("capturing one HIP graph per decode step")
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for t in range(T):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                step(t)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps after {args.warmup} warmup steps")
+    sec, wall = time_graphs(torch, graphs, args.steps, args.warmup)
+    return dict(layers=layers, launches=launches, sec=sec, wall=wall, ws=ws, graphs=graphs)
+
+
+def run_gqa(torch, saga, wl, w, hkv, args):
+    g = w.gqa(hkv)
+    T, L = g.steps, g.L
+    layers = []
+    log(f"generating GQA twin h_k=h_v={hkv} ({g.kv_bytes() / 1e9:.1f} GB)")
+    for layer in range(g.layers):
+        K, V, q = layer_inputs(torch, wl, g, layer)
+        layers.append(dict(K=K, V=V, q=q, out=torch.empty(g.batch, g.h_q, g.head_dim,
+                                                          dtype=torch.bfloat16, device="cuda")))
+    d0 = saga.dims(g.batch, g.h_q, g.h_k, g.h_v, g.head_dim, L, g.rows, g.scale)
+    ws = saga.alloc_workspace(d0, 1)
+
+    def step(t):
+        dm = saga.dims(g.batch, g.h_q, g.h_k, g.h_v, g.head_dim, L + t, g.rows, g.scale)
+        for x in layers:
+            saga.saga_full_attention(dm, x["q"][t], x["K"], x["V"], x["out"], ws)
+
+    for t in range(T):
+        step(t)
+    torch.cuda.synchronize()
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for t in range(T):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=s):
+                step(t)
+            graphs.append(gr)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    sec, _ = time_graphs(torch, graphs, args.steps, args.warmup)
+    per_step_bytes = sum(full_algorithmic_bytes(g, L + (k % T)) for k in range(args.steps))
+    per_step_bytes *= g.layers / args.steps
+    del layers, graphs
+    torch.cuda.empty_cache()
+    return dict(sec=sec, bytes_per_step=per_step_bytes, hkv=hkv)
+
+
+def cpu_baseline(torch, wl, w, layer0):
+    """The fp64 oracle on a bounded sample: layer 0, one refresh step (t=0) and
+    one plain step (t=1), every batch row and query head."""
+    import numpy as np
+    import oracle
+    K = wl.bits(layer0["K"])
+    V = wl.bits(layer0["V"])
+    q = wl.bits(layer0["q"][:2])
+    cores = oracle.max_threads()
+    times = []
+    for t in range(2):
+        t0 = time.perf_counter()
+        oracle.atopn_run(q[: t + 1], K, V, [w.L + s for s in range(t + 1)], w.top_n,
+                         w.refresh_n)
+        times.append(time.perf_counter() - t0)
+    t_refresh = times[0]
+    t_plain = max(times[1] - times[0], 1e-9)
+    # Steady state per decode step: every layer, refresh on 1 step in n.
+    per_layer = t_refresh / w.refresh_n + t_plain * (w.refresh_n - 1) / w.refresh_n
+    per_step = per_layer * w.layers
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": (f"layer 0 of {w.name}: one refresh step (t=0, {t_refresh:.2f} s) and one "
+                       f"plain step (t=1, {t_plain:.2f} s) over all {w.batch}x{w.h_q} "
+                       f"(batch row, query head) pairs; per step = {w.layers} layers with "
+                       f"1 refresh per {w.refresh_n} steps"),
+            "sample_seconds": round(sum(times), 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the pages evaluate on one GPU; sharding is a design note only).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sparse_decode_attention_atop_amd as saga
+    import saga_workload as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    saga.library()          # fail loudly now if the HIP library is missing
+    w = wl.WORKLOADS[args.workload]
+    res = run_saga(torch, saga, wl, w, args)
+    T = w.steps
+    sec = res["sec"]
+    steps_per_s = args.steps / sec
+    ms_per_step = 1e3 * sec / args.steps
+
+    launches = res["launches"]
+    avg_ms = sum(x[2] for x in launches) / len(launches)
+    avg_bytes = sum(x[3] for x in launches) / len(launches)
+    achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
+    avg_sel = sum(x[4] for x in launches) / len(launches) / (w.batch * w.h_q)
+    step_bytes = sum(x[3] for x in launches) / T
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        if tr.get("workload") == w.name:
+            traffic = tr.get("bytes_per_launch")
+
+    extra = {}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(torch, wl, w, res["layers"][0])
+    if not args.no_gqa and w.name in GQA_TWIN:
+        del res["graphs"]
+        for x in res["layers"]:
+            x.clear()
+        res["layers"] = None
+        torch.cuda.empty_cache()
+        gq = run_gqa(torch, saga, wl, w, GQA_TWIN[w.name], args)
+        gqa_sps = args.steps / gq["sec"]
+        extra["gqa_full_attention"] = {
+            "h_kv": gq["hkv"], "steps_per_s": round(gqa_sps, 3),
+            "ms_per_step": round(1e3 * gq["sec"] / args.steps, 4),
+            "hbm_gbs_algorithmic": round(gq["bytes_per_step"] / (gq["sec"] / args.steps) / 1e9, 1)}
+        extra["speedup_vs_gqa_full"] = round(steps_per_s / gqa_sps, 3)
+
+    line = {
+        "metric": "decode-attn steps/s (B x layers) + HBM GB/s % peak, SAGA Atop-N @128K",
+        "value": round(steps_per_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes of the pages' Llama/Qwen decode setups, no weights)",
+        "config": {"workload": w.name, "batch": w.batch, "h_q": w.h_q, "h_k": w.h_k,
+                   "h_v": w.h_v, "head_dim": w.head_dim, "L": w.L, "top_n": w.top_n,
+                   "refresh_n": w.refresh_n, "decode_steps": w.steps, "layers": w.layers},
+        "tokens_per_s": round(steps_per_s * w.batch, 2),
+        "hbm_gbs_step": round(step_bytes / (sec / args.steps) / 1e9, 1),
+        "hbm_frac_step": round(step_bytes / (sec / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "sparse_decode_kernel (with its combine)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "avg_launch_ms": round(avg_ms, 5),
+                     "algorithmic_bytes_per_launch": int(avg_bytes),
+                     "mean_selected_per_head": round(avg_sel, 1)},
+        "cpu_baseline": cpu,
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * saga.h -- C ABI of the SAGA + Atop-N decode-attention library (libsaga.so,
+ * HIP, gfx950 / MI355X).
+ *
+ * One decode step of attention for one layer, for a batch of sequences that
+ * share one context length.  The method is the one described on the pages
+ * "More Value per Key: Asymmetric Sparse Attention for Faster LLM Decoding"
+ * (ai.info AI summary and atlas.scime.ai AI summary):
+ *   - SAGA: the number of key heads h_k is chosen independently of the number
+ *     of value heads h_v (ai.info summary, Key Contributions 3; atlas summary,
+ *     Approach).  Query head i reads key head i / (h_q/h_k) and value head
+ *     i / (h_q/h_v) (contiguous grouping).  h_k == h_v is ordinary GQA.
+ *   - Atop-N: exact top-N logit thresholds are computed once every n steps
+ *     and reused; in between, entries are picked by comparing each logit with
+ *     the reused threshold, with no sort (ai.info summary, Key Contributions 2
+ *     and Methodology).  The probability-value product then reads only the
+ *     selected value rows (ai.info summary, Main Findings, first item).
+ *
+ * The caller owns the refresh schedule: at steps t with t mod n == 0 call
+ * atopn_refresh_thresholds() and then saga_decode_step() with the fresh
+ * thresholds; at other steps call saga_decode_step() with the kept ones.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers named *_dev are device pointers (hipMalloc / torch CUDA memory),
+ * 16-byte aligned.  The library never allocates, frees, copies between host
+ * and device, or synchronises: all work is enqueued on `stream` (a
+ * hipStream_t; NULL = the legacy default stream) and the calls are legal
+ * inside hipGraph stream capture.  The caller keeps every buffer alive until
+ * the enqueued work has finished.  The library holds no state between calls;
+ * concurrent calls need distinct workspaces.
+ *
+ * Layouts (row-major, contiguous):
+ *   q        bf16 [batch][h_q][head_dim]
+ *   k_cache  bf16 [batch][h_k][cache_len][head_dim]
+ *   v_cache  bf16 [batch][h_v][cache_len][head_dim]
+ *   out      bf16 [batch][h_q][head_dim]      (round to nearest even)
+ *   thresholds fp32 [batch][h_q]
+ * A step attends rows 0 .. ctx_len-1 of each cache head.  Logits are
+ * s_j = scale * <q, k_j> computed with fp32 products and sums; softmax and the
+ * value sum are fp32.
+ *
+ * Status codes: every call validates all arguments before enqueuing anything
+ * and returns a saga_status; nothing is launched on a non-zero status except
+ * SAGA_ERR_HIP, which reports a failed launch (hipGetLastError) after a
+ * partial enqueue.
+ */
+#ifndef SAGA_H
+#define SAGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum saga_status {
+    SAGA_OK = 0,
+    SAGA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad dims, misalignment   */
+    SAGA_ERR_UNSUPPORTED = 2,        /* valid but not implemented (head_dim...) */
+    SAGA_ERR_WORKSPACE_TOO_SMALL = 3,
+    SAGA_ERR_HIP = 4                 /* a kernel launch failed                  */
+} saga_status;
+
+/* Problem shape of one layer call.
+ *   batch      >= 1
+ *   h_q, h_k, h_v >= 1; h_k and h_v each divide h_q; h_q/h_k <= 16
+ *   head_dim   64 or 128
+ *   ctx_len    rows attended this step, 1 <= ctx_len <= cache_len
+ *   cache_len  rows allocated per cache head (the head stride), < 2^27
+ *   scale      multiplies q.k (use 1/sqrt(d) unless it is folded into q)   */
+typedef struct saga_dims {
+    int32_t batch;
+    int32_t h_q;
+    int32_t h_k;
+    int32_t h_v;
+    int32_t head_dim;
+    int32_t reserved;   /* must be 0 */
+    int64_t ctx_len;
+    int64_t cache_len;
+    float scale;
+    float reserved2;    /* must be 0 */
+} saga_dims;
+
+/* Bytes of device workspace that every call below needs for `dims` with any
+ * ctx_len <= dims->cache_len and the given top_n.  One workspace may be reused
+ * by every layer and step issued on one stream.  Returns 0 if the dims are
+ * invalid.  Host-only; no device access. */
+size_t saga_workspace_bytes(const saga_dims* dims, int32_t top_n);
+
+/*
+ * Exact top-N threshold refresh (Atop-N's "exact thresholds every n tokens";
+ * ai.info summary, Key Contributions 2 and Methodology).
+ *
+ * For every (b, i): thresholds_dev[b][i] = the top_n-th largest fp32 logit
+ * s[b][i][0..ctx_len) (counting repeated values), or -INFINITY when
+ * top_n >= ctx_len.  The value is bit-identical to a logit that
+ * saga_decode_step() computes for the same q and k_cache, so comparing with
+ * it selects exactly top_n entries when there are no ties (ties at the
+ * threshold are all kept).  -0.0 logits are ranked as +0.0.
+ *
+ *   q_dev, k_cache_dev   inputs, layouts above
+ *   thresholds_dev       output fp32 [batch][h_q]
+ *   logits_debug_dev     optional output fp32 [batch][h_q][ctx_len] (NULL: skip)
+ *   workspace_dev        saga_workspace_bytes(dims, top_n) bytes
+ * Errors: INVALID_ARGUMENT (null q/k/thresholds/workspace, top_n < 1, bad
+ * dims), UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP.
+ */
+int atopn_refresh_thresholds(const saga_dims* dims, int32_t top_n, const void* q_dev,
+                             const void* k_cache_dev, float* thresholds_dev,
+                             float* logits_debug_dev, void* workspace_dev,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * One SAGA Atop-N decode step (selection by per-element comparison; sparse
+ * probability-value product: ai.info summary, Key Contributions 2, Main
+ * Findings first item).
+ *
+ * For every (b, i), with kappa = i/(h_q/h_k), nu = i/(h_q/h_v):
+ *   s_j = scale * <q[b][i], k_cache[b][kappa][j]>          j < ctx_len
+ *   S   = { j : s_j >= thresholds[b][i] }                   (fp32 compare)
+ *   out[b][i] = sum_{j in S} softmax_S(s)_j * v_cache[b][nu][j]; zero if S = {}
+ * Only the value rows in S are read.  The K cache is streamed once per
+ * (b, key head) for all of that head's query heads.
+ *
+ *   thresholds_dev       input fp32 [batch][h_q] (from the last refresh)
+ *   out_dev              output bf16 [batch][h_q][head_dim]
+ *   sel_counts_dev       optional output int32 [batch][h_q] = |S| (NULL: skip)
+ *   sel_bitmap_debug_dev optional output uint32 [batch][h_q][ceil(cache_len/32)]:
+ *                        bit j%32 of word j/32 set iff j in S; the library
+ *                        clears it first (NULL: skip)
+ * Errors: as above.
+ */
+int saga_decode_step(const saga_dims* dims, const void* q_dev, const void* k_cache_dev,
+                     const void* v_cache_dev, const float* thresholds_dev, void* out_dev,
+                     int32_t* sel_counts_dev, uint32_t* sel_bitmap_debug_dev,
+                     void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * Full (dense) decode attention over all ctx_len rows with the same head maps:
+ * the full-attention GQA baseline the pages time against when h_k == h_v, and
+ * "SAGA full attention" when h_k < h_v (ai.info summary, Main Findings:
+ * end-to-end speedups and the merging-alone result).
+ *   out[b][i] = softmax(s)_j-weighted sum of v_cache[b][nu][j], j < ctx_len.
+ * Additionally requires that each key head's query heads map to 1, 2 or 4
+ * value heads with at most 8 query heads per value head (UNSUPPORTED
+ * otherwise).
+ */
+int saga_full_attention(const saga_dims* dims, const void* q_dev, const void* k_cache_dev,
+                        const void* v_cache_dev, void* out_dev, void* workspace_dev,
+                        size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* saga_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int saga_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGA_H */

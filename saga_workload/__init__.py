@@ -11,13 +11,14 @@ context 8K..128K, N in {512, 1024, 2048}, batch 1 and 16, 32 generated
 tokens.  No trained weights or datasets are used; the values are synthetic.
 
 Recipe (per config index ``cfg`` and layer ``layer``):
-  * K, V ~ N(0, 1) in fp32, rounded to bf16 (round to nearest even).
+  * K, V ~ N(0, 1) drawn in fp32 and rounded to bf16 (round to nearest even).
   * q_0 ~ N(0, 1)/sqrt(d) in fp32; q_t = 0.9 q_{t-1} + 0.44 e_t with
     e_t ~ N(0, 1)/sqrt(d); each q_t is rounded to bf16 on its own.
   * Heavy hitters: round(0.01 * rows) positions per (batch row, key head),
     drawn without replacement and dealt round-robin to the query heads of
     that key head's group; each such key row gets 3 * q_0/|q_0| of its query
-    head added in fp32 before the bf16 rounding, so logits are peaked.
+    head added in fp32 to its bf16 values and is rounded to bf16 again, so
+    those logits sit about 3 sigma high.
   * Seeds: 1000*cfg + layer for K/V/positions, that plus 500 for q.
   * The cache holds rows = L + T; decode step t attends ctx_t = L + t rows.
 """
@@ -117,8 +118,9 @@ def make_layer(w: Workload, layer: int = 0, device="cpu", heavy_hitters: bool = 
 
     gkv = torch.Generator(device=device)
     gkv.manual_seed(seed)
-    K32 = _randn((B, hk, rows, d), gkv, device)
-    V = _randn((B, hv, rows, d), gkv, device).to(torch.bfloat16)
+    # torch draws bf16 normals in fp32 and rounds them to nearest even.
+    K = torch.randn((B, hk, rows, d), generator=gkv, device=device, dtype=torch.bfloat16)
+    V = torch.randn((B, hv, rows, d), generator=gkv, device=device, dtype=torch.bfloat16)
     if heavy_hitters:
         count = int(round(0.01 * rows))
         Gk = hq // hk
@@ -127,10 +129,9 @@ def make_layer(w: Workload, layer: int = 0, device="cpu", heavy_hitters: bool = 
             for g in range(hk):
                 pos = torch.randperm(rows, generator=gkv, device=device)[:count]
                 heads = g * Gk + (torch.arange(count, device=device) % Gk)
-                K32[b, g, pos, :] += 3.0 * unit[b, heads, :]
-    K = K32.to(torch.bfloat16)
-    del K32
-    return {"K": K.contiguous(), "V": V.contiguous(), "q": q}
+                K[b, g, pos, :] = (K[b, g, pos, :].float() + 3.0 * unit[b, heads, :]).to(
+                    torch.bfloat16)
+    return {"K": K, "V": V, "q": q}
 
 
 def bits(t: torch.Tensor):

@@ -1,0 +1,204 @@
+"""Python binding of libsaga.so: SAGA + Atop-N decode attention on MI355X.
+
+Thin ctypes marshalling over the C ABI in ``include/saga.h``; every step of
+the computation runs in the library's HIP kernels.  The function names are
+the C names.  Tensors are torch CUDA (ROCm) tensors used only as device
+memory; the stream is torch's current stream unless one is given.
+
+There is no fallback: if ``libsaga.so`` has not been built, or a call
+returns a non-zero status, an exception is raised.
+
+    python -m sparse_decode_attention_atop_amd.build     # builds libsaga.so
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "SagaDims", "SagaError", "dims", "library", "saga_workspace_bytes", "alloc_workspace",
+    "atopn_refresh_thresholds", "saga_decode_step", "saga_full_attention",
+    "saga_status_string", "saga_version", "LIB_PATH", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsaga.so")
+EXPORTED_SYMBOLS = ("saga_workspace_bytes", "atopn_refresh_thresholds", "saga_decode_step",
+                    "saga_full_attention", "saga_status_string", "saga_version")
+
+SAGA_OK = 0
+SAGA_ERR_INVALID_ARGUMENT = 1
+SAGA_ERR_UNSUPPORTED = 2
+SAGA_ERR_WORKSPACE_TOO_SMALL = 3
+SAGA_ERR_HIP = 4
+
+
+class SagaDims(ctypes.Structure):
+    """Mirror of ``saga_dims`` in include/saga.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("h_q", ctypes.c_int32),
+        ("h_k", ctypes.c_int32),
+        ("h_v", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("ctx_len", ctypes.c_int64),
+        ("cache_len", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+        ("reserved2", ctypes.c_float),
+    ]
+
+    def __repr__(self):
+        return (f"SagaDims(batch={self.batch}, h_q={self.h_q}, h_k={self.h_k}, h_v={self.h_v}, "
+                f"head_dim={self.head_dim}, ctx_len={self.ctx_len}, "
+                f"cache_len={self.cache_len}, scale={self.scale})")
+
+
+class SagaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {saga_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def library():
+    """Load libsaga.so once (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m sparse_decode_attention_atop_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        pd = ctypes.POINTER(SagaDims)
+        lib.saga_workspace_bytes.argtypes = [pd, i32]
+        lib.saga_workspace_bytes.restype = sz
+        lib.atopn_refresh_thresholds.argtypes = [pd, i32, vp, vp, vp, vp, vp, sz, vp]
+        lib.atopn_refresh_thresholds.restype = ctypes.c_int
+        lib.saga_decode_step.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.saga_decode_step.restype = ctypes.c_int
+        lib.saga_full_attention.argtypes = [pd, vp, vp, vp, vp, vp, sz, vp]
+        lib.saga_full_attention.restype = ctypes.c_int
+        lib.saga_status_string.argtypes = [ctypes.c_int]
+        lib.saga_status_string.restype = ctypes.c_char_p
+        lib.saga_version.argtypes = []
+        lib.saga_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def dims(batch: int, h_q: int, h_k: int, h_v: int, head_dim: int, ctx_len: int,
+         cache_len: int, scale: float = 1.0) -> SagaDims:
+    return SagaDims(batch, h_q, h_k, h_v, head_dim, 0, ctx_len, cache_len, scale, 0.0)
+
+
+def saga_status_string(status: int) -> str:
+    return library().saga_status_string(int(status)).decode()
+
+
+def saga_version() -> int:
+    return int(library().saga_version())
+
+
+def saga_workspace_bytes(d: SagaDims, top_n: int) -> int:
+    return int(library().saga_workspace_bytes(ctypes.byref(d), int(top_n)))
+
+
+def alloc_workspace(d: SagaDims, top_n: int, device="cuda") -> torch.Tensor:
+    n = saga_workspace_bytes(d, top_n)
+    if n == 0:
+        raise SagaError(SAGA_ERR_INVALID_ARGUMENT, "saga_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype, name: str):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (cuda/hip) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, numel: int, name: str):
+    if t is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ws(workspace: torch.Tensor):
+    return _ptr(workspace, torch.uint8, "workspace"), workspace.numel()
+
+
+def _check(status: int, where: str):
+    if status != SAGA_OK:
+        raise SagaError(status, where)
+
+
+def atopn_refresh_thresholds(d: SagaDims, top_n: int, q: torch.Tensor, k_cache: torch.Tensor,
+                             thresholds: torch.Tensor, workspace: torch.Tensor,
+                             logits_debug: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Exact top-N thresholds ``[B][h_q]`` (fp32) of this step's logits."""
+    bh = d.batch * d.h_q
+    _need(q, bh * d.head_dim, "q")
+    _need(k_cache, d.batch * d.h_k * d.cache_len * d.head_dim, "k_cache")
+    _need(thresholds, bh, "thresholds")
+    _need(logits_debug, bh * d.ctx_len, "logits_debug")
+    ws, nbytes = _ws(workspace)
+    _check(library().atopn_refresh_thresholds(
+        ctypes.byref(d), int(top_n), _ptr(q, torch.bfloat16, "q"),
+        _ptr(k_cache, torch.bfloat16, "k_cache"), _ptr(thresholds, torch.float32, "thresholds"),
+        _ptr(logits_debug, torch.float32, "logits_debug"), ws, nbytes, _stream(stream)),
+        "atopn_refresh_thresholds")
+
+
+def saga_decode_step(d: SagaDims, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     thresholds: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                     sel_counts: Optional[torch.Tensor] = None,
+                     sel_bitmap_debug: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One Atop-N decode step: out ``[B][h_q][d]`` (bf16) from the kept thresholds."""
+    bh = d.batch * d.h_q
+    _need(q, bh * d.head_dim, "q")
+    _need(k_cache, d.batch * d.h_k * d.cache_len * d.head_dim, "k_cache")
+    _need(v_cache, d.batch * d.h_v * d.cache_len * d.head_dim, "v_cache")
+    _need(thresholds, bh, "thresholds")
+    _need(out, bh * d.head_dim, "out")
+    _need(sel_counts, bh, "sel_counts")
+    _need(sel_bitmap_debug, bh * ((d.cache_len + 31) // 32), "sel_bitmap_debug")
+    ws, nbytes = _ws(workspace)
+    _check(library().saga_decode_step(
+        ctypes.byref(d), _ptr(q, torch.bfloat16, "q"), _ptr(k_cache, torch.bfloat16, "k_cache"),
+        _ptr(v_cache, torch.bfloat16, "v_cache"), _ptr(thresholds, torch.float32, "thresholds"),
+        _ptr(out, torch.bfloat16, "out"), _ptr(sel_counts, torch.int32, "sel_counts"),
+        _ptr(sel_bitmap_debug, torch.int32, "sel_bitmap_debug"), ws, nbytes, _stream(stream)),
+        "saga_decode_step")
+
+
+def saga_full_attention(d: SagaDims, q: torch.Tensor, k_cache: torch.Tensor,
+                        v_cache: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                        stream=None) -> None:
+    """Dense decode attention over all ``ctx_len`` rows (GQA / SAGA baseline)."""
+    bh = d.batch * d.h_q
+    _need(q, bh * d.head_dim, "q")
+    _need(k_cache, d.batch * d.h_k * d.cache_len * d.head_dim, "k_cache")
+    _need(v_cache, d.batch * d.h_v * d.cache_len * d.head_dim, "v_cache")
+    _need(out, bh * d.head_dim, "out")
+    ws, nbytes = _ws(workspace)
+    _check(library().saga_full_attention(
+        ctypes.byref(d), _ptr(q, torch.bfloat16, "q"), _ptr(k_cache, torch.bfloat16, "k_cache"),
+        _ptr(v_cache, torch.bfloat16, "v_cache"), _ptr(out, torch.bfloat16, "out"), ws, nbytes,
+        _stream(stream)), "saga_full_attention")

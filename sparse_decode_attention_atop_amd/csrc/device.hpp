@@ -1,0 +1,169 @@
+// device.hpp -- gfx950 device helpers shared by the SAGA / Atop-N kernels.
+//
+// The one piece of arithmetic that every kernel must do identically is the
+// QK tile (qk_tile below): the threshold refresh ranks the logits it produces
+// and the decode step compares the logits it produces against that rank, so
+// both must be the same fp32 values bit for bit.  Both call this one routine,
+// which fixes the MFMA sequence and the accumulation order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace saga {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;            // 4 waves per workgroup
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// ------------------------------------------------------------ conversions
+__device__ __forceinline__ float bf16lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Order-preserving map of fp32 bit patterns to unsigned keys: a > b as floats
+// iff key(a) > key(b).  -0.0 is first folded onto +0.0 so that the key order
+// and the float comparison agree on zeros.
+__device__ __forceinline__ uint32_t float_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// ------------------------------------------------------------ memory
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// ------------------------------------------------------------ wave utilities
+// Orders LDS traffic between lanes of one wave (no workgroup barrier).
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Number of set bits of `mask` in lanes below this one.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Max / sum over the 16 lanes that share lane>>4 (one MFMA row group).
+__device__ __forceinline__ float group16_max(float v)
+{
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, __shfl_xor(v, 8));
+    return v;
+}
+__device__ __forceinline__ float group16_sum(float v)
+{
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    return v;
+}
+
+// ------------------------------------------------------------ the QK tile
+//
+// One wave computes logits for 16*U consecutive cache rows and up to 16 query
+// heads of one key-head group with v_mfma_f32_16x16x32_bf16:
+//   A (16 x 32)  = query heads x a 32-wide slab of head_dim   (q fragment)
+//   B (32 x 16)  = the same slab x 16 cache rows               (K fragment)
+//   D (16 x 16)  = logits[head][row]
+// Lane l supplies A row l%16 / B column l%16 with the 8 slab elements
+// 8*(l/16) .. 8*(l/16)+7, i.e. one 16-byte load per lane per slab; the 64
+// lanes of one load instruction cover 16 rows x 64 contiguous bytes.
+// Lane l receives D[4*(l/16)+i][l%16], i = 0..3: the logits of row l%16 for
+// the head slots 4*(l/16)+i.
+template <int D>
+struct QFrag {
+    u32x4 v[D / 32];
+};
+
+// q_head: row of query head slot (lane%16) or nullptr for an unused slot.
+template <int D>
+__device__ __forceinline__ QFrag<D> load_qfrag(const uint16_t* q_head)
+{
+    QFrag<D> f;
+    const int grp = lane_id() >> 4;
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+        if (q_head) f.v[m] = ld16(q_head + 32 * m + 8 * grp);
+        else f.v[m] = u32x4{0u, 0u, 0u, 0u};
+    }
+    return f;
+}
+
+// Rows row0 + 16u + (lane%16) for u < U; rows at or past `row_end` are read
+// from row_end-1 instead (always a valid row) and must be masked by the caller.
+template <int D, int U>
+struct KTile {
+    u32x4 v[U][D / 32];
+};
+
+template <int D, int U>
+__device__ __forceinline__ void load_ktile(KTile<D, U>& t, const uint16_t* k_head, int64_t row0,
+                                           int64_t row_end)
+{
+    const int col = lane_id() & 15, grp = lane_id() >> 4;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        int64_t r = row0 + 16 * u + col;
+        r = r < row_end ? r : row_end - 1;
+        const uint16_t* p = k_head + r * D + 8 * grp;
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) t.v[u][m] = ld16(p + 32 * m);
+    }
+}
+
+// logits[u][i] = scale * sum_c q[slot 4*(lane/16)+i][c] * K[row0+16u+lane%16][c]
+template <int D, int U>
+__device__ __forceinline__ void qk_tile(const QFrag<D>& qf, const KTile<D, U>& kt, float scale,
+                                        float (&s)[U][4])
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, qf.v[m]), __builtin_bit_cast(bf16x8, kt.v[u][m]),
+                acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[u][i] = acc[i] * scale;
+    }
+}
+
+// ------------------------------------------------------------ partials
+// Per (b, query head, chunk) partial softmax state written by the decode and
+// full-attention kernels and merged by combine_kernel.
+struct Partials {
+    float* m;      // [B*h_q][chunks]  reference max (or -inf: nothing selected)
+    float* l;      // [B*h_q][chunks]  sum of exp(s - m)
+    int32_t* c;    // [B*h_q][chunks]  number of selected rows
+    float* o;      // [B*h_q][chunks][D] sum of exp(s - m) * v
+};
+
+}  // namespace saga

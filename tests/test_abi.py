@@ -1,0 +1,154 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/saga.h
+declares, sizes workspaces, and rejects bad arguments before any launch.
+No call here reaches a kernel, so no GPU is needed."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch  # noqa: F401  (load torch's HIP runtime before the library)
+
+import sparse_decode_attention_atop_amd as saga
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "saga.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_library_built():
+    assert os.path.exists(saga.LIB_PATH), "run `python -m sparse_decode_attention_atop_amd.build`"
+
+
+def test_exports_match_header():
+    declared = header_functions()
+    assert declared == sorted(saga.EXPORTED_SYMBOLS)
+    out = subprocess.run(["nm", "-D", "--defined-only", saga.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(ln.split()[-1] for ln in out.splitlines() if " T " in ln)
+    assert exported == declared, "libsaga.so must export exactly the header's functions"
+    lib = saga.library()
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_status_strings_and_version():
+    assert saga.saga_status_string(0) == "ok"
+    assert saga.saga_status_string(3) == "workspace too small"
+    assert saga.saga_status_string(99) == "unknown status"
+    assert saga.saga_version() >= 100
+
+
+def good_dims(**kw):
+    base = dict(batch=2, h_q=12, h_k=1, h_v=2, head_dim=128, ctx_len=1000, cache_len=1024)
+    base.update(kw)
+    return saga.dims(**base)
+
+
+def test_workspace_sizing():
+    d = good_dims()
+    n = saga.saga_workspace_bytes(d, 64)
+    rows = 2 * 12
+    assert n >= 2 * rows * 1024 * 4          # logits + candidate buffers
+    assert n % 256 == 0
+    # independent of ctx_len and N
+    assert saga.saga_workspace_bytes(good_dims(ctx_len=1), 1) == n
+    assert saga.saga_workspace_bytes(good_dims(), 5000) == n
+    for bad in (dict(batch=0), dict(h_q=12, h_k=5), dict(h_v=5), dict(ctx_len=0),
+                dict(ctx_len=2000), dict(head_dim=96), dict(h_q=34, h_k=2, h_v=2)):
+        assert saga.saga_workspace_bytes(good_dims(**bad), 64) == 0, bad
+
+
+FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced (calls fail validation first)
+
+
+def call_decode(d, ws_bytes, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, tau=FAKE, out=FAKE, counts=None, bitmap=None, ws=FAKE)
+    p.update(ptrs)
+    return saga.library().saga_decode_step(ctypes.byref(d), p["q"], p["k"], p["v"], p["tau"],
+                                           p["out"], p["counts"], p["bitmap"], p["ws"], ws_bytes,
+                                           None)
+
+
+def call_refresh(d, top_n, ws_bytes, **ptrs):
+    p = dict(q=FAKE, k=FAKE, tau=FAKE, dbg=None, ws=FAKE)
+    p.update(ptrs)
+    return saga.library().atopn_refresh_thresholds(ctypes.byref(d), top_n, p["q"], p["k"],
+                                                   p["tau"], p["dbg"], p["ws"], ws_bytes, None)
+
+
+def call_full(d, ws_bytes, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, ws=FAKE)
+    p.update(ptrs)
+    return saga.library().saga_full_attention(ctypes.byref(d), p["q"], p["k"], p["v"], p["out"],
+                                              p["ws"], ws_bytes, None)
+
+
+INVALID, UNSUPPORTED, SMALL = 1, 2, 3
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(batch=0), INVALID), (dict(h_q=0), INVALID), (dict(h_k=5), INVALID),
+    (dict(h_v=7), INVALID), (dict(ctx_len=0), INVALID), (dict(ctx_len=1025), INVALID),
+    (dict(cache_len=1 << 27, ctx_len=10), INVALID), (dict(head_dim=96), UNSUPPORTED),
+    (dict(h_q=34, h_k=2, h_v=2), UNSUPPORTED),
+])
+def test_dims_errors_every_entry_point(bad, code):
+    d = good_dims(**bad)
+    assert call_decode(d, 1 << 40) == code
+    assert call_refresh(d, 8, 1 << 40) == code
+    assert call_full(d, 1 << 40) == code
+
+
+def test_reserved_fields_and_scale():
+    d = good_dims()
+    d.reserved = 1
+    assert call_decode(d, 1 << 40) == INVALID
+    d = good_dims()
+    d.scale = float("nan")
+    assert call_refresh(d, 8, 1 << 40) == INVALID
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "tau", "out", "ws"])
+def test_decode_null_pointers(name):
+    assert call_decode(good_dims(), 1 << 40, **{name: None}) == INVALID
+
+
+@pytest.mark.parametrize("name", ["q", "k", "tau", "ws"])
+def test_refresh_null_pointers(name):
+    assert call_refresh(good_dims(), 8, 1 << 40, **{name: None}) == INVALID
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "out", "ws"])
+def test_full_null_pointers(name):
+    assert call_full(good_dims(), 1 << 40, **{name: None}) == INVALID
+
+
+def test_misaligned_pointers():
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    assert call_decode(good_dims(), 1 << 40, k=odd) == INVALID
+    assert call_refresh(good_dims(), 8, 1 << 40, q=odd) == INVALID
+    assert call_full(good_dims(), 1 << 40, v=odd) == INVALID
+    assert call_decode(good_dims(), 1 << 40, counts=ctypes.c_void_p((1 << 20) + 2)) == INVALID
+
+
+def test_top_n_and_workspace_errors():
+    d = good_dims()
+    assert call_refresh(d, 0, 1 << 40) == INVALID
+    assert call_refresh(d, -5, 1 << 40) == INVALID
+    need = saga.saga_workspace_bytes(d, 8)
+    assert call_decode(d, need - 1) == SMALL
+    assert call_refresh(d, 8, need - 1) == SMALL
+    assert call_full(d, need - 1) == SMALL
+
+
+def test_full_attention_unsupported_head_maps():
+    # 32 query heads per value head exceeds the dense kernel's per-value-head slots.
+    d = good_dims(h_q=32, h_k=2, h_v=1, head_dim=64)
+    assert call_full(d, 1 << 40) == UNSUPPORTED
