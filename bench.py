@@ -94,6 +94,7 @@ def run_saga(torch, saga, wl, w, args):
     log(f"generating {w.layers} layers of {w.name} ({w.kv_bytes() / 1e9:.1f} GB of KV cache)")
     for layer in range(w.layers):
         K, V, q = layer_inputs(torch, wl, w, layer)
+        log(f"  layer {layer} ready")
         layers.append(dict(K=K, V=V, q=q,
                            tau=torch.empty(w.batch, w.h_q, dtype=torch.float32, device="cuda"),
                            out=torch.empty(w.batch, w.h_q, w.head_dim, dtype=torch.bfloat16,
@@ -156,6 +157,7 @@ def run_gqa(torch, saga, wl, w, hkv, args):
     log(f"generating GQA twin h_k=h_v={hkv} ({g.kv_bytes() / 1e9:.1f} GB)")
     for layer in range(g.layers):
         K, V, q = layer_inputs(torch, wl, g, layer)
+        log(f"  GQA layer {layer} ready")
         layers.append(dict(K=K, V=V, q=q, out=torch.empty(g.batch, g.h_q, g.head_dim,
                                                           dtype=torch.bfloat16, device="cuda")))
     d0 = saga.dims(g.batch, g.h_q, g.h_k, g.h_v, g.head_dim, L, g.rows, g.scale)

@@ -16,7 +16,7 @@ using namespace saga;
 
 namespace {
 
-constexpr int kTargetBlocks = 2048;       // workgroups per launch we aim for (256 CUs)
+constexpr int kTargetBlocks = SAGA_TARGET_BLOCKS;
 constexpr int64_t kMaxCacheLen = int64_t(1) << 27;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -40,38 +40,6 @@ int validate_dims(const saga_dims* d)
 
 bool misaligned(const void* p, size_t a) { return ((uintptr_t)p) % a != 0; }
 
-// Workspace layout (byte offsets), identical for every ctx_len <= cache_len.
-struct Layout {
-    int64_t ld;           // row stride of logits / candidates (elements)
-    int max_chunks;
-    size_t pm, pl, pc, po, logits, cand, ghist, done, ccount, state, total;
-};
-
-Layout make_layout(const saga_dims* d)
-{
-    Layout L{};
-    const size_t rows = (size_t)d->batch * d->h_q;
-    L.ld = (int64_t)round_up((size_t)d->cache_len, 64);
-    const int64_t want = kTargetBlocks / ((int64_t)d->batch * d->h_k);
-    const int64_t by_len = (d->cache_len + 127) / 128;   // smallest block tile is 128 rows
-    int64_t mc = want < by_len ? want : by_len;
-    L.max_chunks = (int)(mc < 1 ? 1 : mc);
-    size_t off = 0;
-    auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes, 256); return o; };
-    L.pm = take(rows * L.max_chunks * 4);
-    L.pl = take(rows * L.max_chunks * 4);
-    L.pc = take(rows * L.max_chunks * 4);
-    L.po = take(rows * L.max_chunks * (size_t)d->head_dim * 4);
-    L.logits = take(rows * (size_t)L.ld * 4);
-    L.cand = take(rows * (size_t)L.ld * 4);
-    L.ghist = take(rows * kHistBins * 4);
-    L.done = take(rows * 4);
-    L.ccount = take(rows * 4);
-    L.state = take(rows * 16);
-    L.total = off;
-    return L;
-}
-
 struct Chunking {
     int chunks;
     int64_t rows;
@@ -92,6 +60,42 @@ Chunking plan_chunks(int64_t ctx, int64_t pairs, int64_t block_rows, int max_chu
     return {(int)((ctx + rows - 1) / rows), rows};
 }
 
+// Workspace layout (byte offsets), identical for every ctx_len <= cache_len.
+struct Layout {
+    int max_chunks;
+    int64_t entry_rows;   // selection-list capacity per (b, query head)
+    size_t pm, pl, pc, po, entries, lcount, lmax, sample, pivot, total;
+};
+
+Layout make_layout(const saga_dims* d)
+{
+    Layout L{};
+    const size_t rows = (size_t)d->batch * d->h_q;
+    const int64_t want = kTargetBlocks / ((int64_t)d->batch * d->h_k);
+    const int64_t by_len = (d->cache_len + 127) / 128;   // smallest block tile is 128 rows
+    int64_t mc = want < by_len ? want : by_len;
+    if (mc > kMaxListsPerRow / kWavesPerBlock) mc = kMaxListsPerRow / kWavesPerBlock;
+    L.max_chunks = (int)(mc < 1 ? 1 : mc);
+    // chunks * rows_per_chunk <= ctx + rows_per_chunk(ctx), and rows_per_chunk
+    // never exceeds max(block rows, its value at ctx = cache_len).
+    const int64_t br = decode_block_rows(d->head_dim);
+    const Chunking top = plan_chunks(d->cache_len, (int64_t)d->batch * d->h_k, br, L.max_chunks);
+    L.entry_rows = d->cache_len + (top.rows > br ? top.rows : br);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes, 256); return o; };
+    L.pm = take(rows * L.max_chunks * 4);
+    L.pl = take(rows * L.max_chunks * 4);
+    L.pc = take(rows * L.max_chunks * 4);
+    L.po = take(rows * L.max_chunks * (size_t)d->head_dim * 4);
+    L.entries = take(rows * (size_t)L.entry_rows * 8);
+    L.lcount = take(rows * L.max_chunks * kWavesPerBlock * 4);
+    L.lmax = take(rows * L.max_chunks * kWavesPerBlock * 4);
+    L.sample = take(rows * kSampleMax * 4);
+    L.pivot = take(rows * 4);
+    L.total = off;
+    return L;
+}
+
 Partials partials(void* ws, const Layout& L)
 {
     unsigned char* w = static_cast<unsigned char*>(ws);
@@ -104,6 +108,30 @@ Partials partials(void* ws, const Layout& L)
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SAGA_OK : SAGA_ERR_HIP; }
+
+// Arguments of the stream-select kernel for one call.
+SelectStreamArgs stream_args(const saga_dims* dims, const Layout& L, const Chunking& ch,
+                             const void* q, const void* k, const float* tau, void* ws)
+{
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    SelectStreamArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.tau = tau;
+    a.entries = reinterpret_cast<uint2*>(w + L.entries);
+    a.list_count = reinterpret_cast<int32_t*>(w + L.lcount);
+    a.list_max = reinterpret_cast<float*>(w + L.lmax);
+    a.B = dims->batch;
+    a.hq = dims->h_q;
+    a.hk = dims->h_k;
+    a.Gk = dims->h_q / dims->h_k;
+    a.ctx = dims->ctx_len;
+    a.cache_len = dims->cache_len;
+    a.rows_per_chunk = ch.rows;
+    a.chunks = ch.chunks;
+    a.scale = dims->scale;
+    return a;
+}
 
 }  // namespace
 
@@ -136,48 +164,76 @@ SAGA_EXPORT int atopn_refresh_thresholds(const saga_dims* dims, int32_t top_n, c
     const int64_t ctx = dims->ctx_len;
     const Chunking ch = plan_chunks(ctx, (int64_t)dims->batch * dims->h_k, decode_block_rows(D),
                                     L.max_chunks);
-    const bool need_select = (int64_t)top_n < ctx;
+    float* pivot = reinterpret_cast<float*>(w + L.pivot);
 
-    if (need_select || logits_debug_dev) {
-        LogitsArgs la{};
-        la.q = static_cast<const uint16_t*>(q_dev);
-        la.k = static_cast<const uint16_t*>(k_cache_dev);
-        la.logits = reinterpret_cast<float*>(w + L.logits);
-        la.debug = logits_debug_dev;
-        la.ld = L.ld;
-        la.B = dims->batch;
-        la.hq = dims->h_q;
-        la.hk = dims->h_k;
-        la.Gk = dims->h_q / dims->h_k;
-        la.ctx = ctx;
-        la.cache_len = dims->cache_len;
-        la.rows_per_chunk = ch.rows;
-        la.scale = dims->scale;
-        la.ghist = reinterpret_cast<uint32_t*>(w + L.ghist);
-        la.done = reinterpret_cast<uint32_t*>(w + L.done);
-        la.cand_count = reinterpret_cast<uint32_t*>(w + L.ccount);
-        st = hip_status(launch_qk_logits(D, la, ch.chunks, s));
-        if (st != SAGA_OK) return st;
-    }
-    if (!need_select) {
-        // N >= ctx: every entry is kept, tau = -inf.
+    if ((int64_t)top_n >= ctx) {
+        // N >= ctx: every entry is kept, tau = -inf.  The logits are still
+        // produced when asked for (a pass that selects nothing).
+        if (logits_debug_dev) {
+            st = hip_status(launch_fill_u32(reinterpret_cast<uint32_t*>(pivot), rows, 0x7f800000u, s));
+            if (st != SAGA_OK) return st;
+            SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, pivot, workspace_dev);
+            a.logits_out = logits_debug_dev;
+            st = hip_status(launch_select_stream(D, a, s));
+            if (st != SAGA_OK) return st;
+        }
         return hip_status(launch_fill_u32(reinterpret_cast<uint32_t*>(thresholds_dev), rows,
                                           0xff800000u, s));
     }
-    SelectArgs sa{};
-    sa.logits = reinterpret_cast<const float*>(w + L.logits);
-    sa.ld = L.ld;
-    sa.ctx = ctx;
-    sa.rows = rows;
-    sa.segs = (int)((ctx + kSelectSeg - 1) / kSelectSeg);
-    sa.top_n = (uint32_t)top_n;
-    sa.ghist = reinterpret_cast<uint32_t*>(w + L.ghist);
-    sa.done = reinterpret_cast<uint32_t*>(w + L.done);
-    sa.state = reinterpret_cast<uint32_t*>(w + L.state);
-    sa.cand = reinterpret_cast<uint32_t*>(w + L.cand);
-    sa.cand_count = reinterpret_cast<uint32_t*>(w + L.ccount);
-    sa.tau = thresholds_dev;
-    return hip_status(launch_select(sa, s));
+
+    // 1-2. Pivot from a strided sample of at most kSampleMax rows.  With the
+    // whole context sampled the pivot is tau itself; otherwise its rank in
+    // the sample sits five standard deviations above the expected number of
+    // sample logits >= tau, so at least N logits are >= pivot except with
+    // negligible probability (and step 4 stays exact regardless).
+    SampleArgs sa{};
+    sa.q = static_cast<const uint16_t*>(q_dev);
+    sa.k = static_cast<const uint16_t*>(k_cache_dev);
+    sa.sample = reinterpret_cast<float*>(w + L.sample);
+    sa.pivot = pivot;
+    sa.B = dims->batch;
+    sa.hq = dims->h_q;
+    sa.hk = dims->h_k;
+    sa.Gk = dims->h_q / dims->h_k;
+    sa.cache_len = dims->cache_len;
+    sa.stride = (ctx + kSampleMax - 1) / kSampleMax;
+    sa.m = (int)((ctx + sa.stride - 1) / sa.stride);
+    if (sa.stride == 1) {
+        sa.rank = top_n;
+    } else {
+        const double mu = (double)top_n * sa.m / (double)ctx;
+        double r = ceil(mu + 5.0 * sqrt(mu) + 5.0);
+        if (r > sa.m) r = sa.m;
+        sa.rank = (int)r;
+    }
+    sa.scale = dims->scale;
+    st = hip_status(launch_sample(D, sa, s));
+    if (st != SAGA_OK) return st;
+
+    // 3. Candidate lists: every logit >= pivot.
+    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, pivot, workspace_dev);
+    a.logits_out = logits_debug_dev;
+    st = hip_status(launch_select_stream(D, a, s));
+    if (st != SAGA_OK) return st;
+
+    // 4. Exact N-th largest per row.
+    FinalArgs fa{};
+    fa.q = sa.q;
+    fa.k = sa.k;
+    fa.entries = a.entries;
+    fa.list_count = a.list_count;
+    fa.tau = thresholds_dev;
+    fa.B = dims->batch;
+    fa.hq = dims->h_q;
+    fa.hk = dims->h_k;
+    fa.Gk = sa.Gk;
+    fa.ctx = ctx;
+    fa.cache_len = dims->cache_len;
+    fa.rows_per_chunk = ch.rows;
+    fa.chunks = ch.chunks;
+    fa.top_n = (uint32_t)top_n;
+    fa.scale = dims->scale;
+    return hip_status(launch_refresh_final(D, fa, s));
 }
 
 SAGA_EXPORT int saga_decode_step(const saga_dims* dims, const void* q_dev, const void* k_cache_dev,
@@ -207,29 +263,37 @@ SAGA_EXPORT int saga_decode_step(const saga_dims* dims, const void* q_dev, const
     }
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
                                     decode_block_rows(D), L.max_chunks);
-    DecodeArgs a{};
-    a.q = static_cast<const uint16_t*>(q_dev);
-    a.k = static_cast<const uint16_t*>(k_cache_dev);
-    a.v = static_cast<const uint16_t*>(v_cache_dev);
-    a.tau = thresholds_dev;
+    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, thresholds_dev, workspace_dev);
     a.bitmap = sel_bitmap_debug_dev;
     a.bitmap_words = words;
-    a.part = partials(workspace_dev, L);
-    a.B = dims->batch;
-    a.hq = dims->h_q;
-    a.hk = dims->h_k;
-    a.hv = dims->h_v;
-    a.Gk = dims->h_q / dims->h_k;
-    a.Gv = dims->h_q / dims->h_v;
-    a.ctx = dims->ctx_len;
-    a.cache_len = dims->cache_len;
-    a.rows_per_chunk = ch.rows;
-    a.chunks = ch.chunks;
-    a.scale = dims->scale;
-    a.wave_lds = decode_wave_lds_bytes(D, a.Gk);
-    st = hip_status(launch_sparse_decode(D, a, s));
+    st = hip_status(launch_select_stream(D, a, s));
     if (st != SAGA_OK) return st;
-    return hip_status(launch_combine(D, a.part, rows, ch.chunks, static_cast<uint16_t*>(out_dev),
+
+    // Segments of chunks per gather workgroup: about kGatherTargetBlocks
+    // workgroups in total, at most kMaxListsPerSeg lists each.
+    GatherArgs ga{};
+    ga.v = static_cast<const uint16_t*>(v_cache_dev);
+    ga.entries = a.entries;
+    ga.list_count = a.list_count;
+    ga.list_max = a.list_max;
+    ga.part = partials(workspace_dev, L);
+    ga.B = dims->batch;
+    ga.hq = dims->h_q;
+    ga.hv = dims->h_v;
+    ga.Gv = dims->h_q / dims->h_v;
+    ga.cache_len = dims->cache_len;
+    ga.rows_per_chunk = ch.rows;
+    ga.chunks = ch.chunks;
+    int64_t segs = (kGatherTargetBlocks + rows - 1) / rows;
+    if (segs > ch.chunks) segs = ch.chunks;
+    int64_t cps = (ch.chunks + segs - 1) / segs;
+    const int64_t max_cps = kMaxListsPerSeg / kWavesPerBlock;
+    if (cps > max_cps) cps = max_cps;
+    ga.chunks_per_seg = (int)cps;
+    ga.segs = (int)((ch.chunks + cps - 1) / cps);
+    st = hip_status(launch_gather(D, ga, s));
+    if (st != SAGA_OK) return st;
+    return hip_status(launch_combine(D, ga.part, rows, ga.segs, static_cast<uint16_t*>(out_dev),
                                      sel_counts_dev, s));
 }
 

@@ -1,6 +1,6 @@
-// decode.hip -- SAGA Atop-N decode step: fused K stream, threshold mask,
-// wave-ballot compaction, masked online softmax and sparse value gather; plus
-// the split-sequence combine shared with the full-attention path.
+// decode.hip -- SAGA Atop-N decode step: (1) K stream with the threshold
+// mask and wave-ballot compaction, (2) masked softmax with the sparse value
+// gather, (3) split-sequence combine (shared with the full-attention path).
 //
 // Method: "More Value per Key: Asymmetric Sparse Attention for Faster LLM
 // Decoding" (ai.info AI summary): entries are selected by comparing each
@@ -10,128 +10,35 @@
 // key/value heads (Main Findings, first item).  Key heads are decoupled from
 // value heads (Key Contributions 3).
 //
-// Work decomposition (one launch):
-//   grid.y = (b, key head g), grid.x = a chunk of context rows;
-//   each of the 4 waves streams 16*U-row tiles of K[b][g] (once for all
-//   h_q/h_k query heads of the group: MFMA QK tile from device.hpp), compares
-//   each logit with its head's threshold, compacts the hits into a wave-private
-//   LDS queue with ballot + mbcnt, and when the queue fills (or the chunk
-//   ends) drains it: rescale the running softmax state to the new reference
-//   max, gather the selected V rows of each query head's value head and
-//   accumulate exp(s - m) * v into wave-private fp32 LDS accumulators.
-//   Waves are merged in a fixed order at the end and one (m, l, count, o)
-//   partial per (b, query head, chunk) goes to the workspace; combine_kernel
-//   merges chunks in chunk order.  No float atomics: results are
-//   deterministic run to run.
+// select_stream_kernel: grid.y = (b, key head g), grid.x = a chunk of rows.
+//   Each wave streams 16*U-row K tiles once for all h_q/h_k query heads of the
+//   group (MFMA QK tile from device.hpp), compares every logit with its head's
+//   threshold, and compacts the hits with ballot + popcount straight into a
+//   per-(b, query head, chunk, wave) list of (row, logit) in the workspace,
+//   together with the list length and the list's largest logit.  No LDS, no
+//   waiting on anything but the K stream.
+// gather_kernel: grid.y = (b, query head), grid.x = a segment of chunks.
+//   Reads its lists' lengths and maxima, stages the entries in LDS with their
+//   softmax weights exp(s - M) (M = the segment's largest selected logit),
+//   then gathers the selected rows of the query head's value head with
+//   16-byte loads, many rows in flight per lane, accumulating in fp32.
+//   One (M, l, count, o) partial per (b, query head, segment).
+// combine_kernel merges the partials in segment order.
+// Every sum runs in a fixed order and no float atomics are used, so results
+// are bit-identical run to run.
 #include "kernels.hpp"
 
 namespace saga {
 
 namespace {
 
-template <int D>
-struct WaveState {
-    static constexpr int R = 128 / D;      // value rows gathered per wave instruction
-    static constexpr int LPR = kWave / R;  // lanes per gathered row, 2 elements each
-    uint32_t* qkey;   // [kQueueCap] (row - chunk_start) << 4 | head slot
-    float* qs;        // [kQueueCap] logit of the entry
-    float* o;         // [R][Gk][D]
-    float* l;         // [R][16]
-    float* m_cur;     // [16]
-    float* m_new;     // [16]
-    int32_t* cnt;     // [16]
-
-    __device__ void carve(unsigned char* base, int Gk)
-    {
-        qkey = reinterpret_cast<uint32_t*>(base);
-        qs = reinterpret_cast<float*>(qkey + kQueueCap);
-        o = qs + kQueueCap;
-        l = o + R * Gk * D;
-        m_cur = l + R * 16;
-        m_new = m_cur + 16;
-        cnt = reinterpret_cast<int32_t*>(m_new + 16);
-    }
-};
-
-// Drain the wave's queue of `qn` entries into its softmax accumulators.
-// mx[i]: this lane's running max over selected logits of slot 4*(lane/16)+i
-// (cumulative over the chunk, so it bounds every queued entry).
-template <int D>
-__device__ void drain_queue(const WaveState<D>& w, int qn, const float (&mx)[4], int Gk,
-                            const uint16_t* __restrict__ v, const int64_t* voff, int64_t r0)
-{
-    constexpr int R = WaveState<D>::R, LPR = WaveState<D>::LPR, NB = 8;
-    const int lane = lane_id(), col = lane & 15, grp = lane >> 4;
-
-    // 1. New reference max per head slot.
-    float mg[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mg[i] = group16_max(mx[i]);
-    if (col == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w.m_new[4 * grp + i] = mg[i];
-    }
-    wave_sync();
-
-    // 2. Rescale the accumulators of slots whose max moved.
-    const int r = lane / LPR, e0 = 2 * (lane % LPR);
-    for (int h = 0; h < Gk; ++h) {
-        const float mo = w.m_cur[h], mn = w.m_new[h];
-        if (mn > mo) {                                   // wave-uniform
-            const float alpha = __expf(mo - mn);         // mo = -inf gives 0
-            float2* po = reinterpret_cast<float2*>(w.o + (r * Gk + h) * D + e0);
-            float2 t = *po;
-            t.x *= alpha;
-            t.y *= alpha;
-            *po = t;
-            if ((lane % LPR) == 0) w.l[r * 16 + h] *= alpha;
-        }
-    }
-    wave_sync();
-    if (col == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w.m_cur[4 * grp + i] = mg[i];
-    }
-    wave_sync();
-
-    // 3. Gather the selected value rows, NB entries per lane slot in flight.
-    for (int base = 0; base < qn; base += NB * R) {
-        uint32_t vv[NB];
-        uint32_t key[NB];
-#pragma unroll
-        for (int k = 0; k < NB; ++k) {
-            const int idx = base + k * R + r;
-            key[k] = idx < qn ? w.qkey[idx] : 0xffffffffu;
-            if (key[k] != 0xffffffffu) {
-                const int h = key[k] & 15;
-                const int64_t row = r0 + (key[k] >> 4);
-                vv[k] = *reinterpret_cast<const uint32_t*>(v + voff[h] + row * D + e0);
-            } else {
-                vv[k] = 0u;
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < NB; ++k) {
-            if (key[k] == 0xffffffffu) continue;
-            const int idx = base + k * R + r;
-            const int h = key[k] & 15;
-            const float wgt = __expf(w.qs[idx] - w.m_cur[h]);
-            float2* po = reinterpret_cast<float2*>(w.o + (r * Gk + h) * D + e0);
-            float2 t = *po;
-            t.x += wgt * bf16lo(vv[k]);
-            t.y += wgt * bf16hi(vv[k]);
-            *po = t;
-            if ((lane % LPR) == 0) w.l[r * 16 + h] += wgt;
-        }
-    }
-    wave_sync();
-}
-
 template <int D, int U>
-__global__ __launch_bounds__(kBlock) void sparse_decode_kernel(DecodeArgs a)
+__global__ __launch_bounds__(kBlock) void select_stream_kernel(SelectStreamArgs a)
 {
-    extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int R = WaveState<D>::R;
+    // Hits are staged per (wave, head slot) in LDS and written to the global
+    // lists in runs of up to kStageCap entries, so the lists are written with
+    // whole cache lines instead of scattered 8-byte stores.
+    __shared__ uint2 stage[kWavesPerBlock][16][kStageCap];
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int chunk = blockIdx.x;
@@ -139,139 +46,236 @@ __global__ __launch_bounds__(kBlock) void sparse_decode_kernel(DecodeArgs a)
     const int Gk = a.Gk;
     const int64_t r0 = (int64_t)chunk * a.rows_per_chunk;
     const int64_t r1 = min(r0 + a.rows_per_chunk, a.ctx);
-    const int qh0 = b * a.hq + g * Gk;                  // flat index of slot 0
-
-    int64_t* voff = reinterpret_cast<int64_t*>(smem);
-    WaveState<D> ws;
-    ws.carve(smem + kDecodeLdsHeader + wave * a.wave_lds, Gk);
-
-    if (threadIdx.x < 16) {
-        const int slot = threadIdx.x;
-        const int vh = (g * Gk + slot) / a.Gv;
-        voff[slot] = slot < Gk ? ((int64_t)(b * a.hv + vh) * a.cache_len) * D : 0;
-    }
-    for (int t = lane; t < R * Gk * D; t += kWave) ws.o[t] = 0.f;
-    if (lane < 16) {
-        ws.m_cur[lane] = -INFINITY;
-        ws.cnt[lane] = 0;
-        for (int r = 0; r < R; ++r) ws.l[r * 16 + lane] = 0.f;
-    }
-    __syncthreads();
+    const int64_t capw = a.rows_per_chunk / kWavesPerBlock;
+    const int qh0 = b * a.hq + g * Gk;
+    uint2 (*st)[kStageCap] = stage[wave];
 
     const QFrag<D> qf = load_qfrag<D>(col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr);
     float tau[4], mx[4];
-    int32_t hits[4];
+    int32_t hits[4], flushed[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int slot = 4 * grp + i;
         tau[i] = slot < Gk ? a.tau[qh0 + slot] : INFINITY;
         mx[i] = -INFINITY;
         hits[i] = 0;
+        flushed[i] = 0;
     }
+    const uint32_t below = (1u << col) - 1u;
+
+    // Write the staged entries of slots 4*gf + i (gf = 0..3) to their lists.
+    auto flush = [&](int i) {
+        wave_sync();
+#pragma unroll
+        for (int gf = 0; gf < 4; ++gf) {
+            const int slot = 4 * gf + i;
+            if (slot >= Gk) break;
+            const int n = __shfl(hits[i] - flushed[i], 16 * gf);
+            const int done = __shfl(flushed[i], 16 * gf);
+            if (n > 0 && lane < n) {
+                const int64_t list = ((int64_t)(qh0 + slot) * a.chunks + chunk) * kWavesPerBlock + wave;
+                a.entries[list * capw + done + lane] = st[slot][lane];
+            }
+        }
+        flushed[i] = hits[i];
+        wave_sync();
+    };
 
     const uint16_t* khead = a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
-    int qn = 0;                                          // queued entries (wave-uniform)
     for (int64_t t0 = r0 + wave * 16 * U; t0 < r1; t0 += kWavesPerBlock * 16 * U) {
         KTile<D, U> kt;
         load_ktile<D, U>(kt, khead, t0, r1);
         float s[U][4];
         qk_tile<D, U>(qf, kt, a.scale, s);
-        bool pred[U][4];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const bool valid = t0 + 16 * u + col < r1;
+            const int64_t row = t0 + 16 * u + col;
+            const bool valid = row < r1;
+            if (a.logits_out && valid) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pred[u][i] = valid && s[u][i] >= tau[i];
-                if (pred[u][i]) mx[i] = fmaxf(mx[i], s[u][i]);
+                for (int i = 0; i < 4; ++i)
+                    if (4 * grp + i < Gk) a.logits_out[(int64_t)(qh0 + 4 * grp + i) * a.ctx + row] = s[u][i];
             }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint64_t mask = __ballot(pred[u][i]);
-                if (mask == 0) continue;                 // wave-uniform
+                const bool pred = valid && s[u][i] >= tau[i];
+                const uint64_t mask = __ballot(pred);
+                if (mask == 0) continue;                         // wave-uniform
                 const uint32_t mine = (uint32_t)(mask >> (16 * grp)) & 0xffffu;
+                if (pred) {
+                    mx[i] = fmaxf(mx[i], s[u][i]);
+                    const int pos = hits[i] - flushed[i] + __popc(mine & below);
+                    st[4 * grp + i][pos] = make_uint2((uint32_t)(row - r0), __float_as_uint(s[u][i]));
+                }
                 hits[i] += __popc(mine);
                 if (a.bitmap && col == 0 && mine) {
-                    const int64_t row = t0 + 16 * u;     // multiple of 16
-                    atomicOr(a.bitmap + (int64_t)(qh0 + 4 * grp + i) * a.bitmap_words + row / 32,
-                             mine << (row & 31));
+                    const int64_t row0 = t0 + 16 * u;             // multiple of 16
+                    atomicOr(a.bitmap + (int64_t)(qh0 + 4 * grp + i) * a.bitmap_words + row0 / 32,
+                             mine << (row0 & 31));
                 }
-                const int nsel = __popcll(mask);
-                if (qn + nsel > kQueueCap) {
-                    drain_queue<D>(ws, qn, mx, Gk, a.v, voff, r0);
-                    qn = 0;
-                }
-                if (pred[u][i]) {
-                    const int pos = qn + (int)lanes_below(mask);
-                    ws.qkey[pos] = (uint32_t)((t0 + 16 * u + col - r0) << 4) | (uint32_t)(4 * grp + i);
-                    ws.qs[pos] = s[u][i];
-                }
-                qn += nsel;
+                // A slot gains at most 16 entries per ballot: flush before overflow.
+                if (__ballot(hits[i] - flushed[i] > kStageCap - 16)) flush(i);
             }
         }
     }
-    if (qn > 0) drain_queue<D>(ws, qn, mx, Gk, a.v, voff, r0);
-    if (col == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ws.cnt[4 * grp + i] = hits[i];
-    }
-    __syncthreads();
-
-    // Merge the 4 waves (fixed order) into this chunk's partial.
-    for (int p = threadIdx.x; p < Gk * D; p += kBlock) {
-        const int h = p / D, e = p - h * D;
-        float M = -INFINITY;
-        for (int wv = 0; wv < kWavesPerBlock; ++wv) {
-            WaveState<D> o;
-            o.carve(smem + kDecodeLdsHeader + wv * a.wave_lds, Gk);
-            M = fmaxf(M, o.m_cur[h]);
-        }
-        float acc = 0.f, l = 0.f;
-        int32_t c = 0;
-        for (int wv = 0; wv < kWavesPerBlock; ++wv) {
-            WaveState<D> o;
-            o.carve(smem + kDecodeLdsHeader + wv * a.wave_lds, Gk);
-            const float mw = o.m_cur[h];
-            if (mw > -INFINITY) {
-                const float alpha = __expf(mw - M);
-                for (int r = 0; r < R; ++r) {
-                    acc += alpha * o.o[(r * Gk + h) * D + e];
-                    l += alpha * o.l[r * 16 + h];
-                }
-            }
-            c += o.cnt[h];
-        }
-        const int64_t idx = (int64_t)(qh0 + h) * a.chunks + chunk;
-        a.part.o[idx * D + e] = acc;
-        if (e == 0) {
-            a.part.m[idx] = M;
-            a.part.l[idx] = l;
-            a.part.c[idx] = c;
+    for (int i = 0; i < 4; ++i) {
+        if (__ballot(hits[i] > flushed[i])) flush(i);
+        const float m = group16_max(mx[i]);
+        if (col == 0 && 4 * grp + i < Gk) {
+            const int64_t list = ((int64_t)(qh0 + 4 * grp + i) * a.chunks + chunk) * kWavesPerBlock + wave;
+            a.list_count[list] = hits[i];
+            a.list_max[list] = m;
         }
     }
 }
 
-// Merge the per-chunk partials of one (b, query head) in chunk order:
+// Block-wide (256 threads) max and exclusive prefix sum.
+__device__ float block_max(float v, float* red)
+{
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if (lane_id() == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    return v;
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
+{
+    constexpr int LPR = D / 8;             // lanes per value row (16 bytes each)
+    constexpr int SLOTS = kBlock / LPR;    // rows per workgroup load instruction
+    constexpr int CAPL = 2048;             // entries staged per round
+    constexpr int NB = 8;                  // rows in flight per lane
+    static_assert(SLOTS * D <= CAPL, "reduction scratch reuses the staging buffer");
+    __shared__ int32_t pre[kBlock + 1];
+    __shared__ float red[kWavesPerBlock];
+    __shared__ uint32_t erow[CAPL];
+    __shared__ float ew[CAPL];
+
+    const int seg = blockIdx.x;
+    const int bi = blockIdx.y;
+    const int b = bi / a.hq, i = bi - b * a.hq;
+    const int t = threadIdx.x;
+    const int c0 = seg * a.chunks_per_seg;
+    const int c1 = min(c0 + a.chunks_per_seg, a.chunks);
+    const int nl = (c1 - c0) * kWavesPerBlock;
+    const int64_t capw = a.rows_per_chunk / kWavesPerBlock;
+    const int64_t lbase = ((int64_t)bi * a.chunks + c0) * kWavesPerBlock;
+
+    int32_t cnt = 0;
+    float mx = -INFINITY;
+    if (t < nl) {
+        cnt = a.list_count[lbase + t];
+        mx = a.list_max[lbase + t];
+    }
+    const float M = block_max(mx, red);
+    // exclusive prefix of list lengths
+    pre[t] = cnt;
+    __syncthreads();
+    for (int off = 1; off < kBlock; off <<= 1) {
+        const int32_t v = t >= off ? pre[t - off] : 0;
+        __syncthreads();
+        pre[t] += v;
+        __syncthreads();
+    }
+    const int32_t incl = pre[t];
+    __syncthreads();
+    pre[t + 1] = incl;
+    if (t == 0) pre[0] = 0;
+    __syncthreads();
+    const int32_t total = pre[nl];
+
+    const uint16_t* vh = a.v + ((int64_t)(b * a.hv + i / a.Gv) * a.cache_len) * D;
+    const int slot = t / LPR, lc = t - slot * LPR;
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+    float lsum = 0.f;
+
+    for (int32_t base = 0; base < total; base += CAPL) {
+        const int n = min(CAPL, total - base);
+        for (int e = t; e < n; e += kBlock) {
+            const int32_t E = base + e;
+            int lo = 0, hi = nl - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (pre[mid] <= E) lo = mid;
+                else hi = mid - 1;
+            }
+            const int chunk = c0 + lo / kWavesPerBlock;
+            const uint2 ent = a.entries[(lbase + lo) * capw + (E - pre[lo])];
+            erow[e] = (uint32_t)(chunk * a.rows_per_chunk + ent.x);
+            ew[e] = __expf(__uint_as_float(ent.y) - M);
+        }
+        __syncthreads();
+        for (int e0 = slot; e0 < n; e0 += SLOTS * NB) {
+            u32x4 vv[NB];
+            float w[NB];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const int e = e0 + k * SLOTS;
+                if (e < n) {
+                    vv[k] = ld16(vh + (int64_t)erow[e] * D + 8 * lc);
+                    w[k] = ew[e];
+                } else {
+                    vv[k] = u32x4{0u, 0u, 0u, 0u};
+                    w[k] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc[2 * j] += w[k] * bf16lo(vv[k][j]);
+                    acc[2 * j + 1] += w[k] * bf16hi(vv[k][j]);
+                }
+                lsum += w[k];
+            }
+        }
+        __syncthreads();
+    }
+
+    // Reduce the slots in slot order.
+    float* ored = reinterpret_cast<float*>(erow);       // [SLOTS][D]
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ored[slot * D + 8 * lc + j] = acc[j];
+    if (lc == 0) ew[slot] = lsum;
+    __syncthreads();
+    float l = 0.f;
+    for (int s = 0; s < SLOTS; ++s) l += ew[s];
+    const int64_t idx = (int64_t)bi * a.segs + seg;
+    for (int p = t; p < D; p += kBlock) {
+        float o = 0.f;
+        for (int s = 0; s < SLOTS; ++s) o += ored[s * D + p];
+        a.part.o[idx * D + p] = o;
+    }
+    if (t == 0) {
+        a.part.m[idx] = M;
+        a.part.l[idx] = l;
+        a.part.c[idx] = total;
+    }
+}
+
+// Merge the per-segment partials of one (b, query head) in order:
 //   M = max m_c, l = sum e^(m_c - M) l_c, o = sum e^(m_c - M) o_c, out = o / l
 // (zero when nothing was selected), rounded to bf16.
 template <int D>
-__global__ __launch_bounds__(D) void combine_kernel(Partials p, int chunks, uint16_t* out,
+__global__ __launch_bounds__(D) void combine_kernel(Partials p, int parts, uint16_t* out,
                                                     int32_t* counts)
 {
     const int64_t bh = blockIdx.x;
     const int e = threadIdx.x;
-    const float* pm = p.m + bh * chunks;
-    const float* pl = p.l + bh * chunks;
-    const int32_t* pc = p.c + bh * chunks;
-    const float* po = p.o + bh * chunks * D;
+    const float* pm = p.m + bh * parts;
+    const float* pl = p.l + bh * parts;
+    const int32_t* pc = p.c + bh * parts;
+    const float* po = p.o + bh * parts * D;
     float M = -INFINITY;
-    for (int c = 0; c < chunks; ++c) M = fmaxf(M, pm[c]);
+    for (int c = 0; c < parts; ++c) M = fmaxf(M, pm[c]);
     float acc = 0.f, l = 0.f;
     int32_t n = 0;
-    for (int c = 0; c < chunks; ++c) {
+    for (int c = 0; c < parts; ++c) {
         const float m = pm[c];
         if (m > -INFINITY) {
             const float alpha = __expf(m - M);
@@ -293,24 +297,33 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
 
 }  // namespace
 
-hipError_t launch_sparse_decode(int D, const DecodeArgs& a, hipStream_t s)
+hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t s)
 {
     const dim3 grid(a.chunks, a.B * a.hk);
-    const size_t lds = kDecodeLdsHeader + kWavesPerBlock * a.wave_lds;
     if (D == 64)
-        hipLaunchKernelGGL((sparse_decode_kernel<64, decode_unroll(64)>), grid, dim3(kBlock), lds, s, a);
+        hipLaunchKernelGGL((select_stream_kernel<64, decode_unroll(64)>), grid, dim3(kBlock), 0, s, a);
     else
-        hipLaunchKernelGGL((sparse_decode_kernel<128, decode_unroll(128)>), grid, dim3(kBlock), lds, s, a);
+        hipLaunchKernelGGL((select_stream_kernel<128, decode_unroll(128)>), grid, dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_combine(int D, const Partials& p, int rows, int chunks, uint16_t* out,
+hipError_t launch_gather(int D, const GatherArgs& a, hipStream_t s)
+{
+    const dim3 grid(a.segs, a.B * a.hq);
+    if (D == 64)
+        hipLaunchKernelGGL(gather_kernel<64>, grid, dim3(kBlock), 0, s, a);
+    else
+        hipLaunchKernelGGL(gather_kernel<128>, grid, dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(int D, const Partials& p, int rows, int parts, uint16_t* out,
                           int32_t* counts, hipStream_t s)
 {
     if (D == 64)
-        hipLaunchKernelGGL(combine_kernel<64>, dim3(rows), dim3(64), 0, s, p, chunks, out, counts);
+        hipLaunchKernelGGL(combine_kernel<64>, dim3(rows), dim3(64), 0, s, p, parts, out, counts);
     else
-        hipLaunchKernelGGL(combine_kernel<128>, dim3(rows), dim3(128), 0, s, p, chunks, out, counts);
+        hipLaunchKernelGGL(combine_kernel<128>, dim3(rows), dim3(128), 0, s, p, parts, out, counts);
     return hipGetLastError();
 }
 

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tuning.hpp"
+
 namespace saga {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -48,6 +50,15 @@ __device__ __forceinline__ float key_float(uint32_t k)
 
 // ------------------------------------------------------------ memory
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Streaming load for data read exactly once per call (the K cache).
+__device__ __forceinline__ u32x4 ld16_stream(const void* p)
+{
+#if SAGA_K_NONTEMPORAL
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+    return *reinterpret_cast<const u32x4*>(p);
+#endif
+}
 
 // ------------------------------------------------------------ wave utilities
 // Orders LDS traffic between lanes of one wave (no workgroup barrier).
@@ -134,7 +145,7 @@ __device__ __forceinline__ void load_ktile(KTile<D, U>& t, const uint16_t* k_hea
         r = r < row_end ? r : row_end - 1;
         const uint16_t* p = k_head + r * D + 8 * grp;
 #pragma unroll
-        for (int m = 0; m < D / 32; ++m) t.v[u][m] = ld16(p + 32 * m);
+        for (int m = 0; m < D / 32; ++m) t.v[u][m] = ld16_stream(p + 32 * m);
     }
 }
 

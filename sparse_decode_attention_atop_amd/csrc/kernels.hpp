@@ -12,22 +12,9 @@ namespace saga {
 
 // Rows of one workgroup tile (4 waves x 16*U rows) per kernel family and
 // head_dim; chunk lengths are multiples of these.
-constexpr int decode_unroll(int D) { return D == 64 ? 8 : 4; }
+constexpr int decode_unroll(int D) { return D == 64 ? SAGA_STREAM_U64 : SAGA_STREAM_U128; }
 constexpr int decode_block_rows(int D) { return kWavesPerBlock * 16 * decode_unroll(D); }
 constexpr int full_unroll(int D) { return D == 64 ? 4 : 2; }
-
-// Entry-queue capacity (entries per wave) of the sparse decode kernel.
-constexpr int kQueueCap = 256;
-
-// LDS bytes of one wave in the sparse decode kernel:
-//   queue keys + logits, o[R][Gk][D], l[R][16], m_cur[16], m_new[16], count[16]
-inline __host__ __device__ size_t decode_wave_lds_bytes(int D, int Gk)
-{
-    const int R = 128 / D;
-    size_t b = (size_t)kQueueCap * 8 + (size_t)R * Gk * D * 4 + (size_t)R * 16 * 4 + 3 * 16 * 4;
-    return (b + 15) & ~(size_t)15;
-}
-constexpr size_t kDecodeLdsHeader = 128;   // 16 value-head offsets (int64)
 
 // LDS bytes of one wave in the full-attention kernel:
 //   P[TR][16] fp32, alpha[16], m[16], l[16], o[MAXS][D]
@@ -38,51 +25,77 @@ inline __host__ __device__ size_t full_wave_lds_bytes(int D, int maxs)
     return (b + 15) & ~(size_t)15;
 }
 
-// Radix select geometry: 12 + 10 + 10 bits of the order-preserving key.
-constexpr int kHistBins = 4096;
-constexpr int kSelectSeg = 16384;          // logits per workgroup in the select passes
+// Radix select: 11 + 11 + 10 bits of the order-preserving key.
+constexpr int kHistBins = 2048;
 
-struct DecodeArgs {
+// Threshold refresh: sample size cap, candidates staged in LDS by the final
+// select, and the most selection lists one row can have (4 per chunk).
+constexpr int kSampleMax = 4096;
+constexpr int kFinalStage = 16384;
+constexpr int kMaxListsPerRow = 8192;
+
+// Entries staged per (wave, head slot) in the stream kernel before a flush.
+constexpr int kStageCap = 64;
+
+// Gather segments: lists (4 per chunk) handled by one gather workgroup.
+constexpr int kMaxListsPerSeg = 256;
+constexpr int kGatherTargetBlocks = 1024;
+
+// Stream-select kernel: K stream, threshold mask, compaction into lists.
+// List (b*h_q + i, chunk, wave) holds up to rows_per_chunk/4 entries
+// (row - chunk_start, logit bits) at entries[list * rows_per_chunk/4].
+struct SelectStreamArgs {
     const uint16_t* q;
     const uint16_t* k;
-    const uint16_t* v;
     const float* tau;
     uint32_t* bitmap;        // nullable
     int64_t bitmap_words;    // words per (b, i) row of the bitmap
-    Partials part;
-    int32_t B, hq, hk, hv, Gk, Gv;
+    uint2* entries;
+    int32_t* list_count;     // [B*hq][chunks][4]
+    float* list_max;         // [B*hq][chunks][4]  largest selected logit (-inf if none)
+    float* logits_out;       // nullable [B*hq][ctx]: every logit, for checking
+    int32_t B, hq, hk, Gk;
     int64_t ctx, cache_len, rows_per_chunk;
     int32_t chunks;
     float scale;
-    size_t wave_lds;         // decode_wave_lds_bytes(D, Gk)
 };
 
-struct LogitsArgs {
+// Gather kernel: softmax weights and the sparse value gather over the lists.
+struct GatherArgs {
+    const uint16_t* v;
+    const uint2* entries;
+    const int32_t* list_count;
+    const float* list_max;
+    Partials part;           // one partial per (b*h_q + i, segment)
+    int32_t B, hq, hv, Gv;
+    int64_t cache_len, rows_per_chunk;
+    int32_t chunks, chunks_per_seg, segs;
+};
+
+// Refresh steps 1-2: sampled logits and the per-row pivot.
+struct SampleArgs {
     const uint16_t* q;
     const uint16_t* k;
-    float* logits;           // [B*hq][ld]
-    float* debug;            // nullable [B*hq][ctx]
-    int64_t ld;
+    float* sample;           // [B*hq][kSampleMax]
+    float* pivot;            // [B*hq]
     int32_t B, hq, hk, Gk;
-    int64_t ctx, cache_len, rows_per_chunk;
+    int64_t cache_len, stride;
+    int32_t m, rank;         // sample size, rank of the pivot within the sample
     float scale;
-    // per-row select state cleared by the chunk-0 workgroups
-    uint32_t* ghist;         // [B*hq][kHistBins]
-    uint32_t* done;          // [B*hq]
-    uint32_t* cand_count;    // [B*hq]
 };
 
-struct SelectArgs {
-    const float* logits;     // [rows][ld]
-    int64_t ld, ctx;
-    int32_t rows, segs;
+// Refresh step 4: exact N-th largest from the candidate lists.
+struct FinalArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint2* entries;
+    const int32_t* list_count;
+    float* tau;              // [B*hq] out
+    int32_t B, hq, hk, Gk;
+    int64_t ctx, cache_len, rows_per_chunk;
+    int32_t chunks;
     uint32_t top_n;
-    uint32_t* ghist;         // [rows][kHistBins]
-    uint32_t* done;          // [rows]
-    uint32_t* state;         // [rows][4]: bucket, rank within bucket, bucket size
-    uint32_t* cand;          // [rows][ld]
-    uint32_t* cand_count;    // [rows]
-    float* tau;              // [rows]
+    float scale;
 };
 
 struct FullArgs {
@@ -97,11 +110,12 @@ struct FullArgs {
     size_t wave_lds;
 };
 
-hipError_t launch_sparse_decode(int D, const DecodeArgs& a, hipStream_t s);
-hipError_t launch_combine(int D, const Partials& p, int rows, int chunks, uint16_t* out,
+hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t s);
+hipError_t launch_gather(int D, const GatherArgs& a, hipStream_t s);
+hipError_t launch_combine(int D, const Partials& p, int rows, int parts, uint16_t* out,
                           int32_t* counts, hipStream_t s);
-hipError_t launch_qk_logits(int D, const LogitsArgs& a, int chunks, hipStream_t s);
-hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_sample(int D, const SampleArgs& a, hipStream_t s);
+hipError_t launch_refresh_final(int D, const FinalArgs& a, hipStream_t s);
 hipError_t launch_full(int D, int maxs, const FullArgs& a, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 

@@ -7,73 +7,33 @@
 // that the decode kernel computes for the same inputs (one shared QK tile
 // routine), so s >= tau keeps exactly N entries when there are no ties.
 //
-// Pipeline (4 launches, all on the caller's stream):
-//   1. qk_logits_kernel   stream K once per (b, key head), write fp32 logits
-//                         [B*h_q][ld] to the workspace; chunk-0 workgroups
-//                         also clear the per-row select state.
-//   2. radix_hist_kernel  per (row, segment): LDS histogram of the top 12 bits
-//                         of the order-preserving key, merged into a global
-//                         per-row histogram with integer atomics; the last
-//                         segment of a row to finish scans it and records the
-//                         bucket holding rank N and the rank inside it.
-//   3. radix_compact_kernel per (row, segment): append the keys of that bucket
-//                         to a per-row candidate list (wave-aggregated atomics).
-//   4. radix_final_kernel per row: two 10-bit LDS histogram passes over the
-//                         candidates fix the remaining 20 key bits.
-// Integer counting only, so the result does not depend on scheduling.
+// Pipeline (all on the caller's stream; one pass over the K cache):
+//   1. sample_logits_kernel  logits of a strided sample of at most kSampleMax
+//                            rows per (b, query head), same MFMA QK tile.
+//   2. pivot_kernel          per row: the k-th largest sample logit (LDS radix
+//                            select), with k chosen so that the pivot p lies
+//                            below tau with overwhelming probability.
+//   3. select_stream_kernel  (decode.hip) with p as the threshold: every logit
+//                            >= p goes to the per-(row, chunk, wave) lists.
+//   4. refresh_final_kernel  per row: if the lists hold at least N entries,
+//                            tau is the N-th largest of them (then every entry
+//                            >= tau is in the lists; LDS radix select).
+//                            Otherwise -- or if they are too many to stage --
+//                            the workgroup recomputes the row's logits with the
+//                            same QK tile and radix-selects over all of them.
+// Steps 1-2 only decide how much work step 4 has; they never change tau.
+// Integer counting on order-preserving keys throughout: the result does not
+// depend on scheduling.
 #include "kernels.hpp"
 
 namespace saga {
 
 namespace {
 
-template <int D, int U>
-__global__ __launch_bounds__(kBlock) void qk_logits_kernel(LogitsArgs a)
-{
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
-    const int col = lane & 15, grp = lane >> 4;
-    const int chunk = blockIdx.x;
-    const int b = blockIdx.y / a.hk, g = blockIdx.y - b * a.hk;
-    const int Gk = a.Gk;
-    const int64_t r0 = (int64_t)chunk * a.rows_per_chunk;
-    const int64_t r1 = min(r0 + a.rows_per_chunk, a.ctx);
-    const int qh0 = b * a.hq + g * Gk;
-
-    if (chunk == 0) {
-        for (int t = threadIdx.x; t < Gk * kHistBins; t += kBlock)
-            a.ghist[(int64_t)qh0 * kHistBins + t] = 0u;
-        if (threadIdx.x < Gk) {
-            a.done[qh0 + threadIdx.x] = 0u;
-            a.cand_count[qh0 + threadIdx.x] = 0u;
-        }
-    }
-
-    const QFrag<D> qf = load_qfrag<D>(col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr);
-    const uint16_t* khead = a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
-    for (int64_t t0 = r0 + wave * 16 * U; t0 < r1; t0 += kWavesPerBlock * 16 * U) {
-        KTile<D, U> kt;
-        load_ktile<D, U>(kt, khead, t0, r1);
-        float s[U][4];
-        qk_tile<D, U>(qf, kt, a.scale, s);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t row = t0 + 16 * u + col;
-            if (row >= r1) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int slot = 4 * grp + i;
-                if (slot >= Gk) continue;
-                a.logits[(int64_t)(qh0 + slot) * a.ld + row] = s[u][i];
-                if (a.debug) a.debug[(int64_t)(qh0 + slot) * a.ctx + row] = s[u][i];
-            }
-        }
-    }
-}
-
 // Block-wide search of a histogram held in LDS for the bucket containing
 // rank `rank` (1-based, counted from the largest key).  Thread t owns the
-// BINS/256 consecutive buckets starting from the top.  Returns the bucket in
-// *bin and the rank inside it in *rank_in; all threads see the result.
+// BINS/256 consecutive buckets starting from the top.  All threads receive
+// the bucket, the rank inside it and its size.
 template <int BINS>
 __device__ void find_rank_bucket(const uint32_t* hist, uint32_t rank, uint32_t* scan,
                                  uint32_t* result, uint32_t* bin, uint32_t* rank_in,
@@ -115,122 +75,221 @@ __device__ void find_rank_bucket(const uint32_t* hist, uint32_t rank, uint32_t* 
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kBlock) void radix_hist_kernel(SelectArgs a)
+// Radix digits of the 32-bit key, most significant first: 11, 11, 10 bits.
+__device__ __forceinline__ int digit_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
+__device__ __forceinline__ uint32_t digit_mask(int pass) { return pass == 2 ? 1023u : 2047u; }
+// Bits above the digit of `pass` (they must match the prefix found so far).
+__device__ __forceinline__ uint32_t prefix_mask(int pass)
 {
-    __shared__ uint32_t hist[kHistBins];
-    __shared__ uint32_t scan[kBlock];
-    __shared__ uint32_t result[3];
-    __shared__ int last;
-    const int row = blockIdx.y, seg = blockIdx.x, t = threadIdx.x;
-    for (int k = t; k < kHistBins; k += kBlock) hist[k] = 0u;
-    __syncthreads();
-    const float* s = a.logits + (int64_t)row * a.ld;
-    const int64_t j0 = (int64_t)seg * kSelectSeg;
-    const int64_t j1 = min(j0 + (int64_t)kSelectSeg, a.ctx);
-    for (int64_t j = j0 + t; j < j1; j += kBlock) atomicAdd(&hist[float_key(s[j]) >> 20], 1u);
-    __syncthreads();
-    uint32_t* gh = a.ghist + (int64_t)row * kHistBins;
-    for (int k = t; k < kHistBins; k += kBlock)
-        if (hist[k]) atomicAdd(&gh[k], hist[k]);
-    __threadfence();
-    __syncthreads();
-    if (t == 0) last = atomicAdd(&a.done[row], 1u) == (uint32_t)(a.segs - 1);
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    for (int k = t; k < kHistBins; k += kBlock)
-        hist[k] = __hip_atomic_load(&gh[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    uint32_t bin, rank_in, cnt;
-    find_rank_bucket<kHistBins>(hist, a.top_n, scan, result, &bin, &rank_in, &cnt);
-    if (t == 0) {
-        a.state[row * 4 + 0] = bin;
-        a.state[row * 4 + 1] = rank_in;
-        a.state[row * 4 + 2] = cnt;
-    }
+    return pass == 0 ? 0u : (pass == 1 ? 0xffe00000u : 0xfffffc00u);
 }
 
-__global__ __launch_bounds__(kBlock) void radix_compact_kernel(SelectArgs a)
+struct SelectLds {
+    uint32_t hist[kHistBins];
+    uint32_t scan[kBlock];
+    uint32_t result[3];
+};
+
+// The rank-th largest of n keys held in LDS (1 <= rank <= n).
+__device__ uint32_t lds_radix_select(const uint32_t* keys, uint32_t n, uint32_t rank, SelectLds& w)
 {
-    const int row = blockIdx.y, seg = blockIdx.x, t = threadIdx.x;
-    const uint32_t bucket = a.state[row * 4 + 0];
-    const float* s = a.logits + (int64_t)row * a.ld;
-    uint32_t* cand = a.cand + (int64_t)row * a.ld;
-    const int64_t j0 = (int64_t)seg * kSelectSeg;
-    const int64_t j1 = min(j0 + (int64_t)kSelectSeg, a.ctx);
-    for (int64_t jb = j0; jb < j1; jb += kBlock) {
-        const int64_t j = jb + t;
-        uint32_t key = 0u;
-        bool hit = false;
-        if (j < j1) {
-            key = float_key(s[j]);
-            hit = (key >> 20) == bucket;
+    uint32_t prefix = 0u;
+    for (int pass = 0; pass < 3; ++pass) {
+        const int sh = digit_shift(pass);
+        const uint32_t dm = digit_mask(pass), pm = prefix_mask(pass);
+        for (int k = threadIdx.x; k < kHistBins; k += kBlock) w.hist[k] = 0u;
+        __syncthreads();
+        for (uint32_t k = threadIdx.x; k < n; k += kBlock) {
+            const uint32_t key = keys[k];
+            if ((key & pm) == prefix) atomicAdd(&w.hist[(key >> sh) & dm], 1u);
         }
-        const uint64_t mask = __ballot(hit);
-        if (mask == 0) continue;
-        const int leader = __ffsll((unsigned long long)mask) - 1;
-        uint32_t base = 0u;
-        if (lane_id() == leader) base = atomicAdd(&a.cand_count[row], (uint32_t)__popcll(mask));
-        base = __shfl(base, leader);
-        if (hit) cand[base + lanes_below(mask)] = key;
+        __syncthreads();
+        uint32_t bin, rin, cnt;
+        find_rank_bucket<kHistBins>(w.hist, rank, w.scan, w.result, &bin, &rin, &cnt);
+        prefix |= bin << sh;
+        rank = rin;
+    }
+    return prefix;
+}
+
+// Logits of sampled rows: row k*stride for sample index k < m, for every query
+// head of key head g.  Output sample[b*hq + i][k] (row stride kSampleMax).
+template <int D, int U>
+__global__ __launch_bounds__(kBlock) void sample_logits_kernel(SampleArgs a)
+{
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int b = blockIdx.y / a.hk, g = blockIdx.y - b * a.hk;
+    const int Gk = a.Gk;
+    const int qh0 = b * a.hq + g * Gk;
+    const int k0 = (blockIdx.x * kWavesPerBlock + wave) * 16 * U;   // first sample index
+    if (k0 >= a.m) return;                                          // whole wave idle
+    const QFrag<D> qf = load_qfrag<D>(col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr);
+    const uint16_t* khead = a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
+    KTile<D, U> kt;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        int k = k0 + 16 * u + col;
+        k = k < a.m ? k : a.m - 1;
+        const uint16_t* p = khead + (int64_t)k * a.stride * D + 8 * grp;
+#pragma unroll
+        for (int mm = 0; mm < D / 32; ++mm) kt.v[u][mm] = ld16(p + 32 * mm);
+    }
+    float s[U][4];
+    qk_tile<D, U>(qf, kt, a.scale, s);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int k = k0 + 16 * u + col;
+        if (k >= a.m) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int slot = 4 * grp + i;
+            if (slot < Gk) a.sample[(int64_t)(qh0 + slot) * kSampleMax + k] = s[u][i];
+        }
     }
 }
 
-__global__ __launch_bounds__(kBlock) void radix_final_kernel(SelectArgs a)
+// pivot[row] = the k-th largest of the row's m sample logits.
+__global__ __launch_bounds__(kBlock) void pivot_kernel(SampleArgs a)
 {
-    constexpr int BINS = 1024;
-    __shared__ uint32_t hist[BINS];
-    __shared__ uint32_t scan[kBlock];
-    __shared__ uint32_t result[3];
-    const int row = blockIdx.x, t = threadIdx.x;
-    const uint32_t bucket = a.state[row * 4 + 0];
-    const uint32_t rank = a.state[row * 4 + 1];
-    const uint32_t n = a.cand_count[row];
-    const uint32_t* cand = a.cand + (int64_t)row * a.ld;
+    __shared__ uint32_t keys[kSampleMax];
+    __shared__ SelectLds w;
+    const int row = blockIdx.x;
+    const float* s = a.sample + (int64_t)row * kSampleMax;
+    for (int k = threadIdx.x; k < a.m; k += kBlock) keys[k] = float_key(s[k]);
+    __syncthreads();
+    const uint32_t key = lds_radix_select(keys, (uint32_t)a.m, (uint32_t)a.rank, w);
+    if (threadIdx.x == 0) a.pivot[row] = key_float(key);
+}
 
-    // Pass A: key bits 19..10.
-    for (int k = t; k < BINS; k += kBlock) hist[k] = 0u;
-    __syncthreads();
-    for (uint32_t k = t; k < n; k += kBlock) atomicAdd(&hist[(cand[k] >> 10) & 1023u], 1u);
-    __syncthreads();
-    uint32_t binA, rankA, cntA;
-    find_rank_bucket<BINS>(hist, rank, scan, result, &binA, &rankA, &cntA);
-
-    // Pass B: key bits 9..0 among keys that share bits 19..10.
-    for (int k = t; k < BINS; k += kBlock) hist[k] = 0u;
-    __syncthreads();
-    for (uint32_t k = t; k < n; k += kBlock) {
-        const uint32_t key = cand[k];
-        if (((key >> 10) & 1023u) == binA) atomicAdd(&hist[key & 1023u], 1u);
+// Exact N-th largest of one row by recomputing its logits (three radix passes
+// over the row's key head, each with the shared QK tile).  Used when the
+// candidate lists cannot answer.
+template <int D, int U>
+__device__ uint32_t select_by_recompute(const FinalArgs& a, int row, SelectLds& w)
+{
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int b = row / a.hq, i = row - b * a.hq;
+    const int g = i / a.Gk, slot = i - g * a.Gk;
+    const int qh0 = b * a.hq + g * a.Gk;
+    const QFrag<D> qf = load_qfrag<D>(col < a.Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr);
+    const uint16_t* khead = a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
+    uint32_t prefix = 0u, rank = a.top_n;
+    for (int pass = 0; pass < 3; ++pass) {
+        const int sh = digit_shift(pass);
+        const uint32_t dm = digit_mask(pass), pm = prefix_mask(pass);
+        for (int k = threadIdx.x; k < kHistBins; k += kBlock) w.hist[k] = 0u;
+        __syncthreads();
+        for (int64_t t0 = wave * 16 * U; t0 < a.ctx; t0 += kWavesPerBlock * 16 * U) {
+            KTile<D, U> kt;
+            load_ktile<D, U>(kt, khead, t0, a.ctx);
+            float s[U][4];
+            qk_tile<D, U>(qf, kt, a.scale, s);
+            if (grp == (slot >> 2)) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (t0 + 16 * u + col >= a.ctx) continue;
+                    float v = s[u][0];
+#pragma unroll
+                    for (int ii = 1; ii < 4; ++ii)
+                        if ((slot & 3) == ii) v = s[u][ii];
+                    const uint32_t key = float_key(v);
+                    if ((key & pm) == prefix) atomicAdd(&w.hist[(key >> sh) & dm], 1u);
+                }
+            }
+        }
+        __syncthreads();
+        uint32_t bin, rin, cnt;
+        find_rank_bucket<kHistBins>(w.hist, rank, w.scan, w.result, &bin, &rin, &cnt);
+        prefix |= bin << sh;
+        rank = rin;
     }
+    return prefix;
+}
+
+template <int D, int U>
+__global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
+{
+    __shared__ int32_t pre[kMaxListsPerRow + 1];
+    __shared__ uint32_t keys[kFinalStage];
+    __shared__ SelectLds w;
+    const int row = blockIdx.x, t = threadIdx.x;
+    const int nl = a.chunks * kWavesPerBlock;
+    const int64_t lbase = (int64_t)row * nl;
+    const int64_t capw = a.rows_per_chunk / kWavesPerBlock;
+
+    // Prefix of list lengths: thread t sums a contiguous run of lists.
+    constexpr int PER = kMaxListsPerRow / kBlock;
+    int32_t c[PER], sum = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int l = t * PER + k;
+        c[k] = l < nl ? a.list_count[lbase + l] : 0;
+        sum += c[k];
+    }
+    uint32_t* scan = w.scan;
+    scan[t] = (uint32_t)sum;
     __syncthreads();
-    uint32_t binB, rankB, cntB;
-    find_rank_bucket<BINS>(hist, rankA, scan, result, &binB, &rankB, &cntB);
-    if (t == 0) a.tau[row] = key_float((bucket << 20) | (binA << 10) | binB);
+    for (int off = 1; off < kBlock; off <<= 1) {
+        const uint32_t v = t >= off ? scan[t - off] : 0u;
+        __syncthreads();
+        scan[t] += v;
+        __syncthreads();
+    }
+    int32_t run = (int32_t)scan[t] - sum;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        pre[t * PER + k] = run;
+        run += c[k];
+    }
+    if (t == kBlock - 1) pre[kMaxListsPerRow] = run;
+    __syncthreads();
+    const uint32_t total = (uint32_t)pre[kMaxListsPerRow];
+
+    uint32_t key;
+    if (total >= a.top_n && total <= (uint32_t)kFinalStage) {
+        for (uint32_t E = t; E < total; E += kBlock) {
+            int lo = 0, hi = nl - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if ((uint32_t)pre[mid] <= E) lo = mid;
+                else hi = mid - 1;
+            }
+            const uint2 ent = a.entries[(lbase + lo) * capw + (E - pre[lo])];
+            keys[E] = float_key(__uint_as_float(ent.y));
+        }
+        __syncthreads();
+        key = lds_radix_select(keys, total, a.top_n, w);
+    } else {
+        key = select_by_recompute<D, U>(a, row, w);
+    }
+    if (t == 0) a.tau[row] = key_float(key);
 }
 
 }  // namespace
 
-hipError_t launch_qk_logits(int D, const LogitsArgs& a, int chunks, hipStream_t s)
+hipError_t launch_sample(int D, const SampleArgs& a, hipStream_t s)
 {
-    const dim3 grid(chunks, a.B * a.hk);
+    constexpr int U = 4;
+    const int per_block = kWavesPerBlock * 16 * U;
+    const dim3 grid((a.m + per_block - 1) / per_block, a.B * a.hk);
     if (D == 64)
-        hipLaunchKernelGGL((qk_logits_kernel<64, decode_unroll(64)>), grid, dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((sample_logits_kernel<64, U>), grid, dim3(kBlock), 0, s, a);
     else
-        hipLaunchKernelGGL((qk_logits_kernel<128, decode_unroll(128)>), grid, dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((sample_logits_kernel<128, U>), grid, dim3(kBlock), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pivot_kernel, dim3(a.B * a.hq), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_select(const SelectArgs& a, hipStream_t s)
+hipError_t launch_refresh_final(int D, const FinalArgs& a, hipStream_t s)
 {
-    const dim3 grid(a.segs, a.rows);
-    hipLaunchKernelGGL(radix_hist_kernel, grid, dim3(kBlock), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(radix_compact_kernel, grid, dim3(kBlock), 0, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(radix_final_kernel, dim3(a.rows), dim3(kBlock), 0, s, a);
+    if (D == 64)
+        hipLaunchKernelGGL((refresh_final_kernel<64, decode_unroll(64)>), dim3(a.B * a.hq), dim3(kBlock), 0, s, a);
+    else
+        hipLaunchKernelGGL((refresh_final_kernel<128, decode_unroll(128)>), dim3(a.B * a.hq), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 

@@ -225,3 +225,45 @@ def test_full_attention_matches_oracle(name):
         ref = oracle.full(qb[0], Kb, Vb, ctx)
         err = np.abs(out.float().cpu().numpy() - ref).max()
         assert err <= OUT_TOL, f"{name} ctx={ctx}: {err:.3e}"
+
+
+def _check_refresh_exact(q, K, V, ctx, N):
+    """Thresholds bit-exact vs a host sort of the GPU logits, and outputs vs the oracle."""
+    gpu = run_atopn(q, K, V, [ctx], N, 1)
+    lg, tau, cnt = gpu["logits"][0], gpu["tau"][0], gpu["counts"][0]
+    for b in range(lg.shape[0]):
+        for i in range(lg.shape[1]):
+            assert tau[b, i] == nth_largest_f32(lg[b, i], N), (b, i)
+            assert cnt[b, i] == (lg[b, i] >= tau[b, i]).sum()
+    ref, _ = oracle.masked(to_np_bits(q)[0], to_np_bits(K), to_np_bits(V), ctx, gpu["bitmap"][0])
+    assert np.abs(gpu["out"][0] - ref).max() <= OUT_TOL
+    return gpu
+
+
+def test_refresh_exact_when_the_sample_misleads():
+    """Every sampled row (a multiple of the sample stride) outscores the rest,
+    so the sample pivot leaves fewer than N candidates: the exact recompute
+    path must still return the N-th largest logit."""
+    ctx, N = 40000, 5000
+    stride = -(-ctx // 4096)
+    q, K, V = make_inputs(1, 4, 1, 2, 64, ctx, 1, seed=46, heavy=False)
+    K.mul_(0.05)
+    K[:, :, ::stride, :] = 1.0
+    q.fill_(0.1)
+    gpu = _check_refresh_exact(q, K, V, ctx, N)
+    assert (gpu["counts"][0] >= N).all()
+
+
+def test_refresh_exact_with_ties_beyond_staging():
+    """All logits tie (K = 0) over more rows than the final select stages."""
+    ctx = 20000
+    q, K, V = make_inputs(1, 4, 1, 2, 128, ctx, 1, seed=47)
+    K.zero_()
+    gpu = _check_refresh_exact(q, K, V, ctx, 700)
+    assert (gpu["tau"][0] == 0).all() and (gpu["counts"][0] == ctx).all()
+
+
+def test_refresh_exact_at_long_context():
+    """128K-row context (sampled pivot path), Qwen-like group of 12 heads."""
+    q, K, V = make_inputs(1, 12, 1, 2, 128, 131072 + 2, 1, seed=48)
+    _check_refresh_exact(q, K, V, 131072, 1024)
