@@ -33,6 +33,38 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+KERNEL_SOURCES = ("decode.hip", "device.hpp", "kernels.hpp", "tuning.hpp")
+
+
+def kernel_sources_hash() -> str:
+    """sha256 over the decode kernels' sources: a traffic figure measured with
+    rocprofv3 counters applies only while this hash is unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_decode_attention_atop_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(path, workload):
+    """HBM bytes per decode call from a committed rocprofv3 summary (a JSON block
+    in a markdown file), or None when absent, for another workload, or stale."""
+    if not path or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    start = text.find("```json")
+    if start < 0:
+        return None
+    end = text.find("```", start + 7)
+    try:
+        tr = json.loads(text[start + 7:end])
+    except ValueError:
+        return None
+    if tr.get("workload") != workload or tr.get("kernel_sources") != kernel_sources_hash():
+        return None
+    return tr.get("bytes_per_call")
 DEFAULT_WORKLOAD = "llama_like_128k_b16"
 GQA_TWIN = {"llama_like_128k_b16": 8, "qwen_like_128k_b1": 2, "qwen_like_128k_b16": 2,
             "llama_like_8k": 8, "tiny": 2}
@@ -51,8 +83,40 @@ def parse():
     p.add_argument("--no-gqa", action="store_true", help="skip the full-attention GQA baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--traffic", default=None,
-                   help="JSON with rocprofv3-measured HBM bytes of the decode kernel")
+                   help="markdown summary holding rocprofv3-measured HBM bytes per decode call "
+                        "(default: profiles/traffic_<workload>.md)")
+    p.add_argument("--calibrate", action="store_true",
+                   help="time a plain 4 GiB device copy and read (HBM ceiling; the copy is "
+                        "the known-size kernel that scales rocprofv3 byte counters)")
+    p.add_argument("--eager-only", action="store_true",
+                   help="one eager pass over the decode steps, no timing (for counter runs)")
     return p.parse_args()
+
+
+def calibrate(torch):
+    """Measured HBM ceilings: torch's device copy (read + write) and sum (read)."""
+    n = 4 << 30
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    acc = torch.empty(1, dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps / 1e3
+
+    t_copy = timed(lambda: dst.copy_(src))
+    t_read = timed(lambda: torch.sum(src, dim=0, keepdim=True, dtype=torch.float32, out=acc))
+    print(json.dumps({"calibration": "device copy and read of 4 GiB",
+                      "copy_bytes_read": n, "copy_bytes_written": n,
+                      "copy_gbs": round(2 * n / t_copy / 1e9, 1),
+                      "read_gbs": round(n / t_read / 1e9, 1)}), flush=True)
 
 
 def layer_inputs(torch, wl, w, layer):
@@ -122,6 +186,9 @@ def run_saga(torch, saga, wl, w, args):
     for t in range(T):
         step(t)
     torch.cuda.synchronize()
+    if args.eager_only:
+        log("eager pass done")
+        return None
     launches = []
     for t in range(T):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -233,8 +300,13 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
     saga.library()          # fail loudly now if the HIP library is missing
+    if args.calibrate:
+        calibrate(torch)
+        return
     w = wl.WORKLOADS[args.workload]
     res = run_saga(torch, saga, wl, w, args)
+    if res is None:
+        return
     T = w.steps
     sec = res["sec"]
     steps_per_s = args.steps / sec
@@ -246,12 +318,8 @@ def main():
     achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
     avg_sel = sum(x[4] for x in launches) / len(launches) / (w.batch * w.h_q)
     step_bytes = sum(x[3] for x in launches) / T
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            tr = json.load(f)
-        if tr.get("workload") == w.name:
-            traffic = tr.get("bytes_per_launch")
+    traffic = measured_traffic(args.traffic or os.path.join(ROOT, "profiles",
+                                                            f"traffic_{w.name}.md"), w.name)
 
     extra = {}
     cpu = None
@@ -291,7 +359,8 @@ def main():
         "tokens_per_s": round(steps_per_s * w.batch, 2),
         "hbm_gbs_step": round(step_bytes / (sec / args.steps) / 1e9, 1),
         "hbm_frac_step": round(step_bytes / (sec / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "sparse_decode_kernel (with its combine)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "saga_decode_step (select_stream + gather + combine)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_ms": round(avg_ms, 5),

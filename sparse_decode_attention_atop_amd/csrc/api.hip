@@ -74,7 +74,7 @@ Layout make_layout(const saga_dims* d)
     const int64_t want = kTargetBlocks / ((int64_t)d->batch * d->h_k);
     const int64_t by_len = (d->cache_len + 127) / 128;   // smallest block tile is 128 rows
     int64_t mc = want < by_len ? want : by_len;
-    if (mc > kMaxListsPerRow / kWavesPerBlock) mc = kMaxListsPerRow / kWavesPerBlock;
+    if (mc > kMaxListsPerRow / kWavesPerBlock) mc = kMaxListsPerRow / kWavesPerBlock;   // 512
     L.max_chunks = (int)(mc < 1 ? 1 : mc);
     // chunks * rows_per_chunk <= ctx + rows_per_chunk(ctx), and rows_per_chunk
     // never exceeds max(block rows, its value at ctx = cache_len).
@@ -196,9 +196,17 @@ SAGA_EXPORT int atopn_refresh_thresholds(const saga_dims* dims, int32_t top_n, c
     sa.hk = dims->h_k;
     sa.Gk = dims->h_q / dims->h_k;
     sa.cache_len = dims->cache_len;
-    sa.stride = (ctx + kSampleMax - 1) / kSampleMax;
-    sa.m = (int)((ctx + sa.stride - 1) / sa.stride);
-    if (sa.stride == 1) {
+    // Sample: 16-row blocks, one every `stride` rows (stride a multiple of 16),
+    // at most kSampleMax rows; the whole context when it is that short.
+    const int64_t blocks_max = kSampleMax / 16;
+    if (ctx <= kSampleMax) {
+        sa.stride = 16;
+        sa.m = (int)ctx;
+    } else {
+        sa.stride = (ctx / 16 + blocks_max - 1) / blocks_max * 16;   // every block fully inside ctx
+        sa.m = (int)(ctx / sa.stride) * 16;
+    }
+    if (sa.m == ctx) {
         sa.rank = top_n;
     } else {
         const double mu = (double)top_n * sa.m / (double)ctx;

@@ -35,10 +35,12 @@ namespace {
 template <int D, int U>
 __global__ __launch_bounds__(kBlock) void select_stream_kernel(SelectStreamArgs a)
 {
-    // Hits are staged per (wave, head slot) in LDS and written to the global
-    // lists in runs of up to kStageCap entries, so the lists are written with
-    // whole cache lines instead of scattered 8-byte stores.
-    __shared__ uint2 stage[kWavesPerBlock][16][kStageCap];
+    // Hits are staged per (wave, head slot) in LDS (stage_cap(U) entries each)
+    // and written to the global lists in whole runs, never as scattered
+    // 8-byte stores.  A slot gains at most 16*U entries per tile, so one flush
+    // check per tile suffices.
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int CAPS = stage_cap(U);
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int chunk = blockIdx.x;
@@ -48,83 +50,109 @@ __global__ __launch_bounds__(kBlock) void select_stream_kernel(SelectStreamArgs 
     const int64_t r1 = min(r0 + a.rows_per_chunk, a.ctx);
     const int64_t capw = a.rows_per_chunk / kWavesPerBlock;
     const int qh0 = b * a.hq + g * Gk;
-    uint2 (*st)[kStageCap] = stage[wave];
+    uint2* st = reinterpret_cast<uint2*>(smem) + (size_t)wave * Gk * CAPS;
 
     const QFrag<D> qf = load_qfrag<D>(col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr);
+    // Per lane: head slot 4*grp + i.  staged = entries waiting in LDS,
+    // written = entries already in the global list.
     float tau[4], mx[4];
-    int32_t hits[4], flushed[4];
+    int32_t staged[4], written[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int slot = 4 * grp + i;
         tau[i] = slot < Gk ? a.tau[qh0 + slot] : INFINITY;
         mx[i] = -INFINITY;
-        hits[i] = 0;
-        flushed[i] = 0;
+        staged[i] = 0;
+        written[i] = 0;
     }
     const uint32_t below = (1u << col) - 1u;
+    const int64_t list0 = (int64_t)qh0 * a.chunks * kWavesPerBlock + chunk * kWavesPerBlock + wave;
+    const int64_t list_stride = (int64_t)a.chunks * kWavesPerBlock;   // between head slots
 
-    // Write the staged entries of slots 4*gf + i (gf = 0..3) to their lists.
-    auto flush = [&](int i) {
+    auto pick = [](const int32_t (&v)[4], int i) {
+        return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
+    };
+    auto flush_all = [&]() {
         wave_sync();
-#pragma unroll
-        for (int gf = 0; gf < 4; ++gf) {
-            const int slot = 4 * gf + i;
-            if (slot >= Gk) break;
-            const int n = __shfl(hits[i] - flushed[i], 16 * gf);
-            const int done = __shfl(flushed[i], 16 * gf);
-            if (n > 0 && lane < n) {
-                const int64_t list = ((int64_t)(qh0 + slot) * a.chunks + chunk) * kWavesPerBlock + wave;
-                a.entries[list * capw + done + lane] = st[slot][lane];
-            }
+#pragma unroll 1
+        for (int h = 0; h < Gk; ++h) {
+            const int n = __shfl(pick(staged, h & 3), 16 * (h >> 2));
+            const int off = __shfl(pick(written, h & 3), 16 * (h >> 2));
+            uint2* dst = a.entries + (list0 + h * list_stride) * capw + off;
+            for (int k = lane; k < n; k += kWave) dst[k] = st[h * CAPS + k];
         }
-        flushed[i] = hits[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            written[i] += staged[i];
+            staged[i] = 0;
+        }
         wave_sync();
     };
 
-    const uint16_t* khead = a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
-    for (int64_t t0 = r0 + wave * 16 * U; t0 < r1; t0 += kWavesPerBlock * 16 * U) {
-        KTile<D, U> kt;
-        load_ktile<D, U>(kt, khead, t0, r1);
-        float s[U][4];
-        qk_tile<D, U>(qf, kt, a.scale, s);
+    auto process = [&](const KTile<D, U>& kt, int64_t t0) {
+        bool full = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) full |= staged[i] > CAPS - 16 * U;
+        if (__ballot(full)) flush_all();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            float s[4];
+            qk_group<D>(qf, kt.v[u], a.scale, s);
             const int64_t row = t0 + 16 * u + col;
             const bool valid = row < r1;
             if (a.logits_out && valid) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (4 * grp + i < Gk) a.logits_out[(int64_t)(qh0 + 4 * grp + i) * a.ctx + row] = s[u][i];
+                    if (4 * grp + i < Gk) a.logits_out[(int64_t)(qh0 + 4 * grp + i) * a.ctx + row] = s[i];
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool pred = valid && s[u][i] >= tau[i];
+                const bool pred = valid && s[i] >= tau[i];
                 const uint64_t mask = __ballot(pred);
                 if (mask == 0) continue;                         // wave-uniform
                 const uint32_t mine = (uint32_t)(mask >> (16 * grp)) & 0xffffu;
                 if (pred) {
-                    mx[i] = fmaxf(mx[i], s[u][i]);
-                    const int pos = hits[i] - flushed[i] + __popc(mine & below);
-                    st[4 * grp + i][pos] = make_uint2((uint32_t)(row - r0), __float_as_uint(s[u][i]));
+                    mx[i] = fmaxf(mx[i], s[i]);
+                    st[(4 * grp + i) * CAPS + staged[i] + __popc(mine & below)] =
+                        make_uint2((uint32_t)(row - r0), __float_as_uint(s[i]));
                 }
-                hits[i] += __popc(mine);
+                staged[i] += __popc(mine);
                 if (a.bitmap && col == 0 && mine) {
                     const int64_t row0 = t0 + 16 * u;             // multiple of 16
                     atomicOr(a.bitmap + (int64_t)(qh0 + 4 * grp + i) * a.bitmap_words + row0 / 32,
                              mine << (row0 & 31));
                 }
-                // A slot gains at most 16 entries per ballot: flush before overflow.
-                if (__ballot(hits[i] - flushed[i] > kStageCap - 16)) flush(i);
             }
         }
+    };
+
+    // Software-pipelined stream: the next tile's loads are issued before the
+    // current tile is processed, so every wave keeps a tile in flight.
+    const uint16_t* khead = a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
+    constexpr int64_t kStep = kWavesPerBlock * 16 * U;
+    int64_t t0 = r0 + wave * 16 * U;
+    if (t0 < r1) {
+        KTile<D, U> ka, kb;
+        load_ktile<D, U>(ka, khead, t0, r1);
+        while (true) {
+            const int64_t t1 = t0 + kStep;
+            if (t1 < r1) load_ktile<D, U>(kb, khead, t1, r1);
+            process(ka, t0);
+            if (t1 >= r1) break;
+            const int64_t t2 = t1 + kStep;
+            if (t2 < r1) load_ktile<D, U>(ka, khead, t2, r1);
+            process(kb, t1);
+            if (t2 >= r1) break;
+            t0 = t2;
+        }
     }
+    flush_all();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if (__ballot(hits[i] > flushed[i])) flush(i);
         const float m = group16_max(mx[i]);
         if (col == 0 && 4 * grp + i < Gk) {
-            const int64_t list = ((int64_t)(qh0 + 4 * grp + i) * a.chunks + chunk) * kWavesPerBlock + wave;
-            a.list_count[list] = hits[i];
+            const int64_t list = list0 + (4 * grp + i) * list_stride;
+            a.list_count[list] = written[i];
             a.list_max[list] = m;
         }
     }
@@ -147,7 +175,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
     constexpr int LPR = D / 8;             // lanes per value row (16 bytes each)
     constexpr int SLOTS = kBlock / LPR;    // rows per workgroup load instruction
     constexpr int CAPL = 2048;             // entries staged per round
-    constexpr int NB = 8;                  // rows in flight per lane
+    constexpr int NB = 16;                 // rows in flight per lane
     static_assert(SLOTS * D <= CAPL, "reduction scratch reuses the staging buffer");
     __shared__ int32_t pre[kBlock + 1];
     __shared__ float red[kWavesPerBlock];
@@ -258,34 +286,84 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
     }
 }
 
-// Merge the per-segment partials of one (b, query head) in order:
+// Merge the per-segment partials of one (b, query head) in a fixed order:
 //   M = max m_c, l = sum e^(m_c - M) l_c, o = sum e^(m_c - M) o_c, out = o / l
-// (zero when nothing was selected), rounded to bf16.
+// (zero when nothing was selected), rounded to bf16.  256 threads: PL part
+// lanes x D elements; part lane p takes partials p, p + PL, ...; the part
+// lanes are then summed in order.
 template <int D>
-__global__ __launch_bounds__(D) void combine_kernel(Partials p, int parts, uint16_t* out,
-                                                    int32_t* counts)
+__global__ __launch_bounds__(kBlock) void combine_kernel(Partials p, int parts, uint16_t* out,
+                                                         int32_t* counts)
 {
+    constexpr int PL = kBlock / D;
+    __shared__ float red[kBlock];
+    __shared__ float lsh[PL];
+    __shared__ int32_t csh[kBlock];
     const int64_t bh = blockIdx.x;
-    const int e = threadIdx.x;
+    const int t = threadIdx.x, pl = t / D, e = t - pl * D;
     const float* pm = p.m + bh * parts;
-    const float* pl = p.l + bh * parts;
+    const float* pl_ = p.l + bh * parts;
     const int32_t* pc = p.c + bh * parts;
     const float* po = p.o + bh * parts * D;
+
     float M = -INFINITY;
-    for (int c = 0; c < parts; ++c) M = fmaxf(M, pm[c]);
-    float acc = 0.f, l = 0.f;
     int32_t n = 0;
-    for (int c = 0; c < parts; ++c) {
-        const float m = pm[c];
-        if (m > -INFINITY) {
-            const float alpha = __expf(m - M);
-            acc += alpha * po[(int64_t)c * D + e];
-            l += alpha * pl[c];
-        }
+    for (int c = t; c < parts; c += kBlock) {
+        M = fmaxf(M, pm[c]);
         n += pc[c];
     }
-    out[bh * D + e] = f32_to_bf16_rne(l > 0.f ? acc / l : 0.f);
-    if (counts && e == 0) counts[bh] = n;
+    red[t] = M;
+    csh[t] = n;
+    __syncthreads();
+    for (int off = kBlock / 2; off > 0; off >>= 1) {
+        if (t < off) {
+            red[t] = fmaxf(red[t], red[t + off]);
+            csh[t] += csh[t + off];
+        }
+        __syncthreads();
+    }
+    M = red[0];
+    n = csh[0];
+    __syncthreads();
+    if (M == -INFINITY) {                                  // nothing selected anywhere
+        if (t < D) out[bh * D + t] = 0;
+        if (counts && t == 0) counts[bh] = n;
+        return;
+    }
+    float acc = 0.f, l = 0.f;
+    int c = pl;
+    for (; c + 3 * PL < parts; c += 4 * PL) {
+        float w[4], ov[4], lv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            w[k] = pm[c + k * PL];
+            ov[k] = po[(int64_t)(c + k * PL) * D + e];
+            lv[k] = pl_[c + k * PL];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float a = __expf(w[k] - M);              // -inf partials weigh 0
+            acc += a * ov[k];
+            l += a * lv[k];
+        }
+    }
+    for (; c < parts; c += PL) {
+        const float a = __expf(pm[c] - M);
+        acc += a * po[(int64_t)c * D + e];
+        l += a * pl_[c];
+    }
+    red[t] = acc;
+    if (e == 0) lsh[pl] = l;
+    __syncthreads();
+    if (t < D) {
+        float o = 0.f, L = 0.f;
+        for (int k = 0; k < PL; ++k) {
+            o += red[k * D + t];
+            L += lsh[k];
+        }
+        out[bh * D + t] = f32_to_bf16_rne(L > 0.f ? o / L : 0.f);
+        if (counts && t == 0) counts[bh] = n;
+    }
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
@@ -300,10 +378,11 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
 hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t s)
 {
     const dim3 grid(a.chunks, a.B * a.hk);
+    const size_t lds = (size_t)kWavesPerBlock * a.Gk * stage_cap(decode_unroll(D)) * sizeof(uint2);
     if (D == 64)
-        hipLaunchKernelGGL((select_stream_kernel<64, decode_unroll(64)>), grid, dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((select_stream_kernel<64, decode_unroll(64)>), grid, dim3(kBlock), lds, s, a);
     else
-        hipLaunchKernelGGL((select_stream_kernel<128, decode_unroll(128)>), grid, dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((select_stream_kernel<128, decode_unroll(128)>), grid, dim3(kBlock), lds, s, a);
     return hipGetLastError();
 }
 
@@ -321,9 +400,9 @@ hipError_t launch_combine(int D, const Partials& p, int rows, int parts, uint16_
                           int32_t* counts, hipStream_t s)
 {
     if (D == 64)
-        hipLaunchKernelGGL(combine_kernel<64>, dim3(rows), dim3(64), 0, s, p, parts, out, counts);
+        hipLaunchKernelGGL(combine_kernel<64>, dim3(rows), dim3(kBlock), 0, s, p, parts, out, counts);
     else
-        hipLaunchKernelGGL(combine_kernel<128>, dim3(rows), dim3(128), 0, s, p, parts, out, counts);
+        hipLaunchKernelGGL(combine_kernel<128>, dim3(rows), dim3(kBlock), 0, s, p, parts, out, counts);
     return hipGetLastError();
 }
 

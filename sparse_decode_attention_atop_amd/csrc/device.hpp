@@ -149,22 +149,28 @@ __device__ __forceinline__ void load_ktile(KTile<D, U>& t, const uint16_t* k_hea
     }
 }
 
+// Logits of one 16-row group: s[i] = scale * sum_c q[slot 4*(lane/16)+i][c] *
+// K[row lane%16][c].  Every kernel that produces logits goes through here.
+template <int D>
+__device__ __forceinline__ void qk_group(const QFrag<D>& qf, const u32x4 (&kv)[D / 32], float scale,
+                                         float (&s)[4])
+{
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, qf.v[m]), __builtin_bit_cast(bf16x8, kv[m]), acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = acc[i] * scale;
+}
+
 // logits[u][i] = scale * sum_c q[slot 4*(lane/16)+i][c] * K[row0+16u+lane%16][c]
 template <int D, int U>
 __device__ __forceinline__ void qk_tile(const QFrag<D>& qf, const KTile<D, U>& kt, float scale,
                                         float (&s)[U][4])
 {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < D / 32; ++m)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, qf.v[m]), __builtin_bit_cast(bf16x8, kt.v[u][m]),
-                acc, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[u][i] = acc[i] * scale;
-    }
+    for (int u = 0; u < U; ++u) qk_group<D>(qf, kt.v[u], scale, s[u]);
 }
 
 // ------------------------------------------------------------ partials

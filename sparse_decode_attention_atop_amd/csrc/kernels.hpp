@@ -30,12 +30,12 @@ constexpr int kHistBins = 2048;
 
 // Threshold refresh: sample size cap, candidates staged in LDS by the final
 // select, and the most selection lists one row can have (4 per chunk).
-constexpr int kSampleMax = 4096;
-constexpr int kFinalStage = 16384;
-constexpr int kMaxListsPerRow = 8192;
+constexpr int kSampleMax = 2048;
+constexpr int kFinalStage = 8192;
+constexpr int kMaxListsPerRow = 2048;
 
-// Entries staged per (wave, head slot) in the stream kernel before a flush.
-constexpr int kStageCap = 64;
+// Entries staged per (wave, head slot) in the stream kernel: two tiles' worth.
+constexpr int stage_cap(int U) { return 32 * U; }
 
 // Gather segments: lists (4 per chunk) handled by one gather workgroup.
 constexpr int kMaxListsPerSeg = 256;
@@ -79,8 +79,8 @@ struct SampleArgs {
     float* sample;           // [B*hq][kSampleMax]
     float* pivot;            // [B*hq]
     int32_t B, hq, hk, Gk;
-    int64_t cache_len, stride;
-    int32_t m, rank;         // sample size, rank of the pivot within the sample
+    int64_t cache_len, stride;   // one 16-row sample block every `stride` rows
+    int32_t m, rank;             // sample size, rank of the pivot within the sample
     float scale;
 };
 

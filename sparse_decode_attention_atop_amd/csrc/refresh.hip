@@ -8,8 +8,8 @@
 // routine), so s >= tau keeps exactly N entries when there are no ties.
 //
 // Pipeline (all on the caller's stream; one pass over the K cache):
-//   1. sample_logits_kernel  logits of a strided sample of at most kSampleMax
-//                            rows per (b, query head), same MFMA QK tile.
+//   1. sample_logits_kernel  logits of a sample of at most kSampleMax rows per
+//                            (b, query head): evenly spaced 16-row blocks.
 //   2. pivot_kernel          per row: the k-th largest sample logit (LDS radix
 //                            select), with k chosen so that the pivot p lies
 //                            below tau with overwhelming probability.
@@ -112,8 +112,10 @@ __device__ uint32_t lds_radix_select(const uint32_t* keys, uint32_t n, uint32_t 
     return prefix;
 }
 
-// Logits of sampled rows: row k*stride for sample index k < m, for every query
-// head of key head g.  Output sample[b*hq + i][k] (row stride kSampleMax).
+// Logits of sampled rows for every query head of key head g.  The sample is
+// made of 16-row blocks (one MFMA group each, contiguous in memory): sample
+// index k covers row (k/16)*stride + k%16, k < m.  Output sample[b*hq + i][k]
+// (row stride kSampleMax).
 template <int D, int U>
 __global__ __launch_bounds__(kBlock) void sample_logits_kernel(SampleArgs a)
 {
@@ -131,7 +133,8 @@ __global__ __launch_bounds__(kBlock) void sample_logits_kernel(SampleArgs a)
     for (int u = 0; u < U; ++u) {
         int k = k0 + 16 * u + col;
         k = k < a.m ? k : a.m - 1;
-        const uint16_t* p = khead + (int64_t)k * a.stride * D + 8 * grp;
+        const int64_t row = (int64_t)(k >> 4) * a.stride + (k & 15);
+        const uint16_t* p = khead + row * D + 8 * grp;
 #pragma unroll
         for (int mm = 0; mm < D / 32; ++mm) kt.v[u][mm] = ld16(p + 32 * mm);
     }
@@ -249,15 +252,25 @@ __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
 
     uint32_t key;
     if (total >= a.top_n && total <= (uint32_t)kFinalStage) {
-        for (uint32_t E = t; E < total; E += kBlock) {
-            int lo = 0, hi = nl - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if ((uint32_t)pre[mid] <= E) lo = mid;
-                else hi = mid - 1;
+        // Stage the candidate keys, 8 loads in flight per thread.
+        for (uint32_t E0 = t; E0 < total; E0 += 8 * kBlock) {
+            uint2 ent[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t E = E0 + k * kBlock;
+                if (E < total) {
+                    int lo = 0, hi = nl - 1;
+                    while (lo < hi) {
+                        const int mid = (lo + hi + 1) >> 1;
+                        if ((uint32_t)pre[mid] <= E) lo = mid;
+                        else hi = mid - 1;
+                    }
+                    ent[k] = a.entries[(lbase + lo) * capw + (E - pre[lo])];
+                }
             }
-            const uint2 ent = a.entries[(lbase + lo) * capw + (E - pre[lo])];
-            keys[E] = float_key(__uint_as_float(ent.y));
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (E0 + k * kBlock < total) keys[E0 + k * kBlock] = float_key(__uint_as_float(ent[k].y));
         }
         __syncthreads();
         key = lds_radix_select(keys, total, a.top_n, w);
