@@ -90,6 +90,9 @@ def parse():
                         "the known-size kernel that scales rocprofv3 byte counters)")
     p.add_argument("--eager-only", action="store_true",
                    help="one eager pass over the decode steps, no timing (for counter runs)")
+    p.add_argument("--sweep", action="store_true",
+                   help="Llama-like and Qwen-like shapes over L x N x B: SAGA Atop-N vs the "
+                        "full-attention GQA path, one JSON line per point")
     return p.parse_args()
 
 
@@ -171,25 +174,28 @@ def run_saga(torch, saga, wl, w, args):
     def step(t, events=None):
         dm = saga.dims(w.batch, w.h_q, w.h_k, w.h_v, w.head_dim, L + t, w.rows, w.scale)
         for li, x in enumerate(layers):
-            if t % w.refresh_n == 0:
-                saga.atopn_refresh_thresholds(dm, w.top_n, x["q"][t], x["K"], x["tau"], ws)
             if events is not None:
                 events[li][0].record()
-            saga.saga_decode_step(dm, x["q"][t], x["K"], x["V"], x["tau"], x["out"], ws,
-                                  sel_counts=x["cnt"])
+            if t % w.refresh_n == 0:
+                # Refresh step: fresh thresholds and this step's output in one call.
+                saga.atopn_refresh_decode_step(dm, w.top_n, x["q"][t], x["K"], x["V"], x["tau"],
+                                               x["out"], ws, sel_counts=x["cnt"])
+            else:
+                saga.saga_decode_step(dm, x["q"][t], x["K"], x["V"], x["tau"], x["out"], ws,
+                                      sel_counts=x["cnt"])
             if events is not None:
                 events[li][1].record()
 
-    # Eager pass over one full run: per-launch timing of the decode kernel with
-    # events on the stream it runs on, and the selected counts of every launch.
-    log("eager pass (per-launch decode timing)")
+    # Eager pass over one full run, then a second one with per-call timing by
+    # events on the stream the calls run on, and the selected count of each.
+    log("eager pass (per-call timing)")
     for t in range(T):
         step(t)
     torch.cuda.synchronize()
     if args.eager_only:
         log("eager pass done")
         return None
-    launches = []
+    launches, refreshes = [], []
     for t in range(T):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in layers]
@@ -198,7 +204,8 @@ def run_saga(torch, saga, wl, w, args):
         for li, x in enumerate(layers):
             ms = ev[li][0].elapsed_time(ev[li][1])
             sel = int(x["cnt"].sum().item())
-            launches.append((t, li, ms, decode_algorithmic_bytes(w, L + t, sel), sel))
+            rec = (t, li, ms, decode_algorithmic_bytes(w, L + t, sel), sel)
+            (refreshes if t % w.refresh_n == 0 else launches).append(rec)
 
     log("capturing one HIP graph per decode step")
     graphs = []
@@ -214,7 +221,8 @@ def run_saga(torch, saga, wl, w, args):
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps after {args.warmup} warmup steps")
     sec, wall = time_graphs(torch, graphs, args.steps, args.warmup)
-    return dict(layers=layers, launches=launches, sec=sec, wall=wall, ws=ws, graphs=graphs)
+    return dict(layers=layers, launches=launches, refreshes=refreshes, sec=sec, wall=wall,
+                ws=ws, graphs=graphs)
 
 
 def run_gqa(torch, saga, wl, w, hkv, args):
@@ -285,6 +293,38 @@ def cpu_baseline(torch, wl, w, layer0):
             "sample_seconds": round(sum(times), 2)}
 
 
+MALL_BYTES = 256 << 20
+
+
+def sweep(torch, saga, wl, args):
+    """Per point: enough layers that one step streams >= 4x the 256 MB Infinity
+    Cache (capped at the family's layer count), 64 timed steps (two 32-token
+    runs) after 8 warmup; reports per-layer latency of both paths."""
+    fam_hkv = {"llama": 8, "qwen": 2}
+    args.steps, args.warmup, args.eager_only = 64, 8, False
+    for w0 in wl.sweep():
+        fam = "llama" if "llama" in w0.name else "qwen"
+        per_layer = w0.batch * (w0.h_k + w0.h_v) * w0.rows * w0.head_dim * 2
+        layers = max(2, min(w0.layers, -(-4 * MALL_BYTES // per_layer)))
+        w = w0.with_(layers=layers)
+        res = run_saga(torch, saga, wl, w, args)
+        sec = res["sec"]
+        step_bytes = sum(x[3] for x in res["launches"] + res["refreshes"]) / w.steps
+        del res
+        torch.cuda.empty_cache()
+        gq = run_gqa(torch, saga, wl, w, fam_hkv[fam], args)
+        torch.cuda.empty_cache()
+        saga_ms = 1e3 * sec / args.steps / layers
+        gqa_ms = 1e3 * gq["sec"] / args.steps / layers
+        print(json.dumps({
+            "point": w0.name, "family": fam, "L": w0.L, "top_n": w0.top_n, "batch": w0.batch,
+            "layers_timed": layers, "saga_atopn_ms_per_layer": round(saga_ms, 4),
+            "gqa_full_ms_per_layer": round(gqa_ms, 4), "speedup": round(gqa_ms / saga_ms, 3),
+            "saga_hbm_gbs": round(step_bytes / layers / (saga_ms * 1e-3) / 1e9, 1),
+            "gqa_hbm_gbs": round(gq["bytes_per_step"] / layers / (gqa_ms * 1e-3) / 1e9, 1),
+            "cache_resident": per_layer * layers < 2 * MALL_BYTES}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -303,6 +343,9 @@ def main():
     if args.calibrate:
         calibrate(torch)
         return
+    if args.sweep:
+        sweep(torch, saga, wl, args)
+        return
     w = wl.WORKLOADS[args.workload]
     res = run_saga(torch, saga, wl, w, args)
     if res is None:
@@ -312,12 +355,14 @@ def main():
     steps_per_s = args.steps / sec
     ms_per_step = 1e3 * sec / args.steps
 
-    launches = res["launches"]
+    launches = res["launches"] or res["refreshes"]    # n = 1: every step refreshes
     avg_ms = sum(x[2] for x in launches) / len(launches)
     avg_bytes = sum(x[3] for x in launches) / len(launches)
     achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
     avg_sel = sum(x[4] for x in launches) / len(launches) / (w.batch * w.h_q)
-    step_bytes = sum(x[3] for x in launches) / T
+    refreshes = res["refreshes"]
+    step_bytes = (sum(x[3] for x in launches) + sum(x[3] for x in refreshes)) / T
+    ref_ms = sum(x[2] for x in refreshes) / len(refreshes)
     traffic = measured_traffic(args.traffic or os.path.join(ROOT, "profiles",
                                                             f"traffic_{w.name}.md"), w.name)
 
@@ -366,6 +411,8 @@ def main():
                      "avg_launch_ms": round(avg_ms, 5),
                      "algorithmic_bytes_per_launch": int(avg_bytes),
                      "mean_selected_per_head": round(avg_sel, 1)},
+        "refresh_step": {"call": "atopn_refresh_decode_step", "avg_call_ms": round(ref_ms, 5),
+                         "calls_per_step": round(len(refreshes) / T, 3)},
         "cpu_baseline": cpu,
     }
     line.update(extra)

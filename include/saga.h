@@ -17,8 +17,9 @@
  *     selected value rows (ai.info summary, Main Findings, first item).
  *
  * The caller owns the refresh schedule: at steps t with t mod n == 0 call
- * atopn_refresh_thresholds() and then saga_decode_step() with the fresh
- * thresholds; at other steps call saga_decode_step() with the kept ones.
+ * atopn_refresh_decode_step() (or atopn_refresh_thresholds() and then
+ * saga_decode_step() with the fresh thresholds); at other steps call
+ * saga_decode_step() with the kept ones.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -68,7 +69,9 @@ typedef enum saga_status {
  *   h_q, h_k, h_v >= 1; h_k and h_v each divide h_q; h_q/h_k <= 16
  *   head_dim   64 or 128
  *   ctx_len    rows attended this step, 1 <= ctx_len <= cache_len
- *   cache_len  rows allocated per cache head (the head stride), < 2^27
+ *   cache_len  rows allocated per cache head (the head stride), < 2^27; one
+ *              head must stay under 2 GiB (cache_len * head_dim * 2 < 2^31,
+ *              8M rows at head_dim 128), else SAGA_ERR_UNSUPPORTED
  *   scale      multiplies q.k (use 1/sqrt(d) unless it is folded into q)   */
 typedef struct saga_dims {
     int32_t batch;
@@ -136,6 +139,23 @@ int saga_decode_step(const saga_dims* dims, const void* q_dev, const void* k_cac
                      const void* v_cache_dev, const float* thresholds_dev, void* out_dev,
                      int32_t* sel_counts_dev, uint32_t* sel_bitmap_debug_dev,
                      void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * A refresh step in one call: the same results as atopn_refresh_thresholds()
+ * followed by saga_decode_step() with the fresh thresholds, with one pass over
+ * the K cache instead of two (the refresh's candidate lists already hold every
+ * logit >= the new threshold).  This is the step the caller runs at
+ * t mod n == 0.
+ *
+ *   thresholds_dev   output fp32 [batch][h_q] (kept for the following steps)
+ *   out_dev          output bf16 [batch][h_q][head_dim]
+ *   sel_counts_dev   optional output int32 [batch][h_q] (NULL: skip)
+ * Errors: as atopn_refresh_thresholds() and saga_decode_step().
+ */
+int atopn_refresh_decode_step(const saga_dims* dims, int32_t top_n, const void* q_dev,
+                              const void* k_cache_dev, const void* v_cache_dev,
+                              float* thresholds_dev, void* out_dev, int32_t* sel_counts_dev,
+                              void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
  * Full (dense) decode attention over all ctx_len rows with the same head maps:

@@ -20,13 +20,14 @@ import torch
 
 __all__ = [
     "SagaDims", "SagaError", "dims", "library", "saga_workspace_bytes", "alloc_workspace",
-    "atopn_refresh_thresholds", "saga_decode_step", "saga_full_attention",
-    "saga_status_string", "saga_version", "LIB_PATH", "EXPORTED_SYMBOLS",
+    "atopn_refresh_thresholds", "saga_decode_step", "atopn_refresh_decode_step",
+    "saga_full_attention", "saga_status_string", "saga_version", "LIB_PATH", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsaga.so")
 EXPORTED_SYMBOLS = ("saga_workspace_bytes", "atopn_refresh_thresholds", "saga_decode_step",
-                    "saga_full_attention", "saga_status_string", "saga_version")
+                    "atopn_refresh_decode_step", "saga_full_attention", "saga_status_string",
+                    "saga_version")
 
 SAGA_OK = 0
 SAGA_ERR_INVALID_ARGUMENT = 1
@@ -81,6 +82,8 @@ def library():
         lib.atopn_refresh_thresholds.restype = ctypes.c_int
         lib.saga_decode_step.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.saga_decode_step.restype = ctypes.c_int
+        lib.atopn_refresh_decode_step.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.atopn_refresh_decode_step.restype = ctypes.c_int
         lib.saga_full_attention.argtypes = [pd, vp, vp, vp, vp, vp, sz, vp]
         lib.saga_full_attention.restype = ctypes.c_int
         lib.saga_status_string.argtypes = [ctypes.c_int]
@@ -186,6 +189,27 @@ def saga_decode_step(d: SagaDims, q: torch.Tensor, k_cache: torch.Tensor, v_cach
         _ptr(out, torch.bfloat16, "out"), _ptr(sel_counts, torch.int32, "sel_counts"),
         _ptr(sel_bitmap_debug, torch.int32, "sel_bitmap_debug"), ws, nbytes, _stream(stream)),
         "saga_decode_step")
+
+
+def atopn_refresh_decode_step(d: SagaDims, top_n: int, q: torch.Tensor, k_cache: torch.Tensor,
+                              v_cache: torch.Tensor, thresholds: torch.Tensor, out: torch.Tensor,
+                              workspace: torch.Tensor, sel_counts: Optional[torch.Tensor] = None,
+                              stream=None) -> None:
+    """A refresh step: fresh thresholds (kept for later steps) and this step's output."""
+    bh = d.batch * d.h_q
+    _need(q, bh * d.head_dim, "q")
+    _need(k_cache, d.batch * d.h_k * d.cache_len * d.head_dim, "k_cache")
+    _need(v_cache, d.batch * d.h_v * d.cache_len * d.head_dim, "v_cache")
+    _need(thresholds, bh, "thresholds")
+    _need(out, bh * d.head_dim, "out")
+    _need(sel_counts, bh, "sel_counts")
+    ws, nbytes = _ws(workspace)
+    _check(library().atopn_refresh_decode_step(
+        ctypes.byref(d), int(top_n), _ptr(q, torch.bfloat16, "q"),
+        _ptr(k_cache, torch.bfloat16, "k_cache"), _ptr(v_cache, torch.bfloat16, "v_cache"),
+        _ptr(thresholds, torch.float32, "thresholds"), _ptr(out, torch.bfloat16, "out"),
+        _ptr(sel_counts, torch.int32, "sel_counts"), ws, nbytes, _stream(stream)),
+        "atopn_refresh_decode_step")
 
 
 def saga_full_attention(d: SagaDims, q: torch.Tensor, k_cache: torch.Tensor,

@@ -35,6 +35,8 @@ int validate_dims(const saga_dims* d)
     if (d->h_q / d->h_k > 16) return SAGA_ERR_UNSUPPORTED;
     if ((int64_t)d->batch * d->h_k > 65535) return SAGA_ERR_UNSUPPORTED;
     if ((int64_t)d->batch * d->h_q * d->cache_len > (int64_t(1) << 40)) return SAGA_ERR_UNSUPPORTED;
+    // One cache head is addressed with 32-bit buffer offsets.
+    if (d->cache_len * d->head_dim * 2 >= (int64_t(1) << 31)) return SAGA_ERR_UNSUPPORTED;
     return SAGA_OK;
 }
 
@@ -64,7 +66,7 @@ Chunking plan_chunks(int64_t ctx, int64_t pairs, int64_t block_rows, int max_chu
 struct Layout {
     int max_chunks;
     int64_t entry_rows;   // selection-list capacity per (b, query head)
-    size_t pm, pl, pc, po, entries, lcount, lmax, sample, pivot, total;
+    size_t pm, pl, pc, po, entries, lcount, lmax, sample, pivot, flags, total;
 };
 
 Layout make_layout(const saga_dims* d)
@@ -92,6 +94,7 @@ Layout make_layout(const saga_dims* d)
     L.lmax = take(rows * L.max_chunks * kWavesPerBlock * 4);
     L.sample = take(rows * kSampleMax * 4);
     L.pivot = take(rows * 4);
+    L.flags = take((size_t)d->batch * d->h_k * 4);
     L.total = off;
     return L;
 }
@@ -142,6 +145,147 @@ SAGA_EXPORT size_t saga_workspace_bytes(const saga_dims* dims, int32_t top_n)
     return make_layout(dims).total;
 }
 
+namespace {
+
+// Refresh steps 1-4 (see refresh.hip): sample, pivot, candidate lists, exact
+// N-th largest.  Requires top_n < ctx.  With group_flags, key groups in which
+// a row needed the recompute path are flagged (their lists are incomplete).
+int enqueue_refresh(const saga_dims* dims, int32_t top_n, const void* q_dev,
+                    const void* k_cache_dev, float* thresholds_dev, float* logits_debug_dev,
+                    void* workspace_dev, const Layout& L, const Chunking& ch, hipStream_t s,
+                    uint32_t* group_flags)
+{
+    unsigned char* w = static_cast<unsigned char*>(workspace_dev);
+    const int D = dims->head_dim;
+    const int64_t ctx = dims->ctx_len;
+    float* pivot = reinterpret_cast<float*>(w + L.pivot);
+
+    // 1-2. Pivot from a sample of 16-row blocks, one every `stride` rows
+    // (stride a multiple of 16), at most kSampleMax rows; the whole context
+    // when it is that short, and then the pivot is tau itself.  Otherwise its
+    // rank in the sample sits five standard deviations above the expected
+    // number of sample logits >= tau, so at least N logits are >= pivot except
+    // with negligible probability (and step 4 stays exact regardless).
+    SampleArgs sa{};
+    sa.q = static_cast<const uint16_t*>(q_dev);
+    sa.k = static_cast<const uint16_t*>(k_cache_dev);
+    sa.sample = reinterpret_cast<float*>(w + L.sample);
+    sa.pivot = pivot;
+    sa.group_flags = group_flags;
+    sa.B = dims->batch;
+    sa.hq = dims->h_q;
+    sa.hk = dims->h_k;
+    sa.Gk = dims->h_q / dims->h_k;
+    sa.cache_len = dims->cache_len;
+    const int64_t blocks_max = kSampleMax / 16;
+    if (ctx <= kSampleMax) {
+        sa.stride = 16;
+        sa.m = (int)ctx;
+    } else {
+        sa.stride = (ctx / 16 + blocks_max - 1) / blocks_max * 16;   // every block fully inside ctx
+        sa.m = (int)(ctx / sa.stride) * 16;
+    }
+    if (sa.m == ctx) {
+        sa.rank = top_n;
+    } else {
+        const double mu = (double)top_n * sa.m / (double)ctx;
+        double r = ceil(mu + 5.0 * sqrt(mu) + 5.0);
+        if (r > sa.m) r = sa.m;
+        sa.rank = (int)r;
+    }
+    sa.scale = dims->scale;
+    int st = hip_status(launch_sample(D, sa, s));
+    if (st != SAGA_OK) return st;
+
+    // 3. Candidate lists: every logit >= pivot.
+    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, pivot, workspace_dev);
+    a.logits_out = logits_debug_dev;
+    st = hip_status(launch_select_stream(D, a, s));
+    if (st != SAGA_OK) return st;
+
+    // 4. Exact N-th largest per row.
+    FinalArgs fa{};
+    fa.q = sa.q;
+    fa.k = sa.k;
+    fa.entries = a.entries;
+    fa.list_count = a.list_count;
+    fa.tau = thresholds_dev;
+    fa.group_flags = group_flags;
+    fa.B = dims->batch;
+    fa.hq = dims->h_q;
+    fa.hk = dims->h_k;
+    fa.Gk = sa.Gk;
+    fa.ctx = ctx;
+    fa.cache_len = dims->cache_len;
+    fa.rows_per_chunk = ch.rows;
+    fa.chunks = ch.chunks;
+    fa.top_n = (uint32_t)top_n;
+    fa.scale = dims->scale;
+    return hip_status(launch_refresh_final(D, fa, s));
+}
+
+// Masked softmax + sparse gather over the lists in the workspace, then the
+// combine into out.  With tau_filter, list entries below it are skipped.
+int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunking& ch,
+                           const void* v_cache_dev, const float* tau_filter, void* out_dev,
+                           int32_t* sel_counts_dev, void* workspace_dev, hipStream_t s)
+{
+    unsigned char* w = static_cast<unsigned char*>(workspace_dev);
+    const int D = dims->head_dim;
+    const int rows = dims->batch * dims->h_q;
+    // Each (b, query head) gets `segs` gather workgroups that split its selected
+    // entries evenly: about kGatherTargetBlocks workgroups in all.
+    GatherArgs ga{};
+    ga.v = static_cast<const uint16_t*>(v_cache_dev);
+    ga.entries = reinterpret_cast<const uint2*>(w + L.entries);
+    ga.list_count = reinterpret_cast<const int32_t*>(w + L.lcount);
+    ga.list_max = reinterpret_cast<const float*>(w + L.lmax);
+    ga.tau_filter = tau_filter;
+    ga.part = partials(workspace_dev, L);
+    ga.B = dims->batch;
+    ga.hq = dims->h_q;
+    ga.hv = dims->h_v;
+    ga.Gv = dims->h_q / dims->h_v;
+    ga.cache_len = dims->cache_len;
+    ga.rows_per_chunk = ch.rows;
+    ga.chunks = ch.chunks;
+    int64_t segs = (kGatherTargetBlocks + rows - 1) / rows;
+    if (segs > kGatherMaxSegs) segs = kGatherMaxSegs;
+    if (segs > L.max_chunks) segs = L.max_chunks;       // partials hold max_chunks per row
+    ga.segs = (int)segs;
+    int st = hip_status(launch_gather(D, ga, s));
+    if (st != SAGA_OK) return st;
+    return hip_status(launch_combine(D, ga.part, rows, ga.segs, static_cast<uint16_t*>(out_dev),
+                                     sel_counts_dev, s));
+}
+
+// Decode with kept thresholds: stream-select into the lists, then gather.
+int enqueue_decode(const saga_dims* dims, const Layout& L, const void* q_dev,
+                   const void* k_cache_dev, const void* v_cache_dev, const float* thresholds_dev,
+                   void* out_dev, int32_t* sel_counts_dev, uint32_t* sel_bitmap_debug_dev,
+                   void* workspace_dev, hipStream_t s)
+{
+    const int D = dims->head_dim;
+    const int rows = dims->batch * dims->h_q;
+    const int64_t words = (dims->cache_len + 31) / 32;
+    int st;
+    if (sel_bitmap_debug_dev) {
+        st = hip_status(launch_fill_u32(sel_bitmap_debug_dev, (int64_t)rows * words, 0u, s));
+        if (st != SAGA_OK) return st;
+    }
+    const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
+                                    decode_block_rows(D), L.max_chunks);
+    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, thresholds_dev, workspace_dev);
+    a.bitmap = sel_bitmap_debug_dev;
+    a.bitmap_words = words;
+    st = hip_status(launch_select_stream(D, a, s));
+    if (st != SAGA_OK) return st;
+    return enqueue_gather_combine(dims, L, ch, v_cache_dev, nullptr, out_dev, sel_counts_dev,
+                                  workspace_dev, s);
+}
+
+}  // namespace
+
 SAGA_EXPORT int atopn_refresh_thresholds(const saga_dims* dims, int32_t top_n, const void* q_dev,
                                          const void* k_cache_dev, float* thresholds_dev,
                                          float* logits_debug_dev, void* workspace_dev,
@@ -161,15 +305,13 @@ SAGA_EXPORT int atopn_refresh_thresholds(const saga_dims* dims, int32_t top_n, c
     unsigned char* w = static_cast<unsigned char*>(workspace_dev);
     const int D = dims->head_dim;
     const int rows = dims->batch * dims->h_q;
-    const int64_t ctx = dims->ctx_len;
-    const Chunking ch = plan_chunks(ctx, (int64_t)dims->batch * dims->h_k, decode_block_rows(D),
-                                    L.max_chunks);
-    float* pivot = reinterpret_cast<float*>(w + L.pivot);
-
-    if ((int64_t)top_n >= ctx) {
+    const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
+                                    decode_block_rows(D), L.max_chunks);
+    if ((int64_t)top_n >= dims->ctx_len) {
         // N >= ctx: every entry is kept, tau = -inf.  The logits are still
         // produced when asked for (a pass that selects nothing).
         if (logits_debug_dev) {
+            float* pivot = reinterpret_cast<float*>(w + L.pivot);
             st = hip_status(launch_fill_u32(reinterpret_cast<uint32_t*>(pivot), rows, 0x7f800000u, s));
             if (st != SAGA_OK) return st;
             SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, pivot, workspace_dev);
@@ -180,68 +322,8 @@ SAGA_EXPORT int atopn_refresh_thresholds(const saga_dims* dims, int32_t top_n, c
         return hip_status(launch_fill_u32(reinterpret_cast<uint32_t*>(thresholds_dev), rows,
                                           0xff800000u, s));
     }
-
-    // 1-2. Pivot from a strided sample of at most kSampleMax rows.  With the
-    // whole context sampled the pivot is tau itself; otherwise its rank in
-    // the sample sits five standard deviations above the expected number of
-    // sample logits >= tau, so at least N logits are >= pivot except with
-    // negligible probability (and step 4 stays exact regardless).
-    SampleArgs sa{};
-    sa.q = static_cast<const uint16_t*>(q_dev);
-    sa.k = static_cast<const uint16_t*>(k_cache_dev);
-    sa.sample = reinterpret_cast<float*>(w + L.sample);
-    sa.pivot = pivot;
-    sa.B = dims->batch;
-    sa.hq = dims->h_q;
-    sa.hk = dims->h_k;
-    sa.Gk = dims->h_q / dims->h_k;
-    sa.cache_len = dims->cache_len;
-    // Sample: 16-row blocks, one every `stride` rows (stride a multiple of 16),
-    // at most kSampleMax rows; the whole context when it is that short.
-    const int64_t blocks_max = kSampleMax / 16;
-    if (ctx <= kSampleMax) {
-        sa.stride = 16;
-        sa.m = (int)ctx;
-    } else {
-        sa.stride = (ctx / 16 + blocks_max - 1) / blocks_max * 16;   // every block fully inside ctx
-        sa.m = (int)(ctx / sa.stride) * 16;
-    }
-    if (sa.m == ctx) {
-        sa.rank = top_n;
-    } else {
-        const double mu = (double)top_n * sa.m / (double)ctx;
-        double r = ceil(mu + 5.0 * sqrt(mu) + 5.0);
-        if (r > sa.m) r = sa.m;
-        sa.rank = (int)r;
-    }
-    sa.scale = dims->scale;
-    st = hip_status(launch_sample(D, sa, s));
-    if (st != SAGA_OK) return st;
-
-    // 3. Candidate lists: every logit >= pivot.
-    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, pivot, workspace_dev);
-    a.logits_out = logits_debug_dev;
-    st = hip_status(launch_select_stream(D, a, s));
-    if (st != SAGA_OK) return st;
-
-    // 4. Exact N-th largest per row.
-    FinalArgs fa{};
-    fa.q = sa.q;
-    fa.k = sa.k;
-    fa.entries = a.entries;
-    fa.list_count = a.list_count;
-    fa.tau = thresholds_dev;
-    fa.B = dims->batch;
-    fa.hq = dims->h_q;
-    fa.hk = dims->h_k;
-    fa.Gk = sa.Gk;
-    fa.ctx = ctx;
-    fa.cache_len = dims->cache_len;
-    fa.rows_per_chunk = ch.rows;
-    fa.chunks = ch.chunks;
-    fa.top_n = (uint32_t)top_n;
-    fa.scale = dims->scale;
-    return hip_status(launch_refresh_final(D, fa, s));
+    return enqueue_refresh(dims, top_n, q_dev, k_cache_dev, thresholds_dev, logits_debug_dev,
+                           workspace_dev, L, ch, s, nullptr);
 }
 
 SAGA_EXPORT int saga_decode_step(const saga_dims* dims, const void* q_dev, const void* k_cache_dev,
@@ -260,49 +342,56 @@ SAGA_EXPORT int saga_decode_step(const saga_dims* dims, const void* q_dev, const
         return SAGA_ERR_INVALID_ARGUMENT;
     const Layout L = make_layout(dims);
     if (workspace_bytes < L.total) return SAGA_ERR_WORKSPACE_TOO_SMALL;
+    return enqueue_decode(dims, L, q_dev, k_cache_dev, v_cache_dev, thresholds_dev, out_dev,
+                          sel_counts_dev, sel_bitmap_debug_dev, workspace_dev,
+                          static_cast<hipStream_t>(stream));
+}
+
+SAGA_EXPORT int atopn_refresh_decode_step(const saga_dims* dims, int32_t top_n, const void* q_dev,
+                                          const void* k_cache_dev, const void* v_cache_dev,
+                                          float* thresholds_dev, void* out_dev,
+                                          int32_t* sel_counts_dev, void* workspace_dev,
+                                          size_t workspace_bytes, void* stream)
+{
+    int st = validate_dims(dims);
+    if (st != SAGA_OK) return st;
+    if (top_n < 1 || !q_dev || !k_cache_dev || !v_cache_dev || !thresholds_dev || !out_dev ||
+        !workspace_dev)
+        return SAGA_ERR_INVALID_ARGUMENT;
+    if (misaligned(q_dev, 16) || misaligned(k_cache_dev, 16) || misaligned(v_cache_dev, 16) ||
+        misaligned(thresholds_dev, 4) || misaligned(out_dev, 2) || misaligned(sel_counts_dev, 4) ||
+        misaligned(workspace_dev, 16))
+        return SAGA_ERR_INVALID_ARGUMENT;
+    const Layout L = make_layout(dims);
+    if (workspace_bytes < L.total) return SAGA_ERR_WORKSPACE_TOO_SMALL;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned char* w = static_cast<unsigned char*>(workspace_dev);
     const int D = dims->head_dim;
     const int rows = dims->batch * dims->h_q;
-    const int64_t words = (dims->cache_len + 31) / 32;
-    if (sel_bitmap_debug_dev) {
-        st = hip_status(launch_fill_u32(sel_bitmap_debug_dev, (int64_t)rows * words, 0u, s));
+    if ((int64_t)top_n >= dims->ctx_len) {
+        st = hip_status(launch_fill_u32(reinterpret_cast<uint32_t*>(thresholds_dev), rows,
+                                        0xff800000u, s));
         if (st != SAGA_OK) return st;
+        return enqueue_decode(dims, L, q_dev, k_cache_dev, v_cache_dev, thresholds_dev, out_dev,
+                              sel_counts_dev, nullptr, workspace_dev, s);
     }
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
                                     decode_block_rows(D), L.max_chunks);
+    uint32_t* flags = reinterpret_cast<uint32_t*>(w + L.flags);
+    st = enqueue_refresh(dims, top_n, q_dev, k_cache_dev, thresholds_dev, nullptr, workspace_dev,
+                         L, ch, s, flags);
+    if (st != SAGA_OK) return st;
+    // Key groups whose candidate lists miss selected entries (a row took the
+    // recompute path) are streamed again with the fresh thresholds; every
+    // other workgroup of this launch exits at once.
     SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, thresholds_dev, workspace_dev);
-    a.bitmap = sel_bitmap_debug_dev;
-    a.bitmap_words = words;
+    a.group_flags = flags;
     st = hip_status(launch_select_stream(D, a, s));
     if (st != SAGA_OK) return st;
-
-    // Segments of chunks per gather workgroup: about kGatherTargetBlocks
-    // workgroups in total, at most kMaxListsPerSeg lists each.
-    GatherArgs ga{};
-    ga.v = static_cast<const uint16_t*>(v_cache_dev);
-    ga.entries = a.entries;
-    ga.list_count = a.list_count;
-    ga.list_max = a.list_max;
-    ga.part = partials(workspace_dev, L);
-    ga.B = dims->batch;
-    ga.hq = dims->h_q;
-    ga.hv = dims->h_v;
-    ga.Gv = dims->h_q / dims->h_v;
-    ga.cache_len = dims->cache_len;
-    ga.rows_per_chunk = ch.rows;
-    ga.chunks = ch.chunks;
-    int64_t segs = (kGatherTargetBlocks + rows - 1) / rows;
-    if (segs > ch.chunks) segs = ch.chunks;
-    int64_t cps = (ch.chunks + segs - 1) / segs;
-    const int64_t max_cps = kMaxListsPerSeg / kWavesPerBlock;
-    if (cps > max_cps) cps = max_cps;
-    ga.chunks_per_seg = (int)cps;
-    ga.segs = (int)((ch.chunks + cps - 1) / cps);
-    st = hip_status(launch_gather(D, ga, s));
-    if (st != SAGA_OK) return st;
-    return hip_status(launch_combine(D, ga.part, rows, ga.segs, static_cast<uint16_t*>(out_dev),
-                                     sel_counts_dev, s));
+    // The lists hold every logit >= tau (and more): keep those >= tau.
+    return enqueue_gather_combine(dims, L, ch, v_cache_dev, thresholds_dev, out_dev,
+                                  sel_counts_dev, workspace_dev, s);
 }
 
 SAGA_EXPORT int saga_full_attention(const saga_dims* dims, const void* q_dev,

@@ -32,15 +32,17 @@ namespace saga {
 
 namespace {
 
-template <int D, int U>
+// Stream-select kernel.  Hits are compacted with one ballot per (16-row
+// group u, head index i): the four lane groups' hits for head slots 4*g + i
+// go to one wave-private LDS queue per i in ballot order, so the queue length
+// stays wave-uniform (scalar registers) and each hit costs one mbcnt.  When a
+// queue could overflow, it is split by head slot and appended to the global
+// per-(head, chunk, wave) lists in order.  DEBUG adds the optional logits and
+// selection-bitmap outputs.
+template <int D, int U, bool DEBUG>
 __global__ __launch_bounds__(kBlock) void select_stream_kernel(SelectStreamArgs a)
 {
-    // Hits are staged per (wave, head slot) in LDS (stage_cap(U) entries each)
-    // and written to the global lists in whole runs, never as scattered
-    // 8-byte stores.  A slot gains at most 16*U entries per tile, so one flush
-    // check per tile suffices.
-    extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int CAPS = stage_cap(U);
+    __shared__ uint2 queue[kWavesPerBlock][4][kQueueCap];
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int chunk = blockIdx.x;
@@ -50,100 +52,117 @@ __global__ __launch_bounds__(kBlock) void select_stream_kernel(SelectStreamArgs 
     const int64_t r1 = min(r0 + a.rows_per_chunk, a.ctx);
     const int64_t capw = a.rows_per_chunk / kWavesPerBlock;
     const int qh0 = b * a.hq + g * Gk;
-    uint2* st = reinterpret_cast<uint2*>(smem) + (size_t)wave * Gk * CAPS;
+    uint2 (*q4)[kQueueCap] = queue[wave];
+    if (a.group_flags && a.group_flags[blockIdx.y] == 0u) return;   // whole workgroup
 
     const QFrag<D> qf = load_qfrag<D>(col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr);
-    // Per lane: head slot 4*grp + i.  staged = entries waiting in LDS,
-    // written = entries already in the global list.
     float tau[4], mx[4];
-    int32_t staged[4], written[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int slot = 4 * grp + i;
         tau[i] = slot < Gk ? a.tau[qh0 + slot] : INFINITY;
         mx[i] = -INFINITY;
-        staged[i] = 0;
-        written[i] = 0;
     }
-    const uint32_t below = (1u << col) - 1u;
+    // Wave-uniform bookkeeping: entries waiting in queue i, entries already in
+    // the global list of head slot h.
+    int qn[4] = {0, 0, 0, 0};
+    int written[16];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) written[h] = 0;
     const int64_t list0 = (int64_t)qh0 * a.chunks * kWavesPerBlock + chunk * kWavesPerBlock + wave;
     const int64_t list_stride = (int64_t)a.chunks * kWavesPerBlock;   // between head slots
 
-    auto pick = [](const int32_t (&v)[4], int i) {
-        return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
-    };
+    // Split every queue by head slot (4*gs + i) and append to the global lists.
     auto flush_all = [&]() {
         wave_sync();
-#pragma unroll 1
-        for (int h = 0; h < Gk; ++h) {
-            const int n = __shfl(pick(staged, h & 3), 16 * (h >> 2));
-            const int off = __shfl(pick(written, h & 3), 16 * (h >> 2));
-            uint2* dst = a.entries + (list0 + h * list_stride) * capw + off;
-            for (int k = lane; k < n; k += kWave) dst[k] = st[h * CAPS + k];
-        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            written[i] += staged[i];
-            staged[i] = 0;
+            for (int base = 0; base < qn[i]; base += kWave) {
+                const bool have = base + lane < qn[i];
+                const uint2 e = have ? q4[i][base + lane] : make_uint2(0u, 0u);
+                const int slot = e.x & 15;
+#pragma unroll
+                for (int gs = 0; gs < 4; ++gs) {
+                    const int h = 4 * gs + i;
+                    const uint64_t m = __ballot(have && slot == h);
+                    if (m == 0) continue;
+                    if (have && slot == h)
+                        a.entries[(list0 + h * list_stride) * capw + written[h] + lanes_below(m)] =
+                            make_uint2(e.x >> 4, e.y);
+                    written[h] += __popcll(m);
+                }
+            }
+            qn[i] = 0;
         }
         wave_sync();
     };
 
+    // A tile adds at most 64*U entries to a queue: flush before one can overflow.
+    auto maybe_flush = [&]() {
+        if (max(max(qn[0], qn[1]), max(qn[2], qn[3])) > kQueueCap - kWave * U) flush_all();
+    };
+
     auto process = [&](const KTile<D, U>& kt, int64_t t0) {
-        bool full = false;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) full |= staged[i] > CAPS - 16 * U;
-        if (__ballot(full)) flush_all();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float s[4];
             qk_group<D>(qf, kt.v[u], a.scale, s);
             const int64_t row = t0 + 16 * u + col;
             const bool valid = row < r1;
-            if (a.logits_out && valid) {
+            const uint32_t tag = (uint32_t)(row - r0) << 4;
+            if constexpr (DEBUG) {
+                if (a.logits_out && valid) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (4 * grp + i < Gk) a.logits_out[(int64_t)(qh0 + 4 * grp + i) * a.ctx + row] = s[i];
+                    for (int i = 0; i < 4; ++i)
+                        if (4 * grp + i < Gk)
+                            a.logits_out[(int64_t)(qh0 + 4 * grp + i) * a.ctx + row] = s[i];
+                }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool pred = valid && s[i] >= tau[i];
                 const uint64_t mask = __ballot(pred);
-                if (mask == 0) continue;                         // wave-uniform
-                const uint32_t mine = (uint32_t)(mask >> (16 * grp)) & 0xffffu;
-                if (pred) {
-                    mx[i] = fmaxf(mx[i], s[i]);
-                    st[(4 * grp + i) * CAPS + staged[i] + __popc(mine & below)] =
-                        make_uint2((uint32_t)(row - r0), __float_as_uint(s[i]));
-                }
-                staged[i] += __popc(mine);
-                if (a.bitmap && col == 0 && mine) {
-                    const int64_t row0 = t0 + 16 * u;             // multiple of 16
-                    atomicOr(a.bitmap + (int64_t)(qh0 + 4 * grp + i) * a.bitmap_words + row0 / 32,
-                             mine << (row0 & 31));
+                if (pred)
+                    q4[i][qn[i] + lanes_below(mask)] =
+                        make_uint2(tag | (uint32_t)(4 * grp + i), __float_as_uint(s[i]));
+                qn[i] += __popcll(mask);
+                mx[i] = fmaxf(mx[i], pred ? s[i] : -INFINITY);
+                if constexpr (DEBUG) {
+                    const uint32_t mine = (uint32_t)(mask >> (16 * grp)) & 0xffffu;
+                    if (a.bitmap && col == 0 && mine) {
+                        const int64_t row0 = t0 + 16 * u;         // multiple of 16
+                        atomicOr(a.bitmap + (int64_t)(qh0 + 4 * grp + i) * a.bitmap_words + row0 / 32,
+                                 mine << (row0 & 31));
+                    }
                 }
             }
         }
     };
 
     // Software-pipelined stream: the next tile's loads are issued before the
-    // current tile is processed, so every wave keeps a tile in flight.
-    const uint16_t* khead = a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
+    // current tile is processed, so every wave keeps a tile in flight.  The
+    // buffer resource ends at this chunk's last row r1: prefetches past it
+    // return zeros without touching memory, so every prefetch is issued
+    // unconditionally and the load counters stay the same on every path (a
+    // conditional prefetch makes the compiler wait for it before the current
+    // tile).  Queue flushes (the only global stores) happen before a prefetch.
+    const __amdgpu_buffer_rsrc_t khead =
+        make_rsrc(a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D, (uint32_t)(r1 * D * 2));
     constexpr int64_t kStep = kWavesPerBlock * 16 * U;
     int64_t t0 = r0 + wave * 16 * U;
     if (t0 < r1) {
         KTile<D, U> ka, kb;
-        load_ktile<D, U>(ka, khead, t0, r1);
+        load_ktile_buf<D, U>(ka, khead, (uint32_t)t0);
         while (true) {
-            const int64_t t1 = t0 + kStep;
-            if (t1 < r1) load_ktile<D, U>(kb, khead, t1, r1);
+            maybe_flush();
+            load_ktile_buf<D, U>(kb, khead, (uint32_t)(t0 + kStep));
             process(ka, t0);
-            if (t1 >= r1) break;
-            const int64_t t2 = t1 + kStep;
-            if (t2 < r1) load_ktile<D, U>(ka, khead, t2, r1);
-            process(kb, t1);
-            if (t2 >= r1) break;
-            t0 = t2;
+            if (t0 + kStep >= r1) break;
+            maybe_flush();
+            load_ktile_buf<D, U>(ka, khead, (uint32_t)(t0 + 2 * kStep));
+            process(kb, t0 + kStep);
+            if (t0 + 2 * kStep >= r1) break;
+            t0 += 2 * kStep;
         }
     }
     flush_all();
@@ -152,7 +171,11 @@ __global__ __launch_bounds__(kBlock) void select_stream_kernel(SelectStreamArgs 
         const float m = group16_max(mx[i]);
         if (col == 0 && 4 * grp + i < Gk) {
             const int64_t list = list0 + (4 * grp + i) * list_stride;
-            a.list_count[list] = written[i];
+            int cnt = written[i];
+#pragma unroll
+            for (int gs = 1; gs < 4; ++gs)
+                if (grp == gs) cnt = written[4 * gs + i];
+            a.list_count[list] = cnt;
             a.list_max[list] = m;
         }
     }
@@ -169,6 +192,11 @@ __device__ float block_max(float v, float* red)
     return v;
 }
 
+// Gather kernel: grid.x = segment, grid.y = (b, query head).  The segments of
+// a head split its selected entries (the concatenation of all its lists, in
+// list order) into equal ranges, so a head whose selection grew between
+// refreshes is spread evenly over its workgroups.  M is the head's largest
+// selected logit (from the list maxima), the same in every segment.
 template <int D>
 __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
 {
@@ -176,8 +204,9 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
     constexpr int SLOTS = kBlock / LPR;    // rows per workgroup load instruction
     constexpr int CAPL = 2048;             // entries staged per round
     constexpr int NB = 16;                 // rows in flight per lane
+    constexpr int PER = kMaxListsPerRow / kBlock;
     static_assert(SLOTS * D <= CAPL, "reduction scratch reuses the staging buffer");
-    __shared__ int32_t pre[kBlock + 1];
+    __shared__ int32_t pre[kMaxListsPerRow + 1];
     __shared__ float red[kWavesPerBlock];
     __shared__ uint32_t erow[CAPL];
     __shared__ float ew[CAPL];
@@ -186,44 +215,53 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
     const int bi = blockIdx.y;
     const int b = bi / a.hq, i = bi - b * a.hq;
     const int t = threadIdx.x;
-    const int c0 = seg * a.chunks_per_seg;
-    const int c1 = min(c0 + a.chunks_per_seg, a.chunks);
-    const int nl = (c1 - c0) * kWavesPerBlock;
+    const int nl = a.chunks * kWavesPerBlock;
     const int64_t capw = a.rows_per_chunk / kWavesPerBlock;
-    const int64_t lbase = ((int64_t)bi * a.chunks + c0) * kWavesPerBlock;
+    const int64_t lbase = (int64_t)bi * nl;
 
-    int32_t cnt = 0;
+    // List lengths (prefix) and the head's largest selected logit.
+    int32_t c[PER], sum = 0;
     float mx = -INFINITY;
-    if (t < nl) {
-        cnt = a.list_count[lbase + t];
-        mx = a.list_max[lbase + t];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int l = t * PER + k;
+        c[k] = l < nl ? a.list_count[lbase + l] : 0;
+        sum += c[k];
+        if (l < nl) mx = fmaxf(mx, a.list_max[lbase + l]);
     }
     const float M = block_max(mx, red);
-    // exclusive prefix of list lengths
-    pre[t] = cnt;
+    __shared__ int32_t scan[kBlock];
+    scan[t] = sum;
     __syncthreads();
     for (int off = 1; off < kBlock; off <<= 1) {
-        const int32_t v = t >= off ? pre[t - off] : 0;
+        const int32_t v = t >= off ? scan[t - off] : 0;
         __syncthreads();
-        pre[t] += v;
+        scan[t] += v;
         __syncthreads();
     }
-    const int32_t incl = pre[t];
+    int32_t run = scan[t] - sum;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        pre[t * PER + k] = run;
+        run += c[k];
+    }
+    if (t == kBlock - 1) pre[kMaxListsPerRow] = run;
     __syncthreads();
-    pre[t + 1] = incl;
-    if (t == 0) pre[0] = 0;
-    __syncthreads();
-    const int32_t total = pre[nl];
+    const int32_t total = pre[kMaxListsPerRow];
+    const int32_t e_begin = (int32_t)((int64_t)total * seg / a.segs);
+    const int32_t e_end = (int32_t)((int64_t)total * (seg + 1) / a.segs);
 
     const uint16_t* vh = a.v + ((int64_t)(b * a.hv + i / a.Gv) * a.cache_len) * D;
     const int slot = t / LPR, lc = t - slot * LPR;
+    const float tf = a.tau_filter ? a.tau_filter[bi] : -INFINITY;
     float acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = 0.f;
     float lsum = 0.f;
+    int32_t kept = 0;                                   // entries with logit >= tf
 
-    for (int32_t base = 0; base < total; base += CAPL) {
-        const int n = min(CAPL, total - base);
+    for (int32_t base = e_begin; base < e_end; base += CAPL) {
+        const int n = min(CAPL, e_end - base);
         for (int e = t; e < n; e += kBlock) {
             const int32_t E = base + e;
             int lo = 0, hi = nl - 1;
@@ -232,10 +270,13 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
                 if (pre[mid] <= E) lo = mid;
                 else hi = mid - 1;
             }
-            const int chunk = c0 + lo / kWavesPerBlock;
+            const int chunk = lo / kWavesPerBlock;
             const uint2 ent = a.entries[(lbase + lo) * capw + (E - pre[lo])];
+            const float sv = __uint_as_float(ent.y);
+            const bool keep = sv >= tf;
+            kept += keep;
             erow[e] = (uint32_t)(chunk * a.rows_per_chunk + ent.x);
-            ew[e] = __expf(__uint_as_float(ent.y) - M);
+            ew[e] = keep ? __expf(sv - M) : 0.f;
         }
         __syncthreads();
         for (int e0 = slot; e0 < n; e0 += SLOTS * NB) {
@@ -244,12 +285,11 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
                 const int e = e0 + k * SLOTS;
-                if (e < n) {
+                w[k] = e < n ? ew[e] : 0.f;
+                if (w[k] > 0.f) {             // a zero weight contributes nothing: skip its row
                     vv[k] = ld16(vh + (int64_t)erow[e] * D + 8 * lc);
-                    w[k] = ew[e];
                 } else {
                     vv[k] = u32x4{0u, 0u, 0u, 0u};
-                    w[k] = 0.f;
                 }
             }
 #pragma unroll
@@ -270,9 +310,12 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
 #pragma unroll
     for (int j = 0; j < 8; ++j) ored[slot * D + 8 * lc + j] = acc[j];
     if (lc == 0) ew[slot] = lsum;
+    scan[t] = kept;
     __syncthreads();
     float l = 0.f;
     for (int s = 0; s < SLOTS; ++s) l += ew[s];
+    int32_t nkept = 0;
+    for (int s = 0; s < kBlock; ++s) nkept += scan[s];
     const int64_t idx = (int64_t)bi * a.segs + seg;
     for (int p = t; p < D; p += kBlock) {
         float o = 0.f;
@@ -280,9 +323,9 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
         a.part.o[idx * D + p] = o;
     }
     if (t == 0) {
-        a.part.m[idx] = M;
+        a.part.m[idx] = nkept > 0 ? M : -INFINITY;
         a.part.l[idx] = l;
-        a.part.c[idx] = total;
+        a.part.c[idx] = nkept;
     }
 }
 
@@ -378,11 +421,14 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
 hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t s)
 {
     const dim3 grid(a.chunks, a.B * a.hk);
-    const size_t lds = (size_t)kWavesPerBlock * a.Gk * stage_cap(decode_unroll(D)) * sizeof(uint2);
-    if (D == 64)
-        hipLaunchKernelGGL((select_stream_kernel<64, decode_unroll(64)>), grid, dim3(kBlock), lds, s, a);
-    else
-        hipLaunchKernelGGL((select_stream_kernel<128, decode_unroll(128)>), grid, dim3(kBlock), lds, s, a);
+    const bool dbg = a.bitmap != nullptr || a.logits_out != nullptr;
+    if (D == 64) {
+        if (dbg) hipLaunchKernelGGL((select_stream_kernel<64, decode_unroll(64), true>), grid, dim3(kBlock), 0, s, a);
+        else hipLaunchKernelGGL((select_stream_kernel<64, decode_unroll(64), false>), grid, dim3(kBlock), 0, s, a);
+    } else {
+        if (dbg) hipLaunchKernelGGL((select_stream_kernel<128, decode_unroll(128), true>), grid, dim3(kBlock), 0, s, a);
+        else hipLaunchKernelGGL((select_stream_kernel<128, decode_unroll(128), false>), grid, dim3(kBlock), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -60,6 +60,19 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p)
 #endif
 }
 
+// Raw buffer resources (gfx9 family, word 3 = 0x00020000): 32-bit offsets from
+// an SGPR base, and loads past `bytes` return zero instead of touching memory.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kBufferWord3);
+}
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 // ------------------------------------------------------------ wave utilities
 // Orders LDS traffic between lanes of one wave (no workgroup barrier).
 __device__ __forceinline__ void wave_sync()
@@ -162,6 +175,22 @@ __device__ __forceinline__ void qk_group(const QFrag<D>& qf, const u32x4 (&kv)[D
             __builtin_bit_cast(bf16x8, qf.v[m]), __builtin_bit_cast(bf16x8, kv[m]), acc, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] = acc[i] * scale;
+}
+
+// Same tile through a buffer resource over one key head's first `rows` rows:
+// row indices past the resource read as zero rows (the caller masks them).
+// Offsets are 32-bit: a key head must be smaller than 2 GiB.
+template <int D, int U>
+__device__ __forceinline__ void load_ktile_buf(KTile<D, U>& t, __amdgpu_buffer_rsrc_t k_head,
+                                               uint32_t row0)
+{
+    const int col = lane_id() & 15, grp = lane_id() >> 4;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t off = (row0 + 16 * u + col) * (uint32_t)(D * 2) + 16 * grp;
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) t.v[u][m] = buf_ld16(k_head, off + 64 * m);
+    }
 }
 
 // logits[u][i] = scale * sum_c q[slot 4*(lane/16)+i][c] * K[row0+16u+lane%16][c]

@@ -34,12 +34,15 @@ constexpr int kSampleMax = 2048;
 constexpr int kFinalStage = 8192;
 constexpr int kMaxListsPerRow = 2048;
 
-// Entries staged per (wave, head slot) in the stream kernel: two tiles' worth.
-constexpr int stage_cap(int U) { return 32 * U; }
+// Entries queued per (wave, head index) in the stream kernel before a flush.
+constexpr int kQueueCap = 256;
 
-// Gather segments: lists (4 per chunk) handled by one gather workgroup.
-constexpr int kMaxListsPerSeg = 256;
-constexpr int kGatherTargetBlocks = 1024;
+// Gather: workgroups per launch we aim for, and the most per (b, query head).
+#ifndef SAGA_GATHER_BLOCKS
+#define SAGA_GATHER_BLOCKS 2048
+#endif
+constexpr int kGatherTargetBlocks = SAGA_GATHER_BLOCKS;
+constexpr int kGatherMaxSegs = 16;
 
 // Stream-select kernel: K stream, threshold mask, compaction into lists.
 // List (b*h_q + i, chunk, wave) holds up to rows_per_chunk/4 entries
@@ -54,6 +57,7 @@ struct SelectStreamArgs {
     int32_t* list_count;     // [B*hq][chunks][4]
     float* list_max;         // [B*hq][chunks][4]  largest selected logit (-inf if none)
     float* logits_out;       // nullable [B*hq][ctx]: every logit, for checking
+    const uint32_t* group_flags;  // nullable [B*hk]: run only key groups flagged non-zero
     int32_t B, hq, hk, Gk;
     int64_t ctx, cache_len, rows_per_chunk;
     int32_t chunks;
@@ -66,10 +70,11 @@ struct GatherArgs {
     const uint2* entries;
     const int32_t* list_count;
     const float* list_max;
+    const float* tau_filter; // nullable [B*hq]: keep only entries with logit >= tau_filter
     Partials part;           // one partial per (b*h_q + i, segment)
     int32_t B, hq, hv, Gv;
     int64_t cache_len, rows_per_chunk;
-    int32_t chunks, chunks_per_seg, segs;
+    int32_t chunks, segs;    // segs: equal entry ranges per (b, query head)
 };
 
 // Refresh steps 1-2: sampled logits and the per-row pivot.
@@ -78,6 +83,7 @@ struct SampleArgs {
     const uint16_t* k;
     float* sample;           // [B*hq][kSampleMax]
     float* pivot;            // [B*hq]
+    uint32_t* group_flags;   // nullable [B*hk]: cleared here
     int32_t B, hq, hk, Gk;
     int64_t cache_len, stride;   // one 16-row sample block every `stride` rows
     int32_t m, rank;             // sample size, rank of the pivot within the sample
@@ -91,6 +97,7 @@ struct FinalArgs {
     const uint2* entries;
     const int32_t* list_count;
     float* tau;              // [B*hq] out
+    uint32_t* group_flags;   // nullable [B*hk]: set when a row of the group used the recompute path
     int32_t B, hq, hk, Gk;
     int64_t ctx, cache_len, rows_per_chunk;
     int32_t chunks;

@@ -162,7 +162,13 @@ __global__ __launch_bounds__(kBlock) void pivot_kernel(SampleArgs a)
     for (int k = threadIdx.x; k < a.m; k += kBlock) keys[k] = float_key(s[k]);
     __syncthreads();
     const uint32_t key = lds_radix_select(keys, (uint32_t)a.m, (uint32_t)a.rank, w);
-    if (threadIdx.x == 0) a.pivot[row] = key_float(key);
+    if (threadIdx.x == 0) {
+        a.pivot[row] = key_float(key);
+        if (a.group_flags) {
+            const int b = row / a.hq;
+            a.group_flags[b * a.hk + (row - b * a.hq) / a.Gk] = 0u;
+        }
+    }
 }
 
 // Exact N-th largest of one row by recomputing its logits (three radix passes
@@ -276,6 +282,11 @@ __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
         key = lds_radix_select(keys, total, a.top_n, w);
     } else {
         key = select_by_recompute<D, U>(a, row, w);
+        // The lists miss entries of this row: a fused decode must re-stream its group.
+        if (t == 0 && a.group_flags) {
+            const int b = row / a.hq;
+            a.group_flags[b * a.hk + (row - b * a.hq) / a.Gk] = 1u;
+        }
     }
     if (t == 0) a.tau[row] = key_float(key);
 }

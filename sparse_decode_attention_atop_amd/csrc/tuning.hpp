@@ -3,10 +3,10 @@
 
 // Compile-time tuning constants (defaults are the measured best on MI355X).
 #ifndef SAGA_STREAM_U64
-#define SAGA_STREAM_U64 4            // 16-row K groups per wave tile, head_dim 64
+#define SAGA_STREAM_U64 2            // 16-row K groups per wave tile, head_dim 64
 #endif
 #ifndef SAGA_STREAM_U128
-#define SAGA_STREAM_U128 2           // same, head_dim 128
+#define SAGA_STREAM_U128 1           // same, head_dim 128
 #endif
 #ifndef SAGA_K_NONTEMPORAL
 #define SAGA_K_NONTEMPORAL 0         // stream K with non-temporal loads

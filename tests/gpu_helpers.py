@@ -62,6 +62,44 @@ def run_atopn(q, K, V, ctx_steps, top_n, refresh_n, scale=1.0, logits_every_step
     return res
 
 
+def run_fused(q, K, V, ctx_steps, top_n, refresh_n, scale=1.0):
+    """Atop-N over len(ctx_steps) steps with the one-call refresh step
+    (atopn_refresh_decode_step) at t mod n == 0 and saga_decode_step between.
+
+    Returns per-step lists: tau (float32 [B][hq]), counts, out (float32).
+    """
+    T, B, hq, d = q.shape
+    hk, rows = K.shape[1], K.shape[2]
+    hv = V.shape[1]
+    dev = q.device
+    ws = saga.alloc_workspace(saga.dims(B, hq, hk, hv, d, ctx_steps[0], rows, scale), top_n, dev)
+    tau = torch.empty(B, hq, dtype=torch.float32, device=dev)
+    res = {"tau": [], "counts": [], "out": []}
+    for t, ctx in enumerate(ctx_steps):
+        dm = saga.dims(B, hq, hk, hv, d, ctx, rows, scale)
+        out = torch.empty(B, hq, d, dtype=torch.bfloat16, device=dev)
+        cnt = torch.empty(B, hq, dtype=torch.int32, device=dev)
+        if t % refresh_n == 0:
+            saga.atopn_refresh_decode_step(dm, top_n, q[t], K, V, tau, out, ws, sel_counts=cnt)
+        else:
+            saga.saga_decode_step(dm, q[t], K, V, tau, out, ws, sel_counts=cnt)
+        torch.cuda.synchronize()
+        res["tau"].append(tau.cpu().numpy().copy())
+        res["counts"].append(cnt.cpu().numpy())
+        res["out"].append(bf16_to_f32(out))
+    return res
+
+
+def sampled_rows(ctx: int) -> np.ndarray:
+    """Rows the threshold refresh reads to place its pivot: 16-row blocks, one
+    every `stride` rows (a multiple of 16), at most 128 blocks."""
+    if ctx <= 2048:
+        return np.arange(ctx)
+    stride = -(-(ctx // 16) // 128) * 16
+    starts = np.arange(ctx // stride) * stride
+    return (starts[:, None] + np.arange(16)[None, :]).ravel()
+
+
 def bitmap_to_bool(bm: np.ndarray, ctx: int) -> np.ndarray:
     """[..., words] uint32 -> [..., ctx] bool."""
     bits = np.unpackbits(bm.view(np.uint8), axis=-1, bitorder="little")

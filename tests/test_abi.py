@@ -83,6 +83,14 @@ def call_refresh(d, top_n, ws_bytes, **ptrs):
                                                    p["tau"], p["dbg"], p["ws"], ws_bytes, None)
 
 
+def call_fused(d, top_n, ws_bytes, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, tau=FAKE, out=FAKE, counts=None, ws=FAKE)
+    p.update(ptrs)
+    return saga.library().atopn_refresh_decode_step(ctypes.byref(d), top_n, p["q"], p["k"],
+                                                    p["v"], p["tau"], p["out"], p["counts"],
+                                                    p["ws"], ws_bytes, None)
+
+
 def call_full(d, ws_bytes, **ptrs):
     p = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, ws=FAKE)
     p.update(ptrs)
@@ -103,6 +111,7 @@ def test_dims_errors_every_entry_point(bad, code):
     d = good_dims(**bad)
     assert call_decode(d, 1 << 40) == code
     assert call_refresh(d, 8, 1 << 40) == code
+    assert call_fused(d, 8, 1 << 40) == code
     assert call_full(d, 1 << 40) == code
 
 
@@ -125,6 +134,11 @@ def test_refresh_null_pointers(name):
     assert call_refresh(good_dims(), 8, 1 << 40, **{name: None}) == INVALID
 
 
+@pytest.mark.parametrize("name", ["q", "k", "v", "tau", "out", "ws"])
+def test_fused_null_pointers(name):
+    assert call_fused(good_dims(), 8, 1 << 40, **{name: None}) == INVALID
+
+
 @pytest.mark.parametrize("name", ["q", "k", "v", "out", "ws"])
 def test_full_null_pointers(name):
     assert call_full(good_dims(), 1 << 40, **{name: None}) == INVALID
@@ -135,6 +149,7 @@ def test_misaligned_pointers():
     assert call_decode(good_dims(), 1 << 40, k=odd) == INVALID
     assert call_refresh(good_dims(), 8, 1 << 40, q=odd) == INVALID
     assert call_full(good_dims(), 1 << 40, v=odd) == INVALID
+    assert call_fused(good_dims(), 8, 1 << 40, v=odd) == INVALID
     assert call_decode(good_dims(), 1 << 40, counts=ctypes.c_void_p((1 << 20) + 2)) == INVALID
 
 
@@ -142,9 +157,11 @@ def test_top_n_and_workspace_errors():
     d = good_dims()
     assert call_refresh(d, 0, 1 << 40) == INVALID
     assert call_refresh(d, -5, 1 << 40) == INVALID
+    assert call_fused(d, 0, 1 << 40) == INVALID
     need = saga.saga_workspace_bytes(d, 8)
     assert call_decode(d, need - 1) == SMALL
     assert call_refresh(d, 8, need - 1) == SMALL
+    assert call_fused(d, 8, need - 1) == SMALL
     assert call_full(d, need - 1) == SMALL
 
 

@@ -18,7 +18,7 @@ import oracle
 import saga_workload as wl
 import sparse_decode_attention_atop_amd as saga
 from gpu_helpers import (bitmap_to_bool, logit_tolerance, make_inputs, nth_largest_f32,
-                         run_atopn, to_np_bits)
+                         run_atopn, run_fused, sampled_rows, to_np_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -240,16 +240,24 @@ def _check_refresh_exact(q, K, V, ctx, N):
     return gpu
 
 
+def _misleading_sample(ctx, N, seed):
+    """Inputs whose pivot sample sees only the highest logits: every row the
+    sampler reads scores 1.0 against q, every other row about 0.05, and fewer
+    than N rows score high, so the pivot leaves fewer than N candidates."""
+    q, K, V = make_inputs(1, 4, 1, 2, 64, ctx, 1, seed=seed, heavy=False)
+    rows = sampled_rows(ctx)
+    assert rows.size < N
+    K.mul_(0.05)
+    K[:, :, torch.from_numpy(rows).cuda(), :] = 1.0
+    q.fill_(0.1)
+    return q, K, V
+
+
 def test_refresh_exact_when_the_sample_misleads():
-    """Every sampled row (a multiple of the sample stride) outscores the rest,
-    so the sample pivot leaves fewer than N candidates: the exact recompute
+    """The sample pivot leaves fewer than N candidates: the exact recompute
     path must still return the N-th largest logit."""
     ctx, N = 40000, 5000
-    stride = -(-ctx // 4096)
-    q, K, V = make_inputs(1, 4, 1, 2, 64, ctx, 1, seed=46, heavy=False)
-    K.mul_(0.05)
-    K[:, :, ::stride, :] = 1.0
-    q.fill_(0.1)
+    q, K, V = _misleading_sample(ctx, N, seed=46)
     gpu = _check_refresh_exact(q, K, V, ctx, N)
     assert (gpu["counts"][0] >= N).all()
 
@@ -267,3 +275,60 @@ def test_refresh_exact_at_long_context():
     """128K-row context (sampled pivot path), Qwen-like group of 12 heads."""
     q, K, V = make_inputs(1, 12, 1, 2, 128, 131072 + 2, 1, seed=48)
     _check_refresh_exact(q, K, V, 131072, 1024)
+
+
+# ---- one-call refresh step (atopn_refresh_decode_step) ----------------------
+
+def _check_fused_against_separate(q, K, V, ctx_steps, N, n):
+    """Same thresholds (bit-equal) and counts as refresh + decode called one
+    after the other, and outputs within the bar of the oracle on that mask."""
+    sep = run_atopn(q, K, V, ctx_steps, N, n, logits_every_step=False)
+    fus = run_fused(q, K, V, ctx_steps, N, n)
+    qb, Kb, Vb = to_np_bits(q), to_np_bits(K), to_np_bits(V)
+    for t, ctx in enumerate(ctx_steps):
+        assert np.array_equal(fus["tau"][t].view(np.uint32), sep["tau"][t].view(np.uint32)), t
+        assert np.array_equal(fus["counts"][t], sep["counts"][t]), t
+        ref, _ = oracle.masked(qb[t], Kb, Vb, ctx, sep["bitmap"][t])
+        err = np.abs(fus["out"][t] - ref).max()
+        assert err <= OUT_TOL, f"step {t}: max abs err {err:.3e}"
+    return fus
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen_like_small", "group16_d64", "mha_d128",
+                                  "fewer_value_heads", "gqa_llama_small", "short_ctx"])
+def test_fused_refresh_step_matches_separate_calls(name):
+    c = CASES[name]
+    if isinstance(c, wl.Workload):
+        x = wl.make_layer(c, 0, device="cuda")
+        q, K, V = x["q"], x["K"], x["V"]
+        N, n, T, L = c.top_n, c.refresh_n, c.steps, c.L
+    else:
+        B, hq, hk, hv, d, L, T, N, n = c
+        q, K, V = make_inputs(B, hq, hk, hv, d, L + T, T, seed=70 + len(name))
+    _check_fused_against_separate(q, K, V, [L + t for t in range(T)], N, n)
+
+
+def test_fused_refresh_step_when_the_sample_misleads():
+    """Rows that took the recompute path have incomplete candidate lists; the
+    fused step streams their key group again with the fresh thresholds."""
+    ctx, N = 40000, 5000
+    q, K, V = _misleading_sample(ctx, N, seed=49)
+    _check_fused_against_separate(q, K, V, [ctx], N, 1)
+
+
+def test_fused_refresh_step_ties_beyond_staging():
+    q, K, V = make_inputs(1, 4, 1, 2, 128, 20000, 1, seed=50)
+    K.zero_()
+    fus = _check_fused_against_separate(q, K, V, [20000], 700, 1)
+    assert (fus["counts"][0] == 20000).all()
+
+
+def test_fused_refresh_step_n_covering_context():
+    q, K, V = make_inputs(2, 12, 1, 2, 128, 1300, 2, seed=51)
+    fus = _check_fused_against_separate(q, K, V, [1290, 1300], 5000, 1)
+    assert all(np.isneginf(tau).all() for tau in fus["tau"])
+
+
+def test_fused_refresh_step_at_long_context():
+    q, K, V = make_inputs(1, 12, 1, 2, 128, 131072 + 2, 2, seed=52)
+    _check_fused_against_separate(q, K, V, [131072, 131073], 1024, 2)
