@@ -16,7 +16,15 @@ using namespace saga;
 
 namespace {
 
-constexpr int kTargetBlocks = SAGA_TARGET_BLOCKS;
+// Workgroups per K-stream launch: the stream kernel keeps three workgroups on
+// a CU, and measured on MI355X a launch of about one such round for head_dim
+// 128, or a bit over one for head_dim 64, streams fastest.
+constexpr int64_t kFullTargetBlocks = 2048;   // dense kernel: workgroups per launch
+
+int64_t target_blocks(int head_dim)
+{
+    return head_dim == 128 ? SAGA_TARGET_BLOCKS128 : SAGA_TARGET_BLOCKS64;
+}
 constexpr int64_t kMaxCacheLen = int64_t(1) << 27;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -47,11 +55,13 @@ struct Chunking {
     int64_t rows;
 };
 
-// Split ctx rows into chunks of whole block tiles so that the launch has about
-// kTargetBlocks workgroups and never more chunks than the workspace holds.
-Chunking plan_chunks(int64_t ctx, int64_t pairs, int64_t block_rows, int max_chunks)
+// Split ctx rows into chunks of whole block tiles (block_rows each) so that the
+// launch has about `target` workgroups and never more chunks than the
+// workspace holds.
+Chunking split_rows(int64_t ctx, int64_t pairs, int64_t block_rows, int64_t target,
+                    int max_chunks)
 {
-    int64_t want = kTargetBlocks / pairs;
+    int64_t want = target / pairs;
     if (want < 1) want = 1;
     int64_t c = (ctx + block_rows - 1) / block_rows;
     if (c > want) c = want;
@@ -60,6 +70,12 @@ Chunking plan_chunks(int64_t ctx, int64_t pairs, int64_t block_rows, int max_chu
     int64_t rows = (ctx + c - 1) / c;
     rows = (rows + block_rows - 1) / block_rows * block_rows;
     return {(int)((ctx + rows - 1) / rows), rows};
+}
+
+// Chunking of the K stream (stream-select kernel) for one call.
+Chunking plan_chunks(int64_t ctx, int64_t pairs, int head_dim, int max_chunks)
+{
+    return split_rows(ctx, pairs, decode_block_rows(head_dim), target_blocks(head_dim), max_chunks);
 }
 
 // Workspace layout (byte offsets), identical for every ctx_len <= cache_len.
@@ -73,7 +89,9 @@ Layout make_layout(const saga_dims* d)
 {
     Layout L{};
     const size_t rows = (size_t)d->batch * d->h_q;
-    const int64_t want = kTargetBlocks / ((int64_t)d->batch * d->h_k);
+    const int64_t target = target_blocks(d->head_dim) > kFullTargetBlocks
+                               ? target_blocks(d->head_dim) : kFullTargetBlocks;
+    const int64_t want = target / ((int64_t)d->batch * d->h_k);
     const int64_t by_len = (d->cache_len + 127) / 128;   // smallest block tile is 128 rows
     int64_t mc = want < by_len ? want : by_len;
     if (mc > kMaxListsPerRow / kWavesPerBlock) mc = kMaxListsPerRow / kWavesPerBlock;   // 512
@@ -81,7 +99,7 @@ Layout make_layout(const saga_dims* d)
     // chunks * rows_per_chunk <= ctx + rows_per_chunk(ctx), and rows_per_chunk
     // never exceeds max(block rows, its value at ctx = cache_len).
     const int64_t br = decode_block_rows(d->head_dim);
-    const Chunking top = plan_chunks(d->cache_len, (int64_t)d->batch * d->h_k, br, L.max_chunks);
+    const Chunking top = plan_chunks(d->cache_len, (int64_t)d->batch * d->h_k, d->head_dim, L.max_chunks);
     L.entry_rows = d->cache_len + (top.rows > br ? top.rows : br);
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes, 256); return o; };
@@ -274,7 +292,7 @@ int enqueue_decode(const saga_dims* dims, const Layout& L, const void* q_dev,
         if (st != SAGA_OK) return st;
     }
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
-                                    decode_block_rows(D), L.max_chunks);
+                                    D, L.max_chunks);
     SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, thresholds_dev, workspace_dev);
     a.bitmap = sel_bitmap_debug_dev;
     a.bitmap_words = words;
@@ -306,7 +324,7 @@ SAGA_EXPORT int atopn_refresh_thresholds(const saga_dims* dims, int32_t top_n, c
     const int D = dims->head_dim;
     const int rows = dims->batch * dims->h_q;
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
-                                    decode_block_rows(D), L.max_chunks);
+                                    D, L.max_chunks);
     if ((int64_t)top_n >= dims->ctx_len) {
         // N >= ctx: every entry is kept, tau = -inf.  The logits are still
         // produced when asked for (a pass that selects nothing).
@@ -377,7 +395,7 @@ SAGA_EXPORT int atopn_refresh_decode_step(const saga_dims* dims, int32_t top_n, 
                               sel_counts_dev, nullptr, workspace_dev, s);
     }
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
-                                    decode_block_rows(D), L.max_chunks);
+                                    D, L.max_chunks);
     uint32_t* flags = reinterpret_cast<uint32_t*>(w + L.flags);
     st = enqueue_refresh(dims, top_n, q_dev, k_cache_dev, thresholds_dev, nullptr, workspace_dev,
                          L, ch, s, flags);
@@ -429,8 +447,8 @@ SAGA_EXPORT int saga_full_attention(const saga_dims* dims, const void* q_dev,
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t block_rows = (int64_t)kWavesPerBlock * 16 * full_unroll(D);
-    const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k, block_rows,
-                                    L.max_chunks);
+    const Chunking ch = split_rows(dims->ctx_len, (int64_t)dims->batch * dims->h_k, block_rows,
+                                   kFullTargetBlocks, L.max_chunks);
     FullArgs a{};
     a.q = static_cast<const uint16_t*>(q_dev);
     a.k = static_cast<const uint16_t*>(k_cache_dev);

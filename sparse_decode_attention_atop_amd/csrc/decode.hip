@@ -40,7 +40,7 @@ namespace {
 // per-(head, chunk, wave) lists in order.  DEBUG adds the optional logits and
 // selection-bitmap outputs.
 template <int D, int U, bool DEBUG>
-__global__ __launch_bounds__(kBlock) void select_stream_kernel(SelectStreamArgs a)
+__global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(SelectStreamArgs a)
 {
     __shared__ uint2 queue[kWavesPerBlock][4][kQueueCap];
     const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kBlock) void select_stream_kernel(SelectStreamArgs 
     }
 }
 
-// Block-wide (256 threads) max and exclusive prefix sum.
+// Block-wide (256 threads) reductions and scan.  `red` holds one value per wave.
 __device__ float block_max(float v, float* red)
 {
     for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -192,23 +192,60 @@ __device__ float block_max(float v, float* red)
     return v;
 }
 
+__device__ int32_t block_sum(int32_t v, int32_t* red)
+{
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (lane_id() == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+    return v;
+}
+
+// Inclusive prefix sum over the block in thread order.
+__device__ int32_t block_scan(int32_t v, int32_t* red)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int32_t u = __shfl_up(v, off);
+        if (lane >= off) v += u;
+    }
+    if (lane == kWave - 1) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const int w = threadIdx.x >> 6;
+    int32_t add = 0;
+#pragma unroll
+    for (int k = 0; k < kWavesPerBlock - 1; ++k) add += k < w ? red[k] : 0;
+    __syncthreads();
+    return v + add;
+}
+
 // Gather kernel: grid.x = segment, grid.y = (b, query head).  The segments of
 // a head split its selected entries (the concatenation of all its lists, in
 // list order) into equal ranges, so a head whose selection grew between
 // refreshes is spread evenly over its workgroups.  M is the head's largest
 // selected logit (from the list maxima), the same in every segment.
+//
+// Value rows are read with buffer loads at 32-bit byte offsets inside one
+// value head (under 2 GiB); entries that carry no weight get an offset past
+// the resource's end, which reads zero without touching memory, so the loads
+// need no branch.
 template <int D>
-__global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
+__global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherArgs a)
 {
     constexpr int LPR = D / 8;             // lanes per value row (16 bytes each)
     constexpr int SLOTS = kBlock / LPR;    // rows per workgroup load instruction
-    constexpr int CAPL = 2048;             // entries staged per round
-    constexpr int NB = 16;                 // rows in flight per lane
+    constexpr int CAPL = kGatherStage;     // entries staged per round
+    constexpr int EPT = CAPL / kBlock;     // staged entries per thread
+    constexpr int NB = SAGA_GATHER_NB;     // rows in flight per lane
     constexpr int PER = kMaxListsPerRow / kBlock;
-    static_assert(SLOTS * D <= CAPL, "reduction scratch reuses the staging buffer");
+    constexpr uint32_t kNoRow = 0x80000000u;   // past any value head (< 2^31 bytes)
+    static_assert(SLOTS * D <= kMaxListsPerRow, "slot reduction reuses the prefix array");
+    static_assert(CAPL % kBlock == 0, "staging rounds are whole threads");
     __shared__ int32_t pre[kMaxListsPerRow + 1];
-    __shared__ float red[kWavesPerBlock];
-    __shared__ uint32_t erow[CAPL];
+    __shared__ int32_t red[kWavesPerBlock];
+    __shared__ uint32_t eoff[CAPL];
     __shared__ float ew[CAPL];
 
     const int seg = blockIdx.x;
@@ -229,17 +266,8 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
         sum += c[k];
         if (l < nl) mx = fmaxf(mx, a.list_max[lbase + l]);
     }
-    const float M = block_max(mx, red);
-    __shared__ int32_t scan[kBlock];
-    scan[t] = sum;
-    __syncthreads();
-    for (int off = 1; off < kBlock; off <<= 1) {
-        const int32_t v = t >= off ? scan[t - off] : 0;
-        __syncthreads();
-        scan[t] += v;
-        __syncthreads();
-    }
-    int32_t run = scan[t] - sum;
+    const float M = block_max(mx, reinterpret_cast<float*>(red));
+    int32_t run = block_scan(sum, red) - sum;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         pre[t * PER + k] = run;
@@ -252,6 +280,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
     const int32_t e_end = (int32_t)((int64_t)total * (seg + 1) / a.segs);
 
     const uint16_t* vh = a.v + ((int64_t)(b * a.hv + i / a.Gv) * a.cache_len) * D;
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh, (uint32_t)(a.cache_len * D * 2));
     const int slot = t / LPR, lc = t - slot * LPR;
     const float tf = a.tau_filter ? a.tau_filter[bi] : -INFINITY;
     float acc[8];
@@ -262,21 +291,32 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
 
     for (int32_t base = e_begin; base < e_end; base += CAPL) {
         const int n = min(CAPL, e_end - base);
-        for (int e = t; e < n; e += kBlock) {
-            const int32_t E = base + e;
-            int lo = 0, hi = nl - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (pre[mid] <= E) lo = mid;
+        int lo[EPT];
+        uint2 ent[EPT];
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {                 // all entry loads before any use
+            const int32_t E = base + t + k * kBlock;
+            int l0 = 0, hi = nl - 1;
+            while (l0 < hi) {
+                const int mid = (l0 + hi + 1) >> 1;
+                if (pre[mid] <= E) l0 = mid;
                 else hi = mid - 1;
             }
-            const int chunk = lo / kWavesPerBlock;
-            const uint2 ent = a.entries[(lbase + lo) * capw + (E - pre[lo])];
-            const float sv = __uint_as_float(ent.y);
-            const bool keep = sv >= tf;
-            kept += keep;
-            erow[e] = (uint32_t)(chunk * a.rows_per_chunk + ent.x);
-            ew[e] = keep ? __expf(sv - M) : 0.f;
+            lo[k] = l0;
+            ent[k] = t + k * kBlock < n ? a.entries[(lbase + l0) * capw + (E - pre[l0])]
+                                        : uint2{0u, 0xff800000u};
+        }
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const int e = t + k * kBlock;
+            if (e < n) {
+                const float sv = __uint_as_float(ent[k].y);
+                const bool keep = sv >= tf;
+                kept += keep;
+                const uint32_t r = (uint32_t)((lo[k] / kWavesPerBlock) * a.rows_per_chunk) + ent[k].x;
+                eoff[e] = keep ? r * (uint32_t)(D * 2) : kNoRow;
+                ew[e] = keep ? __expf(sv - M) : 0.f;
+            }
         }
         __syncthreads();
         for (int e0 = slot; e0 < n; e0 += SLOTS * NB) {
@@ -285,12 +325,9 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
                 const int e = e0 + k * SLOTS;
-                w[k] = e < n ? ew[e] : 0.f;
-                if (w[k] > 0.f) {             // a zero weight contributes nothing: skip its row
-                    vv[k] = ld16(vh + (int64_t)erow[e] * D + 8 * lc);
-                } else {
-                    vv[k] = u32x4{0u, 0u, 0u, 0u};
-                }
+                const bool in = e < n;
+                w[k] = in ? ew[e] : 0.f;
+                vv[k] = buf_ld16(vrs, (in ? eoff[e] : kNoRow) + 16u * lc);
             }
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
@@ -306,16 +343,11 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
     }
 
     // Reduce the slots in slot order.
-    float* ored = reinterpret_cast<float*>(erow);       // [SLOTS][D]
+    float* ored = reinterpret_cast<float*>(pre);        // [SLOTS][D]
 #pragma unroll
     for (int j = 0; j < 8; ++j) ored[slot * D + 8 * lc + j] = acc[j];
     if (lc == 0) ew[slot] = lsum;
-    scan[t] = kept;
-    __syncthreads();
-    float l = 0.f;
-    for (int s = 0; s < SLOTS; ++s) l += ew[s];
-    int32_t nkept = 0;
-    for (int s = 0; s < kBlock; ++s) nkept += scan[s];
+    const int32_t nkept = block_sum(kept, red);         // its barrier orders the stores above
     const int64_t idx = (int64_t)bi * a.segs + seg;
     for (int p = t; p < D; p += kBlock) {
         float o = 0.f;
@@ -323,6 +355,8 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a)
         a.part.o[idx * D + p] = o;
     }
     if (t == 0) {
+        float l = 0.f;
+        for (int s = 0; s < SLOTS; ++s) l += ew[s];
         a.part.m[idx] = nkept > 0 ? M : -INFINITY;
         a.part.l[idx] = l;
         a.part.c[idx] = nkept;

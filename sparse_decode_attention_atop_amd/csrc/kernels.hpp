@@ -43,6 +43,7 @@ constexpr int kQueueCap = 256;
 #endif
 constexpr int kGatherTargetBlocks = SAGA_GATHER_BLOCKS;
 constexpr int kGatherMaxSegs = 16;
+constexpr int kGatherStage = 1024;   // entries a gather workgroup stages per round
 
 // Stream-select kernel: K stream, threshold mask, compaction into lists.
 // List (b*h_q + i, chunk, wave) holds up to rows_per_chunk/4 entries

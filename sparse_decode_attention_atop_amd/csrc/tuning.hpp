@@ -11,6 +11,28 @@
 #ifndef SAGA_K_NONTEMPORAL
 #define SAGA_K_NONTEMPORAL 0         // stream K with non-temporal loads
 #endif
-#ifndef SAGA_TARGET_BLOCKS
-#define SAGA_TARGET_BLOCKS 2048      // workgroups per stream launch (256 CUs)
+#ifndef SAGA_TARGET_BLOCKS64
+#define SAGA_TARGET_BLOCKS64 1024    // workgroups per K-stream launch, head_dim 64
+#endif
+#ifndef SAGA_TARGET_BLOCKS128
+#define SAGA_TARGET_BLOCKS128 512    // same, head_dim 128
+#endif
+#ifndef SAGA_GATHER_NB
+#define SAGA_GATHER_NB 8             // value rows in flight per lane in the gather
+#endif
+#ifndef SAGA_GATHER_WAVES
+#define SAGA_GATHER_WAVES 0          // >0: ask for that many waves per SIMD (gather)
+#endif
+#ifndef SAGA_STREAM_WAVES
+#define SAGA_STREAM_WAVES 0          // >0: ask for that many waves per SIMD (K stream)
+#endif
+#if SAGA_GATHER_WAVES > 0
+#define SAGA_GATHER_ATTR __attribute__((amdgpu_waves_per_eu(SAGA_GATHER_WAVES)))
+#else
+#define SAGA_GATHER_ATTR
+#endif
+#if SAGA_STREAM_WAVES > 0
+#define SAGA_STREAM_ATTR __attribute__((amdgpu_waves_per_eu(SAGA_STREAM_WAVES)))
+#else
+#define SAGA_STREAM_ATTR
 #endif
