@@ -252,7 +252,7 @@ int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunkin
     const int D = dims->head_dim;
     const int rows = dims->batch * dims->h_q;
     // Each (b, query head) gets `segs` gather workgroups that split its selected
-    // entries evenly: about kGatherTargetBlocks workgroups in all.
+    // entries evenly: about gather_target_blocks(D) workgroups in all.
     GatherArgs ga{};
     ga.v = static_cast<const uint16_t*>(v_cache_dev);
     ga.entries = reinterpret_cast<const uint2*>(w + L.entries);
@@ -267,7 +267,7 @@ int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunkin
     ga.cache_len = dims->cache_len;
     ga.rows_per_chunk = ch.rows;
     ga.chunks = ch.chunks;
-    int64_t segs = (kGatherTargetBlocks + rows - 1) / rows;
+    int64_t segs = (gather_target_blocks(D) + rows - 1) / rows;
     if (segs > kGatherMaxSegs) segs = kGatherMaxSegs;
     if (segs > L.max_chunks) segs = L.max_chunks;       // partials hold max_chunks per row
     ga.segs = (int)segs;

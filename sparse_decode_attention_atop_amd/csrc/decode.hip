@@ -43,13 +43,16 @@ template <int D, int U, bool DEBUG>
 __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(SelectStreamArgs a)
 {
     __shared__ uint2 queue[kWavesPerBlock][4][kQueueCap];
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    // The wave index is uniform within a wave; saying so keeps the row
+    // bookkeeping and the loop exit scalar (a vector loop exit makes the
+    // compiler wait for every K load in flight on each trip).
+    const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15, grp = lane >> 4;
     const int chunk = blockIdx.x;
     const int b = blockIdx.y / a.hk, g = blockIdx.y - b * a.hk;
     const int Gk = a.Gk;
     const int64_t r0 = (int64_t)chunk * a.rows_per_chunk;
-    const int64_t r1 = min(r0 + a.rows_per_chunk, a.ctx);
+    const int64_t r1 = wave_uniform(min(r0 + a.rows_per_chunk, a.ctx));
     const int64_t capw = a.rows_per_chunk / kWavesPerBlock;
     const int qh0 = b * a.hq + g * Gk;
     uint2 (*q4)[kQueueCap] = queue[wave];
@@ -95,11 +98,19 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
             qn[i] = 0;
         }
         wave_sync();
+        // Let the stores finish (vmcnt(0)) before leaving this rare path: the
+        // code after it then starts from a known-empty store state, and the
+        // compiler needs no full wait on the common path where the merged
+        // state would otherwise be unknown (it would drain the K prefetch).
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     };
 
     // A tile adds at most 64*U entries to a queue: flush before one can overflow.
     auto maybe_flush = [&]() {
-        if (max(max(qn[0], qn[1]), max(qn[2], qn[3])) > kQueueCap - kWave * U) flush_all();
+        // Four scalar compares: no vector temporaries that could alias the
+        // registers of a K tile still in flight (that would force a wait).
+        constexpr int lim = kQueueCap - kWave * U;
+        if (((lim - qn[0]) | (lim - qn[1]) | (lim - qn[2]) | (lim - qn[3])) < 0) flush_all();
     };
 
     auto process = [&](const KTile<D, U>& kt, int64_t t0) {
@@ -151,19 +162,25 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
     constexpr int64_t kStep = kWavesPerBlock * 16 * U;
     int64_t t0 = r0 + wave * 16 * U;
     if (t0 < r1) {
+        // This lane's byte offset in tile t0, advanced one tile pair per trip.
+        constexpr uint32_t kStepBytes = (uint32_t)(kStep * D * 2);
+        uint32_t koff = (uint32_t)(t0 + col) * (uint32_t)(D * 2) + 16u * grp;
+        // Tiles go in pairs and the loop leaves only at the bottom: a second
+        // tile past r1 reads zeros and all its rows are masked, which costs at
+        // most one tile per wave and keeps a single, scalar loop exit (an exit
+        // between the tiles makes the compiler drain the prefetch every trip).
         KTile<D, U> ka, kb;
-        load_ktile_buf<D, U>(ka, khead, (uint32_t)t0);
-        while (true) {
+        load_ktile_at<D, U>(ka, khead, koff);
+        do {
             maybe_flush();
-            load_ktile_buf<D, U>(kb, khead, (uint32_t)(t0 + kStep));
+            load_ktile_at<D, U>(kb, khead, koff + kStepBytes);
             process(ka, t0);
-            if (t0 + kStep >= r1) break;
             maybe_flush();
-            load_ktile_buf<D, U>(ka, khead, (uint32_t)(t0 + 2 * kStep));
+            load_ktile_at<D, U>(ka, khead, koff + 2 * kStepBytes);
             process(kb, t0 + kStep);
-            if (t0 + 2 * kStep >= r1) break;
             t0 += 2 * kStep;
-        }
+            koff += 2 * kStepBytes;
+        } while (t0 < r1);
     }
     flush_all();
 #pragma unroll

@@ -73,6 +73,10 @@ __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt = 0 only:
+// vmcnt bits [3:0] and [15:14] zero, expcnt [6:4] = 7, lgkmcnt [11:8] = 15.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // ------------------------------------------------------------ wave utilities
 // Orders LDS traffic between lanes of one wave (no workgroup barrier).
 __device__ __forceinline__ void wave_sync()
@@ -83,6 +87,15 @@ __device__ __forceinline__ void wave_sync()
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// A value the caller knows is the same in every lane, moved to scalar
+// registers so that branches on it stay scalar.
+__device__ __forceinline__ int64_t wave_uniform(int64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // Number of set bits of `mask` in lanes below this one.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask)
@@ -191,6 +204,21 @@ __device__ __forceinline__ void load_ktile_buf(KTile<D, U>& t, __amdgpu_buffer_r
 #pragma unroll
         for (int m = 0; m < D / 32; ++m) t.v[u][m] = buf_ld16(k_head, off + 64 * m);
     }
+}
+
+// Same tile, given this lane's byte offset of its first 16 bytes in the tile
+// (row0 + lane%16) * 2D + 16*(lane/16): the U x D/32 loads then differ by
+// compile-time constants that fit the instruction's immediate offset field, so
+// a tile costs no per-load address arithmetic.
+template <int D, int U>
+__device__ __forceinline__ void load_ktile_at(KTile<D, U>& t, __amdgpu_buffer_rsrc_t k_head,
+                                              uint32_t lane_off)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m)
+            t.v[u][m] = buf_ld16(k_head, lane_off + (uint32_t)(16 * u * D * 2 + 64 * m));
 }
 
 // logits[u][i] = scale * sum_c q[slot 4*(lane/16)+i][c] * K[row0+16u+lane%16][c]

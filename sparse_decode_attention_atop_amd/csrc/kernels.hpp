@@ -38,10 +38,16 @@ constexpr int kMaxListsPerRow = 2048;
 constexpr int kQueueCap = 256;
 
 // Gather: workgroups per launch we aim for, and the most per (b, query head).
-#ifndef SAGA_GATHER_BLOCKS
-#define SAGA_GATHER_BLOCKS 2048
+#ifndef SAGA_GATHER_BLOCKS64
+#define SAGA_GATHER_BLOCKS64 2048
 #endif
-constexpr int kGatherTargetBlocks = SAGA_GATHER_BLOCKS;
+#ifndef SAGA_GATHER_BLOCKS128
+#define SAGA_GATHER_BLOCKS128 1536
+#endif
+constexpr int gather_target_blocks(int head_dim)
+{
+    return head_dim == 128 ? SAGA_GATHER_BLOCKS128 : SAGA_GATHER_BLOCKS64;
+}
 constexpr int kGatherMaxSegs = 16;
 constexpr int kGatherStage = 1024;   // entries a gather workgroup stages per round
 
