@@ -265,32 +265,29 @@ def run_gqa(torch, saga, wl, w, hkv, args):
     return dict(sec=sec, bytes_per_step=per_step_bytes, hkv=hkv)
 
 
-def cpu_baseline(torch, wl, w, layer0):
-    """The fp64 oracle on a bounded sample: layer 0, one refresh step (t=0) and
-    one plain step (t=1), every batch row and query head."""
-    import numpy as np
+def cpu_baseline(torch, wl, w, layers, n_layers=2):
+    """The fp64 oracle on a bounded sample of the same workload: the whole
+    decode run (all w.steps steps, refreshes every w.refresh_n) of the first
+    n_layers layers, every batch row and query head; scaled to steps/s of all
+    w.layers layers."""
     import oracle
-    K = wl.bits(layer0["K"])
-    V = wl.bits(layer0["V"])
-    q = wl.bits(layer0["q"][:2])
     cores = oracle.max_threads()
-    times = []
-    for t in range(2):
+    sample = layers[:n_layers]
+    total = 0.0
+    for x in sample:
+        K, V, q = wl.bits(x["K"]), wl.bits(x["V"]), wl.bits(x["q"])
         t0 = time.perf_counter()
-        oracle.atopn_run(q[: t + 1], K, V, [w.L + s for s in range(t + 1)], w.top_n,
-                         w.refresh_n)
-        times.append(time.perf_counter() - t0)
-    t_refresh = times[0]
-    t_plain = max(times[1] - times[0], 1e-9)
-    # Steady state per decode step: every layer, refresh on 1 step in n.
-    per_layer = t_refresh / w.refresh_n + t_plain * (w.refresh_n - 1) / w.refresh_n
-    per_step = per_layer * w.layers
+        oracle.atopn_run(q, K, V, [w.L + s for s in range(w.steps)], w.top_n, w.refresh_n)
+        total += time.perf_counter() - t0
+        del K, V, q
+    per_layer_step = total / (len(sample) * w.steps)
+    per_step = per_layer_step * w.layers
     return {"value": 1.0 / per_step, "unit": "steps/s", "cores": cores, "kind": "oracle",
-            "sample": (f"layer 0 of {w.name}: one refresh step (t=0, {t_refresh:.2f} s) and one "
-                       f"plain step (t=1, {t_plain:.2f} s) over all {w.batch}x{w.h_q} "
-                       f"(batch row, query head) pairs; per step = {w.layers} layers with "
-                       f"1 refresh per {w.refresh_n} steps"),
-            "sample_seconds": round(sum(times), 2)}
+            "sample": (f"layers 0-{len(sample) - 1} of {w.name}: the full run of {w.steps} decode "
+                       f"steps (exact refresh every {w.refresh_n}) over all {w.batch}x{w.h_q} "
+                       f"(batch row, query head) pairs, {total:.1f} s; scaled to {w.layers} "
+                       f"layers per step"),
+            "sample_seconds": round(total, 2)}
 
 
 MALL_BYTES = 256 << 20
@@ -370,7 +367,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(torch, wl, w, res["layers"][0])
+        cpu = cpu_baseline(torch, wl, w, res["layers"])
     if not args.no_gqa and w.name in GQA_TWIN:
         del res["graphs"]
         for x in res["layers"]:
