@@ -82,7 +82,7 @@ Chunking plan_chunks(int64_t ctx, int64_t pairs, int head_dim, int max_chunks)
 struct Layout {
     int max_chunks;
     int64_t entry_rows;   // selection-list capacity per (b, query head)
-    size_t pm, pl, pc, po, entries, lcount, lmax, sample, pivot, flags, total;
+    size_t pm, pl, pc, po, entries, overflow, lcount, lmax, sample, pivot, flags, total;
 };
 
 Layout make_layout(const saga_dims* d)
@@ -107,7 +107,8 @@ Layout make_layout(const saga_dims* d)
     L.pl = take(rows * L.max_chunks * 4);
     L.pc = take(rows * L.max_chunks * 4);
     L.po = take(rows * L.max_chunks * (size_t)d->head_dim * 4);
-    L.entries = take(rows * (size_t)L.entry_rows * 8);
+    L.entries = take(rows * L.max_chunks * kWavesPerBlock * (size_t)kListPrimary * 8);
+    L.overflow = take(rows * (size_t)L.entry_rows * 8);
     L.lcount = take(rows * L.max_chunks * kWavesPerBlock * 4);
     L.lmax = take(rows * L.max_chunks * kWavesPerBlock * 4);
     L.sample = take(rows * kSampleMax * 4);
@@ -140,6 +141,7 @@ SelectStreamArgs stream_args(const saga_dims* dims, const Layout& L, const Chunk
     a.k = static_cast<const uint16_t*>(k);
     a.tau = tau;
     a.entries = reinterpret_cast<uint2*>(w + L.entries);
+    a.overflow_at = (int64_t)((L.overflow - L.entries) / 8);
     a.list_count = reinterpret_cast<int32_t*>(w + L.lcount);
     a.list_max = reinterpret_cast<float*>(w + L.lmax);
     a.B = dims->batch;
@@ -226,6 +228,7 @@ int enqueue_refresh(const saga_dims* dims, int32_t top_n, const void* q_dev,
     fa.q = sa.q;
     fa.k = sa.k;
     fa.entries = a.entries;
+    fa.overflow_at = a.overflow_at;
     fa.list_count = a.list_count;
     fa.tau = thresholds_dev;
     fa.group_flags = group_flags;
@@ -256,6 +259,7 @@ int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunkin
     GatherArgs ga{};
     ga.v = static_cast<const uint16_t*>(v_cache_dev);
     ga.entries = reinterpret_cast<const uint2*>(w + L.entries);
+    ga.overflow_at = (int64_t)((L.overflow - L.entries) / 8);
     ga.list_count = reinterpret_cast<const int32_t*>(w + L.lcount);
     ga.list_max = reinterpret_cast<const float*>(w + L.lmax);
     ga.tau_filter = tau_filter;

@@ -83,17 +83,19 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
             for (int base = 0; base < qn[i]; base += kWave) {
                 const bool have = base + lane < qn[i];
                 const uint2 e = have ? q4[i][base + lane] : make_uint2(0u, 0u);
-                const int slot = e.x & 15;
+                const int gs = (e.x & 15) >> 2;                 // head slot 4*gs + i
+                // Each lane finds its own list and position, so one store
+                // writes the whole batch whatever the mix of head slots.
+                int pos = 0;
 #pragma unroll
-                for (int gs = 0; gs < 4; ++gs) {
-                    const int h = 4 * gs + i;
-                    const uint64_t m = __ballot(have && slot == h);
-                    if (m == 0) continue;
-                    if (have && slot == h)
-                        a.entries[(list0 + h * list_stride) * capw + written[h] + lanes_below(m)] =
-                            make_uint2(e.x >> 4, e.y);
-                    written[h] += __popcll(m);
+                for (int g2 = 0; g2 < 4; ++g2) {
+                    const uint64_t m = __ballot(have && gs == g2);
+                    if (gs == g2) pos = written[4 * g2 + i] + (int)lanes_below(m);
+                    written[4 * g2 + i] += __popcll(m);
                 }
+                if (have)
+                    a.entries[list_index(list0 + (4 * gs + i) * list_stride, (uint32_t)pos, capw,
+                                         a.overflow_at)] = make_uint2(e.x >> 4, e.y);
             }
             qn[i] = 0;
         }
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
                 else hi = mid - 1;
             }
             lo[k] = l0;
-            ent[k] = t + k * kBlock < n ? a.entries[(lbase + l0) * capw + (E - pre[l0])]
+            ent[k] = t + k * kBlock < n ? a.entries[list_index(lbase + l0, (uint32_t)(E - pre[l0]), capw, a.overflow_at)]
                                         : uint2{0u, 0xff800000u};
         }
 #pragma unroll

@@ -51,16 +51,31 @@ constexpr int gather_target_blocks(int head_dim)
 constexpr int kGatherMaxSegs = 16;
 constexpr int kGatherStage = 1024;   // entries a gather workgroup stages per round
 
+// Storage of selection list lid = (b*h_q + i) * nl + chunk*4 + wave (nl lists
+// per row in this call, capw = rows_per_chunk/4 entries at most): its first
+// kListPrimary entries sit in a dense primary part at lid * kListPrimary + E,
+// so one call's typical lists share a few tens of megabytes (few pages for the
+// address translation); entries past those go to an overflow part sized for
+// the worst case, which starts at entry overflow_at.
+constexpr int kListPrimary = 64;
+__device__ __forceinline__ int64_t list_index(int64_t lid, uint32_t E, int64_t capw,
+                                              int64_t overflow_at)
+{
+    return E < (uint32_t)kListPrimary ? lid * kListPrimary + E
+                                      : overflow_at + lid * capw + (E - kListPrimary);
+}
+
 // Stream-select kernel: K stream, threshold mask, compaction into lists.
 // List (b*h_q + i, chunk, wave) holds up to rows_per_chunk/4 entries
-// (row - chunk_start, logit bits) at entries[list * rows_per_chunk/4].
+// (row - chunk_start, logit bits) at entries[list_index(list, ...)].
 struct SelectStreamArgs {
     const uint16_t* q;
     const uint16_t* k;
     const float* tau;
     uint32_t* bitmap;        // nullable
     int64_t bitmap_words;    // words per (b, i) row of the bitmap
-    uint2* entries;
+    uint2* entries;          // list storage (see list_index)
+    int64_t overflow_at;
     int32_t* list_count;     // [B*hq][chunks][4]
     float* list_max;         // [B*hq][chunks][4]  largest selected logit (-inf if none)
     float* logits_out;       // nullable [B*hq][ctx]: every logit, for checking
@@ -75,6 +90,7 @@ struct SelectStreamArgs {
 struct GatherArgs {
     const uint16_t* v;
     const uint2* entries;
+    int64_t overflow_at;
     const int32_t* list_count;
     const float* list_max;
     const float* tau_filter; // nullable [B*hq]: keep only entries with logit >= tau_filter
@@ -102,6 +118,7 @@ struct FinalArgs {
     const uint16_t* q;
     const uint16_t* k;
     const uint2* entries;
+    int64_t overflow_at;
     const int32_t* list_count;
     float* tau;              // [B*hq] out
     uint32_t* group_flags;   // nullable [B*hk]: set when a row of the group used the recompute path

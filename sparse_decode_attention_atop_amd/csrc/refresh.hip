@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
                         if ((uint32_t)pre[mid] <= E) lo = mid;
                         else hi = mid - 1;
                     }
-                    ent[k] = a.entries[(lbase + lo) * capw + (E - pre[lo])];
+                    ent[k] = a.entries[list_index(lbase + lo, (uint32_t)(E - pre[lo]), capw, a.overflow_at)];
                 }
             }
 #pragma unroll
