@@ -77,6 +77,8 @@ def log(msg):
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--decompose", action="store_true",
+                   help="time GQA full, SAGA full, Atop-N at GQA heads and SAGA + Atop-N")
     p.add_argument("--steps", type=int, default=320)
     p.add_argument("--warmup", type=int, default=32)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
@@ -226,13 +228,17 @@ def run_saga(torch, saga, wl, w, args):
 
 
 def run_gqa(torch, saga, wl, w, hkv, args):
-    g = w.gqa(hkv)
+    return run_full(torch, saga, wl, w.gqa(hkv), args) | {"hkv": hkv}
+
+
+def run_full(torch, saga, wl, g, args):
+    """Dense attention (saga_full_attention) over every layer of workload g."""
     T, L = g.steps, g.L
     layers = []
-    log(f"generating GQA twin h_k=h_v={hkv} ({g.kv_bytes() / 1e9:.1f} GB)")
+    log(f"generating {g.name}: h_k={g.h_k}, h_v={g.h_v} ({g.kv_bytes() / 1e9:.1f} GB)")
     for layer in range(g.layers):
         K, V, q = layer_inputs(torch, wl, g, layer)
-        log(f"  GQA layer {layer} ready")
+        log(f"  layer {layer} ready")
         layers.append(dict(K=K, V=V, q=q, out=torch.empty(g.batch, g.h_q, g.head_dim,
                                                           dtype=torch.bfloat16, device="cuda")))
     d0 = saga.dims(g.batch, g.h_q, g.h_k, g.h_v, g.head_dim, L, g.rows, g.scale)
@@ -262,7 +268,7 @@ def run_gqa(torch, saga, wl, w, hkv, args):
     per_step_bytes *= g.layers / args.steps
     del layers, graphs
     torch.cuda.empty_cache()
-    return dict(sec=sec, bytes_per_step=per_step_bytes, hkv=hkv)
+    return dict(sec=sec, bytes_per_step=per_step_bytes)
 
 
 def cpu_baseline(torch, wl, w, layers, n_layers=2):
@@ -322,6 +328,38 @@ def sweep(torch, saga, wl, args):
             "cache_resident": per_layer * layers < 2 * MALL_BYTES}), flush=True)
 
 
+def decompose(torch, saga, wl, args):
+    """The pages' decomposition of the speedup on one shape: full-attention GQA,
+    SAGA full attention (merged key heads, no sparsity), Atop-N at the GQA head
+    counts (sparsity, no merging) and SAGA + Atop-N, each on its own seeded
+    inputs, per layer and step (refresh steps included)."""
+    w0 = wl.WORKLOADS[args.workload]
+    hkv = GQA_TWIN[w0.name]
+    per_layer = w0.batch * (w0.h_k + w0.h_v) * w0.rows * w0.head_dim * 2
+    layers = max(2, min(w0.layers, -(-4 * MALL_BYTES // per_layer)))
+    w = w0.with_(layers=layers)
+    args.eager_only = False
+    rows = []
+    for label, kind, x in (("GQA full attention", "full", w.gqa(hkv)),
+                           ("SAGA full attention (merging alone)", "full", w),
+                           ("Atop-N at GQA heads (sparsity alone)", "atopn", w.gqa(hkv)),
+                           ("SAGA + Atop-N", "atopn", w)):
+        if kind == "full":
+            res = run_full(torch, saga, wl, x, args)
+        else:
+            res = run_saga(torch, saga, wl, x, args)
+            del res["graphs"], res["layers"]
+        torch.cuda.empty_cache()
+        ms = 1e3 * res["sec"] / args.steps / layers
+        rows.append((label, x, ms))
+    base = rows[0][2]
+    for label, x, ms in rows:
+        print(json.dumps({"decomposition": label, "workload": w0.name, "h_k": x.h_k, "h_v": x.h_v,
+                          "top_n": x.top_n if "Atop-N" in label else None,
+                          "layers_timed": layers, "ms_per_layer": round(ms, 4),
+                          "speedup_vs_gqa_full": round(base / ms, 3)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -342,6 +380,9 @@ def main():
         return
     if args.sweep:
         sweep(torch, saga, wl, args)
+        return
+    if args.decompose:
+        decompose(torch, saga, wl, args)
         return
     w = wl.WORKLOADS[args.workload]
     res = run_saga(torch, saga, wl, w, args)
