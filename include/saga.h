@@ -158,6 +158,50 @@ int atopn_refresh_decode_step(const saga_dims* dims, int32_t top_n, const void* 
                               void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
+ * Paged caches with per-sequence lengths (a serving-shaped cache: sequences of
+ * different lengths sharing page pools; the step before the method proper,
+ * needed to serve batched decode as the pages' batch-16 setting does).
+ *
+ *   k_pages bf16 [num_pages][h_k][page_rows][head_dim]
+ *   v_pages bf16 [num_pages][h_v][page_rows][head_dim]
+ * Row r (0-based, logical) of sequence b is row r % page_rows of page
+ * block_table[b][r / page_rows] in both pools.  Sequence b attends rows
+ * 0 .. ctx_lens[b]-1 (values outside [0, max_pages * page_rows] are clamped);
+ * dims->ctx_len must be >= every ctx_lens[b] (it sizes the work split) and
+ * dims->cache_len must equal max_pages * page_rows.  page_rows is a multiple of
+ * 256.  A table entry outside [0, num_pages) reads as a page of zero rows that
+ * contribute no value row.  Both arrays are device memory read by the kernels
+ * (the call may be captured in a graph while they change between replays).
+ */
+typedef struct saga_paged {
+    const int32_t* block_table_dev;  /* [batch][max_pages] page index           */
+    const int32_t* ctx_lens_dev;     /* [batch] rows attended per sequence       */
+    int32_t page_rows;               /* rows per page, a multiple of 256         */
+    int32_t max_pages;               /* block_table row stride                   */
+    int64_t num_pages;               /* pages in each pool                       */
+    int64_t reserved;                /* must be 0                                */
+} saga_paged;
+
+/* The three Atop-N calls above on paged caches.  Same results per sequence as
+ * the contiguous calls with ctx_len = ctx_lens[b] (for every b with
+ * top_n >= ctx_lens[b], tau = -inf); the workspace is saga_workspace_bytes(dims,
+ * top_n).  No debug outputs.  Errors: as the contiguous calls, plus
+ * INVALID_ARGUMENT for a null or inconsistent saga_paged. */
+int atopn_refresh_thresholds_paged(const saga_dims* dims, const saga_paged* paged, int32_t top_n,
+                                   const void* q_dev, const void* k_pages_dev,
+                                   float* thresholds_dev, void* workspace_dev,
+                                   size_t workspace_bytes, void* stream);
+int saga_decode_step_paged(const saga_dims* dims, const saga_paged* paged, const void* q_dev,
+                           const void* k_pages_dev, const void* v_pages_dev,
+                           const float* thresholds_dev, void* out_dev, int32_t* sel_counts_dev,
+                           void* workspace_dev, size_t workspace_bytes, void* stream);
+int atopn_refresh_decode_step_paged(const saga_dims* dims, const saga_paged* paged, int32_t top_n,
+                                    const void* q_dev, const void* k_pages_dev,
+                                    const void* v_pages_dev, float* thresholds_dev, void* out_dev,
+                                    int32_t* sel_counts_dev, void* workspace_dev,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * Full (dense) decode attention over all ctx_len rows with the same head maps:
  * the full-attention GQA baseline the pages time against when h_k == h_v, and
  * "SAGA full attention" when h_k < h_v (ai.info summary, Main Findings:

@@ -21,13 +21,15 @@ import torch
 __all__ = [
     "SagaDims", "SagaError", "dims", "library", "saga_workspace_bytes", "alloc_workspace",
     "atopn_refresh_thresholds", "saga_decode_step", "atopn_refresh_decode_step",
-    "saga_full_attention", "saga_status_string", "saga_version", "LIB_PATH", "EXPORTED_SYMBOLS",
+    "SagaPaged", "paged", "atopn_refresh_thresholds_paged", "saga_decode_step_paged",
+    "atopn_refresh_decode_step_paged", "saga_full_attention", "saga_status_string", "saga_version", "LIB_PATH", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsaga.so")
 EXPORTED_SYMBOLS = ("saga_workspace_bytes", "atopn_refresh_thresholds", "saga_decode_step",
-                    "atopn_refresh_decode_step", "saga_full_attention", "saga_status_string",
-                    "saga_version")
+                    "atopn_refresh_decode_step", "atopn_refresh_thresholds_paged",
+                    "saga_decode_step_paged", "atopn_refresh_decode_step_paged",
+                    "saga_full_attention", "saga_status_string", "saga_version")
 
 SAGA_OK = 0
 SAGA_ERR_INVALID_ARGUMENT = 1
@@ -57,6 +59,18 @@ class SagaDims(ctypes.Structure):
                 f"cache_len={self.cache_len}, scale={self.scale})")
 
 
+class SagaPaged(ctypes.Structure):
+    """Mirror of ``saga_paged`` in include/saga.h (paged caches)."""
+    _fields_ = [
+        ("block_table_dev", ctypes.c_void_p),
+        ("ctx_lens_dev", ctypes.c_void_p),
+        ("page_rows", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("reserved", ctypes.c_int64),
+    ]
+
+
 class SagaError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -84,6 +98,14 @@ def library():
         lib.saga_decode_step.restype = ctypes.c_int
         lib.atopn_refresh_decode_step.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.atopn_refresh_decode_step.restype = ctypes.c_int
+        pp = ctypes.POINTER(SagaPaged)
+        lib.atopn_refresh_thresholds_paged.argtypes = [pd, pp, i32, vp, vp, vp, vp, sz, vp]
+        lib.atopn_refresh_thresholds_paged.restype = ctypes.c_int
+        lib.saga_decode_step_paged.argtypes = [pd, pp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.saga_decode_step_paged.restype = ctypes.c_int
+        lib.atopn_refresh_decode_step_paged.argtypes = [pd, pp, i32, vp, vp, vp, vp, vp, vp, vp,
+                                                        sz, vp]
+        lib.atopn_refresh_decode_step_paged.restype = ctypes.c_int
         lib.saga_full_attention.argtypes = [pd, vp, vp, vp, vp, vp, sz, vp]
         lib.saga_full_attention.restype = ctypes.c_int
         lib.saga_status_string.argtypes = [ctypes.c_int]
@@ -210,6 +232,79 @@ def atopn_refresh_decode_step(d: SagaDims, top_n: int, q: torch.Tensor, k_cache:
         _ptr(thresholds, torch.float32, "thresholds"), _ptr(out, torch.bfloat16, "out"),
         _ptr(sel_counts, torch.int32, "sel_counts"), ws, nbytes, _stream(stream)),
         "atopn_refresh_decode_step")
+
+
+def paged(block_table: torch.Tensor, ctx_lens: torch.Tensor, page_rows: int,
+          num_pages: int) -> SagaPaged:
+    """Describe paged caches: block_table int32 [B][max_pages], ctx_lens int32 [B]
+    (device tensors, kept alive by the caller while calls use them)."""
+    if block_table.dim() != 2 or ctx_lens.dim() != 1 or block_table.shape[0] != ctx_lens.shape[0]:
+        raise ValueError("block_table must be [B][max_pages] and ctx_lens [B]")
+    return SagaPaged(_ptr(block_table, torch.int32, "block_table").value,
+                     _ptr(ctx_lens, torch.int32, "ctx_lens").value, int(page_rows),
+                     int(block_table.shape[1]), int(num_pages), 0)
+
+
+def _need_pool(t: torch.Tensor, d: SagaDims, p: SagaPaged, heads: int, name: str):
+    _need(t, p.num_pages * heads * p.page_rows * d.head_dim, name)
+
+
+def atopn_refresh_thresholds_paged(d: SagaDims, p: SagaPaged, top_n: int, q: torch.Tensor,
+                                   k_pages: torch.Tensor, thresholds: torch.Tensor,
+                                   workspace: torch.Tensor, stream=None) -> None:
+    """Exact top-N thresholds on paged caches (per-sequence lengths)."""
+    _need(q, d.batch * d.h_q * d.head_dim, "q")
+    _need_pool(k_pages, d, p, d.h_k, "k_pages")
+    _need(thresholds, d.batch * d.h_q, "thresholds")
+    ws, nbytes = _ws(workspace)
+    _check(library().atopn_refresh_thresholds_paged(
+        ctypes.byref(d), ctypes.byref(p), int(top_n), _ptr(q, torch.bfloat16, "q"),
+        _ptr(k_pages, torch.bfloat16, "k_pages"), _ptr(thresholds, torch.float32, "thresholds"),
+        ws, nbytes, _stream(stream)), "atopn_refresh_thresholds_paged")
+
+
+def saga_decode_step_paged(d: SagaDims, p: SagaPaged, q: torch.Tensor, k_pages: torch.Tensor,
+                           v_pages: torch.Tensor, thresholds: torch.Tensor, out: torch.Tensor,
+                           workspace: torch.Tensor, sel_counts: Optional[torch.Tensor] = None,
+                           stream=None) -> None:
+    """One Atop-N decode step on paged caches."""
+    bh = d.batch * d.h_q
+    _need(q, bh * d.head_dim, "q")
+    _need_pool(k_pages, d, p, d.h_k, "k_pages")
+    _need_pool(v_pages, d, p, d.h_v, "v_pages")
+    _need(thresholds, bh, "thresholds")
+    _need(out, bh * d.head_dim, "out")
+    _need(sel_counts, bh, "sel_counts")
+    ws, nbytes = _ws(workspace)
+    _check(library().saga_decode_step_paged(
+        ctypes.byref(d), ctypes.byref(p), _ptr(q, torch.bfloat16, "q"),
+        _ptr(k_pages, torch.bfloat16, "k_pages"), _ptr(v_pages, torch.bfloat16, "v_pages"),
+        _ptr(thresholds, torch.float32, "thresholds"), _ptr(out, torch.bfloat16, "out"),
+        _ptr(sel_counts, torch.int32, "sel_counts"), ws, nbytes, _stream(stream)),
+        "saga_decode_step_paged")
+
+
+def atopn_refresh_decode_step_paged(d: SagaDims, p: SagaPaged, top_n: int, q: torch.Tensor,
+                                    k_pages: torch.Tensor, v_pages: torch.Tensor,
+                                    thresholds: torch.Tensor, out: torch.Tensor,
+                                    workspace: torch.Tensor,
+                                    sel_counts: Optional[torch.Tensor] = None,
+                                    stream=None) -> None:
+    """A refresh step on paged caches: fresh thresholds and this step's output."""
+    bh = d.batch * d.h_q
+    _need(q, bh * d.head_dim, "q")
+    _need_pool(k_pages, d, p, d.h_k, "k_pages")
+    _need_pool(v_pages, d, p, d.h_v, "v_pages")
+    _need(thresholds, bh, "thresholds")
+    _need(out, bh * d.head_dim, "out")
+    _need(sel_counts, bh, "sel_counts")
+    ws, nbytes = _ws(workspace)
+    _check(library().atopn_refresh_decode_step_paged(
+        ctypes.byref(d), ctypes.byref(p), int(top_n), _ptr(q, torch.bfloat16, "q"),
+        _ptr(k_pages, torch.bfloat16, "k_pages"), _ptr(v_pages, torch.bfloat16, "v_pages"),
+        _ptr(thresholds, torch.float32, "thresholds"), _ptr(out, torch.bfloat16, "out"),
+        _ptr(sel_counts, torch.int32, "sel_counts"), ws, nbytes, _stream(stream)),
+        "atopn_refresh_decode_step_paged")
 
 
 def saga_full_attention(d: SagaDims, q: torch.Tensor, k_cache: torch.Tensor,

@@ -72,10 +72,13 @@ Chunking split_rows(int64_t ctx, int64_t pairs, int64_t block_rows, int64_t targ
     return {(int)((ctx + rows - 1) / rows), rows};
 }
 
-// Chunking of the K stream (stream-select kernel) for one call.
+// Chunking of the K stream (stream-select kernel) for one call.  Chunks are
+// whole tile pairs (the kernel streams pairs), so with pages of kPageQuantum
+// rows no pair straddles two pages.
 Chunking plan_chunks(int64_t ctx, int64_t pairs, int head_dim, int max_chunks)
 {
-    return split_rows(ctx, pairs, decode_block_rows(head_dim), target_blocks(head_dim), max_chunks);
+    return split_rows(ctx, pairs, 2 * decode_block_rows(head_dim), target_blocks(head_dim),
+                      max_chunks);
 }
 
 // Workspace layout (byte offsets), identical for every ctx_len <= cache_len.
@@ -98,7 +101,7 @@ Layout make_layout(const saga_dims* d)
     L.max_chunks = (int)(mc < 1 ? 1 : mc);
     // chunks * rows_per_chunk <= ctx + rows_per_chunk(ctx), and rows_per_chunk
     // never exceeds max(block rows, its value at ctx = cache_len).
-    const int64_t br = decode_block_rows(d->head_dim);
+    const int64_t br = 2 * decode_block_rows(d->head_dim);
     const Chunking top = plan_chunks(d->cache_len, (int64_t)d->batch * d->h_k, d->head_dim, L.max_chunks);
     L.entry_rows = d->cache_len + (top.rows > br ? top.rows : br);
     size_t off = 0;
@@ -133,7 +136,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SAGA_OK : SAGA_ERR_HIP; 
 
 // Arguments of the stream-select kernel for one call.
 SelectStreamArgs stream_args(const saga_dims* dims, const Layout& L, const Chunking& ch,
-                             const void* q, const void* k, const float* tau, void* ws)
+                             const void* q, const void* k, const float* tau, void* ws,
+                             const PagedKV& pg)
 {
     unsigned char* w = static_cast<unsigned char*>(ws);
     SelectStreamArgs a{};
@@ -153,6 +157,7 @@ SelectStreamArgs stream_args(const saga_dims* dims, const Layout& L, const Chunk
     a.rows_per_chunk = ch.rows;
     a.chunks = ch.chunks;
     a.scale = dims->scale;
+    a.pg = pg;
     return a;
 }
 
@@ -173,7 +178,7 @@ namespace {
 int enqueue_refresh(const saga_dims* dims, int32_t top_n, const void* q_dev,
                     const void* k_cache_dev, float* thresholds_dev, float* logits_debug_dev,
                     void* workspace_dev, const Layout& L, const Chunking& ch, hipStream_t s,
-                    uint32_t* group_flags)
+                    uint32_t* group_flags, const PagedKV& pg)
 {
     unsigned char* w = static_cast<unsigned char*>(workspace_dev);
     const int D = dims->head_dim;
@@ -214,11 +219,13 @@ int enqueue_refresh(const saga_dims* dims, int32_t top_n, const void* q_dev,
         sa.rank = (int)r;
     }
     sa.scale = dims->scale;
+    sa.top_n = top_n;
+    sa.pg = pg;
     int st = hip_status(launch_sample(D, sa, s));
     if (st != SAGA_OK) return st;
 
     // 3. Candidate lists: every logit >= pivot.
-    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, pivot, workspace_dev);
+    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, pivot, workspace_dev, pg);
     a.logits_out = logits_debug_dev;
     st = hip_status(launch_select_stream(D, a, s));
     if (st != SAGA_OK) return st;
@@ -242,6 +249,7 @@ int enqueue_refresh(const saga_dims* dims, int32_t top_n, const void* q_dev,
     fa.chunks = ch.chunks;
     fa.top_n = (uint32_t)top_n;
     fa.scale = dims->scale;
+    fa.pg = pg;
     return hip_status(launch_refresh_final(D, fa, s));
 }
 
@@ -249,7 +257,8 @@ int enqueue_refresh(const saga_dims* dims, int32_t top_n, const void* q_dev,
 // combine into out.  With tau_filter, list entries below it are skipped.
 int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunking& ch,
                            const void* v_cache_dev, const float* tau_filter, void* out_dev,
-                           int32_t* sel_counts_dev, void* workspace_dev, hipStream_t s)
+                           int32_t* sel_counts_dev, void* workspace_dev, hipStream_t s,
+                           const PagedKV& pg)
 {
     unsigned char* w = static_cast<unsigned char*>(workspace_dev);
     const int D = dims->head_dim;
@@ -271,6 +280,7 @@ int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunkin
     ga.cache_len = dims->cache_len;
     ga.rows_per_chunk = ch.rows;
     ga.chunks = ch.chunks;
+    ga.pg = pg;
     int64_t segs = (gather_target_blocks(D) + rows - 1) / rows;
     if (segs > kGatherMaxSegs) segs = kGatherMaxSegs;
     if (segs > L.max_chunks) segs = L.max_chunks;       // partials hold max_chunks per row
@@ -285,7 +295,7 @@ int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunkin
 int enqueue_decode(const saga_dims* dims, const Layout& L, const void* q_dev,
                    const void* k_cache_dev, const void* v_cache_dev, const float* thresholds_dev,
                    void* out_dev, int32_t* sel_counts_dev, uint32_t* sel_bitmap_debug_dev,
-                   void* workspace_dev, hipStream_t s)
+                   void* workspace_dev, hipStream_t s, const PagedKV& pg)
 {
     const int D = dims->head_dim;
     const int rows = dims->batch * dims->h_q;
@@ -297,27 +307,42 @@ int enqueue_decode(const saga_dims* dims, const Layout& L, const void* q_dev,
     }
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
                                     D, L.max_chunks);
-    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, thresholds_dev, workspace_dev);
+    SelectStreamArgs a =
+        stream_args(dims, L, ch, q_dev, k_cache_dev, thresholds_dev, workspace_dev, pg);
     a.bitmap = sel_bitmap_debug_dev;
     a.bitmap_words = words;
     st = hip_status(launch_select_stream(D, a, s));
     if (st != SAGA_OK) return st;
     return enqueue_gather_combine(dims, L, ch, v_cache_dev, nullptr, out_dev, sel_counts_dev,
-                                  workspace_dev, s);
+                                  workspace_dev, s, pg);
 }
 
-}  // namespace
-
-SAGA_EXPORT int atopn_refresh_thresholds(const saga_dims* dims, int32_t top_n, const void* q_dev,
-                                         const void* k_cache_dev, float* thresholds_dev,
-                                         float* logits_debug_dev, void* workspace_dev,
-                                         size_t workspace_bytes, void* stream)
+// Checks of a page description against the call's dims: pages of a multiple
+// of kPageQuantum rows and cache_len = max_pages * page_rows.
+int validate_paged(const saga_dims* d, const saga_paged* p, PagedKV* out)
 {
-    int st = validate_dims(dims);
-    if (st != SAGA_OK) return st;
-    if (top_n < 1 || !q_dev || !k_cache_dev || !thresholds_dev || !workspace_dev)
+    if (!p || !p->block_table_dev || !p->ctx_lens_dev) return SAGA_ERR_INVALID_ARGUMENT;
+    if (misaligned(p->block_table_dev, 4) || misaligned(p->ctx_lens_dev, 4))
         return SAGA_ERR_INVALID_ARGUMENT;
-    if (misaligned(q_dev, 16) || misaligned(k_cache_dev, 16) || misaligned(thresholds_dev, 4) ||
+    if (p->page_rows < kPageQuantum || p->page_rows % kPageQuantum != 0 || p->max_pages < 1 ||
+        p->num_pages < 1 || p->reserved != 0)
+        return SAGA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)p->max_pages * p->page_rows != d->cache_len) return SAGA_ERR_INVALID_ARGUMENT;
+    out->block_table = p->block_table_dev;
+    out->ctx_lens = p->ctx_lens_dev;
+    out->page_rows = p->page_rows;
+    out->max_pages = p->max_pages;
+    out->num_pages = p->num_pages;
+    return SAGA_OK;
+}
+
+int do_refresh(const saga_dims* dims, const PagedKV& pg, int32_t top_n, const void* q_dev,
+               const void* k_dev, float* thresholds_dev, float* logits_debug_dev,
+               void* workspace_dev, size_t workspace_bytes, void* stream)
+{
+    if (top_n < 1 || !q_dev || !k_dev || !thresholds_dev || !workspace_dev)
+        return SAGA_ERR_INVALID_ARGUMENT;
+    if (misaligned(q_dev, 16) || misaligned(k_dev, 16) || misaligned(thresholds_dev, 4) ||
         misaligned(logits_debug_dev, 4) || misaligned(workspace_dev, 16))
         return SAGA_ERR_INVALID_ARGUMENT;
     const Layout L = make_layout(dims);
@@ -329,14 +354,15 @@ SAGA_EXPORT int atopn_refresh_thresholds(const saga_dims* dims, int32_t top_n, c
     const int rows = dims->batch * dims->h_q;
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
                                     D, L.max_chunks);
+    int st;
     if ((int64_t)top_n >= dims->ctx_len) {
-        // N >= ctx: every entry is kept, tau = -inf.  The logits are still
-        // produced when asked for (a pass that selects nothing).
+        // N >= ctx (of every sequence): every entry is kept, tau = -inf.  The
+        // logits are still produced when asked for (a pass that selects nothing).
         if (logits_debug_dev) {
             float* pivot = reinterpret_cast<float*>(w + L.pivot);
             st = hip_status(launch_fill_u32(reinterpret_cast<uint32_t*>(pivot), rows, 0x7f800000u, s));
             if (st != SAGA_OK) return st;
-            SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, pivot, workspace_dev);
+            SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_dev, pivot, workspace_dev, pg);
             a.logits_out = logits_debug_dev;
             st = hip_status(launch_select_stream(D, a, s));
             if (st != SAGA_OK) return st;
@@ -344,43 +370,36 @@ SAGA_EXPORT int atopn_refresh_thresholds(const saga_dims* dims, int32_t top_n, c
         return hip_status(launch_fill_u32(reinterpret_cast<uint32_t*>(thresholds_dev), rows,
                                           0xff800000u, s));
     }
-    return enqueue_refresh(dims, top_n, q_dev, k_cache_dev, thresholds_dev, logits_debug_dev,
-                           workspace_dev, L, ch, s, nullptr);
+    return enqueue_refresh(dims, top_n, q_dev, k_dev, thresholds_dev, logits_debug_dev,
+                           workspace_dev, L, ch, s, nullptr, pg);
 }
 
-SAGA_EXPORT int saga_decode_step(const saga_dims* dims, const void* q_dev, const void* k_cache_dev,
-                                 const void* v_cache_dev, const float* thresholds_dev,
-                                 void* out_dev, int32_t* sel_counts_dev,
-                                 uint32_t* sel_bitmap_debug_dev, void* workspace_dev,
-                                 size_t workspace_bytes, void* stream)
+int do_decode(const saga_dims* dims, const PagedKV& pg, const void* q_dev, const void* k_dev,
+              const void* v_dev, const float* thresholds_dev, void* out_dev,
+              int32_t* sel_counts_dev, uint32_t* sel_bitmap_debug_dev, void* workspace_dev,
+              size_t workspace_bytes, void* stream)
 {
-    int st = validate_dims(dims);
-    if (st != SAGA_OK) return st;
-    if (!q_dev || !k_cache_dev || !v_cache_dev || !thresholds_dev || !out_dev || !workspace_dev)
+    if (!q_dev || !k_dev || !v_dev || !thresholds_dev || !out_dev || !workspace_dev)
         return SAGA_ERR_INVALID_ARGUMENT;
-    if (misaligned(q_dev, 16) || misaligned(k_cache_dev, 16) || misaligned(v_cache_dev, 16) ||
+    if (misaligned(q_dev, 16) || misaligned(k_dev, 16) || misaligned(v_dev, 16) ||
         misaligned(thresholds_dev, 4) || misaligned(out_dev, 2) || misaligned(sel_counts_dev, 4) ||
         misaligned(sel_bitmap_debug_dev, 4) || misaligned(workspace_dev, 16))
         return SAGA_ERR_INVALID_ARGUMENT;
     const Layout L = make_layout(dims);
     if (workspace_bytes < L.total) return SAGA_ERR_WORKSPACE_TOO_SMALL;
-    return enqueue_decode(dims, L, q_dev, k_cache_dev, v_cache_dev, thresholds_dev, out_dev,
-                          sel_counts_dev, sel_bitmap_debug_dev, workspace_dev,
-                          static_cast<hipStream_t>(stream));
+    return enqueue_decode(dims, L, q_dev, k_dev, v_dev, thresholds_dev, out_dev, sel_counts_dev,
+                          sel_bitmap_debug_dev, workspace_dev, static_cast<hipStream_t>(stream),
+                          pg);
 }
 
-SAGA_EXPORT int atopn_refresh_decode_step(const saga_dims* dims, int32_t top_n, const void* q_dev,
-                                          const void* k_cache_dev, const void* v_cache_dev,
-                                          float* thresholds_dev, void* out_dev,
-                                          int32_t* sel_counts_dev, void* workspace_dev,
-                                          size_t workspace_bytes, void* stream)
+int do_refresh_decode(const saga_dims* dims, const PagedKV& pg, int32_t top_n,
+                      const void* q_dev, const void* k_dev, const void* v_dev,
+                      float* thresholds_dev, void* out_dev, int32_t* sel_counts_dev,
+                      void* workspace_dev, size_t workspace_bytes, void* stream)
 {
-    int st = validate_dims(dims);
-    if (st != SAGA_OK) return st;
-    if (top_n < 1 || !q_dev || !k_cache_dev || !v_cache_dev || !thresholds_dev || !out_dev ||
-        !workspace_dev)
+    if (top_n < 1 || !q_dev || !k_dev || !v_dev || !thresholds_dev || !out_dev || !workspace_dev)
         return SAGA_ERR_INVALID_ARGUMENT;
-    if (misaligned(q_dev, 16) || misaligned(k_cache_dev, 16) || misaligned(v_cache_dev, 16) ||
+    if (misaligned(q_dev, 16) || misaligned(k_dev, 16) || misaligned(v_dev, 16) ||
         misaligned(thresholds_dev, 4) || misaligned(out_dev, 2) || misaligned(sel_counts_dev, 4) ||
         misaligned(workspace_dev, 16))
         return SAGA_ERR_INVALID_ARGUMENT;
@@ -391,29 +410,114 @@ SAGA_EXPORT int atopn_refresh_decode_step(const saga_dims* dims, int32_t top_n, 
     unsigned char* w = static_cast<unsigned char*>(workspace_dev);
     const int D = dims->head_dim;
     const int rows = dims->batch * dims->h_q;
+    int st;
     if ((int64_t)top_n >= dims->ctx_len) {
         st = hip_status(launch_fill_u32(reinterpret_cast<uint32_t*>(thresholds_dev), rows,
                                         0xff800000u, s));
         if (st != SAGA_OK) return st;
-        return enqueue_decode(dims, L, q_dev, k_cache_dev, v_cache_dev, thresholds_dev, out_dev,
-                              sel_counts_dev, nullptr, workspace_dev, s);
+        return enqueue_decode(dims, L, q_dev, k_dev, v_dev, thresholds_dev, out_dev,
+                              sel_counts_dev, nullptr, workspace_dev, s, pg);
     }
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
                                     D, L.max_chunks);
     uint32_t* flags = reinterpret_cast<uint32_t*>(w + L.flags);
-    st = enqueue_refresh(dims, top_n, q_dev, k_cache_dev, thresholds_dev, nullptr, workspace_dev,
-                         L, ch, s, flags);
+    st = enqueue_refresh(dims, top_n, q_dev, k_dev, thresholds_dev, nullptr, workspace_dev,
+                         L, ch, s, flags, pg);
     if (st != SAGA_OK) return st;
     // Key groups whose candidate lists miss selected entries (a row took the
     // recompute path) are streamed again with the fresh thresholds; every
     // other workgroup of this launch exits at once.
-    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, thresholds_dev, workspace_dev);
+    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_dev, thresholds_dev, workspace_dev, pg);
     a.group_flags = flags;
     st = hip_status(launch_select_stream(D, a, s));
     if (st != SAGA_OK) return st;
     // The lists hold every logit >= tau (and more): keep those >= tau.
-    return enqueue_gather_combine(dims, L, ch, v_cache_dev, thresholds_dev, out_dev,
-                                  sel_counts_dev, workspace_dev, s);
+    return enqueue_gather_combine(dims, L, ch, v_dev, thresholds_dev, out_dev,
+                                  sel_counts_dev, workspace_dev, s, pg);
+}
+
+}  // namespace
+
+SAGA_EXPORT int atopn_refresh_thresholds(const saga_dims* dims, int32_t top_n, const void* q_dev,
+                                         const void* k_cache_dev, float* thresholds_dev,
+                                         float* logits_debug_dev, void* workspace_dev,
+                                         size_t workspace_bytes, void* stream)
+{
+    const int st = validate_dims(dims);
+    if (st != SAGA_OK) return st;
+    return do_refresh(dims, PagedKV{}, top_n, q_dev, k_cache_dev, thresholds_dev, logits_debug_dev,
+                      workspace_dev, workspace_bytes, stream);
+}
+
+SAGA_EXPORT int saga_decode_step(const saga_dims* dims, const void* q_dev, const void* k_cache_dev,
+                                 const void* v_cache_dev, const float* thresholds_dev,
+                                 void* out_dev, int32_t* sel_counts_dev,
+                                 uint32_t* sel_bitmap_debug_dev, void* workspace_dev,
+                                 size_t workspace_bytes, void* stream)
+{
+    const int st = validate_dims(dims);
+    if (st != SAGA_OK) return st;
+    return do_decode(dims, PagedKV{}, q_dev, k_cache_dev, v_cache_dev, thresholds_dev, out_dev,
+                     sel_counts_dev, sel_bitmap_debug_dev, workspace_dev, workspace_bytes, stream);
+}
+
+SAGA_EXPORT int atopn_refresh_decode_step(const saga_dims* dims, int32_t top_n, const void* q_dev,
+                                          const void* k_cache_dev, const void* v_cache_dev,
+                                          float* thresholds_dev, void* out_dev,
+                                          int32_t* sel_counts_dev, void* workspace_dev,
+                                          size_t workspace_bytes, void* stream)
+{
+    const int st = validate_dims(dims);
+    if (st != SAGA_OK) return st;
+    return do_refresh_decode(dims, PagedKV{}, top_n, q_dev, k_cache_dev, v_cache_dev,
+                             thresholds_dev, out_dev, sel_counts_dev, workspace_dev,
+                             workspace_bytes, stream);
+}
+
+SAGA_EXPORT int atopn_refresh_thresholds_paged(const saga_dims* dims, const saga_paged* paged,
+                                               int32_t top_n, const void* q_dev,
+                                               const void* k_pages_dev, float* thresholds_dev,
+                                               void* workspace_dev, size_t workspace_bytes,
+                                               void* stream)
+{
+    int st = validate_dims(dims);
+    if (st != SAGA_OK) return st;
+    PagedKV pg{};
+    st = validate_paged(dims, paged, &pg);
+    if (st != SAGA_OK) return st;
+    return do_refresh(dims, pg, top_n, q_dev, k_pages_dev, thresholds_dev, nullptr, workspace_dev,
+                      workspace_bytes, stream);
+}
+
+SAGA_EXPORT int saga_decode_step_paged(const saga_dims* dims, const saga_paged* paged,
+                                       const void* q_dev, const void* k_pages_dev,
+                                       const void* v_pages_dev, const float* thresholds_dev,
+                                       void* out_dev, int32_t* sel_counts_dev, void* workspace_dev,
+                                       size_t workspace_bytes, void* stream)
+{
+    int st = validate_dims(dims);
+    if (st != SAGA_OK) return st;
+    PagedKV pg{};
+    st = validate_paged(dims, paged, &pg);
+    if (st != SAGA_OK) return st;
+    return do_decode(dims, pg, q_dev, k_pages_dev, v_pages_dev, thresholds_dev, out_dev,
+                     sel_counts_dev, nullptr, workspace_dev, workspace_bytes, stream);
+}
+
+SAGA_EXPORT int atopn_refresh_decode_step_paged(const saga_dims* dims, const saga_paged* paged,
+                                                int32_t top_n, const void* q_dev,
+                                                const void* k_pages_dev, const void* v_pages_dev,
+                                                float* thresholds_dev, void* out_dev,
+                                                int32_t* sel_counts_dev, void* workspace_dev,
+                                                size_t workspace_bytes, void* stream)
+{
+    int st = validate_dims(dims);
+    if (st != SAGA_OK) return st;
+    PagedKV pg{};
+    st = validate_paged(dims, paged, &pg);
+    if (st != SAGA_OK) return st;
+    return do_refresh_decode(dims, pg, top_n, q_dev, k_pages_dev, v_pages_dev, thresholds_dev,
+                             out_dev, sel_counts_dev, workspace_dev, workspace_bytes, stream);
 }
 
 SAGA_EXPORT int saga_full_attention(const saga_dims* dims, const void* q_dev,

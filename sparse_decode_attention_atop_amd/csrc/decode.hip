@@ -39,7 +39,7 @@ namespace {
 // queue could overflow, it is split by head slot and appended to the global
 // per-(head, chunk, wave) lists in order.  DEBUG adds the optional logits and
 // selection-bitmap outputs.
-template <int D, int U, bool DEBUG>
+template <int D, int U, bool DEBUG, bool PAGED>
 __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(SelectStreamArgs a)
 {
     __shared__ uint2 queue[kWavesPerBlock][4][kQueueCap];
@@ -52,7 +52,8 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
     const int b = blockIdx.y / a.hk, g = blockIdx.y - b * a.hk;
     const int Gk = a.Gk;
     const int64_t r0 = (int64_t)chunk * a.rows_per_chunk;
-    const int64_t r1 = wave_uniform(min(r0 + a.rows_per_chunk, a.ctx));
+    const int64_t ctx_b = PAGED ? seq_ctx(a.pg, b, a.ctx) : a.ctx;
+    const int64_t r1 = wave_uniform(min(r0 + a.rows_per_chunk, ctx_b));
     const int64_t capw = a.rows_per_chunk / kWavesPerBlock;
     const int qh0 = b * a.hq + g * Gk;
     uint2 (*q4)[kQueueCap] = queue[wave];
@@ -159,9 +160,44 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
     // unconditionally and the load counters stay the same on every path (a
     // conditional prefetch makes the compiler wait for it before the current
     // tile).  Queue flushes (the only global stores) happen before a prefetch.
+    constexpr int64_t kStep = kWavesPerBlock * 16 * U;
+    if constexpr (PAGED) {
+        // Paged K: a tile pair (2 * kStep rows, pair starts aligned to it) lies
+        // in one page; each pair gets the buffer resource of its page, which
+        // ends at r1 or at the page end, and a table entry outside the pool
+        // gives an empty resource (zeros).
+        const int64_t P = a.pg.page_rows;
+        auto page_rsrc = [&](int64_t row) {
+            const int64_t base = page_base<D>(a.pg, b, g, a.hk, row);
+            int64_t n = r1 - (row - row % P);
+            n = n > P ? P : n;
+            if (n < 0 || base < 0) n = 0;
+            return make_rsrc(a.k + (base < 0 ? 0 : base), (uint32_t)(n * D * 2));
+        };
+        constexpr uint32_t kStepBytes = (uint32_t)(kStep * D * 2);
+        const uint32_t lane_off = (uint32_t)(wave * 16 * U + col) * (uint32_t)(D * 2) + 16u * grp;
+        int64_t tp = r0;                                // first row of the current pair
+        if (tp < r1) {
+            __amdgpu_buffer_rsrc_t ra = page_rsrc(tp);
+            KTile<D, U> ka, kb;
+            load_ktile_at<D, U>(ka, ra, lane_off + (uint32_t)(tp % P) * (uint32_t)(D * 2));
+            do {
+                maybe_flush();
+                load_ktile_at<D, U>(kb, ra,
+                                    lane_off + (uint32_t)(tp % P) * (uint32_t)(D * 2) + kStepBytes);
+                process(ka, tp + wave * 16 * U);
+                const __amdgpu_buffer_rsrc_t rn = page_rsrc(tp + 2 * kStep);
+                maybe_flush();
+                load_ktile_at<D, U>(ka, rn,
+                                    lane_off + (uint32_t)((tp + 2 * kStep) % P) * (uint32_t)(D * 2));
+                process(kb, tp + kStep + wave * 16 * U);
+                tp += 2 * kStep;
+                ra = rn;
+            } while (tp < r1);
+        }
+    } else {
     const __amdgpu_buffer_rsrc_t khead =
         make_rsrc(a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D, (uint32_t)(r1 * D * 2));
-    constexpr int64_t kStep = kWavesPerBlock * 16 * U;
     int64_t t0 = r0 + wave * 16 * U;
     if (t0 < r1) {
         // This lane's byte offset in tile t0, advanced one tile pair per trip.
@@ -183,6 +219,7 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
             t0 += 2 * kStep;
             koff += 2 * kStepBytes;
         } while (t0 < r1);
+    }
     }
     flush_all();
 #pragma unroll
@@ -250,7 +287,7 @@ __device__ int32_t block_scan(int32_t v, int32_t* red)
 // value head (under 2 GiB); entries that carry no weight get an offset past
 // the resource's end, which reads zero without touching memory, so the loads
 // need no branch.
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherArgs a)
 {
     constexpr int LPR = D / 8;             // lanes per value row (16 bytes each)
@@ -264,8 +301,9 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
     static_assert(CAPL % kBlock == 0, "staging rounds are whole threads");
     __shared__ int32_t pre[kMaxListsPerRow + 1];
     __shared__ int32_t red[kWavesPerBlock];
-    __shared__ uint32_t eoff[CAPL];
+    __shared__ uint32_t eoff[CAPL];     // byte offset in the value head; paged: row in page
     __shared__ float ew[CAPL];
+    __shared__ int32_t eps[PAGED ? CAPL : 1];   // paged: page * h_v + value head, -1 if none
 
     const int seg = blockIdx.x;
     const int bi = blockIdx.y;
@@ -298,8 +336,9 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
     const int32_t e_begin = (int32_t)((int64_t)total * seg / a.segs);
     const int32_t e_end = (int32_t)((int64_t)total * (seg + 1) / a.segs);
 
-    const uint16_t* vh = a.v + ((int64_t)(b * a.hv + i / a.Gv) * a.cache_len) * D;
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh, (uint32_t)(a.cache_len * D * 2));
+    const int nu = i / a.Gv;
+    const uint16_t* vh = a.v + ((int64_t)(b * a.hv + nu) * a.cache_len) * D;
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh, (uint32_t)(PAGED ? 0 : a.cache_len * D * 2));
     const int slot = t / LPR, lc = t - slot * LPR;
     const float tf = a.tau_filter ? a.tau_filter[bi] : -INFINITY;
     float acc[8];
@@ -325,6 +364,31 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
             ent[k] = t + k * kBlock < n ? a.entries[list_index(lbase + l0, (uint32_t)(E - pre[l0]), capw, a.overflow_at)]
                                         : uint2{0u, 0xff800000u};
         }
+        if constexpr (PAGED) {
+            // The value row's page: every table read issued before any use.
+            int32_t page[EPT];
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) {
+                const int64_t r = (int64_t)(lo[k] / kWavesPerBlock) * a.rows_per_chunk + ent[k].x;
+                const int64_t pi = r / a.pg.page_rows;
+                page[k] = (t + k * kBlock < n && pi < a.pg.max_pages)
+                              ? a.pg.block_table[(int64_t)b * a.pg.max_pages + pi] : -1;
+            }
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) {
+                const int e = t + k * kBlock;
+                if (e < n) {
+                    const float sv = __uint_as_float(ent[k].y);
+                    const bool keep = sv >= tf;
+                    kept += keep;
+                    const int64_t r = (int64_t)(lo[k] / kWavesPerBlock) * a.rows_per_chunk + ent[k].x;
+                    const bool ok = page[k] >= 0 && page[k] < a.pg.num_pages;   // else reads nothing
+                    eoff[e] = (uint32_t)(r % a.pg.page_rows);
+                    eps[e] = ok ? page[k] * a.hv + nu : -1;
+                    ew[e] = keep && ok ? __expf(sv - M) : 0.f;
+                }
+            }
+        } else {
 #pragma unroll
         for (int k = 0; k < EPT; ++k) {
             const int e = t + k * kBlock;
@@ -337,6 +401,7 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
                 ew[e] = keep ? __expf(sv - M) : 0.f;
             }
         }
+        }
         __syncthreads();
         for (int e0 = slot; e0 < n; e0 += SLOTS * NB) {
             u32x4 vv[NB];
@@ -346,7 +411,14 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
                 const int e = e0 + k * SLOTS;
                 const bool in = e < n;
                 w[k] = in ? ew[e] : 0.f;
-                vv[k] = buf_ld16(vrs, (in ? eoff[e] : kNoRow) + 16u * lc);
+                if constexpr (PAGED) {
+                    if (w[k] > 0.f)                     // weight zero: no row (or no page)
+                        vv[k] = ld16(a.v + ((int64_t)eps[e] * a.pg.page_rows + eoff[e]) * D + 8 * lc);
+                    else
+                        vv[k] = u32x4{0u, 0u, 0u, 0u};
+                } else {
+                    vv[k] = buf_ld16(vrs, (in ? eoff[e] : kNoRow) + 16u * lc);
+                }
             }
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
@@ -475,23 +547,32 @@ hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t s)
 {
     const dim3 grid(a.chunks, a.B * a.hk);
     const bool dbg = a.bitmap != nullptr || a.logits_out != nullptr;
+    const bool paged = a.pg.block_table != nullptr;
+#define SAGA_LAUNCH_STREAM(DD, DBG, PG)                                                        \
+    hipLaunchKernelGGL((select_stream_kernel<DD, decode_unroll(DD), DBG, PG>), grid, dim3(kBlock), \
+                       0, s, a)
     if (D == 64) {
-        if (dbg) hipLaunchKernelGGL((select_stream_kernel<64, decode_unroll(64), true>), grid, dim3(kBlock), 0, s, a);
-        else hipLaunchKernelGGL((select_stream_kernel<64, decode_unroll(64), false>), grid, dim3(kBlock), 0, s, a);
+        if (paged) { if (dbg) SAGA_LAUNCH_STREAM(64, true, true); else SAGA_LAUNCH_STREAM(64, false, true); }
+        else { if (dbg) SAGA_LAUNCH_STREAM(64, true, false); else SAGA_LAUNCH_STREAM(64, false, false); }
     } else {
-        if (dbg) hipLaunchKernelGGL((select_stream_kernel<128, decode_unroll(128), true>), grid, dim3(kBlock), 0, s, a);
-        else hipLaunchKernelGGL((select_stream_kernel<128, decode_unroll(128), false>), grid, dim3(kBlock), 0, s, a);
+        if (paged) { if (dbg) SAGA_LAUNCH_STREAM(128, true, true); else SAGA_LAUNCH_STREAM(128, false, true); }
+        else { if (dbg) SAGA_LAUNCH_STREAM(128, true, false); else SAGA_LAUNCH_STREAM(128, false, false); }
     }
+#undef SAGA_LAUNCH_STREAM
     return hipGetLastError();
 }
 
 hipError_t launch_gather(int D, const GatherArgs& a, hipStream_t s)
 {
     const dim3 grid(a.segs, a.B * a.hq);
-    if (D == 64)
-        hipLaunchKernelGGL(gather_kernel<64>, grid, dim3(kBlock), 0, s, a);
-    else
-        hipLaunchKernelGGL(gather_kernel<128>, grid, dim3(kBlock), 0, s, a);
+    const bool paged = a.pg.block_table != nullptr;
+    if (D == 64) {
+        if (paged) hipLaunchKernelGGL((gather_kernel<64, true>), grid, dim3(kBlock), 0, s, a);
+        else hipLaunchKernelGGL((gather_kernel<64, false>), grid, dim3(kBlock), 0, s, a);
+    } else {
+        if (paged) hipLaunchKernelGGL((gather_kernel<128, true>), grid, dim3(kBlock), 0, s, a);
+        else hipLaunchKernelGGL((gather_kernel<128, false>), grid, dim3(kBlock), 0, s, a);
+    }
     return hipGetLastError();
 }
 

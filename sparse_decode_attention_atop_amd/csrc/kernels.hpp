@@ -65,6 +65,43 @@ __device__ __forceinline__ int64_t list_index(int64_t lid, uint32_t E, int64_t c
                                       : overflow_at + lid * capw + (E - kListPrimary);
 }
 
+// Paged caches.  Sequence b attends ctx_lens[b] rows; its logical row r sits
+// in page block_table[b][r / P] of a pool laid out [num_pages][heads][P][d],
+// at row r % P.  P is a multiple of kPageQuantum, so a pair of stream tiles, a
+// 16-row sample block and a recompute tile never straddle two pages.  With
+// block_table == nullptr the caches are contiguous [B][heads][cache_len][d]
+// and every sequence attends the call's ctx rows.
+constexpr int kPageQuantum = 256;
+struct PagedKV {
+    const int32_t* block_table;   // [B][max_pages], nullptr: contiguous caches
+    const int32_t* ctx_lens;      // [B]
+    int32_t page_rows;            // P
+    int32_t max_pages;
+    int64_t num_pages;
+};
+
+// Rows attended by sequence b (ctx_lens[b] clamped to the table's capacity).
+__device__ __forceinline__ int64_t seq_ctx(const PagedKV& pg, int b, int64_t ctx)
+{
+    if (!pg.block_table) return ctx;
+    int64_t c = pg.ctx_lens[b];
+    const int64_t cap = (int64_t)pg.max_pages * pg.page_rows;
+    return c < 0 ? 0 : (c > cap ? cap : c);
+}
+
+// Element offset of the first row of the page that holds row r of (b, head h)
+// in a pool with nh heads per page, or -1 when the table points outside the
+// pool (the caller then reads nothing).
+template <int D>
+__device__ __forceinline__ int64_t page_base(const PagedKV& pg, int b, int h, int nh, int64_t r)
+{
+    const int64_t p = r / pg.page_rows;
+    if (p >= pg.max_pages) return -1;
+    const int32_t page = pg.block_table[(int64_t)b * pg.max_pages + p];
+    if (page < 0 || page >= pg.num_pages) return -1;
+    return (((int64_t)page * nh + h) * pg.page_rows) * D;
+}
+
 // Stream-select kernel: K stream, threshold mask, compaction into lists.
 // List (b*h_q + i, chunk, wave) holds up to rows_per_chunk/4 entries
 // (row - chunk_start, logit bits) at entries[list_index(list, ...)].
@@ -84,6 +121,7 @@ struct SelectStreamArgs {
     int64_t ctx, cache_len, rows_per_chunk;
     int32_t chunks;
     float scale;
+    PagedKV pg;              // paged caches (block_table != nullptr)
 };
 
 // Gather kernel: softmax weights and the sparse value gather over the lists.
@@ -98,6 +136,7 @@ struct GatherArgs {
     int32_t B, hq, hv, Gv;
     int64_t cache_len, rows_per_chunk;
     int32_t chunks, segs;    // segs: equal entry ranges per (b, query head)
+    PagedKV pg;              // paged caches (block_table != nullptr)
 };
 
 // Refresh steps 1-2: sampled logits and the per-row pivot.
@@ -110,7 +149,9 @@ struct SampleArgs {
     int32_t B, hq, hk, Gk;
     int64_t cache_len, stride;   // one 16-row sample block every `stride` rows
     int32_t m, rank;             // sample size, rank of the pivot within the sample
+    int32_t top_n;               // paged: per-row rank from each sequence's length
     float scale;
+    PagedKV pg;              // paged caches (block_table != nullptr)
 };
 
 // Refresh step 4: exact N-th largest from the candidate lists.
@@ -127,6 +168,7 @@ struct FinalArgs {
     int32_t chunks;
     uint32_t top_n;
     float scale;
+    PagedKV pg;              // paged caches (block_table != nullptr)
 };
 
 struct FullArgs {

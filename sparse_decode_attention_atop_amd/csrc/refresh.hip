@@ -116,7 +116,7 @@ __device__ uint32_t lds_radix_select(const uint32_t* keys, uint32_t n, uint32_t 
 // made of 16-row blocks (one MFMA group each, contiguous in memory): sample
 // index k covers row (k/16)*stride + k%16, k < m.  Output sample[b*hq + i][k]
 // (row stride kSampleMax).
-template <int D, int U>
+template <int D, int U, bool PAGED>
 __global__ __launch_bounds__(kBlock) void sample_logits_kernel(SampleArgs a)
 {
     const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -128,15 +128,24 @@ __global__ __launch_bounds__(kBlock) void sample_logits_kernel(SampleArgs a)
     if (k0 >= a.m) return;                                          // whole wave idle
     const QFrag<D> qf = load_qfrag<D>(col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr);
     const uint16_t* khead = a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
+    const int64_t ctx_b = PAGED ? seq_ctx(a.pg, b, 0) : INT64_MAX;
     KTile<D, U> kt;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         int k = k0 + 16 * u + col;
         k = k < a.m ? k : a.m - 1;
         const int64_t row = (int64_t)(k >> 4) * a.stride + (k & 15);
-        const uint16_t* p = khead + row * D + 8 * grp;
+        const uint16_t* p;
+        if constexpr (PAGED) {
+            // Rows past the sequence (and pages outside the pool) read nothing.
+            const int64_t base = row < ctx_b ? page_base<D>(a.pg, b, g, a.hk, row) : -1;
+            p = base < 0 ? nullptr : a.k + base + (row % a.pg.page_rows) * D + 8 * grp;
+        } else {
+            p = khead + row * D + 8 * grp;
+        }
 #pragma unroll
-        for (int mm = 0; mm < D / 32; ++mm) kt.v[u][mm] = ld16(p + 32 * mm);
+        for (int mm = 0; mm < D / 32; ++mm)
+            kt.v[u][mm] = p ? ld16(p + 32 * mm) : u32x4{0u, 0u, 0u, 0u};
     }
     float s[U][4];
     qk_tile<D, U>(qf, kt, a.scale, s);
@@ -144,10 +153,13 @@ __global__ __launch_bounds__(kBlock) void sample_logits_kernel(SampleArgs a)
     for (int u = 0; u < U; ++u) {
         const int k = k0 + 16 * u + col;
         if (k >= a.m) continue;
+        const int64_t row = (int64_t)(k >> 4) * a.stride + (k & 15);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int slot = 4 * grp + i;
-            if (slot < Gk) a.sample[(int64_t)(qh0 + slot) * kSampleMax + k] = s[u][i];
+            // Paged: rows past the sequence rank below every real logit.
+            if (slot < Gk)
+                a.sample[(int64_t)(qh0 + slot) * kSampleMax + k] = row < ctx_b ? s[u][i] : -INFINITY;
         }
     }
 }
@@ -159,11 +171,33 @@ __global__ __launch_bounds__(kBlock) void pivot_kernel(SampleArgs a)
     __shared__ SelectLds w;
     const int row = blockIdx.x;
     const float* s = a.sample + (int64_t)row * kSampleMax;
+    int rank = a.rank;
+    bool all = false;                                  // pivot -inf: every row is a candidate
+    if (a.pg.block_table) {
+        // Paged: the sample and the rank follow this sequence's length.  The
+        // sample rows past it hold -inf, below every row that counts.
+        const int64_t cb = seq_ctx(a.pg, row / a.hq, 0);
+        int64_t mb = 0;                                // sampled rows below cb
+        for (int j = 0; 16 * j < a.m; ++j) {            // block j: samples 16j .. 16j+15 (< m)
+            const int64_t in_block = a.m - 16 * j < 16 ? a.m - 16 * j : 16;
+            const int64_t v = cb - (int64_t)j * a.stride;
+            mb += v < 0 ? 0 : (v > in_block ? in_block : v);
+        }
+        if ((int64_t)a.top_n >= cb || mb == 0) {
+            all = true;
+        } else if (mb == cb) {
+            rank = a.top_n;
+        } else {
+            const double mu = (double)a.top_n * (double)mb / (double)cb;
+            const double r = ceil(mu + 5.0 * sqrt(mu) + 5.0);
+            rank = (int)(r < (double)mb ? r : (double)mb);
+        }
+    }
     for (int k = threadIdx.x; k < a.m; k += kBlock) keys[k] = float_key(s[k]);
     __syncthreads();
-    const uint32_t key = lds_radix_select(keys, (uint32_t)a.m, (uint32_t)a.rank, w);
+    const uint32_t key = lds_radix_select(keys, (uint32_t)a.m, (uint32_t)rank, w);
     if (threadIdx.x == 0) {
-        a.pivot[row] = key_float(key);
+        a.pivot[row] = all ? -INFINITY : key_float(key);
         if (a.group_flags) {
             const int b = row / a.hq;
             a.group_flags[b * a.hk + (row - b * a.hq) / a.Gk] = 0u;
@@ -174,8 +208,8 @@ __global__ __launch_bounds__(kBlock) void pivot_kernel(SampleArgs a)
 // Exact N-th largest of one row by recomputing its logits (three radix passes
 // over the row's key head, each with the shared QK tile).  Used when the
 // candidate lists cannot answer.
-template <int D, int U>
-__device__ uint32_t select_by_recompute(const FinalArgs& a, int row, SelectLds& w)
+template <int D, int U, bool PAGED>
+__device__ uint32_t select_by_recompute(const FinalArgs& a, int row, int64_t ctx, SelectLds& w)
 {
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
@@ -190,15 +224,27 @@ __device__ uint32_t select_by_recompute(const FinalArgs& a, int row, SelectLds& 
         const uint32_t dm = digit_mask(pass), pm = prefix_mask(pass);
         for (int k = threadIdx.x; k < kHistBins; k += kBlock) w.hist[k] = 0u;
         __syncthreads();
-        for (int64_t t0 = wave * 16 * U; t0 < a.ctx; t0 += kWavesPerBlock * 16 * U) {
+        for (int64_t t0 = wave * 16 * U; t0 < ctx; t0 += kWavesPerBlock * 16 * U) {
             KTile<D, U> kt;
-            load_ktile<D, U>(kt, khead, t0, a.ctx);
+            if constexpr (PAGED) {
+                // The tile lies in one page; a page outside the pool reads zeros.
+                const int64_t base = page_base<D>(a.pg, b, g, a.hk, t0);
+                const uint16_t* p = base < 0 ? nullptr
+                                             : a.k + base + (t0 % a.pg.page_rows + col) * D + 8 * grp;
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int m = 0; m < D / 32; ++m)
+                        kt.v[u][m] = p ? ld16_stream(p + 16 * u * D + 32 * m) : u32x4{0u, 0u, 0u, 0u};
+            } else {
+                load_ktile<D, U>(kt, khead, t0, ctx);
+            }
             float s[U][4];
             qk_tile<D, U>(qf, kt, a.scale, s);
             if (grp == (slot >> 2)) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    if (t0 + 16 * u + col >= a.ctx) continue;
+                    if (t0 + 16 * u + col >= ctx) continue;
                     float v = s[u][0];
 #pragma unroll
                     for (int ii = 1; ii < 4; ++ii)
@@ -217,13 +263,18 @@ __device__ uint32_t select_by_recompute(const FinalArgs& a, int row, SelectLds& 
     return prefix;
 }
 
-template <int D, int U>
+template <int D, int U, bool PAGED>
 __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
 {
     __shared__ int32_t pre[kMaxListsPerRow + 1];
     __shared__ uint32_t keys[kFinalStage];
     __shared__ SelectLds w;
     const int row = blockIdx.x, t = threadIdx.x;
+    const int64_t ctx = PAGED ? seq_ctx(a.pg, row / a.hq, a.ctx) : a.ctx;
+    if (PAGED && (int64_t)a.top_n >= ctx) {            // N covers the sequence: keep everything
+        if (t == 0) a.tau[row] = -INFINITY;
+        return;
+    }
     const int nl = a.chunks * kWavesPerBlock;
     const int64_t lbase = (int64_t)row * nl;
     const int64_t capw = a.rows_per_chunk / kWavesPerBlock;
@@ -281,7 +332,7 @@ __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
         __syncthreads();
         key = lds_radix_select(keys, total, a.top_n, w);
     } else {
-        key = select_by_recompute<D, U>(a, row, w);
+        key = select_by_recompute<D, U, PAGED>(a, row, ctx, w);
         // The lists miss entries of this row: a fused decode must re-stream its group.
         if (t == 0 && a.group_flags) {
             const int b = row / a.hq;
@@ -298,10 +349,14 @@ hipError_t launch_sample(int D, const SampleArgs& a, hipStream_t s)
     constexpr int U = 4;
     const int per_block = kWavesPerBlock * 16 * U;
     const dim3 grid((a.m + per_block - 1) / per_block, a.B * a.hk);
-    if (D == 64)
-        hipLaunchKernelGGL((sample_logits_kernel<64, U>), grid, dim3(kBlock), 0, s, a);
-    else
-        hipLaunchKernelGGL((sample_logits_kernel<128, U>), grid, dim3(kBlock), 0, s, a);
+    const bool paged = a.pg.block_table != nullptr;
+    if (D == 64) {
+        if (paged) hipLaunchKernelGGL((sample_logits_kernel<64, U, true>), grid, dim3(kBlock), 0, s, a);
+        else hipLaunchKernelGGL((sample_logits_kernel<64, U, false>), grid, dim3(kBlock), 0, s, a);
+    } else {
+        if (paged) hipLaunchKernelGGL((sample_logits_kernel<128, U, true>), grid, dim3(kBlock), 0, s, a);
+        else hipLaunchKernelGGL((sample_logits_kernel<128, U, false>), grid, dim3(kBlock), 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pivot_kernel, dim3(a.B * a.hq), dim3(kBlock), 0, s, a);
@@ -310,10 +365,13 @@ hipError_t launch_sample(int D, const SampleArgs& a, hipStream_t s)
 
 hipError_t launch_refresh_final(int D, const FinalArgs& a, hipStream_t s)
 {
-    if (D == 64)
-        hipLaunchKernelGGL((refresh_final_kernel<64, decode_unroll(64)>), dim3(a.B * a.hq), dim3(kBlock), 0, s, a);
-    else
-        hipLaunchKernelGGL((refresh_final_kernel<128, decode_unroll(128)>), dim3(a.B * a.hq), dim3(kBlock), 0, s, a);
+    const bool paged = a.pg.block_table != nullptr;
+#define SAGA_LAUNCH_FINAL(DD, PG)                                                                 \
+    hipLaunchKernelGGL((refresh_final_kernel<DD, decode_unroll(DD), PG>), dim3(a.B * a.hq),        \
+                       dim3(kBlock), 0, s, a)
+    if (D == 64) { if (paged) SAGA_LAUNCH_FINAL(64, true); else SAGA_LAUNCH_FINAL(64, false); }
+    else { if (paged) SAGA_LAUNCH_FINAL(128, true); else SAGA_LAUNCH_FINAL(128, false); }
+#undef SAGA_LAUNCH_FINAL
     return hipGetLastError();
 }
 

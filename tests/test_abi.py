@@ -169,3 +169,42 @@ def test_full_attention_unsupported_head_maps():
     # 32 query heads per value head exceeds the dense kernel's per-value-head slots.
     d = good_dims(h_q=32, h_k=2, h_v=1, head_dim=64)
     assert call_full(d, 1 << 40) == UNSUPPORTED
+
+
+# ---- paged caches -----------------------------------------------------------
+
+def good_paged(**kw):
+    base = dict(block_table_dev=(1 << 20), ctx_lens_dev=(1 << 21), page_rows=256, max_pages=4,
+                num_pages=16, reserved=0)
+    base.update(kw)
+    return saga.SagaPaged(**base)
+
+
+def call_paged(kind, d, p, ws_bytes, top_n=8):
+    lib = saga.library()
+    pp = ctypes.byref(p) if p is not None else None
+    if kind == "refresh":
+        return lib.atopn_refresh_thresholds_paged(ctypes.byref(d), pp, top_n, FAKE, FAKE, FAKE,
+                                                  FAKE, ws_bytes, None)
+    if kind == "decode":
+        return lib.saga_decode_step_paged(ctypes.byref(d), pp, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                          FAKE, ws_bytes, None)
+    return lib.atopn_refresh_decode_step_paged(ctypes.byref(d), pp, top_n, FAKE, FAKE, FAKE, FAKE,
+                                               FAKE, None, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kind", ["refresh", "decode", "fused"])
+def test_paged_argument_checks(kind):
+    d = good_dims(cache_len=1024, ctx_len=1000)         # 4 pages of 256 rows
+    need = saga.saga_workspace_bytes(d, 8)
+    assert call_paged(kind, d, None, 1 << 40) == INVALID
+    assert call_paged(kind, d, good_paged(page_rows=128, max_pages=8), 1 << 40) == INVALID
+    assert call_paged(kind, d, good_paged(page_rows=300), 1 << 40) == INVALID
+    assert call_paged(kind, d, good_paged(max_pages=3), 1 << 40) == INVALID   # != cache_len
+    assert call_paged(kind, d, good_paged(num_pages=0), 1 << 40) == INVALID
+    assert call_paged(kind, d, good_paged(reserved=1), 1 << 40) == INVALID
+    assert call_paged(kind, d, good_paged(block_table_dev=None), 1 << 40) == INVALID
+    assert call_paged(kind, d, good_paged(ctx_lens_dev=(1 << 21) + 2), 1 << 40) == INVALID
+    # a consistent description passes validation and stops at the workspace size
+    assert call_paged(kind, d, good_paged(), need - 1) == SMALL
+    assert call_paged(kind, good_dims(cache_len=1024, head_dim=96), good_paged(), 1 << 40) == UNSUPPORTED

@@ -1,0 +1,167 @@
+"""Paged caches with per-sequence lengths (the *_paged calls) on the GPU.
+
+* Same caches, paged: the contiguous caches scattered over page pools in a
+  shuffled order give bit-identical thresholds, counts and outputs to the
+  contiguous calls (the work split is the same), also with garbage in the
+  unused page-table slots.
+* Per-sequence lengths: every sequence matches the contiguous path run on that
+  sequence alone at its own length (thresholds bit-equal, counts equal,
+  outputs within the output bar of the fp64 oracle on that mask), including a
+  sequence with N >= its length (tau = -inf, full attention).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_decode_attention_atop_amd as saga
+from gpu_helpers import make_inputs, to_np_bits
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+
+
+def to_pages(K, V, P, seed, extra=3):
+    """Scatter [B][h][rows][d] caches over pools of pages of P rows, in a
+    shuffled page order with `extra` unused pages; returns the pools and the
+    block table [B][rows/P]."""
+    B, hk, rows, d = K.shape
+    hv = V.shape[1]
+    maxp = rows // P
+    n = B * maxp + extra
+    perm = torch.from_numpy(np.random.default_rng(seed).permutation(n)[: B * maxp].astype(np.int32))
+    table = perm.view(B, maxp).cuda()
+    kp = torch.zeros(n, hk, P, d, dtype=K.dtype, device="cuda")
+    vp = torch.zeros(n, hv, P, d, dtype=V.dtype, device="cuda")
+    for b in range(B):
+        for p in range(maxp):
+            kp[table[b, p]] = K[b, :, p * P:(p + 1) * P]
+            vp[table[b, p]] = V[b, :, p * P:(p + 1) * P]
+    return kp, vp, table, n
+
+
+def run_contiguous(q, K, V, ctx_steps, N, n):
+    """Refresh at t % n == 0 (one call), decode otherwise; per-step results."""
+    T, B, hq, d = q.shape
+    hk, rows, hv = K.shape[1], K.shape[2], V.shape[1]
+    ws = saga.alloc_workspace(saga.dims(B, hq, hk, hv, d, ctx_steps[0], rows), N)
+    tau = torch.empty(B, hq, device="cuda")
+    res = []
+    for t, ctx in enumerate(ctx_steps):
+        dm = saga.dims(B, hq, hk, hv, d, ctx, rows)
+        out = torch.empty(B, hq, d, dtype=torch.bfloat16, device="cuda")
+        cnt = torch.empty(B, hq, dtype=torch.int32, device="cuda")
+        if t % n == 0:
+            saga.atopn_refresh_decode_step(dm, N, q[t], K, V, tau, out, ws, sel_counts=cnt)
+        else:
+            saga.saga_decode_step(dm, q[t], K, V, tau, out, ws, sel_counts=cnt)
+        torch.cuda.synchronize()
+        res.append((tau.clone(), cnt.clone(), out.clone()))
+    return res
+
+
+def run_paged(q, kp, vp, table, npages, P, rows, ctx_lens_steps, N, n, fused=True):
+    T, B, hq, d = q.shape
+    hk, hv = kp.shape[1], vp.shape[1]
+    ctx_lens = torch.empty(B, dtype=torch.int32, device="cuda")
+    pg = saga.paged(table, ctx_lens, P, npages)
+    ws = saga.alloc_workspace(saga.dims(B, hq, hk, hv, d, max(ctx_lens_steps[0]), rows), N)
+    tau = torch.empty(B, hq, device="cuda")
+    res = []
+    for t, lens in enumerate(ctx_lens_steps):
+        ctx_lens.copy_(torch.tensor(lens, dtype=torch.int32))
+        dm = saga.dims(B, hq, hk, hv, d, max(lens), rows)
+        out = torch.empty(B, hq, d, dtype=torch.bfloat16, device="cuda")
+        cnt = torch.empty(B, hq, dtype=torch.int32, device="cuda")
+        if t % n == 0 and fused:
+            saga.atopn_refresh_decode_step_paged(dm, pg, N, q[t], kp, vp, tau, out, ws,
+                                                 sel_counts=cnt)
+        else:
+            if t % n == 0:
+                saga.atopn_refresh_thresholds_paged(dm, pg, N, q[t], kp, tau, ws)
+            saga.saga_decode_step_paged(dm, pg, q[t], kp, vp, tau, out, ws, sel_counts=cnt)
+        torch.cuda.synchronize()
+        res.append((tau.clone(), cnt.clone(), out.clone()))
+    return res
+
+
+def bits(t):
+    return t.cpu().contiguous().view(torch.int32).numpy() if t.dtype == torch.float32 \
+        else t.cpu().contiguous().view(torch.int16).numpy()
+
+
+PAGED_SHAPES = {
+    # name: (B, hq, hk, hv, d, P, pages per sequence, N, n)
+    "qwen_like_d128": (2, 12, 1, 2, 128, 256, 14, 128, 2),
+    "llama_like_d64": (2, 32, 4, 8, 64, 512, 8, 256, 2),
+    "group16_big_pages": (1, 16, 1, 4, 64, 1024, 5, 100, 3),
+}
+
+
+@pytest.mark.parametrize("name", list(PAGED_SHAPES))
+def test_paged_equals_contiguous_bit_for_bit(name):
+    B, hq, hk, hv, d, P, maxp, N, n = PAGED_SHAPES[name]
+    rows, T = maxp * P, 4
+    q, K, V = make_inputs(B, hq, hk, hv, d, rows, T, seed=80 + len(name))
+    ctx = [rows - 3 * P // 2 + 37 * t for t in range(T)]          # ragged, inside the table
+    print(f"[paged {name}] B={B} rows={rows} P={P} ctx={ctx}", flush=True)
+    ref = run_contiguous(q, K, V, ctx, N, n)
+    kp, vp, table, npages = to_pages(K, V, P, seed=1)
+    got = run_paged(q, kp, vp, table, npages, P, rows, [[c] * B for c in ctx], N, n)
+    for t in range(T):
+        for a, b in zip(ref[t], got[t]):
+            assert np.array_equal(bits(a), bits(b)), f"step {t}"
+
+
+def test_paged_ignores_unused_table_slots():
+    B, hq, hk, hv, d, P, maxp, N, n = PAGED_SHAPES["qwen_like_d128"]
+    rows, T = maxp * P, 2
+    q, K, V = make_inputs(B, hq, hk, hv, d, rows, T, seed=90)
+    ctx = [6 * P + 11, 6 * P + 12]                                  # 7 of 14 pages in use
+    kp, vp, table, npages = to_pages(K, V, P, seed=2)
+    clean = run_paged(q, kp, vp, table, npages, P, rows, [[c] * B for c in ctx], N, n)
+    junk = table.clone()
+    junk[:, 8:] = torch.tensor([-1, 1 << 30, -(1 << 30), npages, 5, 0], dtype=torch.int32,
+                               device="cuda").repeat(B)[: B * (maxp - 8)].view(B, maxp - 8)
+    dirty = run_paged(q, kp, vp, junk, npages, P, rows, [[c] * B for c in ctx], N, n)
+    for t in range(T):
+        for a, b in zip(clean[t], dirty[t]):
+            assert np.array_equal(bits(a), bits(b))
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_per_sequence_lengths_match_each_sequence_alone(fused):
+    B, hq, hk, hv, d, P = 3, 12, 1, 2, 128, 256
+    maxp, N, n, T = 12, 200, 2, 3
+    rows = maxp * P
+    q, K, V = make_inputs(B, hq, hk, hv, d, rows, T, seed=91)
+    lens = [[2900 + t, 700 + 5 * t, 150 + t] for t in range(T)]   # the last: N >= ctx
+    kp, vp, table, npages = to_pages(K, V, P, seed=3)
+    got = run_paged(q, kp, vp, table, npages, P, rows, lens, N, n, fused=fused)
+    for b in range(B):
+        ctx_b = [lens[t][b] for t in range(T)]
+        print(f"[paged varlen b={b}] ctx={ctx_b}", flush=True)
+        qb = q[:, b:b + 1].contiguous()
+        Kb, Vb = K[b:b + 1].contiguous(), V[b:b + 1].contiguous()
+        ref = run_contiguous(qb, Kb, Vb, ctx_b, N, n)
+        for t in range(T):
+            tau_r, cnt_r, _ = ref[t]
+            tau_g, cnt_g, out_g = got[t]
+            assert np.array_equal(bits(tau_r[0]), bits(tau_g[b])), (b, t)
+            assert np.array_equal(cnt_r[0].cpu().numpy(), cnt_g[b].cpu().numpy()), (b, t)
+            if N >= ctx_b[t]:
+                assert torch.isneginf(tau_g[b]).all() and (cnt_g[b] == ctx_b[t]).all()
+            # outputs against the fp64 oracle on the selection of this step
+            dm = saga.dims(1, hq, hk, hv, d, ctx_b[t], rows)
+            ws = saga.alloc_workspace(dm, 1)
+            bm = torch.empty(1, hq, (rows + 31) // 32, dtype=torch.int32, device="cuda")
+            o1 = torch.empty(1, hq, d, dtype=torch.bfloat16, device="cuda")
+            saga.saga_decode_step(dm, qb[t], Kb, Vb, tau_g[b:b + 1].contiguous(), o1, ws,
+                                  sel_bitmap_debug=bm)
+            torch.cuda.synchronize()
+            ref_o, cnt_o = oracle.masked(to_np_bits(qb[t]), to_np_bits(Kb), to_np_bits(Vb),
+                                         ctx_b[t], bm.cpu().numpy().view(np.uint32))
+            assert (cnt_o[0] == cnt_g[b].cpu().numpy()).all()
+            err = np.abs(out_g[b].float().cpu().numpy() - ref_o[0]).max()
+            assert err <= OUT_TOL, f"b={b} t={t}: {err:.3e}"
