@@ -92,6 +92,10 @@ def parse():
                         "the known-size kernel that scales rocprofv3 byte counters)")
     p.add_argument("--eager-only", action="store_true",
                    help="one eager pass over the decode steps, no timing (for counter runs)")
+    p.add_argument("--paged", type=int, default=0,
+                   help="time the schedule on paged caches with pages of this many rows")
+    p.add_argument("--varlen", action="store_true",
+                   help="with --paged: per-sequence lengths drawn from [L/4, L]")
     p.add_argument("--sweep", action="store_true",
                    help="Llama-like and Qwen-like shapes over L x N x B: SAGA Atop-N vs the "
                         "full-attention GQA path, one JSON line per point")
@@ -225,6 +229,88 @@ def run_saga(torch, saga, wl, w, args):
     sec, wall = time_graphs(torch, graphs, args.steps, args.warmup)
     return dict(layers=layers, launches=launches, refreshes=refreshes, sec=sec, wall=wall,
                 ws=ws, graphs=graphs)
+
+
+def to_pages(torch, X, P, perm):
+    """[B][h][rows][d] cache -> pool [pages][h][P][d] (zero-padded last page),
+    sequence b's page p stored at pool page perm[b * max_pages + p]."""
+    B, h, rows, d = X.shape
+    maxp = -(-rows // P)
+    Xp = torch.zeros(B, h, maxp * P, d, dtype=X.dtype, device=X.device)
+    Xp[:, :, :rows] = X
+    Y = Xp.view(B, h, maxp, P, d).permute(0, 2, 1, 3, 4).reshape(B * maxp, h, P, d)
+    del Xp
+    pool = torch.empty_like(Y)
+    pool[torch.from_numpy(perm.astype("int64")).to(X.device)] = Y
+    return pool
+
+
+def run_saga_paged(torch, saga, wl, w, args):
+    """The main schedule on paged caches (pages of args.paged rows, shuffled in
+    the pools).  With args.varlen, sequence b attends L_b + t rows, L_b drawn
+    (seeded) uniformly from [L/4, L]; otherwise every sequence attends L + t."""
+    import numpy as np
+    T, L, P = w.steps, w.L, args.paged
+    maxp = -(-w.rows // P)
+    cache_len = maxp * P
+    rng = np.random.default_rng(7)
+    Lb = (rng.integers(L // 4, L + 1, size=w.batch) if args.varlen
+          else np.full(w.batch, L)).astype(np.int64)
+    perm = rng.permutation(w.batch * maxp).astype(np.int32)
+    table = torch.from_numpy(perm).view(w.batch, maxp).cuda()
+    ctx_lens = torch.empty(w.batch, dtype=torch.int32, device="cuda")
+    pg = saga.paged(table, ctx_lens, P, w.batch * maxp)
+    layers = []
+    log(f"generating {w.layers} paged layers of {w.name} (pages of {P} rows)")
+    for layer in range(w.layers):
+        K, V, q = layer_inputs(torch, wl, w, layer)
+        kp, vp = to_pages(torch, K, P, perm), to_pages(torch, V, P, perm)
+        del K, V
+        layers.append(dict(K=kp, V=vp, q=q,
+                           tau=torch.empty(w.batch, w.h_q, dtype=torch.float32, device="cuda"),
+                           out=torch.empty(w.batch, w.h_q, w.head_dim, dtype=torch.bfloat16,
+                                           device="cuda"),
+                           cnt=torch.empty(w.batch, w.h_q, dtype=torch.int32, device="cuda")))
+        log(f"  layer {layer} ready")
+    lens = [torch.from_numpy((Lb + t).astype(np.int32)).cuda() for t in range(T)]
+    ws = saga.alloc_workspace(saga.dims(w.batch, w.h_q, w.h_k, w.h_v, w.head_dim, int(Lb.max()),
+                                        cache_len, w.scale), w.top_n)
+
+    def step(t):
+        ctx_lens.copy_(lens[t])
+        dm = saga.dims(w.batch, w.h_q, w.h_k, w.h_v, w.head_dim, int(Lb.max()) + t, cache_len,
+                       w.scale)
+        for x in layers:
+            if t % w.refresh_n == 0:
+                saga.atopn_refresh_decode_step_paged(dm, pg, w.top_n, x["q"][t], x["K"], x["V"],
+                                                     x["tau"], x["out"], ws, sel_counts=x["cnt"])
+            else:
+                saga.saga_decode_step_paged(dm, pg, x["q"][t], x["K"], x["V"], x["tau"],
+                                            x["out"], ws, sel_counts=x["cnt"])
+
+    sel = 0
+    for t in range(T):
+        step(t)
+        torch.cuda.synchronize()
+        sel += sum(int(x["cnt"].sum().item()) for x in layers)
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for t in range(T):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                step(t)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} paged steps after {args.warmup} warmup steps")
+    sec, _ = time_graphs(torch, graphs, args.steps, args.warmup)
+    d = w.head_dim
+    k_bytes = w.layers * w.h_k * d * 2 * sum(int((Lb + t).sum()) for t in range(T)) / T
+    step_bytes = (k_bytes + sel * d * 2 / T
+                  + w.layers * (2 * w.batch * w.h_q * d * 2 + w.batch * w.h_q * 4))
+    return dict(sec=sec, step_bytes=step_bytes, ctx=Lb.tolist())
 
 
 def run_gqa(torch, saga, wl, w, hkv, args):
@@ -383,6 +469,19 @@ def main():
         return
     if args.decompose:
         decompose(torch, saga, wl, args)
+        return
+    if args.paged:
+        w = wl.WORKLOADS[args.workload]
+        res = run_saga_paged(torch, saga, wl, w, args)
+        sps = args.steps / res["sec"]
+        gbs = res["step_bytes"] / (res["sec"] / args.steps) / 1e9
+        print(json.dumps({"metric": "decode-attn steps/s on paged caches", "value": round(sps, 3),
+                          "unit": "steps/s", "ms_per_step": round(1e3 * res["sec"] / args.steps, 4),
+                          "steps": args.steps, "warmup": args.warmup,
+                          "hbm_gbs_step": round(gbs, 1), "hbm_frac_step": round(gbs / HBM_PEAK_GBS, 4),
+                          "config": {"workload": w.name, "page_rows": args.paged,
+                                     "varlen": bool(args.varlen), "ctx_lens_at_t0": res["ctx"]}}),
+              flush=True)
         return
     w = wl.WORKLOADS[args.workload]
     res = run_saga(torch, saga, wl, w, args)

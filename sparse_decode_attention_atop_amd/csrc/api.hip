@@ -281,6 +281,10 @@ int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunkin
     ga.rows_per_chunk = ch.rows;
     ga.chunks = ch.chunks;
     ga.pg = pg;
+    if (pg.block_table) {
+        const uint64_t pool = (uint64_t)pg.num_pages * dims->h_v * pg.page_rows * D * 2;
+        ga.pool_bytes = pool + 16 * D <= (uint64_t)kPoolLimit ? (uint32_t)pool : 0u;
+    }
     int64_t segs = (gather_target_blocks(D) + rows - 1) / rows;
     if (segs > kGatherMaxSegs) segs = kGatherMaxSegs;
     if (segs > L.max_chunks) segs = L.max_chunks;       // partials hold max_chunks per row

@@ -287,7 +287,9 @@ __device__ int32_t block_scan(int32_t v, int32_t* red)
 // value head (under 2 GiB); entries that carry no weight get an offset past
 // the resource's end, which reads zero without touching memory, so the loads
 // need no branch.
-template <int D, bool PAGED>
+// PAGED: 0 contiguous caches; 1 paged, V pool under 4 GiB (32-bit offsets into
+// the pool, same load path as contiguous); 2 paged, 64-bit addresses.
+template <int D, int PAGED>
 __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherArgs a)
 {
     constexpr int LPR = D / 8;             // lanes per value row (16 bytes each)
@@ -297,13 +299,14 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
     constexpr int NB = SAGA_GATHER_NB;     // rows in flight per lane
     constexpr int PER = kMaxListsPerRow / kBlock;
     constexpr uint32_t kNoRow = 0x80000000u;   // past any value head (< 2^31 bytes)
+    constexpr uint32_t kNoRowPool = kPoolLimit;  // past any 32-bit-addressed pool
     static_assert(SLOTS * D <= kMaxListsPerRow, "slot reduction reuses the prefix array");
     static_assert(CAPL % kBlock == 0, "staging rounds are whole threads");
     __shared__ int32_t pre[kMaxListsPerRow + 1];
     __shared__ int32_t red[kWavesPerBlock];
     __shared__ uint32_t eoff[CAPL];     // byte offset in the value head; paged: row in page
     __shared__ float ew[CAPL];
-    __shared__ int32_t eps[PAGED ? CAPL : 1];   // paged: page * h_v + value head, -1 if none
+    __shared__ int32_t eps[PAGED == 2 ? CAPL : 1];   // page * h_v + value head, -1 if none
 
     const int seg = blockIdx.x;
     const int bi = blockIdx.y;
@@ -338,7 +341,10 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
 
     const int nu = i / a.Gv;
     const uint16_t* vh = a.v + ((int64_t)(b * a.hv + nu) * a.cache_len) * D;
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh, (uint32_t)(PAGED ? 0 : a.cache_len * D * 2));
+    // Contiguous: the value head; paged (32-bit): the whole pool.
+    const __amdgpu_buffer_rsrc_t vrs =
+        PAGED == 1 ? make_rsrc(a.v, a.pool_bytes)
+                   : make_rsrc(vh, (uint32_t)(PAGED ? 0 : a.cache_len * D * 2));
     const int slot = t / LPR, lc = t - slot * LPR;
     const float tf = a.tau_filter ? a.tau_filter[bi] : -INFINITY;
     float acc[8];
@@ -383,8 +389,14 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
                     kept += keep;
                     const int64_t r = (int64_t)(lo[k] / kWavesPerBlock) * a.rows_per_chunk + ent[k].x;
                     const bool ok = page[k] >= 0 && page[k] < a.pg.num_pages;   // else reads nothing
-                    eoff[e] = (uint32_t)(r % a.pg.page_rows);
-                    eps[e] = ok ? page[k] * a.hv + nu : -1;
+                    if constexpr (PAGED == 1) {
+                        eoff[e] = keep && ok ? (uint32_t)((((int64_t)page[k] * a.hv + nu) *
+                                                           a.pg.page_rows + r % a.pg.page_rows) * (D * 2))
+                                             : kNoRowPool;
+                    } else {
+                        eoff[e] = (uint32_t)(r % a.pg.page_rows);
+                        eps[e] = ok ? page[k] * a.hv + nu : -1;
+                    }
                     ew[e] = keep && ok ? __expf(sv - M) : 0.f;
                 }
             }
@@ -411,11 +423,13 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
                 const int e = e0 + k * SLOTS;
                 const bool in = e < n;
                 w[k] = in ? ew[e] : 0.f;
-                if constexpr (PAGED) {
+                if constexpr (PAGED == 2) {
                     if (w[k] > 0.f)                     // weight zero: no row (or no page)
                         vv[k] = ld16(a.v + ((int64_t)eps[e] * a.pg.page_rows + eoff[e]) * D + 8 * lc);
                     else
                         vv[k] = u32x4{0u, 0u, 0u, 0u};
+                } else if constexpr (PAGED == 1) {
+                    vv[k] = buf_ld16(vrs, (in ? eoff[e] : kNoRowPool) + 16u * lc);
                 } else {
                     vv[k] = buf_ld16(vrs, (in ? eoff[e] : kNoRow) + 16u * lc);
                 }
@@ -565,14 +579,18 @@ hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t s)
 hipError_t launch_gather(int D, const GatherArgs& a, hipStream_t s)
 {
     const dim3 grid(a.segs, a.B * a.hq);
-    const bool paged = a.pg.block_table != nullptr;
+    const int mode = a.pg.block_table == nullptr ? 0 : (a.pool_bytes != 0 ? 1 : 2);
+#define SAGA_LAUNCH_GATHER(DD, M) hipLaunchKernelGGL((gather_kernel<DD, M>), grid, dim3(kBlock), 0, s, a)
     if (D == 64) {
-        if (paged) hipLaunchKernelGGL((gather_kernel<64, true>), grid, dim3(kBlock), 0, s, a);
-        else hipLaunchKernelGGL((gather_kernel<64, false>), grid, dim3(kBlock), 0, s, a);
+        if (mode == 0) SAGA_LAUNCH_GATHER(64, 0);
+        else if (mode == 1) SAGA_LAUNCH_GATHER(64, 1);
+        else SAGA_LAUNCH_GATHER(64, 2);
     } else {
-        if (paged) hipLaunchKernelGGL((gather_kernel<128, true>), grid, dim3(kBlock), 0, s, a);
-        else hipLaunchKernelGGL((gather_kernel<128, false>), grid, dim3(kBlock), 0, s, a);
+        if (mode == 0) SAGA_LAUNCH_GATHER(128, 0);
+        else if (mode == 1) SAGA_LAUNCH_GATHER(128, 1);
+        else SAGA_LAUNCH_GATHER(128, 2);
     }
+#undef SAGA_LAUNCH_GATHER
     return hipGetLastError();
 }
 

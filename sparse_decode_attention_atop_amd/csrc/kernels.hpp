@@ -72,6 +72,9 @@ __device__ __forceinline__ int64_t list_index(int64_t lid, uint32_t E, int64_t c
 // block_table == nullptr the caches are contiguous [B][heads][cache_len][d]
 // and every sequence attends the call's ctx rows.
 constexpr int kPageQuantum = 256;
+// Pools below this many bytes are read with 32-bit offsets; this offset (and
+// any above it) reads zeros.
+constexpr uint32_t kPoolLimit = 0xFFFFF000u;
 struct PagedKV {
     const int32_t* block_table;   // [B][max_pages], nullptr: contiguous caches
     const int32_t* ctx_lens;      // [B]
@@ -133,6 +136,7 @@ struct GatherArgs {
     const float* list_max;
     const float* tau_filter; // nullable [B*hq]: keep only entries with logit >= tau_filter
     Partials part;           // one partial per (b*h_q + i, segment)
+    uint32_t pool_bytes;     // paged: V pool bytes when below kPoolLimit (32-bit offsets), else 0
     int32_t B, hq, hv, Gv;
     int64_t cache_len, rows_per_chunk;
     int32_t chunks, segs;    // segs: equal entry ranges per (b, query head)

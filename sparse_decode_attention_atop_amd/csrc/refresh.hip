@@ -177,12 +177,20 @@ __global__ __launch_bounds__(kBlock) void pivot_kernel(SampleArgs a)
         // Paged: the sample and the rank follow this sequence's length.  The
         // sample rows past it hold -inf, below every row that counts.
         const int64_t cb = seq_ctx(a.pg, row / a.hq, 0);
-        int64_t mb = 0;                                // sampled rows below cb
-        for (int j = 0; 16 * j < a.m; ++j) {            // block j: samples 16j .. 16j+15 (< m)
+        // Sampled rows below cb: block j holds samples 16j .. min(16j+16, m)-1
+        // at rows j*stride + 0..15; one block per thread, then a block sum.
+        int32_t part = 0;
+        for (int j = threadIdx.x; 16 * j < a.m; j += kBlock) {
             const int64_t in_block = a.m - 16 * j < 16 ? a.m - 16 * j : 16;
             const int64_t v = cb - (int64_t)j * a.stride;
-            mb += v < 0 ? 0 : (v > in_block ? in_block : v);
+            part += (int32_t)(v < 0 ? 0 : (v > in_block ? in_block : v));
         }
+        for (int off = kWave / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
+        if (lane_id() == 0) w.scan[threadIdx.x / kWave] = (uint32_t)part;
+        __syncthreads();
+        int64_t mb = 0;
+        for (int k = 0; k < kWavesPerBlock; ++k) mb += w.scan[k];
+        __syncthreads();
         if ((int64_t)a.top_n >= cb || mb == 0) {
             all = true;
         } else if (mb == cb) {

@@ -165,3 +165,31 @@ def test_per_sequence_lengths_match_each_sequence_alone(fused):
             assert (cnt_o[0] == cnt_g[b].cpu().numpy()).all()
             err = np.abs(out_g[b].float().cpu().numpy() - ref_o[0]).max()
             assert err <= OUT_TOL, f"b={b} t={t}: {err:.3e}"
+
+
+def test_paged_pool_beyond_4gib():
+    """A V pool over 4 GiB takes the 64-bit address path of the gather; the
+    data pages sit at the top of the pools."""
+    B, hq, hk, hv, d, P, maxp, N, n = 2, 12, 1, 2, 128, 256, 6, 128, 2
+    rows, T = maxp * P, 2
+    q, K, V = make_inputs(B, hq, hk, hv, d, rows, T, seed=92)
+    ctx = [rows - 100, rows - 99]
+    ref = run_contiguous(q, K, V, ctx, N, n)
+    page_bytes_v = hv * P * d * 2
+    npages = (1 << 32) // page_bytes_v + 64                        # V pool > 4 GiB
+    print(f"[paged >4GiB] V pool {npages * page_bytes_v / 2**30:.2f} GiB", flush=True)
+    top = torch.arange(npages - B * maxp, npages, dtype=torch.int32)
+    perm = top[torch.from_numpy(np.random.default_rng(4).permutation(B * maxp))]
+    table = perm.view(B, maxp).cuda()
+    kp = torch.zeros(npages, hk, P, d, dtype=K.dtype, device="cuda")
+    vp = torch.zeros(npages, hv, P, d, dtype=V.dtype, device="cuda")
+    for b in range(B):
+        for p in range(maxp):
+            kp[table[b, p]] = K[b, :, p * P:(p + 1) * P]
+            vp[table[b, p]] = V[b, :, p * P:(p + 1) * P]
+    got = run_paged(q, kp, vp, table, npages, P, rows, [[c] * B for c in ctx], N, n)
+    del kp, vp
+    torch.cuda.empty_cache()
+    for t in range(T):
+        for a, b in zip(ref[t], got[t]):
+            assert np.array_equal(bits(a), bits(b)), f"step {t}"
