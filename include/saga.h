@@ -202,6 +202,36 @@ int atopn_refresh_decode_step_paged(const saga_dims* dims, const saga_paged* pag
                                     size_t workspace_bytes, void* stream);
 
 /*
+ * Several query tokens per query head and step (speculative verification,
+ * chunked prefill): the pages count the value vectors of a step as
+ * h_q x l_q x N, one selection of N per query token.  Token j (0-based) of the
+ * step sits at row ctx_len - l_q + j of the caches (the step's own rows are
+ * already in them) and attends rows 0 .. ctx_len - l_q + j; it has its own
+ * threshold, refreshed on the same schedule.  Per token the results equal the
+ * one-token calls with that token's q at ctx_len - (l_q - 1 - j).
+ *
+ *   q_dev          bf16 [batch][h_q][l_q][head_dim]
+ *   thresholds_dev fp32 [batch][h_q][l_q]
+ *   out_dev        bf16 [batch][h_q][l_q][head_dim]
+ *   sel_counts_dev optional int32 [batch][h_q][l_q]
+ *   workspace      saga_workspace_bytes() of dims with h_q replaced by h_q * l_q
+ * Requires 1 <= l_q <= ctx_len and (h_q / h_k) * l_q <= 16 (UNSUPPORTED
+ * otherwise).  Errors otherwise as the one-token calls.
+ */
+int atopn_refresh_thresholds_lq(const saga_dims* dims, int32_t l_q, int32_t top_n,
+                                const void* q_dev, const void* k_cache_dev, float* thresholds_dev,
+                                void* workspace_dev, size_t workspace_bytes, void* stream);
+int saga_decode_step_lq(const saga_dims* dims, int32_t l_q, const void* q_dev,
+                        const void* k_cache_dev, const void* v_cache_dev,
+                        const float* thresholds_dev, void* out_dev, int32_t* sel_counts_dev,
+                        void* workspace_dev, size_t workspace_bytes, void* stream);
+int atopn_refresh_decode_step_lq(const saga_dims* dims, int32_t l_q, int32_t top_n,
+                                 const void* q_dev, const void* k_cache_dev,
+                                 const void* v_cache_dev, float* thresholds_dev, void* out_dev,
+                                 int32_t* sel_counts_dev, void* workspace_dev,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * Full (dense) decode attention over all ctx_len rows with the same head maps:
  * the full-attention GQA baseline the pages time against when h_k == h_v, and
  * "SAGA full attention" when h_k < h_v (ai.info summary, Main Findings:

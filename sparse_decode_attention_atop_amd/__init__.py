@@ -22,13 +22,17 @@ __all__ = [
     "SagaDims", "SagaError", "dims", "library", "saga_workspace_bytes", "alloc_workspace",
     "atopn_refresh_thresholds", "saga_decode_step", "atopn_refresh_decode_step",
     "SagaPaged", "paged", "atopn_refresh_thresholds_paged", "saga_decode_step_paged",
-    "atopn_refresh_decode_step_paged", "saga_full_attention", "saga_status_string", "saga_version", "LIB_PATH", "EXPORTED_SYMBOLS",
+    "atopn_refresh_decode_step_paged", "atopn_refresh_thresholds_lq", "saga_decode_step_lq",
+    "atopn_refresh_decode_step_lq", "alloc_workspace_lq", "saga_full_attention",
+    "saga_status_string", "saga_version", "LIB_PATH", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsaga.so")
 EXPORTED_SYMBOLS = ("saga_workspace_bytes", "atopn_refresh_thresholds", "saga_decode_step",
                     "atopn_refresh_decode_step", "atopn_refresh_thresholds_paged",
                     "saga_decode_step_paged", "atopn_refresh_decode_step_paged",
+                    "atopn_refresh_thresholds_lq", "saga_decode_step_lq",
+                    "atopn_refresh_decode_step_lq",
                     "saga_full_attention", "saga_status_string", "saga_version")
 
 SAGA_OK = 0
@@ -106,6 +110,13 @@ def library():
         lib.atopn_refresh_decode_step_paged.argtypes = [pd, pp, i32, vp, vp, vp, vp, vp, vp, vp,
                                                         sz, vp]
         lib.atopn_refresh_decode_step_paged.restype = ctypes.c_int
+        lib.atopn_refresh_thresholds_lq.argtypes = [pd, i32, i32, vp, vp, vp, vp, sz, vp]
+        lib.atopn_refresh_thresholds_lq.restype = ctypes.c_int
+        lib.saga_decode_step_lq.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.saga_decode_step_lq.restype = ctypes.c_int
+        lib.atopn_refresh_decode_step_lq.argtypes = [pd, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                                     sz, vp]
+        lib.atopn_refresh_decode_step_lq.restype = ctypes.c_int
         lib.saga_full_attention.argtypes = [pd, vp, vp, vp, vp, vp, sz, vp]
         lib.saga_full_attention.restype = ctypes.c_int
         lib.saga_status_string.argtypes = [ctypes.c_int]
@@ -305,6 +316,74 @@ def atopn_refresh_decode_step_paged(d: SagaDims, p: SagaPaged, top_n: int, q: to
         _ptr(thresholds, torch.float32, "thresholds"), _ptr(out, torch.bfloat16, "out"),
         _ptr(sel_counts, torch.int32, "sel_counts"), ws, nbytes, _stream(stream)),
         "atopn_refresh_decode_step_paged")
+
+
+def _lq_dims(d: SagaDims, l_q: int) -> SagaDims:
+    return SagaDims(d.batch, d.h_q * l_q, d.h_k, d.h_v, d.head_dim, 0, d.ctx_len, d.cache_len,
+                    d.scale, 0.0)
+
+
+def alloc_workspace_lq(d: SagaDims, l_q: int, top_n: int, device="cuda") -> torch.Tensor:
+    """Workspace for the *_lq calls (h_q * l_q virtual query heads)."""
+    return alloc_workspace(_lq_dims(d, l_q), top_n, device)
+
+
+def atopn_refresh_thresholds_lq(d: SagaDims, l_q: int, top_n: int, q: torch.Tensor,
+                                k_cache: torch.Tensor, thresholds: torch.Tensor,
+                                workspace: torch.Tensor, stream=None) -> None:
+    """Thresholds [B][h_q][l_q] of a step with l_q query tokens per head."""
+    n = d.batch * d.h_q * l_q
+    _need(q, n * d.head_dim, "q")
+    _need(k_cache, d.batch * d.h_k * d.cache_len * d.head_dim, "k_cache")
+    _need(thresholds, n, "thresholds")
+    ws, nbytes = _ws(workspace)
+    _check(library().atopn_refresh_thresholds_lq(
+        ctypes.byref(d), int(l_q), int(top_n), _ptr(q, torch.bfloat16, "q"),
+        _ptr(k_cache, torch.bfloat16, "k_cache"), _ptr(thresholds, torch.float32, "thresholds"),
+        ws, nbytes, _stream(stream)), "atopn_refresh_thresholds_lq")
+
+
+def saga_decode_step_lq(d: SagaDims, l_q: int, q: torch.Tensor, k_cache: torch.Tensor,
+                        v_cache: torch.Tensor, thresholds: torch.Tensor, out: torch.Tensor,
+                        workspace: torch.Tensor, sel_counts: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+    """A decode step with l_q query tokens per head (causal among them)."""
+    n = d.batch * d.h_q * l_q
+    _need(q, n * d.head_dim, "q")
+    _need(k_cache, d.batch * d.h_k * d.cache_len * d.head_dim, "k_cache")
+    _need(v_cache, d.batch * d.h_v * d.cache_len * d.head_dim, "v_cache")
+    _need(thresholds, n, "thresholds")
+    _need(out, n * d.head_dim, "out")
+    _need(sel_counts, n, "sel_counts")
+    ws, nbytes = _ws(workspace)
+    _check(library().saga_decode_step_lq(
+        ctypes.byref(d), int(l_q), _ptr(q, torch.bfloat16, "q"),
+        _ptr(k_cache, torch.bfloat16, "k_cache"), _ptr(v_cache, torch.bfloat16, "v_cache"),
+        _ptr(thresholds, torch.float32, "thresholds"), _ptr(out, torch.bfloat16, "out"),
+        _ptr(sel_counts, torch.int32, "sel_counts"), ws, nbytes, _stream(stream)),
+        "saga_decode_step_lq")
+
+
+def atopn_refresh_decode_step_lq(d: SagaDims, l_q: int, top_n: int, q: torch.Tensor,
+                                 k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 thresholds: torch.Tensor, out: torch.Tensor,
+                                 workspace: torch.Tensor,
+                                 sel_counts: Optional[torch.Tensor] = None, stream=None) -> None:
+    """A refresh step with l_q query tokens per head."""
+    n = d.batch * d.h_q * l_q
+    _need(q, n * d.head_dim, "q")
+    _need(k_cache, d.batch * d.h_k * d.cache_len * d.head_dim, "k_cache")
+    _need(v_cache, d.batch * d.h_v * d.cache_len * d.head_dim, "v_cache")
+    _need(thresholds, n, "thresholds")
+    _need(out, n * d.head_dim, "out")
+    _need(sel_counts, n, "sel_counts")
+    ws, nbytes = _ws(workspace)
+    _check(library().atopn_refresh_decode_step_lq(
+        ctypes.byref(d), int(l_q), int(top_n), _ptr(q, torch.bfloat16, "q"),
+        _ptr(k_cache, torch.bfloat16, "k_cache"), _ptr(v_cache, torch.bfloat16, "v_cache"),
+        _ptr(thresholds, torch.float32, "thresholds"), _ptr(out, torch.bfloat16, "out"),
+        _ptr(sel_counts, torch.int32, "sel_counts"), ws, nbytes, _stream(stream)),
+        "atopn_refresh_decode_step_lq")
 
 
 def saga_full_attention(d: SagaDims, q: torch.Tensor, k_cache: torch.Tensor,

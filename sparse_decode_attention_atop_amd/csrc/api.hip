@@ -134,10 +134,18 @@ Partials partials(void* ws, const Layout& L)
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SAGA_OK : SAGA_ERR_HIP; }
 
+// What each (b, query head) row attends: paged caches and per-sequence
+// lengths (pg), and query tokens per step (lq; the call's h_q then counts
+// virtual heads, one per token).
+struct RowModel {
+    PagedKV pg{};
+    int32_t lq = 1;
+};
+
 // Arguments of the stream-select kernel for one call.
 SelectStreamArgs stream_args(const saga_dims* dims, const Layout& L, const Chunking& ch,
                              const void* q, const void* k, const float* tau, void* ws,
-                             const PagedKV& pg)
+                             const RowModel& rm)
 {
     unsigned char* w = static_cast<unsigned char*>(ws);
     SelectStreamArgs a{};
@@ -157,7 +165,8 @@ SelectStreamArgs stream_args(const saga_dims* dims, const Layout& L, const Chunk
     a.rows_per_chunk = ch.rows;
     a.chunks = ch.chunks;
     a.scale = dims->scale;
-    a.pg = pg;
+    a.pg = rm.pg;
+    a.lq = rm.lq;
     return a;
 }
 
@@ -178,7 +187,7 @@ namespace {
 int enqueue_refresh(const saga_dims* dims, int32_t top_n, const void* q_dev,
                     const void* k_cache_dev, float* thresholds_dev, float* logits_debug_dev,
                     void* workspace_dev, const Layout& L, const Chunking& ch, hipStream_t s,
-                    uint32_t* group_flags, const PagedKV& pg)
+                    uint32_t* group_flags, const RowModel& rm)
 {
     unsigned char* w = static_cast<unsigned char*>(workspace_dev);
     const int D = dims->head_dim;
@@ -220,12 +229,14 @@ int enqueue_refresh(const saga_dims* dims, int32_t top_n, const void* q_dev,
     }
     sa.scale = dims->scale;
     sa.top_n = top_n;
-    sa.pg = pg;
+    sa.ctx = dims->ctx_len;
+    sa.pg = rm.pg;
+    sa.lq = rm.lq;
     int st = hip_status(launch_sample(D, sa, s));
     if (st != SAGA_OK) return st;
 
     // 3. Candidate lists: every logit >= pivot.
-    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, pivot, workspace_dev, pg);
+    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_cache_dev, pivot, workspace_dev, rm);
     a.logits_out = logits_debug_dev;
     st = hip_status(launch_select_stream(D, a, s));
     if (st != SAGA_OK) return st;
@@ -249,7 +260,8 @@ int enqueue_refresh(const saga_dims* dims, int32_t top_n, const void* q_dev,
     fa.chunks = ch.chunks;
     fa.top_n = (uint32_t)top_n;
     fa.scale = dims->scale;
-    fa.pg = pg;
+    fa.pg = rm.pg;
+    fa.lq = rm.lq;
     return hip_status(launch_refresh_final(D, fa, s));
 }
 
@@ -258,7 +270,7 @@ int enqueue_refresh(const saga_dims* dims, int32_t top_n, const void* q_dev,
 int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunking& ch,
                            const void* v_cache_dev, const float* tau_filter, void* out_dev,
                            int32_t* sel_counts_dev, void* workspace_dev, hipStream_t s,
-                           const PagedKV& pg)
+                           const RowModel& rm)
 {
     unsigned char* w = static_cast<unsigned char*>(workspace_dev);
     const int D = dims->head_dim;
@@ -280,9 +292,9 @@ int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunkin
     ga.cache_len = dims->cache_len;
     ga.rows_per_chunk = ch.rows;
     ga.chunks = ch.chunks;
-    ga.pg = pg;
-    if (pg.block_table) {
-        const uint64_t pool = (uint64_t)pg.num_pages * dims->h_v * pg.page_rows * D * 2;
+    ga.pg = rm.pg;
+    if (rm.pg.block_table) {
+        const uint64_t pool = (uint64_t)rm.pg.num_pages * dims->h_v * rm.pg.page_rows * D * 2;
         ga.pool_bytes = pool + 16 * D <= (uint64_t)kPoolLimit ? (uint32_t)pool : 0u;
     }
     int64_t segs = (gather_target_blocks(D) + rows - 1) / rows;
@@ -299,7 +311,7 @@ int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunkin
 int enqueue_decode(const saga_dims* dims, const Layout& L, const void* q_dev,
                    const void* k_cache_dev, const void* v_cache_dev, const float* thresholds_dev,
                    void* out_dev, int32_t* sel_counts_dev, uint32_t* sel_bitmap_debug_dev,
-                   void* workspace_dev, hipStream_t s, const PagedKV& pg)
+                   void* workspace_dev, hipStream_t s, const RowModel& rm)
 {
     const int D = dims->head_dim;
     const int rows = dims->batch * dims->h_q;
@@ -312,13 +324,13 @@ int enqueue_decode(const saga_dims* dims, const Layout& L, const void* q_dev,
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
                                     D, L.max_chunks);
     SelectStreamArgs a =
-        stream_args(dims, L, ch, q_dev, k_cache_dev, thresholds_dev, workspace_dev, pg);
+        stream_args(dims, L, ch, q_dev, k_cache_dev, thresholds_dev, workspace_dev, rm);
     a.bitmap = sel_bitmap_debug_dev;
     a.bitmap_words = words;
     st = hip_status(launch_select_stream(D, a, s));
     if (st != SAGA_OK) return st;
     return enqueue_gather_combine(dims, L, ch, v_cache_dev, nullptr, out_dev, sel_counts_dev,
-                                  workspace_dev, s, pg);
+                                  workspace_dev, s, rm);
 }
 
 // Checks of a page description against the call's dims: pages of a multiple
@@ -340,7 +352,7 @@ int validate_paged(const saga_dims* d, const saga_paged* p, PagedKV* out)
     return SAGA_OK;
 }
 
-int do_refresh(const saga_dims* dims, const PagedKV& pg, int32_t top_n, const void* q_dev,
+int do_refresh(const saga_dims* dims, const RowModel& rm, int32_t top_n, const void* q_dev,
                const void* k_dev, float* thresholds_dev, float* logits_debug_dev,
                void* workspace_dev, size_t workspace_bytes, void* stream)
 {
@@ -366,7 +378,7 @@ int do_refresh(const saga_dims* dims, const PagedKV& pg, int32_t top_n, const vo
             float* pivot = reinterpret_cast<float*>(w + L.pivot);
             st = hip_status(launch_fill_u32(reinterpret_cast<uint32_t*>(pivot), rows, 0x7f800000u, s));
             if (st != SAGA_OK) return st;
-            SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_dev, pivot, workspace_dev, pg);
+            SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_dev, pivot, workspace_dev, rm);
             a.logits_out = logits_debug_dev;
             st = hip_status(launch_select_stream(D, a, s));
             if (st != SAGA_OK) return st;
@@ -375,10 +387,10 @@ int do_refresh(const saga_dims* dims, const PagedKV& pg, int32_t top_n, const vo
                                           0xff800000u, s));
     }
     return enqueue_refresh(dims, top_n, q_dev, k_dev, thresholds_dev, logits_debug_dev,
-                           workspace_dev, L, ch, s, nullptr, pg);
+                           workspace_dev, L, ch, s, nullptr, rm);
 }
 
-int do_decode(const saga_dims* dims, const PagedKV& pg, const void* q_dev, const void* k_dev,
+int do_decode(const saga_dims* dims, const RowModel& rm, const void* q_dev, const void* k_dev,
               const void* v_dev, const float* thresholds_dev, void* out_dev,
               int32_t* sel_counts_dev, uint32_t* sel_bitmap_debug_dev, void* workspace_dev,
               size_t workspace_bytes, void* stream)
@@ -393,10 +405,10 @@ int do_decode(const saga_dims* dims, const PagedKV& pg, const void* q_dev, const
     if (workspace_bytes < L.total) return SAGA_ERR_WORKSPACE_TOO_SMALL;
     return enqueue_decode(dims, L, q_dev, k_dev, v_dev, thresholds_dev, out_dev, sel_counts_dev,
                           sel_bitmap_debug_dev, workspace_dev, static_cast<hipStream_t>(stream),
-                          pg);
+                          rm);
 }
 
-int do_refresh_decode(const saga_dims* dims, const PagedKV& pg, int32_t top_n,
+int do_refresh_decode(const saga_dims* dims, const RowModel& rm, int32_t top_n,
                       const void* q_dev, const void* k_dev, const void* v_dev,
                       float* thresholds_dev, void* out_dev, int32_t* sel_counts_dev,
                       void* workspace_dev, size_t workspace_bytes, void* stream)
@@ -420,24 +432,24 @@ int do_refresh_decode(const saga_dims* dims, const PagedKV& pg, int32_t top_n,
                                         0xff800000u, s));
         if (st != SAGA_OK) return st;
         return enqueue_decode(dims, L, q_dev, k_dev, v_dev, thresholds_dev, out_dev,
-                              sel_counts_dev, nullptr, workspace_dev, s, pg);
+                              sel_counts_dev, nullptr, workspace_dev, s, rm);
     }
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
                                     D, L.max_chunks);
     uint32_t* flags = reinterpret_cast<uint32_t*>(w + L.flags);
     st = enqueue_refresh(dims, top_n, q_dev, k_dev, thresholds_dev, nullptr, workspace_dev,
-                         L, ch, s, flags, pg);
+                         L, ch, s, flags, rm);
     if (st != SAGA_OK) return st;
     // Key groups whose candidate lists miss selected entries (a row took the
     // recompute path) are streamed again with the fresh thresholds; every
     // other workgroup of this launch exits at once.
-    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_dev, thresholds_dev, workspace_dev, pg);
+    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_dev, thresholds_dev, workspace_dev, rm);
     a.group_flags = flags;
     st = hip_status(launch_select_stream(D, a, s));
     if (st != SAGA_OK) return st;
     // The lists hold every logit >= tau (and more): keep those >= tau.
     return enqueue_gather_combine(dims, L, ch, v_dev, thresholds_dev, out_dev,
-                                  sel_counts_dev, workspace_dev, s, pg);
+                                  sel_counts_dev, workspace_dev, s, rm);
 }
 
 }  // namespace
@@ -449,7 +461,7 @@ SAGA_EXPORT int atopn_refresh_thresholds(const saga_dims* dims, int32_t top_n, c
 {
     const int st = validate_dims(dims);
     if (st != SAGA_OK) return st;
-    return do_refresh(dims, PagedKV{}, top_n, q_dev, k_cache_dev, thresholds_dev, logits_debug_dev,
+    return do_refresh(dims, RowModel{}, top_n, q_dev, k_cache_dev, thresholds_dev, logits_debug_dev,
                       workspace_dev, workspace_bytes, stream);
 }
 
@@ -461,7 +473,7 @@ SAGA_EXPORT int saga_decode_step(const saga_dims* dims, const void* q_dev, const
 {
     const int st = validate_dims(dims);
     if (st != SAGA_OK) return st;
-    return do_decode(dims, PagedKV{}, q_dev, k_cache_dev, v_cache_dev, thresholds_dev, out_dev,
+    return do_decode(dims, RowModel{}, q_dev, k_cache_dev, v_cache_dev, thresholds_dev, out_dev,
                      sel_counts_dev, sel_bitmap_debug_dev, workspace_dev, workspace_bytes, stream);
 }
 
@@ -473,7 +485,7 @@ SAGA_EXPORT int atopn_refresh_decode_step(const saga_dims* dims, int32_t top_n, 
 {
     const int st = validate_dims(dims);
     if (st != SAGA_OK) return st;
-    return do_refresh_decode(dims, PagedKV{}, top_n, q_dev, k_cache_dev, v_cache_dev,
+    return do_refresh_decode(dims, RowModel{}, top_n, q_dev, k_cache_dev, v_cache_dev,
                              thresholds_dev, out_dev, sel_counts_dev, workspace_dev,
                              workspace_bytes, stream);
 }
@@ -486,10 +498,10 @@ SAGA_EXPORT int atopn_refresh_thresholds_paged(const saga_dims* dims, const saga
 {
     int st = validate_dims(dims);
     if (st != SAGA_OK) return st;
-    PagedKV pg{};
-    st = validate_paged(dims, paged, &pg);
+    RowModel rm;
+    st = validate_paged(dims, paged, &rm.pg);
     if (st != SAGA_OK) return st;
-    return do_refresh(dims, pg, top_n, q_dev, k_pages_dev, thresholds_dev, nullptr, workspace_dev,
+    return do_refresh(dims, rm, top_n, q_dev, k_pages_dev, thresholds_dev, nullptr, workspace_dev,
                       workspace_bytes, stream);
 }
 
@@ -501,10 +513,10 @@ SAGA_EXPORT int saga_decode_step_paged(const saga_dims* dims, const saga_paged* 
 {
     int st = validate_dims(dims);
     if (st != SAGA_OK) return st;
-    PagedKV pg{};
-    st = validate_paged(dims, paged, &pg);
+    RowModel rm;
+    st = validate_paged(dims, paged, &rm.pg);
     if (st != SAGA_OK) return st;
-    return do_decode(dims, pg, q_dev, k_pages_dev, v_pages_dev, thresholds_dev, out_dev,
+    return do_decode(dims, rm, q_dev, k_pages_dev, v_pages_dev, thresholds_dev, out_dev,
                      sel_counts_dev, nullptr, workspace_dev, workspace_bytes, stream);
 }
 
@@ -517,10 +529,70 @@ SAGA_EXPORT int atopn_refresh_decode_step_paged(const saga_dims* dims, const sag
 {
     int st = validate_dims(dims);
     if (st != SAGA_OK) return st;
-    PagedKV pg{};
-    st = validate_paged(dims, paged, &pg);
+    RowModel rm;
+    st = validate_paged(dims, paged, &rm.pg);
     if (st != SAGA_OK) return st;
-    return do_refresh_decode(dims, pg, top_n, q_dev, k_pages_dev, v_pages_dev, thresholds_dev,
+    return do_refresh_decode(dims, rm, top_n, q_dev, k_pages_dev, v_pages_dev, thresholds_dev,
+                             out_dev, sel_counts_dev, workspace_dev, workspace_bytes, stream);
+}
+
+namespace {
+
+// The call's dims with one virtual query head per (query head, token).
+int lq_dims(const saga_dims* dims, int32_t l_q, saga_dims* v)
+{
+    int st = validate_dims(dims);
+    if (st != SAGA_OK) return st;
+    if (l_q < 1 || (int64_t)l_q > dims->ctx_len) return SAGA_ERR_INVALID_ARGUMENT;
+    *v = *dims;
+    v->h_q = dims->h_q * l_q;
+    return validate_dims(v);         // UNSUPPORTED past 16 query slots per key head
+}
+
+}  // namespace
+
+SAGA_EXPORT int atopn_refresh_thresholds_lq(const saga_dims* dims, int32_t l_q, int32_t top_n,
+                                            const void* q_dev, const void* k_cache_dev,
+                                            float* thresholds_dev, void* workspace_dev,
+                                            size_t workspace_bytes, void* stream)
+{
+    saga_dims v;
+    const int st = lq_dims(dims, l_q, &v);
+    if (st != SAGA_OK) return st;
+    RowModel rm;
+    rm.lq = l_q;
+    return do_refresh(&v, rm, top_n, q_dev, k_cache_dev, thresholds_dev, nullptr, workspace_dev,
+                      workspace_bytes, stream);
+}
+
+SAGA_EXPORT int saga_decode_step_lq(const saga_dims* dims, int32_t l_q, const void* q_dev,
+                                    const void* k_cache_dev, const void* v_cache_dev,
+                                    const float* thresholds_dev, void* out_dev,
+                                    int32_t* sel_counts_dev, void* workspace_dev,
+                                    size_t workspace_bytes, void* stream)
+{
+    saga_dims v;
+    const int st = lq_dims(dims, l_q, &v);
+    if (st != SAGA_OK) return st;
+    RowModel rm;
+    rm.lq = l_q;
+    return do_decode(&v, rm, q_dev, k_cache_dev, v_cache_dev, thresholds_dev, out_dev,
+                     sel_counts_dev, nullptr, workspace_dev, workspace_bytes, stream);
+}
+
+SAGA_EXPORT int atopn_refresh_decode_step_lq(const saga_dims* dims, int32_t l_q, int32_t top_n,
+                                             const void* q_dev, const void* k_cache_dev,
+                                             const void* v_cache_dev, float* thresholds_dev,
+                                             void* out_dev, int32_t* sel_counts_dev,
+                                             void* workspace_dev, size_t workspace_bytes,
+                                             void* stream)
+{
+    saga_dims v;
+    const int st = lq_dims(dims, l_q, &v);
+    if (st != SAGA_OK) return st;
+    RowModel rm;
+    rm.lq = l_q;
+    return do_refresh_decode(&v, rm, top_n, q_dev, k_cache_dev, v_cache_dev, thresholds_dev,
                              out_dev, sel_counts_dev, workspace_dev, workspace_bytes, stream);
 }
 

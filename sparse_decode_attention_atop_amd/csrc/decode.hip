@@ -61,11 +61,14 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
 
     const QFrag<D> qf = load_qfrag<D>(col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr);
     float tau[4], mx[4];
+    int64_t lim[4];          // rows of this lane's head slots: r1, or less for later tokens
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int slot = 4 * grp + i;
         tau[i] = slot < Gk ? a.tau[qh0 + slot] : INFINITY;
         mx[i] = -INFINITY;
+        const int64_t hc = a.lq > 1 ? head_ctx(a.pg, a.lq, b, g * Gk + slot, a.ctx) : r1;
+        lim[i] = hc < r1 ? hc : r1;
     }
     // Wave-uniform bookkeeping: entries waiting in queue i, entries already in
     // the global list of head slot h.
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool pred = valid && s[i] >= tau[i];
+                const bool pred = row < lim[i] && s[i] >= tau[i];
                 const uint64_t mask = __ballot(pred);
                 if (pred)
                     q4[i][qn[i] + lanes_below(mask)] =

@@ -92,6 +92,15 @@ __device__ __forceinline__ int64_t seq_ctx(const PagedKV& pg, int b, int64_t ctx
     return c < 0 ? 0 : (c > cap ? cap : c);
 }
 
+// Several query tokens per step (lq > 1): token j of query head i is the
+// virtual query head i*lq + j (same key and value heads as i), and it attends
+// the rows up to its own position, ctx - (lq - 1 - j), where ctx counts the
+// step's tokens.  Rows attended by virtual head v of sequence b:
+__device__ __forceinline__ int64_t head_ctx(const PagedKV& pg, int lq, int b, int v, int64_t ctx)
+{
+    return seq_ctx(pg, b, ctx) - (lq - 1 - v % lq);
+}
+
 // Element offset of the first row of the page that holds row r of (b, head h)
 // in a pool with nh heads per page, or -1 when the table points outside the
 // pool (the caller then reads nothing).
@@ -124,6 +133,7 @@ struct SelectStreamArgs {
     int64_t ctx, cache_len, rows_per_chunk;
     int32_t chunks;
     float scale;
+    int32_t lq;              // query tokens per query head and step (1: one)
     PagedKV pg;              // paged caches (block_table != nullptr)
 };
 
@@ -151,10 +161,12 @@ struct SampleArgs {
     float* pivot;            // [B*hq]
     uint32_t* group_flags;   // nullable [B*hk]: cleared here
     int32_t B, hq, hk, Gk;
+    int64_t ctx;                 // rows attended (tokens > 1: by the last token)
     int64_t cache_len, stride;   // one 16-row sample block every `stride` rows
     int32_t m, rank;             // sample size, rank of the pivot within the sample
     int32_t top_n;               // paged: per-row rank from each sequence's length
     float scale;
+    int32_t lq;              // query tokens per query head and step (1: one)
     PagedKV pg;              // paged caches (block_table != nullptr)
 };
 
@@ -172,6 +184,7 @@ struct FinalArgs {
     int32_t chunks;
     uint32_t top_n;
     float scale;
+    int32_t lq;              // query tokens per query head and step (1: one)
     PagedKV pg;              // paged caches (block_table != nullptr)
 };
 

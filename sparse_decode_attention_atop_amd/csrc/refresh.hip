@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kBlock) void sample_logits_kernel(SampleArgs a)
     if (k0 >= a.m) return;                                          // whole wave idle
     const QFrag<D> qf = load_qfrag<D>(col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr);
     const uint16_t* khead = a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
-    const int64_t ctx_b = PAGED ? seq_ctx(a.pg, b, 0) : INT64_MAX;
+    const int64_t ctx_b = PAGED ? seq_ctx(a.pg, b, 0) : (a.lq > 1 ? a.ctx : INT64_MAX);
     KTile<D, U> kt;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -157,9 +157,11 @@ __global__ __launch_bounds__(kBlock) void sample_logits_kernel(SampleArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int slot = 4 * grp + i;
-            // Paged: rows past the sequence rank below every real logit.
+            // Rows past the sequence (paged) or past a later token's own
+            // position (lq > 1) rank below every real logit.
+            const int64_t lim = a.lq > 1 ? ctx_b - (a.lq - 1 - (g * Gk + slot) % a.lq) : ctx_b;
             if (slot < Gk)
-                a.sample[(int64_t)(qh0 + slot) * kSampleMax + k] = row < ctx_b ? s[u][i] : -INFINITY;
+                a.sample[(int64_t)(qh0 + slot) * kSampleMax + k] = row < lim ? s[u][i] : -INFINITY;
         }
     }
 }
@@ -173,10 +175,11 @@ __global__ __launch_bounds__(kBlock) void pivot_kernel(SampleArgs a)
     const float* s = a.sample + (int64_t)row * kSampleMax;
     int rank = a.rank;
     bool all = false;                                  // pivot -inf: every row is a candidate
-    if (a.pg.block_table) {
-        // Paged: the sample and the rank follow this sequence's length.  The
-        // sample rows past it hold -inf, below every row that counts.
-        const int64_t cb = seq_ctx(a.pg, row / a.hq, 0);
+    if (a.pg.block_table || a.lq > 1) {
+        // Paged or several tokens: the sample and the rank follow this row's
+        // own length.  The sample rows past it hold -inf, below every row
+        // that counts.
+        const int64_t cb = head_ctx(a.pg, a.lq, row / a.hq, row % a.hq, a.ctx);
         // Sampled rows below cb: block j holds samples 16j .. min(16j+16, m)-1
         // at rows j*stride + 0..15; one block per thread, then a block sum.
         int32_t part = 0;
@@ -278,8 +281,8 @@ __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
     __shared__ uint32_t keys[kFinalStage];
     __shared__ SelectLds w;
     const int row = blockIdx.x, t = threadIdx.x;
-    const int64_t ctx = PAGED ? seq_ctx(a.pg, row / a.hq, a.ctx) : a.ctx;
-    if (PAGED && (int64_t)a.top_n >= ctx) {            // N covers the sequence: keep everything
+    const int64_t ctx = head_ctx(a.pg, a.lq, row / a.hq, row % a.hq, a.ctx);
+    if ((int64_t)a.top_n >= ctx) {                     // N covers the row: keep everything
         if (t == 0) a.tau[row] = -INFINITY;
         return;
     }

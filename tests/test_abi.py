@@ -208,3 +208,28 @@ def test_paged_argument_checks(kind):
     # a consistent description passes validation and stops at the workspace size
     assert call_paged(kind, d, good_paged(), need - 1) == SMALL
     assert call_paged(kind, good_dims(cache_len=1024, head_dim=96), good_paged(), 1 << 40) == UNSUPPORTED
+
+
+# ---- several query tokens per step ------------------------------------------
+
+def call_lq(kind, d, l_q, ws_bytes, top_n=8):
+    lib = saga.library()
+    if kind == "refresh":
+        return lib.atopn_refresh_thresholds_lq(ctypes.byref(d), l_q, top_n, FAKE, FAKE, FAKE, FAKE,
+                                               ws_bytes, None)
+    if kind == "decode":
+        return lib.saga_decode_step_lq(ctypes.byref(d), l_q, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                       FAKE, ws_bytes, None)
+    return lib.atopn_refresh_decode_step_lq(ctypes.byref(d), l_q, top_n, FAKE, FAKE, FAKE, FAKE,
+                                            FAKE, None, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kind", ["refresh", "decode", "fused"])
+def test_lq_argument_checks(kind):
+    d = good_dims(h_q=8, h_k=2, h_v=4, ctx_len=1000)   # 4 query heads per key head
+    assert call_lq(kind, d, 0, 1 << 40) == INVALID
+    assert call_lq(kind, d, 1001, 1 << 40) == INVALID   # more tokens than rows
+    assert call_lq(kind, d, 5, 1 << 40) == UNSUPPORTED  # 4 x 5 > 16 query slots
+    need = saga.saga_workspace_bytes(saga.dims(2, 8 * 4, 2, 4, 128, 1000, 1024), 8)
+    assert call_lq(kind, d, 4, need - 1) == SMALL       # workspace of h_q * l_q heads
+    assert call_lq(kind, good_dims(h_q=8, h_k=2, h_v=3), 2, 1 << 40) == INVALID
