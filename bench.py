@@ -96,6 +96,8 @@ def parse():
                    help="time the schedule on paged caches with pages of this many rows")
     p.add_argument("--varlen", action="store_true",
                    help="with --paged: per-sequence lengths drawn from [L/4, L]")
+    p.add_argument("--lq", type=int, default=0,
+                   help="time the schedule with this many query tokens per head and step")
     p.add_argument("--sweep", action="store_true",
                    help="Llama-like and Qwen-like shapes over L x N x B: SAGA Atop-N vs the "
                         "full-attention GQA path, one JSON line per point")
@@ -313,6 +315,59 @@ def run_saga_paged(torch, saga, wl, w, args):
     return dict(sec=sec, step_bytes=step_bytes, ctx=Lb.tolist())
 
 
+def run_saga_lq(torch, saga, wl, w, args):
+    """The main schedule with args.lq query tokens per head and step (token j
+    of step t attends L + lq*t + j + 1 rows), through the *_lq calls."""
+    lq, T = args.lq, w.steps
+    w2 = w.with_(h_q=w.h_q * lq, L=w.L + (lq - 1) * T)            # rows = L + lq*T
+    layers = []
+    log(f"generating {w.layers} layers of {w.name} with {lq} query tokens per step")
+    for layer in range(w.layers):
+        K, V, q = layer_inputs(torch, wl, w2, layer)
+        layers.append(dict(K=K, V=V, q=q,
+                           tau=torch.empty(w.batch, w.h_q, lq, device="cuda"),
+                           out=torch.empty(w.batch, w.h_q, lq, w.head_dim, dtype=torch.bfloat16,
+                                           device="cuda"),
+                           cnt=torch.empty(w.batch, w.h_q, lq, dtype=torch.int32, device="cuda")))
+        log(f"  layer {layer} ready")
+    ctx = [w.L + lq * (t + 1) for t in range(T)]
+    ws = saga.alloc_workspace_lq(saga.dims(w.batch, w.h_q, w.h_k, w.h_v, w.head_dim, ctx[0],
+                                           w2.rows, w.scale), lq, w.top_n)
+
+    def step(t):
+        dm = saga.dims(w.batch, w.h_q, w.h_k, w.h_v, w.head_dim, ctx[t], w2.rows, w.scale)
+        for x in layers:
+            if t % w.refresh_n == 0:
+                saga.atopn_refresh_decode_step_lq(dm, lq, w.top_n, x["q"][t], x["K"], x["V"],
+                                                  x["tau"], x["out"], ws, sel_counts=x["cnt"])
+            else:
+                saga.saga_decode_step_lq(dm, lq, x["q"][t], x["K"], x["V"], x["tau"], x["out"],
+                                         ws, sel_counts=x["cnt"])
+
+    sel = 0
+    for t in range(T):
+        step(t)
+        torch.cuda.synchronize()
+        sel += sum(int(x["cnt"].sum().item()) for x in layers)
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for t in range(T):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                step(t)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps of {lq} tokens after {args.warmup} warmup steps")
+    sec, _ = time_graphs(torch, graphs, args.steps, args.warmup)
+    d = w.head_dim
+    step_bytes = (w.layers * w.batch * w.h_k * d * 2 * sum(ctx) / T + sel * d * 2 / T
+                  + w.layers * (2 * w.batch * w.h_q * lq * d * 2 + w.batch * w.h_q * lq * 4))
+    return dict(sec=sec, step_bytes=step_bytes)
+
+
 def run_gqa(torch, saga, wl, w, hkv, args):
     return run_full(torch, saga, wl, w.gqa(hkv), args) | {"hkv": hkv}
 
@@ -469,6 +524,19 @@ def main():
         return
     if args.decompose:
         decompose(torch, saga, wl, args)
+        return
+    if args.lq:
+        w = wl.WORKLOADS[args.workload]
+        res = run_saga_lq(torch, saga, wl, w, args)
+        sps = args.steps / res["sec"]
+        gbs = res["step_bytes"] / (res["sec"] / args.steps) / 1e9
+        print(json.dumps({"metric": "decode-attn steps/s, several query tokens per step",
+                          "value": round(sps, 3), "unit": "steps/s",
+                          "tokens_per_s": round(sps * w.batch * args.lq, 2),
+                          "ms_per_step": round(1e3 * res["sec"] / args.steps, 4),
+                          "steps": args.steps, "warmup": args.warmup,
+                          "hbm_gbs_step": round(gbs, 1), "hbm_frac_step": round(gbs / HBM_PEAK_GBS, 4),
+                          "config": {"workload": w.name, "l_q": args.lq}}), flush=True)
         return
     if args.paged:
         w = wl.WORKLOADS[args.workload]
