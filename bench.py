@@ -98,6 +98,8 @@ def parse():
                    help="with --paged: per-sequence lengths drawn from [L/4, L]")
     p.add_argument("--lq", type=int, default=0,
                    help="time the schedule with this many query tokens per head and step")
+    p.add_argument("--fp8k", action="store_true",
+                   help="store the K cache as fp8 E4M3 (the *_fp8k calls)")
     p.add_argument("--sweep", action="store_true",
                    help="Llama-like and Qwen-like shapes over L x N x B: SAGA Atop-N vs the "
                         "full-attention GQA path, one JSON line per point")
@@ -135,11 +137,12 @@ def layer_inputs(torch, wl, w, layer):
     return x["K"], x["V"], x["q"]
 
 
-def decode_algorithmic_bytes(w, ctx, sel_total):
-    """Bytes the fused decode launch must move: K once per (b, key head), the
-    selected V rows, q, out and the thresholds."""
+def decode_algorithmic_bytes(w, ctx, sel_total, k_bytes=2):
+    """Bytes the fused decode launch must move: K once per (b, key head)
+    (k_bytes per element: 2 for bf16, 1 for fp8), the selected V rows, q, out
+    and the thresholds."""
     d = w.head_dim
-    return (w.batch * w.h_k * ctx * d * 2 + sel_total * d * 2
+    return (w.batch * w.h_k * ctx * d * k_bytes + sel_total * d * 2
             + 2 * w.batch * w.h_q * d * 2 + w.batch * w.h_q * 4)
 
 
@@ -368,6 +371,76 @@ def run_saga_lq(torch, saga, wl, w, args):
     return dict(sec=sec, step_bytes=step_bytes)
 
 
+def run_saga_fp8k(torch, saga, wl, w, args):
+    """The main schedule with the K cache stored as fp8 E4M3 (one scale per
+    sequence and key head, amax / 448) and V in bf16, through the *_fp8k calls."""
+    T, L = w.steps, w.L
+    layers = []
+    log(f"generating {w.layers} layers of {w.name} with an fp8 K cache")
+    for layer in range(w.layers):
+        K, V, q = layer_inputs(torch, wl, w, layer)
+        K8, ks = wl.quantize_k_e4m3(K)
+        del K
+        layers.append(dict(K8=K8, ks=ks, V=V, q=q,
+                           tau=torch.empty(w.batch, w.h_q, device="cuda"),
+                           out=torch.empty(w.batch, w.h_q, w.head_dim, dtype=torch.bfloat16,
+                                           device="cuda"),
+                           cnt=torch.empty(w.batch, w.h_q, dtype=torch.int32, device="cuda")))
+        log(f"  layer {layer} ready")
+    torch.cuda.empty_cache()
+    ws = saga.alloc_workspace(saga.dims(w.batch, w.h_q, w.h_k, w.h_v, w.head_dim, L, w.rows,
+                                        w.scale), w.top_n)
+
+    def step(t, events=None):
+        dm = saga.dims(w.batch, w.h_q, w.h_k, w.h_v, w.head_dim, L + t, w.rows, w.scale)
+        for li, x in enumerate(layers):
+            if events is not None:
+                events[li][0].record()
+            if t % w.refresh_n == 0:
+                saga.atopn_refresh_decode_step_fp8k(dm, w.top_n, x["q"][t], x["K8"], x["ks"],
+                                                    x["V"], x["tau"], x["out"], ws,
+                                                    sel_counts=x["cnt"])
+            else:
+                saga.saga_decode_step_fp8k(dm, x["q"][t], x["K8"], x["ks"], x["V"], x["tau"],
+                                           x["out"], ws, sel_counts=x["cnt"])
+            if events is not None:
+                events[li][1].record()
+
+    for t in range(T):
+        step(t)
+    torch.cuda.synchronize()
+    sel, launches = 0, []
+    for t in range(T):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in layers]
+        step(t, ev)
+        torch.cuda.synchronize()
+        for li, x in enumerate(layers):
+            n_sel = int(x["cnt"].sum().item())
+            sel += n_sel
+            if t % w.refresh_n:
+                launches.append((ev[li][0].elapsed_time(ev[li][1]),
+                                 decode_algorithmic_bytes(w, L + t, n_sel, k_bytes=1)))
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for t in range(T):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                step(t)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} fp8-K steps after {args.warmup} warmup steps")
+    sec, _ = time_graphs(torch, graphs, args.steps, args.warmup)
+    step_bytes = sum(decode_algorithmic_bytes(w, L + t, 0, k_bytes=1) for t in range(T)) \
+        * w.layers / T + sel * w.head_dim * 2 / T
+    call_ms = sum(ms for ms, _ in launches) / len(launches)
+    call_gbs = sum(b for _, b in launches) / len(launches) / (call_ms / 1e3) / 1e9
+    return dict(sec=sec, step_bytes=step_bytes, call_ms=call_ms, call_gbs=call_gbs)
+
+
 def run_gqa(torch, saga, wl, w, hkv, args):
     return run_full(torch, saga, wl, w.gqa(hkv), args) | {"hkv": hkv}
 
@@ -537,6 +610,21 @@ def main():
                           "steps": args.steps, "warmup": args.warmup,
                           "hbm_gbs_step": round(gbs, 1), "hbm_frac_step": round(gbs / HBM_PEAK_GBS, 4),
                           "config": {"workload": w.name, "l_q": args.lq}}), flush=True)
+        return
+    if args.fp8k:
+        w = wl.WORKLOADS[args.workload]
+        res = run_saga_fp8k(torch, saga, wl, w, args)
+        sps = args.steps / res["sec"]
+        gbs = res["step_bytes"] / (res["sec"] / args.steps) / 1e9
+        print(json.dumps({"metric": "decode-attn steps/s with an fp8 K cache",
+                          "value": round(sps, 3), "unit": "steps/s",
+                          "ms_per_step": round(1e3 * res["sec"] / args.steps, 4),
+                          "steps": args.steps, "warmup": args.warmup, "dtype": "fp8e4m3 K, bf16 V",
+                          "hbm_gbs_step": round(gbs, 1), "hbm_frac_step": round(gbs / HBM_PEAK_GBS, 4),
+                          "decode_call_us_eager": round(1e3 * res["call_ms"], 2),
+                          "decode_call_gbs_eager": round(res["call_gbs"], 1),
+                          "config": {"workload": w.name, "k_cache": "fp8 e4m3, per-head scale"}}),
+              flush=True)
         return
     if args.paged:
         w = wl.WORKLOADS[args.workload]

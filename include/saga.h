@@ -232,6 +232,38 @@ int atopn_refresh_decode_step_lq(const saga_dims* dims, int32_t l_q, int32_t top
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * An fp8 K cache (the pages list SAGA as combinable with cache quantization:
+ * ai.info summary, Why This Matters).  The dominant K stream then reads one
+ * byte per element instead of two; V stays bf16.
+ *
+ *   k8_cache_dev  [batch][h_k][cache_len][head_dim] bytes, each an fp8 E4M3
+ *                 value in the OCP 8-bit floating point format (bias 7, no
+ *                 infinities, 0x7F / 0xFF are NaN, max 448)
+ *   k_scale_dev   fp32 [batch][h_k] device memory: key row r of (b, g) is
+ *                 k_scale[b][g] * decode(k8[b][g][r][:])
+ * The logits are scale * k_scale[b][kappa(i)] * (q . decode(k8 row)), i.e. the
+ * contiguous calls run on the dequantized cache; everything else (thresholds,
+ * selection, outputs, workspace size, the debug outputs of the refresh and
+ * decode calls) is as the contiguous calls.  A NaN code yields NaN logits,
+ * which never pass a threshold.  Errors: as the contiguous calls, plus
+ * INVALID_ARGUMENT for a null or misaligned k_scale_dev.
+ */
+int atopn_refresh_thresholds_fp8k(const saga_dims* dims, int32_t top_n, const void* q_dev,
+                                  const void* k8_cache_dev, const float* k_scale_dev,
+                                  float* thresholds_dev, float* logits_debug_dev,
+                                  void* workspace_dev, size_t workspace_bytes, void* stream);
+int saga_decode_step_fp8k(const saga_dims* dims, const void* q_dev, const void* k8_cache_dev,
+                          const float* k_scale_dev, const void* v_cache_dev,
+                          const float* thresholds_dev, void* out_dev, int32_t* sel_counts_dev,
+                          uint32_t* sel_bitmap_debug_dev, void* workspace_dev,
+                          size_t workspace_bytes, void* stream);
+int atopn_refresh_decode_step_fp8k(const saga_dims* dims, int32_t top_n, const void* q_dev,
+                                   const void* k8_cache_dev, const float* k_scale_dev,
+                                   const void* v_cache_dev, float* thresholds_dev, void* out_dev,
+                                   int32_t* sel_counts_dev, void* workspace_dev,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * Full (dense) decode attention over all ctx_len rows with the same head maps:
  * the full-attention GQA baseline the pages time against when h_k == h_v, and
  * "SAGA full attention" when h_k < h_v (ai.info summary, Main Findings:

@@ -8,7 +8,9 @@ nothing from the product.
 The arithmetic lives in ``oracle.c`` (plain C, double precision); this module
 only builds that file with gcc and marshals numpy arrays.  Every function
 takes bf16 data as ``uint16`` bit patterns, exactly the values the device
-sees.  Citations of the pages are in ``oracle.c`` next to each function.
+sees; the ``*_e4m3k`` variants take an fp8 E4M3 key cache as ``uint8`` codes
+with one fp32 scale per (batch row, key head).  Citations of the pages are in
+``oracle.c`` next to each function.
 """
 from __future__ import annotations
 
@@ -58,9 +60,18 @@ def _load():
         lib.oracle_exact_topn.argtypes = [i32, i32, i32, i32, i32, i64, i64, dbl, i64, vp, vp,
                                           vp, vp, i32]
         lib.oracle_full.argtypes = [i32, i32, i32, i32, i32, i64, i64, dbl, vp, vp, vp, vp, i32]
+        lib.oracle_logits_e4m3k.argtypes = [i32, i32, i32, i32, i32, i64, i64, dbl, vp, vp, vp,
+                                            vp, i32]
+        lib.oracle_atopn_run_e4m3k.argtypes = [i32, i32, i32, i32, i32, i64, i32, vp, dbl, i64,
+                                               i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        lib.oracle_masked_e4m3k.argtypes = [i32, i32, i32, i32, i32, i64, i64, dbl, vp, vp, vp,
+                                            vp, vp, vp, vp, i32]
+        lib.oracle_e4m3_decode.argtypes = [vp, i64, vp]
+        lib.oracle_e4m3_decode.restype = None
         lib.oracle_max_threads.restype = i32
         for name in ("oracle_logits", "oracle_atopn_run", "oracle_masked",
-                     "oracle_exact_topn", "oracle_full"):
+                     "oracle_exact_topn", "oracle_full", "oracle_logits_e4m3k",
+                     "oracle_atopn_run_e4m3k", "oracle_masked_e4m3k"):
             getattr(lib, name).restype = i32
         _lib = lib
     return _lib
@@ -71,6 +82,20 @@ def _u16(a) -> np.ndarray:
     if a.dtype != np.uint16:
         raise TypeError(f"expected bf16 bit patterns as uint16, got {a.dtype}")
     return a
+
+
+def _u8(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint8:
+        raise TypeError(f"expected E4M3 codes as uint8, got {a.dtype}")
+    return a
+
+
+def _kscale(k_scale, B, hk) -> np.ndarray:
+    k_scale = np.ascontiguousarray(k_scale, dtype=np.float32)
+    if k_scale.shape != (B, hk):
+        raise ValueError("k_scale must be [B][hk]")
+    return k_scale
 
 
 def _ptr(a: np.ndarray):
@@ -102,6 +127,28 @@ def logits(q, K, ctx: int, scale: float = 1.0, nthreads: int = 0) -> np.ndarray:
     return out
 
 
+def e4m3_decode(codes) -> np.ndarray:
+    """Values (float64) of E4M3 codes, same shape; NaN for 0x7F and 0xFF."""
+    codes = _u8(codes)
+    out = np.empty(codes.shape, dtype=np.float64)
+    _load().oracle_e4m3_decode(_ptr(codes), codes.size, _ptr(out))
+    return out
+
+
+def logits_e4m3k(q, K8, k_scale, ctx: int, scale: float = 1.0, nthreads: int = 0) -> np.ndarray:
+    """fp64 logits ``[B][hq][ctx]`` with an E4M3 key cache ``K8 [B][hk][rows][d]``."""
+    q, K8 = _u16(q), _u8(K8)
+    B, hk, cache_len, d = K8.shape
+    hq = q.shape[1]
+    ks = _kscale(k_scale, B, hk)
+    out = np.empty((B, hq, ctx), dtype=np.float64)
+    rc = _load().oracle_logits_e4m3k(B, hq, hk, hk, d, cache_len, ctx, scale, _ptr(q), _ptr(K8),
+                                     _ptr(ks), _ptr(out), nthreads)
+    if rc:
+        raise ValueError("oracle_logits_e4m3k rejected its arguments")
+    return out
+
+
 def nth_largest(s, N: int) -> float:
     """Exact N-th largest of a 1-D array (sorted), ``-inf`` when ``N >= len(s)``."""
     s = np.ascontiguousarray(s, dtype=np.float64)
@@ -116,7 +163,21 @@ def atopn_run(q_steps, K, V, ctx_steps, top_n: int, refresh_n: int, scale: float
     Returns a dict with ``out [T][B][hq][d]``, ``tau [T][B][hq]``,
     ``count [T][B][hq]`` and optionally ``sel``/``logits`` ``[T][B][hq][rows]``.
     """
-    q_steps, K, V = _u16(q_steps), _u16(K), _u16(V)
+    return _atopn(q_steps, _u16(K), None, V, ctx_steps, top_n, refresh_n, scale, want_sel,
+                  want_logits, nthreads)
+
+
+def atopn_run_e4m3k(q_steps, K8, k_scale, V, ctx_steps, top_n: int, refresh_n: int,
+                    scale: float = 1.0, want_sel: bool = False, want_logits: bool = False,
+                    nthreads: int = 0):
+    """``atopn_run`` with an E4M3 key cache ``K8`` and scales ``k_scale [B][hk]``."""
+    return _atopn(q_steps, _u8(K8), k_scale, V, ctx_steps, top_n, refresh_n, scale, want_sel,
+                  want_logits, nthreads)
+
+
+def _atopn(q_steps, K, k_scale, V, ctx_steps, top_n, refresh_n, scale, want_sel, want_logits,
+           nthreads):
+    q_steps, V = _u16(q_steps), _u16(V)
     B, hk, hv, cache_len, d = _cache_shape(K, V)
     T, _, hq, _ = q_steps.shape
     ctx = np.ascontiguousarray(ctx_steps, dtype=np.int64)
@@ -127,11 +188,17 @@ def atopn_run(q_steps, K, V, ctx_steps, top_n: int, refresh_n: int, scale: float
     count = np.empty((T, B, hq), dtype=np.int64)
     sel = np.empty((T, B, hq, cache_len), dtype=np.uint8) if want_sel else None
     lg = np.empty((T, B, hq, cache_len), dtype=np.float64) if want_logits else None
-    rc = _load().oracle_atopn_run(
-        B, hq, hk, hv, d, cache_len, T, _ptr(ctx), scale, top_n, refresh_n,
-        _ptr(q_steps), _ptr(K), _ptr(V), _ptr(out), _ptr(tau), _ptr(count),
-        _ptr(sel) if sel is not None else None, _ptr(lg) if lg is not None else None,
-        nthreads)
+    tail = (_ptr(V), _ptr(out), _ptr(tau), _ptr(count),
+            _ptr(sel) if sel is not None else None, _ptr(lg) if lg is not None else None,
+            nthreads)
+    if k_scale is None:
+        rc = _load().oracle_atopn_run(B, hq, hk, hv, d, cache_len, T, _ptr(ctx), scale, top_n,
+                                      refresh_n, _ptr(q_steps), _ptr(K), *tail)
+    else:
+        ks = _kscale(k_scale, B, hk)
+        rc = _load().oracle_atopn_run_e4m3k(B, hq, hk, hv, d, cache_len, T, _ptr(ctx), scale,
+                                            top_n, refresh_n, _ptr(q_steps), _ptr(K), _ptr(ks),
+                                            *tail)
     if rc:
         raise ValueError("oracle_atopn_run rejected its arguments")
     res = {"out": out, "tau": tau, "count": count}
@@ -156,6 +223,25 @@ def masked(q, K, V, ctx: int, bitmap, scale: float = 1.0, nthreads: int = 0):
                                _ptr(V), _ptr(bitmap), _ptr(out), _ptr(count), nthreads)
     if rc:
         raise ValueError("oracle_masked rejected its arguments")
+    return out, count
+
+
+def masked_e4m3k(q, K8, k_scale, V, ctx: int, bitmap, scale: float = 1.0, nthreads: int = 0):
+    """``masked`` with an E4M3 key cache ``K8`` and scales ``k_scale [B][hk]``."""
+    q, K8, V = _u16(q), _u8(K8), _u16(V)
+    B, hk, hv, cache_len, d = _cache_shape(K8, V)
+    hq = q.shape[1]
+    ks = _kscale(k_scale, B, hk)
+    bitmap = np.ascontiguousarray(bitmap, dtype=np.uint32)
+    if bitmap.shape != (B, hq, (cache_len + 31) // 32):
+        raise ValueError("bitmap must be [B][hq][ceil(rows/32)]")
+    out = np.empty((B, hq, d), dtype=np.float64)
+    count = np.empty((B, hq), dtype=np.int64)
+    rc = _load().oracle_masked_e4m3k(B, hq, hk, hv, d, cache_len, ctx, scale, _ptr(q), _ptr(K8),
+                                     _ptr(ks), _ptr(V), _ptr(bitmap), _ptr(out), _ptr(count),
+                                     nthreads)
+    if rc:
+        raise ValueError("oracle_masked_e4m3k rejected its arguments")
     return out, count
 
 

@@ -10,6 +10,9 @@
  *   [P1] "More Value per Key: Asymmetric Sparse Attention for Faster LLM
  *        Decoding", ai.info AI summary.
  *   [P2] the same paper, atlas.scime.ai AI summary.
+ *   [F8] the OCP 8-bit floating point specification (OFP8), format E4M3:
+ *        the fp8 key cache ([P1] Why This Matters: SAGA combines with cache
+ *        quantization).
  *
  * What is computed (for each layer call, each batch row b, each query head i):
  *   - SAGA head maps: the key-head count h_k and the value-head count h_v are
@@ -31,7 +34,9 @@
  *   threshold used in the same step; inclusive comparison (ties kept);
  *   N >= ctx gives tau = -inf (select everything); an empty selection gives
  *   the zero vector; inputs are bf16 bit patterns, every product and sum is
- *   done in double.
+ *   done in double.  An fp8 key cache holds E4M3 codes with one fp32 scale
+ *   per (batch row, key head); key value = scale * decode(code), and the rest
+ *   is the bf16 computation on those values.
  *
  * Precision: fp64 throughout on exactly the bf16 values the device sees.
  * Parallelism: one OpenMP loop over independent (b, i) pairs; nothing else.
@@ -53,6 +58,53 @@ static double bf16_to_double(uint16_t bits)
     float f;
     memcpy(&f, &u, sizeof f);
     return (double)f;
+}
+
+/* OCP E4M3 ([F8]): sign bit, 4 exponent bits (bias 7), 3 mantissa bits.
+ * Exponent field 0 is subnormal, (m/8) * 2^-6; the all-ones code S.1111.111
+ * is NaN; there are no infinities, so exponent field 15 with m < 7 is an
+ * ordinary normal (largest 1.75 * 2^8 = 448). */
+static double e4m3_to_double(uint8_t code)
+{
+    const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* A key cache [B][hk][cache_len][d]: bf16 bit patterns, or E4M3 codes with
+ * one scale per (batch row, key head). */
+typedef struct {
+    const uint16_t* bf16;
+    const uint8_t* e4m3;
+    const float* scale;   /* [B][hk], with e4m3 */
+} key_cache;
+
+/* Row 0 of one key head of a key cache. */
+typedef struct {
+    const uint16_t* bf16;
+    const uint8_t* e4m3;
+    double scale;
+} key_head;
+
+static key_head key_head_of(const key_cache* kc, int b, int hk, int g, int64_t cache_len, int d)
+{
+    key_head h = {NULL, NULL, 1.0};
+    const int64_t off = (((int64_t)b * hk + g) * cache_len) * d;
+    if (kc->e4m3) {
+        h.e4m3 = kc->e4m3 + off;
+        h.scale = (double)kc->scale[(int64_t)b * hk + g];
+    } else {
+        h.bf16 = kc->bf16 + off;
+    }
+    return h;
+}
+
+/* Element idx (= j * d + c) of a key head, as a double. */
+static double key_at(const key_head* k, int64_t idx)
+{
+    if (k->e4m3) return k->scale * e4m3_to_double(k->e4m3[idx]);
+    return bf16_to_double(k->bf16[idx]);
 }
 
 static int check_dims(int B, int hq, int hk, int hv, int d, int64_t cache_len)
@@ -79,13 +131,13 @@ static const uint16_t* cache_head(const uint16_t* cache, int b, int H, int h,
 }
 
 /* s[j] = scale * sum_c q[c] * K[j][c], for j < ctx  (one query head). */
-static void head_logits(const uint16_t* q, const uint16_t* Kh, int d, int64_t ctx,
+static void head_logits(const uint16_t* q, const key_head* Kh, int d, int64_t ctx,
                         double scale, double* s)
 {
     for (int64_t j = 0; j < ctx; ++j) {
         double acc = 0.0;
         for (int c = 0; c < d; ++c)
-            acc += bf16_to_double(q[c]) * bf16_to_double(Kh[j * d + c]);
+            acc += bf16_to_double(q[c]) * key_at(Kh, j * d + c);
         s[j] = scale * acc;
     }
 }
@@ -133,10 +185,9 @@ static int64_t attend_selected(const double* s, const unsigned char* sel, int64_
 
 /* ------------------------------------------------------------- public API */
 
-/* Logits of one decode step for every (b, i): out s[B][hq][ctx]. */
-int oracle_logits(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t ctx,
-                  double scale, const uint16_t* q, const uint16_t* K, double* s,
-                  int nthreads)
+static int logits_impl(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t ctx,
+                       double scale, const uint16_t* q, const key_cache* K, double* s,
+                       int nthreads)
 {
     if (check_dims(B, hq, hk, hv, d, cache_len) || ctx < 1 || ctx > cache_len) return 1;
     set_threads(nthreads);
@@ -144,10 +195,34 @@ int oracle_logits(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64
 #pragma omp parallel for schedule(dynamic, 1)
     for (int bi = 0; bi < B * hq; ++bi) {
         int b = bi / hq, i = bi % hq;
-        head_logits(q + (int64_t)bi * d, cache_head(K, b, hk, i / Gk, cache_len, d), d,
-                    ctx, scale, s + (int64_t)bi * ctx);
+        const key_head Kh = key_head_of(K, b, hk, i / Gk, cache_len, d);
+        head_logits(q + (int64_t)bi * d, &Kh, d, ctx, scale, s + (int64_t)bi * ctx);
     }
     return 0;
+}
+
+/* Logits of one decode step for every (b, i): out s[B][hq][ctx]. */
+int oracle_logits(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t ctx,
+                  double scale, const uint16_t* q, const uint16_t* K, double* s,
+                  int nthreads)
+{
+    const key_cache kc = {K, NULL, NULL};
+    return logits_impl(B, hq, hk, hv, d, cache_len, ctx, scale, q, &kc, s, nthreads);
+}
+
+/* The same with an E4M3 key cache K8 and per-(b, key head) scales k_scale. */
+int oracle_logits_e4m3k(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t ctx,
+                        double scale, const uint16_t* q, const uint8_t* K8,
+                        const float* k_scale, double* s, int nthreads)
+{
+    const key_cache kc = {NULL, K8, k_scale};
+    return logits_impl(B, hq, hk, hv, d, cache_len, ctx, scale, q, &kc, s, nthreads);
+}
+
+/* Decode n E4M3 codes ([F8]) to doubles (NaN for the two NaN codes). */
+void oracle_e4m3_decode(const uint8_t* codes, int64_t n, double* out)
+{
+    for (int64_t k = 0; k < n; ++k) out[k] = e4m3_to_double(codes[k]);
 }
 
 /* Exact top-N threshold of one logit row: the N-th largest value, -inf if N >= n. */
@@ -175,11 +250,11 @@ double oracle_nth_largest(const double* s, int64_t n, int64_t N)
  *   sel    [T][B][hq][cache_len] uint8, nullable (1 = selected)
  *   logits [T][B][hq][cache_len] double, nullable
  */
-int oracle_atopn_run(int B, int hq, int hk, int hv, int d, int64_t cache_len,
-                     int T, const int64_t* ctx, double scale, int64_t top_n,
-                     int64_t refresh_n, const uint16_t* q, const uint16_t* K,
-                     const uint16_t* V, double* out, double* tau, int64_t* count,
-                     unsigned char* sel, double* logits, int nthreads)
+static int atopn_run_impl(int B, int hq, int hk, int hv, int d, int64_t cache_len,
+                          int T, const int64_t* ctx, double scale, int64_t top_n,
+                          int64_t refresh_n, const uint16_t* q, const key_cache* K,
+                          const uint16_t* V, double* out, double* tau, int64_t* count,
+                          unsigned char* sel, double* logits, int nthreads)
 {
     if (check_dims(B, hq, hk, hv, d, cache_len) || T < 1 || top_n < 1 || refresh_n < 1)
         return 1;
@@ -191,7 +266,7 @@ int oracle_atopn_run(int B, int hq, int hk, int hv, int d, int64_t cache_len,
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
     for (int bi = 0; bi < B * hq; ++bi) {
         const int b = bi / hq, i = bi % hq;
-        const uint16_t* Kh = cache_head(K, b, hk, i / Gk, cache_len, d);
+        const key_head Kh = key_head_of(K, b, hk, i / Gk, cache_len, d);
         const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, d);
         double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);
         unsigned char* S = (unsigned char*)malloc((size_t)cache_len);
@@ -200,7 +275,7 @@ int oracle_atopn_run(int B, int hq, int hk, int hv, int d, int64_t cache_len,
         for (int t = 0; t < T; ++t) {
             const int64_t n = ctx[t];
             const int64_t row = (int64_t)t * B * hq + bi;
-            head_logits(q + row * d, Kh, d, n, scale, s);
+            head_logits(q + row * d, &Kh, d, n, scale, s);
             if (t % refresh_n == 0) threshold = nth_largest(s, n, top_n);
             for (int64_t j = 0; j < n; ++j) S[j] = (s[j] >= threshold);
             count[row] = attend_selected(s, S, n, Vh, d, out + row * d);
@@ -220,12 +295,36 @@ int oracle_atopn_run(int B, int hq, int hk, int hv, int d, int64_t cache_len,
     return err;
 }
 
+int oracle_atopn_run(int B, int hq, int hk, int hv, int d, int64_t cache_len,
+                     int T, const int64_t* ctx, double scale, int64_t top_n,
+                     int64_t refresh_n, const uint16_t* q, const uint16_t* K,
+                     const uint16_t* V, double* out, double* tau, int64_t* count,
+                     unsigned char* sel, double* logits, int nthreads)
+{
+    const key_cache kc = {K, NULL, NULL};
+    return atopn_run_impl(B, hq, hk, hv, d, cache_len, T, ctx, scale, top_n, refresh_n, q,
+                          &kc, V, out, tau, count, sel, logits, nthreads);
+}
+
+/* Atop-N as above with an E4M3 key cache K8 [B][hk][cache_len][d] and
+ * per-(b, key head) scales k_scale [B][hk]. */
+int oracle_atopn_run_e4m3k(int B, int hq, int hk, int hv, int d, int64_t cache_len,
+                           int T, const int64_t* ctx, double scale, int64_t top_n,
+                           int64_t refresh_n, const uint16_t* q, const uint8_t* K8,
+                           const float* k_scale, const uint16_t* V, double* out, double* tau,
+                           int64_t* count, unsigned char* sel, double* logits, int nthreads)
+{
+    const key_cache kc = {NULL, K8, k_scale};
+    return atopn_run_impl(B, hq, hk, hv, d, cache_len, T, ctx, scale, top_n, refresh_n, q,
+                          &kc, V, out, tau, count, sel, logits, nthreads);
+}
+
 /* One step with the selection given by the caller as a bitmap
  * [B][hq][ceil(cache_len/32)] (bit j%32 of word j/32 selects row j): the
  * "use the device's mask" mode that isolates softmax and PV from selection. */
-int oracle_masked(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t ctx,
-                  double scale, const uint16_t* q, const uint16_t* K, const uint16_t* V,
-                  const uint32_t* bitmap, double* out, int64_t* count, int nthreads)
+static int masked_impl(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t ctx,
+                       double scale, const uint16_t* q, const key_cache* K, const uint16_t* V,
+                       const uint32_t* bitmap, double* out, int64_t* count, int nthreads)
 {
     if (check_dims(B, hq, hk, hv, d, cache_len) || ctx < 1 || ctx > cache_len) return 1;
     set_threads(nthreads);
@@ -238,8 +337,8 @@ int oracle_masked(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64
         double* s = (double*)malloc(sizeof(double) * (size_t)ctx);
         unsigned char* S = (unsigned char*)malloc((size_t)ctx);
         if (!s || !S) { err = 1; free(s); free(S); continue; }
-        head_logits(q + (int64_t)bi * d, cache_head(K, b, hk, i / Gk, cache_len, d), d,
-                    ctx, scale, s);
+        const key_head Kh = key_head_of(K, b, hk, i / Gk, cache_len, d);
+        head_logits(q + (int64_t)bi * d, &Kh, d, ctx, scale, s);
         const uint32_t* bits = bitmap + (int64_t)bi * words;
         for (int64_t j = 0; j < ctx; ++j) S[j] = (bits[j / 32] >> (j % 32)) & 1u;
         count[bi] = attend_selected(s, S, ctx, cache_head(V, b, hv, i / Gv, cache_len, d),
@@ -248,6 +347,26 @@ int oracle_masked(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64
         free(S);
     }
     return err;
+}
+
+int oracle_masked(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t ctx,
+                  double scale, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                  const uint32_t* bitmap, double* out, int64_t* count, int nthreads)
+{
+    const key_cache kc = {K, NULL, NULL};
+    return masked_impl(B, hq, hk, hv, d, cache_len, ctx, scale, q, &kc, V, bitmap, out, count,
+                       nthreads);
+}
+
+/* One step over a caller-given bitmap with an E4M3 key cache. */
+int oracle_masked_e4m3k(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t ctx,
+                        double scale, const uint16_t* q, const uint8_t* K8,
+                        const float* k_scale, const uint16_t* V, const uint32_t* bitmap,
+                        double* out, int64_t* count, int nthreads)
+{
+    const key_cache kc = {NULL, K8, k_scale};
+    return masked_impl(B, hq, hk, hv, d, cache_len, ctx, scale, q, &kc, V, bitmap, out, count,
+                       nthreads);
 }
 
 typedef struct { double s; int64_t j; } scored_index;
@@ -319,11 +438,12 @@ int oracle_full(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
     for (int bi = 0; bi < B * hq; ++bi) {
         const int b = bi / hq, i = bi % hq;
-        const uint16_t* Kh = cache_head(K, b, hk, i / Gk, cache_len, d);
+        const key_cache kc = {K, NULL, NULL};
+        const key_head Kh = key_head_of(&kc, b, hk, i / Gk, cache_len, d);
         const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, d);
         double* s = (double*)malloc(sizeof(double) * (size_t)ctx);
         if (!s) { err = 1; continue; }
-        head_logits(q + (int64_t)bi * d, Kh, d, ctx, scale, s);
+        head_logits(q + (int64_t)bi * d, &Kh, d, ctx, scale, s);
         double m = -INFINITY;
         for (int64_t j = 0; j < ctx; ++j) if (s[j] > m) m = s[j];
         double* o = out + (int64_t)bi * d;

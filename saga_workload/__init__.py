@@ -134,6 +134,25 @@ def make_layer(w: Workload, layer: int = 0, device="cpu", heavy_hitters: bool = 
     return {"K": K, "V": V, "q": q}
 
 
+def quantize_k_e4m3(K: torch.Tensor, pow2_scales: bool = False):
+    """An fp8 E4M3 (OCP) copy of a bf16 K cache ``[B][h_k][rows][d]``, the way
+    a serving stack would store it: one fp32 scale per (batch row, key head),
+    scale = amax / 448 (rounded up to a power of two when ``pow2_scales``),
+    codes = round-to-nearest-even(K / scale) by torch's float8_e4m3fn cast.
+
+    Returns ``(codes uint8 [B][h_k][rows][d], k_scale float32 [B][h_k])`` on
+    K's device.  Input preparation only: both sides of a parity check take
+    these same codes and scales.
+    """
+    amax = K.float().abs().amax(dim=(2, 3)).clamp_min(1e-30)
+    scale = amax / 448.0
+    if pow2_scales:
+        scale = torch.exp2(torch.ceil(torch.log2(scale)))
+    x = (K.float() / scale[:, :, None, None]).clamp(-448.0, 448.0)
+    codes = x.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    return codes, scale.to(torch.float32).contiguous()
+
+
 def bits(t: torch.Tensor):
     """bf16 tensor -> numpy uint16 bit patterns (host copy)."""
     import numpy as np

@@ -23,7 +23,8 @@ __all__ = [
     "atopn_refresh_thresholds", "saga_decode_step", "atopn_refresh_decode_step",
     "SagaPaged", "paged", "atopn_refresh_thresholds_paged", "saga_decode_step_paged",
     "atopn_refresh_decode_step_paged", "atopn_refresh_thresholds_lq", "saga_decode_step_lq",
-    "atopn_refresh_decode_step_lq", "alloc_workspace_lq", "saga_full_attention",
+    "atopn_refresh_decode_step_lq", "alloc_workspace_lq", "atopn_refresh_thresholds_fp8k",
+    "saga_decode_step_fp8k", "atopn_refresh_decode_step_fp8k", "saga_full_attention",
     "saga_status_string", "saga_version", "LIB_PATH", "EXPORTED_SYMBOLS",
 ]
 
@@ -32,7 +33,8 @@ EXPORTED_SYMBOLS = ("saga_workspace_bytes", "atopn_refresh_thresholds", "saga_de
                     "atopn_refresh_decode_step", "atopn_refresh_thresholds_paged",
                     "saga_decode_step_paged", "atopn_refresh_decode_step_paged",
                     "atopn_refresh_thresholds_lq", "saga_decode_step_lq",
-                    "atopn_refresh_decode_step_lq",
+                    "atopn_refresh_decode_step_lq", "atopn_refresh_thresholds_fp8k",
+                    "saga_decode_step_fp8k", "atopn_refresh_decode_step_fp8k",
                     "saga_full_attention", "saga_status_string", "saga_version")
 
 SAGA_OK = 0
@@ -117,6 +119,13 @@ def library():
         lib.atopn_refresh_decode_step_lq.argtypes = [pd, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                                      sz, vp]
         lib.atopn_refresh_decode_step_lq.restype = ctypes.c_int
+        lib.atopn_refresh_thresholds_fp8k.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.atopn_refresh_thresholds_fp8k.restype = ctypes.c_int
+        lib.saga_decode_step_fp8k.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.saga_decode_step_fp8k.restype = ctypes.c_int
+        lib.atopn_refresh_decode_step_fp8k.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                       sz, vp]
+        lib.atopn_refresh_decode_step_fp8k.restype = ctypes.c_int
         lib.saga_full_attention.argtypes = [pd, vp, vp, vp, vp, vp, sz, vp]
         lib.saga_full_attention.restype = ctypes.c_int
         lib.saga_status_string.argtypes = [ctypes.c_int]
@@ -384,6 +393,84 @@ def atopn_refresh_decode_step_lq(d: SagaDims, l_q: int, top_n: int, q: torch.Ten
         _ptr(thresholds, torch.float32, "thresholds"), _ptr(out, torch.bfloat16, "out"),
         _ptr(sel_counts, torch.int32, "sel_counts"), ws, nbytes, _stream(stream)),
         "atopn_refresh_decode_step_lq")
+
+
+def _ptr_k8(t: torch.Tensor):
+    """An fp8 E4M3 (OCP) K cache: torch.float8_e4m3fn, or its raw bytes as uint8."""
+    if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+        return _ptr(t, torch.float8_e4m3fn, "k8_cache")
+    return _ptr(t, torch.uint8, "k8_cache")
+
+
+def _need_fp8k(d: SagaDims, k8_cache: torch.Tensor, k_scale: torch.Tensor):
+    _need(k8_cache, d.batch * d.h_k * d.cache_len * d.head_dim, "k8_cache")
+    _need(k_scale, d.batch * d.h_k, "k_scale")
+
+
+def atopn_refresh_thresholds_fp8k(d: SagaDims, top_n: int, q: torch.Tensor,
+                                  k8_cache: torch.Tensor, k_scale: torch.Tensor,
+                                  thresholds: torch.Tensor, workspace: torch.Tensor,
+                                  logits_debug: Optional[torch.Tensor] = None,
+                                  stream=None) -> None:
+    """Refresh thresholds with an fp8 K cache (k_scale fp32 ``[B][h_k]``)."""
+    bh = d.batch * d.h_q
+    _need(q, bh * d.head_dim, "q")
+    _need_fp8k(d, k8_cache, k_scale)
+    _need(thresholds, bh, "thresholds")
+    _need(logits_debug, bh * d.ctx_len, "logits_debug")
+    ws, nbytes = _ws(workspace)
+    _check(library().atopn_refresh_thresholds_fp8k(
+        ctypes.byref(d), int(top_n), _ptr(q, torch.bfloat16, "q"), _ptr_k8(k8_cache),
+        _ptr(k_scale, torch.float32, "k_scale"), _ptr(thresholds, torch.float32, "thresholds"),
+        _ptr(logits_debug, torch.float32, "logits_debug"), ws, nbytes, _stream(stream)),
+        "atopn_refresh_thresholds_fp8k")
+
+
+def saga_decode_step_fp8k(d: SagaDims, q: torch.Tensor, k8_cache: torch.Tensor,
+                          k_scale: torch.Tensor, v_cache: torch.Tensor, thresholds: torch.Tensor,
+                          out: torch.Tensor, workspace: torch.Tensor,
+                          sel_counts: Optional[torch.Tensor] = None,
+                          sel_bitmap_debug: Optional[torch.Tensor] = None, stream=None) -> None:
+    """A decode step with an fp8 K cache and a bf16 V cache."""
+    bh = d.batch * d.h_q
+    _need(q, bh * d.head_dim, "q")
+    _need_fp8k(d, k8_cache, k_scale)
+    _need(v_cache, d.batch * d.h_v * d.cache_len * d.head_dim, "v_cache")
+    _need(thresholds, bh, "thresholds")
+    _need(out, bh * d.head_dim, "out")
+    _need(sel_counts, bh, "sel_counts")
+    _need(sel_bitmap_debug, bh * ((d.cache_len + 31) // 32), "sel_bitmap_debug")
+    ws, nbytes = _ws(workspace)
+    _check(library().saga_decode_step_fp8k(
+        ctypes.byref(d), _ptr(q, torch.bfloat16, "q"), _ptr_k8(k8_cache),
+        _ptr(k_scale, torch.float32, "k_scale"), _ptr(v_cache, torch.bfloat16, "v_cache"),
+        _ptr(thresholds, torch.float32, "thresholds"), _ptr(out, torch.bfloat16, "out"),
+        _ptr(sel_counts, torch.int32, "sel_counts"),
+        _ptr(sel_bitmap_debug, torch.int32, "sel_bitmap_debug"), ws, nbytes, _stream(stream)),
+        "saga_decode_step_fp8k")
+
+
+def atopn_refresh_decode_step_fp8k(d: SagaDims, top_n: int, q: torch.Tensor,
+                                   k8_cache: torch.Tensor, k_scale: torch.Tensor,
+                                   v_cache: torch.Tensor, thresholds: torch.Tensor,
+                                   out: torch.Tensor, workspace: torch.Tensor,
+                                   sel_counts: Optional[torch.Tensor] = None,
+                                   stream=None) -> None:
+    """A refresh step with an fp8 K cache: fresh thresholds and this step's output."""
+    bh = d.batch * d.h_q
+    _need(q, bh * d.head_dim, "q")
+    _need_fp8k(d, k8_cache, k_scale)
+    _need(v_cache, d.batch * d.h_v * d.cache_len * d.head_dim, "v_cache")
+    _need(thresholds, bh, "thresholds")
+    _need(out, bh * d.head_dim, "out")
+    _need(sel_counts, bh, "sel_counts")
+    ws, nbytes = _ws(workspace)
+    _check(library().atopn_refresh_decode_step_fp8k(
+        ctypes.byref(d), int(top_n), _ptr(q, torch.bfloat16, "q"), _ptr_k8(k8_cache),
+        _ptr(k_scale, torch.float32, "k_scale"), _ptr(v_cache, torch.bfloat16, "v_cache"),
+        _ptr(thresholds, torch.float32, "thresholds"), _ptr(out, torch.bfloat16, "out"),
+        _ptr(sel_counts, torch.int32, "sel_counts"), ws, nbytes, _stream(stream)),
+        "atopn_refresh_decode_step_fp8k")
 
 
 def saga_full_attention(d: SagaDims, q: torch.Tensor, k_cache: torch.Tensor,

@@ -135,11 +135,13 @@ Partials partials(void* ws, const Layout& L)
 int hip_status(hipError_t e) { return e == hipSuccess ? SAGA_OK : SAGA_ERR_HIP; }
 
 // What each (b, query head) row attends: paged caches and per-sequence
-// lengths (pg), and query tokens per step (lq; the call's h_q then counts
-// virtual heads, one per token).
+// lengths (pg), query tokens per step (lq; the call's h_q then counts
+// virtual heads, one per token), and an fp8 e4m3 K cache with one scale per
+// (b, key head) (k_scale; null for bf16 K).
 struct RowModel {
     PagedKV pg{};
     int32_t lq = 1;
+    const float* k_scale = nullptr;
 };
 
 // Arguments of the stream-select kernel for one call.
@@ -167,6 +169,7 @@ SelectStreamArgs stream_args(const saga_dims* dims, const Layout& L, const Chunk
     a.scale = dims->scale;
     a.pg = rm.pg;
     a.lq = rm.lq;
+    a.k_scale = rm.k_scale;
     return a;
 }
 
@@ -232,6 +235,7 @@ int enqueue_refresh(const saga_dims* dims, int32_t top_n, const void* q_dev,
     sa.ctx = dims->ctx_len;
     sa.pg = rm.pg;
     sa.lq = rm.lq;
+    sa.k_scale = rm.k_scale;
     int st = hip_status(launch_sample(D, sa, s));
     if (st != SAGA_OK) return st;
 
@@ -262,6 +266,7 @@ int enqueue_refresh(const saga_dims* dims, int32_t top_n, const void* q_dev,
     fa.scale = dims->scale;
     fa.pg = rm.pg;
     fa.lq = rm.lq;
+    fa.k_scale = rm.k_scale;
     return hip_status(launch_refresh_final(D, fa, s));
 }
 
@@ -593,6 +598,61 @@ SAGA_EXPORT int atopn_refresh_decode_step_lq(const saga_dims* dims, int32_t l_q,
     RowModel rm;
     rm.lq = l_q;
     return do_refresh_decode(&v, rm, top_n, q_dev, k_cache_dev, v_cache_dev, thresholds_dev,
+                             out_dev, sel_counts_dev, workspace_dev, workspace_bytes, stream);
+}
+
+namespace {
+
+// An fp8 K cache: a scale pointer (4-byte aligned) per call.
+int fp8k_model(const saga_dims* dims, const float* k_scale_dev, RowModel* rm)
+{
+    const int st = validate_dims(dims);
+    if (st != SAGA_OK) return st;
+    if (!k_scale_dev || misaligned(k_scale_dev, 4)) return SAGA_ERR_INVALID_ARGUMENT;
+    rm->k_scale = k_scale_dev;
+    return SAGA_OK;
+}
+
+}  // namespace
+
+SAGA_EXPORT int atopn_refresh_thresholds_fp8k(const saga_dims* dims, int32_t top_n,
+                                              const void* q_dev, const void* k8_cache_dev,
+                                              const float* k_scale_dev, float* thresholds_dev,
+                                              float* logits_debug_dev, void* workspace_dev,
+                                              size_t workspace_bytes, void* stream)
+{
+    RowModel rm;
+    const int st = fp8k_model(dims, k_scale_dev, &rm);
+    if (st != SAGA_OK) return st;
+    return do_refresh(dims, rm, top_n, q_dev, k8_cache_dev, thresholds_dev, logits_debug_dev,
+                      workspace_dev, workspace_bytes, stream);
+}
+
+SAGA_EXPORT int saga_decode_step_fp8k(const saga_dims* dims, const void* q_dev,
+                                      const void* k8_cache_dev, const float* k_scale_dev,
+                                      const void* v_cache_dev, const float* thresholds_dev,
+                                      void* out_dev, int32_t* sel_counts_dev,
+                                      uint32_t* sel_bitmap_debug_dev, void* workspace_dev,
+                                      size_t workspace_bytes, void* stream)
+{
+    RowModel rm;
+    const int st = fp8k_model(dims, k_scale_dev, &rm);
+    if (st != SAGA_OK) return st;
+    return do_decode(dims, rm, q_dev, k8_cache_dev, v_cache_dev, thresholds_dev, out_dev,
+                     sel_counts_dev, sel_bitmap_debug_dev, workspace_dev, workspace_bytes, stream);
+}
+
+SAGA_EXPORT int atopn_refresh_decode_step_fp8k(const saga_dims* dims, int32_t top_n,
+                                               const void* q_dev, const void* k8_cache_dev,
+                                               const float* k_scale_dev, const void* v_cache_dev,
+                                               float* thresholds_dev, void* out_dev,
+                                               int32_t* sel_counts_dev, void* workspace_dev,
+                                               size_t workspace_bytes, void* stream)
+{
+    RowModel rm;
+    const int st = fp8k_model(dims, k_scale_dev, &rm);
+    if (st != SAGA_OK) return st;
+    return do_refresh_decode(dims, rm, top_n, q_dev, k8_cache_dev, v_cache_dev, thresholds_dev,
                              out_dev, sel_counts_dev, workspace_dev, workspace_bytes, stream);
 }
 

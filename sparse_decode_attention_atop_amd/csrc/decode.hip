@@ -39,7 +39,7 @@ namespace {
 // queue could overflow, it is split by head slot and appended to the global
 // per-(head, chunk, wave) lists in order.  DEBUG adds the optional logits and
 // selection-bitmap outputs.
-template <int D, int U, bool DEBUG, bool PAGED>
+template <int D, int U, bool DEBUG, bool PAGED, bool FP8>
 __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(SelectStreamArgs a)
 {
     __shared__ uint2 queue[kWavesPerBlock][4][kQueueCap];
@@ -60,6 +60,8 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
     if (a.group_flags && a.group_flags[blockIdx.y] == 0u) return;   // whole workgroup
 
     const QFrag<D> qf = load_qfrag<D>(col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr);
+    // Logit scale; an fp8 K cache adds its (b, key head) scale.
+    const float sc = FP8 ? a.scale * a.k_scale[blockIdx.y] : a.scale;
     float tau[4], mx[4];
     int64_t lim[4];          // rows of this lane's head slots: r1, or less for later tokens
 #pragma unroll
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float s[4];
-            qk_group<D>(qf, kt.v[u], a.scale, s);
+            qk_group<D>(qf, kt.v[u], sc, s);
             const int64_t row = t0 + 16 * u + col;
             const bool valid = row < r1;
             const uint32_t tag = (uint32_t)(row - r0) << 4;
@@ -197,6 +199,32 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
                 tp += 2 * kStep;
                 ra = rn;
             } while (tp < r1);
+        }
+    } else if constexpr (FP8) {
+        // fp8 K (one byte per element): the same pipeline on half the bytes;
+        // each tile is widened to bf16 in registers before the QK routine.
+        const uint8_t* k8 = reinterpret_cast<const uint8_t*>(a.k);
+        const __amdgpu_buffer_rsrc_t khead =
+            make_rsrc(k8 + ((int64_t)(b * a.hk + g) * a.cache_len) * D, (uint32_t)(r1 * D));
+        int64_t t0 = r0 + wave * 16 * U;
+        if (t0 < r1) {
+            constexpr uint32_t kStepBytes = (uint32_t)(kStep * D);
+            uint32_t koff = (uint32_t)(t0 + col) * (uint32_t)D + 8u * grp;
+            K8Tile<D, U> ka, kb;
+            KTile<D, U> kt;
+            load_k8tile_at<D, U>(ka, khead, koff);
+            do {
+                maybe_flush();
+                load_k8tile_at<D, U>(kb, khead, koff + kStepBytes);
+                widen_k8tile<D, U>(ka, kt);
+                process(kt, t0);
+                maybe_flush();
+                load_k8tile_at<D, U>(ka, khead, koff + 2 * kStepBytes);
+                widen_k8tile<D, U>(kb, kt);
+                process(kt, t0 + kStep);
+                t0 += 2 * kStep;
+                koff += 2 * kStepBytes;
+            } while (t0 < r1);
         }
     } else {
     const __amdgpu_buffer_rsrc_t khead =
@@ -564,17 +592,20 @@ hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t s)
 {
     const dim3 grid(a.chunks, a.B * a.hk);
     const bool dbg = a.bitmap != nullptr || a.logits_out != nullptr;
-    const bool paged = a.pg.block_table != nullptr;
-#define SAGA_LAUNCH_STREAM(DD, DBG, PG)                                                        \
-    hipLaunchKernelGGL((select_stream_kernel<DD, decode_unroll(DD), DBG, PG>), grid, dim3(kBlock), \
-                       0, s, a)
+    const int kind = a.pg.block_table != nullptr ? 1 : (a.k_scale != nullptr ? 2 : 0);
+#define SAGA_LAUNCH_STREAM(DD, DBG, PG, F8)                                                      \
+    hipLaunchKernelGGL((select_stream_kernel<DD, decode_unroll(DD), DBG, PG, F8>), grid,         \
+                       dim3(kBlock), 0, s, a)
+#define SAGA_LAUNCH_STREAM_D(DD)                                                                 \
+    if (kind == 1) { if (dbg) SAGA_LAUNCH_STREAM(DD, true, true, false); else SAGA_LAUNCH_STREAM(DD, false, true, false); } \
+    else if (kind == 2) { if (dbg) SAGA_LAUNCH_STREAM(DD, true, false, true); else SAGA_LAUNCH_STREAM(DD, false, false, true); } \
+    else { if (dbg) SAGA_LAUNCH_STREAM(DD, true, false, false); else SAGA_LAUNCH_STREAM(DD, false, false, false); }
     if (D == 64) {
-        if (paged) { if (dbg) SAGA_LAUNCH_STREAM(64, true, true); else SAGA_LAUNCH_STREAM(64, false, true); }
-        else { if (dbg) SAGA_LAUNCH_STREAM(64, true, false); else SAGA_LAUNCH_STREAM(64, false, false); }
+        SAGA_LAUNCH_STREAM_D(64)
     } else {
-        if (paged) { if (dbg) SAGA_LAUNCH_STREAM(128, true, true); else SAGA_LAUNCH_STREAM(128, false, true); }
-        else { if (dbg) SAGA_LAUNCH_STREAM(128, true, false); else SAGA_LAUNCH_STREAM(128, false, false); }
+        SAGA_LAUNCH_STREAM_D(128)
     }
+#undef SAGA_LAUNCH_STREAM_D
 #undef SAGA_LAUNCH_STREAM
     return hipGetLastError();
 }

@@ -77,6 +77,25 @@ __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off
 // vmcnt bits [3:0] and [15:14] zero, expcnt [6:4] = 7, lgkmcnt [11:8] = 15.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// Eight fp8 e4m3 (OCP: bias 7, max 448, no infinities) values, in byte order,
+// widened to eight bf16 (exact: 3 mantissa bits fit bf16's 7).
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 x)
+{
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, true));
+    return r;
+}
+
 // ------------------------------------------------------------ wave utilities
 // Orders LDS traffic between lanes of one wave (no workgroup barrier).
 __device__ __forceinline__ void wave_sync()
@@ -219,6 +238,35 @@ __device__ __forceinline__ void load_ktile_at(KTile<D, U>& t, __amdgpu_buffer_rs
 #pragma unroll
         for (int m = 0; m < D / 32; ++m)
             t.v[u][m] = buf_ld16(k_head, lane_off + (uint32_t)(16 * u * D * 2 + 64 * m));
+}
+
+// fp8 K: the same tile layout with one byte per element (8 bytes per lane and
+// MFMA slab), widened to the bf16 tile before the shared QK routine.
+template <int D, int U>
+struct K8Tile {
+    u32x2 v[U][D / 32];
+};
+
+// Lane byte offset (row0 + lane%16) * D + 8*(lane/16); the loads differ by
+// compile-time constants.
+template <int D, int U>
+__device__ __forceinline__ void load_k8tile_at(K8Tile<D, U>& t, __amdgpu_buffer_rsrc_t k_head,
+                                               uint32_t lane_off)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m)
+            t.v[u][m] = buf_ld8(k_head, lane_off + (uint32_t)(16 * u * D + 32 * m));
+}
+
+template <int D, int U>
+__device__ __forceinline__ void widen_k8tile(const K8Tile<D, U>& a, KTile<D, U>& t)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) t.v[u][m] = fp8x8_to_bf16x8(a.v[u][m]);
 }
 
 // logits[u][i] = scale * sum_c q[slot 4*(lane/16)+i][c] * K[row0+16u+lane%16][c]

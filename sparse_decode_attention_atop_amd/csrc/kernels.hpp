@@ -134,6 +134,7 @@ struct SelectStreamArgs {
     int32_t chunks;
     float scale;
     int32_t lq;              // query tokens per query head and step (1: one)
+    const float* k_scale;    // non-null: fp8 e4m3 K, one scale per (b, key head)
     PagedKV pg;              // paged caches (block_table != nullptr)
 };
 
@@ -167,6 +168,7 @@ struct SampleArgs {
     int32_t top_n;               // paged: per-row rank from each sequence's length
     float scale;
     int32_t lq;              // query tokens per query head and step (1: one)
+    const float* k_scale;    // non-null: fp8 e4m3 K, one scale per (b, key head)
     PagedKV pg;              // paged caches (block_table != nullptr)
 };
 
@@ -185,6 +187,7 @@ struct FinalArgs {
     uint32_t top_n;
     float scale;
     int32_t lq;              // query tokens per query head and step (1: one)
+    const float* k_scale;    // non-null: fp8 e4m3 K, one scale per (b, key head)
     PagedKV pg;              // paged caches (block_table != nullptr)
 };
 

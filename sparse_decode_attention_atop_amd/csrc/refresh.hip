@@ -116,7 +116,7 @@ __device__ uint32_t lds_radix_select(const uint32_t* keys, uint32_t n, uint32_t 
 // made of 16-row blocks (one MFMA group each, contiguous in memory): sample
 // index k covers row (k/16)*stride + k%16, k < m.  Output sample[b*hq + i][k]
 // (row stride kSampleMax).
-template <int D, int U, bool PAGED>
+template <int D, int U, bool PAGED, bool FP8>
 __global__ __launch_bounds__(kBlock) void sample_logits_kernel(SampleArgs a)
 {
     const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -140,15 +140,23 @@ __global__ __launch_bounds__(kBlock) void sample_logits_kernel(SampleArgs a)
             // Rows past the sequence (and pages outside the pool) read nothing.
             const int64_t base = row < ctx_b ? page_base<D>(a.pg, b, g, a.hk, row) : -1;
             p = base < 0 ? nullptr : a.k + base + (row % a.pg.page_rows) * D + 8 * grp;
+        } else if constexpr (FP8) {
+            p = nullptr;
+            const uint8_t* p8 = reinterpret_cast<const uint8_t*>(a.k) +
+                                ((int64_t)(b * a.hk + g) * a.cache_len + row) * D + 8 * grp;
+#pragma unroll
+            for (int mm = 0; mm < D / 32; ++mm) kt.v[u][mm] = fp8x8_to_bf16x8(ld8(p8 + 32 * mm));
         } else {
             p = khead + row * D + 8 * grp;
         }
+        if constexpr (!FP8) {
 #pragma unroll
-        for (int mm = 0; mm < D / 32; ++mm)
-            kt.v[u][mm] = p ? ld16(p + 32 * mm) : u32x4{0u, 0u, 0u, 0u};
+            for (int mm = 0; mm < D / 32; ++mm)
+                kt.v[u][mm] = p ? ld16(p + 32 * mm) : u32x4{0u, 0u, 0u, 0u};
+        }
     }
     float s[U][4];
-    qk_tile<D, U>(qf, kt, a.scale, s);
+    qk_tile<D, U>(qf, kt, FP8 ? a.scale * a.k_scale[blockIdx.y] : a.scale, s);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int k = k0 + 16 * u + col;
@@ -219,7 +227,7 @@ __global__ __launch_bounds__(kBlock) void pivot_kernel(SampleArgs a)
 // Exact N-th largest of one row by recomputing its logits (three radix passes
 // over the row's key head, each with the shared QK tile).  Used when the
 // candidate lists cannot answer.
-template <int D, int U, bool PAGED>
+template <int D, int U, bool PAGED, bool FP8>
 __device__ uint32_t select_by_recompute(const FinalArgs& a, int row, int64_t ctx, SelectLds& w)
 {
     const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -229,6 +237,8 @@ __device__ uint32_t select_by_recompute(const FinalArgs& a, int row, int64_t ctx
     const int qh0 = b * a.hq + g * a.Gk;
     const QFrag<D> qf = load_qfrag<D>(col < a.Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr);
     const uint16_t* khead = a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
+    const uint8_t* khead8 = reinterpret_cast<const uint8_t*>(a.k) + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
+    const float sc = FP8 ? a.scale * a.k_scale[b * a.hk + g] : a.scale;
     uint32_t prefix = 0u, rank = a.top_n;
     for (int pass = 0; pass < 3; ++pass) {
         const int sh = digit_shift(pass);
@@ -247,11 +257,21 @@ __device__ uint32_t select_by_recompute(const FinalArgs& a, int row, int64_t ctx
 #pragma unroll
                     for (int m = 0; m < D / 32; ++m)
                         kt.v[u][m] = p ? ld16_stream(p + 16 * u * D + 32 * m) : u32x4{0u, 0u, 0u, 0u};
+            } else if constexpr (FP8) {
+                // Rows past ctx re-read the last row; they are skipped below.
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    int64_t r = t0 + 16 * u + col;
+                    r = r < ctx ? r : ctx - 1;
+#pragma unroll
+                    for (int m = 0; m < D / 32; ++m)
+                        kt.v[u][m] = fp8x8_to_bf16x8(ld8(khead8 + r * D + 8 * grp + 32 * m));
+                }
             } else {
                 load_ktile<D, U>(kt, khead, t0, ctx);
             }
             float s[U][4];
-            qk_tile<D, U>(qf, kt, a.scale, s);
+            qk_tile<D, U>(qf, kt, sc, s);
             if (grp == (slot >> 2)) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -274,7 +294,7 @@ __device__ uint32_t select_by_recompute(const FinalArgs& a, int row, int64_t ctx
     return prefix;
 }
 
-template <int D, int U, bool PAGED>
+template <int D, int U, bool PAGED, bool FP8>
 __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
 {
     __shared__ int32_t pre[kMaxListsPerRow + 1];
@@ -343,7 +363,7 @@ __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
         __syncthreads();
         key = lds_radix_select(keys, total, a.top_n, w);
     } else {
-        key = select_by_recompute<D, U, PAGED>(a, row, ctx, w);
+        key = select_by_recompute<D, U, PAGED, FP8>(a, row, ctx, w);
         // The lists miss entries of this row: a fused decode must re-stream its group.
         if (t == 0 && a.group_flags) {
             const int b = row / a.hq;
@@ -360,14 +380,19 @@ hipError_t launch_sample(int D, const SampleArgs& a, hipStream_t s)
     constexpr int U = 4;
     const int per_block = kWavesPerBlock * 16 * U;
     const dim3 grid((a.m + per_block - 1) / per_block, a.B * a.hk);
-    const bool paged = a.pg.block_table != nullptr;
+    const int kind = a.pg.block_table != nullptr ? 1 : (a.k_scale != nullptr ? 2 : 0);
+#define SAGA_LAUNCH_SAMPLE(DD, PG, F8)                                                            \
+    hipLaunchKernelGGL((sample_logits_kernel<DD, U, PG, F8>), grid, dim3(kBlock), 0, s, a)
     if (D == 64) {
-        if (paged) hipLaunchKernelGGL((sample_logits_kernel<64, U, true>), grid, dim3(kBlock), 0, s, a);
-        else hipLaunchKernelGGL((sample_logits_kernel<64, U, false>), grid, dim3(kBlock), 0, s, a);
+        if (kind == 1) SAGA_LAUNCH_SAMPLE(64, true, false);
+        else if (kind == 2) SAGA_LAUNCH_SAMPLE(64, false, true);
+        else SAGA_LAUNCH_SAMPLE(64, false, false);
     } else {
-        if (paged) hipLaunchKernelGGL((sample_logits_kernel<128, U, true>), grid, dim3(kBlock), 0, s, a);
-        else hipLaunchKernelGGL((sample_logits_kernel<128, U, false>), grid, dim3(kBlock), 0, s, a);
+        if (kind == 1) SAGA_LAUNCH_SAMPLE(128, true, false);
+        else if (kind == 2) SAGA_LAUNCH_SAMPLE(128, false, true);
+        else SAGA_LAUNCH_SAMPLE(128, false, false);
     }
+#undef SAGA_LAUNCH_SAMPLE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pivot_kernel, dim3(a.B * a.hq), dim3(kBlock), 0, s, a);
@@ -376,12 +401,19 @@ hipError_t launch_sample(int D, const SampleArgs& a, hipStream_t s)
 
 hipError_t launch_refresh_final(int D, const FinalArgs& a, hipStream_t s)
 {
-    const bool paged = a.pg.block_table != nullptr;
-#define SAGA_LAUNCH_FINAL(DD, PG)                                                                 \
-    hipLaunchKernelGGL((refresh_final_kernel<DD, decode_unroll(DD), PG>), dim3(a.B * a.hq),        \
+    const int kind = a.pg.block_table != nullptr ? 1 : (a.k_scale != nullptr ? 2 : 0);
+#define SAGA_LAUNCH_FINAL(DD, PG, F8)                                                             \
+    hipLaunchKernelGGL((refresh_final_kernel<DD, decode_unroll(DD), PG, F8>), dim3(a.B * a.hq),    \
                        dim3(kBlock), 0, s, a)
-    if (D == 64) { if (paged) SAGA_LAUNCH_FINAL(64, true); else SAGA_LAUNCH_FINAL(64, false); }
-    else { if (paged) SAGA_LAUNCH_FINAL(128, true); else SAGA_LAUNCH_FINAL(128, false); }
+    if (D == 64) {
+        if (kind == 1) SAGA_LAUNCH_FINAL(64, true, false);
+        else if (kind == 2) SAGA_LAUNCH_FINAL(64, false, true);
+        else SAGA_LAUNCH_FINAL(64, false, false);
+    } else {
+        if (kind == 1) SAGA_LAUNCH_FINAL(128, true, false);
+        else if (kind == 2) SAGA_LAUNCH_FINAL(128, false, true);
+        else SAGA_LAUNCH_FINAL(128, false, false);
+    }
 #undef SAGA_LAUNCH_FINAL
     return hipGetLastError();
 }

@@ -9,8 +9,10 @@ by ``test_oracle_mutants.py`` (every planted mistake must trip at least one).
 
 Sources: "More Value per Key: Asymmetric Sparse Attention for Faster LLM
 Decoding" -- ai.info AI summary (Key Contributions 2 and 3, Main Findings,
-Methodology) and atlas.scime.ai AI summary (Approach, Experimental setup:
-exact top-N and full-attention GQA are listed baselines).
+Methodology, Why This Matters: combinable with cache quantization) and
+atlas.scime.ai AI summary (Approach, Experimental setup: exact top-N and
+full-attention GQA are listed baselines); the OCP 8-bit floating point
+specification for the E4M3 key-cache format.
 """
 from __future__ import annotations
 
@@ -89,6 +91,25 @@ def count_rule_selection(s, N):
     s = np.asarray(s)
     greater = (s[None, :] > s[:, None]).sum(axis=1)
     return greater < N
+
+
+def rand_e4m3(seed, B, hk, rows, d, pow2_scales):
+    """Random E4M3 codes (never the NaN codes) and per-(b, key head) scales:
+    distinct powers of two, or arbitrary positive values."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(B, hk, rows, d), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] ^= 0x01                       # 0x7F/0xFF -> 0x7E/0xFE
+    if pow2_scales:
+        ks = np.array([[2.0 ** (((b * hk + g) % 7) - 3) for g in range(hk)] for b in range(B)])
+    else:
+        ks = rng.uniform(0.01, 0.3, size=(B, hk))
+    return codes, ks.astype(np.float32)
+
+
+def lib_e4m3(codes):
+    """float64 values of E4M3 codes via torch's float8_e4m3fn dtype (library)."""
+    t = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
 
 
 def assert_close(a, b, tol, what):
@@ -282,6 +303,55 @@ def pin_golden_hand_worked():
         assert_close(r["tau"][t][0], step["tau"], 0.0, f"golden tau step {t}")
         sel = r["sel"][t][0][:, :g["ctx"][t]].astype(int).tolist()
         assert sel == step["sel"], f"golden selection step {t}"
+
+
+def pin_e4m3_decode_vs_library_and_format():
+    codes = np.arange(256, dtype=np.uint8)
+    got, lib = oracle.e4m3_decode(codes), lib_e4m3(codes)
+    nan = np.isnan(got)
+    assert nan.tolist() == np.isnan(lib).tolist(), "E4M3 NaN codes"
+    assert sorted(np.flatnonzero(nan).tolist()) == [0x7F, 0xFF], "E4M3 has exactly two NaNs"
+    assert np.array_equal(got[~nan], lib[~nan]), "E4M3 decode vs torch float8_e4m3fn"
+    # Landmarks of the format: largest normal, smallest normal and subnormal, one, signed zero.
+    marks = {0x7E: 448.0, 0xFE: -448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+             0x38: 1.0, 0x3C: 1.5, 0x00: 0.0}
+    for c, v in marks.items():
+        assert got[c] == v, f"E4M3 code {c:#04x}"
+    assert math.copysign(1.0, got[0x80]) == -1.0 and got[0x80] == 0.0, "E4M3 negative zero"
+
+
+def pin_e4m3k_logits_vs_matmul():
+    """Logits with an E4M3 key cache = float64 matmul against scale * decode."""
+    B, hq, hk, d, rows, ctx = 2, 8, 2, 32, 50, 47
+    q, _, _ = rand_case(31, B, hq, hk, hk, d, rows)
+    K8, ks = rand_e4m3(32, B, hk, rows, d, pow2_scales=False)
+    Kf = torch.from_numpy(lib_e4m3(K8) * ks.astype(np.float64)[:, :, None, None])[:, :, :ctx]
+    qt = f64(q[0])
+    ref = torch.matmul(Kf.repeat_interleave(hq // hk, dim=1), qt[..., None])[..., 0] * 0.25
+    got = oracle.logits_e4m3k(q[0], K8, ks, ctx, 0.25)
+    assert_close(got / np.abs(ref.numpy()).max(), ref.numpy() / np.abs(ref.numpy()).max(),
+                 1e-13, "E4M3 logits vs matmul")
+
+
+def pin_e4m3k_reduces_to_bf16_cache():
+    """Power-of-two scales make scale * decode(code) exact in bf16: the E4M3
+    runs must then equal the bf16 runs on those values, bit for bit."""
+    T, B, hq, hk, hv, d, rows = 4, 2, 8, 2, 4, 32, 70
+    q, _, V = rand_case(33, B, hq, hk, hv, d, rows, T=T)
+    K8, ks = rand_e4m3(34, B, hk, rows, d, pow2_scales=True)
+    Kb = to_bits(torch.from_numpy(lib_e4m3(K8) * ks.astype(np.float64)[:, :, None, None]))
+    assert np.array_equal(f64(Kb).numpy(), lib_e4m3(K8) * ks[:, :, None, None]), "not exact"
+    ctx = [60 + t for t in range(T)]
+    a = oracle.atopn_run_e4m3k(q, K8, ks, V, ctx, 9, 2, 0.5, want_sel=True, want_logits=True)
+    b = oracle.atopn_run(q, Kb, V, ctx, 9, 2, 0.5, want_sel=True, want_logits=True)
+    for k in ("out", "tau", "count", "sel", "logits"):
+        assert np.array_equal(a[k], b[k]), f"E4M3 run differs from bf16 run in {k}"
+    bm = np.packbits(b["sel"][1].astype(np.uint8), axis=-1, bitorder="little")
+    bm = np.pad(bm, ((0, 0), (0, 0), (0, (-bm.shape[-1]) % 4))).view(np.uint32)
+    m8 = oracle.masked_e4m3k(q[1], K8, ks, V, ctx[1], bm, 0.5)
+    mb = oracle.masked(q[1], Kb, V, ctx[1], bm, 0.5)
+    assert np.array_equal(m8[0], mb[0]) and np.array_equal(m8[1], mb[1]), "E4M3 masked"
+    assert np.array_equal(m8[1], b["count"][1]), "masked count vs run count"
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -233,3 +233,43 @@ def test_lq_argument_checks(kind):
     need = saga.saga_workspace_bytes(saga.dims(2, 8 * 4, 2, 4, 128, 1000, 1024), 8)
     assert call_lq(kind, d, 4, need - 1) == SMALL       # workspace of h_q * l_q heads
     assert call_lq(kind, good_dims(h_q=8, h_k=2, h_v=3), 2, 1 << 40) == INVALID
+
+
+# ---- fp8 E4M3 K cache --------------------------------------------------------
+
+def call_fp8k(kind, d, ws_bytes, top_n=8, **ptrs):
+    p = dict(q=FAKE, k8=FAKE, ks=FAKE, v=FAKE, tau=FAKE, out=FAKE, ws=FAKE)
+    p.update(ptrs)
+    lib = saga.library()
+    if kind == "refresh":
+        return lib.atopn_refresh_thresholds_fp8k(ctypes.byref(d), top_n, p["q"], p["k8"], p["ks"],
+                                                 p["tau"], None, p["ws"], ws_bytes, None)
+    if kind == "decode":
+        return lib.saga_decode_step_fp8k(ctypes.byref(d), p["q"], p["k8"], p["ks"], p["v"],
+                                         p["tau"], p["out"], None, None, p["ws"], ws_bytes, None)
+    return lib.atopn_refresh_decode_step_fp8k(ctypes.byref(d), top_n, p["q"], p["k8"], p["ks"],
+                                              p["v"], p["tau"], p["out"], None, p["ws"], ws_bytes,
+                                              None)
+
+
+@pytest.mark.parametrize("kind", ["refresh", "decode", "fused"])
+def test_fp8k_argument_checks(kind):
+    d = good_dims()
+    need = saga.saga_workspace_bytes(d, 8)
+    assert call_fp8k(kind, d, 1 << 40, ks=None) == INVALID
+    assert call_fp8k(kind, d, 1 << 40, ks=ctypes.c_void_p((1 << 20) + 2)) == INVALID
+    assert call_fp8k(kind, d, 1 << 40, k8=None) == INVALID
+    assert call_fp8k(kind, d, 1 << 40, q=None) == INVALID
+    assert call_fp8k(kind, d, 1 << 40, k8=ctypes.c_void_p((1 << 20) + 8)) == INVALID
+    assert call_fp8k(kind, good_dims(ctx_len=0), 1 << 40) == INVALID
+    assert call_fp8k(kind, good_dims(head_dim=96), 1 << 40) == UNSUPPORTED
+    assert call_fp8k(kind, d, need - 1) == SMALL         # same workspace as the bf16 calls
+    if kind != "decode":
+        assert call_fp8k(kind, d, 1 << 40, top_n=0) == INVALID
+
+
+def test_fp8k_binding_rejects_wrong_dtypes():
+    d = good_dims()
+    k8 = torch.zeros(4, dtype=torch.bfloat16)
+    with pytest.raises((TypeError, ValueError)):
+        saga.atopn_refresh_thresholds_fp8k(d, 8, k8, k8, k8, k8, k8)

@@ -20,13 +20,13 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
 # (name, original text, mutated text) -- each original must occur exactly once.
 MUTANTS = [
-    ("key_operand_index", "bf16_to_double(Kh[j * d + c]);\n        s[j]",
-     "bf16_to_double(Kh[j * d + (d - 1 - c)]);\n        s[j]"),
+    ("key_operand_index", "key_at(Kh, j * d + c);\n        s[j]",
+     "key_at(Kh, j * d + (d - 1 - c));\n        s[j]"),
     ("dropped_scale", "s[j] = scale * acc;", "s[j] = acc;"),
-    ("key_head_map", "const uint16_t* Kh = cache_head(K, b, hk, i / Gk, cache_len, d);\n"
+    ("key_head_map", "const key_head Kh = key_head_of(K, b, hk, i / Gk, cache_len, d);\n"
      "        const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, d);\n"
      "        double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);",
-     "const uint16_t* Kh = cache_head(K, b, hk, i % hk, cache_len, d);\n"
+     "const key_head Kh = key_head_of(K, b, hk, i % hk, cache_len, d);\n"
      "        const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, d);\n"
      "        double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);"),
     ("value_head_map", "const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, d);\n"
@@ -47,6 +47,13 @@ MUTANTS = [
     ("empty_selection_not_zero", "if (count == 0) return 0;", "if (count == 0) { out[0] = 1.0; return 0; }"),
     ("exact_topn_keeps_one_more", "const int64_t keep = top_n < ctx ? top_n : ctx;",
      "const int64_t keep = top_n < ctx ? top_n + 1 : ctx;"),
+    ("e4m3_exponent_bias", "ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)"),
+    ("e4m3_subnormal_as_normal", "e == 0 ? ldexp((double)m / 8.0, -6)", "e == 0 ? ldexp(1.0 + (double)m / 8.0, -6)"),
+    ("e4m3_no_nan", "if (e == 15 && m == 7) return NAN;", "if (e == 16) return NAN;"),
+    ("e4m3_sign_dropped", "return sign ? -mag : mag;", "return mag;"),
+    ("e4m3_scale_index", "h.scale = (double)kc->scale[(int64_t)b * hk + g];",
+     "h.scale = (double)kc->scale[g];"),
+    ("e4m3_scale_dropped", "if (k->e4m3) return k->scale * e4m3_to_double", "if (k->e4m3) return e4m3_to_double"),
     ("full_softmax_drops_max_row", "for (int64_t j = 0; j < ctx; ++j) if (s[j] > m) m = s[j];\n        double* o",
      "for (int64_t j = 0; j < ctx; ++j) if (s[j] > m) m = s[j];\n        s[0] = -INFINITY;\n        double* o"),
 ]
