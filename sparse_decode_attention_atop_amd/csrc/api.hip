@@ -74,11 +74,12 @@ Chunking split_rows(int64_t ctx, int64_t pairs, int64_t block_rows, int64_t targ
 
 // Chunking of the K stream (stream-select kernel) for one call.  Chunks are
 // whole tile pairs (the kernel streams pairs), so with pages of kPageQuantum
-// rows no pair straddles two pages.
-Chunking plan_chunks(int64_t ctx, int64_t pairs, int head_dim, int max_chunks)
+// rows no pair straddles two pages.  An fp8 K cache (k8) streams tiles of
+// twice the rows.
+Chunking plan_chunks(int64_t ctx, int64_t pairs, int head_dim, int max_chunks, bool k8)
 {
-    return split_rows(ctx, pairs, 2 * decode_block_rows(head_dim), target_blocks(head_dim),
-                      max_chunks);
+    const int64_t block = k8 ? decode_block_rows_k8(head_dim) : decode_block_rows(head_dim);
+    return split_rows(ctx, pairs, 2 * block, target_blocks(head_dim), max_chunks);
 }
 
 // Workspace layout (byte offsets), identical for every ctx_len <= cache_len.
@@ -101,9 +102,16 @@ Layout make_layout(const saga_dims* d)
     L.max_chunks = (int)(mc < 1 ? 1 : mc);
     // chunks * rows_per_chunk <= ctx + rows_per_chunk(ctx), and rows_per_chunk
     // never exceeds max(block rows, its value at ctx = cache_len).
-    const int64_t br = 2 * decode_block_rows(d->head_dim);
-    const Chunking top = plan_chunks(d->cache_len, (int64_t)d->batch * d->h_k, d->head_dim, L.max_chunks);
-    L.entry_rows = d->cache_len + (top.rows > br ? top.rows : br);
+    // The larger of the bf16 and fp8 K plans (one layout serves both).
+    int64_t top_rows = 0;
+    for (const bool k8 : {false, true}) {
+        const int64_t br = 2 * (k8 ? decode_block_rows_k8(d->head_dim) : decode_block_rows(d->head_dim));
+        const Chunking top = plan_chunks(d->cache_len, (int64_t)d->batch * d->h_k, d->head_dim,
+                                         L.max_chunks, k8);
+        const int64_t r = top.rows > br ? top.rows : br;
+        if (r > top_rows) top_rows = r;
+    }
+    L.entry_rows = d->cache_len + top_rows;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes, 256); return o; };
     L.pm = take(rows * L.max_chunks * 4);
@@ -327,7 +335,7 @@ int enqueue_decode(const saga_dims* dims, const Layout& L, const void* q_dev,
         if (st != SAGA_OK) return st;
     }
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
-                                    D, L.max_chunks);
+                                    D, L.max_chunks, rm.k_scale != nullptr);
     SelectStreamArgs a =
         stream_args(dims, L, ch, q_dev, k_cache_dev, thresholds_dev, workspace_dev, rm);
     a.bitmap = sel_bitmap_debug_dev;
@@ -374,7 +382,7 @@ int do_refresh(const saga_dims* dims, const RowModel& rm, int32_t top_n, const v
     const int D = dims->head_dim;
     const int rows = dims->batch * dims->h_q;
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
-                                    D, L.max_chunks);
+                                    D, L.max_chunks, rm.k_scale != nullptr);
     int st;
     if ((int64_t)top_n >= dims->ctx_len) {
         // N >= ctx (of every sequence): every entry is kept, tau = -inf.  The
@@ -440,7 +448,7 @@ int do_refresh_decode(const saga_dims* dims, const RowModel& rm, int32_t top_n,
                               sel_counts_dev, nullptr, workspace_dev, s, rm);
     }
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
-                                    D, L.max_chunks);
+                                    D, L.max_chunks, rm.k_scale != nullptr);
     uint32_t* flags = reinterpret_cast<uint32_t*>(w + L.flags);
     st = enqueue_refresh(dims, top_n, q_dev, k_dev, thresholds_dev, nullptr, workspace_dev,
                          L, ch, s, flags, rm);

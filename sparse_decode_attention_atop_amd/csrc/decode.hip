@@ -59,7 +59,8 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
     uint2 (*q4)[kQueueCap] = queue[wave];
     if (a.group_flags && a.group_flags[blockIdx.y] == 0u) return;   // whole workgroup
 
-    const QFrag<D> qf = load_qfrag<D>(col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr);
+    const uint16_t* qrow = col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr;
+    const QFrag<D> qf = FP8 ? load_qfrag_k8<D>(qrow) : load_qfrag<D>(qrow);
     // Logit scale; an fp8 K cache adds its (b, key head) scale.
     const float sc = FP8 ? a.scale * a.k_scale[blockIdx.y] : a.scale;
     float tau[4], mx[4];
@@ -121,12 +122,12 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
         if (((lim - qn[0]) | (lim - qn[1]) | (lim - qn[2]) | (lim - qn[3])) < 0) flush_all();
     };
 
-    auto process = [&](const KTile<D, U>& kt, int64_t t0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
+    // One 16-row group starting at row g0 (a multiple of 16).
+    auto process_group = [&](const u32x4 (&kv)[D / 32], int64_t g0) {
+        {
             float s[4];
-            qk_group<D>(qf, kt.v[u], sc, s);
-            const int64_t row = t0 + 16 * u + col;
+            qk_group<D>(qf, kv, sc, s);
+            const int64_t row = g0 + col;
             const bool valid = row < r1;
             const uint32_t tag = (uint32_t)(row - r0) << 4;
             if constexpr (DEBUG) {
@@ -148,13 +149,24 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
                 mx[i] = fmaxf(mx[i], pred ? s[i] : -INFINITY);
                 if constexpr (DEBUG) {
                     const uint32_t mine = (uint32_t)(mask >> (16 * grp)) & 0xffffu;
-                    if (a.bitmap && col == 0 && mine) {
-                        const int64_t row0 = t0 + 16 * u;         // multiple of 16
-                        atomicOr(a.bitmap + (int64_t)(qh0 + 4 * grp + i) * a.bitmap_words + row0 / 32,
-                                 mine << (row0 & 31));
-                    }
+                    if (a.bitmap && col == 0 && mine)
+                        atomicOr(a.bitmap + (int64_t)(qh0 + 4 * grp + i) * a.bitmap_words + g0 / 32,
+                                 mine << (g0 & 31));
                 }
             }
+        }
+    };
+    auto process = [&](const KTile<D, U>& kt, int64_t t0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) process_group(kt.v[u], t0 + 16 * u);
+    };
+    // fp8 tile: each group is widened to bf16 just before its MFMA.
+    auto process8 = [&](const K8Tile<D, U>& kt, int64_t t0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            u32x4 kv[D / 32];
+            widen_k8group<D>(kt.g[u], kv);
+            process_group(kv, t0 + 16 * u);
         }
     };
 
@@ -201,27 +213,25 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
             } while (tp < r1);
         }
     } else if constexpr (FP8) {
-        // fp8 K (one byte per element): the same pipeline on half the bytes;
-        // each tile is widened to bf16 in registers before the QK routine.
+        // fp8 K (one byte per element): the same pipeline on half the bytes,
+        // 16-byte loads in the permuted order of the fp8 helpers, each group
+        // widened to bf16 just before its MFMA.
         const uint8_t* k8 = reinterpret_cast<const uint8_t*>(a.k);
         const __amdgpu_buffer_rsrc_t khead =
             make_rsrc(k8 + ((int64_t)(b * a.hk + g) * a.cache_len) * D, (uint32_t)(r1 * D));
         int64_t t0 = r0 + wave * 16 * U;
         if (t0 < r1) {
             constexpr uint32_t kStepBytes = (uint32_t)(kStep * D);
-            uint32_t koff = (uint32_t)(t0 + col) * (uint32_t)D + 8u * grp;
+            uint32_t koff = (uint32_t)(t0 + col) * (uint32_t)D + 16u * grp;
             K8Tile<D, U> ka, kb;
-            KTile<D, U> kt;
             load_k8tile_at<D, U>(ka, khead, koff);
             do {
                 maybe_flush();
                 load_k8tile_at<D, U>(kb, khead, koff + kStepBytes);
-                widen_k8tile<D, U>(ka, kt);
-                process(kt, t0);
+                process8(ka, t0);
                 maybe_flush();
                 load_k8tile_at<D, U>(ka, khead, koff + 2 * kStepBytes);
-                widen_k8tile<D, U>(kb, kt);
-                process(kt, t0 + kStep);
+                process8(kb, t0 + kStep);
                 t0 += 2 * kStep;
                 koff += 2 * kStepBytes;
             } while (t0 < r1);
@@ -594,8 +604,8 @@ hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t s)
     const bool dbg = a.bitmap != nullptr || a.logits_out != nullptr;
     const int kind = a.pg.block_table != nullptr ? 1 : (a.k_scale != nullptr ? 2 : 0);
 #define SAGA_LAUNCH_STREAM(DD, DBG, PG, F8)                                                      \
-    hipLaunchKernelGGL((select_stream_kernel<DD, decode_unroll(DD), DBG, PG, F8>), grid,         \
-                       dim3(kBlock), 0, s, a)
+    hipLaunchKernelGGL((select_stream_kernel<DD, F8 ? decode_unroll_k8(DD) : decode_unroll(DD),  \
+                                             DBG, PG, F8>), grid, dim3(kBlock), 0, s, a)
 #define SAGA_LAUNCH_STREAM_D(DD)                                                                 \
     if (kind == 1) { if (dbg) SAGA_LAUNCH_STREAM(DD, true, true, false); else SAGA_LAUNCH_STREAM(DD, false, true, false); } \
     else if (kind == 2) { if (dbg) SAGA_LAUNCH_STREAM(DD, true, false, true); else SAGA_LAUNCH_STREAM(DD, false, false, true); } \

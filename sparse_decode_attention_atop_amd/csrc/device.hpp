@@ -78,12 +78,6 @@ __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off
 constexpr int kWaitVmcnt0 = 0x0F70;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ u32x2 buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
-}
-__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
-
 // Eight fp8 e4m3 (OCP: bias 7, max 448, no infinities) values, in byte order,
 // widened to eight bf16 (exact: 3 mantissa bits fit bf16's 7).
 __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 x)
@@ -240,14 +234,47 @@ __device__ __forceinline__ void load_ktile_at(KTile<D, U>& t, __amdgpu_buffer_rs
             t.v[u][m] = buf_ld16(k_head, lane_off + (uint32_t)(16 * u * D * 2 + 64 * m));
 }
 
-// fp8 K: the same tile layout with one byte per element (8 bytes per lane and
-// MFMA slab), widened to the bf16 tile before the shared QK routine.
-template <int D, int U>
-struct K8Tile {
-    u32x2 v[U][D / 32];
+// fp8 K (one byte per element).  A lane loads 16 bytes per load: load j of
+// lane group g (= lane/16) holds elements 64j + 16g .. 64j + 16g + 15 of its
+// row, and MFMA slab m = 2j + h takes the h-th 8 of them.  The dot product is
+// the same sum in another order; q is loaded in that same order
+// (load_qfrag_k8), so every fp8 kernel computes identical logits.
+template <int D>
+__device__ __forceinline__ QFrag<D> load_qfrag_k8(const uint16_t* q_head)
+{
+    QFrag<D> f;
+    const int grp = lane_id() >> 4;
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+        if (q_head) f.v[m] = ld16(q_head + 64 * (m >> 1) + 16 * grp + 8 * (m & 1));
+        else f.v[m] = u32x4{0u, 0u, 0u, 0u};
+    }
+    return f;
+}
+
+// One 16-row group of fp8 K: D/64 loads of 16 bytes per lane.
+template <int D>
+struct K8Group {
+    u32x4 v[D / 64];
 };
 
-// Lane byte offset (row0 + lane%16) * D + 8*(lane/16); the loads differ by
+// The group widened (exactly) to the bf16 operand layout of qk_group.
+template <int D>
+__device__ __forceinline__ void widen_k8group(const K8Group<D>& x, u32x4 (&kv)[D / 32])
+{
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) {
+        kv[2 * j] = fp8x8_to_bf16x8(u32x2{x.v[j][0], x.v[j][1]});
+        kv[2 * j + 1] = fp8x8_to_bf16x8(u32x2{x.v[j][2], x.v[j][3]});
+    }
+}
+
+template <int D, int U>
+struct K8Tile {
+    K8Group<D> g[U];
+};
+
+// Lane byte offset (row0 + lane%16) * D + 16*(lane/16); the loads differ by
 // compile-time constants.
 template <int D, int U>
 __device__ __forceinline__ void load_k8tile_at(K8Tile<D, U>& t, __amdgpu_buffer_rsrc_t k_head,
@@ -256,17 +283,18 @@ __device__ __forceinline__ void load_k8tile_at(K8Tile<D, U>& t, __amdgpu_buffer_
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int m = 0; m < D / 32; ++m)
-            t.v[u][m] = buf_ld8(k_head, lane_off + (uint32_t)(16 * u * D + 32 * m));
+        for (int j = 0; j < D / 64; ++j)
+            t.g[u].v[j] = buf_ld16(k_head, lane_off + (uint32_t)(16 * u * D + 64 * j));
 }
 
-template <int D, int U>
-__device__ __forceinline__ void widen_k8tile(const K8Tile<D, U>& a, KTile<D, U>& t)
+// Plain global loads of one group at row pointer p8 (= row * D bytes + 16*(lane/16)).
+template <int D>
+__device__ __forceinline__ K8Group<D> load_k8group(const uint8_t* p8)
 {
+    K8Group<D> x;
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int m = 0; m < D / 32; ++m) t.v[u][m] = fp8x8_to_bf16x8(a.v[u][m]);
+    for (int j = 0; j < D / 64; ++j) x.v[j] = ld16(p8 + 64 * j);
+    return x;
 }
 
 // logits[u][i] = scale * sum_c q[slot 4*(lane/16)+i][c] * K[row0+16u+lane%16][c]

@@ -14,6 +14,9 @@ namespace saga {
 // head_dim; chunk lengths are multiples of these.
 constexpr int decode_unroll(int D) { return D == 64 ? SAGA_STREAM_U64 : SAGA_STREAM_U128; }
 constexpr int decode_block_rows(int D) { return kWavesPerBlock * 16 * decode_unroll(D); }
+// fp8 K: tiles of SAGA_STREAM_K8_UMUL times the rows of bf16 tiles.
+constexpr int decode_unroll_k8(int D) { return SAGA_STREAM_K8_UMUL * decode_unroll(D); }
+constexpr int decode_block_rows_k8(int D) { return kWavesPerBlock * 16 * decode_unroll_k8(D); }
 constexpr int full_unroll(int D) { return D == 64 ? 4 : 2; }
 
 // LDS bytes of one wave in the full-attention kernel:

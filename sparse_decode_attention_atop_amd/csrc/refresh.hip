@@ -126,7 +126,8 @@ __global__ __launch_bounds__(kBlock) void sample_logits_kernel(SampleArgs a)
     const int qh0 = b * a.hq + g * Gk;
     const int k0 = (blockIdx.x * kWavesPerBlock + wave) * 16 * U;   // first sample index
     if (k0 >= a.m) return;                                          // whole wave idle
-    const QFrag<D> qf = load_qfrag<D>(col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr);
+    const uint16_t* qrow = col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr;
+    const QFrag<D> qf = FP8 ? load_qfrag_k8<D>(qrow) : load_qfrag<D>(qrow);
     const uint16_t* khead = a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
     const int64_t ctx_b = PAGED ? seq_ctx(a.pg, b, 0) : (a.lq > 1 ? a.ctx : INT64_MAX);
     KTile<D, U> kt;
@@ -143,9 +144,8 @@ __global__ __launch_bounds__(kBlock) void sample_logits_kernel(SampleArgs a)
         } else if constexpr (FP8) {
             p = nullptr;
             const uint8_t* p8 = reinterpret_cast<const uint8_t*>(a.k) +
-                                ((int64_t)(b * a.hk + g) * a.cache_len + row) * D + 8 * grp;
-#pragma unroll
-            for (int mm = 0; mm < D / 32; ++mm) kt.v[u][mm] = fp8x8_to_bf16x8(ld8(p8 + 32 * mm));
+                                ((int64_t)(b * a.hk + g) * a.cache_len + row) * D + 16 * grp;
+            widen_k8group<D>(load_k8group<D>(p8), kt.v[u]);
         } else {
             p = khead + row * D + 8 * grp;
         }
@@ -235,7 +235,8 @@ __device__ uint32_t select_by_recompute(const FinalArgs& a, int row, int64_t ctx
     const int b = row / a.hq, i = row - b * a.hq;
     const int g = i / a.Gk, slot = i - g * a.Gk;
     const int qh0 = b * a.hq + g * a.Gk;
-    const QFrag<D> qf = load_qfrag<D>(col < a.Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr);
+    const uint16_t* qrow = col < a.Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr;
+    const QFrag<D> qf = FP8 ? load_qfrag_k8<D>(qrow) : load_qfrag<D>(qrow);
     const uint16_t* khead = a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
     const uint8_t* khead8 = reinterpret_cast<const uint8_t*>(a.k) + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
     const float sc = FP8 ? a.scale * a.k_scale[b * a.hk + g] : a.scale;
@@ -263,9 +264,7 @@ __device__ uint32_t select_by_recompute(const FinalArgs& a, int row, int64_t ctx
                 for (int u = 0; u < U; ++u) {
                     int64_t r = t0 + 16 * u + col;
                     r = r < ctx ? r : ctx - 1;
-#pragma unroll
-                    for (int m = 0; m < D / 32; ++m)
-                        kt.v[u][m] = fp8x8_to_bf16x8(ld8(khead8 + r * D + 8 * grp + 32 * m));
+                    widen_k8group<D>(load_k8group<D>(khead8 + r * D + 16 * grp), kt.v[u]);
                 }
             } else {
                 load_ktile<D, U>(kt, khead, t0, ctx);

@@ -8,6 +8,9 @@
 #ifndef SAGA_STREAM_U128
 #define SAGA_STREAM_U128 1           // same, head_dim 128
 #endif
+#ifndef SAGA_STREAM_K8_UMUL
+#define SAGA_STREAM_K8_UMUL 1        // fp8 K: 16-row groups per tile, times the bf16 count
+#endif
 #ifndef SAGA_K_NONTEMPORAL
 #define SAGA_K_NONTEMPORAL 0         // stream K with non-temporal loads
 #endif

@@ -1,11 +1,18 @@
 """An fp8 E4M3 K cache (the *_fp8k calls) on the GPU.
 
 * Power-of-two scales: scale * decode(code) is then exact in bf16, the kernels
-  widen the codes exactly and fold the scale into the logit scale, so every
-  result (logits, thresholds, counts, selection bitmap, outputs) must be
-  bit-identical to the bf16 calls run on that dequantized cache -- which the
-  bf16 parity tests tie to the oracle.  Also at the Llama-like 128K batch-16
-  shape the benchmark times, and on the recompute path of the refresh.
+  widen the codes exactly and fold the scale into the logit scale.  They sum
+  the head dimension in another order than the bf16 kernels (16-byte loads
+  that span two MFMA slabs); reordering the head dimension of q and K alike
+  leaves attention unchanged and makes the bf16 calls sum in that order.  So
+  logits, thresholds, counts and selection bitmaps must be bit-identical to
+  the bf16 calls run on the dequantized cache with q and K so reordered --
+  and the bf16 parity tests tie those to the oracle.  The fp8 stream's tiles
+  have twice the rows, so the selected entries reach the gather in another
+  order and its fp32 sums round differently: outputs must be equal or one
+  bf16 step apart.  Also at
+  the Llama-like 128K batch-16 shape the benchmark times, and on the
+  recompute path of the refresh.
 * General scales (amax / 448 per head): logits within the logit bar of the
   fp64 oracle on the E4M3 cache, thresholds bit-exact against a host sort of
   the GPU logits, selection equal to the oracle's away from the threshold,
@@ -33,6 +40,22 @@ def dequant_bf16(K8, ks):
     Kb = x.to(torch.bfloat16)
     assert torch.equal(Kb.to(torch.float32), x), "dequantized cache is not exact in bf16"
     return Kb.contiguous()
+
+
+def fp8_order(d):
+    """Head-dim positions as the fp8 kernels sum them: MFMA slab m, lane group
+    g, element e is head-dim index 64*(m//2) + 16*g + 8*(m%2) + e, where the
+    bf16 kernels use 32*m + 8*g + e."""
+    idx = [64 * (m // 2) + 16 * g + 8 * (m % 2) + e
+           for m in range(d // 32) for g in range(4) for e in range(8)]
+    assert sorted(idx) == list(range(d))
+    return torch.tensor(idx, device="cuda")
+
+
+def bf16_twin(q, K8, ks):
+    """q and the dequantized cache, head dimension in the fp8 kernels' order."""
+    idx = fp8_order(q.shape[-1])
+    return q[..., idx].contiguous(), dequant_bf16(K8, ks)[..., idx].contiguous()
 
 
 def run_fp8(q, K8, ks, V, ctx_steps, N, n, fused=False, debug=True):
@@ -78,6 +101,18 @@ def same_bits(a, b):
     return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
+def bf16_step_apart(a, b):
+    """Two bf16 outputs (as float32) equal or one bf16 rounding step apart
+    (plus 1e-6 for values near zero, where fp32 sums carry absolute error)."""
+    m = np.maximum(np.abs(a), np.abs(b))
+    ulp = np.exp2(np.floor(np.log2(np.where(m > 0, m, 1.0))) - 7)
+    return a.shape == b.shape and bool((np.abs(a - b) <= np.where(m > 0, ulp, 0) + 1e-6).all())
+
+
+def match(key, a, b):
+    return bf16_step_apart(a, b) if key == "out" else same_bits(a, b)
+
+
 SHAPES = {
     # name: (B, hq, hk, hv, d, L, T, N, n)
     "qwen_like_small": (2, 12, 1, 2, 128, 3000, 5, 100, 3),
@@ -100,20 +135,20 @@ def test_pow2_scales_bit_identical_to_bf16_calls(name):
     q, K8, ks, V, ctx, N, n = inputs(name, 200 + len(name), pow2=True)
     print(f"[fp8k pow2 {name}] K8{tuple(K8.shape)} ctx={ctx} N={N} n={n}", flush=True)
     got = run_fp8(q, K8, ks, V, ctx, N, n)
-    ref = run_atopn(q, dequant_bf16(K8, ks), V, ctx, N, n)
+    ref = run_atopn(*bf16_twin(q, K8, ks), V, ctx, N, n)
     for k in ("tau", "logits", "counts", "bitmap", "out"):
         for t in range(len(ctx)):
-            assert same_bits(got[k][t], ref[k][t]), f"{k} differs at step {t}"
+            assert match(k, got[k][t], ref[k][t]), f"{k} differs at step {t}"
 
 
 @pytest.mark.parametrize("name", ["qwen_like_small", "llama_like_small", "short_ctx"])
 def test_pow2_scales_fused_refresh_step_bit_identical(name):
     q, K8, ks, V, ctx, N, n = inputs(name, 210 + len(name), pow2=True)
     got = run_fp8(q, K8, ks, V, ctx, N, n, fused=True, debug=False)
-    ref = run_fused(q, dequant_bf16(K8, ks), V, ctx, N, n)
+    ref = run_fused(*bf16_twin(q, K8, ks), V, ctx, N, n)
     for k in ("tau", "counts", "out"):
         for t in range(len(ctx)):
-            assert same_bits(got[k][t], ref[k][t]), f"{k} differs at step {t}"
+            assert match(k, got[k][t], ref[k][t]), f"{k} differs at step {t}"
 
 
 def test_pow2_scales_recompute_path_bit_identical():
@@ -127,13 +162,13 @@ def test_pow2_scales_recompute_path_bit_identical():
     K[:, :, torch.from_numpy(rows).cuda(), :] = 1.0
     q.fill_(0.1)
     K8, ks = wl.quantize_k_e4m3(K, pow2_scales=True)
-    Kd = dequant_bf16(K8, ks)
+    qd, Kd = bf16_twin(q, K8, ks)
     for fused in (False, True):
         got = run_fp8(q, K8, ks, V, [ctx], N, 1, fused=fused, debug=not fused)
-        ref = (run_fused if fused else run_atopn)(q, Kd, V, [ctx], N, 1)
+        ref = (run_fused if fused else run_atopn)(qd, Kd, V, [ctx], N, 1)
         assert (got["counts"][0] >= N).all()
         for k in ("tau", "counts", "out"):
-            assert same_bits(got[k][0], ref[k][0]), (fused, k)
+            assert match(k, got[k][0], ref[k][0]), (fused, k)
 
 
 def test_pow2_scales_at_the_benchmark_shape():
@@ -143,15 +178,15 @@ def test_pow2_scales_at_the_benchmark_shape():
     x = wl.make_layer(w, 0, device="cuda", steps=2)
     q, K, V = x["q"], x["K"], x["V"]
     K8, ks = wl.quantize_k_e4m3(K, pow2_scales=True)
-    Kd = dequant_bf16(K8, ks)
+    qd, Kd = bf16_twin(q, K8, ks)
     del K, x
     ctx = [w.ctx(0), w.ctx(1)]
     print(f"[fp8k full] {w.name} ctx={ctx}", flush=True)
     got = run_fp8(q, K8, ks, V, ctx, w.top_n, 2, fused=True, debug=False)
-    ref = run_fused(q, Kd, V, ctx, w.top_n, 2)
+    ref = run_fused(qd, Kd, V, ctx, w.top_n, 2)
     for k in ("tau", "counts", "out"):
         for t in range(2):
-            assert same_bits(got[k][t], ref[k][t]), f"{k} differs at step {t}"
+            assert match(k, got[k][t], ref[k][t]), f"{k} differs at step {t}"
 
 
 _cache = {}
