@@ -21,7 +21,7 @@
 #define SAGA_TARGET_BLOCKS128 512    // same, head_dim 128
 #endif
 #ifndef SAGA_GATHER_NB
-#define SAGA_GATHER_NB 8             // value rows in flight per lane in the gather
+#define SAGA_GATHER_NB 4             // value rows in flight per lane in the gather
 #endif
 #ifndef SAGA_GATHER_WAVES
 #define SAGA_GATHER_WAVES 0          // >0: ask for that many waves per SIMD (gather)
