@@ -510,6 +510,59 @@ def cpu_baseline(torch, wl, w, layers, n_layers=2):
             "sample_seconds": round(total, 2)}
 
 
+def atopn_recall(wl, w, layer_x, b=0):
+    """Informational: how much of the exact top-N set the Atop-N selection
+    keeps at each step (stale thresholds between refreshes), from the oracle
+    on layer 0, batch row b, every query head, the whole decode run."""
+    import numpy as np
+    import oracle
+    q = wl.bits(layer_x["q"][:, b:b + 1])
+    K, V = wl.bits(layer_x["K"][b:b + 1]), wl.bits(layer_x["V"][b:b + 1])
+    ctx = [w.L + s for s in range(w.steps)]
+    r = oracle.atopn_run(q, K, V, ctx, w.top_n, w.refresh_n, want_sel=True, want_logits=True)
+    rec = np.empty((w.steps, w.h_q))
+    for t, n in enumerate(ctx):
+        for i in range(w.h_q):
+            s = r["logits"][t, 0, i, :n]
+            top = np.argpartition(-s, w.top_n - 1)[:w.top_n]       # exact top-N (no ties)
+            rec[t, i] = r["sel"][t, 0, i, top].mean()
+    refresh = [t for t in range(w.steps) if t % w.refresh_n == 0]
+    stale = [t for t in range(w.steps) if t % w.refresh_n]
+    return {"mean": round(float(rec.mean()), 5), "min": round(float(rec.min()), 5),
+            "at_refresh_steps": round(float(rec[refresh].mean()), 5),
+            "between_refreshes": round(float(rec[stale].mean()), 5) if stale else None,
+            "mean_selected_per_head": round(float(r["count"].mean()), 1),
+            "sample": f"oracle, layer 0 of {w.name}, batch row {b}, all {w.h_q} query heads, "
+                      f"{w.steps} steps"}
+
+
+def torch_rates(torch):
+    """Streaming rates of torch's own device kernels (copy_, sum) over 2 GiB,
+    measured in the same run: a reference point next to the 8 TB/s spec peak,
+    not a ceiling (torch's reduction reads slower than the library's K stream)."""
+    n = 1 << 29                                         # fp32 elements: 2 GiB
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+
+    def rate(fn, bytes_per_call, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return bytes_per_call * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    copy = rate(lambda: b.copy_(a), 2 * 4 * n)
+    read = rate(lambda: a.sum(), 4 * n)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(copy, 1), "sum_gbs": round(read, 1),
+            "how": "torch copy_ (bytes read + written) and sum (bytes read) over 2 GiB fp32"}
+
+
 MALL_BYTES = 256 << 20
 
 
@@ -664,6 +717,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(torch, wl, w, res["layers"])
+        log("Atop-N recall against exact top-N (oracle, informational)")
+        extra["atopn_recall"] = atopn_recall(wl, w, res["layers"][0])
     if not args.no_gqa and w.name in GQA_TWIN:
         del res["graphs"]
         for x in res["layers"]:
@@ -677,6 +732,7 @@ def main():
             "ms_per_step": round(1e3 * gq["sec"] / args.steps, 4),
             "hbm_gbs_algorithmic": round(gq["bytes_per_step"] / (gq["sec"] / args.steps) / 1e9, 1)}
         extra["speedup_vs_gqa_full"] = round(steps_per_s / gqa_sps, 3)
+    extra["torch_reference_rates"] = torch_rates(torch)
 
     line = {
         "metric": "decode-attn steps/s (B x layers) + HBM GB/s % peak, SAGA Atop-N @128K",
