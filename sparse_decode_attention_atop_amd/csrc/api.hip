@@ -16,9 +16,10 @@ using namespace saga;
 
 namespace {
 
-// Workgroups per K-stream launch: the stream kernel keeps three workgroups on
-// a CU, and measured on MI355X a launch of about one such round for head_dim
-// 128, or a bit over one for head_dim 64, streams fastest.
+// Workgroups per K-stream launch: four stream workgroups fit a CU at
+// head_dim 64 (100 VGPRs) and 32 KB of LDS each; measured on MI355X, about one
+// such round (1024) at head_dim 64 and half of it (512) at head_dim 128
+// stream fastest.
 constexpr int64_t kFullTargetBlocks = 2048;   // dense kernel: workgroups per launch
 
 int64_t target_blocks(int head_dim)
