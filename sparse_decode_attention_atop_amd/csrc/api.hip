@@ -16,14 +16,16 @@ using namespace saga;
 
 namespace {
 
-// Workgroups per K-stream launch: four stream workgroups fit a CU at
-// head_dim 64 (100 VGPRs) and 32 KB of LDS each; measured on MI355X, about one
-// such round (1024) at head_dim 64 and half of it (512) at head_dim 128
-// stream fastest.
+// Workgroups per K-stream launch.  Each workgroup streams one contiguous
+// chunk; measured on MI355X, fewer concurrent streams per CU read faster as
+// long as every CU gets the same count: three per CU (768) at head_dim 64,
+// two (512) at head_dim 128, and four (1024) for the half-size rows of an fp8
+// K cache at head_dim 64.
 constexpr int64_t kFullTargetBlocks = 2048;   // dense kernel: workgroups per launch
 
-int64_t target_blocks(int head_dim)
+int64_t target_blocks(int head_dim, bool k8 = false)
 {
+    if (k8) return head_dim == 128 ? SAGA_TARGET_BLOCKS128_K8 : SAGA_TARGET_BLOCKS64_K8;
     return head_dim == 128 ? SAGA_TARGET_BLOCKS128 : SAGA_TARGET_BLOCKS64;
 }
 constexpr int64_t kMaxCacheLen = int64_t(1) << 27;
@@ -80,7 +82,7 @@ Chunking split_rows(int64_t ctx, int64_t pairs, int64_t block_rows, int64_t targ
 Chunking plan_chunks(int64_t ctx, int64_t pairs, int head_dim, int max_chunks, bool k8)
 {
     const int64_t block = k8 ? decode_block_rows_k8(head_dim) : decode_block_rows(head_dim);
-    return split_rows(ctx, pairs, 2 * block, target_blocks(head_dim), max_chunks);
+    return split_rows(ctx, pairs, 2 * block, target_blocks(head_dim, k8), max_chunks);
 }
 
 // Workspace layout (byte offsets), identical for every ctx_len <= cache_len.
@@ -97,7 +99,7 @@ Layout make_layout(const saga_dims* d)
     const int64_t target = target_blocks(d->head_dim) > kFullTargetBlocks
                                ? target_blocks(d->head_dim) : kFullTargetBlocks;
     const int64_t want = target / ((int64_t)d->batch * d->h_k);
-    const int64_t by_len = (d->cache_len + 127) / 128;   // smallest block tile is 128 rows
+    const int64_t by_len = (d->cache_len + 127) / 128;   // smallest tile pair is 128 rows
     int64_t mc = want < by_len ? want : by_len;
     if (mc > kMaxListsPerRow / kWavesPerBlock) mc = kMaxListsPerRow / kWavesPerBlock;   // 512
     L.max_chunks = (int)(mc < 1 ? 1 : mc);

@@ -180,13 +180,22 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
     constexpr int64_t kStep = kWavesPerBlock * 16 * U;
     if constexpr (PAGED) {
         // Paged K: a tile pair (2 * kStep rows, pair starts aligned to it) lies
-        // in one page; each pair gets the buffer resource of its page, which
-        // ends at r1 or at the page end, and a table entry outside the pool
-        // gives an empty resource (zeros).
+        // in one page (page_rows is a multiple of the pair).  The page and the
+        // pair's byte offset in it advance incrementally (one division per
+        // workgroup), each page gets a buffer resource that ends at r1 or at
+        // the page end, a table entry outside the pool gives an empty resource
+        // (zeros), and the next page's table entry is read one page ahead.
+        static_assert(kPageQuantum % (2 * kStep) == 0, "a tile pair must not straddle pages");
         const int64_t P = a.pg.page_rows;
-        auto page_rsrc = [&](int64_t row) {
-            const int64_t base = page_base<D>(a.pg, b, g, a.hk, row);
-            int64_t n = r1 - (row - row % P);
+        const uint32_t page_bytes = (uint32_t)(P * D * 2);   // < 2^31 (checked on the host)
+        auto lookup = [&](int64_t p) -> int64_t {             // element offset, or -1
+            if (p >= a.pg.max_pages) return -1;
+            const int32_t page = a.pg.block_table[(int64_t)b * a.pg.max_pages + p];
+            if (page < 0 || page >= a.pg.num_pages) return -1;
+            return (((int64_t)page * a.hk + g) * P) * D;
+        };
+        auto page_rsrc = [&](int64_t p, int64_t base) {
+            int64_t n = r1 - p * P;
             n = n > P ? P : n;
             if (n < 0 || base < 0) n = 0;
             return make_rsrc(a.k + (base < 0 ? 0 : base), (uint32_t)(n * D * 2));
@@ -195,21 +204,27 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
         const uint32_t lane_off = (uint32_t)(wave * 16 * U + col) * (uint32_t)(D * 2) + 16u * grp;
         int64_t tp = r0;                                // first row of the current pair
         if (tp < r1) {
-            __amdgpu_buffer_rsrc_t ra = page_rsrc(tp);
+            int64_t pi = tp / P;                        // page of the current pair
+            uint32_t in = (uint32_t)(tp - pi * P) * (uint32_t)(D * 2);   // its byte offset there
+            __amdgpu_buffer_rsrc_t ra = page_rsrc(pi, lookup(pi));
+            int64_t base_n = lookup(pi + 1);
             KTile<D, U> ka, kb;
-            load_ktile_at<D, U>(ka, ra, lane_off + (uint32_t)(tp % P) * (uint32_t)(D * 2));
+            load_ktile_at<D, U>(ka, ra, lane_off + in);
             do {
                 maybe_flush();
-                load_ktile_at<D, U>(kb, ra,
-                                    lane_off + (uint32_t)(tp % P) * (uint32_t)(D * 2) + kStepBytes);
+                load_ktile_at<D, U>(kb, ra, lane_off + in + kStepBytes);
                 process(ka, tp + wave * 16 * U);
-                const __amdgpu_buffer_rsrc_t rn = page_rsrc(tp + 2 * kStep);
+                in += 2 * kStepBytes;
+                if (in == page_bytes) {                 // the next pair opens a new page
+                    in = 0;
+                    ++pi;
+                    ra = page_rsrc(pi, base_n);
+                    base_n = lookup(pi + 1);
+                }
                 maybe_flush();
-                load_ktile_at<D, U>(ka, rn,
-                                    lane_off + (uint32_t)((tp + 2 * kStep) % P) * (uint32_t)(D * 2));
+                load_ktile_at<D, U>(ka, ra, lane_off + in);
                 process(kb, tp + kStep + wave * 16 * U);
                 tp += 2 * kStep;
-                ra = rn;
             } while (tp < r1);
         }
     } else if constexpr (FP8) {

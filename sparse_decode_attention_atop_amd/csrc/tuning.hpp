@@ -3,7 +3,7 @@
 
 // Compile-time tuning constants (defaults are the measured best on MI355X).
 #ifndef SAGA_STREAM_U64
-#define SAGA_STREAM_U64 2            // 16-row K groups per wave tile, head_dim 64
+#define SAGA_STREAM_U64 1            // 16-row K groups per wave tile, head_dim 64
 #endif
 #ifndef SAGA_STREAM_U128
 #define SAGA_STREAM_U128 1           // same, head_dim 128
@@ -15,10 +15,16 @@
 #define SAGA_K_NONTEMPORAL 0         // stream K with non-temporal loads
 #endif
 #ifndef SAGA_TARGET_BLOCKS64
-#define SAGA_TARGET_BLOCKS64 1024    // workgroups per K-stream launch, head_dim 64
+#define SAGA_TARGET_BLOCKS64 768     // workgroups per K-stream launch, head_dim 64
 #endif
 #ifndef SAGA_TARGET_BLOCKS128
 #define SAGA_TARGET_BLOCKS128 512    // same, head_dim 128
+#endif
+#ifndef SAGA_TARGET_BLOCKS64_K8
+#define SAGA_TARGET_BLOCKS64_K8 1024 // same with an fp8 K cache, head_dim 64
+#endif
+#ifndef SAGA_TARGET_BLOCKS128_K8
+#define SAGA_TARGET_BLOCKS128_K8 512 // same with an fp8 K cache, head_dim 128
 #endif
 #ifndef SAGA_GATHER_NB
 #define SAGA_GATHER_NB 4             // value rows in flight per lane in the gather
