@@ -21,7 +21,7 @@ namespace {
 // long as every CU gets the same count: three per CU (768) at head_dim 64,
 // two (512) at head_dim 128, and four (1024) for the half-size rows of an fp8
 // K cache at head_dim 64.
-constexpr int64_t kFullTargetBlocks = 2048;   // dense kernel: workgroups per launch
+constexpr int64_t kFullTargetBlocks = SAGA_FULL_BLOCKS;   // dense kernel: workgroups per launch
 
 int64_t target_blocks(int head_dim, bool k8 = false)
 {

@@ -26,6 +26,9 @@
 #ifndef SAGA_TARGET_BLOCKS128_K8
 #define SAGA_TARGET_BLOCKS128_K8 512 // same with an fp8 K cache, head_dim 128
 #endif
+#ifndef SAGA_FULL_BLOCKS
+#define SAGA_FULL_BLOCKS 512         // workgroups per dense (full-attention) launch
+#endif
 #ifndef SAGA_GATHER_NB
 #define SAGA_GATHER_NB 4             // value rows in flight per lane in the gather
 #endif
