@@ -100,6 +100,9 @@ def parse():
                    help="time the schedule with this many query tokens per head and step")
     p.add_argument("--fp8k", action="store_true",
                    help="store the K cache as fp8 E4M3 (the *_fp8k calls)")
+    p.add_argument("--sigma", action="store_true",
+                   help="Sigma-style heads: twice the key heads at half the key head dimension "
+                        "(same K bytes), value heads unchanged; main schedule only")
     p.add_argument("--sweep", action="store_true",
                    help="Llama-like and Qwen-like shapes over L x N x B: SAGA Atop-N vs the "
                         "full-attention GQA path, one JSON line per point")
@@ -141,13 +144,14 @@ def decode_algorithmic_bytes(w, ctx, sel_total, k_bytes=2):
     """Bytes the fused decode launch must move: K once per (b, key head)
     (k_bytes per element: 2 for bf16, 1 for fp8), the selected V rows, q, out
     and the thresholds."""
-    d = w.head_dim
-    return (w.batch * w.h_k * ctx * d * k_bytes + sel_total * d * 2
-            + 2 * w.batch * w.h_q * d * 2 + w.batch * w.h_q * 4)
+    d, dv = w.head_dim, w.head_dim_v or w.head_dim
+    return (w.batch * w.h_k * ctx * d * k_bytes + sel_total * dv * 2
+            + w.batch * w.h_q * (d + dv) * 2 + w.batch * w.h_q * 4)
 
 
 def full_algorithmic_bytes(w, ctx):
-    return w.batch * (w.h_k + w.h_v) * ctx * w.head_dim * 2 + 2 * w.batch * w.h_q * w.head_dim * 2
+    d, dv = w.head_dim, w.head_dim_v or w.head_dim
+    return w.batch * ctx * (w.h_k * d + w.h_v * dv) * 2 + w.batch * w.h_q * (d + dv) * 2
 
 
 def time_graphs(torch, graphs, steps, warmup):
@@ -175,15 +179,17 @@ def run_saga(torch, saga, wl, w, args):
         log(f"  layer {layer} ready")
         layers.append(dict(K=K, V=V, q=q,
                            tau=torch.empty(w.batch, w.h_q, dtype=torch.float32, device="cuda"),
-                           out=torch.empty(w.batch, w.h_q, w.head_dim, dtype=torch.bfloat16,
-                                           device="cuda"),
+                           out=torch.empty(w.batch, w.h_q, w.head_dim_v or w.head_dim,
+                                           dtype=torch.bfloat16, device="cuda"),
                            cnt=torch.empty(w.batch, w.h_q, dtype=torch.int32, device="cuda")))
     torch.cuda.synchronize()
-    d0 = saga.dims(w.batch, w.h_q, w.h_k, w.h_v, w.head_dim, L, w.rows, w.scale)
+    d0 = saga.dims(w.batch, w.h_q, w.h_k, w.h_v, w.head_dim, L, w.rows, w.scale,
+                   head_dim_v=w.head_dim_v)
     ws = saga.alloc_workspace(d0, w.top_n)
 
     def step(t, events=None):
-        dm = saga.dims(w.batch, w.h_q, w.h_k, w.h_v, w.head_dim, L + t, w.rows, w.scale)
+        dm = saga.dims(w.batch, w.h_q, w.h_k, w.h_v, w.head_dim, L + t, w.rows, w.scale,
+                       head_dim_v=w.head_dim_v)
         for li, x in enumerate(layers):
             if events is not None:
                 events[li][0].record()
@@ -453,13 +459,15 @@ def run_full(torch, saga, wl, g, args):
     for layer in range(g.layers):
         K, V, q = layer_inputs(torch, wl, g, layer)
         log(f"  layer {layer} ready")
-        layers.append(dict(K=K, V=V, q=q, out=torch.empty(g.batch, g.h_q, g.head_dim,
+        layers.append(dict(K=K, V=V, q=q, out=torch.empty(g.batch, g.h_q, g.head_dim_v or g.head_dim,
                                                           dtype=torch.bfloat16, device="cuda")))
-    d0 = saga.dims(g.batch, g.h_q, g.h_k, g.h_v, g.head_dim, L, g.rows, g.scale)
+    d0 = saga.dims(g.batch, g.h_q, g.h_k, g.h_v, g.head_dim, L, g.rows, g.scale,
+                   head_dim_v=g.head_dim_v)
     ws = saga.alloc_workspace(d0, 1)
 
     def step(t):
-        dm = saga.dims(g.batch, g.h_q, g.h_k, g.h_v, g.head_dim, L + t, g.rows, g.scale)
+        dm = saga.dims(g.batch, g.h_q, g.h_k, g.h_v, g.head_dim, L + t, g.rows, g.scale,
+                       head_dim_v=g.head_dim_v)
         for x in layers:
             saga.saga_full_attention(dm, x["q"][t], x["K"], x["V"], x["out"], ws)
 
@@ -693,6 +701,10 @@ def main():
               flush=True)
         return
     w = wl.WORKLOADS[args.workload]
+    if args.sigma:
+        # The pages' Sigma-style alternative: (2 h_k, d_k / 2) instead of (h_k, d_k), d_v kept.
+        w = w.with_(name=w.name + "_sigma", h_k=2 * w.h_k, head_dim=w.head_dim // 2,
+                    head_dim_v=w.head_dim)
     res = run_saga(torch, saga, wl, w, args)
     if res is None:
         return
@@ -748,7 +760,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; shapes of the pages' Llama/Qwen decode setups, no weights)",
         "config": {"workload": w.name, "batch": w.batch, "h_q": w.h_q, "h_k": w.h_k,
-                   "h_v": w.h_v, "head_dim": w.head_dim, "L": w.L, "top_n": w.top_n,
+                   "h_v": w.h_v, "head_dim": w.head_dim, "head_dim_v": w.head_dim_v or w.head_dim,
+                   "L": w.L, "top_n": w.top_n,
                    "refresh_n": w.refresh_n, "decode_steps": w.steps, "layers": w.layers},
         "tokens_per_s": round(steps_per_s * w.batch, 2),
         "hbm_gbs_step": round(step_bytes / (sec / args.steps) / 1e9, 1),

@@ -31,11 +31,12 @@
  * the enqueued work has finished.  The library holds no state between calls;
  * concurrent calls need distinct workspaces.
  *
- * Layouts (row-major, contiguous):
- *   q        bf16 [batch][h_q][head_dim]
- *   k_cache  bf16 [batch][h_k][cache_len][head_dim]
- *   v_cache  bf16 [batch][h_v][cache_len][head_dim]
- *   out      bf16 [batch][h_q][head_dim]      (round to nearest even)
+ * Layouts (row-major, contiguous; d_k = head_dim, d_v = head_dim_v or, when
+ * that is 0, head_dim):
+ *   q        bf16 [batch][h_q][d_k]
+ *   k_cache  bf16 [batch][h_k][cache_len][d_k]
+ *   v_cache  bf16 [batch][h_v][cache_len][d_v]
+ *   out      bf16 [batch][h_q][d_v]           (round to nearest even)
  *   thresholds fp32 [batch][h_q]
  * A step attends rows 0 .. ctx_len-1 of each cache head.  Logits are
  * s_j = scale * <q, k_j> computed with fp32 products and sums; softmax and the
@@ -67,19 +68,24 @@ typedef enum saga_status {
 /* Problem shape of one layer call.
  *   batch      >= 1
  *   h_q, h_k, h_v >= 1; h_k and h_v each divide h_q; h_q/h_k <= 16
- *   head_dim   64 or 128
+ *   head_dim   d_k, the q / key head dimension: 32, 64 or 128
+ *   head_dim_v d_v, the value / output head dimension: 32, 64 or 128, or 0
+ *              for d_v = d_k.  The key and value dimensions are independent
+ *              (the pages compare a Sigma-style (h_k, d_k) = (2, 32) with
+ *              SAGA's (1, 64) at h_v = 8, d_v = 64: ai.info summary, Main
+ *              Findings, "head count beats head dimension")
  *   ctx_len    rows attended this step, 1 <= ctx_len <= cache_len
  *   cache_len  rows allocated per cache head (the head stride), < 2^27; one
- *              head must stay under 2 GiB (cache_len * head_dim * 2 < 2^31,
- *              8M rows at head_dim 128), else SAGA_ERR_UNSUPPORTED
- *   scale      multiplies q.k (use 1/sqrt(d) unless it is folded into q)   */
+ *              head must stay under 2 GiB (cache_len * max(d_k, d_v) * 2 <
+ *              2^31, 8M rows at 128), else SAGA_ERR_UNSUPPORTED
+ *   scale      multiplies q.k (use 1/sqrt(d_k) unless it is folded into q) */
 typedef struct saga_dims {
     int32_t batch;
     int32_t h_q;
     int32_t h_k;
     int32_t h_v;
     int32_t head_dim;
-    int32_t reserved;   /* must be 0 */
+    int32_t head_dim_v; /* 0: same as head_dim */
     int64_t ctx_len;
     int64_t cache_len;
     float scale;
@@ -128,7 +134,7 @@ int atopn_refresh_thresholds(const saga_dims* dims, int32_t top_n, const void* q
  * (b, key head) for all of that head's query heads.
  *
  *   thresholds_dev       input fp32 [batch][h_q] (from the last refresh)
- *   out_dev              output bf16 [batch][h_q][head_dim]
+ *   out_dev              output bf16 [batch][h_q][d_v]
  *   sel_counts_dev       optional output int32 [batch][h_q] = |S| (NULL: skip)
  *   sel_bitmap_debug_dev optional output uint32 [batch][h_q][ceil(cache_len/32)]:
  *                        bit j%32 of word j/32 set iff j in S; the library
@@ -148,7 +154,7 @@ int saga_decode_step(const saga_dims* dims, const void* q_dev, const void* k_cac
  * t mod n == 0.
  *
  *   thresholds_dev   output fp32 [batch][h_q] (kept for the following steps)
- *   out_dev          output bf16 [batch][h_q][head_dim]
+ *   out_dev          output bf16 [batch][h_q][d_v]
  *   sel_counts_dev   optional output int32 [batch][h_q] (NULL: skip)
  * Errors: as atopn_refresh_thresholds() and saga_decode_step().
  */
@@ -162,8 +168,8 @@ int atopn_refresh_decode_step(const saga_dims* dims, int32_t top_n, const void* 
  * different lengths sharing page pools; the step before the method proper,
  * needed to serve batched decode as the pages' batch-16 setting does).
  *
- *   k_pages bf16 [num_pages][h_k][page_rows][head_dim]
- *   v_pages bf16 [num_pages][h_v][page_rows][head_dim]
+ *   k_pages bf16 [num_pages][h_k][page_rows][d_k]
+ *   v_pages bf16 [num_pages][h_v][page_rows][d_v]
  * Row r (0-based, logical) of sequence b is row r % page_rows of page
  * block_table[b][r / page_rows] in both pools.  Sequence b attends rows
  * 0 .. ctx_lens[b]-1 (values outside [0, max_pages * page_rows] are clamped);
@@ -210,9 +216,9 @@ int atopn_refresh_decode_step_paged(const saga_dims* dims, const saga_paged* pag
  * threshold, refreshed on the same schedule.  Per token the results equal the
  * one-token calls with that token's q at ctx_len - (l_q - 1 - j).
  *
- *   q_dev          bf16 [batch][h_q][l_q][head_dim]
+ *   q_dev          bf16 [batch][h_q][l_q][d_k]
  *   thresholds_dev fp32 [batch][h_q][l_q]
- *   out_dev        bf16 [batch][h_q][l_q][head_dim]
+ *   out_dev        bf16 [batch][h_q][l_q][d_v]
  *   sel_counts_dev optional int32 [batch][h_q][l_q]
  *   workspace      saga_workspace_bytes() of dims with h_q replaced by h_q * l_q
  * Requires 1 <= l_q <= ctx_len and (h_q / h_k) * l_q <= 16 (UNSUPPORTED
@@ -236,7 +242,7 @@ int atopn_refresh_decode_step_lq(const saga_dims* dims, int32_t l_q, int32_t top
  * ai.info summary, Why This Matters).  The dominant K stream then reads one
  * byte per element instead of two; V stays bf16.
  *
- *   k8_cache_dev  [batch][h_k][cache_len][head_dim] bytes, each an fp8 E4M3
+ *   k8_cache_dev  [batch][h_k][cache_len][d_k] bytes, each an fp8 E4M3
  *                 value in the OCP 8-bit floating point format (bias 7, no
  *                 infinities, 0x7F / 0xFF are NaN, max 448)
  *   k_scale_dev   fp32 [batch][h_k] device memory: key row r of (b, g) is
@@ -244,9 +250,10 @@ int atopn_refresh_decode_step_lq(const saga_dims* dims, int32_t l_q, int32_t top
  * The logits are scale * k_scale[b][kappa(i)] * (q . decode(k8 row)), i.e. the
  * contiguous calls run on the dequantized cache; everything else (thresholds,
  * selection, outputs, workspace size, the debug outputs of the refresh and
- * decode calls) is as the contiguous calls.  A NaN code yields NaN logits,
- * which never pass a threshold.  Errors: as the contiguous calls, plus
- * INVALID_ARGUMENT for a null or misaligned k_scale_dev.
+ * decode calls) is as the contiguous calls.  The two E4M3 NaN codes are not
+ * valid cache contents (results with them are unspecified).  Errors: as the
+ * contiguous calls, plus INVALID_ARGUMENT for a null or misaligned
+ * k_scale_dev and UNSUPPORTED for d_k = 32.
  */
 int atopn_refresh_thresholds_fp8k(const saga_dims* dims, int32_t top_n, const void* q_dev,
                                   const void* k8_cache_dev, const float* k_scale_dev,

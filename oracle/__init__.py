@@ -53,19 +53,20 @@ def _load():
         lib.oracle_logits.argtypes = [i32, i32, i32, i32, i32, i64, i64, dbl, vp, vp, vp, i32]
         lib.oracle_nth_largest.argtypes = [vp, i64, i64]
         lib.oracle_nth_largest.restype = dbl
-        lib.oracle_atopn_run.argtypes = [i32, i32, i32, i32, i32, i64, i32, vp, dbl, i64, i64,
-                                         vp, vp, vp, vp, vp, vp, vp, vp, i32]
-        lib.oracle_masked.argtypes = [i32, i32, i32, i32, i32, i64, i64, dbl, vp, vp, vp, vp,
-                                      vp, vp, i32]
-        lib.oracle_exact_topn.argtypes = [i32, i32, i32, i32, i32, i64, i64, dbl, i64, vp, vp,
-                                          vp, vp, i32]
-        lib.oracle_full.argtypes = [i32, i32, i32, i32, i32, i64, i64, dbl, vp, vp, vp, vp, i32]
+        lib.oracle_atopn_run.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, vp, dbl, i64,
+                                         i64, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        lib.oracle_masked.argtypes = [i32, i32, i32, i32, i32, i32, i64, i64, dbl, vp, vp, vp,
+                                      vp, vp, vp, i32]
+        lib.oracle_exact_topn.argtypes = [i32, i32, i32, i32, i32, i32, i64, i64, dbl, i64, vp,
+                                          vp, vp, vp, i32]
+        lib.oracle_full.argtypes = [i32, i32, i32, i32, i32, i32, i64, i64, dbl, vp, vp, vp, vp,
+                                    i32]
         lib.oracle_logits_e4m3k.argtypes = [i32, i32, i32, i32, i32, i64, i64, dbl, vp, vp, vp,
                                             vp, i32]
-        lib.oracle_atopn_run_e4m3k.argtypes = [i32, i32, i32, i32, i32, i64, i32, vp, dbl, i64,
-                                               i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
-        lib.oracle_masked_e4m3k.argtypes = [i32, i32, i32, i32, i32, i64, i64, dbl, vp, vp, vp,
-                                            vp, vp, vp, vp, i32]
+        lib.oracle_atopn_run_e4m3k.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, vp, dbl,
+                                               i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        lib.oracle_masked_e4m3k.argtypes = [i32, i32, i32, i32, i32, i32, i64, i64, dbl, vp, vp,
+                                            vp, vp, vp, vp, vp, i32]
         lib.oracle_e4m3_decode.argtypes = [vp, i64, vp]
         lib.oracle_e4m3_decode.restype = None
         lib.oracle_max_threads.restype = i32
@@ -103,11 +104,13 @@ def _ptr(a: np.ndarray):
 
 
 def _cache_shape(K, V):
+    """(B, hk, hv, cache_len, d, dv): K and V share batch and rows; the key and
+    value head dimensions d and dv are independent."""
     B, hk, cache_len, d = K.shape
-    B2, hv, cache_len2, d2 = V.shape
-    if (B, cache_len, d) != (B2, cache_len2, d2):
-        raise ValueError("K and V caches disagree on batch, rows or head_dim")
-    return B, hk, hv, cache_len, d
+    B2, hv, cache_len2, dv = V.shape
+    if (B, cache_len) != (B2, cache_len2):
+        raise ValueError("K and V caches disagree on batch or rows")
+    return B, hk, hv, cache_len, d, dv
 
 
 def max_threads() -> int:
@@ -160,7 +163,7 @@ def atopn_run(q_steps, K, V, ctx_steps, top_n: int, refresh_n: int, scale: float
     """Atop-N over T steps of one layer.
 
     ``q_steps`` is ``[T][B][hq][d]``; ``ctx_steps`` the rows attended per step.
-    Returns a dict with ``out [T][B][hq][d]``, ``tau [T][B][hq]``,
+    Returns a dict with ``out [T][B][hq][dv]``, ``tau [T][B][hq]``,
     ``count [T][B][hq]`` and optionally ``sel``/``logits`` ``[T][B][hq][rows]``.
     """
     return _atopn(q_steps, _u16(K), None, V, ctx_steps, top_n, refresh_n, scale, want_sel,
@@ -178,12 +181,12 @@ def atopn_run_e4m3k(q_steps, K8, k_scale, V, ctx_steps, top_n: int, refresh_n: i
 def _atopn(q_steps, K, k_scale, V, ctx_steps, top_n, refresh_n, scale, want_sel, want_logits,
            nthreads):
     q_steps, V = _u16(q_steps), _u16(V)
-    B, hk, hv, cache_len, d = _cache_shape(K, V)
+    B, hk, hv, cache_len, d, dv = _cache_shape(K, V)
     T, _, hq, _ = q_steps.shape
     ctx = np.ascontiguousarray(ctx_steps, dtype=np.int64)
     if ctx.shape != (T,):
         raise ValueError("ctx_steps must hold one length per step")
-    out = np.empty((T, B, hq, d), dtype=np.float64)
+    out = np.empty((T, B, hq, dv), dtype=np.float64)
     tau = np.empty((T, B, hq), dtype=np.float64)
     count = np.empty((T, B, hq), dtype=np.int64)
     sel = np.empty((T, B, hq, cache_len), dtype=np.uint8) if want_sel else None
@@ -192,13 +195,13 @@ def _atopn(q_steps, K, k_scale, V, ctx_steps, top_n, refresh_n, scale, want_sel,
             _ptr(sel) if sel is not None else None, _ptr(lg) if lg is not None else None,
             nthreads)
     if k_scale is None:
-        rc = _load().oracle_atopn_run(B, hq, hk, hv, d, cache_len, T, _ptr(ctx), scale, top_n,
-                                      refresh_n, _ptr(q_steps), _ptr(K), *tail)
+        rc = _load().oracle_atopn_run(B, hq, hk, hv, d, dv, cache_len, T, _ptr(ctx), scale,
+                                      top_n, refresh_n, _ptr(q_steps), _ptr(K), *tail)
     else:
         ks = _kscale(k_scale, B, hk)
-        rc = _load().oracle_atopn_run_e4m3k(B, hq, hk, hv, d, cache_len, T, _ptr(ctx), scale,
-                                            top_n, refresh_n, _ptr(q_steps), _ptr(K), _ptr(ks),
-                                            *tail)
+        rc = _load().oracle_atopn_run_e4m3k(B, hq, hk, hv, d, dv, cache_len, T, _ptr(ctx),
+                                            scale, top_n, refresh_n, _ptr(q_steps), _ptr(K),
+                                            _ptr(ks), *tail)
     if rc:
         raise ValueError("oracle_atopn_run rejected its arguments")
     res = {"out": out, "tau": tau, "count": count}
@@ -212,14 +215,14 @@ def _atopn(q_steps, K, k_scale, V, ctx_steps, top_n, refresh_n, scale, want_sel,
 def masked(q, K, V, ctx: int, bitmap, scale: float = 1.0, nthreads: int = 0):
     """One step over a caller-given selection bitmap ``[B][hq][ceil(rows/32)]`` (uint32)."""
     q, K, V = _u16(q), _u16(K), _u16(V)
-    B, hk, hv, cache_len, d = _cache_shape(K, V)
+    B, hk, hv, cache_len, d, dv = _cache_shape(K, V)
     hq = q.shape[1]
     bitmap = np.ascontiguousarray(bitmap, dtype=np.uint32)
     if bitmap.shape != (B, hq, (cache_len + 31) // 32):
         raise ValueError("bitmap must be [B][hq][ceil(rows/32)]")
-    out = np.empty((B, hq, d), dtype=np.float64)
+    out = np.empty((B, hq, dv), dtype=np.float64)
     count = np.empty((B, hq), dtype=np.int64)
-    rc = _load().oracle_masked(B, hq, hk, hv, d, cache_len, ctx, scale, _ptr(q), _ptr(K),
+    rc = _load().oracle_masked(B, hq, hk, hv, d, dv, cache_len, ctx, scale, _ptr(q), _ptr(K),
                                _ptr(V), _ptr(bitmap), _ptr(out), _ptr(count), nthreads)
     if rc:
         raise ValueError("oracle_masked rejected its arguments")
@@ -229,15 +232,15 @@ def masked(q, K, V, ctx: int, bitmap, scale: float = 1.0, nthreads: int = 0):
 def masked_e4m3k(q, K8, k_scale, V, ctx: int, bitmap, scale: float = 1.0, nthreads: int = 0):
     """``masked`` with an E4M3 key cache ``K8`` and scales ``k_scale [B][hk]``."""
     q, K8, V = _u16(q), _u8(K8), _u16(V)
-    B, hk, hv, cache_len, d = _cache_shape(K8, V)
+    B, hk, hv, cache_len, d, dv = _cache_shape(K8, V)
     hq = q.shape[1]
     ks = _kscale(k_scale, B, hk)
     bitmap = np.ascontiguousarray(bitmap, dtype=np.uint32)
     if bitmap.shape != (B, hq, (cache_len + 31) // 32):
         raise ValueError("bitmap must be [B][hq][ceil(rows/32)]")
-    out = np.empty((B, hq, d), dtype=np.float64)
+    out = np.empty((B, hq, dv), dtype=np.float64)
     count = np.empty((B, hq), dtype=np.int64)
-    rc = _load().oracle_masked_e4m3k(B, hq, hk, hv, d, cache_len, ctx, scale, _ptr(q), _ptr(K8),
+    rc = _load().oracle_masked_e4m3k(B, hq, hk, hv, d, dv, cache_len, ctx, scale, _ptr(q), _ptr(K8),
                                      _ptr(ks), _ptr(V), _ptr(bitmap), _ptr(out), _ptr(count),
                                      nthreads)
     if rc:
@@ -248,10 +251,10 @@ def masked_e4m3k(q, K8, k_scale, V, ctx: int, bitmap, scale: float = 1.0, nthrea
 def exact_topn(q, K, V, ctx: int, top_n: int, scale: float = 1.0, nthreads: int = 0):
     """Exact top-N attention of one step (index sort, first N, softmax)."""
     q, K, V = _u16(q), _u16(K), _u16(V)
-    B, hk, hv, cache_len, d = _cache_shape(K, V)
+    B, hk, hv, cache_len, d, dv = _cache_shape(K, V)
     hq = q.shape[1]
-    out = np.empty((B, hq, d), dtype=np.float64)
-    rc = _load().oracle_exact_topn(B, hq, hk, hv, d, cache_len, ctx, scale, top_n, _ptr(q),
+    out = np.empty((B, hq, dv), dtype=np.float64)
+    rc = _load().oracle_exact_topn(B, hq, hk, hv, d, dv, cache_len, ctx, scale, top_n, _ptr(q),
                                    _ptr(K), _ptr(V), _ptr(out), nthreads)
     if rc:
         raise ValueError("oracle_exact_topn rejected its arguments")
@@ -261,10 +264,10 @@ def exact_topn(q, K, V, ctx: int, top_n: int, scale: float = 1.0, nthreads: int 
 def full(q, K, V, ctx: int, scale: float = 1.0, nthreads: int = 0):
     """Dense softmax attention of one step over all ``ctx`` rows."""
     q, K, V = _u16(q), _u16(K), _u16(V)
-    B, hk, hv, cache_len, d = _cache_shape(K, V)
+    B, hk, hv, cache_len, d, dv = _cache_shape(K, V)
     hq = q.shape[1]
-    out = np.empty((B, hq, d), dtype=np.float64)
-    rc = _load().oracle_full(B, hq, hk, hv, d, cache_len, ctx, scale, _ptr(q), _ptr(K),
+    out = np.empty((B, hq, dv), dtype=np.float64)
+    rc = _load().oracle_full(B, hq, hk, hv, d, dv, cache_len, ctx, scale, _ptr(q), _ptr(K),
                              _ptr(V), _ptr(out), nthreads)
     if rc:
         raise ValueError("oracle_full rejected its arguments")

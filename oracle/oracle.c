@@ -36,7 +36,9 @@
  *   the zero vector; inputs are bf16 bit patterns, every product and sum is
  *   done in double.  An fp8 key cache holds E4M3 codes with one fp32 scale
  *   per (batch row, key head); key value = scale * decode(code), and the rest
- *   is the bf16 computation on those values.
+ *   is the bf16 computation on those values.  The key/query head dimension d
+ *   and the value/output head dimension dv are independent ([P1] Main
+ *   Findings: a Sigma-style variant trades key heads for key head dimension).
  *
  * Precision: fp64 throughout on exactly the bf16 values the device sees.
  * Parallelism: one OpenMP loop over independent (b, i) pairs; nothing else.
@@ -107,9 +109,9 @@ static double key_at(const key_head* k, int64_t idx)
     return bf16_to_double(k->bf16[idx]);
 }
 
-static int check_dims(int B, int hq, int hk, int hv, int d, int64_t cache_len)
+static int check_dims(int B, int hq, int hk, int hv, int d, int dv, int64_t cache_len)
 {
-    if (B < 1 || hq < 1 || hk < 1 || hv < 1 || d < 1 || cache_len < 1) return 1;
+    if (B < 1 || hq < 1 || hk < 1 || hv < 1 || d < 1 || dv < 1 || cache_len < 1) return 1;
     if (hq % hk != 0 || hq % hv != 0) return 1;
     return 0;
 }
@@ -164,22 +166,22 @@ static double nth_largest(const double* s, int64_t n, int64_t N)
  *   m = max_S s_j, w_j = exp(s_j - m), out = sum_S w_j V_j / sum_S w_j.
  * An empty selection gives out = 0.  Returns |S|. */
 static int64_t attend_selected(const double* s, const unsigned char* sel, int64_t ctx,
-                               const uint16_t* Vh, int d, double* out)
+                               const uint16_t* Vh, int dv, double* out)
 {
     int64_t count = 0;
     double m = -INFINITY;
     for (int64_t j = 0; j < ctx; ++j)
         if (sel[j]) { ++count; if (s[j] > m) m = s[j]; }
-    for (int c = 0; c < d; ++c) out[c] = 0.0;
+    for (int c = 0; c < dv; ++c) out[c] = 0.0;
     if (count == 0) return 0;
     double denom = 0.0;
     for (int64_t j = 0; j < ctx; ++j) {
         if (!sel[j]) continue;
         double w = exp(s[j] - m);
         denom += w;
-        for (int c = 0; c < d; ++c) out[c] += w * bf16_to_double(Vh[j * d + c]);
+        for (int c = 0; c < dv; ++c) out[c] += w * bf16_to_double(Vh[j * dv + c]);
     }
-    for (int c = 0; c < d; ++c) out[c] /= denom;
+    for (int c = 0; c < dv; ++c) out[c] /= denom;
     return count;
 }
 
@@ -189,7 +191,7 @@ static int logits_impl(int B, int hq, int hk, int hv, int d, int64_t cache_len, 
                        double scale, const uint16_t* q, const key_cache* K, double* s,
                        int nthreads)
 {
-    if (check_dims(B, hq, hk, hv, d, cache_len) || ctx < 1 || ctx > cache_len) return 1;
+    if (check_dims(B, hq, hk, hv, d, d, cache_len) || ctx < 1 || ctx > cache_len) return 1;
     set_threads(nthreads);
     const int Gk = hq / hk;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -250,13 +252,13 @@ double oracle_nth_largest(const double* s, int64_t n, int64_t N)
  *   sel    [T][B][hq][cache_len] uint8, nullable (1 = selected)
  *   logits [T][B][hq][cache_len] double, nullable
  */
-static int atopn_run_impl(int B, int hq, int hk, int hv, int d, int64_t cache_len,
+static int atopn_run_impl(int B, int hq, int hk, int hv, int d, int dv, int64_t cache_len,
                           int T, const int64_t* ctx, double scale, int64_t top_n,
                           int64_t refresh_n, const uint16_t* q, const key_cache* K,
                           const uint16_t* V, double* out, double* tau, int64_t* count,
                           unsigned char* sel, double* logits, int nthreads)
 {
-    if (check_dims(B, hq, hk, hv, d, cache_len) || T < 1 || top_n < 1 || refresh_n < 1)
+    if (check_dims(B, hq, hk, hv, d, dv, cache_len) || T < 1 || top_n < 1 || refresh_n < 1)
         return 1;
     for (int t = 0; t < T; ++t)
         if (ctx[t] < 1 || ctx[t] > cache_len) return 1;
@@ -267,7 +269,7 @@ static int atopn_run_impl(int B, int hq, int hk, int hv, int d, int64_t cache_le
     for (int bi = 0; bi < B * hq; ++bi) {
         const int b = bi / hq, i = bi % hq;
         const key_head Kh = key_head_of(K, b, hk, i / Gk, cache_len, d);
-        const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, d);
+        const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, dv);
         double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);
         unsigned char* S = (unsigned char*)malloc((size_t)cache_len);
         if (!s || !S) { err = 1; free(s); free(S); continue; }
@@ -278,7 +280,7 @@ static int atopn_run_impl(int B, int hq, int hk, int hv, int d, int64_t cache_le
             head_logits(q + row * d, &Kh, d, n, scale, s);
             if (t % refresh_n == 0) threshold = nth_largest(s, n, top_n);
             for (int64_t j = 0; j < n; ++j) S[j] = (s[j] >= threshold);
-            count[row] = attend_selected(s, S, n, Vh, d, out + row * d);
+            count[row] = attend_selected(s, S, n, Vh, dv, out + row * dv);
             tau[row] = threshold;
             if (sel) {
                 memset(sel + row * cache_len, 0, (size_t)cache_len);
@@ -295,38 +297,38 @@ static int atopn_run_impl(int B, int hq, int hk, int hv, int d, int64_t cache_le
     return err;
 }
 
-int oracle_atopn_run(int B, int hq, int hk, int hv, int d, int64_t cache_len,
+int oracle_atopn_run(int B, int hq, int hk, int hv, int d, int dv, int64_t cache_len,
                      int T, const int64_t* ctx, double scale, int64_t top_n,
                      int64_t refresh_n, const uint16_t* q, const uint16_t* K,
                      const uint16_t* V, double* out, double* tau, int64_t* count,
                      unsigned char* sel, double* logits, int nthreads)
 {
     const key_cache kc = {K, NULL, NULL};
-    return atopn_run_impl(B, hq, hk, hv, d, cache_len, T, ctx, scale, top_n, refresh_n, q,
+    return atopn_run_impl(B, hq, hk, hv, d, dv, cache_len, T, ctx, scale, top_n, refresh_n, q,
                           &kc, V, out, tau, count, sel, logits, nthreads);
 }
 
 /* Atop-N as above with an E4M3 key cache K8 [B][hk][cache_len][d] and
  * per-(b, key head) scales k_scale [B][hk]. */
-int oracle_atopn_run_e4m3k(int B, int hq, int hk, int hv, int d, int64_t cache_len,
+int oracle_atopn_run_e4m3k(int B, int hq, int hk, int hv, int d, int dv, int64_t cache_len,
                            int T, const int64_t* ctx, double scale, int64_t top_n,
                            int64_t refresh_n, const uint16_t* q, const uint8_t* K8,
                            const float* k_scale, const uint16_t* V, double* out, double* tau,
                            int64_t* count, unsigned char* sel, double* logits, int nthreads)
 {
     const key_cache kc = {NULL, K8, k_scale};
-    return atopn_run_impl(B, hq, hk, hv, d, cache_len, T, ctx, scale, top_n, refresh_n, q,
+    return atopn_run_impl(B, hq, hk, hv, d, dv, cache_len, T, ctx, scale, top_n, refresh_n, q,
                           &kc, V, out, tau, count, sel, logits, nthreads);
 }
 
 /* One step with the selection given by the caller as a bitmap
  * [B][hq][ceil(cache_len/32)] (bit j%32 of word j/32 selects row j): the
  * "use the device's mask" mode that isolates softmax and PV from selection. */
-static int masked_impl(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t ctx,
+static int masked_impl(int B, int hq, int hk, int hv, int d, int dv, int64_t cache_len, int64_t ctx,
                        double scale, const uint16_t* q, const key_cache* K, const uint16_t* V,
                        const uint32_t* bitmap, double* out, int64_t* count, int nthreads)
 {
-    if (check_dims(B, hq, hk, hv, d, cache_len) || ctx < 1 || ctx > cache_len) return 1;
+    if (check_dims(B, hq, hk, hv, d, dv, cache_len) || ctx < 1 || ctx > cache_len) return 1;
     set_threads(nthreads);
     const int Gk = hq / hk, Gv = hq / hv;
     const int64_t words = (cache_len + 31) / 32;
@@ -341,31 +343,31 @@ static int masked_impl(int B, int hq, int hk, int hv, int d, int64_t cache_len, 
         head_logits(q + (int64_t)bi * d, &Kh, d, ctx, scale, s);
         const uint32_t* bits = bitmap + (int64_t)bi * words;
         for (int64_t j = 0; j < ctx; ++j) S[j] = (bits[j / 32] >> (j % 32)) & 1u;
-        count[bi] = attend_selected(s, S, ctx, cache_head(V, b, hv, i / Gv, cache_len, d),
-                                    d, out + (int64_t)bi * d);
+        count[bi] = attend_selected(s, S, ctx, cache_head(V, b, hv, i / Gv, cache_len, dv),
+                                    dv, out + (int64_t)bi * dv);
         free(s);
         free(S);
     }
     return err;
 }
 
-int oracle_masked(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t ctx,
+int oracle_masked(int B, int hq, int hk, int hv, int d, int dv, int64_t cache_len, int64_t ctx,
                   double scale, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                   const uint32_t* bitmap, double* out, int64_t* count, int nthreads)
 {
     const key_cache kc = {K, NULL, NULL};
-    return masked_impl(B, hq, hk, hv, d, cache_len, ctx, scale, q, &kc, V, bitmap, out, count,
+    return masked_impl(B, hq, hk, hv, d, dv, cache_len, ctx, scale, q, &kc, V, bitmap, out, count,
                        nthreads);
 }
 
 /* One step over a caller-given bitmap with an E4M3 key cache. */
-int oracle_masked_e4m3k(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t ctx,
+int oracle_masked_e4m3k(int B, int hq, int hk, int hv, int d, int dv, int64_t cache_len, int64_t ctx,
                         double scale, const uint16_t* q, const uint8_t* K8,
                         const float* k_scale, const uint16_t* V, const uint32_t* bitmap,
                         double* out, int64_t* count, int nthreads)
 {
     const key_cache kc = {NULL, K8, k_scale};
-    return masked_impl(B, hq, hk, hv, d, cache_len, ctx, scale, q, &kc, V, bitmap, out, count,
+    return masked_impl(B, hq, hk, hv, d, dv, cache_len, ctx, scale, q, &kc, V, bitmap, out, count,
                        nthreads);
 }
 
@@ -384,11 +386,11 @@ static int cmp_scored_desc(const void* a, const void* b)
  * Experimental setup): rank the indices by logit (descending, index breaks
  * ties), keep the first min(N, ctx), softmax over those and apply to V.
  * Written without thresholds, independently of oracle_atopn_run. */
-int oracle_exact_topn(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t ctx,
+int oracle_exact_topn(int B, int hq, int hk, int hv, int d, int dv, int64_t cache_len, int64_t ctx,
                       double scale, int64_t top_n, const uint16_t* q, const uint16_t* K,
                       const uint16_t* V, double* out, int nthreads)
 {
-    if (check_dims(B, hq, hk, hv, d, cache_len) || ctx < 1 || ctx > cache_len || top_n < 1)
+    if (check_dims(B, hq, hk, hv, d, dv, cache_len) || ctx < 1 || ctx > cache_len || top_n < 1)
         return 1;
     set_threads(nthreads);
     const int Gk = hq / hk, Gv = hq / hv;
@@ -397,7 +399,7 @@ int oracle_exact_topn(int B, int hq, int hk, int hv, int d, int64_t cache_len, i
     for (int bi = 0; bi < B * hq; ++bi) {
         const int b = bi / hq, i = bi % hq;
         const uint16_t* Kh = cache_head(K, b, hk, i / Gk, cache_len, d);
-        const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, d);
+        const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, dv);
         const uint16_t* qi = q + (int64_t)bi * d;
         scored_index* idx = (scored_index*)malloc(sizeof(scored_index) * (size_t)ctx);
         if (!idx) { err = 1; continue; }
@@ -410,15 +412,15 @@ int oracle_exact_topn(int B, int hq, int hk, int hv, int d, int64_t cache_len, i
         }
         qsort(idx, (size_t)ctx, sizeof(scored_index), cmp_scored_desc);
         const int64_t keep = top_n < ctx ? top_n : ctx;
-        double* o = out + (int64_t)bi * d;
-        for (int c = 0; c < d; ++c) o[c] = 0.0;
+        double* o = out + (int64_t)bi * dv;
+        for (int c = 0; c < dv; ++c) o[c] = 0.0;
         double denom = 0.0;
         for (int64_t r = 0; r < keep; ++r) {
             double w = exp(idx[r].s - idx[0].s); /* idx[0] holds the maximum */
             denom += w;
-            for (int c = 0; c < d; ++c) o[c] += w * bf16_to_double(Vh[idx[r].j * d + c]);
+            for (int c = 0; c < dv; ++c) o[c] += w * bf16_to_double(Vh[idx[r].j * dv + c]);
         }
-        for (int c = 0; c < d; ++c) o[c] /= denom;
+        for (int c = 0; c < dv; ++c) o[c] /= denom;
         free(idx);
     }
     return err;
@@ -427,11 +429,11 @@ int oracle_exact_topn(int B, int hq, int hk, int hv, int d, int64_t cache_len, i
 /* Full (dense) decode attention of one step: softmax over every attended row.
  * This is the full-attention GQA/SAGA baseline the pages time against
  * ([P1] Main Findings, end-to-end speedups and the flash-attention note). */
-int oracle_full(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t ctx,
+int oracle_full(int B, int hq, int hk, int hv, int d, int dv, int64_t cache_len, int64_t ctx,
                 double scale, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                 double* out, int nthreads)
 {
-    if (check_dims(B, hq, hk, hv, d, cache_len) || ctx < 1 || ctx > cache_len) return 1;
+    if (check_dims(B, hq, hk, hv, d, dv, cache_len) || ctx < 1 || ctx > cache_len) return 1;
     set_threads(nthreads);
     const int Gk = hq / hk, Gv = hq / hv;
     int err = 0;
@@ -440,21 +442,21 @@ int oracle_full(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t
         const int b = bi / hq, i = bi % hq;
         const key_cache kc = {K, NULL, NULL};
         const key_head Kh = key_head_of(&kc, b, hk, i / Gk, cache_len, d);
-        const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, d);
+        const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, dv);
         double* s = (double*)malloc(sizeof(double) * (size_t)ctx);
         if (!s) { err = 1; continue; }
         head_logits(q + (int64_t)bi * d, &Kh, d, ctx, scale, s);
         double m = -INFINITY;
         for (int64_t j = 0; j < ctx; ++j) if (s[j] > m) m = s[j];
-        double* o = out + (int64_t)bi * d;
-        for (int c = 0; c < d; ++c) o[c] = 0.0;
+        double* o = out + (int64_t)bi * dv;
+        for (int c = 0; c < dv; ++c) o[c] = 0.0;
         double denom = 0.0;
         for (int64_t j = 0; j < ctx; ++j) {
             double w = exp(s[j] - m);
             denom += w;
-            for (int c = 0; c < d; ++c) o[c] += w * bf16_to_double(Vh[j * d + c]);
+            for (int c = 0; c < dv; ++c) o[c] += w * bf16_to_double(Vh[j * dv + c]);
         }
-        for (int c = 0; c < d; ++c) o[c] /= denom;
+        for (int c = 0; c < dv; ++c) o[c] /= denom;
         free(s);
     }
     return err;

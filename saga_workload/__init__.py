@@ -46,6 +46,7 @@ class Workload:
     steps: int           # T decode steps
     layers: int
     scale: float = 1.0   # 1/sqrt(d) is folded into q
+    head_dim_v: int = 0  # value head dimension; 0: same as head_dim
 
     @property
     def rows(self) -> int:
@@ -62,7 +63,8 @@ class Workload:
         return dataclasses.replace(self, name=self.name + f"_gqa{h_kv}", h_k=h_kv, h_v=h_kv)
 
     def kv_bytes(self) -> int:
-        return self.layers * self.batch * (self.h_k + self.h_v) * self.rows * self.head_dim * 2
+        dv = self.head_dim_v or self.head_dim
+        return self.layers * self.batch * (self.h_k * self.head_dim + self.h_v * dv) * self.rows * 2
 
 
 # The five workload families.  index is the seed base.
@@ -98,8 +100,8 @@ def make_layer(w: Workload, layer: int = 0, device="cpu", heavy_hitters: bool = 
                steps: Optional[int] = None) -> Dict[str, torch.Tensor]:
     """Draw one layer's K/V caches and the query of every decode step.
 
-    Returns ``K [B][h_k][rows][d]``, ``V [B][h_v][rows][d]`` and
-    ``q [T][B][h_q][d]``, all bf16 on ``device``.
+    Returns ``K [B][h_k][rows][d]``, ``V [B][h_v][rows][d_v]`` and
+    ``q [T][B][h_q][d]``, all bf16 on ``device`` (d_v = head_dim_v, or d).
     """
     device = torch.device(device)
     T = w.steps if steps is None else steps
@@ -120,7 +122,8 @@ def make_layer(w: Workload, layer: int = 0, device="cpu", heavy_hitters: bool = 
     gkv.manual_seed(seed)
     # torch draws bf16 normals in fp32 and rounds them to nearest even.
     K = torch.randn((B, hk, rows, d), generator=gkv, device=device, dtype=torch.bfloat16)
-    V = torch.randn((B, hv, rows, d), generator=gkv, device=device, dtype=torch.bfloat16)
+    V = torch.randn((B, hv, rows, w.head_dim_v or d), generator=gkv, device=device,
+                    dtype=torch.bfloat16)
     if heavy_hitters:
         count = int(round(0.01 * rows))
         Gk = hq // hk

@@ -52,7 +52,7 @@ class SagaDims(ctypes.Structure):
         ("h_k", ctypes.c_int32),
         ("h_v", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("head_dim_v", ctypes.c_int32),
         ("ctx_len", ctypes.c_int64),
         ("cache_len", ctypes.c_int64),
         ("scale", ctypes.c_float),
@@ -61,7 +61,7 @@ class SagaDims(ctypes.Structure):
 
     def __repr__(self):
         return (f"SagaDims(batch={self.batch}, h_q={self.h_q}, h_k={self.h_k}, h_v={self.h_v}, "
-                f"head_dim={self.head_dim}, ctx_len={self.ctx_len}, "
+                f"head_dim={self.head_dim}, head_dim_v={self.head_dim_v}, ctx_len={self.ctx_len}, "
                 f"cache_len={self.cache_len}, scale={self.scale})")
 
 
@@ -137,8 +137,13 @@ def library():
 
 
 def dims(batch: int, h_q: int, h_k: int, h_v: int, head_dim: int, ctx_len: int,
-         cache_len: int, scale: float = 1.0) -> SagaDims:
-    return SagaDims(batch, h_q, h_k, h_v, head_dim, 0, ctx_len, cache_len, scale, 0.0)
+         cache_len: int, scale: float = 1.0, head_dim_v: int = 0) -> SagaDims:
+    """Shape of one layer call; head_dim is d_k, head_dim_v is d_v (0: same as d_k)."""
+    return SagaDims(batch, h_q, h_k, h_v, head_dim, head_dim_v, ctx_len, cache_len, scale, 0.0)
+
+
+def _dv(d: SagaDims) -> int:
+    return d.head_dim_v or d.head_dim
 
 
 def saga_status_string(status: int) -> str:
@@ -219,9 +224,9 @@ def saga_decode_step(d: SagaDims, q: torch.Tensor, k_cache: torch.Tensor, v_cach
     bh = d.batch * d.h_q
     _need(q, bh * d.head_dim, "q")
     _need(k_cache, d.batch * d.h_k * d.cache_len * d.head_dim, "k_cache")
-    _need(v_cache, d.batch * d.h_v * d.cache_len * d.head_dim, "v_cache")
+    _need(v_cache, d.batch * d.h_v * d.cache_len * _dv(d), "v_cache")
     _need(thresholds, bh, "thresholds")
-    _need(out, bh * d.head_dim, "out")
+    _need(out, bh * _dv(d), "out")
     _need(sel_counts, bh, "sel_counts")
     _need(sel_bitmap_debug, bh * ((d.cache_len + 31) // 32), "sel_bitmap_debug")
     ws, nbytes = _ws(workspace)
@@ -241,9 +246,9 @@ def atopn_refresh_decode_step(d: SagaDims, top_n: int, q: torch.Tensor, k_cache:
     bh = d.batch * d.h_q
     _need(q, bh * d.head_dim, "q")
     _need(k_cache, d.batch * d.h_k * d.cache_len * d.head_dim, "k_cache")
-    _need(v_cache, d.batch * d.h_v * d.cache_len * d.head_dim, "v_cache")
+    _need(v_cache, d.batch * d.h_v * d.cache_len * _dv(d), "v_cache")
     _need(thresholds, bh, "thresholds")
-    _need(out, bh * d.head_dim, "out")
+    _need(out, bh * _dv(d), "out")
     _need(sel_counts, bh, "sel_counts")
     ws, nbytes = _ws(workspace)
     _check(library().atopn_refresh_decode_step(
@@ -265,8 +270,8 @@ def paged(block_table: torch.Tensor, ctx_lens: torch.Tensor, page_rows: int,
                      int(block_table.shape[1]), int(num_pages), 0)
 
 
-def _need_pool(t: torch.Tensor, d: SagaDims, p: SagaPaged, heads: int, name: str):
-    _need(t, p.num_pages * heads * p.page_rows * d.head_dim, name)
+def _need_pool(t: torch.Tensor, d: SagaDims, p: SagaPaged, heads: int, dim: int, name: str):
+    _need(t, p.num_pages * heads * p.page_rows * dim, name)
 
 
 def atopn_refresh_thresholds_paged(d: SagaDims, p: SagaPaged, top_n: int, q: torch.Tensor,
@@ -274,7 +279,7 @@ def atopn_refresh_thresholds_paged(d: SagaDims, p: SagaPaged, top_n: int, q: tor
                                    workspace: torch.Tensor, stream=None) -> None:
     """Exact top-N thresholds on paged caches (per-sequence lengths)."""
     _need(q, d.batch * d.h_q * d.head_dim, "q")
-    _need_pool(k_pages, d, p, d.h_k, "k_pages")
+    _need_pool(k_pages, d, p, d.h_k, d.head_dim, "k_pages")
     _need(thresholds, d.batch * d.h_q, "thresholds")
     ws, nbytes = _ws(workspace)
     _check(library().atopn_refresh_thresholds_paged(
@@ -290,10 +295,10 @@ def saga_decode_step_paged(d: SagaDims, p: SagaPaged, q: torch.Tensor, k_pages: 
     """One Atop-N decode step on paged caches."""
     bh = d.batch * d.h_q
     _need(q, bh * d.head_dim, "q")
-    _need_pool(k_pages, d, p, d.h_k, "k_pages")
-    _need_pool(v_pages, d, p, d.h_v, "v_pages")
+    _need_pool(k_pages, d, p, d.h_k, d.head_dim, "k_pages")
+    _need_pool(v_pages, d, p, d.h_v, _dv(d), "v_pages")
     _need(thresholds, bh, "thresholds")
-    _need(out, bh * d.head_dim, "out")
+    _need(out, bh * _dv(d), "out")
     _need(sel_counts, bh, "sel_counts")
     ws, nbytes = _ws(workspace)
     _check(library().saga_decode_step_paged(
@@ -313,10 +318,10 @@ def atopn_refresh_decode_step_paged(d: SagaDims, p: SagaPaged, top_n: int, q: to
     """A refresh step on paged caches: fresh thresholds and this step's output."""
     bh = d.batch * d.h_q
     _need(q, bh * d.head_dim, "q")
-    _need_pool(k_pages, d, p, d.h_k, "k_pages")
-    _need_pool(v_pages, d, p, d.h_v, "v_pages")
+    _need_pool(k_pages, d, p, d.h_k, d.head_dim, "k_pages")
+    _need_pool(v_pages, d, p, d.h_v, _dv(d), "v_pages")
     _need(thresholds, bh, "thresholds")
-    _need(out, bh * d.head_dim, "out")
+    _need(out, bh * _dv(d), "out")
     _need(sel_counts, bh, "sel_counts")
     ws, nbytes = _ws(workspace)
     _check(library().atopn_refresh_decode_step_paged(
@@ -328,8 +333,8 @@ def atopn_refresh_decode_step_paged(d: SagaDims, p: SagaPaged, top_n: int, q: to
 
 
 def _lq_dims(d: SagaDims, l_q: int) -> SagaDims:
-    return SagaDims(d.batch, d.h_q * l_q, d.h_k, d.h_v, d.head_dim, 0, d.ctx_len, d.cache_len,
-                    d.scale, 0.0)
+    return SagaDims(d.batch, d.h_q * l_q, d.h_k, d.h_v, d.head_dim, d.head_dim_v, d.ctx_len,
+                    d.cache_len, d.scale, 0.0)
 
 
 def alloc_workspace_lq(d: SagaDims, l_q: int, top_n: int, device="cuda") -> torch.Tensor:
@@ -360,9 +365,9 @@ def saga_decode_step_lq(d: SagaDims, l_q: int, q: torch.Tensor, k_cache: torch.T
     n = d.batch * d.h_q * l_q
     _need(q, n * d.head_dim, "q")
     _need(k_cache, d.batch * d.h_k * d.cache_len * d.head_dim, "k_cache")
-    _need(v_cache, d.batch * d.h_v * d.cache_len * d.head_dim, "v_cache")
+    _need(v_cache, d.batch * d.h_v * d.cache_len * _dv(d), "v_cache")
     _need(thresholds, n, "thresholds")
-    _need(out, n * d.head_dim, "out")
+    _need(out, n * _dv(d), "out")
     _need(sel_counts, n, "sel_counts")
     ws, nbytes = _ws(workspace)
     _check(library().saga_decode_step_lq(
@@ -382,9 +387,9 @@ def atopn_refresh_decode_step_lq(d: SagaDims, l_q: int, top_n: int, q: torch.Ten
     n = d.batch * d.h_q * l_q
     _need(q, n * d.head_dim, "q")
     _need(k_cache, d.batch * d.h_k * d.cache_len * d.head_dim, "k_cache")
-    _need(v_cache, d.batch * d.h_v * d.cache_len * d.head_dim, "v_cache")
+    _need(v_cache, d.batch * d.h_v * d.cache_len * _dv(d), "v_cache")
     _need(thresholds, n, "thresholds")
-    _need(out, n * d.head_dim, "out")
+    _need(out, n * _dv(d), "out")
     _need(sel_counts, n, "sel_counts")
     ws, nbytes = _ws(workspace)
     _check(library().atopn_refresh_decode_step_lq(
@@ -435,9 +440,9 @@ def saga_decode_step_fp8k(d: SagaDims, q: torch.Tensor, k8_cache: torch.Tensor,
     bh = d.batch * d.h_q
     _need(q, bh * d.head_dim, "q")
     _need_fp8k(d, k8_cache, k_scale)
-    _need(v_cache, d.batch * d.h_v * d.cache_len * d.head_dim, "v_cache")
+    _need(v_cache, d.batch * d.h_v * d.cache_len * _dv(d), "v_cache")
     _need(thresholds, bh, "thresholds")
-    _need(out, bh * d.head_dim, "out")
+    _need(out, bh * _dv(d), "out")
     _need(sel_counts, bh, "sel_counts")
     _need(sel_bitmap_debug, bh * ((d.cache_len + 31) // 32), "sel_bitmap_debug")
     ws, nbytes = _ws(workspace)
@@ -460,9 +465,9 @@ def atopn_refresh_decode_step_fp8k(d: SagaDims, top_n: int, q: torch.Tensor,
     bh = d.batch * d.h_q
     _need(q, bh * d.head_dim, "q")
     _need_fp8k(d, k8_cache, k_scale)
-    _need(v_cache, d.batch * d.h_v * d.cache_len * d.head_dim, "v_cache")
+    _need(v_cache, d.batch * d.h_v * d.cache_len * _dv(d), "v_cache")
     _need(thresholds, bh, "thresholds")
-    _need(out, bh * d.head_dim, "out")
+    _need(out, bh * _dv(d), "out")
     _need(sel_counts, bh, "sel_counts")
     ws, nbytes = _ws(workspace)
     _check(library().atopn_refresh_decode_step_fp8k(
@@ -480,8 +485,8 @@ def saga_full_attention(d: SagaDims, q: torch.Tensor, k_cache: torch.Tensor,
     bh = d.batch * d.h_q
     _need(q, bh * d.head_dim, "q")
     _need(k_cache, d.batch * d.h_k * d.cache_len * d.head_dim, "k_cache")
-    _need(v_cache, d.batch * d.h_v * d.cache_len * d.head_dim, "v_cache")
-    _need(out, bh * d.head_dim, "out")
+    _need(v_cache, d.batch * d.h_v * d.cache_len * _dv(d), "v_cache")
+    _need(out, bh * _dv(d), "out")
     ws, nbytes = _ws(workspace)
     _check(library().saga_full_attention(
         ctypes.byref(d), _ptr(q, torch.bfloat16, "q"), _ptr(k_cache, torch.bfloat16, "k_cache"),

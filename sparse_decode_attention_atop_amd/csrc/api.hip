@@ -26,28 +26,36 @@ constexpr int64_t kFullTargetBlocks = SAGA_FULL_BLOCKS;   // dense kernel: workg
 int64_t target_blocks(int head_dim, bool k8 = false)
 {
     if (k8) return head_dim == 128 ? SAGA_TARGET_BLOCKS128_K8 : SAGA_TARGET_BLOCKS64_K8;
+    if (head_dim == 32) return SAGA_TARGET_BLOCKS32;
     return head_dim == 128 ? SAGA_TARGET_BLOCKS128 : SAGA_TARGET_BLOCKS64;
 }
 constexpr int64_t kMaxCacheLen = int64_t(1) << 27;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Value / output head dimension (head_dim_v, or head_dim when that is 0).
+int value_dim(const saga_dims* d) { return d->head_dim_v ? d->head_dim_v : d->head_dim; }
+
+bool supported_dim(int x) { return x == 32 || x == 64 || x == 128; }
+
 int validate_dims(const saga_dims* d)
 {
     if (!d) return SAGA_ERR_INVALID_ARGUMENT;
-    if (d->batch < 1 || d->h_q < 1 || d->h_k < 1 || d->h_v < 1 || d->head_dim < 1)
+    if (d->batch < 1 || d->h_q < 1 || d->h_k < 1 || d->h_v < 1 || d->head_dim < 1 ||
+        d->head_dim_v < 0)
         return SAGA_ERR_INVALID_ARGUMENT;
-    if (d->reserved != 0 || d->reserved2 != 0.0f) return SAGA_ERR_INVALID_ARGUMENT;
+    if (d->reserved2 != 0.0f) return SAGA_ERR_INVALID_ARGUMENT;
     if (d->h_q % d->h_k != 0 || d->h_q % d->h_v != 0) return SAGA_ERR_INVALID_ARGUMENT;
     if (d->cache_len < 1 || d->cache_len >= kMaxCacheLen) return SAGA_ERR_INVALID_ARGUMENT;
     if (d->ctx_len < 1 || d->ctx_len > d->cache_len) return SAGA_ERR_INVALID_ARGUMENT;
     if (!isfinite(d->scale)) return SAGA_ERR_INVALID_ARGUMENT;
-    if (d->head_dim != 64 && d->head_dim != 128) return SAGA_ERR_UNSUPPORTED;
+    if (!supported_dim(d->head_dim) || !supported_dim(value_dim(d))) return SAGA_ERR_UNSUPPORTED;
     if (d->h_q / d->h_k > 16) return SAGA_ERR_UNSUPPORTED;
     if ((int64_t)d->batch * d->h_k > 65535) return SAGA_ERR_UNSUPPORTED;
     if ((int64_t)d->batch * d->h_q * d->cache_len > (int64_t(1) << 40)) return SAGA_ERR_UNSUPPORTED;
     // One cache head is addressed with 32-bit buffer offsets.
-    if (d->cache_len * d->head_dim * 2 >= (int64_t(1) << 31)) return SAGA_ERR_UNSUPPORTED;
+    const int64_t dmax = d->head_dim > value_dim(d) ? d->head_dim : value_dim(d);
+    if (d->cache_len * dmax * 2 >= (int64_t(1) << 31)) return SAGA_ERR_UNSUPPORTED;
     return SAGA_OK;
 }
 
@@ -120,7 +128,7 @@ Layout make_layout(const saga_dims* d)
     L.pm = take(rows * L.max_chunks * 4);
     L.pl = take(rows * L.max_chunks * 4);
     L.pc = take(rows * L.max_chunks * 4);
-    L.po = take(rows * L.max_chunks * (size_t)d->head_dim * 4);
+    L.po = take(rows * L.max_chunks * (size_t)value_dim(d) * 4);
     L.entries = take(rows * L.max_chunks * kWavesPerBlock * (size_t)kListPrimary * 8);
     L.overflow = take(rows * (size_t)L.entry_rows * 8);
     L.lcount = take(rows * L.max_chunks * kWavesPerBlock * 4);
@@ -289,7 +297,7 @@ int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunkin
                            const RowModel& rm)
 {
     unsigned char* w = static_cast<unsigned char*>(workspace_dev);
-    const int D = dims->head_dim;
+    const int D = value_dim(dims);                      // the gather reads V rows only
     const int rows = dims->batch * dims->h_q;
     // Each (b, query head) gets `segs` gather workgroups that split its selected
     // entries evenly: about gather_target_blocks(D) workgroups in all.
@@ -620,6 +628,7 @@ int fp8k_model(const saga_dims* dims, const float* k_scale_dev, RowModel* rm)
     const int st = validate_dims(dims);
     if (st != SAGA_OK) return st;
     if (!k_scale_dev || misaligned(k_scale_dev, 4)) return SAGA_ERR_INVALID_ARGUMENT;
+    if (dims->head_dim < 64) return SAGA_ERR_UNSUPPORTED;   // fp8 loads cover 64 bytes of a row
     rm->k_scale = k_scale_dev;
     return SAGA_OK;
 }
@@ -682,7 +691,7 @@ SAGA_EXPORT int saga_full_attention(const saga_dims* dims, const void* q_dev,
     const Layout L = make_layout(dims);
     if (workspace_bytes < L.total) return SAGA_ERR_WORKSPACE_TOO_SMALL;
 
-    const int D = dims->head_dim;
+    const int D = dims->head_dim, DV = value_dim(dims);
     const int Gk = dims->h_q / dims->h_k, Gv = dims->h_q / dims->h_v;
     // Value heads touched by one key head's query heads, and query heads per
     // (key head, value head) pair.
@@ -701,7 +710,7 @@ SAGA_EXPORT int saga_full_attention(const saga_dims* dims, const void* q_dev,
     const int maxs_t = maxs <= 2 ? 2 : (maxs <= 4 ? 4 : 8);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t block_rows = (int64_t)kWavesPerBlock * 16 * full_unroll(D);
+    const int64_t block_rows = (int64_t)kWavesPerBlock * 16 * full_unroll(D, DV);
     const Chunking ch = split_rows(dims->ctx_len, (int64_t)dims->batch * dims->h_k, block_rows,
                                    kFullTargetBlocks, L.max_chunks);
     FullArgs a{};
@@ -721,10 +730,10 @@ SAGA_EXPORT int saga_full_attention(const saga_dims* dims, const void* q_dev,
     a.rows_per_chunk = ch.rows;
     a.chunks = ch.chunks;
     a.scale = dims->scale;
-    a.wave_lds = full_wave_lds_bytes(D, maxs_t);
-    st = hip_status(launch_full(D, maxs_t, a, s));
+    a.wave_lds = full_wave_lds_bytes(D, DV, maxs_t);
+    st = hip_status(launch_full(D, DV, maxs_t, a, s));
     if (st != SAGA_OK) return st;
-    return hip_status(launch_combine(D, a.part, dims->batch * dims->h_q, ch.chunks,
+    return hip_status(launch_combine(DV, a.part, dims->batch * dims->h_q, ch.chunks,
                                      static_cast<uint16_t*>(out_dev), nullptr, s));
 }
 

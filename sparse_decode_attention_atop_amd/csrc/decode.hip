@@ -621,16 +621,22 @@ hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t s)
 #define SAGA_LAUNCH_STREAM(DD, DBG, PG, F8)                                                      \
     hipLaunchKernelGGL((select_stream_kernel<DD, F8 ? decode_unroll_k8(DD) : decode_unroll(DD),  \
                                              DBG, PG, F8>), grid, dim3(kBlock), 0, s, a)
-#define SAGA_LAUNCH_STREAM_D(DD)                                                                 \
+#define SAGA_LAUNCH_STREAM_BF(DD)                                                                \
     if (kind == 1) { if (dbg) SAGA_LAUNCH_STREAM(DD, true, true, false); else SAGA_LAUNCH_STREAM(DD, false, true, false); } \
-    else if (kind == 2) { if (dbg) SAGA_LAUNCH_STREAM(DD, true, false, true); else SAGA_LAUNCH_STREAM(DD, false, false, true); } \
     else { if (dbg) SAGA_LAUNCH_STREAM(DD, true, false, false); else SAGA_LAUNCH_STREAM(DD, false, false, false); }
-    if (D == 64) {
+#define SAGA_LAUNCH_STREAM_D(DD)                                                                 \
+    if (kind == 2) { if (dbg) SAGA_LAUNCH_STREAM(DD, true, false, true); else SAGA_LAUNCH_STREAM(DD, false, false, true); } \
+    else { SAGA_LAUNCH_STREAM_BF(DD) }
+    if (D == 32) {
+        if (kind == 2) return hipErrorInvalidValue;      // no fp8 K at head_dim 32 (the API rejects it)
+        SAGA_LAUNCH_STREAM_BF(32)
+    } else if (D == 64) {
         SAGA_LAUNCH_STREAM_D(64)
     } else {
         SAGA_LAUNCH_STREAM_D(128)
     }
 #undef SAGA_LAUNCH_STREAM_D
+#undef SAGA_LAUNCH_STREAM_BF
 #undef SAGA_LAUNCH_STREAM
     return hipGetLastError();
 }
@@ -640,7 +646,11 @@ hipError_t launch_gather(int D, const GatherArgs& a, hipStream_t s)
     const dim3 grid(a.segs, a.B * a.hq);
     const int mode = a.pg.block_table == nullptr ? 0 : (a.pool_bytes != 0 ? 1 : 2);
 #define SAGA_LAUNCH_GATHER(DD, M) hipLaunchKernelGGL((gather_kernel<DD, M>), grid, dim3(kBlock), 0, s, a)
-    if (D == 64) {
+    if (D == 32) {
+        if (mode == 0) SAGA_LAUNCH_GATHER(32, 0);
+        else if (mode == 1) SAGA_LAUNCH_GATHER(32, 1);
+        else SAGA_LAUNCH_GATHER(32, 2);
+    } else if (D == 64) {
         if (mode == 0) SAGA_LAUNCH_GATHER(64, 0);
         else if (mode == 1) SAGA_LAUNCH_GATHER(64, 1);
         else SAGA_LAUNCH_GATHER(64, 2);
@@ -656,7 +666,9 @@ hipError_t launch_gather(int D, const GatherArgs& a, hipStream_t s)
 hipError_t launch_combine(int D, const Partials& p, int rows, int parts, uint16_t* out,
                           int32_t* counts, hipStream_t s)
 {
-    if (D == 64)
+    if (D == 32)
+        hipLaunchKernelGGL(combine_kernel<32>, dim3(rows), dim3(kBlock), 0, s, p, parts, out, counts);
+    else if (D == 64)
         hipLaunchKernelGGL(combine_kernel<64>, dim3(rows), dim3(kBlock), 0, s, p, parts, out, counts);
     else
         hipLaunchKernelGGL(combine_kernel<128>, dim3(rows), dim3(kBlock), 0, s, p, parts, out, counts);

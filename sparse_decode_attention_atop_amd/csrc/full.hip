@@ -21,12 +21,12 @@ namespace saga {
 
 namespace {
 
-template <int D, int U, int MAXS>
+template <int DK, int DV, int U, int MAXS>
 __global__ __launch_bounds__(kBlock) void full_attn_kernel(FullArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int TR = 16 * U;            // rows per wave tile
-    constexpr int LPRV = D / 8;           // lanes per V row (16 bytes each)
+    constexpr int LPRV = DV / 8;          // lanes per V row (16 bytes each)
     constexpr int RPI = kWave / LPRV;     // V rows per load instruction
     constexpr int NV = TR / RPI;          // V loads per lane per tile
     const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -50,11 +50,11 @@ __global__ __launch_bounds__(kBlock) void full_attn_kernel(FullArgs a)
     float* alpha_l = P + TR * 16;                        // [16]
     float* m_l = alpha_l + 16;                           // [16]
     float* l_l = m_l + 16;                               // [16]
-    float* o_l = l_l + 16;                               // [MAXS][D]
+    float* o_l = l_l + 16;                               // [MAXS][DV]
 
-    const QFrag<D> qf = load_qfrag<D>(col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr);
-    const uint16_t* khead = a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
-    const uint16_t* vhead = a.v + ((int64_t)(b * a.hv + (ns > 0 ? vh : 0)) * a.cache_len) * D;
+    const QFrag<DK> qf = load_qfrag<DK>(col < Gk ? a.q + (int64_t)(qh0 + col) * DK : nullptr);
+    const uint16_t* khead = a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * DK;
+    const uint16_t* vhead = a.v + ((int64_t)(b * a.hv + (ns > 0 ? vh : 0)) * a.cache_len) * DV;
     const int vrow = lane / LPRV, vcol = 8 * (lane % LPRV);
 
     float m_run[4], l_part[4];
@@ -70,19 +70,19 @@ __global__ __launch_bounds__(kBlock) void full_attn_kernel(FullArgs a)
         for (int e = 0; e < 8; ++e) oacc[k][e] = 0.f;
 
     for (int64_t t0 = r0 + rs * TR; t0 < r1; t0 += rowsets * TR) {
-        KTile<D, U> kt;
-        load_ktile<D, U>(kt, khead, t0, r1);
+        KTile<DK, U> kt;
+        load_ktile<DK, U>(kt, khead, t0, r1);
         u32x4 vt[NV];
         if (ns > 0) {
 #pragma unroll
             for (int k = 0; k < NV; ++k) {
                 int64_t row = t0 + k * RPI + vrow;
                 row = row < r1 ? row : r1 - 1;
-                vt[k] = ld16(vhead + row * D + vcol);
+                vt[k] = ld16(vhead + row * DV + vcol);
             }
         }
         float s[U][4];
-        qk_tile<D, U>(qf, kt, a.scale, s);
+        qk_tile<DK, U>(qf, kt, a.scale, s);
 
         float alpha[4];
 #pragma unroll
@@ -166,14 +166,14 @@ __global__ __launch_bounds__(kBlock) void full_attn_kernel(FullArgs a)
         for (int k = 0; k < MAXS; ++k)
             if (k < ns) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) o_l[k * D + vcol + e] = oacc[k][e];
+                for (int e = 0; e < 8; ++e) o_l[k * DV + vcol + e] = oacc[k][e];
             }
     }
     __syncthreads();
 
     // Merge row sets in a fixed order.
-    for (int p = threadIdx.x; p < Gk * D; p += kBlock) {
-        const int h = p / D, e = p - h * D;
+    for (int p = threadIdx.x; p < Gk * DV; p += kBlock) {
+        const int h = p / DV, e = p - h * DV;
         const int vh_h = (i0 + h) / Gv;
         const int vsel_h = vh_h - i0 / Gv;
         const int k_h = h - (max(vh_h * Gv, i0) - i0);
@@ -189,12 +189,12 @@ __global__ __launch_bounds__(kBlock) void full_attn_kernel(FullArgs a)
             const float mw = base[TR * 16 + 16 + h];
             if (mw > -INFINITY) {
                 const float al = __expf(mw - M);
-                acc += al * base[TR * 16 + 48 + k_h * D + e];
+                acc += al * base[TR * 16 + 48 + k_h * DV + e];
                 l += al * base[TR * 16 + 32 + h];
             }
         }
         const int64_t idx = (int64_t)(qh0 + h) * a.chunks + chunk;
-        a.part.o[idx * D + e] = acc;
+        a.part.o[idx * DV + e] = acc;
         if (e == 0) {
             a.part.m[idx] = M;
             a.part.l[idx] = l;
@@ -203,26 +203,36 @@ __global__ __launch_bounds__(kBlock) void full_attn_kernel(FullArgs a)
     }
 }
 
-template <int D>
+template <int DK, int DV>
 hipError_t launch_full_d(int maxs, const FullArgs& a, hipStream_t s)
 {
     const dim3 grid(a.chunks, a.B * a.hk);
     const size_t lds = kWavesPerBlock * a.wave_lds;
-    constexpr int U = full_unroll(D);
+    constexpr int U = full_unroll(DK, DV);
     if (maxs <= 2)
-        hipLaunchKernelGGL((full_attn_kernel<D, U, 2>), grid, dim3(kBlock), lds, s, a);
+        hipLaunchKernelGGL((full_attn_kernel<DK, DV, U, 2>), grid, dim3(kBlock), lds, s, a);
     else if (maxs <= 4)
-        hipLaunchKernelGGL((full_attn_kernel<D, U, 4>), grid, dim3(kBlock), lds, s, a);
+        hipLaunchKernelGGL((full_attn_kernel<DK, DV, U, 4>), grid, dim3(kBlock), lds, s, a);
     else
-        hipLaunchKernelGGL((full_attn_kernel<D, U, 8>), grid, dim3(kBlock), lds, s, a);
+        hipLaunchKernelGGL((full_attn_kernel<DK, DV, U, 8>), grid, dim3(kBlock), lds, s, a);
     return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_full_dk(int DV, int maxs, const FullArgs& a, hipStream_t s)
+{
+    if (DV == 32) return launch_full_d<DK, 32>(maxs, a, s);
+    if (DV == 64) return launch_full_d<DK, 64>(maxs, a, s);
+    return launch_full_d<DK, 128>(maxs, a, s);
 }
 
 }  // namespace
 
-hipError_t launch_full(int D, int maxs, const FullArgs& a, hipStream_t s)
+hipError_t launch_full(int DK, int DV, int maxs, const FullArgs& a, hipStream_t s)
 {
-    return D == 64 ? launch_full_d<64>(maxs, a, s) : launch_full_d<128>(maxs, a, s);
+    if (DK == 32) return launch_full_dk<32>(DV, maxs, a, s);
+    if (DK == 64) return launch_full_dk<64>(DV, maxs, a, s);
+    return launch_full_dk<128>(DV, maxs, a, s);
 }
 
 }  // namespace saga

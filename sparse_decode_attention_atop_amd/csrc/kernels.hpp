@@ -11,20 +11,25 @@
 namespace saga {
 
 // Rows of one workgroup tile (4 waves x 16*U rows) per kernel family and
-// head_dim; chunk lengths are multiples of these.
-constexpr int decode_unroll(int D) { return D == 64 ? SAGA_STREAM_U64 : SAGA_STREAM_U128; }
+// key head_dim; chunk lengths are multiples of these.
+constexpr int decode_unroll(int D)
+{
+    return D == 32 ? SAGA_STREAM_U32 : (D == 64 ? SAGA_STREAM_U64 : SAGA_STREAM_U128);
+}
 constexpr int decode_block_rows(int D) { return kWavesPerBlock * 16 * decode_unroll(D); }
 // fp8 K: tiles of SAGA_STREAM_K8_UMUL times the rows of bf16 tiles.
 constexpr int decode_unroll_k8(int D) { return SAGA_STREAM_K8_UMUL * decode_unroll(D); }
 constexpr int decode_block_rows_k8(int D) { return kWavesPerBlock * 16 * decode_unroll_k8(D); }
-constexpr int full_unroll(int D) { return D == 64 ? 4 : 2; }
+// Dense kernel: 16-row groups per wave tile (the K tile and the V tile of the
+// same rows are in registers together).
+constexpr int full_unroll(int DK, int DV) { return (DK == 128 || DV == 128) ? 2 : 4; }
 
 // LDS bytes of one wave in the full-attention kernel:
-//   P[TR][16] fp32, alpha[16], m[16], l[16], o[MAXS][D]
-inline __host__ __device__ size_t full_wave_lds_bytes(int D, int maxs)
+//   P[TR][16] fp32, alpha[16], m[16], l[16], o[MAXS][DV]
+inline __host__ __device__ size_t full_wave_lds_bytes(int DK, int DV, int maxs)
 {
-    const int TR = 16 * full_unroll(D);
-    size_t b = (size_t)TR * 16 * 4 + 3 * 16 * 4 + (size_t)maxs * D * 4;
+    const int TR = 16 * full_unroll(DK, DV);
+    size_t b = (size_t)TR * 16 * 4 + 3 * 16 * 4 + (size_t)maxs * DV * 4;
     return (b + 15) & ~(size_t)15;
 }
 
@@ -212,7 +217,7 @@ hipError_t launch_combine(int D, const Partials& p, int rows, int parts, uint16_
                           int32_t* counts, hipStream_t s);
 hipError_t launch_sample(int D, const SampleArgs& a, hipStream_t s);
 hipError_t launch_refresh_final(int D, const FinalArgs& a, hipStream_t s);
-hipError_t launch_full(int D, int maxs, const FullArgs& a, hipStream_t s);
+hipError_t launch_full(int DK, int DV, int maxs, const FullArgs& a, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 
 }  // namespace saga

@@ -382,7 +382,11 @@ hipError_t launch_sample(int D, const SampleArgs& a, hipStream_t s)
     const int kind = a.pg.block_table != nullptr ? 1 : (a.k_scale != nullptr ? 2 : 0);
 #define SAGA_LAUNCH_SAMPLE(DD, PG, F8)                                                            \
     hipLaunchKernelGGL((sample_logits_kernel<DD, U, PG, F8>), grid, dim3(kBlock), 0, s, a)
-    if (D == 64) {
+    if (D == 32) {
+        if (kind == 2) return hipErrorInvalidValue;      // no fp8 K at head_dim 32 (the API rejects it)
+        if (kind == 1) SAGA_LAUNCH_SAMPLE(32, true, false);
+        else SAGA_LAUNCH_SAMPLE(32, false, false);
+    } else if (D == 64) {
         if (kind == 1) SAGA_LAUNCH_SAMPLE(64, true, false);
         else if (kind == 2) SAGA_LAUNCH_SAMPLE(64, false, true);
         else SAGA_LAUNCH_SAMPLE(64, false, false);
@@ -404,7 +408,11 @@ hipError_t launch_refresh_final(int D, const FinalArgs& a, hipStream_t s)
 #define SAGA_LAUNCH_FINAL(DD, PG, F8)                                                             \
     hipLaunchKernelGGL((refresh_final_kernel<DD, decode_unroll(DD), PG, F8>), dim3(a.B * a.hq),    \
                        dim3(kBlock), 0, s, a)
-    if (D == 64) {
+    if (D == 32) {
+        if (kind == 2) return hipErrorInvalidValue;      // no fp8 K at head_dim 32 (the API rejects it)
+        if (kind == 1) SAGA_LAUNCH_FINAL(32, true, false);
+        else SAGA_LAUNCH_FINAL(32, false, false);
+    } else if (D == 64) {
         if (kind == 1) SAGA_LAUNCH_FINAL(64, true, false);
         else if (kind == 2) SAGA_LAUNCH_FINAL(64, false, true);
         else SAGA_LAUNCH_FINAL(64, false, false);

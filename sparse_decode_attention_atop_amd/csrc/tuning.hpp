@@ -5,6 +5,9 @@
 #ifndef SAGA_STREAM_U64
 #define SAGA_STREAM_U64 1            // 16-row K groups per wave tile, head_dim 64
 #endif
+#ifndef SAGA_STREAM_U32
+#define SAGA_STREAM_U32 1            // same, head_dim 32
+#endif
 #ifndef SAGA_STREAM_U128
 #define SAGA_STREAM_U128 1           // same, head_dim 128
 #endif
@@ -19,6 +22,9 @@
 #endif
 #ifndef SAGA_TARGET_BLOCKS128
 #define SAGA_TARGET_BLOCKS128 512    // same, head_dim 128
+#endif
+#ifndef SAGA_TARGET_BLOCKS32
+#define SAGA_TARGET_BLOCKS32 1024    // same, head_dim 32 (64-byte rows, as fp8 at 64)
 #endif
 #ifndef SAGA_TARGET_BLOCKS64_K8
 #define SAGA_TARGET_BLOCKS64_K8 1024 // same with an fp8 K cache, head_dim 64

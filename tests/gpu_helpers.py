@@ -17,9 +17,10 @@ def bf16_to_f32(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy()
 
 
-def make_inputs(B, hq, hk, hv, d, rows, T, seed, device="cuda", q_scale=None, heavy=True):
-    """Seeded inputs via the workload generator (random shape, not a named config)."""
-    w = wl.Workload("adhoc", 900 + seed, B, hq, hk, hv, d, rows - T, 1, 1, T, 1)
+def make_inputs(B, hq, hk, hv, d, rows, T, seed, device="cuda", q_scale=None, heavy=True, dv=0):
+    """Seeded inputs via the workload generator (random shape, not a named config);
+    dv: value head dimension (0: same as d)."""
+    w = wl.Workload("adhoc", 900 + seed, B, hq, hk, hv, d, rows - T, 1, 1, T, 1, head_dim_v=dv)
     x = wl.make_layer(w, 0, device=device, heavy_hitters=heavy)
     return x["q"], x["K"], x["V"]
 
@@ -33,23 +34,24 @@ def run_atopn(q, K, V, ctx_steps, top_n, refresh_n, scale=1.0, logits_every_step
     """
     T, B, hq, d = q.shape
     hk, rows = K.shape[1], K.shape[2]
-    hv = V.shape[1]
+    hv, dv = V.shape[1], V.shape[3]
+    dvx = 0 if dv == d else dv
     dev = q.device
-    dims0 = saga.dims(B, hq, hk, hv, d, ctx_steps[0], rows, scale)
+    dims0 = saga.dims(B, hq, hk, hv, d, ctx_steps[0], rows, scale, head_dim_v=dvx)
     ws = saga.alloc_workspace(dims0, top_n, dev)
     tau = torch.empty(B, hq, dtype=torch.float32, device=dev)
     tau_scratch = torch.empty_like(tau)
     words = (rows + 31) // 32
     res = {"tau": [], "logits": [], "counts": [], "bitmap": [], "out": []}
     for t, ctx in enumerate(ctx_steps):
-        dm = saga.dims(B, hq, hk, hv, d, ctx, rows, scale)
+        dm = saga.dims(B, hq, hk, hv, d, ctx, rows, scale, head_dim_v=dvx)
         lg = torch.empty(B, hq, ctx, dtype=torch.float32, device=dev)
         if t % refresh_n == 0:
             saga.atopn_refresh_thresholds(dm, top_n, q[t], K, tau, ws, logits_debug=lg)
         elif logits_every_step:
             # Logits of a plain step, for checking; the kept thresholds are untouched.
             saga.atopn_refresh_thresholds(dm, top_n, q[t], K, tau_scratch, ws, logits_debug=lg)
-        out = torch.empty(B, hq, d, dtype=torch.bfloat16, device=dev)
+        out = torch.empty(B, hq, dv, dtype=torch.bfloat16, device=dev)
         cnt = torch.empty(B, hq, dtype=torch.int32, device=dev)
         bm = torch.empty(B, hq, words, dtype=torch.int32, device=dev)
         saga.saga_decode_step(dm, q[t], K, V, tau, out, ws, sel_counts=cnt, sel_bitmap_debug=bm)
@@ -70,14 +72,16 @@ def run_fused(q, K, V, ctx_steps, top_n, refresh_n, scale=1.0):
     """
     T, B, hq, d = q.shape
     hk, rows = K.shape[1], K.shape[2]
-    hv = V.shape[1]
+    hv, dv = V.shape[1], V.shape[3]
+    dvx = 0 if dv == d else dv
     dev = q.device
-    ws = saga.alloc_workspace(saga.dims(B, hq, hk, hv, d, ctx_steps[0], rows, scale), top_n, dev)
+    ws = saga.alloc_workspace(saga.dims(B, hq, hk, hv, d, ctx_steps[0], rows, scale, head_dim_v=dvx),
+                              top_n, dev)
     tau = torch.empty(B, hq, dtype=torch.float32, device=dev)
     res = {"tau": [], "counts": [], "out": []}
     for t, ctx in enumerate(ctx_steps):
-        dm = saga.dims(B, hq, hk, hv, d, ctx, rows, scale)
-        out = torch.empty(B, hq, d, dtype=torch.bfloat16, device=dev)
+        dm = saga.dims(B, hq, hk, hv, d, ctx, rows, scale, head_dim_v=dvx)
+        out = torch.empty(B, hq, dv, dtype=torch.bfloat16, device=dev)
         cnt = torch.empty(B, hq, dtype=torch.int32, device=dev)
         if t % refresh_n == 0:
             saga.atopn_refresh_decode_step(dm, top_n, q[t], K, V, tau, out, ws, sel_counts=cnt)

@@ -93,6 +93,24 @@ def count_rule_selection(s, N):
     return greater < N
 
 
+def rand_case_dkdv(seed, B, hq, hk, hv, dk, dv, rows, T=1):
+    """Random bf16 q/K/V bits with key dimension dk and value dimension dv."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(T, B, hq, dk, generator=g).to(torch.bfloat16)
+    K = torch.randn(B, hk, rows, dk, generator=g).to(torch.bfloat16)
+    V = torch.randn(B, hv, rows, dv, generator=g).to(torch.bfloat16)
+    u = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    return u(q), u(K), u(V)
+
+
+def mask_bitmap(mask, rows):
+    """bool [..][ctx] -> uint32 [..][ceil(rows/32)], bit j%32 of word j/32 = mask[j]."""
+    words = (rows + 31) // 32
+    full = np.zeros(mask.shape[:-1] + (words * 32,), dtype=np.uint8)
+    full[..., :mask.shape[-1]] = mask
+    return np.packbits(full, axis=-1, bitorder="little").view(np.uint32)
+
+
 def rand_e4m3(seed, B, hk, rows, d, pow2_scales):
     """Random E4M3 codes (never the NaN codes) and per-(b, key head) scales:
     distinct powers of two, or arbitrary positive values."""
@@ -352,6 +370,29 @@ def pin_e4m3k_reduces_to_bf16_cache():
     mb = oracle.masked(q[1], Kb, V, ctx[1], bm, 0.5)
     assert np.array_equal(m8[0], mb[0]) and np.array_equal(m8[1], mb[1]), "E4M3 masked"
     assert np.array_equal(m8[1], b["count"][1]), "masked count vs run count"
+
+
+def pin_key_and_value_dims_independent():
+    """d_k != d_v (the pages' Sigma-style (h_k, d_k) = (2, 32) against d_v = 64, and
+    the reverse): full, exact top-N, Atop-N at n = 1 and masked mode against torch's
+    scaled-dot-product attention, which takes separate key and value dimensions."""
+    for (B, hq, hk, hv, dk, dv, rows, N) in ((2, 8, 2, 4, 32, 64, 48, 6),
+                                             (1, 6, 1, 2, 64, 16, 70, 9)):
+        q, K, V = rand_case_dkdv(40 + dk, B, hq, hk, hv, dk, dv, rows, T=2)
+        ctx = rows - 5
+        full = oracle.full(q[0], K, V, ctx, 0.5)
+        assert full.shape == (B, hq, dv)
+        assert_close(full, sdpa_ref(q[0], K, V, ctx, 0.5), 1e-12, "full, d_k != d_v")
+        m = topk_mask(lib_logits(q[0], K, ctx, 0.5), N)
+        want = sdpa_ref(q[0], K, V, ctx, 0.5, m)
+        assert_close(oracle.exact_topn(q[0], K, V, ctx, N, 0.5), want, 1e-12, "exact top-N, d_k != d_v")
+        r = oracle.atopn_run(q, K, V, [ctx, ctx + 1], N, 1, 0.5, want_sel=True)
+        assert_close(r["out"][0], want, 1e-12, "Atop-N n=1, d_k != d_v")
+        m1 = topk_mask(lib_logits(q[1], K, ctx + 1, 0.5), N)
+        assert_close(r["out"][1], sdpa_ref(q[1], K, V, ctx + 1, 0.5, m1), 1e-12, "step 1")
+        o, cnt = oracle.masked(q[0], K, V, ctx, mask_bitmap(m, rows), 0.5)
+        assert_close(o, want, 1e-12, "masked, d_k != d_v")
+        assert (cnt == N).all()
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -117,7 +117,7 @@ def test_dims_errors_every_entry_point(bad, code):
 
 def test_reserved_fields_and_scale():
     d = good_dims()
-    d.reserved = 1
+    d.reserved2 = 1.0
     assert call_decode(d, 1 << 40) == INVALID
     d = good_dims()
     d.scale = float("nan")
@@ -151,6 +151,26 @@ def test_misaligned_pointers():
     assert call_full(good_dims(), 1 << 40, v=odd) == INVALID
     assert call_fused(good_dims(), 8, 1 << 40, v=odd) == INVALID
     assert call_decode(good_dims(), 1 << 40, counts=ctypes.c_void_p((1 << 20) + 2)) == INVALID
+
+
+def test_key_and_value_head_dims():
+    # d_k and d_v are independent: 32, 64 or 128 each; 0 means d_v = d_k.
+    for dk in (32, 64, 128):
+        for dv in (0, 32, 64, 128):
+            d = good_dims(head_dim=dk, head_dim_v=dv)
+            assert saga.saga_workspace_bytes(d, 8) > 0, (dk, dv)
+            assert call_decode(d, 8) == SMALL, (dk, dv)        # valid dims: stops at the workspace
+            assert call_full(d, 8) == SMALL, (dk, dv)
+    assert call_decode(good_dims(head_dim_v=-1), 1 << 40) == INVALID
+    assert call_decode(good_dims(head_dim_v=96), 1 << 40) == UNSUPPORTED
+    assert call_refresh(good_dims(head_dim=48), 8, 1 << 40) == UNSUPPORTED
+    # partials are sized by d_v: a larger value dimension needs a larger workspace
+    small = saga.saga_workspace_bytes(good_dims(head_dim=128, head_dim_v=32), 8)
+    large = saga.saga_workspace_bytes(good_dims(head_dim=32, head_dim_v=128), 8)
+    assert large > small
+    # one head must stay under 2 GiB for the larger of the two dimensions
+    assert call_decode(good_dims(head_dim=32, head_dim_v=128, cache_len=1 << 23, ctx_len=10),
+                       1 << 40) == UNSUPPORTED
 
 
 def test_top_n_and_workspace_errors():
@@ -263,6 +283,7 @@ def test_fp8k_argument_checks(kind):
     assert call_fp8k(kind, d, 1 << 40, k8=ctypes.c_void_p((1 << 20) + 8)) == INVALID
     assert call_fp8k(kind, good_dims(ctx_len=0), 1 << 40) == INVALID
     assert call_fp8k(kind, good_dims(head_dim=96), 1 << 40) == UNSUPPORTED
+    assert call_fp8k(kind, good_dims(head_dim=32), 1 << 40) == UNSUPPORTED   # fp8 needs d_k >= 64
     assert call_fp8k(kind, d, need - 1) == SMALL         # same workspace as the bf16 calls
     if kind != "decode":
         assert call_fp8k(kind, d, 1 << 40, top_n=0) == INVALID

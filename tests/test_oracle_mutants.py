@@ -24,26 +24,32 @@ MUTANTS = [
      "key_at(Kh, j * d + (d - 1 - c));\n        s[j]"),
     ("dropped_scale", "s[j] = scale * acc;", "s[j] = acc;"),
     ("key_head_map", "const key_head Kh = key_head_of(K, b, hk, i / Gk, cache_len, d);\n"
-     "        const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, d);\n"
+     "        const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, dv);\n"
      "        double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);",
      "const key_head Kh = key_head_of(K, b, hk, i % hk, cache_len, d);\n"
-     "        const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, d);\n"
+     "        const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, dv);\n"
      "        double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);"),
-    ("value_head_map", "const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, d);\n"
+    ("value_head_map", "const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, dv);\n"
      "        double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);",
-     "const uint16_t* Vh = cache_head(V, b, hv, i / Gk % hv, cache_len, d);\n"
+     "const uint16_t* Vh = cache_head(V, b, hv, i / Gk % hv, cache_len, dv);\n"
      "        double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);"),
+    ("value_head_stride_is_key_dim", "const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, dv);\n"
+     "        double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);",
+     "const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, d);\n"
+     "        double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);"),
+    ("output_stride_is_key_dim", "count[row] = attend_selected(s, S, n, Vh, dv, out + row * dv);",
+     "count[row] = attend_selected(s, S, n, Vh, dv, out + row * d);"),
     ("threshold_rank_off_by_one", "double t = tmp[N - 1];", "double t = tmp[N];"),
     ("sort_ascending", "return (x < y) - (x > y);", "return (x > y) - (x < y);"),
     ("strict_comparison", "S[j] = (s[j] >= threshold);", "S[j] = (s[j] > threshold);"),
     ("refresh_phase", "if (t % refresh_n == 0) threshold", "if ((t + 1) % refresh_n == 0) threshold"),
     ("refresh_never", "if (t % refresh_n == 0) threshold", "if (t == 0) threshold"),
-    ("softmax_sign", "double w = exp(s[j] - m);\n        denom += w;\n        for (int c = 0; c < d; ++c) out[c]",
-     "double w = exp(m - s[j]);\n        denom += w;\n        for (int c = 0; c < d; ++c) out[c]"),
-    ("dropped_normalisation", "for (int c = 0; c < d; ++c) out[c] /= denom;\n    return count;",
-     "for (int c = 0; c < d; ++c) out[c] /= 1.0;\n    return count;"),
-    ("value_row_index", "out[c] += w * bf16_to_double(Vh[j * d + c]);\n    }\n    for (int c = 0; c < d; ++c) out[c] /= denom;\n    return count;",
-     "out[c] += w * bf16_to_double(Vh[(ctx - 1 - j) * d + c]);\n    }\n    for (int c = 0; c < d; ++c) out[c] /= denom;\n    return count;"),
+    ("softmax_sign", "double w = exp(s[j] - m);\n        denom += w;\n        for (int c = 0; c < dv; ++c) out[c]",
+     "double w = exp(m - s[j]);\n        denom += w;\n        for (int c = 0; c < dv; ++c) out[c]"),
+    ("dropped_normalisation", "for (int c = 0; c < dv; ++c) out[c] /= denom;\n    return count;",
+     "for (int c = 0; c < dv; ++c) out[c] /= 1.0;\n    return count;"),
+    ("value_row_index", "out[c] += w * bf16_to_double(Vh[j * dv + c]);\n    }\n    for (int c = 0; c < dv; ++c) out[c] /= denom;\n    return count;",
+     "out[c] += w * bf16_to_double(Vh[(ctx - 1 - j) * dv + c]);\n    }\n    for (int c = 0; c < dv; ++c) out[c] /= denom;\n    return count;"),
     ("empty_selection_not_zero", "if (count == 0) return 0;", "if (count == 0) { out[0] = 1.0; return 0; }"),
     ("exact_topn_keeps_one_more", "const int64_t keep = top_n < ctx ? top_n : ctx;",
      "const int64_t keep = top_n < ctx ? top_n + 1 : ctx;"),
