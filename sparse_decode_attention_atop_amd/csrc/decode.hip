@@ -536,7 +536,8 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(Partials p, int parts, 
     constexpr int PL = kBlock / D;
     __shared__ float red[kBlock];
     __shared__ float lsh[PL];
-    __shared__ int32_t csh[kBlock];
+    __shared__ float wred[kWavesPerBlock];
+    __shared__ int32_t cred[kWavesPerBlock];
     const int64_t bh = blockIdx.x;
     const int t = threadIdx.x, pl = t / D, e = t - pl * D;
     const float* pm = p.m + bh * parts;
@@ -550,26 +551,25 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(Partials p, int parts, 
         M = fmaxf(M, pm[c]);
         n += pc[c];
     }
-    red[t] = M;
-    csh[t] = n;
-    __syncthreads();
-    for (int off = kBlock / 2; off > 0; off >>= 1) {
-        if (t < off) {
-            red[t] = fmaxf(red[t], red[t + off]);
-            csh[t] += csh[t + off];
-        }
-        __syncthreads();
-    }
-    M = red[0];
-    n = csh[0];
-    __syncthreads();
+    // This thread's first partial, loaded before the reductions need M.
+    const bool have0 = pl < parts;
+    const float w0 = have0 ? pm[pl] : -INFINITY;
+    const float o0 = have0 ? po[(int64_t)pl * D + e] : 0.f;
+    const float l0 = have0 ? pl_[pl] : 0.f;
+    M = block_max(M, wred);
+    n = block_sum(n, cred);
     if (M == -INFINITY) {                                  // nothing selected anywhere
         if (t < D) out[bh * D + t] = 0;
         if (counts && t == 0) counts[bh] = n;
         return;
     }
     float acc = 0.f, l = 0.f;
-    int c = pl;
+    if (have0) {
+        const float a = __expf(w0 - M);                    // -inf partials weigh 0
+        acc += a * o0;
+        l += a * l0;
+    }
+    int c = pl + PL;
     for (; c + 3 * PL < parts; c += 4 * PL) {
         float w[4], ov[4], lv[4];
 #pragma unroll
