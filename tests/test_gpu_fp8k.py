@@ -7,10 +7,10 @@
   leaves attention unchanged and makes the bf16 calls sum in that order.  So
   logits, thresholds, counts and selection bitmaps must be bit-identical to
   the bf16 calls run on the dequantized cache with q and K so reordered --
-  and the bf16 parity tests tie those to the oracle.  The fp8 stream's tiles
-  have twice the rows, so the selected entries reach the gather in another
-  order and its fp32 sums round differently: outputs must be equal or one
-  bf16 step apart.  Also at
+  and the bf16 parity tests tie those to the oracle.  The fp8 stream's tile
+  and launch sizes are tuned on their own (they may differ from bf16's), so
+  the selected entries can reach the gather in another order and its fp32
+  sums round differently: outputs must be equal or one bf16 step apart.  Also at
   the Llama-like 128K batch-16 shape the benchmark times, and on the
   recompute path of the refresh.
 * General scales (amax / 448 per head): logits within the logit bar of the
