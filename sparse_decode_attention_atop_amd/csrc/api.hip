@@ -83,14 +83,26 @@ Chunking split_rows(int64_t ctx, int64_t pairs, int64_t block_rows, int64_t targ
     return {(int)((ctx + rows - 1) / rows), rows};
 }
 
-// Chunking of the K stream (stream-select kernel) for one call.  Chunks are
-// whole tile pairs (the kernel streams pairs), so with pages of kPageQuantum
-// rows no pair straddles two pages.  An fp8 K cache (k8) streams tiles of
-// twice the rows.
-Chunking plan_chunks(int64_t ctx, int64_t pairs, int head_dim, int max_chunks, bool k8)
+// Chunking of the K stream (stream-select kernel) for one call.  The chunk
+// count comes from a plan in whole tile pairs (the kernel streams pairs).
+// Paged caches keep those pair-sized chunks, so with pages of kPageQuantum
+// rows no pair starts in one page and ends in the next.  Contiguous caches
+// keep the count but round the rows per chunk to whole tiles only: a pair's
+// second tile past the chunk end reads zeros and selects nothing, and the
+// last chunk is then about as long as the others (131073 rows in 12 chunks:
+// 11 of 10944 rows and one of 10689, rather than 11 of 11008 and one of
+// 9985).  Never more rows per chunk than the pair plan.
+Chunking plan_chunks(int64_t ctx, int64_t pairs, int head_dim, int max_chunks, bool k8,
+                     bool paged)
 {
     const int64_t block = k8 ? decode_block_rows_k8(head_dim) : decode_block_rows(head_dim);
-    return split_rows(ctx, pairs, 2 * block, target_blocks(head_dim, k8), max_chunks);
+    Chunking c = split_rows(ctx, pairs, 2 * block, target_blocks(head_dim, k8), max_chunks);
+    if (!paged) {
+        int64_t rows = (ctx + c.chunks - 1) / c.chunks;
+        rows = (rows + block - 1) / block * block;
+        c = {(int)((ctx + rows - 1) / rows), rows};
+    }
+    return c;
 }
 
 // Workspace layout (byte offsets), identical for every ctx_len <= cache_len.
@@ -117,8 +129,9 @@ Layout make_layout(const saga_dims* d)
     int64_t top_rows = 0;
     for (const bool k8 : {false, true}) {
         const int64_t br = 2 * (k8 ? decode_block_rows_k8(d->head_dim) : decode_block_rows(d->head_dim));
+        // The paged plan: its chunks are at least as long as the contiguous one's.
         const Chunking top = plan_chunks(d->cache_len, (int64_t)d->batch * d->h_k, d->head_dim,
-                                         L.max_chunks, k8);
+                                         L.max_chunks, k8, true);
         const int64_t r = top.rows > br ? top.rows : br;
         if (r > top_rows) top_rows = r;
     }
@@ -346,7 +359,8 @@ int enqueue_decode(const saga_dims* dims, const Layout& L, const void* q_dev,
         if (st != SAGA_OK) return st;
     }
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
-                                    D, L.max_chunks, rm.k_scale != nullptr);
+                                    D, L.max_chunks, rm.k_scale != nullptr,
+                                    rm.pg.block_table != nullptr);
     SelectStreamArgs a =
         stream_args(dims, L, ch, q_dev, k_cache_dev, thresholds_dev, workspace_dev, rm);
     a.bitmap = sel_bitmap_debug_dev;
@@ -393,7 +407,8 @@ int do_refresh(const saga_dims* dims, const RowModel& rm, int32_t top_n, const v
     const int D = dims->head_dim;
     const int rows = dims->batch * dims->h_q;
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
-                                    D, L.max_chunks, rm.k_scale != nullptr);
+                                    D, L.max_chunks, rm.k_scale != nullptr,
+                                    rm.pg.block_table != nullptr);
     int st;
     if ((int64_t)top_n >= dims->ctx_len) {
         // N >= ctx (of every sequence): every entry is kept, tau = -inf.  The
@@ -459,7 +474,8 @@ int do_refresh_decode(const saga_dims* dims, const RowModel& rm, int32_t top_n,
                               sel_counts_dev, nullptr, workspace_dev, s, rm);
     }
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
-                                    D, L.max_chunks, rm.k_scale != nullptr);
+                                    D, L.max_chunks, rm.k_scale != nullptr,
+                                    rm.pg.block_table != nullptr);
     uint32_t* flags = reinterpret_cast<uint32_t*>(w + L.flags);
     st = enqueue_refresh(dims, top_n, q_dev, k_dev, thresholds_dev, nullptr, workspace_dev,
                          L, ch, s, flags, rm);

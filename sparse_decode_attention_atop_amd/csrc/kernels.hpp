@@ -56,7 +56,7 @@ constexpr int gather_target_blocks(int head_dim)
 {
     return head_dim == 128 ? SAGA_GATHER_BLOCKS128 : SAGA_GATHER_BLOCKS64;
 }
-constexpr int kGatherMaxSegs = 16;
+constexpr int kGatherMaxSegs = SAGA_GATHER_MAX_SEGS;
 constexpr int kGatherStage = 1024;   // entries a gather workgroup stages per round
 
 // Storage of selection list lid = (b*h_q + i) * nl + chunk*4 + wave (nl lists

@@ -32,6 +32,9 @@
 #ifndef SAGA_TARGET_BLOCKS128_K8
 #define SAGA_TARGET_BLOCKS128_K8 512 // same with an fp8 K cache, head_dim 128
 #endif
+#ifndef SAGA_GATHER_MAX_SEGS
+#define SAGA_GATHER_MAX_SEGS 16      // most gather workgroups per (b, query head)
+#endif
 #ifndef SAGA_FULL_BLOCKS
 #define SAGA_FULL_BLOCKS 512         // workgroups per dense (full-attention) launch
 #endif
