@@ -293,46 +293,6 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
     }
 }
 
-// Block-wide (256 threads) reductions and scan.  `red` holds one value per wave.
-__device__ float block_max(float v, float* red)
-{
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    if (lane_id() == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
-    return v;
-}
-
-__device__ int32_t block_sum(int32_t v, int32_t* red)
-{
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    if (lane_id() == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    v = red[0] + red[1] + red[2] + red[3];
-    __syncthreads();
-    return v;
-}
-
-// Inclusive prefix sum over the block in thread order.
-__device__ int32_t block_scan(int32_t v, int32_t* red)
-{
-    const int lane = lane_id();
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int32_t u = __shfl_up(v, off);
-        if (lane >= off) v += u;
-    }
-    if (lane == kWave - 1) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    const int w = threadIdx.x >> 6;
-    int32_t add = 0;
-#pragma unroll
-    for (int k = 0; k < kWavesPerBlock - 1; ++k) add += k < w ? red[k] : 0;
-    __syncthreads();
-    return v + add;
-}
-
 // Gather kernel: grid.x = segment, grid.y = (b, query head).  The segments of
 // a head split its selected entries (the concatenation of all its lists, in
 // list order) into equal ranges, so a head whose selection grew between

@@ -10,14 +10,16 @@
 // Pipeline (all on the caller's stream; one pass over the K cache):
 //   1. sample_logits_kernel  logits of a sample of at most kSampleMax rows per
 //                            (b, query head): evenly spaced 16-row blocks.
-//   2. pivot_kernel          per row: the k-th largest sample logit (LDS radix
-//                            select), with k chosen so that the pivot p lies
-//                            below tau with overwhelming probability.
+//   2. pivot_kernel          per row: the k-th largest sample logit (radix
+//                            select on keys held in registers), with k chosen
+//                            so that the pivot p lies below tau with
+//                            overwhelming probability.
 //   3. select_stream_kernel  (decode.hip) with p as the threshold: every logit
 //                            >= p goes to the per-(row, chunk, wave) lists.
 //   4. refresh_final_kernel  per row: if the lists hold at least N entries,
 //                            tau is the N-th largest of them (then every entry
-//                            >= tau is in the lists; LDS radix select).
+//                            >= tau is in the lists; radix select on the
+//                            candidates held in registers).
 //                            Otherwise -- or if they are too many to stage --
 //                            the workgroup recomputes the row's logits with the
 //                            same QK tile and radix-selects over all of them.
@@ -47,15 +49,8 @@ __device__ void find_rank_bucket(const uint32_t* hist, uint32_t rank, uint32_t* 
         c[k] = hist[BINS - 1 - PER * t - k];
         sum += c[k];
     }
-    scan[t] = sum;
-    __syncthreads();
-    for (int off = 1; off < kBlock; off <<= 1) {
-        const uint32_t v = t >= off ? scan[t - off] : 0u;
-        __syncthreads();
-        scan[t] += v;
-        __syncthreads();
-    }
-    uint32_t above = scan[t] - sum;
+    // Counts of one row stay below 2^31, so the signed scan is exact.
+    uint32_t above = (uint32_t)block_scan((int32_t)sum, reinterpret_cast<int32_t*>(scan)) - sum;
     if (above < rank && above + sum >= rank) {
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
@@ -84,32 +79,107 @@ __device__ __forceinline__ uint32_t prefix_mask(int pass)
     return pass == 0 ? 0u : (pass == 1 ? 0xffe00000u : 0xfffffc00u);
 }
 
+// Exclusive max-scan over the block in thread order (0 before thread 0).
+__device__ __forceinline__ uint32_t block_scan_max_excl(uint32_t v, uint32_t* red)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t u = __shfl_up(v, off);
+        if (lane >= off) v = v > u ? v : u;
+    }
+    if (lane == kWave - 1) red[threadIdx.x >> 6] = v;
+    const uint32_t below = __shfl_up(v, 1);
+    __syncthreads();
+    const int w = threadIdx.x >> 6;
+    uint32_t x = lane > 0 ? below : 0u;
+#pragma unroll
+    for (int k = 0; k < kWavesPerBlock - 1; ++k)
+        if (k < w && red[k] > x) x = red[k];
+    __syncthreads();
+    return x;
+}
+
+// Histogram width of the register-resident select: 12-bit digits.
+constexpr int kRegDigit = 12;
+constexpr int kRegBins = 1 << kRegDigit;
+static_assert(kRegBins >= kHistBins, "one histogram serves both selects");
+
 struct SelectLds {
-    uint32_t hist[kHistBins];
+    alignas(16) uint32_t hist[kRegBins];
     uint32_t scan[kBlock];
     uint32_t result[3];
 };
 
-// The rank-th largest of n keys held in LDS (1 <= rank <= n).
-__device__ uint32_t lds_radix_select(const uint32_t* keys, uint32_t n, uint32_t rank, SelectLds& w)
+// The rank-th largest (1 <= rank <= n) of n keys held in registers by the
+// block: key j of thread t is item t + j * kBlock, valid below n.  A radix
+// select on u = key - (smallest key), in digits of up to 12 bits from the top
+// bit of the largest u down.  Counting from the range rather than from the
+// key's sign and exponent spreads the keys over the bins from the first pass
+// (few LDS atomics on one bin), and a range below 2^24 takes two passes.
+template <int KPT>
+__device__ uint32_t reg_radix_select(const uint32_t (&kv)[KPT], uint32_t n, uint32_t rank,
+                                     SelectLds& w)
 {
-    uint32_t prefix = 0u;
-    for (int pass = 0; pass < 3; ++pass) {
-        const int sh = digit_shift(pass);
-        const uint32_t dm = digit_mask(pass), pm = prefix_mask(pass);
-        for (int k = threadIdx.x; k < kHistBins; k += kBlock) w.hist[k] = 0u;
+    const int t = threadIdx.x;
+    uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        if (j * kBlock >= n) break;                   // block-uniform: no key left
+        if (t + j * kBlock < n) {
+            lo = kv[j] < lo ? kv[j] : lo;
+            hi = kv[j] > hi ? kv[j] : hi;
+        }
+    }
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        const uint32_t a = __shfl_xor(lo, off), b = __shfl_xor(hi, off);
+        lo = a < lo ? a : lo;
+        hi = b > hi ? b : hi;
+    }
+    if (lane_id() == 0) {
+        w.scan[t / kWave] = lo;
+        w.scan[kWavesPerBlock + t / kWave] = hi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kWavesPerBlock; ++k) {
+        lo = w.scan[k] < lo ? w.scan[k] : lo;
+        hi = w.scan[kWavesPerBlock + k] > hi ? w.scan[kWavesPerBlock + k] : hi;
+    }
+    __syncthreads();
+    const uint32_t range = hi - lo;
+    if (range == 0u) return lo;                       // every key is the same
+    const int bits = 32 - __clz(range);
+    int s = bits > kRegDigit ? bits - kRegDigit : 0;  // lowest bit of this pass's digit
+    int d = bits - s;                                 // its width (1..12)
+    int sp = 0;                                       // lowest bit of the digits already chosen
+    bool first = true;
+    uint32_t sel = 0u;                                // u >> sp of the answer, once chosen
+    for (;;) {
+#pragma unroll
+        for (int k = 0; k < kRegBins / (4 * kBlock); ++k)
+            reinterpret_cast<uint4*>(w.hist)[t + k * kBlock] = make_uint4(0u, 0u, 0u, 0u);
         __syncthreads();
-        for (uint32_t k = threadIdx.x; k < n; k += kBlock) {
-            const uint32_t key = keys[k];
-            if ((key & pm) == prefix) atomicAdd(&w.hist[(key >> sh) & dm], 1u);
+        const uint32_t dm = (1u << d) - 1u;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            if (j * kBlock >= n) break;               // block-uniform: no key left
+            const uint32_t u = kv[j] - lo;
+            if (t + j * kBlock < n && (first || (u >> sp) == sel))
+                atomicAdd(&w.hist[(u >> s) & dm], 1u);
         }
         __syncthreads();
         uint32_t bin, rin, cnt;
-        find_rank_bucket<kHistBins>(w.hist, rank, w.scan, w.result, &bin, &rin, &cnt);
-        prefix |= bin << sh;
+        find_rank_bucket<kRegBins>(w.hist, rank, w.scan, w.result, &bin, &rin, &cnt);
+        sel = first ? bin : (sel << d) | bin;
         rank = rin;
+        if (s == 0) break;
+        first = false;
+        sp = s;
+        d = s > kRegDigit ? kRegDigit : s;
+        s -= d;
     }
-    return prefix;
+    return lo + sel;
 }
 
 // Logits of sampled rows for every query head of key head g.  The sample is
@@ -177,7 +247,6 @@ __global__ __launch_bounds__(kBlock) void sample_logits_kernel(SampleArgs a)
 // pivot[row] = the k-th largest of the row's m sample logits.
 __global__ __launch_bounds__(kBlock) void pivot_kernel(SampleArgs a)
 {
-    __shared__ uint32_t keys[kSampleMax];
     __shared__ SelectLds w;
     const int row = blockIdx.x;
     const float* s = a.sample + (int64_t)row * kSampleMax;
@@ -212,9 +281,14 @@ __global__ __launch_bounds__(kBlock) void pivot_kernel(SampleArgs a)
             rank = (int)(r < (double)mb ? r : (double)mb);
         }
     }
-    for (int k = threadIdx.x; k < a.m; k += kBlock) keys[k] = float_key(s[k]);
-    __syncthreads();
-    const uint32_t key = lds_radix_select(keys, (uint32_t)a.m, (uint32_t)rank, w);
+    constexpr int KPT = kSampleMax / kBlock;
+    uint32_t kv[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int k = threadIdx.x + j * kBlock;
+        kv[j] = k < a.m ? float_key(s[k]) : 0u;
+    }
+    const uint32_t key = reg_radix_select<KPT>(kv, (uint32_t)a.m, (uint32_t)rank, w);
     if (threadIdx.x == 0) {
         a.pivot[row] = all ? -INFINITY : key_float(key);
         if (a.group_flags) {
@@ -297,7 +371,7 @@ template <int D, int U, bool PAGED, bool FP8>
 __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
 {
     __shared__ int32_t pre[kMaxListsPerRow + 1];
-    __shared__ uint32_t keys[kFinalStage];
+    __shared__ uint32_t own[kFinalStage];
     __shared__ SelectLds w;
     const int row = blockIdx.x, t = threadIdx.x;
     const int64_t ctx = head_ctx(a.pg, a.lq, row / a.hq, row % a.hq, a.ctx);
@@ -318,18 +392,11 @@ __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
         c[k] = l < nl ? a.list_count[lbase + l] : 0;
         sum += c[k];
     }
-    uint32_t* scan = w.scan;
-    scan[t] = (uint32_t)sum;
-    __syncthreads();
-    for (int off = 1; off < kBlock; off <<= 1) {
-        const uint32_t v = t >= off ? scan[t - off] : 0u;
-        __syncthreads();
-        scan[t] += v;
-        __syncthreads();
-    }
-    int32_t run = (int32_t)scan[t] - sum;
+    int32_t run = block_scan(sum, reinterpret_cast<int32_t*>(w.scan)) - sum;
+    int32_t first[PER];                  // first entry of each of this thread's lists
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
+        first[k] = run;
         pre[t * PER + k] = run;
         run += c[k];
     }
@@ -339,28 +406,58 @@ __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
 
     uint32_t key;
     if (total >= a.top_n && total <= (uint32_t)kFinalStage) {
-        // Stage the candidate keys, 8 loads in flight per thread.
-        for (uint32_t E0 = t; E0 < total; E0 += 8 * kBlock) {
-            uint2 ent[8];
+        // The list of every entry, with no search: each non-empty list marks
+        // its first entry with its index, and an inclusive max-scan over the
+        // marks (runs of `per` entries per thread) carries it to the entries
+        // that follow.
+        for (uint32_t E = t; E < total; E += kBlock) own[E] = 0u;
+        __syncthreads();
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const uint32_t E = E0 + k * kBlock;
-                if (E < total) {
-                    int lo = 0, hi = nl - 1;
-                    while (lo < hi) {
-                        const int mid = (lo + hi + 1) >> 1;
-                        if ((uint32_t)pre[mid] <= E) lo = mid;
-                        else hi = mid - 1;
-                    }
-                    ent[k] = a.entries[list_index(lbase + lo, (uint32_t)(E - pre[lo]), capw, a.overflow_at)];
-                }
-            }
+        for (int k = 0; k < PER; ++k)
+            if (c[k] > 0) own[first[k]] = (uint32_t)(t * PER + k);
+        __syncthreads();
+        constexpr int KPT = kFinalStage / kBlock;
+        const uint32_t per = (total + kBlock - 1) / kBlock;   // <= KPT
+        const uint32_t r0 = min(t * per, total), r1 = min(r0 + per, total);
+        uint32_t mk[KPT];
+        uint32_t m = 0u;
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (E0 + k * kBlock < total) keys[E0 + k * kBlock] = float_key(__uint_as_float(ent[k].y));
+        for (int j = 0; j < KPT; ++j) {
+            if ((uint32_t)j >= per) break;                   // block-uniform
+            mk[j] = r0 + j < r1 ? own[r0 + j] : 0u;
+            m = max(m, mk[j]);
+        }
+        uint32_t runmax = block_scan_max_excl(m, w.scan);
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            if ((uint32_t)j >= per) break;
+            runmax = max(runmax, mk[j]);
+            if (r0 + j < r1) own[r0 + j] = runmax;
         }
         __syncthreads();
-        key = lds_radix_select(keys, total, a.top_n, w);
+        // Load the candidates into registers (coalesced: entry t + k * kBlock
+        // of thread t).  No branches: a slot past the end reads the last
+        // entry again and is masked by the select, so every LDS read and
+        // load is issued before any of them is waited for.
+        uint32_t l[KPT], off[KPT], kv[KPT];
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            if (k * kBlock >= (int)total) break;             // block-uniform
+            const uint32_t E = t + k * kBlock;
+            off[k] = E < total ? E : total - 1;
+            l[k] = own[off[k]];
+        }
+#pragma unroll
+        for (int k = 0; k < KPT; ++k)
+            if (k * kBlock < (int)total) off[k] -= (uint32_t)pre[l[k]];
+#pragma unroll
+        for (int k = 0; k < KPT; ++k)
+            if (k * kBlock < (int)total)
+                kv[k] = a.entries[list_index(lbase + l[k], off[k], capw, a.overflow_at)].y;
+#pragma unroll
+        for (int k = 0; k < KPT; ++k)
+            if (k * kBlock < (int)total) kv[k] = float_key(__uint_as_float(kv[k]));
+        key = reg_radix_select<KPT>(kv, total, a.top_n, w);
     } else {
         key = select_by_recompute<D, U, PAGED, FP8>(a, row, ctx, w);
         // The lists miss entries of this row: a fused decode must re-stream its group.
