@@ -332,15 +332,23 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
     const int64_t capw = a.rows_per_chunk / kWavesPerBlock;
     const int64_t lbase = (int64_t)bi * nl;
 
-    // List lengths (prefix) and the head's largest selected logit.
+    // List lengths (prefix) and the head's largest selected logit.  The
+    // loads are unconditional (lists past nl read the last list again and are
+    // masked after), so all of them are in flight before the first wait.
     int32_t c[PER], sum = 0;
-    float mx = -INFINITY;
+    float lm[PER], mx = -INFINITY;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-        const int l = t * PER + k;
-        c[k] = l < nl ? a.list_count[lbase + l] : 0;
+        const int l = t * PER + k < nl ? t * PER + k : nl - 1;
+        c[k] = a.list_count[lbase + l];
+        lm[k] = a.list_max[lbase + l];
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const bool in = t * PER + k < nl;
+        c[k] = in ? c[k] : 0;
         sum += c[k];
-        if (l < nl) mx = fmaxf(mx, a.list_max[lbase + l]);
+        mx = fmaxf(mx, in ? lm[k] : -INFINITY);
     }
     const float M = block_max(mx, reinterpret_cast<float*>(red));
     int32_t run = block_scan(sum, red) - sum;
@@ -371,21 +379,32 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
 
     for (int32_t base = e_begin; base < e_end; base += CAPL) {
         const int n = min(CAPL, e_end - base);
+        // Thread t stages entries EPT*t .. EPT*t + EPT-1 of this round: one
+        // binary search over the list offsets for the first, a forward walk
+        // for the rest.  Slots past n take entry n-1 again (masked below), so
+        // the loads carry no branch and all are in flight before any is used.
         int lo[EPT];
-        uint2 ent[EPT];
-#pragma unroll
-        for (int k = 0; k < EPT; ++k) {                 // all entry loads before any use
-            const int32_t E = base + t + k * kBlock;
+        uint32_t in_list[EPT];
+        {
+            const int32_t E0 = base + min(EPT * t, n - 1);
             int l0 = 0, hi = nl - 1;
             while (l0 < hi) {
                 const int mid = (l0 + hi + 1) >> 1;
-                if (pre[mid] <= E) l0 = mid;
+                if (pre[mid] <= E0) l0 = mid;
                 else hi = mid - 1;
             }
-            lo[k] = l0;
-            ent[k] = t + k * kBlock < n ? a.entries[list_index(lbase + l0, (uint32_t)(E - pre[l0]), capw, a.overflow_at)]
-                                        : uint2{0u, 0xff800000u};
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) {
+                const int32_t E = base + min(EPT * t + k, n - 1);
+                while (pre[l0 + 1] <= E) ++l0;          // skips empty lists; stops below nl
+                lo[k] = l0;
+                in_list[k] = (uint32_t)(E - pre[l0]);
+            }
         }
+        uint2 ent[EPT];
+#pragma unroll
+        for (int k = 0; k < EPT; ++k)
+            ent[k] = a.entries[list_index(lbase + lo[k], in_list[k], capw, a.overflow_at)];
         if constexpr (PAGED) {
             // The value row's page: every table read issued before any use.
             int32_t page[EPT];
@@ -393,12 +412,12 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
             for (int k = 0; k < EPT; ++k) {
                 const int64_t r = (int64_t)(lo[k] / kWavesPerBlock) * a.rows_per_chunk + ent[k].x;
                 const int64_t pi = r / a.pg.page_rows;
-                page[k] = (t + k * kBlock < n && pi < a.pg.max_pages)
+                page[k] = (EPT * t + k < n && pi < a.pg.max_pages)
                               ? a.pg.block_table[(int64_t)b * a.pg.max_pages + pi] : -1;
             }
 #pragma unroll
             for (int k = 0; k < EPT; ++k) {
-                const int e = t + k * kBlock;
+                const int e = EPT * t + k;
                 if (e < n) {
                     const float sv = __uint_as_float(ent[k].y);
                     const bool keep = sv >= tf;
@@ -419,7 +438,7 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
         } else {
 #pragma unroll
         for (int k = 0; k < EPT; ++k) {
-            const int e = t + k * kBlock;
+            const int e = EPT * t + k;
             if (e < n) {
                 const float sv = __uint_as_float(ent[k].y);
                 const bool keep = sv >= tf;

@@ -201,16 +201,33 @@ __global__ __launch_bounds__(kBlock) void sample_logits_kernel(SampleArgs a)
     const uint16_t* khead = a.k + ((int64_t)(b * a.hk + g) * a.cache_len) * D;
     const int64_t ctx_b = PAGED ? seq_ctx(a.pg, b, 0) : (a.lq > 1 ? a.ctx : INT64_MAX);
     KTile<D, U> kt;
+    // Paged: every page-table read is issued before any K load (an index past
+    // the table reads its last entry and the row is then dropped).
+    int32_t page[U];
+    if constexpr (PAGED) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int k = k0 + 16 * u + col;
+            k = k < a.m ? k : a.m - 1;
+            const int64_t pi = ((int64_t)(k >> 4) * a.stride + (k & 15)) / a.pg.page_rows;
+            page[u] = a.pg.block_table[(int64_t)b * a.pg.max_pages +
+                                       (pi < a.pg.max_pages ? pi : a.pg.max_pages - 1)];
+        }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         int k = k0 + 16 * u + col;
         k = k < a.m ? k : a.m - 1;
         const int64_t row = (int64_t)(k >> 4) * a.stride + (k & 15);
         const uint16_t* p;
+        bool ok = true;
         if constexpr (PAGED) {
-            // Rows past the sequence (and pages outside the pool) read nothing.
-            const int64_t base = row < ctx_b ? page_base<D>(a.pg, b, g, a.hk, row) : -1;
-            p = base < 0 ? nullptr : a.k + base + (row % a.pg.page_rows) * D + 8 * grp;
+            // Rows past the sequence, past the table or on a page outside the
+            // pool load row 0 of page 0 (the pool holds at least one page)
+            // and are zeroed.
+            const int64_t P = a.pg.page_rows;
+            ok = row < ctx_b && row / P < a.pg.max_pages && page[u] >= 0 && page[u] < a.pg.num_pages;
+            p = (ok ? a.k + (((int64_t)page[u] * a.hk + g) * P + row % P) * D : a.k) + 8 * grp;
         } else if constexpr (FP8) {
             p = nullptr;
             const uint8_t* p8 = reinterpret_cast<const uint8_t*>(a.k) +
@@ -220,9 +237,12 @@ __global__ __launch_bounds__(kBlock) void sample_logits_kernel(SampleArgs a)
             p = khead + row * D + 8 * grp;
         }
         if constexpr (!FP8) {
+            // Loads without a branch: all of them in flight before the first wait.
 #pragma unroll
-            for (int mm = 0; mm < D / 32; ++mm)
-                kt.v[u][mm] = p ? ld16(p + 32 * mm) : u32x4{0u, 0u, 0u, 0u};
+            for (int mm = 0; mm < D / 32; ++mm) {
+                const u32x4 x = ld16(p + 32 * mm);
+                kt.v[u][mm] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+            }
         }
     }
     float s[U][4];
@@ -281,12 +301,15 @@ __global__ __launch_bounds__(kBlock) void pivot_kernel(SampleArgs a)
             rank = (int)(r < (double)mb ? r : (double)mb);
         }
     }
+    // Unconditional loads (slots past m read sample 0 or m-1 again and are
+    // masked by the select), all in flight before the first wait.
     constexpr int KPT = kSampleMax / kBlock;
     uint32_t kv[KPT];
+    const int last = a.m > 0 ? a.m - 1 : 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         const int k = threadIdx.x + j * kBlock;
-        kv[j] = k < a.m ? float_key(s[k]) : 0u;
+        kv[j] = float_key(s[k < a.m ? k : last]);
     }
     const uint32_t key = reg_radix_select<KPT>(kv, (uint32_t)a.m, (uint32_t)rank, w);
     if (threadIdx.x == 0) {
