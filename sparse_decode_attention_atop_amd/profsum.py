@@ -12,6 +12,11 @@
         copy of ``bench.py --calibrate``; prints a markdown table and the JSON
         block that ``bench.py`` reads.
 
+    python -m sparse_decode_attention_atop_amd.profsum util DIR
+        MFMA and VALU use per kernel of a plain decode call from a
+        ``rocprofv3 --pmc MfmaUtil VALUBusy MfmaFlopsBF16`` run written as CSV
+        (rocprofv3's own derived counters, one value per dispatch).
+
 Launches are classified by order: a stream-select launch right after the
 pivot kernel is a refresh step's candidate pass, one right after the final
 select is its repair pass, any other starts a plain decode call; a gather and
@@ -120,11 +125,28 @@ def traffic(workload, fdir, wdir, cfdir, cwdir):
     return "\n".join(lines) + "\n\n```json\n" + json.dumps(blob, indent=1) + "\n```\n"
 
 
+def util(d):
+    names = ["MfmaUtil", "VALUBusy", "MfmaFlopsBF16"]
+    kinds = ["select_stream", "gather_kernel", "combine_kernel"]
+    per = {nm: _decode_calls(_counter(d, nm)) for nm in names}
+    n = min(len(c) for c in per.values())
+    mean = lambda nm, k: sum(c[k] for c in per[nm][:n]) / n
+    lines = [f"Plain decode calls measured: {n}.", "",
+             "| kernel | MFMA busy (% of SIMD cycles) | VALU busy (%) | bf16 MFMA GFLOP per launch |",
+             "|---|---|---|---|"]
+    for k in kinds:
+        lines.append(f"| `{k}` | {mean('MfmaUtil', k):.2f} | {mean('VALUBusy', k):.2f} | "
+                     f"{mean('MfmaFlopsBF16', k) / 1e9:.3f} |")
+    return "\n".join(lines)
+
+
 def main(argv):
     if len(argv) >= 2 and argv[0] == "trace":
         print(trace(argv[1], int(argv[2]) if len(argv) > 2 else 25))
     elif len(argv) == 6 and argv[0] == "traffic":
         print(traffic(*argv[1:]))
+    elif len(argv) == 2 and argv[0] == "util":
+        print(util(argv[1]))
     else:
         print(__doc__, file=sys.stderr)
         return 2
