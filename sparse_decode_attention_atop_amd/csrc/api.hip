@@ -116,8 +116,11 @@ Layout make_layout(const saga_dims* d)
 {
     Layout L{};
     const size_t rows = (size_t)d->batch * d->h_q;
-    const int64_t target = target_blocks(d->head_dim) > kFullTargetBlocks
-                               ? target_blocks(d->head_dim) : kFullTargetBlocks;
+    // Room for the largest launch any call makes: the bf16 and fp8 K streams
+    // and the dense kernel.
+    int64_t target = kFullTargetBlocks;
+    for (const bool k8 : {false, true})
+        if (target_blocks(d->head_dim, k8) > target) target = target_blocks(d->head_dim, k8);
     const int64_t want = target / ((int64_t)d->batch * d->h_k);
     const int64_t by_len = (d->cache_len + 127) / 128;   // smallest tile pair is 128 rows
     int64_t mc = want < by_len ? want : by_len;
