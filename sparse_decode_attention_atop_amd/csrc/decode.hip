@@ -17,7 +17,7 @@
 //   per-(b, query head, chunk, wave) list of (row, logit) in the workspace,
 //   together with the list length and the list's largest logit.  No LDS, no
 //   waiting on anything but the K stream.
-// gather_kernel: grid.y = (b, query head), grid.x = a segment of chunks.
+// gather_kernel: one workgroup per (b, query head, segment of its entries).
 //   Reads its lists' lengths and maxima, stages the entries in LDS with their
 //   softmax weights exp(s - M) (M = the segment's largest selected logit),
 //   then gathers the selected rows of the query head's value head with
@@ -293,7 +293,8 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
     }
 }
 
-// Gather kernel: grid.x = segment, grid.y = (b, query head).  The segments of
+// Gather kernel: a 1-D grid, workgroup (b*h_q + i) * segs + segment (1-D so
+// that b*h_q may exceed the 65535 limit of a grid's y dimension).  The segments of
 // a head split its selected entries (the concatenation of all its lists, in
 // list order) into equal ranges, so a head whose selection grew between
 // refreshes is spread evenly over its workgroups.  M is the head's largest
@@ -324,8 +325,8 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
     __shared__ float ew[CAPL];
     __shared__ int32_t eps[PAGED == 2 ? CAPL : 1];   // page * h_v + value head, -1 if none
 
-    const int seg = blockIdx.x;
-    const int bi = blockIdx.y;
+    const int bi = blockIdx.x / a.segs;
+    const int seg = blockIdx.x - bi * a.segs;
     const int b = bi / a.hq, i = bi - b * a.hq;
     const int t = threadIdx.x;
     const int nl = a.chunks * kWavesPerBlock;
@@ -622,7 +623,7 @@ hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t s)
 
 hipError_t launch_gather(int D, const GatherArgs& a, hipStream_t s)
 {
-    const dim3 grid(a.segs, a.B * a.hq);
+    const dim3 grid((unsigned)a.segs * (unsigned)(a.B * a.hq));
     const int mode = a.pg.block_table == nullptr ? 0 : (a.pool_bytes != 0 ? 1 : 2);
 #define SAGA_LAUNCH_GATHER(DD, M) hipLaunchKernelGGL((gather_kernel<DD, M>), grid, dim3(kBlock), 0, s, a)
     if (D == 32) {

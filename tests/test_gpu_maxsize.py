@@ -82,3 +82,25 @@ def test_largest_cache_head(d):
             assert err <= 1e-2, f"(b={b}, i={i}) step {t}: {err:.3e}"
     del q, K, V, ws
     torch.cuda.empty_cache()
+
+
+def test_more_query_rows_than_a_grid_dimension():
+    """B*h_q above 65535 (the limit of a launch grid's y dimension); B*h_k stays
+    under the library's own limit.  Every row: tau bit-equal to the N-th largest
+    GPU logit, counts, and outputs within 1e-2 of the oracle on the GPU's mask."""
+    from gpu_helpers import run_atopn, to_np_bits
+    B, hq, hk, hv, d, N = 2100, 32, 4, 8, 64, 16
+    assert B * hq > 65535 and B * hk <= 65535
+    print(f"[maxsize] B*h_q = {B * hq}", flush=True)
+    q, K, V = make_inputs(B, hq, hk, hv, d, 130, 2, seed=82, heavy=False)
+    ctx_steps = [128, 129]
+    gpu = run_atopn(q, K, V, ctx_steps, N, 2)
+    qb, Kb, Vb = to_np_bits(q), to_np_bits(K), to_np_bits(V)
+    lg, tau = gpu["logits"][0], gpu["tau"][0]
+    nth = np.sort(lg.astype(np.float32), axis=-1)[..., ::-1][..., N - 1]
+    assert np.array_equal(tau.view(np.uint32), nth.view(np.uint32))
+    for t, ctx in enumerate(ctx_steps):
+        ref, cnt = oracle.masked(qb[t], Kb, Vb, ctx, gpu["bitmap"][t])
+        assert (cnt == gpu["counts"][t]).all(), t
+        err = np.abs(gpu["out"][t] - ref).max()
+        assert err <= 1e-2, f"step {t}: max abs err {err:.3e}"
