@@ -67,7 +67,9 @@ typedef enum saga_status {
 
 /* Problem shape of one layer call.
  *   batch      >= 1
- *   h_q, h_k, h_v >= 1; h_k and h_v each divide h_q; h_q/h_k <= 16
+ *   h_q, h_k, h_v >= 1; h_k and h_v each divide h_q; h_q/h_k <= 16;
+ *              batch * h_k <= 65535 and batch * h_q * cache_len <= 2^40, else
+ *              SAGA_ERR_UNSUPPORTED
  *   head_dim   d_k, the q / key head dimension: 32, 64 or 128
  *   head_dim_v d_v, the value / output head dimension: 32, 64 or 128, or 0
  *              for d_v = d_k.  The key and value dimensions are independent
