@@ -106,6 +106,9 @@ INVALID, UNSUPPORTED, SMALL = 1, 2, 3
     (dict(h_v=7), INVALID), (dict(ctx_len=0), INVALID), (dict(ctx_len=1025), INVALID),
     (dict(cache_len=1 << 27, ctx_len=10), INVALID), (dict(head_dim=96), UNSUPPORTED),
     (dict(h_q=34, h_k=2, h_v=2), UNSUPPORTED),
+    (dict(batch=1 << 14, h_q=8, h_k=4, h_v=4), UNSUPPORTED),          # batch * h_k > 65535
+    (dict(batch=1 << 14, h_q=16, h_k=1, h_v=1, cache_len=(1 << 22) + 64, ctx_len=10),
+     UNSUPPORTED),                                                    # batch * h_q * cache_len > 2^40
 ])
 def test_dims_errors_every_entry_point(bad, code):
     d = good_dims(**bad)
