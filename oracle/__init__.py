@@ -9,7 +9,8 @@ The arithmetic lives in ``oracle.c`` (plain C, double precision); this module
 only builds that file with gcc and marshals numpy arrays.  Every function
 takes bf16 data as ``uint16`` bit patterns, exactly the values the device
 sees; the ``*_e4m3k`` variants take an fp8 E4M3 key cache as ``uint8`` codes
-with one fp32 scale per (batch row, key head).  Citations of the pages are in
+with one fp32 scale per (batch row, key head), and the ``*_e4m3kv`` variants
+also an E4M3 value cache with one scale per (batch row, value head).  Citations of the pages are in
 ``oracle.c`` next to each function.
 """
 from __future__ import annotations
@@ -67,12 +68,18 @@ def _load():
                                                i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
         lib.oracle_masked_e4m3k.argtypes = [i32, i32, i32, i32, i32, i32, i64, i64, dbl, vp, vp,
                                             vp, vp, vp, vp, vp, i32]
+        lib.oracle_atopn_run_e4m3kv.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, vp, dbl,
+                                                i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                vp, i32]
+        lib.oracle_masked_e4m3kv.argtypes = [i32, i32, i32, i32, i32, i32, i64, i64, dbl, vp,
+                                             vp, vp, vp, vp, vp, vp, vp, i32]
         lib.oracle_e4m3_decode.argtypes = [vp, i64, vp]
         lib.oracle_e4m3_decode.restype = None
         lib.oracle_max_threads.restype = i32
         for name in ("oracle_logits", "oracle_atopn_run", "oracle_masked",
                      "oracle_exact_topn", "oracle_full", "oracle_logits_e4m3k",
-                     "oracle_atopn_run_e4m3k", "oracle_masked_e4m3k"):
+                     "oracle_atopn_run_e4m3k", "oracle_masked_e4m3k", "oracle_atopn_run_e4m3kv",
+                     "oracle_masked_e4m3kv"):
             getattr(lib, name).restype = i32
         _lib = lib
     return _lib
@@ -101,6 +108,13 @@ def _kscale(k_scale, B, hk) -> np.ndarray:
 
 def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _vscale(v_scale, B, hv) -> np.ndarray:
+    v_scale = np.ascontiguousarray(v_scale, dtype=np.float32)
+    if v_scale.shape != (B, hv):
+        raise ValueError("v_scale must be [B][hv]")
+    return v_scale
 
 
 def _cache_shape(K, V):
@@ -178,9 +192,19 @@ def atopn_run_e4m3k(q_steps, K8, k_scale, V, ctx_steps, top_n: int, refresh_n: i
                   want_logits, nthreads)
 
 
+def atopn_run_e4m3kv(q_steps, K8, k_scale, V8, v_scale, ctx_steps, top_n: int, refresh_n: int,
+                     scale: float = 1.0, want_sel: bool = False, want_logits: bool = False,
+                     nthreads: int = 0):
+    """``atopn_run`` with E4M3 key and value caches: ``K8`` with ``k_scale [B][hk]``,
+    ``V8`` with ``v_scale [B][hv]`` (a value element is v_scale * e4m3(code))."""
+    return _atopn(q_steps, _u8(K8), k_scale, V8, ctx_steps, top_n, refresh_n, scale, want_sel,
+                  want_logits, nthreads, v_scale=v_scale)
+
+
 def _atopn(q_steps, K, k_scale, V, ctx_steps, top_n, refresh_n, scale, want_sel, want_logits,
-           nthreads):
-    q_steps, V = _u16(q_steps), _u16(V)
+           nthreads, v_scale=None):
+    q_steps = _u16(q_steps)
+    V = _u16(V) if v_scale is None else _u8(V)
     B, hk, hv, cache_len, d, dv = _cache_shape(K, V)
     T, _, hq, _ = q_steps.shape
     ctx = np.ascontiguousarray(ctx_steps, dtype=np.int64)
@@ -194,7 +218,12 @@ def _atopn(q_steps, K, k_scale, V, ctx_steps, top_n, refresh_n, scale, want_sel,
     tail = (_ptr(V), _ptr(out), _ptr(tau), _ptr(count),
             _ptr(sel) if sel is not None else None, _ptr(lg) if lg is not None else None,
             nthreads)
-    if k_scale is None:
+    if v_scale is not None:
+        ks, vs = _kscale(k_scale, B, hk), _vscale(v_scale, B, hv)
+        rc = _load().oracle_atopn_run_e4m3kv(B, hq, hk, hv, d, dv, cache_len, T, _ptr(ctx),
+                                             scale, top_n, refresh_n, _ptr(q_steps), _ptr(K),
+                                             _ptr(ks), _ptr(V), _ptr(vs), *tail[1:])
+    elif k_scale is None:
         rc = _load().oracle_atopn_run(B, hq, hk, hv, d, dv, cache_len, T, _ptr(ctx), scale,
                                       top_n, refresh_n, _ptr(q_steps), _ptr(K), *tail)
     else:
@@ -245,6 +274,26 @@ def masked_e4m3k(q, K8, k_scale, V, ctx: int, bitmap, scale: float = 1.0, nthrea
                                      nthreads)
     if rc:
         raise ValueError("oracle_masked_e4m3k rejected its arguments")
+    return out, count
+
+
+def masked_e4m3kv(q, K8, k_scale, V8, v_scale, ctx: int, bitmap, scale: float = 1.0,
+                  nthreads: int = 0):
+    """``masked`` with E4M3 key and value caches (scales ``[B][hk]`` and ``[B][hv]``)."""
+    q, K8, V8 = _u16(q), _u8(K8), _u8(V8)
+    B, hk, hv, cache_len, d, dv = _cache_shape(K8, V8)
+    hq = q.shape[1]
+    ks, vs = _kscale(k_scale, B, hk), _vscale(v_scale, B, hv)
+    bitmap = np.ascontiguousarray(bitmap, dtype=np.uint32)
+    if bitmap.shape != (B, hq, (cache_len + 31) // 32):
+        raise ValueError("bitmap must be [B][hq][ceil(rows/32)]")
+    out = np.empty((B, hq, dv), dtype=np.float64)
+    count = np.empty((B, hq), dtype=np.int64)
+    rc = _load().oracle_masked_e4m3kv(B, hq, hk, hv, d, dv, cache_len, ctx, scale, _ptr(q),
+                                      _ptr(K8), _ptr(ks), _ptr(V8), _ptr(vs), _ptr(bitmap),
+                                      _ptr(out), _ptr(count), nthreads)
+    if rc:
+        raise ValueError("oracle_masked_e4m3kv rejected its arguments")
     return out, count
 
 

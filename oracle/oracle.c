@@ -74,36 +74,36 @@ static double e4m3_to_double(uint8_t code)
     return sign ? -mag : mag;
 }
 
-/* A key cache [B][hk][cache_len][d]: bf16 bit patterns, or E4M3 codes with
- * one scale per (batch row, key head). */
+/* A key or value cache [B][H][cache_len][d]: bf16 bit patterns, or E4M3
+ * codes with one scale per (batch row, head): element = scale * e4m3(code). */
 typedef struct {
     const uint16_t* bf16;
     const uint8_t* e4m3;
-    const float* scale;   /* [B][hk], with e4m3 */
-} key_cache;
+    const float* scale;   /* [B][H], with e4m3 */
+} kv_cache;
 
-/* Row 0 of one key head of a key cache. */
+/* Row 0 of one head of a cache. */
 typedef struct {
     const uint16_t* bf16;
     const uint8_t* e4m3;
     double scale;
-} key_head;
+} kv_head;
 
-static key_head key_head_of(const key_cache* kc, int b, int hk, int g, int64_t cache_len, int d)
+static kv_head head_of(const kv_cache* kc, int b, int H, int h, int64_t cache_len, int d)
 {
-    key_head h = {NULL, NULL, 1.0};
-    const int64_t off = (((int64_t)b * hk + g) * cache_len) * d;
+    kv_head r = {NULL, NULL, 1.0};
+    const int64_t off = (((int64_t)b * H + h) * cache_len) * d;
     if (kc->e4m3) {
-        h.e4m3 = kc->e4m3 + off;
-        h.scale = (double)kc->scale[(int64_t)b * hk + g];
+        r.e4m3 = kc->e4m3 + off;
+        r.scale = (double)kc->scale[(int64_t)b * H + h];
     } else {
-        h.bf16 = kc->bf16 + off;
+        r.bf16 = kc->bf16 + off;
     }
-    return h;
+    return r;
 }
 
-/* Element idx (= j * d + c) of a key head, as a double. */
-static double key_at(const key_head* k, int64_t idx)
+/* Element idx (= j * d + c) of a head, as a double. */
+static double elem_at(const kv_head* k, int64_t idx)
 {
     if (k->e4m3) return k->scale * e4m3_to_double(k->e4m3[idx]);
     return bf16_to_double(k->bf16[idx]);
@@ -133,13 +133,13 @@ static const uint16_t* cache_head(const uint16_t* cache, int b, int H, int h,
 }
 
 /* s[j] = scale * sum_c q[c] * K[j][c], for j < ctx  (one query head). */
-static void head_logits(const uint16_t* q, const key_head* Kh, int d, int64_t ctx,
+static void head_logits(const uint16_t* q, const kv_head* Kh, int d, int64_t ctx,
                         double scale, double* s)
 {
     for (int64_t j = 0; j < ctx; ++j) {
         double acc = 0.0;
         for (int c = 0; c < d; ++c)
-            acc += bf16_to_double(q[c]) * key_at(Kh, j * d + c);
+            acc += bf16_to_double(q[c]) * elem_at(Kh, j * d + c);
         s[j] = scale * acc;
     }
 }
@@ -166,7 +166,7 @@ static double nth_largest(const double* s, int64_t n, int64_t N)
  *   m = max_S s_j, w_j = exp(s_j - m), out = sum_S w_j V_j / sum_S w_j.
  * An empty selection gives out = 0.  Returns |S|. */
 static int64_t attend_selected(const double* s, const unsigned char* sel, int64_t ctx,
-                               const uint16_t* Vh, int dv, double* out)
+                               const kv_head* Vh, int dv, double* out)
 {
     int64_t count = 0;
     double m = -INFINITY;
@@ -179,7 +179,7 @@ static int64_t attend_selected(const double* s, const unsigned char* sel, int64_
         if (!sel[j]) continue;
         double w = exp(s[j] - m);
         denom += w;
-        for (int c = 0; c < dv; ++c) out[c] += w * bf16_to_double(Vh[j * dv + c]);
+        for (int c = 0; c < dv; ++c) out[c] += w * elem_at(Vh, j * dv + c);
     }
     for (int c = 0; c < dv; ++c) out[c] /= denom;
     return count;
@@ -188,7 +188,7 @@ static int64_t attend_selected(const double* s, const unsigned char* sel, int64_
 /* ------------------------------------------------------------- public API */
 
 static int logits_impl(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64_t ctx,
-                       double scale, const uint16_t* q, const key_cache* K, double* s,
+                       double scale, const uint16_t* q, const kv_cache* K, double* s,
                        int nthreads)
 {
     if (check_dims(B, hq, hk, hv, d, d, cache_len) || ctx < 1 || ctx > cache_len) return 1;
@@ -197,7 +197,7 @@ static int logits_impl(int B, int hq, int hk, int hv, int d, int64_t cache_len, 
 #pragma omp parallel for schedule(dynamic, 1)
     for (int bi = 0; bi < B * hq; ++bi) {
         int b = bi / hq, i = bi % hq;
-        const key_head Kh = key_head_of(K, b, hk, i / Gk, cache_len, d);
+        const kv_head Kh = head_of(K, b, hk, i / Gk, cache_len, d);
         head_logits(q + (int64_t)bi * d, &Kh, d, ctx, scale, s + (int64_t)bi * ctx);
     }
     return 0;
@@ -208,7 +208,7 @@ int oracle_logits(int B, int hq, int hk, int hv, int d, int64_t cache_len, int64
                   double scale, const uint16_t* q, const uint16_t* K, double* s,
                   int nthreads)
 {
-    const key_cache kc = {K, NULL, NULL};
+    const kv_cache kc = {K, NULL, NULL};
     return logits_impl(B, hq, hk, hv, d, cache_len, ctx, scale, q, &kc, s, nthreads);
 }
 
@@ -217,7 +217,7 @@ int oracle_logits_e4m3k(int B, int hq, int hk, int hv, int d, int64_t cache_len,
                         double scale, const uint16_t* q, const uint8_t* K8,
                         const float* k_scale, double* s, int nthreads)
 {
-    const key_cache kc = {NULL, K8, k_scale};
+    const kv_cache kc = {NULL, K8, k_scale};
     return logits_impl(B, hq, hk, hv, d, cache_len, ctx, scale, q, &kc, s, nthreads);
 }
 
@@ -254,8 +254,8 @@ double oracle_nth_largest(const double* s, int64_t n, int64_t N)
  */
 static int atopn_run_impl(int B, int hq, int hk, int hv, int d, int dv, int64_t cache_len,
                           int T, const int64_t* ctx, double scale, int64_t top_n,
-                          int64_t refresh_n, const uint16_t* q, const key_cache* K,
-                          const uint16_t* V, double* out, double* tau, int64_t* count,
+                          int64_t refresh_n, const uint16_t* q, const kv_cache* K,
+                          const kv_cache* V, double* out, double* tau, int64_t* count,
                           unsigned char* sel, double* logits, int nthreads)
 {
     if (check_dims(B, hq, hk, hv, d, dv, cache_len) || T < 1 || top_n < 1 || refresh_n < 1)
@@ -268,8 +268,8 @@ static int atopn_run_impl(int B, int hq, int hk, int hv, int d, int dv, int64_t 
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
     for (int bi = 0; bi < B * hq; ++bi) {
         const int b = bi / hq, i = bi % hq;
-        const key_head Kh = key_head_of(K, b, hk, i / Gk, cache_len, d);
-        const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, dv);
+        const kv_head Kh = head_of(K, b, hk, i / Gk, cache_len, d);
+        const kv_head Vh = head_of(V, b, hv, i / Gv, cache_len, dv);
         double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);
         unsigned char* S = (unsigned char*)malloc((size_t)cache_len);
         if (!s || !S) { err = 1; free(s); free(S); continue; }
@@ -280,7 +280,7 @@ static int atopn_run_impl(int B, int hq, int hk, int hv, int d, int dv, int64_t 
             head_logits(q + row * d, &Kh, d, n, scale, s);
             if (t % refresh_n == 0) threshold = nth_largest(s, n, top_n);
             for (int64_t j = 0; j < n; ++j) S[j] = (s[j] >= threshold);
-            count[row] = attend_selected(s, S, n, Vh, dv, out + row * dv);
+            count[row] = attend_selected(s, S, n, &Vh, dv, out + row * dv);
             tau[row] = threshold;
             if (sel) {
                 memset(sel + row * cache_len, 0, (size_t)cache_len);
@@ -303,9 +303,9 @@ int oracle_atopn_run(int B, int hq, int hk, int hv, int d, int dv, int64_t cache
                      const uint16_t* V, double* out, double* tau, int64_t* count,
                      unsigned char* sel, double* logits, int nthreads)
 {
-    const key_cache kc = {K, NULL, NULL};
+    const kv_cache kc = {K, NULL, NULL}, vc = {V, NULL, NULL};
     return atopn_run_impl(B, hq, hk, hv, d, dv, cache_len, T, ctx, scale, top_n, refresh_n, q,
-                          &kc, V, out, tau, count, sel, logits, nthreads);
+                          &kc, &vc, out, tau, count, sel, logits, nthreads);
 }
 
 /* Atop-N as above with an E4M3 key cache K8 [B][hk][cache_len][d] and
@@ -316,16 +316,31 @@ int oracle_atopn_run_e4m3k(int B, int hq, int hk, int hv, int d, int dv, int64_t
                            const float* k_scale, const uint16_t* V, double* out, double* tau,
                            int64_t* count, unsigned char* sel, double* logits, int nthreads)
 {
-    const key_cache kc = {NULL, K8, k_scale};
+    const kv_cache kc = {NULL, K8, k_scale}, vc = {V, NULL, NULL};
     return atopn_run_impl(B, hq, hk, hv, d, dv, cache_len, T, ctx, scale, top_n, refresh_n, q,
-                          &kc, V, out, tau, count, sel, logits, nthreads);
+                          &kc, &vc, out, tau, count, sel, logits, nthreads);
+}
+
+/* Atop-N with E4M3 key and value caches: K8 [B][hk][cache_len][d] with
+ * k_scale [B][hk], V8 [B][hv][cache_len][dv] with v_scale [B][hv]; a value
+ * element is v_scale * e4m3(code), decoded like a key element. */
+int oracle_atopn_run_e4m3kv(int B, int hq, int hk, int hv, int d, int dv, int64_t cache_len,
+                            int T, const int64_t* ctx, double scale, int64_t top_n,
+                            int64_t refresh_n, const uint16_t* q, const uint8_t* K8,
+                            const float* k_scale, const uint8_t* V8, const float* v_scale,
+                            double* out, double* tau, int64_t* count, unsigned char* sel,
+                            double* logits, int nthreads)
+{
+    const kv_cache kc = {NULL, K8, k_scale}, vc = {NULL, V8, v_scale};
+    return atopn_run_impl(B, hq, hk, hv, d, dv, cache_len, T, ctx, scale, top_n, refresh_n, q,
+                          &kc, &vc, out, tau, count, sel, logits, nthreads);
 }
 
 /* One step with the selection given by the caller as a bitmap
  * [B][hq][ceil(cache_len/32)] (bit j%32 of word j/32 selects row j): the
  * "use the device's mask" mode that isolates softmax and PV from selection. */
 static int masked_impl(int B, int hq, int hk, int hv, int d, int dv, int64_t cache_len, int64_t ctx,
-                       double scale, const uint16_t* q, const key_cache* K, const uint16_t* V,
+                       double scale, const uint16_t* q, const kv_cache* K, const kv_cache* V,
                        const uint32_t* bitmap, double* out, int64_t* count, int nthreads)
 {
     if (check_dims(B, hq, hk, hv, d, dv, cache_len) || ctx < 1 || ctx > cache_len) return 1;
@@ -339,12 +354,12 @@ static int masked_impl(int B, int hq, int hk, int hv, int d, int dv, int64_t cac
         double* s = (double*)malloc(sizeof(double) * (size_t)ctx);
         unsigned char* S = (unsigned char*)malloc((size_t)ctx);
         if (!s || !S) { err = 1; free(s); free(S); continue; }
-        const key_head Kh = key_head_of(K, b, hk, i / Gk, cache_len, d);
+        const kv_head Kh = head_of(K, b, hk, i / Gk, cache_len, d);
         head_logits(q + (int64_t)bi * d, &Kh, d, ctx, scale, s);
         const uint32_t* bits = bitmap + (int64_t)bi * words;
         for (int64_t j = 0; j < ctx; ++j) S[j] = (bits[j / 32] >> (j % 32)) & 1u;
-        count[bi] = attend_selected(s, S, ctx, cache_head(V, b, hv, i / Gv, cache_len, dv),
-                                    dv, out + (int64_t)bi * dv);
+        const kv_head Vh = head_of(V, b, hv, i / Gv, cache_len, dv);
+        count[bi] = attend_selected(s, S, ctx, &Vh, dv, out + (int64_t)bi * dv);
         free(s);
         free(S);
     }
@@ -355,8 +370,8 @@ int oracle_masked(int B, int hq, int hk, int hv, int d, int dv, int64_t cache_le
                   double scale, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                   const uint32_t* bitmap, double* out, int64_t* count, int nthreads)
 {
-    const key_cache kc = {K, NULL, NULL};
-    return masked_impl(B, hq, hk, hv, d, dv, cache_len, ctx, scale, q, &kc, V, bitmap, out, count,
+    const kv_cache kc = {K, NULL, NULL}, vc = {V, NULL, NULL};
+    return masked_impl(B, hq, hk, hv, d, dv, cache_len, ctx, scale, q, &kc, &vc, bitmap, out, count,
                        nthreads);
 }
 
@@ -366,8 +381,19 @@ int oracle_masked_e4m3k(int B, int hq, int hk, int hv, int d, int dv, int64_t ca
                         const float* k_scale, const uint16_t* V, const uint32_t* bitmap,
                         double* out, int64_t* count, int nthreads)
 {
-    const key_cache kc = {NULL, K8, k_scale};
-    return masked_impl(B, hq, hk, hv, d, dv, cache_len, ctx, scale, q, &kc, V, bitmap, out, count,
+    const kv_cache kc = {NULL, K8, k_scale}, vc = {V, NULL, NULL};
+    return masked_impl(B, hq, hk, hv, d, dv, cache_len, ctx, scale, q, &kc, &vc, bitmap, out, count,
+                       nthreads);
+}
+
+/* One step over a caller-given bitmap with E4M3 key and value caches. */
+int oracle_masked_e4m3kv(int B, int hq, int hk, int hv, int d, int dv, int64_t cache_len,
+                         int64_t ctx, double scale, const uint16_t* q, const uint8_t* K8,
+                         const float* k_scale, const uint8_t* V8, const float* v_scale,
+                         const uint32_t* bitmap, double* out, int64_t* count, int nthreads)
+{
+    const kv_cache kc = {NULL, K8, k_scale}, vc = {NULL, V8, v_scale};
+    return masked_impl(B, hq, hk, hv, d, dv, cache_len, ctx, scale, q, &kc, &vc, bitmap, out, count,
                        nthreads);
 }
 
@@ -440,8 +466,8 @@ int oracle_full(int B, int hq, int hk, int hv, int d, int dv, int64_t cache_len,
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
     for (int bi = 0; bi < B * hq; ++bi) {
         const int b = bi / hq, i = bi % hq;
-        const key_cache kc = {K, NULL, NULL};
-        const key_head Kh = key_head_of(&kc, b, hk, i / Gk, cache_len, d);
+        const kv_cache kc = {K, NULL, NULL};
+        const kv_head Kh = head_of(&kc, b, hk, i / Gk, cache_len, d);
         const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, dv);
         double* s = (double*)malloc(sizeof(double) * (size_t)ctx);
         if (!s) { err = 1; continue; }

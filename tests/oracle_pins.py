@@ -372,6 +372,47 @@ def pin_e4m3k_reduces_to_bf16_cache():
     assert np.array_equal(m8[1], b["count"][1]), "masked count vs run count"
 
 
+def pin_e4m3kv_reduces_to_bf16_caches():
+    """E4M3 key and value caches with power-of-two scales: every scale * decode(code)
+    is exact in bf16, so the E4M3 K/V runs must equal the bf16 runs on the values
+    that torch's float8_e4m3fn decode gives, bit for bit (separate V decoding path)."""
+    T, B, hq, hk, hv, d, rows = 4, 2, 8, 2, 4, 32, 70
+    q, _, _ = rand_case(35, B, hq, hk, hv, d, rows, T=T)
+    K8, ks = rand_e4m3(36, B, hk, rows, d, pow2_scales=True)
+    V8, vs = rand_e4m3(37, B, hv, rows, d, pow2_scales=True)
+    deq = lambda c, sc: lib_e4m3(c) * sc.astype(np.float64)[:, :, None, None]
+    Kb, Vb = to_bits(torch.from_numpy(deq(K8, ks))), to_bits(torch.from_numpy(deq(V8, vs)))
+    assert np.array_equal(f64(Vb).numpy(), deq(V8, vs)), "not exact"
+    ctx = [60 + t for t in range(T)]
+    a = oracle.atopn_run_e4m3kv(q, K8, ks, V8, vs, ctx, 9, 2, 0.5, want_sel=True, want_logits=True)
+    b = oracle.atopn_run(q, Kb, Vb, ctx, 9, 2, 0.5, want_sel=True, want_logits=True)
+    for k in ("out", "tau", "count", "sel", "logits"):
+        assert np.array_equal(a[k], b[k]), f"E4M3 K/V run differs from bf16 run in {k}"
+    bm = mask_bitmap(b["sel"][1][..., :ctx[1]].astype(bool), rows)
+    m8 = oracle.masked_e4m3kv(q[1], K8, ks, V8, vs, ctx[1], bm, 0.5)
+    mb = oracle.masked(q[1], Kb, Vb, ctx[1], bm, 0.5)
+    assert np.array_equal(m8[0], mb[0]) and np.array_equal(m8[1], mb[1]), "E4M3 K/V masked"
+
+
+def pin_e4m3kv_full_vs_library_attention():
+    """Arbitrary (not power-of-two) scales: with N covering the context the E4M3
+    K/V run is full attention over v_scale * decode(code), equal to torch's
+    scaled-dot-product attention on torch-decoded float64 caches."""
+    B, hq, hk, hv, d, rows = 2, 8, 2, 4, 32, 50
+    q, _, _ = rand_case(38, B, hq, hk, hv, d, rows, T=1)
+    K8, ks = rand_e4m3(39, B, hk, rows, d, pow2_scales=False)
+    V8, vs = rand_e4m3(40, B, hv, rows, d, pow2_scales=False)
+    ctx = rows - 3
+    Kt = torch.from_numpy(lib_e4m3(K8) * ks.astype(np.float64)[:, :, None, None])[:, :, :ctx]
+    Vt = torch.from_numpy(lib_e4m3(V8) * vs.astype(np.float64)[:, :, None, None])[:, :, :ctx]
+    want = torch.nn.functional.scaled_dot_product_attention(
+        f64(q[0])[:, :, None, :], Kt.repeat_interleave(hq // hk, dim=1),
+        Vt.repeat_interleave(hq // hv, dim=1), scale=0.25)[:, :, 0, :].numpy()
+    r = oracle.atopn_run_e4m3kv(q, K8, ks, V8, vs, [ctx], rows, 1, 0.25)
+    assert (r["count"][0] == ctx).all()
+    assert_close(r["out"][0], want, 1e-12, "E4M3 K/V full attention vs torch")
+
+
 def pin_key_and_value_dims_independent():
     """d_k != d_v (the pages' Sigma-style (h_k, d_k) = (2, 32) against d_v = 64, and
     the reverse): full, exact top-N, Atop-N at n = 1 and masked mode against torch's

@@ -20,25 +20,25 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
 # (name, original text, mutated text) -- each original must occur exactly once.
 MUTANTS = [
-    ("key_operand_index", "key_at(Kh, j * d + c);\n        s[j]",
-     "key_at(Kh, j * d + (d - 1 - c));\n        s[j]"),
+    ("key_operand_index", "elem_at(Kh, j * d + c);\n        s[j]",
+     "elem_at(Kh, j * d + (d - 1 - c));\n        s[j]"),
     ("dropped_scale", "s[j] = scale * acc;", "s[j] = acc;"),
-    ("key_head_map", "const key_head Kh = key_head_of(K, b, hk, i / Gk, cache_len, d);\n"
-     "        const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, dv);\n"
+    ("key_head_map", "const kv_head Kh = head_of(K, b, hk, i / Gk, cache_len, d);\n"
+     "        const kv_head Vh = head_of(V, b, hv, i / Gv, cache_len, dv);\n"
      "        double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);",
-     "const key_head Kh = key_head_of(K, b, hk, i % hk, cache_len, d);\n"
-     "        const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, dv);\n"
+     "const kv_head Kh = head_of(K, b, hk, i % hk, cache_len, d);\n"
+     "        const kv_head Vh = head_of(V, b, hv, i / Gv, cache_len, dv);\n"
      "        double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);"),
-    ("value_head_map", "const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, dv);\n"
+    ("value_head_map", "const kv_head Vh = head_of(V, b, hv, i / Gv, cache_len, dv);\n"
      "        double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);",
-     "const uint16_t* Vh = cache_head(V, b, hv, i / Gk % hv, cache_len, dv);\n"
+     "const kv_head Vh = head_of(V, b, hv, i / Gk % hv, cache_len, dv);\n"
      "        double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);"),
-    ("value_head_stride_is_key_dim", "const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, dv);\n"
+    ("value_head_stride_is_key_dim", "const kv_head Vh = head_of(V, b, hv, i / Gv, cache_len, dv);\n"
      "        double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);",
-     "const uint16_t* Vh = cache_head(V, b, hv, i / Gv, cache_len, d);\n"
+     "const kv_head Vh = head_of(V, b, hv, i / Gv, cache_len, d);\n"
      "        double* s = (double*)malloc(sizeof(double) * (size_t)cache_len);"),
-    ("output_stride_is_key_dim", "count[row] = attend_selected(s, S, n, Vh, dv, out + row * dv);",
-     "count[row] = attend_selected(s, S, n, Vh, dv, out + row * d);"),
+    ("output_stride_is_key_dim", "count[row] = attend_selected(s, S, n, &Vh, dv, out + row * dv);",
+     "count[row] = attend_selected(s, S, n, &Vh, dv, out + row * d);"),
     ("threshold_rank_off_by_one", "double t = tmp[N - 1];", "double t = tmp[N];"),
     ("sort_ascending", "return (x < y) - (x > y);", "return (x > y) - (x < y);"),
     ("strict_comparison", "S[j] = (s[j] >= threshold);", "S[j] = (s[j] > threshold);"),
@@ -48,8 +48,8 @@ MUTANTS = [
      "double w = exp(m - s[j]);\n        denom += w;\n        for (int c = 0; c < dv; ++c) out[c]"),
     ("dropped_normalisation", "for (int c = 0; c < dv; ++c) out[c] /= denom;\n    return count;",
      "for (int c = 0; c < dv; ++c) out[c] /= 1.0;\n    return count;"),
-    ("value_row_index", "out[c] += w * bf16_to_double(Vh[j * dv + c]);\n    }\n    for (int c = 0; c < dv; ++c) out[c] /= denom;\n    return count;",
-     "out[c] += w * bf16_to_double(Vh[(ctx - 1 - j) * dv + c]);\n    }\n    for (int c = 0; c < dv; ++c) out[c] /= denom;\n    return count;"),
+    ("value_row_index", "out[c] += w * elem_at(Vh, j * dv + c);\n    }\n    for (int c = 0; c < dv; ++c) out[c] /= denom;\n    return count;",
+     "out[c] += w * elem_at(Vh, (ctx - 1 - j) * dv + c);\n    }\n    for (int c = 0; c < dv; ++c) out[c] /= denom;\n    return count;"),
     ("empty_selection_not_zero", "if (count == 0) return 0;", "if (count == 0) { out[0] = 1.0; return 0; }"),
     ("exact_topn_keeps_one_more", "const int64_t keep = top_n < ctx ? top_n : ctx;",
      "const int64_t keep = top_n < ctx ? top_n + 1 : ctx;"),
@@ -57,8 +57,14 @@ MUTANTS = [
     ("e4m3_subnormal_as_normal", "e == 0 ? ldexp((double)m / 8.0, -6)", "e == 0 ? ldexp(1.0 + (double)m / 8.0, -6)"),
     ("e4m3_no_nan", "if (e == 15 && m == 7) return NAN;", "if (e == 16) return NAN;"),
     ("e4m3_sign_dropped", "return sign ? -mag : mag;", "return mag;"),
-    ("e4m3_scale_index", "h.scale = (double)kc->scale[(int64_t)b * hk + g];",
-     "h.scale = (double)kc->scale[g];"),
+    ("e4m3_scale_index", "r.scale = (double)kc->scale[(int64_t)b * H + h];",
+     "r.scale = (double)kc->scale[h];"),
+    ("e4m3_value_scale_is_key_scale",
+     "vc = {NULL, V8, v_scale};\n    return atopn_run_impl",
+     "vc = {NULL, V8, k_scale};\n    return atopn_run_impl"),
+    ("e4m3_value_codes_read_as_bf16",
+     "vc = {NULL, V8, v_scale};\n    return masked_impl",
+     "vc = {(const uint16_t*)V8, NULL, NULL};\n    return masked_impl"),
     ("e4m3_scale_dropped", "if (k->e4m3) return k->scale * e4m3_to_double", "if (k->e4m3) return e4m3_to_double"),
     ("full_softmax_drops_max_row", "for (int64_t j = 0; j < ctx; ++j) if (s[j] > m) m = s[j];\n        double* o",
      "for (int64_t j = 0; j < ctx; ++j) if (s[j] > m) m = s[j];\n        s[0] = -INFINITY;\n        double* o"),
