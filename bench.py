@@ -100,6 +100,8 @@ def parse():
                    help="time the schedule with this many query tokens per head and step")
     p.add_argument("--fp8k", action="store_true",
                    help="store the K cache as fp8 E4M3 (the *_fp8k calls)")
+    p.add_argument("--fp8kv", action="store_true",
+                   help="store the K and V caches as fp8 E4M3 (the *_fp8kv calls)")
     p.add_argument("--sigma", action="store_true",
                    help="Sigma-style heads: twice the key heads at half the key head dimension "
                         "(same K bytes), value heads unchanged; main schedule only")
@@ -140,12 +142,12 @@ def layer_inputs(torch, wl, w, layer):
     return x["K"], x["V"], x["q"]
 
 
-def decode_algorithmic_bytes(w, ctx, sel_total, k_bytes=2):
+def decode_algorithmic_bytes(w, ctx, sel_total, k_bytes=2, v_bytes=2):
     """Bytes the fused decode launch must move: K once per (b, key head)
-    (k_bytes per element: 2 for bf16, 1 for fp8), the selected V rows, q, out
-    and the thresholds."""
+    (k_bytes per element: 2 for bf16, 1 for fp8), the selected V rows (v_bytes
+    per element), q, out and the thresholds."""
     d, dv = w.head_dim, w.head_dim_v or w.head_dim
-    return (w.batch * w.h_k * ctx * d * k_bytes + sel_total * dv * 2
+    return (w.batch * w.h_k * ctx * d * k_bytes + sel_total * dv * v_bytes
             + w.batch * w.h_q * (d + dv) * 2 + w.batch * w.h_q * 4)
 
 
@@ -377,17 +379,22 @@ def run_saga_lq(torch, saga, wl, w, args):
     return dict(sec=sec, step_bytes=step_bytes)
 
 
-def run_saga_fp8k(torch, saga, wl, w, args):
+def run_saga_fp8k(torch, saga, wl, w, args, v8=False):
     """The main schedule with the K cache stored as fp8 E4M3 (one scale per
-    sequence and key head, amax / 448) and V in bf16, through the *_fp8k calls."""
+    sequence and key head, amax / 448) and V in bf16, through the *_fp8k calls;
+    with v8 the V cache too (one scale per sequence and value head), through
+    the *_fp8kv calls (thresholds from atopn_refresh_thresholds_fp8k)."""
     T, L = w.steps, w.L
     layers = []
-    log(f"generating {w.layers} layers of {w.name} with an fp8 K cache")
+    log(f"generating {w.layers} layers of {w.name} with an fp8 K{'/V' if v8 else ''} cache")
     for layer in range(w.layers):
         K, V, q = layer_inputs(torch, wl, w, layer)
         K8, ks = wl.quantize_k_e4m3(K)
         del K
-        layers.append(dict(K8=K8, ks=ks, V=V, q=q,
+        vs = None
+        if v8:
+            V, vs = wl.quantize_k_e4m3(V)
+        layers.append(dict(K8=K8, ks=ks, V=V, vs=vs, q=q,
                            tau=torch.empty(w.batch, w.h_q, device="cuda"),
                            out=torch.empty(w.batch, w.h_q, w.head_dim, dtype=torch.bfloat16,
                                            device="cuda"),
@@ -402,7 +409,14 @@ def run_saga_fp8k(torch, saga, wl, w, args):
         for li, x in enumerate(layers):
             if events is not None:
                 events[li][0].record()
-            if t % w.refresh_n == 0:
+            if v8 and t % w.refresh_n == 0:
+                saga.atopn_refresh_decode_step_fp8kv(dm, w.top_n, x["q"][t], x["K8"], x["ks"],
+                                                     x["V"], x["vs"], x["tau"], x["out"], ws,
+                                                     sel_counts=x["cnt"])
+            elif v8:
+                saga.saga_decode_step_fp8kv(dm, x["q"][t], x["K8"], x["ks"], x["V"], x["vs"],
+                                            x["tau"], x["out"], ws, sel_counts=x["cnt"])
+            elif t % w.refresh_n == 0:
                 saga.atopn_refresh_decode_step_fp8k(dm, w.top_n, x["q"][t], x["K8"], x["ks"],
                                                     x["V"], x["tau"], x["out"], ws,
                                                     sel_counts=x["cnt"])
@@ -426,7 +440,8 @@ def run_saga_fp8k(torch, saga, wl, w, args):
             sel += n_sel
             if t % w.refresh_n:
                 launches.append((ev[li][0].elapsed_time(ev[li][1]),
-                                 decode_algorithmic_bytes(w, L + t, n_sel, k_bytes=1)))
+                                 decode_algorithmic_bytes(w, L + t, n_sel, k_bytes=1,
+                                                          v_bytes=1 if v8 else 2)))
     graphs = []
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -438,10 +453,11 @@ def run_saga_fp8k(torch, saga, wl, w, args):
             graphs.append(g)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    log(f"timing {args.steps} fp8-K steps after {args.warmup} warmup steps")
+    log(f"timing {args.steps} fp8 steps after {args.warmup} warmup steps")
     sec, _ = time_graphs(torch, graphs, args.steps, args.warmup)
-    step_bytes = sum(decode_algorithmic_bytes(w, L + t, 0, k_bytes=1) for t in range(T)) \
-        * w.layers / T + sel * w.head_dim * 2 / T
+    vb = 1 if v8 else 2
+    step_bytes = sum(decode_algorithmic_bytes(w, L + t, 0, k_bytes=1, v_bytes=vb)
+                     for t in range(T)) * w.layers / T + sel * w.head_dim * vb / T
     call_ms = sum(ms for ms, _ in launches) / len(launches)
     call_gbs = sum(b for _, b in launches) / len(launches) / (call_ms / 1e3) / 1e9
     return dict(sec=sec, step_bytes=step_bytes, call_ms=call_ms, call_gbs=call_gbs)
@@ -672,19 +688,23 @@ def main():
                           "hbm_gbs_step": round(gbs, 1), "hbm_frac_step": round(gbs / HBM_PEAK_GBS, 4),
                           "config": {"workload": w.name, "l_q": args.lq}}), flush=True)
         return
-    if args.fp8k:
+    if args.fp8k or args.fp8kv:
         w = wl.WORKLOADS[args.workload]
-        res = run_saga_fp8k(torch, saga, wl, w, args)
+        res = run_saga_fp8k(torch, saga, wl, w, args, v8=args.fp8kv)
         sps = args.steps / res["sec"]
         gbs = res["step_bytes"] / (res["sec"] / args.steps) / 1e9
-        print(json.dumps({"metric": "decode-attn steps/s with an fp8 K cache",
+        kv = "fp8 K and V caches" if args.fp8kv else "an fp8 K cache"
+        print(json.dumps({"metric": f"decode-attn steps/s with {kv}",
                           "value": round(sps, 3), "unit": "steps/s",
                           "ms_per_step": round(1e3 * res["sec"] / args.steps, 4),
-                          "steps": args.steps, "warmup": args.warmup, "dtype": "fp8e4m3 K, bf16 V",
+                          "steps": args.steps, "warmup": args.warmup,
+                          "dtype": "fp8e4m3 K, fp8e4m3 V" if args.fp8kv else "fp8e4m3 K, bf16 V",
                           "hbm_gbs_step": round(gbs, 1), "hbm_frac_step": round(gbs / HBM_PEAK_GBS, 4),
                           "decode_call_us_eager": round(1e3 * res["call_ms"], 2),
                           "decode_call_gbs_eager": round(res["call_gbs"], 1),
-                          "config": {"workload": w.name, "k_cache": "fp8 e4m3, per-head scale"}}),
+                          "config": {"workload": w.name, "k_cache": "fp8 e4m3, per-head scale",
+                                     "v_cache": ("fp8 e4m3, per-head scale" if args.fp8kv
+                                                 else "bf16")}}),
               flush=True)
         return
     if args.paged:

@@ -273,6 +273,32 @@ int atopn_refresh_decode_step_fp8k(const saga_dims* dims, int32_t top_n, const v
                                    size_t workspace_bytes, void* stream);
 
 /*
+ * fp8 K and V caches (the same quantization applied to the value cache as
+ * well).  The V gather then reads d_v bytes per selected row instead of
+ * 2 * d_v.  Thresholds come from atopn_refresh_thresholds_fp8k (they depend
+ * on K only).
+ *   v8_cache_dev  [batch][h_v][cache_len][d_v] bytes, fp8 E4M3 as k8_cache_dev
+ *   v_scale_dev   fp32 [batch][h_v] device memory: value row r of (b, nu) is
+ *                 v_scale[b][nu] * decode(v8[b][nu][r][:])
+ * Outputs are the contiguous calls' on the dequantized caches (each output
+ * row is accumulated on the decoded codes and scaled once by its value head's
+ * scale); thresholds, selection, counts and workspace as the fp8 K calls.
+ * Errors: as the fp8 K calls, plus INVALID_ARGUMENT for a null or misaligned
+ * v_scale_dev.
+ */
+int saga_decode_step_fp8kv(const saga_dims* dims, const void* q_dev, const void* k8_cache_dev,
+                           const float* k_scale_dev, const void* v8_cache_dev,
+                           const float* v_scale_dev, const float* thresholds_dev, void* out_dev,
+                           int32_t* sel_counts_dev, uint32_t* sel_bitmap_debug_dev,
+                           void* workspace_dev, size_t workspace_bytes, void* stream);
+int atopn_refresh_decode_step_fp8kv(const saga_dims* dims, int32_t top_n, const void* q_dev,
+                                    const void* k8_cache_dev, const float* k_scale_dev,
+                                    const void* v8_cache_dev, const float* v_scale_dev,
+                                    float* thresholds_dev, void* out_dev,
+                                    int32_t* sel_counts_dev, void* workspace_dev,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * Full (dense) decode attention over all ctx_len rows with the same head maps:
  * the full-attention GQA baseline the pages time against when h_k == h_v, and
  * "SAGA full attention" when h_k < h_v (ai.info summary, Main Findings:

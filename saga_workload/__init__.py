@@ -138,12 +138,12 @@ def make_layer(w: Workload, layer: int = 0, device="cpu", heavy_hitters: bool = 
 
 
 def quantize_k_e4m3(K: torch.Tensor, pow2_scales: bool = False):
-    """An fp8 E4M3 (OCP) copy of a bf16 K cache ``[B][h_k][rows][d]``, the way
-    a serving stack would store it: one fp32 scale per (batch row, key head),
+    """An fp8 E4M3 (OCP) copy of a bf16 K (or V) cache ``[B][h][rows][d]``, the
+    way a serving stack would store it: one fp32 scale per (batch row, head),
     scale = amax / 448 (rounded up to a power of two when ``pow2_scales``),
     codes = round-to-nearest-even(K / scale) by torch's float8_e4m3fn cast.
 
-    Returns ``(codes uint8 [B][h_k][rows][d], k_scale float32 [B][h_k])`` on
+    Returns ``(codes uint8 [B][h][rows][d], scale float32 [B][h])`` on
     K's device.  Input preparation only: both sides of a parity check take
     these same codes and scales.
     """

@@ -24,7 +24,8 @@ __all__ = [
     "SagaPaged", "paged", "atopn_refresh_thresholds_paged", "saga_decode_step_paged",
     "atopn_refresh_decode_step_paged", "atopn_refresh_thresholds_lq", "saga_decode_step_lq",
     "atopn_refresh_decode_step_lq", "alloc_workspace_lq", "atopn_refresh_thresholds_fp8k",
-    "saga_decode_step_fp8k", "atopn_refresh_decode_step_fp8k", "saga_full_attention",
+    "saga_decode_step_fp8k", "atopn_refresh_decode_step_fp8k", "saga_decode_step_fp8kv",
+    "atopn_refresh_decode_step_fp8kv", "saga_full_attention",
     "saga_status_string", "saga_version", "LIB_PATH", "EXPORTED_SYMBOLS",
 ]
 
@@ -35,6 +36,7 @@ EXPORTED_SYMBOLS = ("saga_workspace_bytes", "atopn_refresh_thresholds", "saga_de
                     "atopn_refresh_thresholds_lq", "saga_decode_step_lq",
                     "atopn_refresh_decode_step_lq", "atopn_refresh_thresholds_fp8k",
                     "saga_decode_step_fp8k", "atopn_refresh_decode_step_fp8k",
+                    "saga_decode_step_fp8kv", "atopn_refresh_decode_step_fp8kv",
                     "saga_full_attention", "saga_status_string", "saga_version")
 
 SAGA_OK = 0
@@ -126,6 +128,12 @@ def library():
         lib.atopn_refresh_decode_step_fp8k.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                                        sz, vp]
         lib.atopn_refresh_decode_step_fp8k.restype = ctypes.c_int
+        lib.saga_decode_step_fp8kv.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                               vp]
+        lib.saga_decode_step_fp8kv.restype = ctypes.c_int
+        lib.atopn_refresh_decode_step_fp8kv.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                        vp, sz, vp]
+        lib.atopn_refresh_decode_step_fp8kv.restype = ctypes.c_int
         lib.saga_full_attention.argtypes = [pd, vp, vp, vp, vp, vp, sz, vp]
         lib.saga_full_attention.restype = ctypes.c_int
         lib.saga_status_string.argtypes = [ctypes.c_int]
@@ -400,11 +408,11 @@ def atopn_refresh_decode_step_lq(d: SagaDims, l_q: int, top_n: int, q: torch.Ten
         "atopn_refresh_decode_step_lq")
 
 
-def _ptr_k8(t: torch.Tensor):
-    """An fp8 E4M3 (OCP) K cache: torch.float8_e4m3fn, or its raw bytes as uint8."""
+def _ptr_k8(t: torch.Tensor, name: str = "k8_cache"):
+    """An fp8 E4M3 (OCP) cache: torch.float8_e4m3fn, or its raw bytes as uint8."""
     if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
-        return _ptr(t, torch.float8_e4m3fn, "k8_cache")
-    return _ptr(t, torch.uint8, "k8_cache")
+        return _ptr(t, torch.float8_e4m3fn, name)
+    return _ptr(t, torch.uint8, name)
 
 
 def _need_fp8k(d: SagaDims, k8_cache: torch.Tensor, k_scale: torch.Tensor):
@@ -476,6 +484,60 @@ def atopn_refresh_decode_step_fp8k(d: SagaDims, top_n: int, q: torch.Tensor,
         _ptr(thresholds, torch.float32, "thresholds"), _ptr(out, torch.bfloat16, "out"),
         _ptr(sel_counts, torch.int32, "sel_counts"), ws, nbytes, _stream(stream)),
         "atopn_refresh_decode_step_fp8k")
+
+
+def _need_fp8v(d: SagaDims, v8_cache: torch.Tensor, v_scale: torch.Tensor):
+    _need(v8_cache, d.batch * d.h_v * d.cache_len * _dv(d), "v8_cache")
+    _need(v_scale, d.batch * d.h_v, "v_scale")
+
+
+def saga_decode_step_fp8kv(d: SagaDims, q: torch.Tensor, k8_cache: torch.Tensor,
+                           k_scale: torch.Tensor, v8_cache: torch.Tensor, v_scale: torch.Tensor,
+                           thresholds: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                           sel_counts: Optional[torch.Tensor] = None,
+                           sel_bitmap_debug: Optional[torch.Tensor] = None, stream=None) -> None:
+    """A decode step with fp8 K and V caches (v_scale fp32 ``[B][h_v]``)."""
+    bh = d.batch * d.h_q
+    _need(q, bh * d.head_dim, "q")
+    _need_fp8k(d, k8_cache, k_scale)
+    _need_fp8v(d, v8_cache, v_scale)
+    _need(thresholds, bh, "thresholds")
+    _need(out, bh * _dv(d), "out")
+    _need(sel_counts, bh, "sel_counts")
+    _need(sel_bitmap_debug, bh * ((d.cache_len + 31) // 32), "sel_bitmap_debug")
+    ws, nbytes = _ws(workspace)
+    _check(library().saga_decode_step_fp8kv(
+        ctypes.byref(d), _ptr(q, torch.bfloat16, "q"), _ptr_k8(k8_cache),
+        _ptr(k_scale, torch.float32, "k_scale"), _ptr_k8(v8_cache, "v8_cache"),
+        _ptr(v_scale, torch.float32, "v_scale"), _ptr(thresholds, torch.float32, "thresholds"),
+        _ptr(out, torch.bfloat16, "out"), _ptr(sel_counts, torch.int32, "sel_counts"),
+        _ptr(sel_bitmap_debug, torch.int32, "sel_bitmap_debug"), ws, nbytes, _stream(stream)),
+        "saga_decode_step_fp8kv")
+
+
+def atopn_refresh_decode_step_fp8kv(d: SagaDims, top_n: int, q: torch.Tensor,
+                                    k8_cache: torch.Tensor, k_scale: torch.Tensor,
+                                    v8_cache: torch.Tensor, v_scale: torch.Tensor,
+                                    thresholds: torch.Tensor, out: torch.Tensor,
+                                    workspace: torch.Tensor,
+                                    sel_counts: Optional[torch.Tensor] = None,
+                                    stream=None) -> None:
+    """A refresh step with fp8 K and V caches: fresh thresholds and this step's output."""
+    bh = d.batch * d.h_q
+    _need(q, bh * d.head_dim, "q")
+    _need_fp8k(d, k8_cache, k_scale)
+    _need_fp8v(d, v8_cache, v_scale)
+    _need(thresholds, bh, "thresholds")
+    _need(out, bh * _dv(d), "out")
+    _need(sel_counts, bh, "sel_counts")
+    ws, nbytes = _ws(workspace)
+    _check(library().atopn_refresh_decode_step_fp8kv(
+        ctypes.byref(d), int(top_n), _ptr(q, torch.bfloat16, "q"), _ptr_k8(k8_cache),
+        _ptr(k_scale, torch.float32, "k_scale"), _ptr_k8(v8_cache, "v8_cache"),
+        _ptr(v_scale, torch.float32, "v_scale"), _ptr(thresholds, torch.float32, "thresholds"),
+        _ptr(out, torch.bfloat16, "out"), _ptr(sel_counts, torch.int32, "sel_counts"), ws,
+        nbytes, _stream(stream)),
+        "atopn_refresh_decode_step_fp8kv")
 
 
 def saga_full_attention(d: SagaDims, q: torch.Tensor, k_cache: torch.Tensor,

@@ -177,6 +177,7 @@ struct RowModel {
     PagedKV pg{};
     int32_t lq = 1;
     const float* k_scale = nullptr;
+    const float* v_scale = nullptr;   // non-null: fp8 e4m3 V cache, one scale per (b, value head)
 };
 
 // Arguments of the stream-select kernel for one call.
@@ -324,6 +325,7 @@ int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunkin
     ga.list_count = reinterpret_cast<const int32_t*>(w + L.lcount);
     ga.list_max = reinterpret_cast<const float*>(w + L.lmax);
     ga.tau_filter = tau_filter;
+    ga.v_scale = rm.v_scale;
     ga.part = partials(workspace_dev, L);
     ga.B = dims->batch;
     ga.hq = dims->h_q;
@@ -692,6 +694,50 @@ SAGA_EXPORT int atopn_refresh_decode_step_fp8k(const saga_dims* dims, int32_t to
     const int st = fp8k_model(dims, k_scale_dev, &rm);
     if (st != SAGA_OK) return st;
     return do_refresh_decode(dims, rm, top_n, q_dev, k8_cache_dev, v_cache_dev, thresholds_dev,
+                             out_dev, sel_counts_dev, workspace_dev, workspace_bytes, stream);
+}
+
+namespace {
+
+// fp8 K and V caches: both scale pointers (4-byte aligned) per call.
+int fp8kv_model(const saga_dims* dims, const float* k_scale_dev, const float* v_scale_dev,
+                RowModel* rm)
+{
+    const int st = fp8k_model(dims, k_scale_dev, rm);
+    if (st != SAGA_OK) return st;
+    if (!v_scale_dev || misaligned(v_scale_dev, 4)) return SAGA_ERR_INVALID_ARGUMENT;
+    rm->v_scale = v_scale_dev;
+    return SAGA_OK;
+}
+
+}  // namespace
+
+SAGA_EXPORT int saga_decode_step_fp8kv(const saga_dims* dims, const void* q_dev,
+                                       const void* k8_cache_dev, const float* k_scale_dev,
+                                       const void* v8_cache_dev, const float* v_scale_dev,
+                                       const float* thresholds_dev, void* out_dev,
+                                       int32_t* sel_counts_dev, uint32_t* sel_bitmap_debug_dev,
+                                       void* workspace_dev, size_t workspace_bytes, void* stream)
+{
+    RowModel rm;
+    const int st = fp8kv_model(dims, k_scale_dev, v_scale_dev, &rm);
+    if (st != SAGA_OK) return st;
+    return do_decode(dims, rm, q_dev, k8_cache_dev, v8_cache_dev, thresholds_dev, out_dev,
+                     sel_counts_dev, sel_bitmap_debug_dev, workspace_dev, workspace_bytes, stream);
+}
+
+SAGA_EXPORT int atopn_refresh_decode_step_fp8kv(const saga_dims* dims, int32_t top_n,
+                                                const void* q_dev, const void* k8_cache_dev,
+                                                const float* k_scale_dev, const void* v8_cache_dev,
+                                                const float* v_scale_dev, float* thresholds_dev,
+                                                void* out_dev, int32_t* sel_counts_dev,
+                                                void* workspace_dev, size_t workspace_bytes,
+                                                void* stream)
+{
+    RowModel rm;
+    const int st = fp8kv_model(dims, k_scale_dev, v_scale_dev, &rm);
+    if (st != SAGA_OK) return st;
+    return do_refresh_decode(dims, rm, top_n, q_dev, k8_cache_dev, v8_cache_dev, thresholds_dev,
                              out_dev, sel_counts_dev, workspace_dev, workspace_bytes, stream);
 }
 

@@ -306,18 +306,25 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
 // need no branch.
 // PAGED: 0 contiguous caches; 1 paged, V pool under 4 GiB (32-bit offsets into
 // the pool, same load path as contiguous); 2 paged, 64-bit addresses.
-template <int D, int PAGED>
+// V8 (contiguous caches only): an fp8 E4M3 value cache, d bytes per row, one
+// scale per (b, value head).  Each lane loads 16 codes, widens them exactly
+// to bf16, and the segment's sum is multiplied by the head's scale once.
+template <int D, int PAGED, bool V8>
 __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherArgs a)
 {
-    constexpr int LPR = D / 8;             // lanes per value row (16 bytes each)
+    static_assert(!V8 || PAGED == 0, "fp8 values: contiguous caches only");
+    constexpr int VB = V8 ? 1 : 2;         // bytes per value element
+    constexpr int EPL = 16 / VB;           // elements per lane load (16 bytes)
+    constexpr int LPR = D / EPL;           // lanes per value row
     constexpr int SLOTS = kBlock / LPR;    // rows per workgroup load instruction
+    constexpr int RED = V8 ? SLOTS / 2 : SLOTS;   // slot sums held at once in the reduction
     constexpr int CAPL = kGatherStage;     // entries staged per round
     constexpr int EPT = CAPL / kBlock;     // staged entries per thread
     constexpr int NB = SAGA_GATHER_NB;     // rows in flight per lane
     constexpr int PER = kMaxListsPerRow / kBlock;
     constexpr uint32_t kNoRow = 0x80000000u;   // past any value head (< 2^31 bytes)
     constexpr uint32_t kNoRowPool = kPoolLimit;  // past any 32-bit-addressed pool
-    static_assert(SLOTS * D <= kMaxListsPerRow, "slot reduction reuses the prefix array");
+    static_assert(RED * D <= kMaxListsPerRow, "slot reduction reuses the prefix array");
     static_assert(CAPL % kBlock == 0, "staging rounds are whole threads");
     __shared__ int32_t pre[kMaxListsPerRow + 1];
     __shared__ int32_t red[kWavesPerBlock];
@@ -365,16 +372,17 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
     const int32_t e_end = (int32_t)((int64_t)total * (seg + 1) / a.segs);
 
     const int nu = i / a.Gv;
-    const uint16_t* vh = a.v + ((int64_t)(b * a.hv + nu) * a.cache_len) * D;
+    const unsigned char* vh = reinterpret_cast<const unsigned char*>(a.v) +
+                              ((int64_t)(b * a.hv + nu) * a.cache_len) * D * VB;
     // Contiguous: the value head; paged (32-bit): the whole pool.
     const __amdgpu_buffer_rsrc_t vrs =
         PAGED == 1 ? make_rsrc(a.v, a.pool_bytes)
-                   : make_rsrc(vh, (uint32_t)(PAGED ? 0 : a.cache_len * D * 2));
+                   : make_rsrc(vh, (uint32_t)(PAGED ? 0 : a.cache_len * D * VB));
     const int slot = t / LPR, lc = t - slot * LPR;
     const float tf = a.tau_filter ? a.tau_filter[bi] : -INFINITY;
-    float acc[8];
+    float acc[EPL];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+    for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
     float lsum = 0.f;
     int32_t kept = 0;                                   // entries with logit >= tf
 
@@ -445,7 +453,7 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
                 const bool keep = sv >= tf;
                 kept += keep;
                 const uint32_t r = (uint32_t)((lo[k] / kWavesPerBlock) * a.rows_per_chunk) + ent[k].x;
-                eoff[e] = keep ? r * (uint32_t)(D * 2) : kNoRow;
+                eoff[e] = keep ? r * (uint32_t)(D * VB) : kNoRow;
                 ew[e] = keep ? __expf(sv - M) : 0.f;
             }
         }
@@ -472,10 +480,23 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
             }
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
+                if constexpr (V8) {
+                    // Codes 0-7 then 8-15 of the lane's 16, widened in order.
+                    const u32x4 h0 = fp8x8_to_bf16x8(u32x2{vv[k][0], vv[k][1]});
+                    const u32x4 h1 = fp8x8_to_bf16x8(u32x2{vv[k][2], vv[k][3]});
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc[2 * j] += w[k] * bf16lo(vv[k][j]);
-                    acc[2 * j + 1] += w[k] * bf16hi(vv[k][j]);
+                    for (int j = 0; j < 4; ++j) {
+                        acc[2 * j] += w[k] * bf16lo(h0[j]);
+                        acc[2 * j + 1] += w[k] * bf16hi(h0[j]);
+                        acc[8 + 2 * j] += w[k] * bf16lo(h1[j]);
+                        acc[8 + 2 * j + 1] += w[k] * bf16hi(h1[j]);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc[2 * j] += w[k] * bf16lo(vv[k][j]);
+                        acc[2 * j + 1] += w[k] * bf16hi(vv[k][j]);
+                    }
                 }
                 lsum += w[k];
             }
@@ -483,17 +504,31 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
         __syncthreads();
     }
 
-    // Reduce the slots in slot order.
-    float* ored = reinterpret_cast<float*>(pre);        // [SLOTS][D]
+    // Reduce the slots in slot order.  fp8 values: the slots' sums take twice
+    // the prefix array, so slot s + SLOTS/2 is first added to slot s.
+    float* ored = reinterpret_cast<float*>(pre);        // [RED][D]
+    if constexpr (V8) {
+        if (slot < RED) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ored[slot * D + 8 * lc + j] = acc[j];
+            for (int j = 0; j < EPL; ++j) ored[slot * D + EPL * lc + j] = acc[j];
+        }
+        __syncthreads();
+        if (slot >= RED) {
+#pragma unroll
+            for (int j = 0; j < EPL; ++j) ored[(slot - RED) * D + EPL * lc + j] += acc[j];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) ored[slot * D + EPL * lc + j] = acc[j];
+    }
     if (lc == 0) ew[slot] = lsum;
     const int32_t nkept = block_sum(kept, red);         // its barrier orders the stores above
     const int64_t idx = (int64_t)bi * a.segs + seg;
+    const float vscale = V8 ? a.v_scale[b * a.hv + nu] : 1.f;
     for (int p = t; p < D; p += kBlock) {
         float o = 0.f;
-        for (int s = 0; s < SLOTS; ++s) o += ored[s * D + p];
-        a.part.o[idx * D + p] = o;
+        for (int s = 0; s < RED; ++s) o += ored[s * D + p];
+        a.part.o[idx * D + p] = V8 ? o * vscale : o;
     }
     if (t == 0) {
         float l = 0.f;
@@ -625,20 +660,22 @@ hipError_t launch_gather(int D, const GatherArgs& a, hipStream_t s)
 {
     const dim3 grid((unsigned)a.segs * (unsigned)(a.B * a.hq));
     const int mode = a.pg.block_table == nullptr ? 0 : (a.pool_bytes != 0 ? 1 : 2);
-#define SAGA_LAUNCH_GATHER(DD, M) hipLaunchKernelGGL((gather_kernel<DD, M>), grid, dim3(kBlock), 0, s, a)
+    if (a.v_scale && mode != 0) return hipErrorInvalidValue;   // fp8 values: contiguous only
+#define SAGA_LAUNCH_GATHER(DD, M, V8) \
+    hipLaunchKernelGGL((gather_kernel<DD, M, V8>), grid, dim3(kBlock), 0, s, a)
+#define SAGA_LAUNCH_GATHER_D(DD)                                                   \
+    if (a.v_scale) SAGA_LAUNCH_GATHER(DD, 0, true);                                \
+    else if (mode == 0) SAGA_LAUNCH_GATHER(DD, 0, false);                          \
+    else if (mode == 1) SAGA_LAUNCH_GATHER(DD, 1, false);                          \
+    else SAGA_LAUNCH_GATHER(DD, 2, false);
     if (D == 32) {
-        if (mode == 0) SAGA_LAUNCH_GATHER(32, 0);
-        else if (mode == 1) SAGA_LAUNCH_GATHER(32, 1);
-        else SAGA_LAUNCH_GATHER(32, 2);
+        SAGA_LAUNCH_GATHER_D(32)
     } else if (D == 64) {
-        if (mode == 0) SAGA_LAUNCH_GATHER(64, 0);
-        else if (mode == 1) SAGA_LAUNCH_GATHER(64, 1);
-        else SAGA_LAUNCH_GATHER(64, 2);
+        SAGA_LAUNCH_GATHER_D(64)
     } else {
-        if (mode == 0) SAGA_LAUNCH_GATHER(128, 0);
-        else if (mode == 1) SAGA_LAUNCH_GATHER(128, 1);
-        else SAGA_LAUNCH_GATHER(128, 2);
+        SAGA_LAUNCH_GATHER_D(128)
     }
+#undef SAGA_LAUNCH_GATHER_D
 #undef SAGA_LAUNCH_GATHER
     return hipGetLastError();
 }

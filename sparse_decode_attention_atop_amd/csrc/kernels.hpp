@@ -154,6 +154,7 @@ struct GatherArgs {
     const int32_t* list_count;
     const float* list_max;
     const float* tau_filter; // nullable [B*hq]: keep only entries with logit >= tau_filter
+    const float* v_scale;    // non-null: fp8 e4m3 V (d_v bytes per row), one scale per (b, value head)
     Partials part;           // one partial per (b*h_q + i, segment)
     uint32_t pool_bytes;     // paged: V pool bytes when below kPoolLimit (32-bit offsets), else 0
     int32_t B, hq, hv, Gv;

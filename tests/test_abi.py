@@ -292,6 +292,35 @@ def test_fp8k_argument_checks(kind):
         assert call_fp8k(kind, d, 1 << 40, top_n=0) == INVALID
 
 
+def call_fp8kv(kind, d, ws_bytes, top_n=8, **ptrs):
+    p = dict(q=FAKE, k8=FAKE, ks=FAKE, v8=FAKE, vs=FAKE, tau=FAKE, out=FAKE, ws=FAKE)
+    p.update(ptrs)
+    lib = saga.library()
+    if kind == "decode":
+        return lib.saga_decode_step_fp8kv(ctypes.byref(d), p["q"], p["k8"], p["ks"], p["v8"],
+                                          p["vs"], p["tau"], p["out"], None, None, p["ws"],
+                                          ws_bytes, None)
+    return lib.atopn_refresh_decode_step_fp8kv(ctypes.byref(d), top_n, p["q"], p["k8"], p["ks"],
+                                               p["v8"], p["vs"], p["tau"], p["out"], None,
+                                               p["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kind", ["decode", "fused"])
+def test_fp8kv_argument_checks(kind):
+    d = good_dims()
+    need = saga.saga_workspace_bytes(d, 8)
+    assert call_fp8kv(kind, d, 1 << 40, vs=None) == INVALID
+    assert call_fp8kv(kind, d, 1 << 40, vs=ctypes.c_void_p((1 << 20) + 2)) == INVALID
+    assert call_fp8kv(kind, d, 1 << 40, ks=None) == INVALID
+    assert call_fp8kv(kind, d, 1 << 40, v8=None) == INVALID
+    assert call_fp8kv(kind, d, 1 << 40, v8=ctypes.c_void_p((1 << 20) + 8)) == INVALID
+    assert call_fp8kv(kind, good_dims(head_dim=32), 1 << 40) == UNSUPPORTED
+    assert call_fp8kv(kind, good_dims(head_dim_v=96), 1 << 40) == UNSUPPORTED
+    assert call_fp8kv(kind, d, need - 1) == SMALL        # same workspace as the bf16 calls
+    if kind == "fused":
+        assert call_fp8kv(kind, d, 1 << 40, top_n=0) == INVALID
+
+
 def test_fp8k_binding_rejects_wrong_dtypes():
     d = good_dims()
     k8 = torch.zeros(4, dtype=torch.bfloat16)
