@@ -38,12 +38,13 @@ def run_fp8kv(q, K8, ks, V8, vs, ctx_steps, N, n, fused=False):
     refresh, or the one-call refresh step when fused)."""
     T, B, hq, d = q.shape
     hk, rows, hv, dv = K8.shape[1], K8.shape[2], V8.shape[1], V8.shape[3]
-    ws = saga.alloc_workspace(saga.dims(B, hq, hk, hv, d, ctx_steps[0], rows), N)
+    dvx = 0 if dv == d else dv
+    ws = saga.alloc_workspace(saga.dims(B, hq, hk, hv, d, ctx_steps[0], rows, head_dim_v=dvx), N)
     tau = torch.empty(B, hq, device="cuda")
     words = (rows + 31) // 32
     res = {"tau": [], "counts": [], "bitmap": [], "out": []}
     for t, ctx in enumerate(ctx_steps):
-        dm = saga.dims(B, hq, hk, hv, d, ctx, rows)
+        dm = saga.dims(B, hq, hk, hv, d, ctx, rows, head_dim_v=dvx)
         out = torch.empty(B, hq, dv, dtype=torch.bfloat16, device="cuda")
         cnt = torch.empty(B, hq, dtype=torch.int32, device="cuda")
         bm = None
@@ -138,3 +139,23 @@ def test_general_scales_fused_refresh_step_matches_separate_calls(name):
         assert np.array_equal(fus["counts"][t], sep["counts"][t]), t
         ref, _ = oracle.masked_e4m3kv(qb[t], K8n, ksn, V8n, vsn, c, sep["bitmap"][t])
         assert np.abs(fus["out"][t] - ref).max() <= OUT_TOL, t
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 32), (128, 64), (64, 128)])
+def test_general_scales_key_and_value_dims_differ(dk, dv):
+    """fp8 K at d_k and fp8 V at d_v (every value-row width the fp8 gather has)."""
+    B, hq, hk, hv, L, T, N, n = 2, 8, 2, 4, 1800, 3, 40, 2
+    q, K, V = make_inputs(B, hq, hk, hv, dk, L + T, T, seed=440 + dk + dv, dv=dv)
+    K8, ks = wl.quantize_k_e4m3(K)
+    V8, vs = wl.quantize_k_e4m3(V)
+    ctx = [L + t for t in range(T)]
+    print(f"[fp8kv dk={dk} dv={dv}] V8{tuple(V8.shape)}", flush=True)
+    gpu = run_fp8kv(q, K8, ks, V8, vs, ctx, N, n)
+    qb, K8n, ksn, V8n, vsn = (to_np_bits(q), K8.cpu().numpy(), ks.cpu().numpy(),
+                              V8.cpu().numpy(), vs.cpu().numpy())
+    for t, c in enumerate(ctx):
+        ref, cnt = oracle.masked_e4m3kv(qb[t], K8n, ksn, V8n, vsn, c, gpu["bitmap"][t])
+        assert ref.shape[-1] == dv
+        assert (cnt == gpu["counts"][t]).all(), t
+        err = np.abs(gpu["out"][t] - ref).max()
+        assert err <= OUT_TOL, f"step {t}: max abs err {err:.3e}"
