@@ -1,0 +1,264 @@
+// launch_stubs.cpp -- host stand-ins for the kernel launchers of libsaga.so,
+// for a CPU build of the C-ABI host code (api.hip) under AddressSanitizer and
+// UndefinedBehaviorSanitizer.
+//
+// Each stub receives exactly the arguments the real launcher would, checks the
+// launch shape the kernel assumes, and then reads or writes the first and the
+// last element of every buffer region that the kernel indexes, at the largest
+// index the kernel's own indexing can reach for those arguments.  The caller
+// (abi_driver.cpp) passes host heap buffers of exactly the documented sizes in
+// place of device memory, so a workspace region, a chunk plan or an output
+// size that is too small for its kernel shows up as a heap-buffer-overflow.
+// Regions that live inside the caller's workspace are also recorded by name
+// with the extent the kernel uses ([lowest, highest] element touched), and
+// the driver checks after each call that no two regions overlap: an overrun
+// from one region into the next stays inside the workspace allocation, where
+// the address sanitizer cannot see it.
+// Nothing here computes attention.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <type_traits>
+#include <vector>
+
+#include "kernels.hpp"
+
+namespace saga {
+
+int g_launches = 0;   // launches since the driver last cleared it
+
+struct TouchedRange {
+    const char* name;
+    uintptr_t lo, hi;     // bytes [lo, hi)
+};
+std::vector<TouchedRange> g_ranges;   // cleared by the driver
+
+namespace {
+
+volatile unsigned char g_sink;
+
+[[noreturn]] void fail(const char* what)
+{
+    fprintf(stderr, "launch stub: %s\n", what);
+    abort();
+}
+#define EXPECT(c) do { if (!(c)) fail(#c); } while (0)
+
+template <typename T>
+void rd(const T* p, int64_t i)
+{
+    EXPECT(p != nullptr && i >= 0);
+    const volatile unsigned char* b = reinterpret_cast<const volatile unsigned char*>(p + i);
+    for (size_t k = 0; k < sizeof(T); ++k) g_sink = b[k];
+}
+template <typename T>
+void wr(T* p, int64_t i)
+{
+    EXPECT(p != nullptr && i >= 0);
+    volatile unsigned char* b = reinterpret_cast<volatile unsigned char*>(p + i);
+    for (size_t k = 0; k < sizeof(T); ++k) b[k] = b[k];
+}
+// Records elements [i0, i1] of p as region `name`.
+template <typename T>
+void note(const char* name, const T* p, int64_t i0, int64_t i1)
+{
+    g_ranges.push_back({name, reinterpret_cast<uintptr_t>(p + i0), reinterpret_cast<uintptr_t>(p + i1 + 1)});
+}
+// First and last element of [0, n).
+template <typename T> void rd_span(const T* p, int64_t n) { if (n > 0) { rd(p, 0); rd(p, n - 1); } }
+template <typename T> void wr_span(T* p, int64_t n) { if (n > 0) { wr(p, 0); wr(p, n - 1); } }
+// Same, recorded as a named region.
+template <typename T>
+void rd_span(const char* name, const T* p, int64_t n) { if (n > 0) { rd_span(p, n); note(name, p, 0, n - 1); } }
+template <typename T>
+void wr_span(const char* name, T* p, int64_t n) { if (n > 0) { wr_span(p, n); note(name, p, 0, n - 1); } }
+
+// Selection-list entries: list lid holds at most capw entries (see list_index).
+int64_t entry_index(int64_t lid, int64_t E, int64_t capw, int64_t overflow_at)
+{
+    return E < kListPrimary ? lid * kListPrimary + E : overflow_at + lid * capw + (E - kListPrimary);
+}
+template <typename T>
+void touch_lists(T* entries, int64_t lists, int64_t capw, int64_t overflow_at)
+{
+    EXPECT(capw >= 1);
+    const int64_t last = lists - 1;
+    const int64_t top = capw - 1 < kListPrimary ? capw - 1 : kListPrimary - 1;
+    note("list entries (primary)", entries, 0, entry_index(last, top, capw, overflow_at));
+    if (capw > kListPrimary)
+        note("list entries (overflow)", entries, entry_index(0, kListPrimary, capw, overflow_at),
+             entry_index(last, capw - 1, capw, overflow_at));
+    for (const int64_t lid : {(int64_t)0, last}) {
+        const int64_t hi = capw - 1;
+        const int64_t e1 = hi < kListPrimary ? hi : kListPrimary - 1;
+        if constexpr (std::is_const_v<T>) {
+            rd(entries, entry_index(lid, 0, capw, overflow_at));
+            rd(entries, entry_index(lid, e1, capw, overflow_at));
+            if (hi >= kListPrimary) {
+                rd(entries, entry_index(lid, kListPrimary, capw, overflow_at));
+                rd(entries, entry_index(lid, hi, capw, overflow_at));
+            }
+        } else {
+            wr(entries, entry_index(lid, 0, capw, overflow_at));
+            wr(entries, entry_index(lid, e1, capw, overflow_at));
+            if (hi >= kListPrimary) {
+                wr(entries, entry_index(lid, kListPrimary, capw, overflow_at));
+                wr(entries, entry_index(lid, hi, capw, overflow_at));
+            }
+        }
+    }
+}
+
+// Last K (or V) element a kernel reads for a contiguous cache of `heads`
+// heads: row ctx - 1 of the last head.  esize: bytes per element.
+void touch_cache(const void* c, int B, int heads, int64_t cache_len, int64_t ctx, int D, int esize)
+{
+    const unsigned char* p = static_cast<const unsigned char*>(c);
+    rd(p, 0);
+    rd(p, (((int64_t)B * heads - 1) * cache_len + ctx - 1) * D * esize + (int64_t)D * esize - 1);
+}
+
+void touch_paged(const PagedKV& pg, int B)
+{
+    rd(pg.ctx_lens, B - 1);
+    rd(pg.block_table, (int64_t)B * pg.max_pages - 1);
+}
+
+void touch_partials(const Partials& p, int64_t parts, int D)
+{
+    wr_span("partials m", p.m, parts);
+    wr_span("partials l", p.l, parts);
+    wr_span("partials c", p.c, parts);
+    wr_span("partials o", p.o, parts * D);
+}
+
+}  // namespace
+
+hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t)
+{
+    ++g_launches;
+    EXPECT(D == 32 || D == 64 || D == 128);
+    EXPECT(a.B >= 1 && a.hk >= 1 && a.hq == a.hk * a.Gk && a.Gk <= 16);
+    EXPECT((int64_t)a.B * a.hk <= 65535);                       // grid.y
+    EXPECT(a.chunks >= 1 && a.rows_per_chunk >= 1);
+    EXPECT((int64_t)a.chunks * a.rows_per_chunk >= a.ctx);      // every row in a chunk
+    EXPECT((int64_t)(a.chunks - 1) * a.rows_per_chunk < a.ctx); // no chunk entirely empty
+    EXPECT(a.rows_per_chunk % 64 == 0);                         // whole 4-wave tiles
+    EXPECT((int64_t)a.chunks * kWavesPerBlock <= kMaxListsPerRow);
+    const int64_t lists = (int64_t)a.B * a.hq * a.chunks * kWavesPerBlock;
+    const int64_t capw = a.rows_per_chunk / kWavesPerBlock;
+    wr_span("list counts", a.list_count, lists);
+    wr_span("list maxima", a.list_max, lists);
+    touch_lists(a.entries, lists, capw, a.overflow_at);
+    rd_span(a.q, (int64_t)a.B * a.hq * D);
+    rd_span(a.tau, (int64_t)a.B * a.hq);
+    if (a.group_flags) rd_span("group flags", a.group_flags, (int64_t)a.B * a.hk);
+    if (a.k_scale) rd_span(a.k_scale, (int64_t)a.B * a.hk);
+    if (a.logits_out) wr_span(a.logits_out, (int64_t)a.B * a.hq * a.ctx);
+    if (a.bitmap) {
+        EXPECT(a.bitmap_words * 32 >= a.cache_len);
+        wr(a.bitmap, 0);
+        wr(a.bitmap, ((int64_t)a.B * a.hq - 1) * a.bitmap_words + (a.ctx - 1) / 32);
+    }
+    if (a.pg.block_table) touch_paged(a.pg, a.B);
+    else touch_cache(a.k, a.B, a.hk, a.cache_len, a.ctx, D, a.k_scale ? 1 : 2);
+    return hipSuccess;
+}
+
+hipError_t launch_gather(int D, const GatherArgs& a, hipStream_t)
+{
+    ++g_launches;
+    EXPECT(D == 32 || D == 64 || D == 128);
+    EXPECT(a.segs >= 1 && a.chunks >= 1);
+    EXPECT((int64_t)a.chunks * kWavesPerBlock <= kMaxListsPerRow);
+    EXPECT(a.hq == a.hv * a.Gv);
+    EXPECT((int64_t)a.segs * a.B * a.hq <= 0x7fffffffLL);      // 1-D grid
+    const int64_t lists = (int64_t)a.B * a.hq * a.chunks * kWavesPerBlock;
+    rd_span("list counts", a.list_count, lists);
+    rd_span("list maxima", a.list_max, lists);
+    touch_lists(a.entries, lists, a.rows_per_chunk / kWavesPerBlock, a.overflow_at);
+    if (a.tau_filter) rd_span(a.tau_filter, (int64_t)a.B * a.hq);
+    if (a.v_scale) rd_span(a.v_scale, (int64_t)a.B * a.hv);
+    touch_partials(a.part, (int64_t)a.B * a.hq * a.segs, D);
+    if (a.pg.block_table) touch_paged(a.pg, a.B);
+    else touch_cache(a.v, a.B, a.hv, a.cache_len, a.cache_len, D, a.v_scale ? 1 : 2);
+    return hipSuccess;
+}
+
+hipError_t launch_combine(int D, const Partials& p, int rows, int parts, uint16_t* out,
+                          int32_t* counts, hipStream_t)
+{
+    ++g_launches;
+    EXPECT(D == 32 || D == 64 || D == 128);
+    EXPECT(rows >= 1 && parts >= 1);
+    const int64_t n = (int64_t)rows * parts;
+    rd_span("partials m", p.m, n);
+    rd_span("partials l", p.l, n);
+    rd_span("partials c", p.c, n);
+    rd_span("partials o", p.o, n * D);
+    wr_span(out, (int64_t)rows * D);
+    if (counts) wr_span(counts, rows);
+    return hipSuccess;
+}
+
+hipError_t launch_sample(int D, const SampleArgs& a, hipStream_t)
+{
+    ++g_launches;
+    EXPECT(D == 32 || D == 64 || D == 128);
+    EXPECT(a.m >= 1 && a.m <= kSampleMax && (a.m % 16 == 0 || a.m == a.ctx));
+    EXPECT(a.stride % 16 == 0 && a.stride >= 16);
+    EXPECT(a.rank >= 1 && a.rank <= a.m);
+    const int64_t last_row = (int64_t)((a.m - 1) / 16) * a.stride + (a.m - 1) % 16;
+    EXPECT(last_row < a.ctx);
+    rd_span(a.q, (int64_t)a.B * a.hq * D);
+    wr_span("sample logits", a.sample, ((int64_t)a.B * a.hq - 1) * kSampleMax + a.m);
+    wr_span("pivots", a.pivot, (int64_t)a.B * a.hq);
+    if (a.group_flags) wr_span("group flags", a.group_flags, (int64_t)a.B * a.hk);
+    if (a.k_scale) rd_span(a.k_scale, (int64_t)a.B * a.hk);
+    if (a.pg.block_table) touch_paged(a.pg, a.B);
+    else touch_cache(a.k, a.B, a.hk, a.cache_len, last_row + 1, D, a.k_scale ? 1 : 2);
+    return hipSuccess;
+}
+
+hipError_t launch_refresh_final(int D, const FinalArgs& a, hipStream_t)
+{
+    ++g_launches;
+    EXPECT(D == 32 || D == 64 || D == 128);
+    EXPECT(a.top_n >= 1 && (int64_t)a.top_n < a.ctx);
+    EXPECT((int64_t)a.chunks * kWavesPerBlock <= kMaxListsPerRow);
+    const int64_t lists = (int64_t)a.B * a.hq * a.chunks * kWavesPerBlock;
+    rd_span("list counts", a.list_count, lists);
+    touch_lists(a.entries, lists, a.rows_per_chunk / kWavesPerBlock, a.overflow_at);
+    wr_span(a.tau, (int64_t)a.B * a.hq);
+    if (a.group_flags) wr_span("group flags", a.group_flags, (int64_t)a.B * a.hk);
+    rd_span(a.q, (int64_t)a.B * a.hq * D);
+    if (a.k_scale) rd_span(a.k_scale, (int64_t)a.B * a.hk);
+    if (a.pg.block_table) touch_paged(a.pg, a.B);
+    else touch_cache(a.k, a.B, a.hk, a.cache_len, a.ctx, D, a.k_scale ? 1 : 2);
+    return hipSuccess;
+}
+
+hipError_t launch_full(int DK, int DV, int maxs, const FullArgs& a, hipStream_t)
+{
+    ++g_launches;
+    EXPECT(maxs == 2 || maxs == 4 || maxs == 8);
+    EXPECT(a.nv >= 1 && a.nv <= 4);
+    EXPECT(a.chunks >= 1 && (int64_t)a.chunks * a.rows_per_chunk >= a.ctx);
+    EXPECT((int64_t)(a.chunks - 1) * a.rows_per_chunk < a.ctx);
+    EXPECT((int64_t)a.B * a.hk <= 65535);
+    EXPECT(a.wave_lds * kWavesPerBlock <= 160 * 1024);
+    touch_partials(a.part, (int64_t)a.B * a.hq * a.chunks, DV);
+    rd_span(a.q, (int64_t)a.B * a.hq * DK);
+    touch_cache(a.k, a.B, a.hk, a.cache_len, a.ctx, DK, 2);
+    touch_cache(a.v, a.B, a.hv, a.cache_len, a.ctx, DV, 2);
+    return hipSuccess;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t, hipStream_t)
+{
+    ++g_launches;
+    wr_span(p, n);
+    return hipSuccess;
+}
+
+}  // namespace saga

@@ -3,7 +3,9 @@
 Token j of a step with l_q tokens attends rows 0 .. ctx - l_q + j and keeps a
 threshold of its own.  Per token the calls must equal the one-token calls run
 with that token's queries at ctx - (l_q - 1 - j): thresholds bit-equal, counts
-equal, and outputs within the output bar of the fp64 oracle on that mask.
+equal, and outputs within the output bar of the fp64 oracle on that mask.  The
+thresholds and selections are also checked against the oracle's Atop-N run of
+that token's sub-problem (tau within 1e-4; sets equal away from 1e-3 of tau).
 """
 import numpy as np
 import pytest
@@ -11,11 +13,12 @@ import torch
 
 import oracle
 import sparse_decode_attention_atop_amd as saga
-from gpu_helpers import make_inputs, to_np_bits
+from gpu_helpers import Guards, bitmap_to_bool, make_inputs, to_np_bits
 
 pytestmark = pytest.mark.gpu
 
 OUT_TOL = 1e-2
+NEAR_TAU = 1e-3
 
 LQ_SHAPES = {
     # name: (B, hq, hk, hv, d, L, T, N, n, l_q)
@@ -30,13 +33,14 @@ def run_lq(q, K, V, ctx_steps, N, n, lq, fused=True):
     T, B, hql, d = q.shape
     hq = hql // lq
     hk, rows, hv = K.shape[1], K.shape[2], V.shape[1]
-    ws = saga.alloc_workspace_lq(saga.dims(B, hq, hk, hv, d, ctx_steps[0], rows), lq, N)
-    tau = torch.empty(B, hq, lq, device="cuda")
+    g = Guards()
+    ws = g.workspace(saga.dims(B, hq, hk, hv, d, ctx_steps[0], rows), N, lq=lq)
+    tau = g.empty((B, hq, lq), torch.float32, "tau")
     res = []
     for t, ctx in enumerate(ctx_steps):
         dm = saga.dims(B, hq, hk, hv, d, ctx, rows)
-        out = torch.empty(B, hq, lq, d, dtype=torch.bfloat16, device="cuda")
-        cnt = torch.empty(B, hq, lq, dtype=torch.int32, device="cuda")
+        out = g.empty((B, hq, lq, d), torch.bfloat16, "out")
+        cnt = g.empty((B, hq, lq), torch.int32, "sel_counts")
         if t % n == 0 and fused:
             saga.atopn_refresh_decode_step_lq(dm, lq, N, q[t], K, V, tau, out, ws, sel_counts=cnt)
         else:
@@ -44,6 +48,8 @@ def run_lq(q, K, V, ctx_steps, N, n, lq, fused=True):
                 saga.atopn_refresh_thresholds_lq(dm, lq, N, q[t], K, tau, ws)
             saga.saga_decode_step_lq(dm, lq, q[t], K, V, tau, out, ws, sel_counts=cnt)
         torch.cuda.synchronize()
+        g.check(f"at step {t}")
+        g.bufs = g.bufs[:2]
         res.append((tau.clone(), cnt.clone(), out.clone()))
     return res
 
@@ -52,18 +58,21 @@ def run_one_token(q, K, V, ctx_steps, N, n):
     """The one-token calls; also the selection bitmap of every step."""
     T, B, hq, d = q.shape
     hk, rows, hv = K.shape[1], K.shape[2], V.shape[1]
-    ws = saga.alloc_workspace(saga.dims(B, hq, hk, hv, d, ctx_steps[0], rows), N)
-    tau = torch.empty(B, hq, device="cuda")
+    g = Guards()
+    ws = g.workspace(saga.dims(B, hq, hk, hv, d, ctx_steps[0], rows), N)
+    tau = g.empty((B, hq), torch.float32, "tau")
     res = []
     for t, ctx in enumerate(ctx_steps):
         dm = saga.dims(B, hq, hk, hv, d, ctx, rows)
         if t % n == 0:
             saga.atopn_refresh_thresholds(dm, N, q[t], K, tau, ws)
-        out = torch.empty(B, hq, d, dtype=torch.bfloat16, device="cuda")
-        cnt = torch.empty(B, hq, dtype=torch.int32, device="cuda")
-        bm = torch.empty(B, hq, (rows + 31) // 32, dtype=torch.int32, device="cuda")
+        out = g.empty((B, hq, d), torch.bfloat16, "out")
+        cnt = g.empty((B, hq), torch.int32, "sel_counts")
+        bm = g.empty((B, hq, (rows + 31) // 32), torch.int32, "sel_bitmap")
         saga.saga_decode_step(dm, q[t], K, V, tau, out, ws, sel_counts=cnt, sel_bitmap_debug=bm)
         torch.cuda.synchronize()
+        g.check(f"at step {t}")
+        g.bufs = g.bufs[:2]
         res.append((tau.clone(), cnt.clone(), out.clone(), bm.cpu().numpy().view(np.uint32)))
     return res
 
@@ -87,6 +96,8 @@ def test_each_token_equals_the_one_token_path(name, fused):
         qj = q[:, :, j::lq].contiguous()                             # [T][B][hq][d]
         ctx_j = [c - (lq - 1 - j) for c in ctx]
         ref = run_one_token(qj, K, V, ctx_j, N, n)
+        orc = oracle.atopn_run(to_np_bits(qj), Kb, Vb, ctx_j, N, n, want_sel=True,
+                               want_logits=True)
         for t in range(T):
             tau_r, cnt_r, _, bm = ref[t]
             tau_g, cnt_g, out_g = got[t]
@@ -96,5 +107,13 @@ def test_each_token_equals_the_one_token_path(name, fused):
                 assert torch.isneginf(tau_g[:, :, j]).all()
             ref_o, cnt_o = oracle.masked(qb[t][:, j::lq], Kb, Vb, ctx_j[t], bm)
             assert (cnt_o == cnt_g[:, :, j].cpu().numpy()).all()
+            tau_o = orc["tau"][t]
+            tg = tau_g[:, :, j].cpu().numpy().astype(np.float64)
+            assert ((np.abs(tg - tau_o) <= 1e-4) | (np.isneginf(tg) & np.isneginf(tau_o))).all()
+            sel = bitmap_to_bool(bm, ctx_j[t])
+            s_o = orc["logits"][t, :, :, :ctx_j[t]]
+            near = np.abs(s_o - tau_o[..., None]) <= NEAR_TAU
+            bad = (sel != orc["sel"][t, :, :, :ctx_j[t]].astype(bool)) & ~near
+            assert not bad.any(), f"token {j} step {t}: {bad.sum()} entries differ from the oracle"
             err = np.abs(out_g[:, :, j].float().cpu().numpy() - ref_o).max()
             assert err <= OUT_TOL, f"token {j} step {t}: {err:.3e}"

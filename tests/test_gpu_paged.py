@@ -15,11 +15,12 @@ import torch
 
 import oracle
 import sparse_decode_attention_atop_amd as saga
-from gpu_helpers import make_inputs, to_np_bits
+from gpu_helpers import Guards, bitmap_to_bool, make_inputs, to_np_bits
 
 pytestmark = pytest.mark.gpu
 
 OUT_TOL = 1e-2
+NEAR_TAU = 1e-3
 
 
 def to_pages(K, V, P, seed, extra=3):
@@ -45,18 +46,21 @@ def run_contiguous(q, K, V, ctx_steps, N, n):
     """Refresh at t % n == 0 (one call), decode otherwise; per-step results."""
     T, B, hq, d = q.shape
     hk, rows, hv = K.shape[1], K.shape[2], V.shape[1]
-    ws = saga.alloc_workspace(saga.dims(B, hq, hk, hv, d, ctx_steps[0], rows), N)
-    tau = torch.empty(B, hq, device="cuda")
+    g = Guards()
+    ws = g.workspace(saga.dims(B, hq, hk, hv, d, ctx_steps[0], rows), N)
+    tau = g.empty((B, hq), torch.float32, "tau")
     res = []
     for t, ctx in enumerate(ctx_steps):
         dm = saga.dims(B, hq, hk, hv, d, ctx, rows)
-        out = torch.empty(B, hq, d, dtype=torch.bfloat16, device="cuda")
-        cnt = torch.empty(B, hq, dtype=torch.int32, device="cuda")
+        out = g.empty((B, hq, d), torch.bfloat16, "out")
+        cnt = g.empty((B, hq), torch.int32, "sel_counts")
         if t % n == 0:
             saga.atopn_refresh_decode_step(dm, N, q[t], K, V, tau, out, ws, sel_counts=cnt)
         else:
             saga.saga_decode_step(dm, q[t], K, V, tau, out, ws, sel_counts=cnt)
         torch.cuda.synchronize()
+        g.check(f"at step {t}")
+        g.bufs = g.bufs[:2]
         res.append((tau.clone(), cnt.clone(), out.clone()))
     return res
 
@@ -64,16 +68,17 @@ def run_contiguous(q, K, V, ctx_steps, N, n):
 def run_paged(q, kp, vp, table, npages, P, rows, ctx_lens_steps, N, n, fused=True):
     T, B, hq, d = q.shape
     hk, hv = kp.shape[1], vp.shape[1]
+    g = Guards()
     ctx_lens = torch.empty(B, dtype=torch.int32, device="cuda")
     pg = saga.paged(table, ctx_lens, P, npages)
-    ws = saga.alloc_workspace(saga.dims(B, hq, hk, hv, d, max(ctx_lens_steps[0]), rows), N)
-    tau = torch.empty(B, hq, device="cuda")
+    ws = g.workspace(saga.dims(B, hq, hk, hv, d, max(ctx_lens_steps[0]), rows), N)
+    tau = g.empty((B, hq), torch.float32, "tau")
     res = []
     for t, lens in enumerate(ctx_lens_steps):
         ctx_lens.copy_(torch.tensor(lens, dtype=torch.int32))
         dm = saga.dims(B, hq, hk, hv, d, max(lens), rows)
-        out = torch.empty(B, hq, d, dtype=torch.bfloat16, device="cuda")
-        cnt = torch.empty(B, hq, dtype=torch.int32, device="cuda")
+        out = g.empty((B, hq, d), torch.bfloat16, "out")
+        cnt = g.empty((B, hq), torch.int32, "sel_counts")
         if t % n == 0 and fused:
             saga.atopn_refresh_decode_step_paged(dm, pg, N, q[t], kp, vp, tau, out, ws,
                                                  sel_counts=cnt)
@@ -82,6 +87,8 @@ def run_paged(q, kp, vp, table, npages, P, rows, ctx_lens_steps, N, n, fused=Tru
                 saga.atopn_refresh_thresholds_paged(dm, pg, N, q[t], kp, tau, ws)
             saga.saga_decode_step_paged(dm, pg, q[t], kp, vp, tau, out, ws, sel_counts=cnt)
         torch.cuda.synchronize()
+        g.check(f"at step {t}")
+        g.bufs = g.bufs[:2]
         res.append((tau.clone(), cnt.clone(), out.clone()))
     return res
 
@@ -145,6 +152,9 @@ def test_per_sequence_lengths_match_each_sequence_alone(fused):
         qb = q[:, b:b + 1].contiguous()
         Kb, Vb = K[b:b + 1].contiguous(), V[b:b + 1].contiguous()
         ref = run_contiguous(qb, Kb, Vb, ctx_b, N, n)
+        # The oracle on this sequence alone at its own lengths.
+        orc = oracle.atopn_run(to_np_bits(qb), to_np_bits(Kb), to_np_bits(Vb), ctx_b, N, n,
+                               want_sel=True, want_logits=True)
         for t in range(T):
             tau_r, cnt_r, _ = ref[t]
             tau_g, cnt_g, out_g = got[t]
@@ -160,9 +170,19 @@ def test_per_sequence_lengths_match_each_sequence_alone(fused):
             saga.saga_decode_step(dm, qb[t], Kb, Vb, tau_g[b:b + 1].contiguous(), o1, ws,
                                   sel_bitmap_debug=bm)
             torch.cuda.synchronize()
+            bm_np = bm.cpu().numpy().view(np.uint32)
             ref_o, cnt_o = oracle.masked(to_np_bits(qb[t]), to_np_bits(Kb), to_np_bits(Vb),
-                                         ctx_b[t], bm.cpu().numpy().view(np.uint32))
+                                         ctx_b[t], bm_np)
             assert (cnt_o[0] == cnt_g[b].cpu().numpy()).all()
+            # Thresholds and selection against the oracle's Atop-N run.
+            tau_o = orc["tau"][t, 0]
+            tg = tau_g[b].cpu().numpy().astype(np.float64)
+            assert ((np.abs(tg - tau_o) <= 1e-4) | (np.isneginf(tg) & np.isneginf(tau_o))).all()
+            sel = bitmap_to_bool(bm_np[0], ctx_b[t])
+            s = orc["logits"][t, 0, :, :ctx_b[t]]
+            near = np.abs(s - tau_o[:, None]) <= NEAR_TAU
+            bad = (sel != orc["sel"][t, 0, :, :ctx_b[t]].astype(bool)) & ~near
+            assert not bad.any(), f"b={b} t={t}: {bad.sum()} entries differ from the oracle"
             err = np.abs(out_g[b].float().cpu().numpy() - ref_o[0]).max()
             assert err <= OUT_TOL, f"b={b} t={t}: {err:.3e}"
 
