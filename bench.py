@@ -88,8 +88,9 @@ def parse():
                    help="markdown summary holding rocprofv3-measured HBM bytes per decode call "
                         "(default: profiles/traffic_<workload>.md)")
     p.add_argument("--calibrate", action="store_true",
-                   help="time a plain 4 GiB device copy and read (HBM ceiling; the copy is "
-                        "the known-size kernel that scales rocprofv3 byte counters)")
+                   help="measured HBM ceilings: sequential read and random-row probe kernels, "
+                        "and a 4 GiB device copy (the known-size kernel that scales rocprofv3 "
+                        "byte counters)")
     p.add_argument("--eager-only", action="store_true",
                    help="one eager pass over the decode steps, no timing (for counter runs)")
     p.add_argument("--paged", type=int, default=0,
@@ -112,29 +113,70 @@ def parse():
 
 
 def calibrate(torch):
-    """Measured HBM ceilings: torch's device copy (read + write) and sum (read)."""
+    """Measured HBM ceilings for the decode step's two access patterns, from
+    the committed probe kernels (libsaga_probe.so): a sequential read of
+    contiguous per-workgroup chunks (the K stream) and reads of pseudo-random
+    64/128/256-byte rows of an 8 GiB buffer with fresh rows every launch (the
+    value gather), each swept over workgroup counts and loads in flight; plus
+    torch's 4 GiB device copy, the known-size kernel that scales rocprofv3's
+    byte counters.  Prints one JSON line."""
+    from sparse_decode_attention_atop_amd import probe
+
+    def timed(fn, reps=10):
+        fn(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps):
+            fn(r + 1)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3
+
+    sink = torch.empty(1 << 20, dtype=torch.int32, device="cuda")
+    seq = []
+    buf = torch.ones(4 << 30, dtype=torch.uint8, device="cuda")
+    for total in (1 << 30, 4 << 30):
+        for wg in (256, 512, 768, 1024, 1536, 2048):
+            nbytes = total // (wg * 4096) * (wg * 4096)
+            for depth in (1, 2, 4):
+                sec = timed(lambda r: probe.probe_read(buf, nbytes, wg, depth, sink))
+                seq.append({"bytes": nbytes, "workgroups": wg, "depth": depth,
+                            "us": round(sec * 1e6, 2), "gbs": round(nbytes / sec / 1e9, 1)})
+                log(f"read {nbytes >> 20} MiB wg={wg} depth={depth}: {seq[-1]['gbs']} GB/s")
+    del buf
+    torch.cuda.empty_cache()
+    rows_res = {}
+    big = torch.ones(8 << 30, dtype=torch.uint8, device="cuda")
+    gather_bytes = 148 << 20                 # about one Llama-like 128K B=16 gather
+    for rb in (64, 128, 256):
+        pts = []
+        n = gather_bytes // rb
+        for wg in (1024, 2048, 4096):
+            for depth in (2, 4, 8):
+                sec = timed(lambda r: probe.probe_rows(big, rb, n, 1000 * r + wg + depth, wg,
+                                                       depth, sink))
+                pts.append({"rows": n, "workgroups": wg, "depth": depth,
+                            "us": round(sec * 1e6, 2), "gbs": round(n * rb / sec / 1e9, 1)})
+                log(f"rows {rb} B x {n} wg={wg} depth={depth}: {pts[-1]['gbs']} GB/s")
+        best = max(pts, key=lambda p: p["gbs"])
+        rows_res[str(rb)] = {"best_gbs": best["gbs"], "best": best, "table": pts}
+    del big
+    torch.cuda.empty_cache()
     n = 4 << 30
     src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
     dst = torch.empty_like(src)
-    acc = torch.empty(1, dtype=torch.float32, device="cuda")
-
-    def timed(fn, reps=10):
-        fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps / 1e3
-
-    t_copy = timed(lambda: dst.copy_(src))
-    t_read = timed(lambda: torch.sum(src, dim=0, keepdim=True, dtype=torch.float32, out=acc))
-    print(json.dumps({"calibration": "device copy and read of 4 GiB",
-                      "copy_bytes_read": n, "copy_bytes_written": n,
-                      "copy_gbs": round(2 * n / t_copy / 1e9, 1),
-                      "read_gbs": round(n / t_read / 1e9, 1)}), flush=True)
+    t_copy = timed(lambda r: dst.copy_(src))
+    best_seq = {tot: max((p for p in seq if p["bytes"] > tot // 2 and p["bytes"] <= tot),
+                         key=lambda p: p["gbs"]) for tot in (1 << 30, 4 << 30)}
+    print(json.dumps({
+        "calibration": "HBM ceilings of the decode step's access patterns (probe kernels)",
+        "peak_gbs": HBM_PEAK_GBS,
+        "sequential_read": {"best_1gib": best_seq[1 << 30], "best_4gib": best_seq[4 << 30],
+                            "table": seq},
+        "random_rows": rows_res,
+        "torch_copy_4gib": {"bytes_read": n, "bytes_written": n,
+                            "gbs_read_plus_written": round(2 * n / t_copy / 1e9, 1)}}), flush=True)
 
 
 def layer_inputs(torch, wl, w, layer):

@@ -4,7 +4,9 @@
 
 Each ``csrc/*.hip`` file is compiled to an object for gfx950 and the objects
 are linked into ``sparse_decode_attention_atop_amd/libsaga.so``.  Only the
-symbols declared in ``include/saga.h`` are exported.
+symbols declared in ``include/saga.h`` are exported.  The HBM measurement
+kernels in ``probe/*.hip`` are linked into ``libsaga_probe.so`` (symbols of
+``include/saga_probe.h``); the decode library does not use them.
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsaga.so")
+PROBE_LIB = os.path.join(PKG, "libsaga_probe.so")
+PROBE_SRC = os.path.join(PKG, "probe")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -32,8 +36,8 @@ CFLAGS = [
 ]
 
 
-def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+def sources(folder=CSRC):
+    return sorted(glob.glob(os.path.join(folder, "*.hip")))
 
 
 def _compile(src: str, extra=(), build_dir=BUILD_DIR) -> str:
@@ -50,24 +54,33 @@ def _compile(src: str, extra=(), build_dir=BUILD_DIR) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
-    """Compile every HIP source and link libsaga.so; returns the library path.
-
-    ``extra_flags`` (e.g. ``-DSAGA_STREAM_U64=4``) and ``out`` build a variant
-    with other tuning constants somewhere else."""
-    build_dir = BUILD_DIR if out == LIB else out + ".objs"
-    os.makedirs(build_dir, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, tuple(extra_flags), build_dir), srcs))
+def _link(objs, out):
     tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, out)
+
+
+def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
+    """Compile every HIP source and link libsaga.so; returns the library path.
+    The default build also links libsaga_probe.so.
+
+    ``extra_flags`` (e.g. ``-DSAGA_STREAM_U64=4``) and ``out`` build a variant
+    with other tuning constants somewhere else."""
+    build_dir = BUILD_DIR if out == LIB else out + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = sources()
+    probe_srcs = sources(PROBE_SRC) if out == LIB else []
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probe_srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, tuple(extra_flags), build_dir), srcs))
+        probe_objs = list(ex.map(lambda s: _compile(s, (), build_dir), probe_srcs))
+    _link(objs, out)
+    if probe_objs:
+        _link(probe_objs, PROBE_LIB)
     if verbose:
-        print(f"built {out}")
+        print(f"built {out}" + (f" and {PROBE_LIB}" if probe_objs else ""))
     return out
 
 

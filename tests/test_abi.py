@@ -15,8 +15,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "saga.h")
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text,
                                  flags=re.M)))
@@ -36,6 +36,26 @@ def test_exports_match_header():
     lib = saga.library()
     for name in declared:
         assert hasattr(lib, name)
+
+
+def test_probe_library_exports_match_its_header():
+    """The HBM measurement kernels (libsaga_probe.so) export exactly the
+    functions include/saga_probe.h declares."""
+    from sparse_decode_attention_atop_amd import probe
+    declared = header_functions(os.path.join(ROOT, "include", "saga_probe.h"))
+    assert declared == sorted(probe.EXPORTED_SYMBOLS)
+    out = subprocess.run(["nm", "-D", "--defined-only", probe.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(ln.split()[-1] for ln in out.splitlines() if " T " in ln)
+    assert exported == declared
+    lib = probe.library()
+    fake = ctypes.c_void_p(1 << 20)
+    # Arguments are checked before any launch (no GPU needed for these).
+    assert lib.saga_probe_read(None, 4096, 1, 1, fake, None) == 1
+    assert lib.saga_probe_read(fake, 4096 * 3, 2, 1, fake, None) == 1      # not whole chunks
+    assert lib.saga_probe_read(fake, 4096, 1, 3, fake, None) == 1          # depth 3
+    assert lib.saga_probe_rows(fake, 1 << 20, 96, 10, 0, 1, 2, fake, None) == 1
+    assert lib.saga_probe_rows(fake, 1 << 20, 128, 0, 0, 1, 2, fake, None) == 1
 
 
 def test_status_strings_and_version():
