@@ -149,6 +149,30 @@ int saga_decode_step(const saga_dims* dims, const void* q_dev, const void* k_cac
                      void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
+ * saga_decode_step() without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the workspace is a device array inside
+ * the library, SAGA_NOALLOC_SCRATCH_BYTES bytes per device, held by each GPU
+ * the library runs on until the process ends.  Results are bit-identical to
+ * saga_decode_step() with the same arguments (no selection bitmap here).
+ *
+ * The call allocates nothing.  Its first call on a device looks the array up
+ * (hipGetSymbolAddress, with that device current); make that first call
+ * outside stream capture.  Every call on one device shares that device's
+ * array: calls that overlap in time on one device (concurrent streams or
+ * threads) race on it and must be serialised by the caller.  The array keeps
+ * the last call's contents; nothing in it needs to start at zero.
+ *
+ * Errors: as saga_decode_step(), and SAGA_ERR_WORKSPACE_TOO_SMALL when
+ * saga_workspace_bytes(dims, top_n) exceeds SAGA_NOALLOC_SCRATCH_BYTES (for
+ * example batch 1 at 128K context fits; batch 16 does not).
+ */
+#define SAGA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int saga_decode_step_noalloc(const saga_dims* dims, const void* q_dev, const void* k_cache_dev,
+                             const void* v_cache_dev, const float* thresholds_dev, void* out_dev,
+                             int32_t* sel_counts_dev, void* stream);
+
+/*
  * A refresh step in one call: the same results as atopn_refresh_thresholds()
  * followed by saga_decode_step() with the fresh thresholds, with one pass over
  * the K cache instead of two (the refresh's candidate lists already hold every

@@ -37,7 +37,10 @@ EXPORTED_SYMBOLS = ("saga_workspace_bytes", "atopn_refresh_thresholds", "saga_de
                     "atopn_refresh_decode_step_lq", "atopn_refresh_thresholds_fp8k",
                     "saga_decode_step_fp8k", "atopn_refresh_decode_step_fp8k",
                     "saga_decode_step_fp8kv", "atopn_refresh_decode_step_fp8kv",
-                    "saga_full_attention", "saga_status_string", "saga_version")
+                    "saga_full_attention", "saga_decode_step_noalloc", "saga_status_string",
+                    "saga_version")
+
+NOALLOC_SCRATCH_BYTES = 64 << 20     # SAGA_NOALLOC_SCRATCH_BYTES in include/saga.h
 
 SAGA_OK = 0
 SAGA_ERR_INVALID_ARGUMENT = 1
@@ -136,6 +139,8 @@ def library():
         lib.atopn_refresh_decode_step_fp8kv.restype = ctypes.c_int
         lib.saga_full_attention.argtypes = [pd, vp, vp, vp, vp, vp, sz, vp]
         lib.saga_full_attention.restype = ctypes.c_int
+        lib.saga_decode_step_noalloc.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp]
+        lib.saga_decode_step_noalloc.restype = ctypes.c_int
         lib.saga_status_string.argtypes = [ctypes.c_int]
         lib.saga_status_string.restype = ctypes.c_char_p
         lib.saga_version.argtypes = []
@@ -554,3 +559,22 @@ def saga_full_attention(d: SagaDims, q: torch.Tensor, k_cache: torch.Tensor,
         ctypes.byref(d), _ptr(q, torch.bfloat16, "q"), _ptr(k_cache, torch.bfloat16, "k_cache"),
         _ptr(v_cache, torch.bfloat16, "v_cache"), _ptr(out, torch.bfloat16, "out"), ws, nbytes,
         _stream(stream)), "saga_full_attention")
+
+
+def saga_decode_step_noalloc(d: SagaDims, q: torch.Tensor, k_cache: torch.Tensor,
+                             v_cache: torch.Tensor, thresholds: torch.Tensor, out: torch.Tensor,
+                             sel_counts: Optional[torch.Tensor] = None, stream=None) -> None:
+    """saga_decode_step without a workspace: the library's own per-device
+    scratch (NOALLOC_SCRATCH_BYTES) is used; calls on one device must not overlap."""
+    bh = d.batch * d.h_q
+    _need(q, bh * d.head_dim, "q")
+    _need(k_cache, d.batch * d.h_k * d.cache_len * d.head_dim, "k_cache")
+    _need(v_cache, d.batch * d.h_v * d.cache_len * _dv(d), "v_cache")
+    _need(thresholds, bh, "thresholds")
+    _need(out, bh * _dv(d), "out")
+    _need(sel_counts, bh, "sel_counts")
+    _check(library().saga_decode_step_noalloc(
+        ctypes.byref(d), _ptr(q, torch.bfloat16, "q"), _ptr(k_cache, torch.bfloat16, "k_cache"),
+        _ptr(v_cache, torch.bfloat16, "v_cache"), _ptr(thresholds, torch.float32, "thresholds"),
+        _ptr(out, torch.bfloat16, "out"), _ptr(sel_counts, torch.int32, "sel_counts"),
+        _stream(stream)), "saga_decode_step_noalloc")

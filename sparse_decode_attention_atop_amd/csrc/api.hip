@@ -499,6 +499,27 @@ int do_refresh_decode(const saga_dims* dims, const RowModel& rm, int32_t top_n,
 
 }  // namespace
 
+namespace saga {
+
+// saga_decode_step with the selection bitmap off, for the other source files
+// of the library (declared in kernels.hpp).
+size_t decode_workspace_bytes(const saga_dims* dims)
+{
+    return validate_dims(dims) == SAGA_OK ? make_layout(dims).total : 0;
+}
+
+int decode_step(const saga_dims* dims, const void* q_dev, const void* k_dev, const void* v_dev,
+                const float* thresholds_dev, void* out_dev, int32_t* sel_counts_dev,
+                void* workspace_dev, size_t workspace_bytes, void* stream)
+{
+    const int st = validate_dims(dims);
+    if (st != SAGA_OK) return st;
+    return do_decode(dims, RowModel{}, q_dev, k_dev, v_dev, thresholds_dev, out_dev,
+                     sel_counts_dev, nullptr, workspace_dev, workspace_bytes, stream);
+}
+
+}  // namespace saga
+
 SAGA_EXPORT int atopn_refresh_thresholds(const saga_dims* dims, int32_t top_n, const void* q_dev,
                                          const void* k_cache_dev, float* thresholds_dev,
                                          float* logits_debug_dev, void* workspace_dev,

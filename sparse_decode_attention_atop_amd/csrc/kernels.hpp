@@ -222,3 +222,14 @@ hipError_t launch_full(int DK, int DV, int maxs, const FullArgs& a, hipStream_t 
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 
 }  // namespace saga
+
+// Host entry points of api.hip used by the other source files (not exported).
+struct saga_dims;
+namespace saga {
+// Workspace bytes of a decode step for dims (0 if the dims are invalid).
+size_t decode_workspace_bytes(const saga_dims* dims);
+// saga_decode_step without the selection bitmap.
+int decode_step(const saga_dims* dims, const void* q_dev, const void* k_dev, const void* v_dev,
+                const float* thresholds_dev, void* out_dev, int32_t* sel_counts_dev,
+                void* workspace_dev, size_t workspace_bytes, void* stream);
+}  // namespace saga
