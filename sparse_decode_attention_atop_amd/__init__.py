@@ -30,6 +30,9 @@ __all__ = [
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsaga.so")
+# Another build of the same library (e.g. with other tuning constants, from
+# build.build(extra_flags=..., out=...)) for measurements; the in-tree build otherwise.
+LIB_PATH = os.environ.get("SAGA_LIBRARY", LIB_PATH)
 EXPORTED_SYMBOLS = ("saga_workspace_bytes", "atopn_refresh_thresholds", "saga_decode_step",
                     "atopn_refresh_decode_step", "atopn_refresh_thresholds_paged",
                     "saga_decode_step_paged", "atopn_refresh_decode_step_paged",

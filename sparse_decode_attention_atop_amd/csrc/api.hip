@@ -349,7 +349,112 @@ int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunkin
                                      sel_counts_dev, s));
 }
 
-// Decode with kept thresholds: stream-select into the lists, then gather.
+// The small-batch path (fused.hip): with few (b, key head) groups a decode
+// call is a chain of latency-bound launches, so the value gather runs inside
+// the K-stream kernel, from entries kept in LDS.  The chunks are the pair
+// plan of the stream (the same for paged and contiguous caches, so both give
+// the same sums), shortened when needed so that a chunk's worst case (every
+// row selected for every head slot) fits the LDS budget; never more chunks
+// than the workspace's partials hold.
+struct FusedPlan {
+    bool use = false;
+    Chunking ch{};
+    int32_t qcap = 0, hcap = 0, unroll = 1;
+    size_t lds = 0;
+};
+
+FusedPlan plan_fused(const saga_dims* dims, const Layout& L, const RowModel& rm)
+{
+    FusedPlan best;
+    if (rm.v_scale) return best;                    // fp8 values: the list path
+    const int64_t groups = (int64_t)dims->batch * dims->h_k;
+    if (groups > SAGA_FUSED_MAX_GROUPS) return best;
+    const int D = dims->head_dim, DV = value_dim(dims);
+    const bool k8 = rm.k_scale != nullptr;
+    const int Gk = dims->h_q / dims->h_k;
+    const int64_t per_queue = (Gk + 3) / 4;         // head slots sharing one queue
+    // LDS bytes per row of a chunk: the queues (4 waves x 4 queues x 1/4 row x
+    // per_queue entries of 8 bytes) and the per-slot index lists (G_k x 2 bytes).
+    const int64_t row_bytes = 32 * per_queue + 2 * Gk;
+    const int64_t R = kBlock / (Gk * (DV / 8));
+    const size_t red = (size_t)(R * Gk * DV + R * Gk) * 4;
+    auto lds_of = [&](int64_t rows) {
+        const size_t lists = round_up((size_t)rows * row_bytes, 16);
+        return lists > red ? lists : red;
+    };
+    // Tiles of two 16-row groups halve a long chunk's dependent round trips;
+    // they are taken unless their longer pairs cost more than 30% of the chunks.
+    for (const int U : {1, 2}) {
+        const int64_t pair = 2 * fused_block_rows(U, k8);
+        Chunking ch = split_rows(dims->ctx_len, groups, pair, target_blocks(D, k8), L.max_chunks);
+        // Shorten the chunks until their worst case fits the LDS with every
+        // workgroup of the launch resident at once.
+        bool ok = false;
+        for (;;) {
+            const int64_t per_cu = (groups * ch.chunks + kComputeUnits - 1) / kComputeUnits;
+            const size_t cap = (size_t)kLdsPerCu / (size_t)per_cu;
+            if (lds_of(ch.rows) <= (cap < (size_t)kLdsPerGroup ? cap : (size_t)kLdsPerGroup)) {
+                ok = true;
+                break;
+            }
+            if (ch.rows <= pair) break;
+            ch.rows -= pair;
+            ch.chunks = (int)((dims->ctx_len + ch.rows - 1) / ch.rows);
+            if (ch.chunks > L.max_chunks) break;
+        }
+        if (!ok) continue;
+        if (best.use && 10 * ch.chunks < 7 * best.ch.chunks) continue;
+        FusedPlan f;
+        f.use = true;
+        f.unroll = U;
+        f.ch = ch;
+        f.qcap = (int32_t)(ch.rows / kWavesPerBlock * per_queue);
+        f.hcap = (int32_t)ch.rows;
+        f.lds = lds_of(ch.rows);
+        best = f;
+    }
+    return best;
+}
+
+int enqueue_fused(const saga_dims* dims, const Layout& L, const FusedPlan& f, const void* q_dev,
+                  const void* k_cache_dev, const void* v_cache_dev, const float* thresholds_dev,
+                  void* out_dev, int32_t* sel_counts_dev, uint32_t* sel_bitmap_debug_dev,
+                  int64_t words, void* workspace_dev, hipStream_t s, const RowModel& rm)
+{
+    FusedArgs a{};
+    a.q = static_cast<const uint16_t*>(q_dev);
+    a.k = static_cast<const uint16_t*>(k_cache_dev);
+    a.v = static_cast<const uint16_t*>(v_cache_dev);
+    a.tau = thresholds_dev;
+    a.bitmap = sel_bitmap_debug_dev;
+    a.bitmap_words = words;
+    a.part = partials(workspace_dev, L);
+    a.B = dims->batch;
+    a.hq = dims->h_q;
+    a.hk = dims->h_k;
+    a.hv = dims->h_v;
+    a.Gk = dims->h_q / dims->h_k;
+    a.Gv = dims->h_q / dims->h_v;
+    a.ctx = dims->ctx_len;
+    a.cache_len = dims->cache_len;
+    a.rows_per_chunk = f.ch.rows;
+    a.chunks = f.ch.chunks;
+    a.qcap = f.qcap;
+    a.hcap = f.hcap;
+    a.unroll = f.unroll;
+    a.scale = dims->scale;
+    a.lq = rm.lq;
+    a.k_scale = rm.k_scale;
+    a.pg = rm.pg;
+    const int st = hip_status(launch_select_gather(dims->head_dim, value_dim(dims), a, f.lds, s));
+    if (st != SAGA_OK) return st;
+    return hip_status(launch_combine_parts(value_dim(dims), a.part, dims->batch * dims->h_q,
+                                           f.ch.chunks, static_cast<uint16_t*>(out_dev),
+                                           sel_counts_dev, s));
+}
+
+// Decode with kept thresholds: stream-select into the lists, then gather
+// (or the small-batch path above).
 int enqueue_decode(const saga_dims* dims, const Layout& L, const void* q_dev,
                    const void* k_cache_dev, const void* v_cache_dev, const float* thresholds_dev,
                    void* out_dev, int32_t* sel_counts_dev, uint32_t* sel_bitmap_debug_dev,
@@ -363,6 +468,10 @@ int enqueue_decode(const saga_dims* dims, const Layout& L, const void* q_dev,
         st = hip_status(launch_fill_u32(sel_bitmap_debug_dev, (int64_t)rows * words, 0u, s));
         if (st != SAGA_OK) return st;
     }
+    const FusedPlan f = plan_fused(dims, L, rm);
+    if (f.use)
+        return enqueue_fused(dims, L, f, q_dev, k_cache_dev, v_cache_dev, thresholds_dev, out_dev,
+                             sel_counts_dev, sel_bitmap_debug_dev, words, workspace_dev, s, rm);
     const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
                                     D, L.max_chunks, rm.k_scale != nullptr,
                                     rm.pg.block_table != nullptr);

@@ -20,6 +20,18 @@ constexpr int decode_block_rows(int D) { return kWavesPerBlock * 16 * decode_unr
 // fp8 K: tiles of SAGA_STREAM_K8_UMUL times the rows of bf16 tiles.
 constexpr int decode_unroll_k8(int D) { return SAGA_STREAM_K8_UMUL * decode_unroll(D); }
 constexpr int decode_block_rows_k8(int D) { return kWavesPerBlock * 16 * decode_unroll_k8(D); }
+// MI355X: compute units, LDS per CU, and the LDS one workgroup may use.
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kLdsPerCu = 160 * 1024;
+constexpr int64_t kLdsPerGroup = 64 * 1024;
+
+// Small-batch fused path: 16-row groups per wave tile, 1 or 2, chosen per call
+// (2 halves the dependent round trips of a long chunk; a tile pair of 2 is
+// 256 rows, which still never straddles a page).
+constexpr int fused_block_rows(int U, bool k8)
+{
+    return kWavesPerBlock * 16 * U * (k8 ? SAGA_STREAM_K8_UMUL : 1);
+}
 // Dense kernel: 16-row groups per wave tile (the K tile and the V tile of the
 // same rows are in registers together).
 constexpr int full_unroll(int DK, int DV) { return (DK == 128 || DV == 128) ? 2 : 4; }
@@ -212,6 +224,35 @@ struct FullArgs {
     size_t wave_lds;
 };
 
+// Small-batch path (fused.hip): K stream, mask, compaction and value gather
+// in one kernel; one partial per (b*h_q + i, chunk).  The selected entries of
+// a chunk stay in LDS: qcap entries per (wave, queue), enough for every row
+// of the wave's share of the chunk for the ceil(G_k/4) head slots of a queue,
+// then G_k lists of hcap 16-bit entry indices, one per head slot.
+struct FusedArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* tau;
+    uint32_t* bitmap;        // nullable
+    int64_t bitmap_words;
+    float* logits_out;       // nullable [B*hq][ctx]
+    Partials part;           // [B*hq][chunks]
+    int32_t B, hq, hk, hv, Gk, Gv;
+    int64_t ctx, cache_len, rows_per_chunk;
+    int32_t chunks, qcap;
+    int32_t hcap;            // entries per head slot list (rows_per_chunk)
+    int32_t unroll;          // 16-row groups per wave tile: 1 or 2
+    float scale;
+    int32_t lq;
+    const float* k_scale;    // non-null: fp8 e4m3 K
+    PagedKV pg;
+};
+
+hipError_t launch_select_gather(int D, int DV, const FusedArgs& a, size_t lds_bytes,
+                                hipStream_t s);
+hipError_t launch_combine_parts(int D, const Partials& p, int rows, int parts, uint16_t* out,
+                                int32_t* counts, hipStream_t s);
 hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t s);
 hipError_t launch_gather(int D, const GatherArgs& a, hipStream_t s);
 hipError_t launch_combine(int D, const Partials& p, int rows, int parts, uint16_t* out,

@@ -57,3 +57,6 @@
 #else
 #define SAGA_STREAM_ATTR
 #endif
+#ifndef SAGA_FUSED_MAX_GROUPS
+#define SAGA_FUSED_MAX_GROUPS 4      // decode calls with at most this many (b, key head) groups
+#endif                               // take the fused small-batch path

@@ -254,6 +254,52 @@ hipError_t launch_full(int DK, int DV, int maxs, const FullArgs& a, hipStream_t)
     return hipSuccess;
 }
 
+hipError_t launch_select_gather(int D, int DV, const FusedArgs& a, size_t lds_bytes, hipStream_t)
+{
+    ++g_launches;
+    EXPECT(D == 32 || D == 64 || D == 128);
+    EXPECT(DV == 32 || DV == 64 || DV == 128);
+    EXPECT(a.B >= 1 && a.hk >= 1 && a.hq == a.hk * a.Gk && a.Gk <= 16 && a.hq == a.hv * a.Gv);
+    EXPECT((int64_t)a.B * a.hk <= 65535);
+    EXPECT(a.chunks >= 1 && (int64_t)a.chunks * a.rows_per_chunk >= a.ctx);
+    EXPECT((int64_t)(a.chunks - 1) * a.rows_per_chunk < a.ctx);
+    EXPECT(a.unroll == 1 || a.unroll == 2);
+    EXPECT(a.rows_per_chunk % (2 * fused_block_rows(a.unroll, a.k_scale != nullptr)) == 0);
+    // Every row of a wave's share, for every head slot of a queue, fits.
+    EXPECT((int64_t)a.qcap >= a.rows_per_chunk / kWavesPerBlock * ((a.Gk + 3) / 4));
+    EXPECT(a.hcap >= a.rows_per_chunk);                         // a slot's list holds every row
+    EXPECT((int64_t)16 * a.qcap <= 65536);                      // 16-bit entry indices
+    EXPECT(lds_bytes >= (size_t)16 * a.qcap * 8 + (size_t)a.Gk * a.hcap * 2);
+    EXPECT(lds_bytes <= (size_t)kLdsPerGroup);
+    const int64_t per_cu = ((int64_t)a.B * a.hk * a.chunks + kComputeUnits - 1) / kComputeUnits;
+    EXPECT((int64_t)lds_bytes * per_cu <= kLdsPerCu);           // every workgroup resident
+    const int64_t P = (int64_t)a.Gk * (DV / 8), R = kBlock / P;
+    EXPECT(R >= 1 && lds_bytes >= (size_t)(R * a.Gk * DV + R * a.Gk) * 4);
+    touch_partials(a.part, (int64_t)a.B * a.hq * a.chunks, DV);
+    rd_span(a.q, (int64_t)a.B * a.hq * D);
+    rd_span(a.tau, (int64_t)a.B * a.hq);
+    if (a.k_scale) rd_span(a.k_scale, (int64_t)a.B * a.hk);
+    if (a.logits_out) wr_span(a.logits_out, (int64_t)a.B * a.hq * a.ctx);
+    if (a.bitmap) {
+        wr(a.bitmap, 0);
+        wr(a.bitmap, ((int64_t)a.B * a.hq - 1) * a.bitmap_words + (a.ctx - 1) / 32);
+    }
+    if (a.pg.block_table) {
+        touch_paged(a.pg, a.B);
+    } else {
+        touch_cache(a.k, a.B, a.hk, a.cache_len, a.ctx, D, a.k_scale ? 1 : 2);
+        touch_cache(a.v, a.B, a.hv, a.cache_len, a.cache_len, DV, 2);
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_combine_parts(int D, const Partials& p, int rows, int parts, uint16_t* out,
+                                int32_t* counts, hipStream_t s)
+{
+    EXPECT(D % 16 == 0);
+    return launch_combine(D, p, rows, parts, out, counts, s);   // same buffers, same extents
+}
+
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t, hipStream_t)
 {
     ++g_launches;
