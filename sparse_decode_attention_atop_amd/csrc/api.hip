@@ -109,7 +109,8 @@ Chunking plan_chunks(int64_t ctx, int64_t pairs, int head_dim, int max_chunks, b
 struct Layout {
     int max_chunks;
     int64_t entry_rows;   // selection-list capacity per (b, query head)
-    size_t pm, pl, pc, po, entries, overflow, lcount, lmax, sample, pivot, flags, total;
+    int64_t top_rows;     // rows per chunk of the paged plan at cache_len
+    size_t pm, pl, pc, po, entries, overflow, lcount, lmax, sample, pivot, flags, plan, total;
 };
 
 Layout make_layout(const saga_dims* d)
@@ -121,7 +122,9 @@ Layout make_layout(const saga_dims* d)
     int64_t target = kFullTargetBlocks;
     for (const bool k8 : {false, true})
         if (target_blocks(d->head_dim, k8) > target) target = target_blocks(d->head_dim, k8);
-    const int64_t want = target / ((int64_t)d->batch * d->h_k);
+    // Twice the chunks of the largest launch: paged calls with per-sequence
+    // lengths give long sequences more chunks than a uniform split would.
+    const int64_t want = 2 * target / ((int64_t)d->batch * d->h_k);
     const int64_t by_len = (d->cache_len + 127) / 128;   // smallest tile pair is 128 rows
     int64_t mc = want < by_len ? want : by_len;
     if (mc > kMaxListsPerRow / kWavesPerBlock) mc = kMaxListsPerRow / kWavesPerBlock;   // 512
@@ -138,6 +141,7 @@ Layout make_layout(const saga_dims* d)
         const int64_t r = top.rows > br ? top.rows : br;
         if (r > top_rows) top_rows = r;
     }
+    L.top_rows = top_rows;
     L.entry_rows = d->cache_len + top_rows;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes, 256); return o; };
@@ -152,6 +156,7 @@ Layout make_layout(const saga_dims* d)
     L.sample = take(rows * kSampleMax * 4);
     L.pivot = take(rows * 4);
     L.flags = take((size_t)d->batch * d->h_k * 4);
+    L.plan = take(((size_t)d->batch + 1) * 4);
     L.total = off;
     return L;
 }
@@ -180,6 +185,37 @@ struct RowModel {
     const float* v_scale = nullptr;   // non-null: fp8 e4m3 V cache, one scale per (b, value head)
 };
 
+// Chunking of a list-path call.  Paged caches: the launch has room for
+// twice the chunks of the uniform plan at ctx_len (never more than the
+// workspace holds) and the kernels take their rows per chunk from the
+// sequence lengths on the device (PagedKV::plan_*), so that a batch of mixed
+// lengths still spreads over about the stream's target of workgroups.
+Chunking list_chunks(const saga_dims* dims, const Layout& L, void* ws, RowModel* rm)
+{
+    const int D = dims->head_dim;
+    const bool k8 = rm->k_scale != nullptr, paged = rm->pg.block_table != nullptr;
+    Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k, D, L.max_chunks,
+                              k8, paged);
+    if (!paged) return ch;
+    const int64_t cap = 2 * (int64_t)ch.chunks < L.max_chunks ? 2 * (int64_t)ch.chunks : L.max_chunks;
+    const int64_t target = target_blocks(D, k8), rows = (int64_t)dims->batch * dims->h_k;
+    rm->pg.plan_cap = (int32_t)cap;
+    rm->pg.plan_target = (int32_t)target;
+    rm->pg.plan_quantum = 2 * (k8 ? decode_block_rows_k8(D) : decode_block_rows(D));
+    rm->pg.plan_rows_max = L.top_rows;
+    // Work items of the K stream: h_k * sum_b ceil(len_b / r) < h_k * sum / r
+    // + B * h_k.  The device plan takes r >= h_k * sum / target unless that
+    // exceeds top_rows, when r = top_rows and len_b <= ctx bound the count;
+    // no sequence has more than cap chunks.
+    int64_t grid = target + rows;
+    const int64_t by_rows = rows * ((dims->ctx_len + L.top_rows - 1) / L.top_rows);
+    if (by_rows > grid) grid = by_rows;
+    if (rows * cap < grid) grid = rows * cap;
+    rm->pg.plan_grid = grid;
+    rm->pg.plan = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(ws) + L.plan);
+    return {(int)cap, L.top_rows};
+}
+
 // Arguments of the stream-select kernel for one call.
 SelectStreamArgs stream_args(const saga_dims* dims, const Layout& L, const Chunking& ch,
                              const void* q, const void* k, const float* tau, void* ws,
@@ -192,6 +228,7 @@ SelectStreamArgs stream_args(const saga_dims* dims, const Layout& L, const Chunk
     a.tau = tau;
     a.entries = reinterpret_cast<uint2*>(w + L.entries);
     a.overflow_at = (int64_t)((L.overflow - L.entries) / 8);
+    a.head_stride = L.entry_rows;
     a.list_count = reinterpret_cast<int32_t*>(w + L.lcount);
     a.list_max = reinterpret_cast<float*>(w + L.lmax);
     a.B = dims->batch;
@@ -287,6 +324,7 @@ int enqueue_refresh(const saga_dims* dims, int32_t top_n, const void* q_dev,
     fa.k = sa.k;
     fa.entries = a.entries;
     fa.overflow_at = a.overflow_at;
+    fa.head_stride = a.head_stride;
     fa.list_count = a.list_count;
     fa.tau = thresholds_dev;
     fa.group_flags = group_flags;
@@ -322,6 +360,7 @@ int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunkin
     ga.v = static_cast<const uint16_t*>(v_cache_dev);
     ga.entries = reinterpret_cast<const uint2*>(w + L.entries);
     ga.overflow_at = (int64_t)((L.overflow - L.entries) / 8);
+    ga.head_stride = L.entry_rows;
     ga.list_count = reinterpret_cast<const int32_t*>(w + L.lcount);
     ga.list_max = reinterpret_cast<const float*>(w + L.lmax);
     ga.tau_filter = tau_filter;
@@ -329,7 +368,9 @@ int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunkin
     ga.part = partials(workspace_dev, L);
     ga.B = dims->batch;
     ga.hq = dims->h_q;
+    ga.hk = dims->h_k;
     ga.hv = dims->h_v;
+    ga.ctx = dims->ctx_len;
     ga.Gv = dims->h_q / dims->h_v;
     ga.cache_len = dims->cache_len;
     ga.rows_per_chunk = ch.rows;
@@ -472,17 +513,16 @@ int enqueue_decode(const saga_dims* dims, const Layout& L, const void* q_dev,
     if (f.use)
         return enqueue_fused(dims, L, f, q_dev, k_cache_dev, v_cache_dev, thresholds_dev, out_dev,
                              sel_counts_dev, sel_bitmap_debug_dev, words, workspace_dev, s, rm);
-    const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
-                                    D, L.max_chunks, rm.k_scale != nullptr,
-                                    rm.pg.block_table != nullptr);
+    RowModel lrm = rm;
+    const Chunking ch = list_chunks(dims, L, workspace_dev, &lrm);
     SelectStreamArgs a =
-        stream_args(dims, L, ch, q_dev, k_cache_dev, thresholds_dev, workspace_dev, rm);
+        stream_args(dims, L, ch, q_dev, k_cache_dev, thresholds_dev, workspace_dev, lrm);
     a.bitmap = sel_bitmap_debug_dev;
     a.bitmap_words = words;
     st = hip_status(launch_select_stream(D, a, s));
     if (st != SAGA_OK) return st;
     return enqueue_gather_combine(dims, L, ch, v_cache_dev, nullptr, out_dev, sel_counts_dev,
-                                  workspace_dev, s, rm);
+                                  workspace_dev, s, lrm);
 }
 
 // Checks of a page description against the call's dims: pages of a multiple
@@ -520,9 +560,8 @@ int do_refresh(const saga_dims* dims, const RowModel& rm, int32_t top_n, const v
     unsigned char* w = static_cast<unsigned char*>(workspace_dev);
     const int D = dims->head_dim;
     const int rows = dims->batch * dims->h_q;
-    const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
-                                    D, L.max_chunks, rm.k_scale != nullptr,
-                                    rm.pg.block_table != nullptr);
+    RowModel lrm = rm;
+    const Chunking ch = list_chunks(dims, L, workspace_dev, &lrm);
     int st;
     if ((int64_t)top_n >= dims->ctx_len) {
         // N >= ctx (of every sequence): every entry is kept, tau = -inf.  The
@@ -531,7 +570,7 @@ int do_refresh(const saga_dims* dims, const RowModel& rm, int32_t top_n, const v
             float* pivot = reinterpret_cast<float*>(w + L.pivot);
             st = hip_status(launch_fill_u32(reinterpret_cast<uint32_t*>(pivot), rows, 0x7f800000u, s));
             if (st != SAGA_OK) return st;
-            SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_dev, pivot, workspace_dev, rm);
+            SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_dev, pivot, workspace_dev, lrm);
             a.logits_out = logits_debug_dev;
             st = hip_status(launch_select_stream(D, a, s));
             if (st != SAGA_OK) return st;
@@ -540,7 +579,7 @@ int do_refresh(const saga_dims* dims, const RowModel& rm, int32_t top_n, const v
                                           0xff800000u, s));
     }
     return enqueue_refresh(dims, top_n, q_dev, k_dev, thresholds_dev, logits_debug_dev,
-                           workspace_dev, L, ch, s, nullptr, rm);
+                           workspace_dev, L, ch, s, nullptr, lrm);
 }
 
 int do_decode(const saga_dims* dims, const RowModel& rm, const void* q_dev, const void* k_dev,
@@ -587,23 +626,22 @@ int do_refresh_decode(const saga_dims* dims, const RowModel& rm, int32_t top_n,
         return enqueue_decode(dims, L, q_dev, k_dev, v_dev, thresholds_dev, out_dev,
                               sel_counts_dev, nullptr, workspace_dev, s, rm);
     }
-    const Chunking ch = plan_chunks(dims->ctx_len, (int64_t)dims->batch * dims->h_k,
-                                    D, L.max_chunks, rm.k_scale != nullptr,
-                                    rm.pg.block_table != nullptr);
+    RowModel lrm = rm;
+    const Chunking ch = list_chunks(dims, L, workspace_dev, &lrm);
     uint32_t* flags = reinterpret_cast<uint32_t*>(w + L.flags);
     st = enqueue_refresh(dims, top_n, q_dev, k_dev, thresholds_dev, nullptr, workspace_dev,
-                         L, ch, s, flags, rm);
+                         L, ch, s, flags, lrm);
     if (st != SAGA_OK) return st;
     // Key groups whose candidate lists miss selected entries (a row took the
     // recompute path) are streamed again with the fresh thresholds; every
     // other workgroup of this launch exits at once.
-    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_dev, thresholds_dev, workspace_dev, rm);
+    SelectStreamArgs a = stream_args(dims, L, ch, q_dev, k_dev, thresholds_dev, workspace_dev, lrm);
     a.group_flags = flags;
     st = hip_status(launch_select_stream(D, a, s));
     if (st != SAGA_OK) return st;
     // The lists hold every logit >= tau (and more): keep those >= tau.
     return enqueue_gather_combine(dims, L, ch, v_dev, thresholds_dev, out_dev,
-                                  sel_counts_dev, workspace_dev, s, rm);
+                                  sel_counts_dev, workspace_dev, s, lrm);
 }
 
 }  // namespace

@@ -48,21 +48,44 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
     // compiler wait for every K load in flight on each trip).
     const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15, grp = lane >> 4;
-    const int chunk = blockIdx.x;
-    const int b = blockIdx.y / a.hk, g = blockIdx.y - b * a.hk;
+    int chunk = blockIdx.x;
+    int b = blockIdx.y / a.hk, g = blockIdx.y - b * a.hk;
     const int Gk = a.Gk;
-    const int64_t r0 = (int64_t)chunk * a.rows_per_chunk;
+    // Paged caches with a work split from the lengths: this call's rows per
+    // chunk (the same in every kernel of the call) and this workgroup's work
+    // item (a 1-D launch, see paged_item); the LDS of the queues, not yet in
+    // use, serves the block reductions.
+    int64_t rpc = a.rows_per_chunk;
+    if constexpr (PAGED) {
+        if (a.pg.plan_cap) {
+            int64_t* red = reinterpret_cast<int64_t*>(&queue[0][0][0]);
+            const uint32_t len0 = plan_len(a.pg, threadIdx.x, a.B, a.ctx);
+            rpc = paged_rows_per_chunk(a.pg, a.B, a.hk, a.ctx, len0, red);
+            if (blockIdx.x == 0) {           // the plan, for the gather and threshold kernels
+                const uint32_t r32 = (uint32_t)rpc;
+                for (int s = threadIdx.x; s < a.B; s += kBlock) {
+                    const uint32_t c = s < kBlock ? len0 : plan_len(a.pg, s, a.B, a.ctx);
+                    a.pg.plan[1 + s] = (int32_t)((c + r32 - 1) / r32);
+                }
+                if (threadIdx.x == 0) a.pg.plan[0] = (int32_t)rpc;
+            }
+            if (!paged_item(a.pg, a.B, a.hk, a.ctx, rpc, len0, blockIdx.x, red, &b, &g, &chunk))
+                return;                                                // whole workgroup
+        }
+    }
+    const int bg = b * a.hk + g;
+    const int64_t r0 = (int64_t)chunk * rpc;
     const int64_t ctx_b = PAGED ? seq_ctx(a.pg, b, a.ctx) : a.ctx;
-    const int64_t r1 = wave_uniform(min(r0 + a.rows_per_chunk, ctx_b));
-    const int64_t capw = a.rows_per_chunk / kWavesPerBlock;
+    const int64_t r1 = wave_uniform(min(r0 + rpc, ctx_b));
+    const int64_t capw = rpc / kWavesPerBlock;
     const int qh0 = b * a.hq + g * Gk;
     uint2 (*q4)[kQueueCap] = queue[wave];
-    if (a.group_flags && a.group_flags[blockIdx.y] == 0u) return;   // whole workgroup
+    if (a.group_flags && a.group_flags[bg] == 0u) return;   // whole workgroup
 
     const uint16_t* qrow = col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr;
     const QFrag<D> qf = FP8 ? load_qfrag_k8<D>(qrow) : load_qfrag<D>(qrow);
     // Logit scale; an fp8 K cache adds its (b, key head) scale.
-    const float sc = FP8 ? a.scale * a.k_scale[blockIdx.y] : a.scale;
+    const float sc = FP8 ? a.scale * a.k_scale[bg] : a.scale;
     float tau[4], mx[4];
     int64_t lim[4];          // rows of this lane's head slots: r1, or less for later tokens
 #pragma unroll
@@ -79,8 +102,10 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
     int written[16];
 #pragma unroll
     for (int h = 0; h < 16; ++h) written[h] = 0;
-    const int64_t list0 = (int64_t)qh0 * a.chunks * kWavesPerBlock + chunk * kWavesPerBlock + wave;
-    const int64_t list_stride = (int64_t)a.chunks * kWavesPerBlock;   // between head slots
+    const int64_t nl = (int64_t)a.chunks * kWavesPerBlock;          // lists per row
+    const int64_t local = chunk * kWavesPerBlock + wave;               // this wave's list
+    const int64_t list0 = (int64_t)qh0 * nl + local;
+    const int64_t list_stride = nl;                                    // between head slots
 
     // Split every queue by head slot (4*gs + i) and append to the global lists.
     auto flush_all = [&]() {
@@ -101,8 +126,8 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
                     written[4 * g2 + i] += __popcll(m);
                 }
                 if (have)
-                    a.entries[list_index(list0 + (4 * gs + i) * list_stride, (uint32_t)pos, capw,
-                                         a.overflow_at)] = make_uint2(e.x >> 4, e.y);
+                    a.entries[list_index(qh0 + 4 * gs + i, local, (uint32_t)pos, capw, nl,
+                                         a.head_stride, a.overflow_at)] = make_uint2(e.x >> 4, e.y);
             }
             qn[i] = 0;
         }
@@ -337,12 +362,16 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
     const int b = bi / a.hq, i = bi - b * a.hq;
     const int t = threadIdx.x;
     const int nl = a.chunks * kWavesPerBlock;
-    const int64_t capw = a.rows_per_chunk / kWavesPerBlock;
     const int64_t lbase = (int64_t)bi * nl;
 
     // List lengths (prefix) and the head's largest selected logit.  The
     // loads are unconditional (lists past nl read the last list again and are
     // masked after), so all of them are in flight before the first wait.
+    // Paged caches with a work split from the lengths: the K stream's plan
+    // (rows per chunk, this sequence's chunks), loaded with the list lengths.
+    const bool plan = PAGED != 0 && a.pg.plan_cap != 0;
+    const int32_t plan_rows = plan ? a.pg.plan[0] : 0;
+    const int32_t plan_chunks = plan ? a.pg.plan[1 + b] : 0;
     int32_t c[PER], sum = 0;
     float lm[PER], mx = -INFINITY;
 #pragma unroll
@@ -351,9 +380,13 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
         c[k] = a.list_count[lbase + l];
         lm[k] = a.list_max[lbase + l];
     }
+    // Then the lists of this sequence's chunks only.
+    const int64_t rpc = plan ? plan_rows : a.rows_per_chunk;
+    const int nlv = plan ? plan_chunks * kWavesPerBlock : nl;
+    const int64_t capw = rpc / kWavesPerBlock;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-        const bool in = t * PER + k < nl;
+        const bool in = t * PER + k < nlv;
         c[k] = in ? c[k] : 0;
         sum += c[k];
         mx = fmaxf(mx, in ? lm[k] : -INFINITY);
@@ -413,13 +446,14 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
         uint2 ent[EPT];
 #pragma unroll
         for (int k = 0; k < EPT; ++k)
-            ent[k] = a.entries[list_index(lbase + lo[k], in_list[k], capw, a.overflow_at)];
+            ent[k] = a.entries[list_index(bi, lo[k], in_list[k], capw, nl, a.head_stride,
+                                          a.overflow_at)];
         if constexpr (PAGED) {
             // The value row's page: every table read issued before any use.
             int32_t page[EPT];
 #pragma unroll
             for (int k = 0; k < EPT; ++k) {
-                const int64_t r = (int64_t)(lo[k] / kWavesPerBlock) * a.rows_per_chunk + ent[k].x;
+                const int64_t r = (int64_t)(lo[k] / kWavesPerBlock) * rpc + ent[k].x;
                 const int64_t pi = r / a.pg.page_rows;
                 page[k] = (EPT * t + k < n && pi < a.pg.max_pages)
                               ? a.pg.block_table[(int64_t)b * a.pg.max_pages + pi] : -1;
@@ -431,7 +465,7 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
                     const float sv = __uint_as_float(ent[k].y);
                     const bool keep = sv >= tf;
                     kept += keep;
-                    const int64_t r = (int64_t)(lo[k] / kWavesPerBlock) * a.rows_per_chunk + ent[k].x;
+                    const int64_t r = (int64_t)(lo[k] / kWavesPerBlock) * rpc + ent[k].x;
                     const bool ok = page[k] >= 0 && page[k] < a.pg.num_pages;   // else reads nothing
                     if constexpr (PAGED == 1) {
                         eoff[e] = keep && ok ? (uint32_t)((((int64_t)page[k] * a.hv + nu) *
@@ -452,7 +486,7 @@ __global__ __launch_bounds__(kBlock) SAGA_GATHER_ATTR void gather_kernel(GatherA
                 const float sv = __uint_as_float(ent[k].y);
                 const bool keep = sv >= tf;
                 kept += keep;
-                const uint32_t r = (uint32_t)((lo[k] / kWavesPerBlock) * a.rows_per_chunk) + ent[k].x;
+                const uint32_t r = (uint32_t)((lo[k] / kWavesPerBlock) * rpc) + ent[k].x;
                 eoff[e] = keep ? r * (uint32_t)(D * VB) : kNoRow;
                 ew[e] = keep ? __expf(sv - M) : 0.f;
             }
@@ -630,7 +664,10 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
 
 hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t s)
 {
-    const dim3 grid(a.chunks, a.B * a.hk);
+    // Paged calls with the work split from the lengths: a 1-D launch over the
+    // work items (paged_item).
+    const dim3 grid = a.pg.plan_cap ? dim3((unsigned)a.pg.plan_grid, 1)
+                                    : dim3(a.chunks, a.B * a.hk);
     const bool dbg = a.bitmap != nullptr || a.logits_out != nullptr;
     const int kind = a.pg.block_table != nullptr ? 1 : (a.k_scale != nullptr ? 2 : 0);
 #define SAGA_LAUNCH_STREAM(DD, DBG, PG, F8)                                                      \

@@ -71,18 +71,22 @@ constexpr int gather_target_blocks(int head_dim)
 constexpr int kGatherMaxSegs = SAGA_GATHER_MAX_SEGS;
 constexpr int kGatherStage = 1024;   // entries a gather workgroup stages per round
 
-// Storage of selection list lid = (b*h_q + i) * nl + chunk*4 + wave (nl lists
-// per row in this call, capw = rows_per_chunk/4 entries at most): its first
-// kListPrimary entries sit in a dense primary part at lid * kListPrimary + E,
-// so one call's typical lists share a few tens of megabytes (few pages for the
-// address translation); entries past those go to an overflow part sized for
-// the worst case, which starts at entry overflow_at.
+// Storage of selection list `local` (= chunk*4 + wave; nl lists per row) of
+// row `head` (= b*h_q + i), at most capw = rows_per_chunk/4 entries: its first
+// kListPrimary entries sit in a dense primary part at (head*nl + local) *
+// kListPrimary + E, so one call's typical lists share a few tens of megabytes
+// (few pages for the address translation); entries past those go to an
+// overflow part sized for the worst case, head_stride entries per row
+// starting at entry overflow_at (a row's chunks * rows_per_chunk never exceed
+// head_stride).
 constexpr int kListPrimary = 64;
-__device__ __forceinline__ int64_t list_index(int64_t lid, uint32_t E, int64_t capw,
+__device__ __forceinline__ int64_t list_index(int64_t head, int64_t local, uint32_t E,
+                                              int64_t capw, int64_t nl, int64_t head_stride,
                                               int64_t overflow_at)
 {
-    return E < (uint32_t)kListPrimary ? lid * kListPrimary + E
-                                      : overflow_at + lid * capw + (E - kListPrimary);
+    return E < (uint32_t)kListPrimary
+               ? (head * nl + local) * kListPrimary + E
+               : overflow_at + head * head_stride + local * capw + (E - kListPrimary);
 }
 
 // Paged caches.  Sequence b attends ctx_lens[b] rows; its logical row r sits
@@ -101,6 +105,14 @@ struct PagedKV {
     int32_t page_rows;            // P
     int32_t max_pages;
     int64_t num_pages;
+    // Work split from the lengths (list path; plan_cap == 0: the host's rows).
+    int32_t plan_cap;             // most chunks per sequence (the lists' chunks)
+    int32_t plan_target;          // workgroups the batch's rows are spread over
+    int64_t plan_quantum;         // rows per chunk: a multiple of this (a tile pair)
+    int64_t plan_rows_max;        // and at most this
+    int64_t plan_grid;            // K-stream workgroups: at least the call's work items
+    int32_t* plan;                // workspace [1 + B]: rows per chunk, then each sequence's
+                                  // chunks; written by the K stream for the kernels after it
 };
 
 // Rows attended by sequence b (ctx_lens[b] clamped to the table's capacity).
@@ -110,6 +122,184 @@ __device__ __forceinline__ int64_t seq_ctx(const PagedKV& pg, int b, int64_t ctx
     int64_t c = pg.ctx_lens[b];
     const int64_t cap = (int64_t)pg.max_pages * pg.page_rows;
     return c < 0 ? 0 : (c > cap ? cap : c);
+}
+
+// Length of sequence b as the work split of a paged call sees it: ctx_lens[b]
+// clamped to the table and to the call's ctx (the bound the host planned
+// with); 0 for b >= B.  Lengths and rows per chunk stay below 2^27.
+__device__ __forceinline__ uint32_t plan_len(const PagedKV& pg, int b, int B, int64_t ctx)
+{
+    if (b >= B) return 0u;
+    const int64_t c = seq_ctx(pg, b, ctx);
+    return (uint32_t)(c < ctx ? c : ctx);
+}
+
+// Rows per chunk of a call on paged caches with per-sequence lengths, computed
+// on the device from the lengths so that graph-captured calls follow them.
+// Each sequence is cut into chunks of r rows (its last one shorter), h_k rows
+// of chunks per sequence being the K stream's work items.  r is the smallest
+// multiple of plan_quantum for which the items fit in plan_target workgroups
+// (one round of resident streams on every CU), at most plan_rows_max (the
+// list storage) and at least what keeps every sequence within plan_cap
+// chunks.  Every kernel that writes or reads the selection lists of such a
+// call computes it the same way.  len0 = plan_len(threadIdx.x): thread t
+// holds sequence t, so with B <= kBlock the search reads no memory.  All
+// threads of the workgroup must call it (it synchronises); `red` is LDS for
+// 8 int64 values followed by kBlock lengths (1088 bytes, 8-byte aligned).
+__device__ __forceinline__ int64_t paged_rows_per_chunk(const PagedKV& pg, int B, int hk,
+                                                        int64_t ctx, uint32_t len0, int64_t* red)
+{
+    uint32_t* lens = reinterpret_cast<uint32_t*>(red + 2 * kWavesPerBlock);
+    lens[threadIdx.x] = len0;      // ordered before its reads by the barrier below
+    int64_t sum = len0;
+    uint32_t mx = len0;
+    for (int b = threadIdx.x + kBlock; b < B; b += kBlock) {
+        const uint32_t c = plan_len(pg, b, B, ctx);
+        sum += c;
+        mx = c > mx ? c : mx;
+    }
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        sum += __shfl_xor(sum, off);
+        const uint32_t o = __shfl_xor(mx, off);
+        mx = o > mx ? o : mx;
+    }
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        red[threadIdx.x / kWave] = sum;
+        red[kWavesPerBlock + threadIdx.x / kWave] = mx;
+    }
+    __syncthreads();
+    sum = 0;
+    int64_t m = 0;
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+        sum += red[w];
+        m = red[kWavesPerBlock + w] > m ? red[kWavesPerBlock + w] : m;
+    }
+    __syncthreads();
+    sum = wave_uniform(sum);       // the same in every lane: keep the search scalar
+    m = wave_uniform(m);
+    const int64_t q = pg.plan_quantum, target = pg.plan_target;
+    auto up = [q](int64_t x) { return (x + q - 1) / q * q; };
+    int64_t r = up(((int64_t)hk * sum + target - 1) / target);   // items >= h_k * sum / r
+    r = r < pg.plan_rows_max ? r : pg.plan_rows_max;
+    const int64_t need = up((m + pg.plan_cap - 1) / pg.plan_cap);   // chunks <= plan_cap
+    r = r > need ? r : need;
+    r = r > q ? r : q;
+    // Work items for rows-per-chunk rr.
+    auto items = [&](int64_t rr) {
+        const uint32_t r32 = (uint32_t)rr;
+        int64_t n = (len0 + r32 - 1) / r32;
+        for (int b = threadIdx.x + kBlock; b < B; b += kBlock)
+            n += (plan_len(pg, b, B, ctx) + r32 - 1) / r32;
+        for (int off = kWave / 2; off > 0; off >>= 1) n += __shfl_xor(n, off);
+        if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = n;
+        __syncthreads();
+        n = 0;
+        for (int w = 0; w < kWavesPerBlock; ++w) n += red[w];
+        __syncthreads();
+        return wave_uniform(n) * hk;
+    };
+    // Rounding every sequence's last chunk up adds up to one item per (b, key
+    // head): find the smallest r whose items fit.  r = up(longest) (one chunk
+    // per sequence) is the most that can help; beyond plan_rows_max nothing
+    // is allowed.  With every length in LDS, each thread tests one candidate
+    // (r + t * plan_quantum) and the first that fits wins; otherwise, or past
+    // those candidates, bisection.
+    int64_t lo = r / q, hi = up(m) / q;              // in quanta
+    hi = hi < pg.plan_rows_max / q ? hi : pg.plan_rows_max / q;
+    if (hi <= lo) return r;
+    bool bisect = true;
+    if (B <= kBlock) {
+        const int64_t cand = lo + threadIdx.x;
+        bool ok = cand >= hi;
+        if (!ok) {
+            const uint32_t rc = (uint32_t)(cand * q);
+            int64_t n = 0;
+            for (int b = 0; b < B; ++b) n += (lens[b] + rc - 1) / rc;
+            ok = n * hk <= target;
+        }
+        const uint64_t bal = __ballot(ok);
+        if ((threadIdx.x & (kWave - 1)) == 0)
+            red[threadIdx.x / kWave] = bal ? (threadIdx.x & ~(kWave - 1)) + __ffsll((unsigned long long)bal) - 1
+                                           : kBlock;
+        __syncthreads();
+        int64_t first = kBlock;
+        for (int w = 0; w < kWavesPerBlock; ++w) first = red[w] < first ? red[w] : first;
+        __syncthreads();
+        first = wave_uniform(first);
+        if (first < kBlock) return (lo + first) * q;
+        lo += kBlock - 1;                            // items(lo * q) > target
+        bisect = hi > lo;
+    } else {
+        bisect = items(r) > target;
+    }
+    if (bisect) {
+        while (hi - lo > 1) {                        // items(hi * q) is the best there is
+            const int64_t mid = lo + (hi - lo) / 2;
+            if (items(mid * q) > target) lo = mid; else hi = mid;
+        }
+        r = hi * q;
+    }
+    return r;
+}
+
+// Chunks of sequence b for rows-per-chunk r (0 for an empty sequence).
+__device__ __forceinline__ int64_t paged_chunks(const PagedKV& pg, int b, int64_t ctx, int64_t r)
+{
+    int64_t c = seq_ctx(pg, b, ctx);
+    c = c < ctx ? c : ctx;
+    return wave_uniform((c + r - 1) / r);
+}
+
+// The K stream of such a call is a 1-D launch of plan_grid workgroups over
+// its work items: sequence by sequence, h_k key heads of paged_chunks(b)
+// chunks each, chunk fastest.  Item `item` -> (b, g, chunk); false when the
+// call has fewer items.  Consecutive workgroups take consecutive items, so the
+// live ones are spread over the XCDs (which take workgroups round-robin) and
+// the few idle ones sit at the end of the grid.  Block-wide, same calling
+// rules and len0 as paged_rows_per_chunk; `red` is LDS for 8 values.
+__device__ __forceinline__ bool paged_item(const PagedKV& pg, int B, int hk, int64_t ctx,
+                                           int64_t r, uint32_t len0, int64_t item, int64_t* red,
+                                           int* b_out, int* g_out, int* chunk_out)
+{
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    int64_t base = 0;                           // items of the sequences before this pass
+    bool found = false;
+    for (int b0 = 0; b0 < B && !found; b0 += kBlock) {
+        const int b = b0 + threadIdx.x;        // one sequence per thread (not wave-uniform)
+        const uint32_t c = b0 == 0 ? len0 : plan_len(pg, b, B, ctx);
+        const int64_t n = (int64_t)((c + (uint32_t)r - 1) / (uint32_t)r) * hk;
+        int64_t incl = n;                       // inclusive scan over the block
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int64_t u = __shfl_up(incl, off);
+            if (lane >= off) incl += u;
+        }
+        if (lane == kWave - 1) red[w] = incl;
+        if (threadIdx.x == 0) red[kWavesPerBlock] = -1;
+        __syncthreads();
+        int64_t total = 0;
+        for (int k = 0; k < kWavesPerBlock; ++k) {
+            incl += k < w ? red[k] : 0;
+            total += red[k];
+        }
+        const int64_t lo = base + incl - n;
+        if (n > 0 && item >= lo && item < lo + n) {
+            red[kWavesPerBlock] = b;
+            red[kWavesPerBlock + 1] = item - lo;
+        }
+        __syncthreads();
+        found = red[kWavesPerBlock] >= 0;
+        base += total;
+        const int bf = (int)red[kWavesPerBlock];
+        const int64_t off = red[kWavesPerBlock + 1];
+        __syncthreads();                        // red is rewritten by the next pass
+        if (found) {
+            const int64_t nb = paged_chunks(pg, bf, ctx, r);
+            *b_out = __builtin_amdgcn_readfirstlane(bf);
+            *g_out = __builtin_amdgcn_readfirstlane((int)(off / nb));
+            *chunk_out = __builtin_amdgcn_readfirstlane((int)(off - off / nb * nb));
+        }
+    }
+    return found;
 }
 
 // Several query tokens per step (lq > 1): token j of query head i is the
@@ -145,6 +335,7 @@ struct SelectStreamArgs {
     int64_t bitmap_words;    // words per (b, i) row of the bitmap
     uint2* entries;          // list storage (see list_index)
     int64_t overflow_at;
+    int64_t head_stride;     // overflow entries per row (see list_index)
     int32_t* list_count;     // [B*hq][chunks][4]
     float* list_max;         // [B*hq][chunks][4]  largest selected logit (-inf if none)
     float* logits_out;       // nullable [B*hq][ctx]: every logit, for checking
@@ -163,14 +354,15 @@ struct GatherArgs {
     const uint16_t* v;
     const uint2* entries;
     int64_t overflow_at;
+    int64_t head_stride;     // overflow entries per row (see list_index)
     const int32_t* list_count;
     const float* list_max;
     const float* tau_filter; // nullable [B*hq]: keep only entries with logit >= tau_filter
     const float* v_scale;    // non-null: fp8 e4m3 V (d_v bytes per row), one scale per (b, value head)
     Partials part;           // one partial per (b*h_q + i, segment)
     uint32_t pool_bytes;     // paged: V pool bytes when below kPoolLimit (32-bit offsets), else 0
-    int32_t B, hq, hv, Gv;
-    int64_t cache_len, rows_per_chunk;
+    int32_t B, hq, hk, hv, Gv;
+    int64_t ctx, cache_len, rows_per_chunk;
     int32_t chunks, segs;    // segs: equal entry ranges per (b, query head)
     PagedKV pg;              // paged caches (block_table != nullptr)
 };
@@ -199,6 +391,7 @@ struct FinalArgs {
     const uint16_t* k;
     const uint2* entries;
     int64_t overflow_at;
+    int64_t head_stride;     // overflow entries per row (see list_index)
     const int32_t* list_count;
     float* tau;              // [B*hq] out
     uint32_t* group_flags;   // nullable [B*hk]: set when a row of the group used the recompute path

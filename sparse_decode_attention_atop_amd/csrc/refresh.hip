@@ -398,13 +398,17 @@ __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
     __shared__ SelectLds w;
     const int row = blockIdx.x, t = threadIdx.x;
     const int64_t ctx = head_ctx(a.pg, a.lq, row / a.hq, row % a.hq, a.ctx);
+    // Paged caches with a work split from the lengths: the lists of this
+    // sequence's chunks only, from the K stream's plan.
+    const bool plan = PAGED && a.pg.plan_cap != 0;
+    const int64_t rpc = plan ? a.pg.plan[0] : a.rows_per_chunk;
+    const int nl = a.chunks * kWavesPerBlock;
+    const int nlv = plan ? a.pg.plan[1 + row / a.hq] * kWavesPerBlock : nl;
     if ((int64_t)a.top_n >= ctx) {                     // N covers the row: keep everything
         if (t == 0) a.tau[row] = -INFINITY;
         return;
     }
-    const int nl = a.chunks * kWavesPerBlock;
-    const int64_t lbase = (int64_t)row * nl;
-    const int64_t capw = a.rows_per_chunk / kWavesPerBlock;
+    const int64_t capw = rpc / kWavesPerBlock;
 
     // Prefix of list lengths: thread t sums a contiguous run of lists.
     constexpr int PER = kMaxListsPerRow / kBlock;
@@ -412,7 +416,7 @@ __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         const int l = t * PER + k;
-        c[k] = l < nl ? a.list_count[lbase + l] : 0;
+        c[k] = l < nlv ? a.list_count[(int64_t)row * nl + l] : 0;
         sum += c[k];
     }
     int32_t run = block_scan(sum, reinterpret_cast<int32_t*>(w.scan)) - sum;
@@ -476,7 +480,8 @@ __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
 #pragma unroll
         for (int k = 0; k < KPT; ++k)
             if (k * kBlock < (int)total)
-                kv[k] = a.entries[list_index(lbase + l[k], off[k], capw, a.overflow_at)].y;
+                kv[k] = a.entries[list_index(row, l[k], off[k], capw, nl, a.head_stride,
+                                             a.overflow_at)].y;
 #pragma unroll
         for (int k = 0; k < KPT; ++k)
             if (k * kBlock < (int)total) kv[k] = float_key(__uint_as_float(kv[k]));

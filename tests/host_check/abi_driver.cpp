@@ -205,12 +205,21 @@ void valid_calls(const Shape& s)
             pg.page_rows = P;
             pg.max_pages = maxp;
             pg.num_pages = np;
-            ok(atopn_refresh_thresholds_paged(&d, &pg, s.top_n, q, kp, tau, ws, wsb, nullptr),
-               "refresh_paged");
-            ok(saga_decode_step_paged(&d, &pg, q, kp, vp, tau, out, cnt, ws, wsb, nullptr),
-               "decode_paged");
-            ok(atopn_refresh_decode_step_paged(&d, &pg, s.top_n, q, kp, vp, tau, out, cnt, ws,
-                                               wsb, nullptr), "refresh_decode_paged");
+            // Every sequence at ctx_len; lengths from ctx_len down to 0 (the
+            // kernels' work split follows them); every sequence empty.
+            for (int pattern = 0; pattern < 3; ++pattern) {
+                for (int bb = 0; bb < s.B; ++bb)
+                    lens[bb] = pattern == 0 ? (int32_t)ctx
+                             : pattern == 1 ? (int32_t)(ctx - ctx * bb / s.B)
+                                            : 0;
+                if (pattern == 1 && s.B > 1) lens[s.B - 1] = 0;
+                ok(atopn_refresh_thresholds_paged(&d, &pg, s.top_n, q, kp, tau, ws, wsb, nullptr),
+                   "refresh_paged");
+                ok(saga_decode_step_paged(&d, &pg, q, kp, vp, tau, out, cnt, ws, wsb, nullptr),
+                   "decode_paged");
+                ok(atopn_refresh_decode_step_paged(&d, &pg, s.top_n, q, kp, vp, tau, out, cnt, ws,
+                                                   wsb, nullptr), "refresh_decode_paged");
+            }
         }
 
         // Two query tokens per step when the group allows it.

@@ -73,40 +73,131 @@ void rd_span(const char* name, const T* p, int64_t n) { if (n > 0) { rd_span(p, 
 template <typename T>
 void wr_span(const char* name, T* p, int64_t n) { if (n > 0) { wr_span(p, n); note(name, p, 0, n - 1); } }
 
-// Selection-list entries: list lid holds at most capw entries (see list_index).
-int64_t entry_index(int64_t lid, int64_t E, int64_t capw, int64_t overflow_at)
+// Selection-list entries: list `local` of row `head` holds at most capw
+// entries (see list_index).
+int64_t entry_index(int64_t head, int64_t local, int64_t E, int64_t capw, int64_t nl,
+                    int64_t head_stride, int64_t overflow_at)
 {
-    return E < kListPrimary ? lid * kListPrimary + E : overflow_at + lid * capw + (E - kListPrimary);
+    return E < kListPrimary ? (head * nl + local) * kListPrimary + E
+                            : overflow_at + head * head_stride + local * capw + (E - kListPrimary);
 }
-template <typename T>
-void touch_lists(T* entries, int64_t lists, int64_t capw, int64_t overflow_at)
+
+// The lists a call's kernels index: rows 0 .. heads-1, lists 0 .. used-1 of
+// the nl per row, capw entries each.
+struct ListUse {
+    int64_t heads, nl, used, capw, head_stride, overflow_at;
+};
+
+// Host model of paged_rows_per_chunk / paged_chunks (kernels.hpp), from the
+// lengths the driver passes in host memory: the rows per chunk and the most
+// chunks any sequence uses and the K stream's work items.
+void paged_plan(const PagedKV& pg, int B, int hk, int64_t ctx, int64_t* rpc, int64_t* most,
+                int64_t* items)
 {
-    EXPECT(capw >= 1);
-    const int64_t last = lists - 1;
-    const int64_t top = capw - 1 < kListPrimary ? capw - 1 : kListPrimary - 1;
-    note("list entries (primary)", entries, 0, entry_index(last, top, capw, overflow_at));
-    if (capw > kListPrimary)
-        note("list entries (overflow)", entries, entry_index(0, kListPrimary, capw, overflow_at),
-             entry_index(last, capw - 1, capw, overflow_at));
-    for (const int64_t lid : {(int64_t)0, last}) {
-        const int64_t hi = capw - 1;
-        const int64_t e1 = hi < kListPrimary ? hi : kListPrimary - 1;
-        if constexpr (std::is_const_v<T>) {
-            rd(entries, entry_index(lid, 0, capw, overflow_at));
-            rd(entries, entry_index(lid, e1, capw, overflow_at));
-            if (hi >= kListPrimary) {
-                rd(entries, entry_index(lid, kListPrimary, capw, overflow_at));
-                rd(entries, entry_index(lid, hi, capw, overflow_at));
+    const int64_t cap = (int64_t)pg.max_pages * pg.page_rows;
+    int64_t sum = 0, mx = 0;
+    for (int b = 0; b < B; ++b) {
+        int64_t c = pg.ctx_lens[b];
+        c = c < 0 ? 0 : (c > cap ? cap : c);
+        c = c < ctx ? c : ctx;
+        sum += c;
+        mx = c > mx ? c : mx;
+    }
+    const int64_t q = pg.plan_quantum;
+    auto up = [q](int64_t x) { return (x + q - 1) / q * q; };
+    int64_t r = up(((int64_t)hk * sum + pg.plan_target - 1) / pg.plan_target);
+    r = r < pg.plan_rows_max ? r : pg.plan_rows_max;
+    const int64_t need = up((mx + pg.plan_cap - 1) / pg.plan_cap);
+    r = r > need ? r : need;
+    r = r > q ? r : q;
+    auto count = [&](int64_t rr) {
+        int64_t n = 0;
+        for (int b = 0; b < B; ++b) {
+            int64_t c = pg.ctx_lens[b];
+            c = c < 0 ? 0 : (c > cap ? cap : c);
+            c = c < ctx ? c : ctx;
+            n += (c + rr - 1) / rr * hk;
+        }
+        return n;
+    };
+    if (count(r) > pg.plan_target) {
+        int64_t lo = r / q, hi = up(mx) / q;
+        hi = hi < pg.plan_rows_max / q ? hi : pg.plan_rows_max / q;
+        if (hi > lo) {
+            while (hi - lo > 1) {
+                const int64_t mid = lo + (hi - lo) / 2;
+                if (count(mid * q) > pg.plan_target) lo = mid; else hi = mid;
             }
-        } else {
-            wr(entries, entry_index(lid, 0, capw, overflow_at));
-            wr(entries, entry_index(lid, e1, capw, overflow_at));
-            if (hi >= kListPrimary) {
-                wr(entries, entry_index(lid, kListPrimary, capw, overflow_at));
-                wr(entries, entry_index(lid, hi, capw, overflow_at));
-            }
+            r = hi * q;
         }
     }
+    *rpc = r;
+    *most = (mx + r - 1) / r;
+    *items = count(r);
+}
+
+// Lists of one list-path call; checks the chunk plan the kernels follow.
+ListUse list_use(int B, int hq, int hk, int64_t ctx, int chunks, int64_t rows_per_chunk,
+                 const PagedKV& pg, int64_t head_stride, int64_t overflow_at)
+{
+    EXPECT(chunks >= 1 && rows_per_chunk >= 1);
+    EXPECT((int64_t)chunks * kWavesPerBlock <= kMaxListsPerRow);
+    int64_t rpc = rows_per_chunk, used_chunks = chunks;
+    if (pg.block_table && pg.plan_cap) {
+        EXPECT(pg.plan_cap == chunks);
+        EXPECT(pg.plan_target >= 1 && pg.plan_quantum >= 64 && pg.plan_quantum % 64 == 0);
+        EXPECT(pg.plan_rows_max >= pg.plan_quantum);
+        int64_t items = 0;
+        paged_plan(pg, B, hk, ctx, &rpc, &used_chunks, &items);
+        EXPECT(used_chunks <= chunks);                    // every row of every sequence
+        EXPECT(rpc <= pg.plan_rows_max);
+        EXPECT(items <= pg.plan_grid);                    // one K-stream workgroup per item
+        EXPECT(pg.plan_grid <= (int64_t)B * hk * chunks && pg.plan_grid <= 0x7fffffffLL);
+    } else {
+        EXPECT((int64_t)chunks * rows_per_chunk >= ctx);      // every row in a chunk
+        EXPECT((int64_t)(chunks - 1) * rows_per_chunk < ctx); // no chunk entirely empty
+    }
+    EXPECT(rpc % 64 == 0);                                    // whole 4-wave tiles
+    // A row's overflow entries (the last at used*rpc - kListPrimary - 1 past
+    // the row's start) stay inside its head_stride slots.
+    EXPECT(used_chunks * rpc <= head_stride + kListPrimary);
+    return {(int64_t)B * hq, (int64_t)chunks * kWavesPerBlock, used_chunks * kWavesPerBlock,
+            rpc / kWavesPerBlock, head_stride, overflow_at};
+}
+
+template <typename T>
+void touch_lists(T* entries, const ListUse& u)
+{
+    EXPECT(u.capw >= 1 && u.heads >= 1 && u.used >= 0 && u.used <= u.nl);
+    if (u.used == 0) return;                     // every sequence empty: no list is used
+    const int64_t h1 = u.heads - 1, l1 = u.used - 1;
+    const int64_t top = u.capw - 1 < kListPrimary ? u.capw - 1 : kListPrimary - 1;
+    auto at = [&](int64_t h, int64_t l, int64_t E) {
+        return entry_index(h, l, E, u.capw, u.nl, u.head_stride, u.overflow_at);
+    };
+    note("list entries (primary)", entries, 0, at(h1, l1, top));
+    if (u.capw > kListPrimary)
+        note("list entries (overflow)", entries, at(0, 0, kListPrimary), at(h1, l1, u.capw - 1));
+    for (const int64_t h : {(int64_t)0, h1})
+        for (const int64_t lid : {(int64_t)0, l1}) {
+            const int64_t hi = u.capw - 1;
+            const int64_t e1 = hi < kListPrimary ? hi : kListPrimary - 1;
+            if constexpr (std::is_const_v<T>) {
+                rd(entries, at(h, lid, 0));
+                rd(entries, at(h, lid, e1));
+                if (hi >= kListPrimary) {
+                    rd(entries, at(h, lid, kListPrimary));
+                    rd(entries, at(h, lid, hi));
+                }
+            } else {
+                wr(entries, at(h, lid, 0));
+                wr(entries, at(h, lid, e1));
+                if (hi >= kListPrimary) {
+                    wr(entries, at(h, lid, kListPrimary));
+                    wr(entries, at(h, lid, hi));
+                }
+            }
+        }
 }
 
 // Last K (or V) element a kernel reads for a contiguous cache of `heads`
@@ -140,16 +231,13 @@ hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t)
     EXPECT(D == 32 || D == 64 || D == 128);
     EXPECT(a.B >= 1 && a.hk >= 1 && a.hq == a.hk * a.Gk && a.Gk <= 16);
     EXPECT((int64_t)a.B * a.hk <= 65535);                       // grid.y
-    EXPECT(a.chunks >= 1 && a.rows_per_chunk >= 1);
-    EXPECT((int64_t)a.chunks * a.rows_per_chunk >= a.ctx);      // every row in a chunk
-    EXPECT((int64_t)(a.chunks - 1) * a.rows_per_chunk < a.ctx); // no chunk entirely empty
-    EXPECT(a.rows_per_chunk % 64 == 0);                         // whole 4-wave tiles
-    EXPECT((int64_t)a.chunks * kWavesPerBlock <= kMaxListsPerRow);
+    const ListUse u = list_use(a.B, a.hq, a.hk, a.ctx, a.chunks, a.rows_per_chunk, a.pg,
+                               a.head_stride, a.overflow_at);
     const int64_t lists = (int64_t)a.B * a.hq * a.chunks * kWavesPerBlock;
-    const int64_t capw = a.rows_per_chunk / kWavesPerBlock;
     wr_span("list counts", a.list_count, lists);
     wr_span("list maxima", a.list_max, lists);
-    touch_lists(a.entries, lists, capw, a.overflow_at);
+    touch_lists(a.entries, u);
+    if (a.pg.block_table && a.pg.plan_cap) wr_span("paged plan", a.pg.plan, (int64_t)a.B + 1);
     rd_span(a.q, (int64_t)a.B * a.hq * D);
     rd_span(a.tau, (int64_t)a.B * a.hq);
     if (a.group_flags) rd_span("group flags", a.group_flags, (int64_t)a.B * a.hk);
@@ -169,14 +257,16 @@ hipError_t launch_gather(int D, const GatherArgs& a, hipStream_t)
 {
     ++g_launches;
     EXPECT(D == 32 || D == 64 || D == 128);
-    EXPECT(a.segs >= 1 && a.chunks >= 1);
-    EXPECT((int64_t)a.chunks * kWavesPerBlock <= kMaxListsPerRow);
-    EXPECT(a.hq == a.hv * a.Gv);
+    EXPECT(a.segs >= 1);
+    EXPECT(a.hq == a.hv * a.Gv && a.hq % a.hk == 0);
     EXPECT((int64_t)a.segs * a.B * a.hq <= 0x7fffffffLL);      // 1-D grid
+    const ListUse u = list_use(a.B, a.hq, a.hk, a.ctx, a.chunks, a.rows_per_chunk, a.pg,
+                               a.head_stride, a.overflow_at);
     const int64_t lists = (int64_t)a.B * a.hq * a.chunks * kWavesPerBlock;
     rd_span("list counts", a.list_count, lists);
     rd_span("list maxima", a.list_max, lists);
-    touch_lists(a.entries, lists, a.rows_per_chunk / kWavesPerBlock, a.overflow_at);
+    touch_lists(a.entries, u);
+    if (a.pg.block_table && a.pg.plan_cap) rd_span("paged plan", a.pg.plan, (int64_t)a.B + 1);
     if (a.tau_filter) rd_span(a.tau_filter, (int64_t)a.B * a.hq);
     if (a.v_scale) rd_span(a.v_scale, (int64_t)a.B * a.hv);
     touch_partials(a.part, (int64_t)a.B * a.hq * a.segs, D);
@@ -225,10 +315,12 @@ hipError_t launch_refresh_final(int D, const FinalArgs& a, hipStream_t)
     ++g_launches;
     EXPECT(D == 32 || D == 64 || D == 128);
     EXPECT(a.top_n >= 1 && (int64_t)a.top_n < a.ctx);
-    EXPECT((int64_t)a.chunks * kWavesPerBlock <= kMaxListsPerRow);
+    const ListUse u = list_use(a.B, a.hq, a.hk, a.ctx, a.chunks, a.rows_per_chunk, a.pg,
+                               a.head_stride, a.overflow_at);
     const int64_t lists = (int64_t)a.B * a.hq * a.chunks * kWavesPerBlock;
     rd_span("list counts", a.list_count, lists);
-    touch_lists(a.entries, lists, a.rows_per_chunk / kWavesPerBlock, a.overflow_at);
+    touch_lists(a.entries, u);
+    if (a.pg.block_table && a.pg.plan_cap) rd_span("paged plan", a.pg.plan, (int64_t)a.B + 1);
     wr_span(a.tau, (int64_t)a.B * a.hq);
     if (a.group_flags) wr_span("group flags", a.group_flags, (int64_t)a.B * a.hk);
     rd_span(a.q, (int64_t)a.B * a.hq * D);
