@@ -57,7 +57,17 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
     // use, serves the block reductions.
     int64_t rpc = a.rows_per_chunk;
     if constexpr (PAGED) {
-        if (a.pg.plan_cap) {
+        if (a.pg.plan_cap && a.B <= kWave) {
+            // Every wave computes the plan on its own (no LDS, no barrier).
+            const uint32_t len = plan_len(a.pg, lane, a.B, a.ctx);
+            rpc = paged_rows_per_chunk_wave(a.pg, a.B, a.hk, len);
+            if (blockIdx.x == 0 && wave == 0) {   // the plan, for the kernels after this one
+                if (lane < a.B) a.pg.plan[1 + lane] = (int32_t)((len + (uint32_t)rpc - 1) / (uint32_t)rpc);
+                if (lane == 0) a.pg.plan[0] = (int32_t)rpc;
+            }
+            if (!paged_item_wave(a.hk, rpc, len, blockIdx.x, &b, &g, &chunk))
+                return;                                                // whole workgroup
+        } else if (a.pg.plan_cap) {
             int64_t* red = reinterpret_cast<int64_t*>(&queue[0][0][0]);
             const uint32_t len0 = plan_len(a.pg, threadIdx.x, a.B, a.ctx);
             rpc = paged_rows_per_chunk(a.pg, a.B, a.hk, a.ctx, len0, red);

@@ -242,6 +242,83 @@ __device__ __forceinline__ int64_t paged_rows_per_chunk(const PagedKV& pg, int B
     return r;
 }
 
+// The same plan computed by one wave on its own, for B <= kWave: lane l holds
+// plan_len(l) in `len`; no LDS and no barrier (every wave of a workgroup
+// gets the same result).  Candidates r + (base + lane) * plan_quantum are
+// tested 64 at a time; the first that fits wins (the same r as the block
+// version's search).
+__device__ __forceinline__ int64_t readlane64(int64_t v, int l)
+{
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), l);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int64_t paged_rows_per_chunk_wave(const PagedKV& pg, int B, int hk,
+                                                             uint32_t len)
+{
+    int64_t sum = len;
+    uint32_t mx = len;
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        sum += __shfl_xor(sum, off);
+        const uint32_t o = __shfl_xor(mx, off);
+        mx = o > mx ? o : mx;
+    }
+    sum = wave_uniform(sum);
+    const int64_t m = __builtin_amdgcn_readfirstlane(mx);
+    const int64_t q = pg.plan_quantum, target = pg.plan_target;
+    auto up = [q](int64_t x) { return (x + q - 1) / q * q; };
+    int64_t r = up(((int64_t)hk * sum + target - 1) / target);
+    r = r < pg.plan_rows_max ? r : pg.plan_rows_max;
+    const int64_t need = up((m + pg.plan_cap - 1) / pg.plan_cap);
+    r = r > need ? r : need;
+    r = r > q ? r : q;
+    const int64_t lo = r / q;
+    int64_t hi = up(m) / q;
+    hi = hi < pg.plan_rows_max / q ? hi : pg.plan_rows_max / q;
+    if (hi <= lo) return r;
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int64_t base = lo;; base += kWave) {     // ends: candidates >= hi always fit
+        const int64_t cand = base + lane;
+        bool ok = cand >= hi;
+        if (!ok) {
+            const uint32_t rc = (uint32_t)(cand * q);
+            int64_t n = 0;
+            for (int b = 0; b < B; ++b) {
+                const uint32_t lb = __builtin_amdgcn_readlane(len, b);
+                n += (lb + rc - 1) / rc;
+            }
+            ok = n * hk <= target;
+        }
+        const uint64_t bal = __ballot(ok);
+        if (bal) return (base + __ffsll((unsigned long long)bal) - 1) * q;
+    }
+}
+
+// paged_item for B <= kWave, one wave on its own (same inputs as
+// paged_rows_per_chunk_wave).
+__device__ __forceinline__ bool paged_item_wave(int hk, int64_t r, uint32_t len, int64_t item,
+                                                int* b_out, int* g_out, int* chunk_out)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t n = (int64_t)((len + (uint32_t)r - 1) / (uint32_t)r) * hk;
+    int64_t incl = n;
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int64_t u = __shfl_up(incl, off);
+        if (lane >= off) incl += u;
+    }
+    const int64_t lo = incl - n;
+    const uint64_t bal = __ballot(n > 0 && item >= lo && item < lo + n);
+    if (!bal) return false;
+    const int lb = __ffsll((unsigned long long)bal) - 1;
+    const int64_t off = item - readlane64(lo, lb);
+    const int64_t nb = readlane64(n, lb) / hk;
+    *b_out = lb;
+    *g_out = (int)(off / nb);
+    *chunk_out = (int)(off - off / nb * nb);
+    return true;
+}
+
 // Chunks of sequence b for rows-per-chunk r (0 for an empty sequence).
 __device__ __forceinline__ int64_t paged_chunks(const PagedKV& pg, int b, int64_t ctx, int64_t r)
 {
