@@ -97,6 +97,9 @@ def parse():
                    help="time the schedule on paged caches with pages of this many rows")
     p.add_argument("--varlen", action="store_true",
                    help="with --paged: per-sequence lengths drawn from [L/4, L]")
+    p.add_argument("--top-n", type=int, default=0,
+                   help="main schedule with this N instead of the workload's (the workload is "
+                        "then reported as <name>_n<N>)")
     p.add_argument("--lq", type=int, default=0,
                    help="time the schedule with this many query tokens per head and step")
     p.add_argument("--fp8k", action="store_true",
@@ -763,6 +766,8 @@ def main():
               flush=True)
         return
     w = wl.WORKLOADS[args.workload]
+    if args.top_n:
+        w = w.with_(name=f"{w.name}_n{args.top_n}", top_n=args.top_n)
     if args.sigma:
         # The pages' Sigma-style alternative: (2 h_k, d_k / 2) instead of (h_k, d_k), d_v kept.
         w = w.with_(name=w.name + "_sigma", h_k=2 * w.h_k, head_dim=w.head_dim // 2,

@@ -111,6 +111,14 @@ size_t saga_workspace_bytes(const saga_dims* dims, int32_t top_n);
  * it selects exactly top_n entries when there are no ties (ties at the
  * threshold are all kept).  -0.0 logits are ranked as +0.0.
  *
+ * Cost.  One pass over K collects the candidates at or above a pivot taken
+ * from a sample of at most 2048 rows (about 1.7 * top_n of them); the answer
+ * is then selected among the candidates, in registers up to 8192 per row and
+ * by three radix passes over the candidate lists above that, so any top_n
+ * costs one K pass plus work proportional to top_n.  Only when the sample
+ * misleads (fewer than top_n candidates, rare by construction) does a row
+ * recompute its logits, three more passes over its key head.
+ *
  *   q_dev, k_cache_dev   inputs, layouts above
  *   thresholds_dev       output fp32 [batch][h_q]
  *   logits_debug_dev     optional output fp32 [batch][h_q][ctx_len] (NULL: skip)

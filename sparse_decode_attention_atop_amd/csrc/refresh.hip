@@ -390,6 +390,57 @@ __device__ uint32_t select_by_recompute(const FinalArgs& a, int row, int64_t ctx
     return prefix;
 }
 
+// Exact N-th largest of one row from candidate lists too long to stage
+// (more than kFinalStage entries, at least N of them): three radix passes
+// (11, 11, 10 bits) over the keys of every list entry, read from the lists
+// on each pass.  `pre` holds the lists' entry offsets (pre[l] = entries before
+// list l, pre[kMaxListsPerRow] = total).  Thread t takes EPT consecutive
+// entries per round: one binary search over the offsets for the first, a
+// forward walk for the rest.
+template <int EPT>
+__device__ uint32_t select_from_lists(const FinalArgs& a, int row, int nl, int64_t capw,
+                                      const int32_t* pre, uint32_t total, SelectLds& w)
+{
+    uint32_t prefix = 0u, rank = a.top_n;
+    for (int pass = 0; pass < 3; ++pass) {
+        const int sh = digit_shift(pass);
+        const uint32_t dm = digit_mask(pass), pm = prefix_mask(pass);
+        for (int k = threadIdx.x; k < kHistBins; k += kBlock) w.hist[k] = 0u;
+        __syncthreads();
+        for (uint32_t base = 0; base < total; base += kBlock * EPT) {
+            const uint32_t E0 = base + threadIdx.x * EPT;
+            if (E0 < total) {
+                int l0 = 0, hi = kMaxListsPerRow - 1;     // the last list starting at or before E0
+                while (l0 < hi) {
+                    const int mid = (l0 + hi + 1) >> 1;
+                    if ((uint32_t)pre[mid] <= E0) l0 = mid;
+                    else hi = mid - 1;
+                }
+                uint32_t kv[EPT];
+#pragma unroll
+                for (int k = 0; k < EPT; ++k) {
+                    const uint32_t E = E0 + k < total ? E0 + k : total - 1;
+                    while ((uint32_t)pre[l0 + 1] <= E) ++l0;   // skips empty lists; stops below the last
+                    kv[k] = a.entries[list_index(row, l0, E - (uint32_t)pre[l0], capw, nl,
+                                                 a.head_stride, a.overflow_at)].y;
+                }
+#pragma unroll
+                for (int k = 0; k < EPT; ++k) {
+                    const uint32_t key = float_key(__uint_as_float(kv[k]));
+                    if (E0 + k < total && (key & pm) == prefix)
+                        atomicAdd(&w.hist[(key >> sh) & dm], 1u);
+                }
+            }
+        }
+        __syncthreads();
+        uint32_t bin, rin, cnt;
+        find_rank_bucket<kHistBins>(w.hist, rank, w.scan, w.result, &bin, &rin, &cnt);
+        prefix |= bin << sh;
+        rank = rin;
+    }
+    return prefix;
+}
+
 template <int D, int U, bool PAGED, bool FP8>
 __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
 {
@@ -486,6 +537,10 @@ __global__ __launch_bounds__(kBlock) void refresh_final_kernel(FinalArgs a)
         for (int k = 0; k < KPT; ++k)
             if (k * kBlock < (int)total) kv[k] = float_key(__uint_as_float(kv[k]));
         key = reg_radix_select<KPT>(kv, total, a.top_n, w);
+    } else if (total >= a.top_n) {
+        // The lists are complete (every logit >= the pivot) but too long to
+        // stage: select over them in place, no K traffic.
+        key = select_from_lists<8>(a, row, nl, capw, pre, total, w);
     } else {
         key = select_by_recompute<D, U, PAGED, FP8>(a, row, ctx, w);
         // The lists miss entries of this row: a fused decode must re-stream its group.

@@ -4,6 +4,8 @@ Each input is built so that a given path runs, and the test checks on the host
 (from the GPU's own debug logits and the sampling rule) that it does:
 - a candidate set of more than 6144 entries per row, which fills nearly every
   register slot of the final select but stays under the 8192-entry staging cap;
+- a candidate set above that cap, which the select reads from the lists in
+  place (three radix passes over the entries) instead of recomputing logits;
 - a candidate set in which every logit is equal (the select's zero-range case);
 - selected rows in two far-apart bands, so the gather's walk over the list
   offsets crosses long runs of empty lists.
@@ -59,6 +61,23 @@ def test_select_with_candidates_near_the_staging_cap():
     lg = gpu["logits"][0]
     counts = [candidates(lg[b, i], N, ctx) for b in range(lg.shape[0]) for i in range(lg.shape[1])]
     assert any(6144 < c <= STAGE for c in counts), counts
+
+
+def test_select_with_candidates_above_the_staging_cap():
+    ctx, N = 40000, 7000
+    q, K, V = make_inputs(2, 8, 2, 4, 64, ctx, 1, seed=73, heavy=False)
+    print(f"[refresh paths] above cap: q{tuple(q.shape)} ctx={ctx} N={N}", flush=True)
+    gpu = check_exact(q, K, V, ctx, N)
+    lg = gpu["logits"][0]
+    counts = [candidates(lg[b, i], N, ctx) for b in range(lg.shape[0]) for i in range(lg.shape[1])]
+    assert any(c > STAGE for c in counts), counts
+    # The one-call refresh step on the same inputs: the same thresholds, and its
+    # gather reads the long candidate lists filtered by tau.
+    fz = run_fused(q, K, V, [ctx], N, 1)
+    assert np.array_equal(fz["tau"][0].view(np.uint32), gpu["tau"][0].view(np.uint32))
+    assert np.array_equal(fz["counts"][0], gpu["counts"][0])
+    ref, _ = oracle.masked(to_np_bits(q)[0], to_np_bits(K), to_np_bits(V), ctx, gpu["bitmap"][0])
+    assert np.abs(fz["out"][0] - ref).max() <= OUT_TOL
 
 
 def test_select_when_every_candidate_ties():
