@@ -110,7 +110,8 @@ def test_each_token_equals_the_one_token_path(name, fused):
             tau_o = orc["tau"][t]
             tg = tau_g[:, :, j].cpu().numpy().astype(np.float64)
             both_inf = np.isneginf(tg) & np.isneginf(tau_o)
-            assert (both_inf | (np.abs(np.where(both_inf, 0.0, tg - tau_o)) <= 1e-4)).all()
+            diff = np.subtract(tg, tau_o, out=np.zeros_like(tg), where=~both_inf)
+            assert (both_inf | (np.abs(diff) <= 1e-4)).all()
             sel = bitmap_to_bool(bm, ctx_j[t])
             s_o = orc["logits"][t, :, :, :ctx_j[t]]
             near = np.abs(s_o - tau_o[..., None]) <= NEAR_TAU

@@ -178,7 +178,8 @@ def test_per_sequence_lengths_match_each_sequence_alone(fused):
             tau_o = orc["tau"][t, 0]
             tg = tau_g[b].cpu().numpy().astype(np.float64)
             both_inf = np.isneginf(tg) & np.isneginf(tau_o)
-            assert (both_inf | (np.abs(np.where(both_inf, 0.0, tg - tau_o)) <= 1e-4)).all()
+            diff = np.subtract(tg, tau_o, out=np.zeros_like(tg), where=~both_inf)
+            assert (both_inf | (np.abs(diff) <= 1e-4)).all()
             sel = bitmap_to_bool(bm_np[0], ctx_b[t])
             s = orc["logits"][t, 0, :, :ctx_b[t]]
             near = np.abs(s - tau_o[:, None]) <= NEAR_TAU
