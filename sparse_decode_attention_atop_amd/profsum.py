@@ -12,6 +12,9 @@
         copy of ``bench.py --calibrate``; prints a markdown table and the JSON
         block that ``bench.py`` reads.
 
+    python -m sparse_decode_attention_atop_amd.profsum sweep FILE
+        the markdown table of a ``bench.py --sweep`` run (its JSON lines).
+
     python -m sparse_decode_attention_atop_amd.profsum util DIR
         MFMA and VALU use per kernel of a plain decode call from a
         ``rocprofv3 --pmc MfmaUtil VALUBusy MfmaFlopsBF16`` run written as CSV
@@ -32,8 +35,9 @@ import re
 import sqlite3
 import sys
 
-OURS = re.compile(r"select_stream|gather_kernel|combine_kernel|refresh_final|pivot_kernel|"
-                  r"sample_logits|full_attn|fill_u32")
+# This library's kernels (not torch's vectorized_gather_kernel and the like).
+OURS = re.compile(r"(?<![A-Za-z_])(select_stream|gather_kernel|combine_kernel|refresh_final|"
+                  r"pivot_kernel|sample_logits|full_attn|fill_u32)")
 
 
 def short(name: str) -> str:
@@ -125,6 +129,23 @@ def traffic(workload, fdir, wdir, cfdir, cwdir):
     return "\n".join(lines) + "\n\n```json\n" + json.dumps(blob, indent=1) + "\n```\n"
 
 
+def sweep(path):
+    """Markdown table of bench.py --sweep's JSON lines (other lines skipped)."""
+    pts = []
+    for ln in open(path):
+        ln = ln.strip()
+        if ln.startswith("{") and '"point"' in ln:
+            pts.append(json.loads(ln))
+    out = ["| family | L | N | B | layers | saga (ms/layer) | gqa (ms/layer) | speedup | "
+           "saga GB/s | gqa GB/s |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for p in pts:
+        out.append(f"| {p['family']} | {p['L']} | {p['top_n']} | {p['batch']} | "
+                   f"{p['layers_timed']} | {p['saga_atopn_ms_per_layer']:.4f} | "
+                   f"{p['gqa_full_ms_per_layer']:.4f} | {p['speedup']:.2f} | "
+                   f"{p['saga_hbm_gbs']:.0f} | {p['gqa_hbm_gbs']:.0f} |")
+    return "\n".join(out)
+
+
 def util(d):
     names = ["MfmaUtil", "VALUBusy", "MfmaFlopsBF16"]
     kinds = ["select_stream", "gather_kernel", "combine_kernel"]
@@ -145,6 +166,8 @@ def main(argv):
         print(trace(argv[1], int(argv[2]) if len(argv) > 2 else 25))
     elif len(argv) == 6 and argv[0] == "traffic":
         print(traffic(*argv[1:]))
+    elif len(argv) == 2 and argv[0] == "sweep":
+        print(sweep(argv[1]))
     elif len(argv) == 2 and argv[0] == "util":
         print(util(argv[1]))
     else:

@@ -18,6 +18,7 @@ SAMPLE = "saga::sample_logits_kernel<64, 4, false, false>(saga::SampleArgs)"
 PIVOT = "saga::pivot_kernel(float*, float*, int)"
 FINAL = "saga::refresh_final_kernel<64, 1, false, false>(saga::FinalArgs)"
 TORCH = "at::native::vectorized_elementwise_kernel<4>(int, float*)"
+TORCH_GATHER = "void at::native::vectorized_gather_kernel<16, long>(char*, char*, long*, int)"
 
 
 def seq(*names):
@@ -55,3 +56,21 @@ def test_counter_csv_sums_dimensions_per_dispatch(tmp_path):
     got = profsum._counter(str(tmp_path), "FETCH_SIZE")
     assert got == {1: (S, 101.0), 2: (G, 7.0)}
     assert profsum._calibration(str(tmp_path), "FETCH_SIZE") == 101.0
+
+
+def test_torch_gather_kernels_are_not_ours():
+    d = seq(S, TORCH_GATHER, G, C)
+    calls = profsum._decode_calls(d)
+    assert calls == [{"select_stream": 0.0, "gather_kernel": 20.0, "combine_kernel": 30.0}]
+
+
+def test_sweep_table_from_json_lines(tmp_path):
+    f = tmp_path / "sweep.log"
+    f.write_text('[bench] progress\n'
+                 '{"point": "p", "family": "llama", "L": 8192, "top_n": 512, "batch": 1, '
+                 '"layers_timed": 16, "saga_atopn_ms_per_layer": 0.0184, '
+                 '"gqa_full_ms_per_layer": 0.0164, "speedup": 0.891, "saga_hbm_gbs": 345.2, '
+                 '"gqa_hbm_gbs": 1022.0, "cache_resident": false}\n')
+    lines = profsum.sweep(str(f)).splitlines()
+    assert len(lines) == 3
+    assert lines[2] == "| llama | 8192 | 512 | 1 | 16 | 0.0184 | 0.0164 | 0.89 | 345 | 1022 |"
