@@ -175,7 +175,7 @@ int saga_decode_step(const saga_dims* dims, const void* q_dev, const void* k_cac
  * saga_workspace_bytes(dims, top_n) exceeds SAGA_NOALLOC_SCRATCH_BYTES (for
  * example batch 1 at 128K context fits; batch 16 does not).
  */
-#define SAGA_NOALLOC_SCRATCH_BYTES (64u << 20)
+#define SAGA_NOALLOC_SCRATCH_BYTES (128u << 20)
 int saga_decode_step_noalloc(const saga_dims* dims, const void* q_dev, const void* k_cache_dev,
                              const void* v_cache_dev, const float* thresholds_dev, void* out_dev,
                              int32_t* sel_counts_dev, void* stream);

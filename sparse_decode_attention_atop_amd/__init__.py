@@ -43,7 +43,7 @@ EXPORTED_SYMBOLS = ("saga_workspace_bytes", "atopn_refresh_thresholds", "saga_de
                     "saga_full_attention", "saga_decode_step_noalloc", "saga_status_string",
                     "saga_version")
 
-NOALLOC_SCRATCH_BYTES = 64 << 20     # SAGA_NOALLOC_SCRATCH_BYTES in include/saga.h
+NOALLOC_SCRATCH_BYTES = 128 << 20    # SAGA_NOALLOC_SCRATCH_BYTES in include/saga.h
 
 SAGA_OK = 0
 SAGA_ERR_INVALID_ARGUMENT = 1

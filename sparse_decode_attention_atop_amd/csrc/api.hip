@@ -396,7 +396,12 @@ int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunkin
 // plan of the stream (the same for paged and contiguous caches, so both give
 // the same sums), shortened when needed so that a chunk's worst case (every
 // row selected for every head slot) fits the LDS budget; never more chunks
-// than the workspace's partials hold.
+// than the workspace's partials hold.  Launches of fewer than kFusedMinBlocks
+// workgroups (short contexts) keep the list path: there a chunk's selected
+// value rows are many for one workgroup to read, and the list path's gather
+// spreads them over many.
+constexpr int64_t kFusedMinBlocks = 128;
+
 struct FusedPlan {
     bool use = false;
     Chunking ch{};
@@ -443,7 +448,7 @@ FusedPlan plan_fused(const saga_dims* dims, const Layout& L, const RowModel& rm)
             ch.chunks = (int)((dims->ctx_len + ch.rows - 1) / ch.rows);
             if (ch.chunks > L.max_chunks) break;
         }
-        if (!ok) continue;
+        if (!ok || groups * ch.chunks < kFusedMinBlocks) continue;
         if (best.use && 10 * ch.chunks < 7 * best.ch.chunks) continue;
         FusedPlan f;
         f.use = true;

@@ -468,6 +468,7 @@ int main(int argc, char** argv)
         const Shape bigs[] = {
             {"llama_like_128k_b16", 16, 32, 4, 8, 64, 0, 131104, 2048},
             {"qwen_like_128k_b1", 1, 12, 1, 2, 128, 0, 131104, 1024},
+            {"llama_like_128k_b1", 1, 32, 4, 8, 64, 0, 131104, 2048},
             {"qwen_like_128k_b16", 16, 12, 1, 2, 128, 0, 131104, 1024},
             {"paged_128k", 2, 32, 4, 8, 64, 0, 131072, 2048},
             {"largest_head_d128", 1, 4, 1, 1, 128, 0, ((int64_t)1 << 23) - 1, 1024},

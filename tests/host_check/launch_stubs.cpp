@@ -360,6 +360,7 @@ hipError_t launch_select_gather(int D, int DV, const FusedArgs& a, size_t lds_by
     // Every row of a wave's share, for every head slot of a queue, fits.
     EXPECT((int64_t)a.qcap >= a.rows_per_chunk / kWavesPerBlock * ((a.Gk + 3) / 4));
     EXPECT(a.hcap >= a.rows_per_chunk);                         // a slot's list holds every row
+    EXPECT((int64_t)a.B * a.hk * a.chunks >= 128);              // the plan's smallest fused launch
     EXPECT((int64_t)16 * a.qcap <= 65536);                      // 16-bit entry indices
     EXPECT(lds_bytes >= (size_t)16 * a.qcap * 8 + (size_t)a.Gk * a.hcap * 2);
     EXPECT(lds_bytes <= (size_t)kLdsPerGroup);

@@ -48,11 +48,13 @@ def test_no_alloc_matches_workspace_call_twice():
     compare(q[0], K, V, 3000, 100)
 
 
-def test_no_alloc_at_long_context():
-    """Qwen-like heads at 128K context, batch 1 (27 MiB of scratch)."""
-    w = wl.QWEN_128K_B1
+@pytest.mark.parametrize("name", ["qwen_like_128k_b1", "sweep_llama_L131072_N2048_B1"])
+def test_no_alloc_at_long_context(name):
+    """Batch 1 at 128K context: Qwen-like heads (27 MiB of scratch) and
+    Llama-like heads (69 MiB)."""
+    w = {x.name: x for x in [wl.QWEN_128K_B1, *wl.sweep()]}[name]
     x = wl.make_layer(w, 0, device="cuda", steps=1)
-    print("[no-alloc] qwen_like 128K batch 1", flush=True)
+    print(f"[no-alloc] {name}", flush=True)
     compare(x["q"][0], x["K"], x["V"], w.L, w.top_n)
 
 
