@@ -189,6 +189,59 @@ def test_per_sequence_lengths_match_each_sequence_alone(fused):
             assert err <= OUT_TOL, f"b={b} t={t}: {err:.3e}"
 
 
+@pytest.mark.parametrize("B", [80, 264])
+def test_many_sequences_work_split(B):
+    """More sequences than one wave (80) and than one workgroup (264) holds:
+    the K stream's work split from the lengths then takes its workgroup-wide
+    forms (a candidate search over lengths held in LDS; with more than 256
+    sequences, several passes and a bisection).  Lengths are mixed, a few are
+    0 and a few below N.  Every sequence's thresholds and counts must equal
+    that sequence run alone on contiguous caches (bit for bit), empty
+    sequences select nothing and output zeros, and sampled sequences' outputs
+    are checked against the fp64 oracle on the GPU's selection."""
+    hq, hk, hv, d, P = 4, 1, 2, 64, 256
+    maxp, N, n, T = 6, 64, 2, 2
+    rows = maxp * P
+    q, K, V = make_inputs(B, hq, hk, hv, d, rows, T, seed=93 + B)
+    rng = np.random.default_rng(B)
+    base = rng.integers(1, rows - T, size=B)
+    base[:3] = 0                                   # empty sequences
+    base[3:6] = [5, 30, 63]                        # N >= ctx
+    lens = [[int(x) + t if x else 0 for x in base] for t in range(T)]
+    print(f"[paged many sequences] B={B}", flush=True)
+    kp, vp, table, npages = to_pages(K, V, P, seed=4)
+    got = run_paged(q, kp, vp, table, npages, P, rows, lens, N, n)
+    for b in range(B):
+        ctx_b = [lens[t][b] for t in range(T)]
+        if ctx_b[0] == 0:
+            for t in range(T):
+                tau_g, cnt_g, out_g = got[t]
+                assert torch.isneginf(tau_g[b]).all() and (cnt_g[b] == 0).all()
+                assert (out_g[b].float() == 0).all()
+            continue
+        qb = q[:, b:b + 1].contiguous()
+        Kb, Vb = K[b:b + 1].contiguous(), V[b:b + 1].contiguous()
+        ref = run_contiguous(qb, Kb, Vb, ctx_b, N, n)
+        for t in range(T):
+            tau_r, cnt_r, out_r = ref[t]
+            tau_g, cnt_g, out_g = got[t]
+            assert np.array_equal(bits(tau_r[0]), bits(tau_g[b])), (b, t)
+            assert np.array_equal(cnt_r[0].cpu().numpy(), cnt_g[b].cpu().numpy()), (b, t)
+        if b % 37 == 3:                            # sampled: outputs against the oracle
+            t = T - 1
+            dm = saga.dims(1, hq, hk, hv, d, ctx_b[t], rows)
+            ws = saga.alloc_workspace(dm, 1)
+            bm = torch.empty(1, hq, (rows + 31) // 32, dtype=torch.int32, device="cuda")
+            o1 = torch.empty(1, hq, d, dtype=torch.bfloat16, device="cuda")
+            saga.saga_decode_step(dm, qb[t], Kb, Vb, got[t][0][b:b + 1].contiguous(), o1, ws,
+                                  sel_bitmap_debug=bm)
+            torch.cuda.synchronize()
+            ref_o, _ = oracle.masked(to_np_bits(qb[t]), to_np_bits(Kb), to_np_bits(Vb),
+                                     ctx_b[t], bm.cpu().numpy().view(np.uint32))
+            err = np.abs(got[t][2][b].float().cpu().numpy() - ref_o[0]).max()
+            assert err <= OUT_TOL, f"b={b}: {err:.3e}"
+
+
 def test_paged_pool_beyond_4gib():
     """A V pool over 4 GiB takes the 64-bit address path of the gather; the
     data pages sit at the top of the pools."""
