@@ -15,8 +15,9 @@ that row's key and value heads):
 The GPU logits come from a separate refresh call with its own workspace (the
 same QK routine the decode kernels run).  The same check runs at three points
 of the L x N x B sweep, and the full-attention path is checked at the 128K
-GQA twins that form the bench's speedup denominator.  Bars as in
-test_gpu_parity.py."""
+GQA twins that form the bench's speedup denominator, and at N = 8192, where
+the threshold select works on candidate lists above its staging size.  Bars
+as in test_gpu_parity.py."""
 import numpy as np
 import pytest
 import torch
@@ -95,6 +96,14 @@ def test_bench_schedule_full_size(name):
 @pytest.mark.parametrize("name", SWEEP_POINTS)
 def test_bench_schedule_sweep_points(name):
     check_schedule(workload(name), 0)
+
+
+def test_bench_schedule_large_n():
+    """The benchmark's Llama-like 128K B=16 layer at N = 8192 (bench.py
+    --top-n 8192): the refresh's candidate lists then hold more than the 8192
+    entries the register select stages, and it selects among them in place."""
+    w = wl.WORKLOADS["llama_like_128k_b16"]
+    check_schedule(w.with_(name=w.name + "_n8192", top_n=8192), 0)
 
 
 @pytest.mark.parametrize("name", ["llama_like_128k_b16", "qwen_like_128k_b16"])
