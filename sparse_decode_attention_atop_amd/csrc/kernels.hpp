@@ -141,8 +141,9 @@ __device__ __forceinline__ uint32_t plan_len(const PagedKV& pg, int b, int B, in
 // multiple of plan_quantum for which the items fit in plan_target workgroups
 // (one round of resident streams on every CU), at most plan_rows_max (the
 // list storage) and at least what keeps every sequence within plan_cap
-// chunks.  Every kernel that writes or reads the selection lists of such a
-// call computes it the same way.  len0 = plan_len(threadIdx.x): thread t
+// chunks.  The K stream computes it and stores it, with each sequence's chunk
+// count, in PagedKV::plan for the gather and threshold kernels of the same
+// call.  len0 = plan_len(threadIdx.x): thread t
 // holds sequence t, so with B <= kBlock the search reads no memory.  All
 // threads of the workgroup must call it (it synchronises); `red` is LDS for
 // 8 int64 values followed by kBlock lengths (1088 bytes, 8-byte aligned).
