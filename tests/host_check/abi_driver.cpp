@@ -22,6 +22,7 @@
 
 namespace saga {
 extern int g_launches;
+extern int g_fused_launches;
 struct TouchedRange {
     const char* name;
     uintptr_t lo, hi;
@@ -123,6 +124,48 @@ bool full_supported(const Shape& s)
         }
     }
     return nv <= 4 && maxs <= 8;
+}
+
+// Which path saga_decode_step takes: the small-batch path needs at most four
+// (b, key head) groups and a plan of at least 128 workgroups whose worst case
+// fits the LDS with the whole launch resident; otherwise the list path.
+void plan_choices()
+{
+    struct Case {
+        Shape s;
+        int64_t ctx;
+        bool fused;
+    };
+    const Case cases[] = {
+        {{"qwen_like_128k_b1", 1, 12, 1, 2, 128, 0, 131104, 1024}, 131104, true},
+        {{"qwen_like_8k_b1", 1, 12, 1, 2, 128, 0, 8207, 1024}, 8207, false},     // 65 workgroups
+        {{"qwen_like_16k_b1", 1, 12, 1, 2, 128, 0, 16399, 1024}, 16399, true},   // 129
+        {{"llama_like_8k_b1", 1, 32, 4, 8, 64, 0, 8207, 512}, 8207, true},
+        {{"llama_like_64k_b1", 1, 32, 4, 8, 64, 0, 65551, 1024}, 65551, true},
+        {{"llama_like_128k_b1", 1, 32, 4, 8, 64, 0, 131104, 2048}, 131104, false},  // LDS
+        {{"llama_like_128k_b2", 2, 32, 4, 8, 64, 0, 131104, 2048}, 131104, false},  // 8 groups
+    };
+    for (const Case& c : cases) {
+        const Shape& s = c.s;
+        const int64_t bh = (int64_t)s.B * s.hq;
+        Arena a;
+        void* q = a.get(bh * s.dk * 2);
+        void* k = a.get((size_t)s.B * s.hk * s.cache_len * s.dk * 2);
+        void* v = a.get((size_t)s.B * s.hv * s.cache_len * s.dk * 2);
+        float* tau = static_cast<float*>(a.get(bh * 4));
+        void* out = a.get(bh * s.dk * 2);
+        const saga_dims d = make_dims(s, c.ctx);
+        const size_t wsb = saga_workspace_bytes(&d, s.top_n);
+        void* ws = a.get(wsb);
+        saga::g_launches = saga::g_fused_launches = 0;
+        const int st = saga_decode_step(&d, q, k, v, tau, out, nullptr, nullptr, ws, wsb, nullptr);
+        CHECK(st == SAGA_OK, "%s: status %d", s.name, st);
+        CHECK((saga::g_fused_launches > 0) == c.fused, "%s: small-batch path %s", s.name,
+              c.fused ? "expected" : "not expected");
+        saga::g_ranges.clear();
+    }
+    saga::g_launches = saga::g_fused_launches = 0;
+    fprintf(stderr, "plan choices checked\n");
 }
 
 void valid_calls(const Shape& s)
@@ -448,6 +491,7 @@ int main(int argc, char** argv)
 {
     const bool big = argc > 1 && strcmp(argv[1], "--big") == 0;
     error_paths();
+    if (big) plan_choices();
     const Shape shapes[] = {
         {"tiny", 1, 4, 1, 2, 64, 0, 1032, 64},
         {"llama_like_8k", 1, 32, 4, 8, 64, 0, 8224, 512},

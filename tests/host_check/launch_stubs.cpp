@@ -26,6 +26,7 @@
 namespace saga {
 
 int g_launches = 0;   // launches since the driver last cleared it
+int g_fused_launches = 0;   // select_gather launches (the small-batch path), same
 
 struct TouchedRange {
     const char* name;
@@ -349,6 +350,7 @@ hipError_t launch_full(int DK, int DV, int maxs, const FullArgs& a, hipStream_t)
 hipError_t launch_select_gather(int D, int DV, const FusedArgs& a, size_t lds_bytes, hipStream_t)
 {
     ++g_launches;
+    ++g_fused_launches;
     EXPECT(D == 32 || D == 64 || D == 128);
     EXPECT(DV == 32 || DV == 64 || DV == 128);
     EXPECT(a.B >= 1 && a.hk >= 1 && a.hq == a.hk * a.Gk && a.Gk <= 16 && a.hq == a.hv * a.Gv);
