@@ -135,6 +135,7 @@ void plan_choices()
         Shape s;
         int64_t ctx;
         bool fused;
+        bool fp8k = false;   // the fp8 K call
     };
     const Case cases[] = {
         {{"qwen_like_128k_b1", 1, 12, 1, 2, 128, 0, 131104, 1024}, 131104, true},
@@ -144,21 +145,30 @@ void plan_choices()
         {{"llama_like_64k_b1", 1, 32, 4, 8, 64, 0, 65551, 1024}, 65551, true},
         {{"llama_like_128k_b1", 1, 32, 4, 8, 64, 0, 131104, 2048}, 131104, false},  // LDS
         {{"llama_like_128k_b2", 2, 32, 4, 8, 64, 0, 131104, 2048}, 131104, false},  // 8 groups
+        {{"qwen_like_40k_b1_fp8k", 1, 12, 1, 2, 128, 0, 40003, 500}, 40000, true, true},
+        {{"qwen_like_3k_b2_fp8k", 2, 12, 1, 2, 128, 0, 3005, 100}, 3000, false, true},
+        {{"dk64_dv128_40k_b1", 1, 12, 1, 2, 64, 128, 40003, 500}, 40000, true},
+        {{"sigma_like_dk32_dv64_30k", 1, 16, 2, 8, 32, 64, 30003, 300}, 30000, true},
     };
     for (const Case& c : cases) {
         const Shape& s = c.s;
+        const int dv = s.dv ? s.dv : s.dk;
         const int64_t bh = (int64_t)s.B * s.hq;
         Arena a;
         void* q = a.get(bh * s.dk * 2);
         void* k = a.get((size_t)s.B * s.hk * s.cache_len * s.dk * 2);
-        void* v = a.get((size_t)s.B * s.hv * s.cache_len * s.dk * 2);
+        void* v = a.get((size_t)s.B * s.hv * s.cache_len * dv * 2);
+        float* ks = static_cast<float*>(a.get((size_t)s.B * s.hk * 4));
         float* tau = static_cast<float*>(a.get(bh * 4));
-        void* out = a.get(bh * s.dk * 2);
+        void* out = a.get(bh * dv * 2);
         const saga_dims d = make_dims(s, c.ctx);
         const size_t wsb = saga_workspace_bytes(&d, s.top_n);
         void* ws = a.get(wsb);
         saga::g_launches = saga::g_fused_launches = 0;
-        const int st = saga_decode_step(&d, q, k, v, tau, out, nullptr, nullptr, ws, wsb, nullptr);
+        const int st =
+            c.fp8k ? saga_decode_step_fp8k(&d, q, k, ks, v, tau, out, nullptr, nullptr, ws, wsb,
+                                           nullptr)
+                   : saga_decode_step(&d, q, k, v, tau, out, nullptr, nullptr, ws, wsb, nullptr);
         CHECK(st == SAGA_OK, "%s: status %d", s.name, st);
         CHECK((saga::g_fused_launches > 0) == c.fused, "%s: small-batch path %s", s.name,
               c.fused ? "expected" : "not expected");

@@ -31,6 +31,10 @@ SHAPES = {
     "dk128_dv32": (1, 8, 2, 4, 128, 32, 1500, 3, 50, 2),
     "dk32_dv32": (1, 4, 1, 2, 32, 32, 900, 3, 20, 3),
     "dk32_dv128": (2, 8, 2, 4, 32, 128, 1200, 3, 40, 2),
+    # Long single sequences: enough workgroups for the small-batch path (the
+    # value gather inside the K-stream kernel); the shapes above take the list path.
+    "dk64_dv128_long": (1, 12, 1, 2, 64, 128, 40000, 3, 500, 2),
+    "sigma_like_dk32_dv64_long": (1, 16, 2, 8, 32, 64, 30000, 3, 300, 2),
 }
 
 _cache = {}

@@ -17,6 +17,8 @@
   fp64 oracle on the E4M3 cache, thresholds bit-exact against a host sort of
   the GPU logits, selection equal to the oracle's away from the threshold,
   outputs within the output bar of the oracle on the GPU's mask.
+* The short shapes take the list path (select lists, then a gather launch);
+  the 40K single-sequence shape takes the small-batch path.
 """
 import numpy as np
 import pytest
@@ -120,6 +122,9 @@ SHAPES = {
     "group16_d64": (3, 16, 1, 4, 64, 1500, 4, 40, 2),
     "mha_d128": (2, 8, 8, 8, 128, 700, 3, 33, 2),
     "short_ctx": (1, 4, 2, 4, 64, 17, 3, 5, 2),
+    # One sequence, one key head, 40K rows: enough workgroups for the
+    # small-batch path (the value gather inside the K-stream kernel).
+    "qwen_like_long": (1, 12, 1, 2, 128, 40000, 3, 500, 2),
 }
 
 
@@ -141,7 +146,8 @@ def test_pow2_scales_bit_identical_to_bf16_calls(name):
             assert match(k, got[k][t], ref[k][t]), f"{k} differs at step {t}"
 
 
-@pytest.mark.parametrize("name", ["qwen_like_small", "llama_like_small", "short_ctx"])
+@pytest.mark.parametrize("name", ["qwen_like_small", "llama_like_small", "short_ctx",
+                                  "qwen_like_long"])
 def test_pow2_scales_fused_refresh_step_bit_identical(name):
     q, K8, ks, V, ctx, N, n = inputs(name, 210 + len(name), pow2=True)
     got = run_fp8(q, K8, ks, V, ctx, N, n, fused=True, debug=False)
@@ -214,7 +220,7 @@ def tolerance(qbits, kval, ctx):
     return (1e-5 * torch.matmul(kf, qf[..., None])[..., 0] + 1e-6).numpy()
 
 
-GENERAL = ["qwen_like_small", "llama_like_small", "mha_d128"]
+GENERAL = ["qwen_like_small", "llama_like_small", "mha_d128", "qwen_like_long"]
 
 
 @pytest.mark.parametrize("name", GENERAL)
