@@ -405,7 +405,7 @@ constexpr int64_t kFusedMinBlocks = 128;
 struct FusedPlan {
     bool use = false;
     Chunking ch{};
-    int32_t qcap = 0, hcap = 0, unroll = 1;
+    int32_t scap = 0, unroll = 1;
     size_t lds = 0;
 };
 
@@ -418,10 +418,9 @@ FusedPlan plan_fused(const saga_dims* dims, const Layout& L, const RowModel& rm)
     const int D = dims->head_dim, DV = value_dim(dims);
     const bool k8 = rm.k_scale != nullptr;
     const int Gk = dims->h_q / dims->h_k;
-    const int64_t per_queue = (Gk + 3) / 4;         // head slots sharing one queue
-    // LDS bytes per row of a chunk: the queues (4 waves x 4 queues x 1/4 row x
-    // per_queue entries of 8 bytes) and the per-slot index lists (G_k x 2 bytes).
-    const int64_t row_bytes = 32 * per_queue + 2 * Gk;
+    // LDS bytes per row of a chunk: one 8-byte queue entry per head slot (a
+    // wave's queue of a slot holds every row of its quarter of the chunk).
+    const int64_t row_bytes = 8 * (int64_t)Gk;
     const int64_t R = kBlock / (Gk * (DV / 8));
     const size_t red = (size_t)(R * Gk * DV + R * Gk) * 4;
     auto lds_of = [&](int64_t rows) {
@@ -454,8 +453,7 @@ FusedPlan plan_fused(const saga_dims* dims, const Layout& L, const RowModel& rm)
         f.use = true;
         f.unroll = U;
         f.ch = ch;
-        f.qcap = (int32_t)(ch.rows / kWavesPerBlock * per_queue);
-        f.hcap = (int32_t)ch.rows;
+        f.scap = (int32_t)(ch.rows / kWavesPerBlock);
         f.lds = lds_of(ch.rows);
         best = f;
     }
@@ -485,8 +483,7 @@ int enqueue_fused(const saga_dims* dims, const Layout& L, const FusedPlan& f, co
     a.cache_len = dims->cache_len;
     a.rows_per_chunk = f.ch.rows;
     a.chunks = f.ch.chunks;
-    a.qcap = f.qcap;
-    a.hcap = f.hcap;
+    a.scap = f.scap;
     a.unroll = f.unroll;
     a.scale = dims->scale;
     a.lq = rm.lq;

@@ -16,17 +16,14 @@
 // (b, query head, chunk).  combine_parts_kernel merges the chunk partials.
 //
 // select_gather_kernel: grid (chunks, B * h_k), 256 threads.
-//   Stream: as select_stream_kernel, except that the four per-wave queues
-//   (queue i holds the hits of head slots 4*g + i, lane group g) hold every
-//   entry the wave can produce, so they are never flushed.
-//   Sort: each wave counts its own queue entries per head slot (ballots),
-//   then writes their LDS indices into per-slot lists at offsets from the
-//   counts of the waves before it: slot s's list holds its entries in a fixed
-//   order (waves in order, then queue order).
+//   Stream: as select_stream_kernel, except that each wave compacts its hits
+//   straight into one LDS queue per head slot, sized for every row of the
+//   wave's share of the chunk, so the queues are never flushed.  Slot s's
+//   entries are then in a fixed order: waves in order, then row order.
 //   Gather: thread t serves value-row chunk c (16 bytes), head slot h and
-//   replica r.  It takes entries r, r + R, ... of slot h's list, NB value rows
-//   in flight, and accumulates exp(s - m_h) * v with m_h the slot's largest
-//   selected logit in this chunk.  Replicas are then added in replica order,
+//   replica r.  It takes entries r, r + R, ... of slot h (the four waves'
+//   queues of slot h, concatenated), NB value rows in flight, and accumulates
+//   exp(s - m_h) * v with m_h the slot's largest selected logit in this chunk.  Replicas are then added in replica order,
 //   so every sum has a fixed order and results are bit-reproducible.
 // combine_parts_kernel: grid (B*h_q rows) x (D / 16 slices); thread t takes
 //   partials t, t + 256, ...; M = max m, then sum e^(m - M) (l, o) in a fixed
@@ -40,9 +37,8 @@ namespace {
 template <int D, int DV, int U, bool DEBUG, bool PAGED, bool FP8>
 __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_gather_kernel(FusedArgs a)
 {
-    extern __shared__ uint2 fq[];                  // [4 waves][4 queues][qcap]
+    extern __shared__ uint2 fq[];                  // [4 waves][G_k head slots][scap]
     __shared__ float hmax[kWavesPerBlock][16];
-    __shared__ int32_t qcount[kWavesPerBlock][4];
     const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15, grp = lane >> 4;
     const int chunk = blockIdx.x;
@@ -52,8 +48,11 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_gather_kernel(
     const int64_t ctx_b = PAGED ? seq_ctx(a.pg, b, a.ctx) : a.ctx;
     const int64_t r1 = wave_uniform(min(r0 + a.rows_per_chunk, ctx_b));
     const int qh0 = b * a.hq + g * Gk;
-    const int qcap = a.qcap;
-    uint2* qw = fq + (int64_t)wave * 4 * qcap;     // this wave's four queues
+    const int scap = a.scap;
+    uint2* qw = fq + (int64_t)wave * Gk * scap;    // this wave's head-slot queues
+    // This lane's group in a ballot: the hits below this lane in it are its
+    // group-mates' (rows of the same head slot).
+    const uint64_t grp_bits = 0xffffull << (16 * grp);
 
     const uint16_t* qrow = col < Gk ? a.q + (int64_t)(qh0 + col) * D : nullptr;
     const QFrag<D> qf = FP8 ? load_qfrag_k8<D>(qrow) : load_qfrag<D>(qrow);
@@ -68,14 +67,16 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_gather_kernel(
         const int64_t hc = a.lq > 1 ? head_ctx(a.pg, a.lq, b, g * Gk + slot, a.ctx) : r1;
         lim[i] = hc < r1 ? hc : r1;
     }
-    int qn[4] = {0, 0, 0, 0};
+    // Entries so far in the queue of this lane's head slot 4*grp + i (the
+    // same in the 16 lanes of a group).
+    uint32_t qn[4] = {0u, 0u, 0u, 0u};
 
     // One 16-row group at row g0: logits, mask, compaction into the queues.
     auto process_group = [&](const u32x4 (&kv)[D / 32], int64_t g0) {
         float s[4];
         qk_group<D>(qf, kv, sc, s);
         const int64_t row = g0 + col;
-        const uint32_t tag = (uint32_t)(row - r0) << 4;
+        const uint32_t tag = (uint32_t)(row - r0);
         if constexpr (DEBUG) {
             if (a.logits_out && row < r1) {
 #pragma unroll
@@ -87,11 +88,14 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_gather_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bool pred = row < lim[i] && s[i] >= tau[i];
-            const uint64_t mask = __ballot(pred);
+            // The hits of this lane's group (head slot 4*grp + i) go to that
+            // slot's queue, after its earlier entries, in row order.
+            const uint64_t mask = __ballot(pred), ours = mask & grp_bits;
+            const uint32_t at = __builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(ours >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ours, qn[i]));
             if (pred)
-                qw[i * qcap + qn[i] + lanes_below(mask)] =
-                    make_uint2(tag | (uint32_t)(4 * grp + i), __float_as_uint(s[i]));
-            qn[i] += __popcll(mask);
+                qw[(4 * grp + i) * scap + (int)at] = make_uint2(tag, __float_as_uint(s[i]));
+            qn[i] += (uint32_t)__popcll(ours);
             mx[i] = fmaxf(mx[i], pred ? s[i] : -INFINITY);
             if constexpr (DEBUG) {
                 const uint32_t mine = (uint32_t)(mask >> (16 * grp)) & 0xffffu;
@@ -197,63 +201,16 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_gather_kernel(
         }
     }
 
-    // Per-slot largest selected logit of this wave, the queue lengths, and the
-    // number of entries of each head slot in this wave's queues (slot s lives
-    // in queue s & 3; one ballot per candidate slot and 64 entries).
+    // Per-slot largest selected logit and entry count of this wave.
     __shared__ int32_t hcnt[kWavesPerBlock][16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float m = group16_max(mx[i]);
         if (col == 0) hmax[wave][4 * grp + i] = m;
     }
-    wave_sync();
-    int32_t run[4][4];                              // [queue i][lane group gs]: slot 4*gs + i
+    if (col == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int gs = 0; gs < 4; ++gs) run[i][gs] = 0;
-        for (int base = 0; base < qn[i]; base += kWave) {
-            const bool valid = base + lane < qn[i];
-            const uint32_t slot = valid ? (qw[i * qcap + base + lane].x & 15u) : 16u;
-#pragma unroll
-            for (int gs = 0; gs < 4; ++gs)
-                run[i][gs] += __popcll(__ballot(slot == (uint32_t)(4 * gs + i)));
-        }
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            qcount[wave][i] = qn[i];
-#pragma unroll
-            for (int gs = 0; gs < 4; ++gs) hcnt[wave][4 * gs + i] = run[i][gs];
-        }
-    }
-    __syncthreads();
-
-    // Per-head lists of entry indices, in a fixed order: waves in order, then
-    // queue order.  hidx[s][k] is the LDS index of slot s's k-th entry.
-    const int hcap = a.hcap;
-    uint16_t* hidx = reinterpret_cast<uint16_t*>(fq + (int64_t)16 * qcap);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int32_t pos[4];
-#pragma unroll
-        for (int gs = 0; gs < 4; ++gs) {
-            pos[gs] = 0;
-            for (int w = 0; w < wave; ++w) pos[gs] += hcnt[w][4 * gs + i];
-        }
-        for (int base = 0; base < qn[i]; base += kWave) {
-            const bool valid = base + lane < qn[i];
-            const int e = (wave * 4 + i) * qcap + base + lane;
-            const uint32_t slot = valid ? (fq[e].x & 15u) : 16u;
-#pragma unroll
-            for (int gs = 0; gs < 4; ++gs) {
-                const uint64_t m = __ballot(slot == (uint32_t)(4 * gs + i));
-                if (slot == (uint32_t)(4 * gs + i))
-                    hidx[(4 * gs + i) * hcap + pos[gs] + (int)lanes_below(m)] = (uint16_t)e;
-                pos[gs] += __popcll(m);
-            }
-        }
+        for (int i = 0; i < 4; ++i) hcnt[wave][4 * grp + i] = (int32_t)qn[i];
     }
     __syncthreads();
 
@@ -271,12 +228,24 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_gather_kernel(
     float lsum = 0.f;
     int32_t nsel = 0;
     float M = -INFINITY;
+    // Slot h's k-th entry sits in wave w's queue of slot h, w the last wave
+    // whose entries start at or below k (c1, c2, c3 for waves 1-3): LDS index
+    // k + o_w, with o_w = (w*G_k + h)*scap minus the entries of the waves
+    // before w.  Named values, not arrays: an array indexed by a compare
+    // would be kept in scratch memory.
+    static_assert(kWavesPerBlock == 4, "the wave lookup below covers four waves");
+    int32_t c1 = 0, c2 = 0, c3 = 0, o0 = 0, o1 = 0, o2 = 0, o3 = 0;
     if (active) {
-#pragma unroll
-        for (int w = 0; w < kWavesPerBlock; ++w) {
-            M = fmaxf(M, hmax[w][h]);
-            nsel += hcnt[w][h];
-        }
+        const int32_t n0 = hcnt[0][h], n1 = hcnt[1][h], n2 = hcnt[2][h], n3 = hcnt[3][h];
+        M = fmaxf(fmaxf(hmax[0][h], hmax[1][h]), fmaxf(hmax[2][h], hmax[3][h]));
+        c1 = n0;
+        c2 = c1 + n1;
+        c3 = c2 + n2;
+        nsel = c3 + n3;
+        o0 = h * scap;
+        o1 = (Gk + h) * scap - c1;
+        o2 = (2 * Gk + h) * scap - c2;
+        o3 = (3 * Gk + h) * scap - c3;
     }
     if (active && rep < nsel) {
         const int vi = g * Gk + h;                  // query head (virtual when lq > 1)
@@ -286,7 +255,6 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_gather_kernel(
         // wave.  Slots past the head's count re-read its entry `rep` with
         // weight zero, so the loads carry no branch.
         const uint16_t* vh = a.v + ((int64_t)(b * a.hv + nu) * a.cache_len) * DV + 8 * c;
-        const uint16_t* hl = hidx + h * hcap;
         for (int k0 = rep; k0 < nsel; k0 += NB * R) {
             u32x4 vv[NB];
             float wj[NB];
@@ -294,8 +262,10 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_gather_kernel(
             for (int j = 0; j < NB; ++j) {
                 const int k = k0 + j * R;
                 const bool valid = k < nsel;
-                const uint2 e = fq[hl[valid ? k : rep]];
-                const uint32_t row = (uint32_t)(r0 + (e.x >> 4));
+                const int kk = valid ? k : rep;
+                const int o = kk >= c3 ? o3 : kk >= c2 ? o2 : kk >= c1 ? o1 : o0;
+                const uint2 e = fq[kk + o];
+                const uint32_t row = (uint32_t)(r0 + e.x);
                 wj[j] = valid ? __expf(__uint_as_float(e.y) - M) : 0.f;
                 if constexpr (PAGED) {
                     // A page outside the pool reads as zero.

@@ -497,9 +497,8 @@ struct FullArgs {
 
 // Small-batch path (fused.hip): K stream, mask, compaction and value gather
 // in one kernel; one partial per (b*h_q + i, chunk).  The selected entries of
-// a chunk stay in LDS: qcap entries per (wave, queue), enough for every row
-// of the wave's share of the chunk for the ceil(G_k/4) head slots of a queue,
-// then G_k lists of hcap 16-bit entry indices, one per head slot.
+// a chunk stay in LDS: one queue per (wave, head slot) of scap 8-byte entries,
+// enough for every row of the wave's share of the chunk (rows_per_chunk / 4).
 struct FusedArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -511,8 +510,8 @@ struct FusedArgs {
     Partials part;           // [B*hq][chunks]
     int32_t B, hq, hk, hv, Gk, Gv;
     int64_t ctx, cache_len, rows_per_chunk;
-    int32_t chunks, qcap;
-    int32_t hcap;            // entries per head slot list (rows_per_chunk)
+    int32_t chunks;
+    int32_t scap;            // entries per (wave, head slot) queue
     int32_t unroll;          // 16-row groups per wave tile: 1 or 2
     float scale;
     int32_t lq;

@@ -143,7 +143,7 @@ void plan_choices()
         {{"qwen_like_16k_b1", 1, 12, 1, 2, 128, 0, 16399, 1024}, 16399, true},   // 129
         {{"llama_like_8k_b1", 1, 32, 4, 8, 64, 0, 8207, 512}, 8207, true},
         {{"llama_like_64k_b1", 1, 32, 4, 8, 64, 0, 65551, 1024}, 65551, true},
-        {{"llama_like_128k_b1", 1, 32, 4, 8, 64, 0, 131104, 2048}, 131104, false},  // LDS
+        {{"llama_like_128k_b1", 1, 32, 4, 8, 64, 0, 131104, 2048}, 131104, true},
         {{"llama_like_128k_b2", 2, 32, 4, 8, 64, 0, 131104, 2048}, 131104, false},  // 8 groups
         {{"qwen_like_40k_b1_fp8k", 1, 12, 1, 2, 128, 0, 40003, 500}, 40000, true, true},
         {{"qwen_like_3k_b2_fp8k", 2, 12, 1, 2, 128, 0, 3005, 100}, 3000, false, true},

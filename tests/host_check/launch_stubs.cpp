@@ -359,12 +359,10 @@ hipError_t launch_select_gather(int D, int DV, const FusedArgs& a, size_t lds_by
     EXPECT((int64_t)(a.chunks - 1) * a.rows_per_chunk < a.ctx);
     EXPECT(a.unroll == 1 || a.unroll == 2);
     EXPECT(a.rows_per_chunk % (2 * fused_block_rows(a.unroll, a.k_scale != nullptr)) == 0);
-    // Every row of a wave's share, for every head slot of a queue, fits.
-    EXPECT((int64_t)a.qcap >= a.rows_per_chunk / kWavesPerBlock * ((a.Gk + 3) / 4));
-    EXPECT(a.hcap >= a.rows_per_chunk);                         // a slot's list holds every row
+    // Every row of a wave's share fits its queue of each head slot.
+    EXPECT((int64_t)a.scap * kWavesPerBlock >= a.rows_per_chunk);
     EXPECT((int64_t)a.B * a.hk * a.chunks >= 128);              // the plan's smallest fused launch
-    EXPECT((int64_t)16 * a.qcap <= 65536);                      // 16-bit entry indices
-    EXPECT(lds_bytes >= (size_t)16 * a.qcap * 8 + (size_t)a.Gk * a.hcap * 2);
+    EXPECT(lds_bytes >= (size_t)kWavesPerBlock * a.Gk * a.scap * 8);
     EXPECT(lds_bytes <= (size_t)kLdsPerGroup);
     const int64_t per_cu = ((int64_t)a.B * a.hk * a.chunks + kComputeUnits - 1) / kComputeUnits;
     EXPECT((int64_t)lds_bytes * per_cu <= kLdsPerCu);           // every workgroup resident
