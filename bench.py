@@ -854,7 +854,7 @@ def main():
         "hbm_gbs_step": round(step_bytes / (sec / args.steps) / 1e9, 1),
         "hbm_frac_step": round(step_bytes / (sec / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm",
-                     "kernel": "saga_decode_step (select_stream + gather + combine)",
+                     "kernel": "saga_decode_step (one plain call: K stream, selection, value gather, combine)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_ms": round(avg_ms, 5),

@@ -400,7 +400,7 @@ int enqueue_gather_combine(const saga_dims* dims, const Layout& L, const Chunkin
 // workgroups (short contexts) keep the list path: there a chunk's selected
 // value rows are many for one workgroup to read, and the list path's gather
 // spreads them over many.
-constexpr int64_t kFusedMinBlocks = 128;
+constexpr int64_t kFusedMinBlocks = 64;
 
 struct FusedPlan {
     bool use = false;

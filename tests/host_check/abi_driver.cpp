@@ -127,7 +127,7 @@ bool full_supported(const Shape& s)
 }
 
 // Which path saga_decode_step takes: the small-batch path needs at most four
-// (b, key head) groups and a plan of at least 128 workgroups whose worst case
+// (b, key head) groups and a plan of at least 64 workgroups whose worst case
 // fits the LDS with the whole launch resident; otherwise the list path.
 void plan_choices()
 {
@@ -139,7 +139,8 @@ void plan_choices()
     };
     const Case cases[] = {
         {{"qwen_like_128k_b1", 1, 12, 1, 2, 128, 0, 131104, 1024}, 131104, true},
-        {{"qwen_like_8k_b1", 1, 12, 1, 2, 128, 0, 8207, 1024}, 8207, false},     // 65 workgroups
+        {{"qwen_like_4k_b1", 1, 12, 1, 2, 128, 0, 4111, 1024}, 4111, false},     // 33 workgroups
+        {{"qwen_like_8k_b1", 1, 12, 1, 2, 128, 0, 8207, 1024}, 8207, true},      // 65
         {{"qwen_like_16k_b1", 1, 12, 1, 2, 128, 0, 16399, 1024}, 16399, true},   // 129
         {{"llama_like_8k_b1", 1, 32, 4, 8, 64, 0, 8207, 512}, 8207, true},
         {{"llama_like_64k_b1", 1, 32, 4, 8, 64, 0, 65551, 1024}, 65551, true},

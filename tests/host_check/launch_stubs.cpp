@@ -361,7 +361,7 @@ hipError_t launch_select_gather(int D, int DV, const FusedArgs& a, size_t lds_by
     EXPECT(a.rows_per_chunk % (2 * fused_block_rows(a.unroll, a.k_scale != nullptr)) == 0);
     // Every row of a wave's share fits its queue of each head slot.
     EXPECT((int64_t)a.scap * kWavesPerBlock >= a.rows_per_chunk);
-    EXPECT((int64_t)a.B * a.hk * a.chunks >= 128);              // the plan's smallest fused launch
+    EXPECT((int64_t)a.B * a.hk * a.chunks >= 64);               // the plan's smallest fused launch
     EXPECT(lds_bytes >= (size_t)kWavesPerBlock * a.Gk * a.scap * 8);
     EXPECT(lds_bytes <= (size_t)kLdsPerGroup);
     const int64_t per_cu = ((int64_t)a.B * a.hk * a.chunks + kComputeUnits - 1) / kComputeUnits;

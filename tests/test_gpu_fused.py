@@ -27,7 +27,7 @@ OUT_TOL = 1e-2
 
 SHAPES = {
     # name: (B, hq, hk, hv, d, ctx) -- at most 4 (b, key head) groups, at least
-    # 128 fused workgroups.  Plans (16-row groups per wave tile, chunks x rows):
+    # 64 fused workgroups.  Plans (16-row groups per wave tile, chunks x rows):
     "qwen_like_long": (1, 12, 1, 2, 128, 40000),      # 1, 313 x 128
     "llama_like": (1, 32, 4, 8, 64, 30000),           # 2, 118 x 256
     "group16_two_rows": (2, 16, 1, 4, 64, 20000),     # 1, 157 x 128

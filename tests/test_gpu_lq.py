@@ -26,7 +26,7 @@ LQ_SHAPES = {
     "group4_lq4_d128": (2, 8, 2, 4, 128, 2000, 3, 100, 2, 4),
     "mha_lq16": (1, 4, 4, 4, 64, 900, 3, 40, 3, 16),
     "short_context_lq4": (1, 8, 2, 4, 64, 60, 3, 64, 2, 4),        # N >= ctx for every token
-    "small_batch_path_lq4": (1, 8, 2, 4, 128, 40000, 3, 500, 2, 4),  # >= 128 fused workgroups
+    "small_batch_path_lq4": (1, 8, 2, 4, 128, 40000, 3, 500, 2, 4),  # >= 64 fused workgroups
 }
 
 

@@ -103,7 +103,7 @@ PAGED_SHAPES = {
     "qwen_like_d128": (2, 12, 1, 2, 128, 256, 14, 128, 2),
     "llama_like_d64": (2, 32, 4, 8, 64, 512, 8, 256, 2),
     "group16_big_pages": (1, 16, 1, 4, 64, 1024, 5, 100, 3),
-    # long enough for the small-batch path (at least 128 fused workgroups)
+    # long enough for the small-batch path (at least 64 fused workgroups)
     "qwen_like_small_batch_path": (1, 12, 1, 2, 128, 256, 160, 512, 2),
     "group16_small_batch_path": (2, 16, 1, 4, 64, 1024, 40, 200, 3),
 }
