@@ -33,6 +33,7 @@ SHAPES = {
     "group16_two_rows": (2, 16, 1, 4, 64, 20000),     # 1, 157 x 128
     "group4": (1, 4, 1, 2, 128, 40000),               # 1, 313 x 128
     "llama_like_64k": (1, 32, 4, 8, 64, 65551),       # 2, 129 x 512
+    "llama_like_128k": (1, 32, 4, 8, 64, 131104),     # 2, 171 x 768 (48 KB of queues)
 }
 
 
@@ -64,7 +65,8 @@ def test_every_row_selected_is_full_attention(name):
     assert err <= OUT_TOL, f"{name}: {err:.3e}"
 
 
-@pytest.mark.parametrize("name", ["qwen_like_long", "llama_like", "llama_like_64k"])
+@pytest.mark.parametrize("name", ["qwen_like_long", "llama_like", "llama_like_64k",
+                                  "llama_like_128k"])
 def test_all_logits_tied_keeps_every_row(name):
     B, hq, hk, hv, d, ctx = SHAPES[name]
     q, K, V = make_inputs(B, hq, hk, hv, d, ctx + 3, 1, seed=210 + len(name))
