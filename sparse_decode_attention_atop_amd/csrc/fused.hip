@@ -23,8 +23,9 @@
 //   Gather: thread t serves value-row chunk c (16 bytes), head slot h and
 //   replica r.  It takes entries r, r + R, ... of slot h (the four waves'
 //   queues of slot h, concatenated), NB value rows in flight, and accumulates
-//   exp(s - m_h) * v with m_h the slot's largest selected logit in this chunk.  Replicas are then added in replica order,
-//   so every sum has a fixed order and results are bit-reproducible.
+//   exp(s - m_h) * v with m_h the slot's largest selected logit in this
+//   chunk.  Replicas are then added in replica order, so every sum has a
+//   fixed order and results are bit-reproducible.
 // combine_parts_kernel: grid (B*h_q rows) x (D / 16 slices); thread t takes
 //   partials t, t + 256, ...; M = max m, then sum e^(m - M) (l, o) in a fixed
 //   reduction tree; out = o / l in bf16 (zero when nothing was selected).
