@@ -496,8 +496,27 @@ int enqueue_fused(const saga_dims* dims, const Layout& L, const FusedPlan& f, co
                                            sel_counts_dev, s));
 }
 
+// Large-batch calls gather in the K stream's tail (decode.hip, tail_gather):
+// contiguous bf16 V with d_v = d_k of 64 (at most 8 query heads per key head)
+// or 128, value heads of one key group addressable with 32-bit offsets, and
+// a launch of at least kTailMinBlocks workgroups (fewer, longer chunks would
+// leave each workgroup many value rows to read on its own, where the list
+// path's gather spreads them).
+constexpr int64_t kTailMinBlocks = 256;
+
+bool use_tail(const saga_dims* dims, const RowModel& rm, const Chunking& ch)
+{
+    if (!SAGA_TAIL_GATHER || rm.pg.block_table || rm.v_scale) return false;
+    const int D = dims->head_dim, Gk = dims->h_q / dims->h_k, Gv = dims->h_q / dims->h_v;
+    if (value_dim(dims) != D || (D != 64 && D != 128) || Gk > (D == 64 ? 8 : 16)) return false;
+    if ((int64_t)dims->batch * dims->h_k * ch.chunks < kTailMinBlocks) return false;
+    // Value heads one key group reads: ceil over its query heads' map.
+    const int64_t nvh = (Gk + Gv - 1) / Gv + 1;
+    return nvh * dims->cache_len * D * 2 < ((int64_t)1 << 31);
+}
+
 // Decode with kept thresholds: stream-select into the lists, then gather
-// (or the small-batch path above).
+// (or the small-batch path above, or the tail gather).
 int enqueue_decode(const saga_dims* dims, const Layout& L, const void* q_dev,
                    const void* k_cache_dev, const void* v_cache_dev, const float* thresholds_dev,
                    void* out_dev, int32_t* sel_counts_dev, uint32_t* sel_bitmap_debug_dev,
@@ -521,6 +540,16 @@ int enqueue_decode(const saga_dims* dims, const Layout& L, const void* q_dev,
         stream_args(dims, L, ch, q_dev, k_cache_dev, thresholds_dev, workspace_dev, lrm);
     a.bitmap = sel_bitmap_debug_dev;
     a.bitmap_words = words;
+    if (use_tail(dims, lrm, ch)) {
+        a.v = static_cast<const uint16_t*>(v_cache_dev);
+        a.part = partials(workspace_dev, L);
+        a.hv = dims->h_v;
+        a.Gv = dims->h_q / dims->h_v;
+        st = hip_status(launch_select_stream(D, a, s));
+        if (st != SAGA_OK) return st;
+        return hip_status(launch_combine(D, a.part, rows, ch.chunks,
+                                         static_cast<uint16_t*>(out_dev), sel_counts_dev, s));
+    }
     st = hip_status(launch_select_stream(D, a, s));
     if (st != SAGA_OK) return st;
     return enqueue_gather_combine(dims, L, ch, v_cache_dev, nullptr, out_dev, sel_counts_dev,

@@ -32,6 +32,205 @@ namespace saga {
 
 namespace {
 
+// Value gather in the K stream's tail (large batches; contiguous bf16 V with
+// d_v = d_k).  The workgroup has just written its chunk's selected entries
+// to its lists (one per head slot and wave) and knows each wave's counts and
+// largest logits, so it gathers their value rows itself: no gather launch,
+// no list-length prologue, and workgroups whose stream ends early gather
+// while the others still stream.
+//   Order: the chunk's entries are taken in one flat order, head slot first,
+//   then wave, then list position, and staged in LDS (byte offset of the
+//   value row in the group's value heads with the head slot in its low four
+//   bits, weight exp(s - M_h), M_h the slot's largest selected logit in this
+//   chunk), at most CAPL per round.  Wave w takes the w-th quarter of each
+//   round in order, C lanes per value row, NB rows in flight per lane, and
+//   keeps one running sum for the head slot it is in; where the slot changes
+//   it sums its lanes' rows (fixed butterfly) and adds them to its own
+//   (wave, slot) partial in LDS.  So a head slot that selected many rows is
+//   spread over all four waves, every sum has a fixed order, and results are
+//   bit-reproducible.  The four waves' partials are added in wave order into
+//   one partial per (b, query head, chunk), merged by combine_kernel.
+// GKT: most head slots a key group may have (8 at d = 64, 16 at d = 128).
+template <int D, int GKT>
+__device__ __forceinline__ void tail_gather(const SelectStreamArgs& a, unsigned char* qlds,
+                                            const int (&written)[16],
+                                            const float (&mx)[4], int b, int g, int chunk,
+                                            int64_t r0, int qh0, int64_t capw, int64_t nl,
+                                            int wave, int lane)
+{
+    constexpr int C = D / 8;                  // 16-byte pieces of a value row
+    constexpr int SLW = kWave / C;            // value rows per wave load instruction
+    constexpr int NB = SAGA_TAIL_NB;          // value rows in flight per lane
+    constexpr int CAPL = 2048;                // entries staged per round
+    constexpr int EPT = CAPL / kBlock;
+    constexpr uint32_t kNoRow = 0x80000000u;  // past the value heads (< 2^31 bytes, host-checked)
+    constexpr size_t kPartFloats = (size_t)kWavesPerBlock * GKT * D;
+    constexpr size_t kPartBytes = kPartFloats * 4;
+    constexpr size_t kQueueBytes = sizeof(uint2) * kWavesPerBlock * 4 * kQueueCap;
+    static_assert(kPartBytes <= kQueueBytes, "the (wave, slot) partials live in the queues' LDS");
+    __shared__ int32_t tcnt[kWavesPerBlock][16];
+    __shared__ float tmx[kWavesPerBlock][16];
+    __shared__ int32_t tpre[4 * 16 + 1];      // flat start of list (head slot, wave)
+    __shared__ float tM[16];
+    __shared__ float wl[kWavesPerBlock * GKT];   // (wave, slot) weight sums
+    // The stream's queues (no longer used) hold the (wave, slot) partials and,
+    // when they fit, the staged entries too.
+    constexpr bool kStageInQueue = kPartBytes + CAPL * 8 <= kQueueBytes;
+    __shared__ uint2 extra[kStageInQueue ? 1 : CAPL];
+    float* wpart = reinterpret_cast<float*>(qlds);          // [wave][GKT][D]
+    uint2* stage = kStageInQueue ? reinterpret_cast<uint2*>(qlds + kPartBytes) : extra;
+    const int Gk = a.Gk;
+    const int col = lane & 15, grp = lane >> 4;
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float m = group16_max(mx[i]);
+        if (col == 0) tmx[wave][4 * grp + i] = m;
+    }
+    if (lane < 16) {
+        int32_t c = 0;
+#pragma unroll
+        for (int h = 0; h < 16; ++h) c = lane == h ? written[h] : c;
+        tcnt[wave][lane] = c;
+    }
+    __syncthreads();                           // every wave's queue flushed
+    for (int i = threadIdx.x; i < (int)kPartFloats; i += kBlock) wpart[i] = 0.f;
+    if (threadIdx.x < kWavesPerBlock * GKT) wl[threadIdx.x] = 0.f;
+    if (wave == 0) {
+        const int h = lane >> 2, w = lane & 3;
+        const int32_t n = h < Gk ? tcnt[w][h] : 0;
+        int32_t incl = n;
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int32_t u = __shfl_up(incl, off);
+            if (lane >= off) incl += u;
+        }
+        tpre[lane] = incl - n;
+        if (lane == kWave - 1) tpre[64] = incl;
+        if (lane < 16)
+            tM[lane] = fmaxf(fmaxf(tmx[0][lane], tmx[1][lane]), fmaxf(tmx[2][lane], tmx[3][lane]));
+    }
+    __syncthreads();
+    const int32_t total = tpre[64];
+
+    // Value heads of this key group's query heads (virtual heads when lq > 1).
+    const int vi0 = g * Gk;
+    const int nu0 = vi0 / a.Gv;
+    const int nvh = (vi0 + Gk - 1) / a.Gv - nu0 + 1;
+    const __amdgpu_buffer_rsrc_t vrs =
+        make_rsrc(a.v + ((int64_t)(b * a.hv + nu0) * a.cache_len) * D,
+                  (uint32_t)((int64_t)nvh * a.cache_len * D * 2));
+    const int t = threadIdx.x, c = lane % C, sl = lane / C;
+    float cur[8], ls = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cur[j] = 0.f;
+    int hc = -1;                               // the wave's current head slot
+    auto flush = [&](int h) {
+#pragma unroll
+        for (int off = C; off < kWave; off <<= 1) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) cur[j] += __shfl_xor(cur[j], off);
+            ls += __shfl_xor(ls, off);
+        }
+        if (sl == 0) {
+            float* dst = wpart + (wave * GKT + h) * D + 8 * c;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dst[j] += cur[j];
+            if (c == 0) wl[wave * GKT + h] += ls;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cur[j] = 0.f;
+        ls = 0.f;
+    };
+
+    for (int32_t base = 0; base < total; base += CAPL) {
+        const int n = min(CAPL, total - base);
+        // Stage entries t, t + 256, ...: list by binary search over the flat
+        // starts, all loads in flight before any is used.
+        uint2 ent[EPT];
+        int lst[EPT];
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const int32_t f = base + min(t + k * kBlock, n - 1);
+            int l = 0;
+#pragma unroll
+            for (int st = 32; st > 0; st >>= 1) l = tpre[l + st] <= f ? l + st : l;
+            lst[k] = l;
+            ent[k] = a.entries[list_index(qh0 + (l >> 2), (int64_t)chunk * kWavesPerBlock + (l & 3),
+                                          (uint32_t)(f - tpre[l]), capw, nl, a.head_stride,
+                                          a.overflow_at)];
+        }
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const int e = t + k * kBlock;
+            if (e < n) {
+                const int h = lst[k] >> 2;
+                const uint32_t nrel = (uint32_t)((vi0 + h) / a.Gv - nu0);
+                const uint32_t row = (uint32_t)(r0 + ent[k].x);
+                const uint32_t off = (nrel * (uint32_t)a.cache_len + row) * (uint32_t)(D * 2);
+                stage[e] = make_uint2(off | (uint32_t)h,
+                                      __float_as_uint(__expf(__uint_as_float(ent[k].y) - tM[h])));
+            }
+        }
+        __syncthreads();
+        const int e_lo = wave * n / kWavesPerBlock, e_hi = (wave + 1) * n / kWavesPerBlock;
+        for (int e0 = e_lo; e0 < e_hi; e0 += SLW * NB) {
+            const int e_last = min(e0 + SLW * NB, e_hi) - 1;
+            const int h_first = __builtin_amdgcn_readfirstlane((int)(stage[e0].x & 15u));
+            const int h_last = __builtin_amdgcn_readfirstlane((int)(stage[e_last].x & 15u));
+            u32x4 vv[NB];
+            float w[NB];
+            int hh[NB];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const int e = e0 + k * SLW + sl;
+                const bool in = e <= e_last;
+                const uint2 st = stage[in ? e : e_last];
+                hh[k] = (int)(st.x & 15u);
+                w[k] = in ? __uint_as_float(st.y) : 0.f;
+                vv[k] = buf_ld16(vrs, (in ? (st.x & ~15u) : kNoRow) + 16u * c);
+            }
+            for (int h = h_first; h <= h_last; ++h) {
+                if (h != hc) {
+                    if (hc >= 0) flush(hc);
+                    hc = h;
+                }
+#pragma unroll
+                for (int k = 0; k < NB; ++k) {
+                    const bool m = hh[k] == h;
+                    ls += m ? w[k] : 0.f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        cur[2 * q] = m ? fmaf(w[k], bf16lo(vv[k][q]), cur[2 * q]) : cur[2 * q];
+                        cur[2 * q + 1] = m ? fmaf(w[k], bf16hi(vv[k][q]), cur[2 * q + 1]) : cur[2 * q + 1];
+                    }
+                }
+            }
+        }
+        __syncthreads();                       // the stage is rewritten by the next round
+    }
+    if (hc >= 0) flush(hc);
+    __syncthreads();
+
+    const int64_t prow0 = (int64_t)qh0 * a.chunks + chunk;   // partial of head slot 0
+    for (int idx = t; idx < Gk * D; idx += kBlock) {
+        const int h = idx / D, p = idx - h * D;
+        float o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w) o += wpart[(w * GKT + h) * D + p];
+        a.part.o[(prow0 + (int64_t)h * a.chunks) * D + p] = o;
+    }
+    if (t < Gk) {
+        float l = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w) l += wl[w * GKT + t];
+        const int32_t nh = tpre[4 * t + 4] - tpre[4 * t];
+        const int64_t pi = prow0 + (int64_t)t * a.chunks;
+        a.part.m[pi] = nh > 0 ? tM[t] : -INFINITY;
+        a.part.l[pi] = l;
+        a.part.c[pi] = nh;
+    }
+}
+
 // Stream-select kernel.  Hits are compacted with one ballot per (16-row
 // group u, head index i): the four lane groups' hits for head slots 4*g + i
 // go to one wave-private LDS queue per i in ballot order, so the queue length
@@ -39,7 +238,7 @@ namespace {
 // queue could overflow, it is split by head slot and appended to the global
 // per-(head, chunk, wave) lists in order.  DEBUG adds the optional logits and
 // selection-bitmap outputs.
-template <int D, int U, bool DEBUG, bool PAGED, bool FP8>
+template <int D, int U, bool DEBUG, bool PAGED, bool FP8, int GKT>
 __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(SelectStreamArgs a)
 {
     __shared__ uint2 queue[kWavesPerBlock][4][kQueueCap];
@@ -313,6 +512,14 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
     }
     }
     flush_all();
+    if constexpr (GKT > 0) {
+        static_assert(!PAGED, "the tail gather reads contiguous value caches");
+        static_assert(sizeof(queue) == sizeof(uint2) * kWavesPerBlock * 4 * kQueueCap,
+                      "tail_gather reuses the queues' LDS");
+        tail_gather<D, GKT>(a, reinterpret_cast<unsigned char*>(&queue[0][0][0]), written, mx, b,
+                            g, chunk, r0, qh0, capw, nl, wave, lane);
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float m = group16_max(mx[i]);
@@ -682,7 +889,25 @@ hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t s)
     const int kind = a.pg.block_table != nullptr ? 1 : (a.k_scale != nullptr ? 2 : 0);
 #define SAGA_LAUNCH_STREAM(DD, DBG, PG, F8)                                                      \
     hipLaunchKernelGGL((select_stream_kernel<DD, F8 ? decode_unroll_k8(DD) : decode_unroll(DD),  \
-                                             DBG, PG, F8>), grid, dim3(kBlock), 0, s, a)
+                                             DBG, PG, F8, 0>), grid, dim3(kBlock), 0, s, a)
+#define SAGA_LAUNCH_TAIL(DD, DBG, F8)                                                            \
+    hipLaunchKernelGGL((select_stream_kernel<DD, F8 ? decode_unroll_k8(DD) : decode_unroll(DD),  \
+                                             DBG, false, F8, DD == 64 ? 8 : 16>),                 \
+                       grid, dim3(kBlock), 0, s, a)
+    if (a.v) {
+        // The tail gather: contiguous caches, d = 64 (at most 8 head slots) or 128.
+        if (a.pg.block_table || (D != 64 && D != 128) || a.Gk > (D == 64 ? 8 : 16))
+            return hipErrorInvalidValue;
+        if (D == 64) {
+            if (kind == 2) { if (dbg) SAGA_LAUNCH_TAIL(64, true, true); else SAGA_LAUNCH_TAIL(64, false, true); }
+            else { if (dbg) SAGA_LAUNCH_TAIL(64, true, false); else SAGA_LAUNCH_TAIL(64, false, false); }
+        } else {
+            if (kind == 2) { if (dbg) SAGA_LAUNCH_TAIL(128, true, true); else SAGA_LAUNCH_TAIL(128, false, true); }
+            else { if (dbg) SAGA_LAUNCH_TAIL(128, true, false); else SAGA_LAUNCH_TAIL(128, false, false); }
+        }
+#undef SAGA_LAUNCH_TAIL
+        return hipGetLastError();
+    }
 #define SAGA_LAUNCH_STREAM_BF(DD)                                                                \
     if (kind == 1) { if (dbg) SAGA_LAUNCH_STREAM(DD, true, true, false); else SAGA_LAUNCH_STREAM(DD, false, true, false); } \
     else { if (dbg) SAGA_LAUNCH_STREAM(DD, true, false, false); else SAGA_LAUNCH_STREAM(DD, false, false, false); }

@@ -41,6 +41,12 @@
 #ifndef SAGA_GATHER_NB
 #define SAGA_GATHER_NB 4             // value rows in flight per lane in the gather
 #endif
+#ifndef SAGA_TAIL_GATHER
+#define SAGA_TAIL_GATHER 1           // large-batch decode calls gather in the K stream's tail
+#endif
+#ifndef SAGA_TAIL_NB
+#define SAGA_TAIL_NB 8               // value rows in flight per lane in that tail gather
+#endif
 #ifndef SAGA_GATHER_WAVES
 #define SAGA_GATHER_WAVES 0          // >0: ask for that many waves per SIMD (gather)
 #endif

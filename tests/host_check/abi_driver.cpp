@@ -23,6 +23,7 @@
 namespace saga {
 extern int g_launches;
 extern int g_fused_launches;
+extern int g_tail_launches;
 struct TouchedRange {
     const char* name;
     uintptr_t lo, hi;
@@ -128,7 +129,10 @@ bool full_supported(const Shape& s)
 
 // Which path saga_decode_step takes: the small-batch path needs at most four
 // (b, key head) groups and a plan of at least 64 workgroups whose worst case
-// fits the LDS with the whole launch resident; otherwise the list path.
+// fits the LDS with the whole launch resident.  Otherwise the K stream gathers
+// in its tail when V is contiguous bf16 with d_v = d_k of 64 (at most 8 query
+// heads per key head) or 128 and the launch has at least 256 workgroups; else
+// the list path (stream, gather, combine).
 void plan_choices()
 {
     struct Case {
@@ -136,6 +140,7 @@ void plan_choices()
         int64_t ctx;
         bool fused;
         bool fp8k = false;   // the fp8 K call
+        bool tail = false;   // the K stream gathers in its tail
     };
     const Case cases[] = {
         {{"qwen_like_128k_b1", 1, 12, 1, 2, 128, 0, 131104, 1024}, 131104, true},
@@ -147,11 +152,26 @@ void plan_choices()
         {{"llama_like_8k_b1", 1, 32, 4, 8, 64, 0, 8207, 512}, 8207, true},
         {{"llama_like_64k_b1", 1, 32, 4, 8, 64, 0, 65551, 1024}, 65551, true},
         {{"llama_like_128k_b1", 1, 32, 4, 8, 64, 0, 131104, 2048}, 131104, true},
-        {{"llama_like_128k_b2", 2, 32, 4, 8, 64, 0, 131104, 2048}, 131104, false},  // 8 groups
+        {{"llama_like_128k_b2", 2, 32, 4, 8, 64, 0, 131104, 2048}, 131104, false, false, true},  // 8 groups
         {{"qwen_like_40k_b1_fp8k", 1, 12, 1, 2, 128, 0, 40003, 500}, 40000, true, true},
         {{"qwen_like_3k_b2_fp8k", 2, 12, 1, 2, 128, 0, 3005, 100}, 3000, false, true},
         {{"dk64_dv128_40k_b1", 1, 12, 1, 2, 64, 128, 40003, 500}, 40000, true},
         {{"sigma_like_dk32_dv64_30k", 1, 16, 2, 8, 32, 64, 30003, 300}, 30000, true},
+        // Large batches: the tail gather, or the list path where it does not apply.
+        {{"llama_like_128k_b16", 16, 32, 4, 8, 64, 0, 131104, 2048}, 131104, false, false, true},
+        {{"qwen_like_128k_b16", 16, 12, 1, 2, 128, 0, 131104, 1024}, 131104, false, false, true},
+        {{"llama_like_128k_b16_fp8k", 16, 32, 4, 8, 64, 0, 131104, 2048}, 131104, false, true, true},
+        {{"tail_llama_like_2k_b4", 4, 32, 4, 8, 64, 0, 2103, 100}, 2100, false, false, true},    // 272
+        {{"tail_qwen_like_4k_b16", 16, 12, 1, 2, 128, 0, 4103, 200}, 4100, false, false, true},
+        {{"tail_group16_d128_b8", 8, 16, 1, 4, 128, 0, 4003, 300}, 4000, false, false, true},
+        {{"tail_fewer_value_heads_b8", 8, 8, 4, 2, 64, 0, 1103, 50}, 1100, false, false, true},
+        {{"tail_mha_d64_b4", 4, 8, 8, 8, 64, 0, 1103, 40}, 1100, false, false, true},
+        {{"tail_fp8k_llama_like_b4", 4, 32, 4, 8, 64, 0, 2503, 64}, 2500, false, true, true},
+        {{"gqa_llama_small_b2", 2, 32, 8, 8, 64, 0, 2052, 64}, 2049, false, false, true},   // 272
+        {{"llama_like_1k_b4", 4, 32, 4, 8, 64, 0, 1024, 64}, 1000, false, false, false},    // 128
+        {{"group16_d64_b16", 16, 16, 1, 4, 64, 0, 8200, 300}, 8192, false, false, false},   // G_k 16
+        {{"dk64_dv128_b16", 16, 12, 1, 2, 64, 128, 8200, 300}, 8192, false, false, false},  // d_v != d_k
+        {{"mha_d32_b16", 16, 8, 8, 8, 32, 0, 8200, 300}, 8192, false, false, false},        // d = 32
     };
     for (const Case& c : cases) {
         const Shape& s = c.s;
@@ -167,7 +187,7 @@ void plan_choices()
         const saga_dims d = make_dims(s, c.ctx);
         const size_t wsb = saga_workspace_bytes(&d, s.top_n);
         void* ws = a.get(wsb);
-        saga::g_launches = saga::g_fused_launches = 0;
+        saga::g_launches = saga::g_fused_launches = saga::g_tail_launches = 0;
         const int st =
             c.fp8k ? saga_decode_step_fp8k(&d, q, k, ks, v, tau, out, nullptr, nullptr, ws, wsb,
                                            nullptr)
@@ -175,9 +195,11 @@ void plan_choices()
         CHECK(st == SAGA_OK, "%s: status %d", s.name, st);
         CHECK((saga::g_fused_launches > 0) == c.fused, "%s: small-batch path %s", s.name,
               c.fused ? "expected" : "not expected");
+        CHECK((saga::g_tail_launches > 0) == c.tail, "%s: tail gather %s", s.name,
+              c.tail ? "expected" : "not expected");
         saga::g_ranges.clear();
     }
-    saga::g_launches = saga::g_fused_launches = 0;
+    saga::g_launches = saga::g_fused_launches = saga::g_tail_launches = 0;
     fprintf(stderr, "plan choices checked\n");
 }
 

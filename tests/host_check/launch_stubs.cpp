@@ -27,6 +27,7 @@ namespace saga {
 
 int g_launches = 0;   // launches since the driver last cleared it
 int g_fused_launches = 0;   // select_gather launches (the small-batch path), same
+int g_tail_launches = 0;    // K-stream launches that gather in their tail, same
 
 struct TouchedRange {
     const char* name;
@@ -235,8 +236,22 @@ hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t)
     const ListUse u = list_use(a.B, a.hq, a.hk, a.ctx, a.chunks, a.rows_per_chunk, a.pg,
                                a.head_stride, a.overflow_at);
     const int64_t lists = (int64_t)a.B * a.hq * a.chunks * kWavesPerBlock;
-    wr_span("list counts", a.list_count, lists);
-    wr_span("list maxima", a.list_max, lists);
+    if (a.v) {
+        // The tail gather: contiguous bf16 V with d_v = d_k, at most 8 (d = 64)
+        // or 16 (d = 128) head slots, one partial per (b*h_q + i, chunk), the
+        // key group's value heads under 2^31 bytes (32-bit buffer offsets).
+        ++g_tail_launches;
+        EXPECT(!a.pg.block_table && (D == 64 || D == 128) && a.Gk <= (D == 64 ? 8 : 16));
+        EXPECT(a.hv >= 1 && a.Gv >= 1 && a.hq == a.hv * a.Gv);
+        EXPECT(a.chunks >= 1 && (int64_t)a.chunks * a.rows_per_chunk >= a.ctx);
+        const int64_t nvh = (int64_t)(a.Gk + a.Gv - 1) / a.Gv + 1;
+        EXPECT(nvh * a.cache_len * D * 2 < ((int64_t)1 << 31));
+        touch_partials(a.part, (int64_t)a.B * a.hq * a.chunks, D);
+        touch_cache(a.v, a.B, a.hv, a.cache_len, a.ctx, D, 2);
+    } else {
+        wr_span("list counts", a.list_count, lists);
+        wr_span("list maxima", a.list_max, lists);
+    }
     touch_lists(a.entries, u);
     if (a.pg.block_table && a.pg.plan_cap) wr_span("paged plan", a.pg.plan, (int64_t)a.B + 1);
     rd_span(a.q, (int64_t)a.B * a.hq * D);

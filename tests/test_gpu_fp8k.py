@@ -122,6 +122,8 @@ SHAPES = {
     "group16_d64": (3, 16, 1, 4, 64, 1500, 4, 40, 2),
     "mha_d128": (2, 8, 8, 8, 128, 700, 3, 33, 2),
     "short_ctx": (1, 4, 2, 4, 64, 17, 3, 5, 2),
+    # 320 workgroups: the K stream gathers the (bf16) value rows in its tail
+    "tail_llama_like": (4, 32, 4, 8, 64, 2500, 3, 64, 2),
     # One sequence, one key head, 40K rows: enough workgroups for the
     # small-batch path (the value gather inside the K-stream kernel).
     "qwen_like_long": (1, 12, 1, 2, 128, 40000, 3, 500, 2),

@@ -35,6 +35,15 @@ CASES = {
     "fewer_value_heads": (1, 8, 4, 2, 64, 900, 3, 20, 3),
     "gqa_llama_small": (2, 32, 8, 8, 64, 2049, 3, 64, 2),
     "short_ctx": (1, 4, 2, 4, 64, 17, 3, 5, 2),
+    # Launches of at least 256 workgroups, where the K stream gathers the value
+    # rows in its tail: key groups spanning two value heads (G_k 8, G_v 4),
+    # value heads shared by two key groups (G_k 2, G_v 4), one query head per
+    # key head, and at d = 128 up to 16 query heads per key head.
+    "tail_llama_like": (4, 32, 4, 8, 64, 2100, 3, 100, 2),
+    "tail_qwen_like_d128": (16, 12, 1, 2, 128, 4100, 3, 200, 2),
+    "tail_group16_d128": (8, 16, 1, 4, 128, 4000, 3, 300, 2),
+    "tail_fewer_value_heads": (8, 8, 4, 2, 64, 1100, 3, 50, 2),
+    "tail_mha_d64": (4, 8, 8, 8, 64, 1100, 3, 40, 2),
 }
 
 _cache = {}
@@ -179,6 +188,33 @@ def test_n_covering_context_is_full_attention():
         assert np.abs(out.float().cpu().numpy() - ref).max() <= OUT_TOL
 
 
+def test_tail_gather_every_row_selected():
+    """N >= ctx on a launch that gathers in the K stream's tail: every row of a
+    chunk is selected for all 16 head slots (4096 entries per workgroup, two
+    staging rounds), so the call is full attention."""
+    B, hq, hk, hv, d, rows = 16, 16, 1, 4, 128, 8192
+    q, K, V = make_inputs(B, hq, hk, hv, d, rows, 1, seed=46)
+    gpu = run_atopn(q, K, V, [rows], rows + 5, 1, logits_every_step=False)
+    assert np.isneginf(gpu["tau"][0]).all() and (gpu["counts"][0] == rows).all()
+    ref = oracle.full(to_np_bits(q)[0], to_np_bits(K), to_np_bits(V), rows)
+    assert np.abs(gpu["out"][0] - ref).max() <= OUT_TOL
+
+
+def test_tail_gather_plain_and_debug_calls_agree():
+    """The tail-gathering K stream with and without the debug outputs (logits,
+    selection bitmap) gives bit-identical outputs and counts."""
+    B, hq, hk, hv, d, L, T, N, n = CASES["tail_llama_like"]
+    q, K, V = make_inputs(B, hq, hk, hv, d, L + T, T, seed=47)
+    ctx = [L + t for t in range(T)]
+    dbg = run_atopn(q, K, V, ctx, N, n, logits_every_step=False)
+    plain = run_fused(q, K, V, ctx, N, n)
+    for t in range(T):
+        if t % n == 0:
+            continue                                   # refresh steps take another gather
+        assert np.array_equal(plain["counts"][t], dbg["counts"][t]), t
+        assert np.array_equal(plain["out"][t].view(np.uint32), dbg["out"][t].view(np.uint32)), t
+
+
 def test_infinite_threshold_selects_nothing():
     q, K, V = make_inputs(2, 8, 2, 4, 64, 600, 1, seed=42)
     d = saga.dims(2, 8, 2, 4, 64, 600, 600)
@@ -312,7 +348,8 @@ def _check_fused_against_separate(q, K, V, ctx_steps, N, n):
 
 
 @pytest.mark.parametrize("name", ["tiny", "qwen_like_small", "group16_d64", "mha_d128",
-                                  "fewer_value_heads", "gqa_llama_small", "short_ctx"])
+                                  "fewer_value_heads", "gqa_llama_small", "short_ctx",
+                                  "tail_qwen_like_d128"])
 def test_fused_refresh_step_matches_separate_calls(name):
     c = CASES[name]
     if isinstance(c, wl.Workload):
