@@ -149,6 +149,16 @@ def calibrate(torch):
                 seq.append({"bytes": nbytes, "workgroups": wg, "depth": depth,
                             "us": round(sec * 1e6, 2), "gbs": round(nbytes / sec / 1e9, 1)})
                 log(f"read {nbytes >> 20} MiB wg={wg} depth={depth}: {seq[-1]['gbs']} GB/s")
+    tiles = []
+    for rb in (128, 256):
+        for wg in (512, 768, 1024):
+            nbytes = (1 << 30) // (wg * 16384) * (wg * 16384)
+            for nt in (1, 2):
+                sec = timed(lambda r: probe.probe_read_tiles(buf, nbytes, rb, wg, nt, sink))
+                tiles.append({"bytes": nbytes, "row_bytes": rb, "workgroups": wg, "tiles": nt,
+                              "us": round(sec * 1e6, 2), "gbs": round(nbytes / sec / 1e9, 1)})
+                log(f"tiles {rb} B rows {nbytes >> 20} MiB wg={wg} tiles={nt}: "
+                    f"{tiles[-1]['gbs']} GB/s")
     del buf
     torch.cuda.empty_cache()
     rows_res = {}
@@ -179,6 +189,8 @@ def calibrate(torch):
         "peak_gbs": HBM_PEAK_GBS,
         "sequential_read": {"best_1gib": best_seq[1 << 30], "best_4gib": best_seq[4 << 30],
                             "table": seq},
+        "sequential_read_stream_lanes": {"best": max(tiles, key=lambda p: p["gbs"]),
+                                         "table": tiles},
         "random_rows": rows_res,
         "torch_copy_4gib": {"bytes_read": n, "bytes_written": n,
                             "gbs_read_plus_written": round(2 * n / t_copy / 1e9, 1)}}), flush=True)

@@ -37,6 +37,15 @@ extern "C" {
 int saga_probe_read(const void* buf_dev, size_t bytes, int32_t workgroups, int32_t depth,
                     uint32_t* sink_dev, void* stream);
 
+/* The same sequential read in the K stream's lane mapping: the 4 waves of
+ * each workgroup read 16-row tiles of row_bytes (128 or 256) bytes, lane l
+ * loading 16 bytes of row l % 16 at bytes 16 * (l / 16) + 64 m for
+ * m < row_bytes / 64, `tiles` (1 or 2) tiles per wave in each of two batches
+ * in flight.  bytes is a multiple of workgroups * 16384 and below 2^40; the
+ * chunk of a workgroup is below 2^31 bytes.  sink_dev: uint32 [workgroups]. */
+int saga_probe_read_tiles(const void* buf_dev, size_t bytes, int32_t row_bytes,
+                          int32_t workgroups, int32_t tiles, uint32_t* sink_dev, void* stream);
+
 /* Random-row read: `rows` rows of row_bytes (64, 128 or 256) bytes each, from
  * the buf_bytes / row_bytes rows of buf_dev (buf_bytes a multiple of row_bytes,
  * below 2^40).  Row k of the launch is row hash(seed, k) mod (buf_bytes /

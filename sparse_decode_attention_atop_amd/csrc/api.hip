@@ -501,8 +501,14 @@ int enqueue_fused(const saga_dims* dims, const Layout& L, const FusedPlan& f, co
 // or 128, value heads of one key group addressable with 32-bit offsets, and
 // a launch of at least kTailMinBlocks workgroups (fewer, longer chunks would
 // leave each workgroup many value rows to read on its own, where the list
-// path's gather spreads them).
+// path's gather spreads them).  At d = 128 the chunks must also be at least
+// kTailMinRows128 rows: the workgroups then share a CU two at a time and keep
+// half as many value rows in flight, and over shorter chunks (Qwen-like batch
+// 16 at 32K context and below) the tail outlasts the stream it follows, so
+// the list path is faster; at d = 64 the tail was faster at every length
+// measured (8K to 128K).
 constexpr int64_t kTailMinBlocks = 256;
+constexpr int64_t kTailMinRows128 = 2048;
 
 bool use_tail(const saga_dims* dims, const RowModel& rm, const Chunking& ch)
 {
@@ -510,6 +516,7 @@ bool use_tail(const saga_dims* dims, const RowModel& rm, const Chunking& ch)
     const int D = dims->head_dim, Gk = dims->h_q / dims->h_k, Gv = dims->h_q / dims->h_v;
     if (value_dim(dims) != D || (D != 64 && D != 128) || Gk > (D == 64 ? 8 : 16)) return false;
     if ((int64_t)dims->batch * dims->h_k * ch.chunks < kTailMinBlocks) return false;
+    if (D == 128 && ch.rows < kTailMinRows128) return false;
     // Value heads one key group reads: ceil over its query heads' map.
     const int64_t nvh = (Gk + Gv - 1) / Gv + 1;
     return nvh * dims->cache_len * D * 2 < ((int64_t)1 << 31);

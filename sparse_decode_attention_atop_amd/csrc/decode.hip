@@ -60,7 +60,7 @@ __device__ __forceinline__ void tail_gather(const SelectStreamArgs& a, unsigned 
 {
     constexpr int C = D / 8;                  // 16-byte pieces of a value row
     constexpr int SLW = kWave / C;            // value rows per wave load instruction
-    constexpr int NB = SAGA_TAIL_NB;          // value rows in flight per lane
+    constexpr int NB = D == 128 ? SAGA_TAIL_NB128 : SAGA_TAIL_NB;   // value rows in flight per lane
     constexpr int CAPL = 2048;                // entries staged per round
     constexpr int EPT = CAPL / kBlock;
     constexpr uint32_t kNoRow = 0x80000000u;  // past the value heads (< 2^31 bytes, host-checked)

@@ -45,7 +45,10 @@
 #define SAGA_TAIL_GATHER 1           // large-batch decode calls gather in the K stream's tail
 #endif
 #ifndef SAGA_TAIL_NB
-#define SAGA_TAIL_NB 8               // value rows in flight per lane in that tail gather
+#define SAGA_TAIL_NB 8               // value rows in flight per lane in that tail gather (d = 64)
+#endif
+#ifndef SAGA_TAIL_NB128
+#define SAGA_TAIL_NB128 8            // same at d = 128
 #endif
 #ifndef SAGA_GATHER_WAVES
 #define SAGA_GATHER_WAVES 0          // >0: ask for that many waves per SIMD (gather)

@@ -10,7 +10,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                         "libsaga_probe.so")
-EXPORTED_SYMBOLS = ("saga_probe_read", "saga_probe_rows")
+EXPORTED_SYMBOLS = ("saga_probe_read", "saga_probe_read_tiles", "saga_probe_rows")
 
 _lib = None
 
@@ -26,6 +26,8 @@ def library():
                                  ctypes.c_int64, ctypes.c_uint32)
         lib.saga_probe_read.argtypes = [vp, sz, i32, i32, vp, vp]
         lib.saga_probe_read.restype = ctypes.c_int
+        lib.saga_probe_read_tiles.argtypes = [vp, sz, i32, i32, i32, vp, vp]
+        lib.saga_probe_read_tiles.restype = ctypes.c_int
         lib.saga_probe_rows.argtypes = [vp, sz, i32, i64, u32, i32, i32, vp, vp]
         lib.saga_probe_rows.restype = ctypes.c_int
         _lib = lib
@@ -45,6 +47,18 @@ def probe_read(buf: torch.Tensor, nbytes: int, workgroups: int, depth: int,
                                    ctypes.c_void_p(sink.data_ptr()), _stream())
     if st != 0:
         raise RuntimeError(f"saga_probe_read: status {st}")
+
+
+def probe_read_tiles(buf: torch.Tensor, nbytes: int, row_bytes: int, workgroups: int,
+                     tiles: int, sink: torch.Tensor) -> None:
+    """Sequential read of the first nbytes of buf in the K stream's lane mapping."""
+    assert buf.is_cuda and buf.dtype == torch.uint8 and buf.numel() >= nbytes
+    assert sink.is_cuda and sink.dtype == torch.int32 and sink.numel() >= workgroups
+    st = library().saga_probe_read_tiles(ctypes.c_void_p(buf.data_ptr()), nbytes, row_bytes,
+                                         workgroups, tiles, ctypes.c_void_p(sink.data_ptr()),
+                                         _stream())
+    if st != 0:
+        raise RuntimeError(f"saga_probe_read_tiles: status {st}")
 
 
 def probe_rows(buf: torch.Tensor, row_bytes: int, rows: int, seed: int, workgroups: int,

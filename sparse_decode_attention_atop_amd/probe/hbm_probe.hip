@@ -6,6 +6,12 @@
 //   read_kernel   contiguous chunks, one per workgroup, 16-byte loads through a
 //                 buffer resource, two batches of DEPTH loads per lane in
 //                 flight (the K stream's pattern: every key row read once);
+//   tiles_kernel  the same chunks read in the K stream's own lane mapping:
+//                 each wave reads 16-row tiles of RB-byte rows, lane l loading
+//                 16 bytes of row l % 16 at bytes 16 * (l / 16) + 64 m (an MFMA
+//                 operand's layout: one load instruction covers 16 rows x 64
+//                 bytes, half of each 128-byte line), TILES tiles per wave in
+//                 each of two batches in flight;
 //   rows_kernel   rows of RB bytes at pseudo-random places in the buffer,
 //                 RB/16 lanes per row, DEPTH rows in flight per lane (the
 //                 sparse value gather's pattern).
@@ -82,6 +88,49 @@ __global__ __launch_bounds__(kBlock) void read_kernel(const unsigned char* buf, 
     fold_to_sink(acc, sink);
 }
 
+// Workgroup w reads bytes [w * chunk, (w + 1) * chunk) as 16-row tiles: wave
+// v takes tiles v, v + 4, ..., M = RB / 64 loads per lane and tile.
+template <int RB, int TILES>
+__global__ __launch_bounds__(kBlock) void tiles_kernel(const unsigned char* buf, uint32_t chunk,
+                                                       uint32_t* sink)
+{
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(buf + (uint64_t)blockIdx.x * chunk), (short)0, (int)chunk,
+        0x00020000);
+    constexpr int M = RB / 64;
+    constexpr uint32_t kTile = 16 * RB;                  // one wave's tile
+    constexpr uint32_t kStep = 4 * kTile;                // one tile per wave
+    constexpr uint32_t kBatch = TILES * kStep;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    u32x4 a[TILES][M], b[TILES][M];
+    uint32_t off = w * kTile + (lane & 15) * RB + (lane >> 4) * 16;
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int m = 0; m < M; ++m) a[t][m] = buf_ld16(r, off + t * kStep + 64 * m);
+    for (uint32_t base = 0; base < chunk; base += 2 * kBatch) {
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+            for (int m = 0; m < M; ++m) b[t][m] = buf_ld16(r, off + kBatch + t * kStep + 64 * m);
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc ^= a[t][m];
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+            for (int m = 0; m < M; ++m) a[t][m] = buf_ld16(r, off + 2 * kBatch + t * kStep + 64 * m);
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc ^= b[t][m];
+        off += 2 * kBatch;
+    }
+    fold_to_sink(acc, sink);
+}
+
 // Rows k = first .. first + per - 1 of the launch for workgroup w; lane group
 // `slot` (RB/16 lanes) reads rows first + slot, first + slot + SLOTS, ...
 template <int RB, int DEPTH>
@@ -136,6 +185,33 @@ PROBE_EXPORT int saga_probe_read(const void* buf_dev, size_t bytes, int32_t work
     case 4: hipLaunchKernelGGL(read_kernel<4>, grid, dim3(kBlock), 0, s, b, (uint32_t)chunk, sink_dev); break;
     case 8: hipLaunchKernelGGL(read_kernel<8>, grid, dim3(kBlock), 0, s, b, (uint32_t)chunk, sink_dev); break;
     default: return 1;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+PROBE_EXPORT int saga_probe_read_tiles(const void* buf_dev, size_t bytes, int32_t row_bytes,
+                                       int32_t workgroups, int32_t tiles, uint32_t* sink_dev,
+                                       void* stream)
+{
+    if (!buf_dev || !sink_dev || !aligned256(buf_dev) || ((uintptr_t)sink_dev & 3u))
+        return 1;
+    if (row_bytes != 128 && row_bytes != 256) return 1;
+    if (tiles != 1 && tiles != 2) return 1;
+    if (workgroups < 1 || workgroups > 65535 || bytes == 0 || bytes >= (size_t(1) << 40))
+        return 1;
+    if (bytes % ((size_t)workgroups * 16384) != 0) return 1;
+    const size_t chunk = bytes / workgroups;
+    if (chunk >= (size_t(1) << 31)) return 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const unsigned char* b = static_cast<const unsigned char*>(buf_dev);
+    const dim3 grid((unsigned)workgroups);
+    const uint32_t c = (uint32_t)chunk;
+    if (row_bytes == 128) {
+        if (tiles == 1) hipLaunchKernelGGL((tiles_kernel<128, 1>), grid, dim3(kBlock), 0, s, b, c, sink_dev);
+        else hipLaunchKernelGGL((tiles_kernel<128, 2>), grid, dim3(kBlock), 0, s, b, c, sink_dev);
+    } else {
+        if (tiles == 1) hipLaunchKernelGGL((tiles_kernel<256, 1>), grid, dim3(kBlock), 0, s, b, c, sink_dev);
+        else hipLaunchKernelGGL((tiles_kernel<256, 2>), grid, dim3(kBlock), 0, s, b, c, sink_dev);
     }
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }

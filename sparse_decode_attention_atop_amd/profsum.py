@@ -85,7 +85,9 @@ def _calibration(d: str, name: str) -> float:
 
 
 def _decode_calls(disp):
-    """Group dispatches (sorted by id) into plain decode calls."""
+    """Group dispatches (sorted by id) into plain decode calls: a K stream, then
+    a gather and a combine, or (the K stream gathering in its tail) only a
+    combine."""
     calls, cur, prev = [], None, ""
     for i in sorted(disp):
         k, v = disp[i]
@@ -100,7 +102,7 @@ def _decode_calls(disp):
         elif cur is not None and ("gather_kernel" in k or "combine_kernel" in k):
             cur[k.split("<")[0].split("::")[-1].split()[-1]] = v
         prev = k
-    return [c for c in calls if len(c) == 3]
+    return [c for c in calls if "combine_kernel" in c]
 
 
 def traffic(workload, fdir, wdir, cfdir, cwdir):
@@ -109,8 +111,9 @@ def traffic(workload, fdir, wdir, cfdir, cwdir):
     fetch = _decode_calls(_counter(fdir, "FETCH_SIZE"))
     write = _decode_calls(_counter(wdir, "WRITE_SIZE"))
     n = min(len(fetch), len(write))
-    kinds = ["select_stream", "gather_kernel", "combine_kernel"]
-    mean = lambda calls, k: sum(c[k] for c in calls[:n]) / n * 1024.0
+    kinds = [k for k in ("select_stream", "gather_kernel", "combine_kernel")
+             if any(k in c for c in fetch[:n])]
+    mean = lambda calls, k: sum(c.get(k, 0.0) for c in calls[:n]) / n * 1024.0
     lines = [f"Plain decode calls measured: {n}; scale factors fetch {ff:.4f}, write {wf:.4f}.", "",
              "| kernel | fetch raw (MiB) | fetch scaled (MiB) | write scaled (MiB) |",
              "|---|---|---|---|"]

@@ -162,8 +162,11 @@ void plan_choices()
         {{"qwen_like_128k_b16", 16, 12, 1, 2, 128, 0, 131104, 1024}, 131104, false, false, true},
         {{"llama_like_128k_b16_fp8k", 16, 32, 4, 8, 64, 0, 131104, 2048}, 131104, false, true, true},
         {{"tail_llama_like_2k_b4", 4, 32, 4, 8, 64, 0, 2103, 100}, 2100, false, false, true},    // 272
-        {{"tail_qwen_like_4k_b16", 16, 12, 1, 2, 128, 0, 4103, 200}, 4100, false, false, true},
-        {{"tail_group16_d128_b8", 8, 16, 1, 4, 128, 0, 4003, 300}, 4000, false, false, true},
+        {{"qwen_like_4k_b16", 16, 12, 1, 2, 128, 0, 4103, 200}, 4100, false, false, false},  // 128-row chunks
+        {{"qwen_like_32k_b16", 16, 12, 1, 2, 128, 0, 32771, 1024}, 32768, false, false, false},  // 1024
+        {{"qwen_like_64k_b16", 16, 12, 1, 2, 128, 0, 65539, 1024}, 65536, false, false, true},   // 2048
+        {{"tail_qwen_like_16k_b32", 32, 24, 2, 4, 128, 0, 16403, 200}, 16400, false, false, true},
+        {{"tail_group16_d128_b32", 32, 32, 2, 8, 128, 0, 16403, 300}, 16400, false, false, true},
         {{"tail_fewer_value_heads_b8", 8, 8, 4, 2, 64, 0, 1103, 50}, 1100, false, false, true},
         {{"tail_mha_d64_b4", 4, 8, 8, 8, 64, 0, 1103, 40}, 1100, false, false, true},
         {{"tail_fp8k_llama_like_b4", 4, 32, 4, 8, 64, 0, 2503, 64}, 2500, false, true, true},

@@ -54,6 +54,9 @@ def test_probe_library_exports_match_its_header():
     assert lib.saga_probe_read(None, 4096, 1, 1, fake, None) == 1
     assert lib.saga_probe_read(fake, 4096 * 3, 2, 1, fake, None) == 1      # not whole chunks
     assert lib.saga_probe_read(fake, 4096, 1, 3, fake, None) == 1          # depth 3
+    assert lib.saga_probe_read_tiles(fake, 16384, 64, 1, 1, fake, None) == 1    # row bytes
+    assert lib.saga_probe_read_tiles(fake, 16384, 128, 1, 3, fake, None) == 1   # tiles 3
+    assert lib.saga_probe_read_tiles(fake, 8192, 128, 1, 1, fake, None) == 1    # not whole chunks
     assert lib.saga_probe_rows(fake, 1 << 20, 96, 10, 0, 1, 2, fake, None) == 1
     assert lib.saga_probe_rows(fake, 1 << 20, 128, 0, 0, 1, 2, fake, None) == 1
 

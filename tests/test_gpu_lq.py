@@ -27,7 +27,7 @@ LQ_SHAPES = {
     "mha_lq16": (1, 4, 4, 4, 64, 900, 3, 40, 3, 16),
     "short_context_lq4": (1, 8, 2, 4, 64, 60, 3, 64, 2, 4),        # N >= ctx for every token
     "small_batch_path_lq4": (1, 8, 2, 4, 128, 40000, 3, 500, 2, 4),  # >= 64 fused workgroups
-    "tail_gather_lq4_d128": (8, 8, 2, 4, 128, 2000, 3, 100, 2, 4),   # 256 workgroups, 16 slots
+    "tail_gather_lq4_d128": (32, 8, 2, 4, 128, 16400, 2, 200, 2, 4),  # 512 workgroups, 16 slots
 }
 
 

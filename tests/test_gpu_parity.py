@@ -38,10 +38,11 @@ CASES = {
     # Launches of at least 256 workgroups, where the K stream gathers the value
     # rows in its tail: key groups spanning two value heads (G_k 8, G_v 4),
     # value heads shared by two key groups (G_k 2, G_v 4), one query head per
-    # key head, and at d = 128 up to 16 query heads per key head.
+    # key head, and at d = 128 (chunks of at least 2048 rows) up to 16 query
+    # heads per key head.
     "tail_llama_like": (4, 32, 4, 8, 64, 2100, 3, 100, 2),
-    "tail_qwen_like_d128": (16, 12, 1, 2, 128, 4100, 3, 200, 2),
-    "tail_group16_d128": (8, 16, 1, 4, 128, 4000, 3, 300, 2),
+    "tail_qwen_like_d128": (32, 24, 2, 4, 128, 16400, 3, 400, 2),
+    "tail_group16_d128": (32, 32, 2, 8, 128, 16400, 3, 300, 2),
     "tail_fewer_value_heads": (8, 8, 4, 2, 64, 1100, 3, 50, 2),
     "tail_mha_d64": (4, 8, 8, 8, 64, 1100, 3, 40, 2),
 }
@@ -190,9 +191,9 @@ def test_n_covering_context_is_full_attention():
 
 def test_tail_gather_every_row_selected():
     """N >= ctx on a launch that gathers in the K stream's tail: every row of a
-    chunk is selected for all 16 head slots (4096 entries per workgroup, two
-    staging rounds), so the call is full attention."""
-    B, hq, hk, hv, d, rows = 16, 16, 1, 4, 128, 8192
+    chunk is selected for all 16 head slots (16 x 2048 entries per workgroup,
+    16 staging rounds), so the call is full attention."""
+    B, hq, hk, hv, d, rows = 32, 32, 2, 8, 128, 16384
     q, K, V = make_inputs(B, hq, hk, hv, d, rows, 1, seed=46)
     gpu = run_atopn(q, K, V, [rows], rows + 5, 1, logits_every_step=False)
     assert np.isneginf(gpu["tau"][0]).all() and (gpu["counts"][0] == rows).all()

@@ -2,7 +2,8 @@
 grouped into plain decode calls, and how counter CSVs are read.
 
 A plain decode call is a stream-select launch followed by its gather and
-combine.  A refresh step's candidate pass (a stream launch right after the
+combine, or, when the stream gathers the value rows in its tail, by its
+combine alone.  A refresh step's candidate pass (a stream launch right after the
 pivot kernel) and its repair pass (right after the final select) are not
 plain calls, and neither are their gathers and combines.  Other libraries'
 kernels between ours are ignored.
@@ -12,6 +13,7 @@ import csv
 from sparse_decode_attention_atop_amd import profsum
 
 S = "saga::select_stream_kernel<64, 1, false, false, false>(saga::SelectStreamArgs)"
+ST = "saga::select_stream_kernel<64, 1, false, false, false, 8>(saga::SelectStreamArgs)"
 G = "saga::gather_kernel<64, 0, false>(saga::GatherArgs)"
 C = "saga::combine_kernel<64>(saga::Partials, int, unsigned short*, int*)"
 SAMPLE = "saga::sample_logits_kernel<64, 4, false, false>(saga::SampleArgs)"
@@ -31,6 +33,16 @@ def test_plain_calls_are_grouped_with_their_gather_and_combine():
     calls = profsum._decode_calls(d)
     assert calls == [{"select_stream": 0.0, "gather_kernel": 10.0, "combine_kernel": 20.0},
                      {"select_stream": 40.0, "gather_kernel": 50.0, "combine_kernel": 60.0}]
+
+
+def test_tail_gathering_calls_are_a_stream_and_a_combine():
+    # Tail-gathering stream launches, then a refresh step (whose repair pass
+    # is followed by the list path's gather and combine), then another call.
+    d = seq(ST, C, TORCH, ST, C, SAMPLE, PIVOT, S, FINAL, S, G, C, ST, C)
+    calls = profsum._decode_calls(d)
+    assert calls == [{"select_stream": 0.0, "combine_kernel": 10.0},
+                     {"select_stream": 30.0, "combine_kernel": 40.0},
+                     {"select_stream": 120.0, "combine_kernel": 130.0}]
 
 
 def test_refresh_step_launches_are_not_plain_calls():
