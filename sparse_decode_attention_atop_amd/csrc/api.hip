@@ -497,8 +497,8 @@ int enqueue_fused(const saga_dims* dims, const Layout& L, const FusedPlan& f, co
 }
 
 // Large-batch calls gather in the K stream's tail (decode.hip, tail_gather):
-// contiguous bf16 V with d_v = d_k of 64 (at most 8 query heads per key head)
-// or 128, value heads of one key group addressable with 32-bit offsets, and
+// contiguous V (bf16, or fp8 with an fp8 K cache) with d_v = d_k of 64 or
+// 128, value heads of one key group addressable with 32-bit offsets, and
 // a launch of at least kTailMinBlocks workgroups (fewer, longer chunks would
 // leave each workgroup many value rows to read on its own, where the list
 // path's gather spreads them).  At d = 128 the chunks must also be at least
@@ -512,14 +512,15 @@ constexpr int64_t kTailMinRows128 = 2048;
 
 bool use_tail(const saga_dims* dims, const RowModel& rm, const Chunking& ch)
 {
-    if (!SAGA_TAIL_GATHER || rm.pg.block_table || rm.v_scale) return false;
+    if (!SAGA_TAIL_GATHER || rm.pg.block_table) return false;
+    if (rm.v_scale && !rm.k_scale) return false;         // fp8 V comes with fp8 K
     const int D = dims->head_dim, Gk = dims->h_q / dims->h_k, Gv = dims->h_q / dims->h_v;
-    if (value_dim(dims) != D || (D != 64 && D != 128) || Gk > (D == 64 ? 8 : 16)) return false;
+    if (value_dim(dims) != D || (D != 64 && D != 128) || Gk > 16) return false;
     if ((int64_t)dims->batch * dims->h_k * ch.chunks < kTailMinBlocks) return false;
     if (D == 128 && ch.rows < kTailMinRows128) return false;
     // Value heads one key group reads: ceil over its query heads' map.
     const int64_t nvh = (Gk + Gv - 1) / Gv + 1;
-    return nvh * dims->cache_len * D * 2 < ((int64_t)1 << 31);
+    return nvh * dims->cache_len * D * (rm.v_scale ? 1 : 2) < ((int64_t)1 << 31);
 }
 
 // Decode with kept thresholds: stream-select into the lists, then gather
@@ -552,6 +553,7 @@ int enqueue_decode(const saga_dims* dims, const Layout& L, const void* q_dev,
         a.part = partials(workspace_dev, L);
         a.hv = dims->h_v;
         a.Gv = dims->h_q / dims->h_v;
+        a.v_scale = lrm.v_scale;
         st = hip_status(launch_select_stream(D, a, s));
         if (st != SAGA_OK) return st;
         return hip_status(launch_combine(D, a.part, rows, ch.chunks,

@@ -50,17 +50,26 @@ namespace {
 //   spread over all four waves, every sum has a fixed order, and results are
 //   bit-reproducible.  The four waves' partials are added in wave order into
 //   one partial per (b, query head, chunk), merged by combine_kernel.
-// GKT: most head slots a key group may have (8 at d = 64, 16 at d = 128).
-template <int D, int GKT>
+// GKT: most head slots a key group may have (16: the (wave, slot) partials
+// then fill half of the queues' 32 KB at d = 64 and all of it at d = 128).
+// V8: an fp8 E4M3 value cache (d bytes per row, one scale per (b, value
+// head)): each lane loads 16 codes and widens them exactly, and a head slot's
+// partial is multiplied by its value head's scale once.
+template <int D, int GKT, bool V8>
 __device__ __forceinline__ void tail_gather(const SelectStreamArgs& a, unsigned char* qlds,
                                             const int (&written)[16],
                                             const float (&mx)[4], int b, int g, int chunk,
                                             int64_t r0, int qh0, int64_t capw, int64_t nl,
                                             int wave, int lane)
 {
-    constexpr int C = D / 8;                  // 16-byte pieces of a value row
+    constexpr int VB = V8 ? 1 : 2;            // bytes per value element
+    constexpr int EPL = 16 / VB;              // elements per lane load (16 bytes)
+    constexpr int C = D / EPL;                // 16-byte pieces of a value row
     constexpr int SLW = kWave / C;            // value rows per wave load instruction
-    constexpr int NB = D == 128 ? SAGA_TAIL_NB128 : SAGA_TAIL_NB;   // value rows in flight per lane
+    // Value rows in flight per lane.  An fp8 row is half as wide, so a wave
+    // load covers twice the rows; the fp8 count keeps the kernel within the
+    // 128 VGPRs that the four workgroups per CU of the fp8 K launch need.
+    constexpr int NB = V8 ? SAGA_TAIL_NB_V8 : (D == 128 ? SAGA_TAIL_NB128 : SAGA_TAIL_NB);
     constexpr int CAPL = 2048;                // entries staged per round
     constexpr int EPT = CAPL / kBlock;
     constexpr uint32_t kNoRow = 0x80000000u;  // past the value heads (< 2^31 bytes, host-checked)
@@ -116,29 +125,30 @@ __device__ __forceinline__ void tail_gather(const SelectStreamArgs& a, unsigned 
     const int vi0 = g * Gk;
     const int nu0 = vi0 / a.Gv;
     const int nvh = (vi0 + Gk - 1) / a.Gv - nu0 + 1;
+    const unsigned char* vb = reinterpret_cast<const unsigned char*>(a.v);
     const __amdgpu_buffer_rsrc_t vrs =
-        make_rsrc(a.v + ((int64_t)(b * a.hv + nu0) * a.cache_len) * D,
-                  (uint32_t)((int64_t)nvh * a.cache_len * D * 2));
+        make_rsrc(vb + ((int64_t)(b * a.hv + nu0) * a.cache_len) * D * VB,
+                  (uint32_t)((int64_t)nvh * a.cache_len * D * VB));
     const int t = threadIdx.x, c = lane % C, sl = lane / C;
-    float cur[8], ls = 0.f;
+    float cur[EPL], ls = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) cur[j] = 0.f;
+    for (int j = 0; j < EPL; ++j) cur[j] = 0.f;
     int hc = -1;                               // the wave's current head slot
     auto flush = [&](int h) {
 #pragma unroll
         for (int off = C; off < kWave; off <<= 1) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) cur[j] += __shfl_xor(cur[j], off);
+            for (int j = 0; j < EPL; ++j) cur[j] += __shfl_xor(cur[j], off);
             ls += __shfl_xor(ls, off);
         }
         if (sl == 0) {
-            float* dst = wpart + (wave * GKT + h) * D + 8 * c;
+            float* dst = wpart + (wave * GKT + h) * D + EPL * c;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) dst[j] += cur[j];
+            for (int j = 0; j < EPL; ++j) dst[j] += cur[j];
             if (c == 0) wl[wave * GKT + h] += ls;
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) cur[j] = 0.f;
+        for (int j = 0; j < EPL; ++j) cur[j] = 0.f;
         ls = 0.f;
     };
 
@@ -166,7 +176,7 @@ __device__ __forceinline__ void tail_gather(const SelectStreamArgs& a, unsigned 
                 const int h = lst[k] >> 2;
                 const uint32_t nrel = (uint32_t)((vi0 + h) / a.Gv - nu0);
                 const uint32_t row = (uint32_t)(r0 + ent[k].x);
-                const uint32_t off = (nrel * (uint32_t)a.cache_len + row) * (uint32_t)(D * 2);
+                const uint32_t off = (nrel * (uint32_t)a.cache_len + row) * (uint32_t)(D * VB);
                 stage[e] = make_uint2(off | (uint32_t)h,
                                       __float_as_uint(__expf(__uint_as_float(ent[k].y) - tM[h])));
             }
@@ -198,10 +208,23 @@ __device__ __forceinline__ void tail_gather(const SelectStreamArgs& a, unsigned 
                 for (int k = 0; k < NB; ++k) {
                     const bool m = hh[k] == h;
                     ls += m ? w[k] : 0.f;
+                    if constexpr (V8) {
+                        // Codes 0-7 then 8-15 of the lane's 16, widened in order.
+                        const u32x4 x0 = fp8x8_to_bf16x8(u32x2{vv[k][0], vv[k][1]});
+                        const u32x4 x1 = fp8x8_to_bf16x8(u32x2{vv[k][2], vv[k][3]});
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        cur[2 * q] = m ? fmaf(w[k], bf16lo(vv[k][q]), cur[2 * q]) : cur[2 * q];
-                        cur[2 * q + 1] = m ? fmaf(w[k], bf16hi(vv[k][q]), cur[2 * q + 1]) : cur[2 * q + 1];
+                        for (int q = 0; q < 4; ++q) {
+                            cur[2 * q] = m ? fmaf(w[k], bf16lo(x0[q]), cur[2 * q]) : cur[2 * q];
+                            cur[2 * q + 1] = m ? fmaf(w[k], bf16hi(x0[q]), cur[2 * q + 1]) : cur[2 * q + 1];
+                            cur[8 + 2 * q] = m ? fmaf(w[k], bf16lo(x1[q]), cur[8 + 2 * q]) : cur[8 + 2 * q];
+                            cur[9 + 2 * q] = m ? fmaf(w[k], bf16hi(x1[q]), cur[9 + 2 * q]) : cur[9 + 2 * q];
+                        }
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            cur[2 * q] = m ? fmaf(w[k], bf16lo(vv[k][q]), cur[2 * q]) : cur[2 * q];
+                            cur[2 * q + 1] = m ? fmaf(w[k], bf16hi(vv[k][q]), cur[2 * q + 1]) : cur[2 * q + 1];
+                        }
                     }
                 }
             }
@@ -217,6 +240,7 @@ __device__ __forceinline__ void tail_gather(const SelectStreamArgs& a, unsigned 
         float o = 0.f;
 #pragma unroll
         for (int w = 0; w < kWavesPerBlock; ++w) o += wpart[(w * GKT + h) * D + p];
+        if constexpr (V8) o *= a.v_scale[b * a.hv + (vi0 + h) / a.Gv];
         a.part.o[(prow0 + (int64_t)h * a.chunks) * D + p] = o;
     }
     if (t < Gk) {
@@ -238,7 +262,7 @@ __device__ __forceinline__ void tail_gather(const SelectStreamArgs& a, unsigned 
 // queue could overflow, it is split by head slot and appended to the global
 // per-(head, chunk, wave) lists in order.  DEBUG adds the optional logits and
 // selection-bitmap outputs.
-template <int D, int U, bool DEBUG, bool PAGED, bool FP8, int GKT>
+template <int D, int U, bool DEBUG, bool PAGED, bool FP8, int GKT, bool V8>
 __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(SelectStreamArgs a)
 {
     __shared__ uint2 queue[kWavesPerBlock][4][kQueueCap];
@@ -516,7 +540,7 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
         static_assert(!PAGED, "the tail gather reads contiguous value caches");
         static_assert(sizeof(queue) == sizeof(uint2) * kWavesPerBlock * 4 * kQueueCap,
                       "tail_gather reuses the queues' LDS");
-        tail_gather<D, GKT>(a, reinterpret_cast<unsigned char*>(&queue[0][0][0]), written, mx, b,
+        tail_gather<D, GKT, V8>(a, reinterpret_cast<unsigned char*>(&queue[0][0][0]), written, mx, b,
                             g, chunk, r0, qh0, capw, nl, wave, lane);
         return;
     }
@@ -889,14 +913,18 @@ hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t s)
     const int kind = a.pg.block_table != nullptr ? 1 : (a.k_scale != nullptr ? 2 : 0);
 #define SAGA_LAUNCH_STREAM(DD, DBG, PG, F8)                                                      \
     hipLaunchKernelGGL((select_stream_kernel<DD, F8 ? decode_unroll_k8(DD) : decode_unroll(DD),  \
-                                             DBG, PG, F8, 0>), grid, dim3(kBlock), 0, s, a)
+                                             DBG, PG, F8, 0, false>), grid, dim3(kBlock), 0, s, a)
 #define SAGA_LAUNCH_TAIL(DD, DBG, F8)                                                            \
-    hipLaunchKernelGGL((select_stream_kernel<DD, F8 ? decode_unroll_k8(DD) : decode_unroll(DD),  \
-                                             DBG, false, F8, DD == 64 ? 8 : 16>),                 \
-                       grid, dim3(kBlock), 0, s, a)
+    if (a.v_scale) hipLaunchKernelGGL((select_stream_kernel<DD, F8 ? decode_unroll_k8(DD) :       \
+                                                            decode_unroll(DD), DBG, false, F8, 16, F8>), \
+                                      grid, dim3(kBlock), 0, s, a);                              \
+    else hipLaunchKernelGGL((select_stream_kernel<DD, F8 ? decode_unroll_k8(DD) : decode_unroll(DD), \
+                                                  DBG, false, F8, 16, false>),                   \
+                            grid, dim3(kBlock), 0, s, a)
     if (a.v) {
-        // The tail gather: contiguous caches, d = 64 (at most 8 head slots) or 128.
-        if (a.pg.block_table || (D != 64 && D != 128) || a.Gk > (D == 64 ? 8 : 16))
+        // The tail gather: contiguous caches, d = 64 or 128, at most 16 head
+        // slots; an fp8 V cache comes with an fp8 K cache.
+        if (a.pg.block_table || (D != 64 && D != 128) || a.Gk > 16 || (a.v_scale && kind != 2))
             return hipErrorInvalidValue;
         if (D == 64) {
             if (kind == 2) { if (dbg) SAGA_LAUNCH_TAIL(64, true, true); else SAGA_LAUNCH_TAIL(64, false, true); }

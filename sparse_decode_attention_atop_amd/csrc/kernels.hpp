@@ -426,11 +426,12 @@ struct SelectStreamArgs {
     const float* k_scale;    // non-null: fp8 e4m3 K, one scale per (b, key head)
     PagedKV pg;              // paged caches (block_table != nullptr)
     // Value gather in the stream's tail (v non-null; contiguous bf16 V with
-    // d_v = d_k): each workgroup gathers its own chunk's selected value rows
+    // d_v = d_k of 64 or 128): each workgroup gathers its own chunk's selected value rows
     // and writes one partial per (b*h_q + i, chunk) instead of list lengths.
     const uint16_t* v;
     Partials part;
     int32_t hv, Gv;
+    const float* v_scale;    // non-null: fp8 e4m3 V (d bytes per row), one scale per (b, value head)
 };
 
 // Gather kernel: softmax weights and the sparse value gather over the lists.

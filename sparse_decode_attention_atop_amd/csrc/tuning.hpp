@@ -50,6 +50,9 @@
 #ifndef SAGA_TAIL_NB128
 #define SAGA_TAIL_NB128 8            // same at d = 128
 #endif
+#ifndef SAGA_TAIL_NB_V8
+#define SAGA_TAIL_NB_V8 3            // same with an fp8 V cache (16 codes per lane load)
+#endif
 #ifndef SAGA_GATHER_WAVES
 #define SAGA_GATHER_WAVES 0          // >0: ask for that many waves per SIMD (gather)
 #endif

@@ -130,9 +130,9 @@ bool full_supported(const Shape& s)
 // Which path saga_decode_step takes: the small-batch path needs at most four
 // (b, key head) groups and a plan of at least 64 workgroups whose worst case
 // fits the LDS with the whole launch resident.  Otherwise the K stream gathers
-// in its tail when V is contiguous bf16 with d_v = d_k of 64 (at most 8 query
-// heads per key head) or 128 and the launch has at least 256 workgroups; else
-// the list path (stream, gather, combine).
+// in its tail when V is contiguous bf16 with d_v = d_k of 64, or of 128 with
+// chunks of at least 2048 rows, and the launch has at least 256 workgroups;
+// else the list path (stream, gather, combine).
 void plan_choices()
 {
     struct Case {
@@ -141,6 +141,7 @@ void plan_choices()
         bool fused;
         bool fp8k = false;   // the fp8 K call
         bool tail = false;   // the K stream gathers in its tail
+        bool fp8kv = false;  // the fp8 K and V call
     };
     const Case cases[] = {
         {{"qwen_like_128k_b1", 1, 12, 1, 2, 128, 0, 131104, 1024}, 131104, true},
@@ -170,9 +171,13 @@ void plan_choices()
         {{"tail_fewer_value_heads_b8", 8, 8, 4, 2, 64, 0, 1103, 50}, 1100, false, false, true},
         {{"tail_mha_d64_b4", 4, 8, 8, 8, 64, 0, 1103, 40}, 1100, false, false, true},
         {{"tail_fp8k_llama_like_b4", 4, 32, 4, 8, 64, 0, 2503, 64}, 2500, false, true, true},
+        {{"llama_like_128k_b16_fp8kv", 16, 32, 4, 8, 64, 0, 131104, 2048}, 131104, false, false, true, true},
+        {{"tail_fp8kv_qwen_like_16k_b32", 32, 24, 2, 4, 128, 0, 16403, 200}, 16400, false, false, true, true},
+        {{"qwen_like_4k_b16_fp8kv", 16, 12, 1, 2, 128, 0, 4103, 200}, 4100, false, false, false, true},
         {{"gqa_llama_small_b2", 2, 32, 8, 8, 64, 0, 2052, 64}, 2049, false, false, true},   // 272
+        {{"tail_group16_d64_b16", 16, 16, 1, 4, 64, 0, 2103, 100}, 2100, false, false, true}, // 272
         {{"llama_like_1k_b4", 4, 32, 4, 8, 64, 0, 1024, 64}, 1000, false, false, false},    // 128
-        {{"group16_d64_b16", 16, 16, 1, 4, 64, 0, 8200, 300}, 8192, false, false, false},   // G_k 16
+        {{"group16_d64_b16", 16, 16, 1, 4, 64, 0, 8200, 300}, 8192, false, false, true},    // G_k 16
         {{"dk64_dv128_b16", 16, 12, 1, 2, 64, 128, 8200, 300}, 8192, false, false, false},  // d_v != d_k
         {{"mha_d32_b16", 16, 8, 8, 8, 32, 0, 8200, 300}, 8192, false, false, false},        // d = 32
     };
@@ -185,6 +190,7 @@ void plan_choices()
         void* k = a.get((size_t)s.B * s.hk * s.cache_len * s.dk * 2);
         void* v = a.get((size_t)s.B * s.hv * s.cache_len * dv * 2);
         float* ks = static_cast<float*>(a.get((size_t)s.B * s.hk * 4));
+        float* vs = static_cast<float*>(a.get((size_t)s.B * s.hv * 4));
         float* tau = static_cast<float*>(a.get(bh * 4));
         void* out = a.get(bh * dv * 2);
         const saga_dims d = make_dims(s, c.ctx);
@@ -192,9 +198,11 @@ void plan_choices()
         void* ws = a.get(wsb);
         saga::g_launches = saga::g_fused_launches = saga::g_tail_launches = 0;
         const int st =
-            c.fp8k ? saga_decode_step_fp8k(&d, q, k, ks, v, tau, out, nullptr, nullptr, ws, wsb,
-                                           nullptr)
-                   : saga_decode_step(&d, q, k, v, tau, out, nullptr, nullptr, ws, wsb, nullptr);
+            c.fp8kv ? saga_decode_step_fp8kv(&d, q, k, ks, v, vs, tau, out, nullptr, nullptr, ws,
+                                             wsb, nullptr)
+            : c.fp8k ? saga_decode_step_fp8k(&d, q, k, ks, v, tau, out, nullptr, nullptr, ws, wsb,
+                                             nullptr)
+                     : saga_decode_step(&d, q, k, v, tau, out, nullptr, nullptr, ws, wsb, nullptr);
         CHECK(st == SAGA_OK, "%s: status %d", s.name, st);
         CHECK((saga::g_fused_launches > 0) == c.fused, "%s: small-batch path %s", s.name,
               c.fused ? "expected" : "not expected");

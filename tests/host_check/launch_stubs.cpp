@@ -237,17 +237,19 @@ hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t)
                                a.head_stride, a.overflow_at);
     const int64_t lists = (int64_t)a.B * a.hq * a.chunks * kWavesPerBlock;
     if (a.v) {
-        // The tail gather: contiguous bf16 V with d_v = d_k, at most 8 (d = 64)
-        // or 16 (d = 128) head slots, one partial per (b*h_q + i, chunk), the
-        // key group's value heads under 2^31 bytes (32-bit buffer offsets).
+        // The tail gather: contiguous bf16 V with d_v = d_k, at most 16 head
+        // slots, one partial per (b*h_q + i, chunk), the key group's value
+        // heads under 2^31 bytes (32-bit buffer offsets).
         ++g_tail_launches;
-        EXPECT(!a.pg.block_table && (D == 64 || D == 128) && a.Gk <= (D == 64 ? 8 : 16));
+        EXPECT(!a.pg.block_table && (D == 64 || D == 128) && a.Gk <= 16);
         EXPECT(a.hv >= 1 && a.Gv >= 1 && a.hq == a.hv * a.Gv);
         EXPECT(a.chunks >= 1 && (int64_t)a.chunks * a.rows_per_chunk >= a.ctx);
         const int64_t nvh = (int64_t)(a.Gk + a.Gv - 1) / a.Gv + 1;
-        EXPECT(nvh * a.cache_len * D * 2 < ((int64_t)1 << 31));
+        EXPECT(nvh * a.cache_len * D * (a.v_scale ? 1 : 2) < ((int64_t)1 << 31));
+        EXPECT(!a.v_scale || a.k_scale);
         touch_partials(a.part, (int64_t)a.B * a.hq * a.chunks, D);
-        touch_cache(a.v, a.B, a.hv, a.cache_len, a.ctx, D, 2);
+        touch_cache(a.v, a.B, a.hv, a.cache_len, a.ctx, D, a.v_scale ? 1 : 2);
+        if (a.v_scale) rd_span(a.v_scale, (int64_t)a.B * a.hv);
     } else {
         wr_span("list counts", a.list_count, lists);
         wr_span("list maxima", a.list_max, lists);

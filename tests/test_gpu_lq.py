@@ -28,6 +28,7 @@ LQ_SHAPES = {
     "short_context_lq4": (1, 8, 2, 4, 64, 60, 3, 64, 2, 4),        # N >= ctx for every token
     "small_batch_path_lq4": (1, 8, 2, 4, 128, 40000, 3, 500, 2, 4),  # >= 64 fused workgroups
     "tail_gather_lq4_d128": (32, 8, 2, 4, 128, 16400, 2, 200, 2, 4),  # 512 workgroups, 16 slots
+    "tail_gather_llama_like_lq2": (4, 32, 4, 8, 64, 3000, 3, 128, 2, 2),  # 384 workgroups, 16 slots
 }
 
 

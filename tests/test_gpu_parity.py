@@ -38,13 +38,14 @@ CASES = {
     # Launches of at least 256 workgroups, where the K stream gathers the value
     # rows in its tail: key groups spanning two value heads (G_k 8, G_v 4),
     # value heads shared by two key groups (G_k 2, G_v 4), one query head per
-    # key head, and at d = 128 (chunks of at least 2048 rows) up to 16 query
-    # heads per key head.
+    # key head, and up to 16 query heads per key head (d = 128: chunks of at
+    # least 2048 rows).
     "tail_llama_like": (4, 32, 4, 8, 64, 2100, 3, 100, 2),
     "tail_qwen_like_d128": (32, 24, 2, 4, 128, 16400, 3, 400, 2),
     "tail_group16_d128": (32, 32, 2, 8, 128, 16400, 3, 300, 2),
     "tail_fewer_value_heads": (8, 8, 4, 2, 64, 1100, 3, 50, 2),
     "tail_mha_d64": (4, 8, 8, 8, 64, 1100, 3, 40, 2),
+    "tail_group16_d64": (16, 16, 1, 4, 64, 2100, 3, 100, 2),
 }
 
 _cache = {}
