@@ -56,11 +56,15 @@ namespace {
 // head)): each lane loads 16 codes and widens them exactly, and a head slot's
 // partial is multiplied by its value head's scale once.
 template <int D, int GKT, bool V8>
+// qe/qp: the wave's last queue entries (block k of queue i in lane order,
+// x = ~0u where the queue ends) and their list positions; `flushed`: the wave
+// wrote entries to its lists earlier in the stream.
 __device__ __forceinline__ void tail_gather(const SelectStreamArgs& a, unsigned char* qlds,
                                             const int (&written)[16],
-                                            const float (&mx)[4], int b, int g, int chunk,
-                                            int64_t r0, int qh0, int64_t capw, int64_t nl,
-                                            int wave, int lane)
+                                            const uint2 (&qe)[4][4], const int (&qp)[4][4],
+                                            bool flushed, const float (&mx)[4], int b, int g,
+                                            int chunk, int64_t r0, int qh0, int64_t capw,
+                                            int64_t nl, int wave, int lane)
 {
     constexpr int VB = V8 ? 1 : 2;            // bytes per value element
     constexpr int EPL = 16 / VB;              // elements per lane load (16 bytes)
@@ -82,6 +86,7 @@ __device__ __forceinline__ void tail_gather(const SelectStreamArgs& a, unsigned 
     __shared__ int32_t tpre[4 * 16 + 1];      // flat start of list (head slot, wave)
     __shared__ float tM[16];
     __shared__ float wl[kWavesPerBlock * GKT];   // (wave, slot) weight sums
+    __shared__ int32_t tfl[kWavesPerBlock + 1];  // waves that flushed; [4]: stage directly
     // The stream's queues (no longer used) hold the (wave, slot) partials and,
     // when they fit, the staged entries too.
     constexpr bool kStageInQueue = kPartBytes + CAPL * 8 <= kQueueBytes;
@@ -102,7 +107,8 @@ __device__ __forceinline__ void tail_gather(const SelectStreamArgs& a, unsigned 
         for (int h = 0; h < 16; ++h) c = lane == h ? written[h] : c;
         tcnt[wave][lane] = c;
     }
-    __syncthreads();                           // every wave's queue flushed
+    if (lane == 0) tfl[wave] = flushed ? 1 : 0;
+    __syncthreads();                           // every wave's queue is in its registers
     for (int i = threadIdx.x; i < (int)kPartFloats; i += kBlock) wpart[i] = 0.f;
     if (threadIdx.x < kWavesPerBlock * GKT) wl[threadIdx.x] = 0.f;
     if (wave == 0) {
@@ -114,12 +120,18 @@ __device__ __forceinline__ void tail_gather(const SelectStreamArgs& a, unsigned 
             if (lane >= off) incl += u;
         }
         tpre[lane] = incl - n;
-        if (lane == kWave - 1) tpre[64] = incl;
+        if (lane == kWave - 1) {
+            tpre[64] = incl;
+            // The whole chunk's entries are still in the waves' registers and
+            // fit one staging round: stage them from there.
+            tfl[kWavesPerBlock] = (tfl[0] | tfl[1] | tfl[2] | tfl[3]) == 0 && incl <= CAPL;
+        }
         if (lane < 16)
             tM[lane] = fmaxf(fmaxf(tmx[0][lane], tmx[1][lane]), fmaxf(tmx[2][lane], tmx[3][lane]));
     }
     __syncthreads();
     const int32_t total = tpre[64];
+    const bool direct = tfl[kWavesPerBlock] != 0;
 
     // Value heads of this key group's query heads (virtual heads when lq > 1).
     const int vi0 = g * Gk;
@@ -152,10 +164,45 @@ __device__ __forceinline__ void tail_gather(const SelectStreamArgs& a, unsigned 
         ls = 0.f;
     };
 
+    const int64_t local0 = (int64_t)chunk * kWavesPerBlock + wave;   // this wave's lists
+    if (direct) {
+        // Each lane stages its own entries at their flat places.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint2 e = qe[i][k];
+                if (e.x != ~0u) {
+                    const int h = 4 * (int)((e.x & 15u) >> 2) + i;
+                    const int f = tpre[4 * h + wave] + qp[i][k];
+                    const uint32_t nrel = (uint32_t)((vi0 + h) / a.Gv - nu0);
+                    const uint32_t row = (uint32_t)(r0 + (e.x >> 4));
+                    const uint32_t off = (nrel * (uint32_t)a.cache_len + row) * (uint32_t)(D * VB);
+                    stage[f] = make_uint2(off | (uint32_t)h,
+                                          __float_as_uint(__expf(__uint_as_float(e.y) - tM[h])));
+                }
+            }
+        }
+    } else {
+        // Store them to the lists, after the entries flushed earlier.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint2 e = qe[i][k];
+                if (e.x != ~0u)
+                    a.entries[list_index(qh0 + 4 * (int)((e.x & 15u) >> 2) + i, local0,
+                                         (uint32_t)qp[i][k], capw, nl, a.head_stride,
+                                         a.overflow_at)] = make_uint2(e.x >> 4, e.y);
+            }
+        }
+        __syncthreads();                       // every wave's lists are complete
+    }
     for (int32_t base = 0; base < total; base += CAPL) {
         const int n = min(CAPL, total - base);
         // Stage entries t, t + 256, ...: list by binary search over the flat
         // starts, all loads in flight before any is used.
+        if (!direct) {
         uint2 ent[EPT];
         int lst[EPT];
 #pragma unroll
@@ -180,6 +227,7 @@ __device__ __forceinline__ void tail_gather(const SelectStreamArgs& a, unsigned 
                 stage[e] = make_uint2(off | (uint32_t)h,
                                       __float_as_uint(__expf(__uint_as_float(ent[k].y) - tM[h])));
             }
+        }
         }
         __syncthreads();
         const int e_lo = wave * n / kWavesPerBlock, e_hi = (wave + 1) * n / kWavesPerBlock;
@@ -535,15 +583,42 @@ __global__ __launch_bounds__(kBlock) SAGA_STREAM_ATTR void select_stream_kernel(
         } while (t0 < r1);
     }
     }
-    flush_all();
     if constexpr (GKT > 0) {
         static_assert(!PAGED, "the tail gather reads contiguous value caches");
+        // The queues' last entries go to registers with the list positions
+        // flush_all would give them: the tail stages them from there, or
+        // stores them to the lists when it must read the lists anyway.
+        bool flushed = false;
+#pragma unroll
+        for (int h = 0; h < 16; ++h) flushed |= written[h] != 0;
+        uint2 qe[4][4];
+        int qp[4][4];
+        wave_sync();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const bool have = kWave * k + lane < qn[i];
+                const uint2 e = have ? q4[i][kWave * k + lane] : make_uint2(~0u, 0u);
+                const int gs = (e.x & 15) >> 2;
+                int pos = 0;
+#pragma unroll
+                for (int g2 = 0; g2 < 4; ++g2) {
+                    const uint64_t m = __ballot(have && gs == g2);
+                    if (gs == g2) pos = written[4 * g2 + i] + (int)lanes_below(m);
+                    written[4 * g2 + i] += __popcll(m);
+                }
+                qe[i][k] = e;
+                qp[i][k] = pos;
+            }
+        }
         static_assert(sizeof(queue) == sizeof(uint2) * kWavesPerBlock * 4 * kQueueCap,
                       "tail_gather reuses the queues' LDS");
-        tail_gather<D, GKT, V8>(a, reinterpret_cast<unsigned char*>(&queue[0][0][0]), written, mx, b,
-                            g, chunk, r0, qh0, capw, nl, wave, lane);
+        tail_gather<D, GKT, V8>(a, reinterpret_cast<unsigned char*>(&queue[0][0][0]), written,
+                                qe, qp, flushed, mx, b, g, chunk, r0, qh0, capw, nl, wave, lane);
         return;
     }
+    flush_all();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float m = group16_max(mx[i]);
