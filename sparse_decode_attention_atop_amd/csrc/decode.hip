@@ -50,8 +50,8 @@ namespace {
 //   spread over all four waves, every sum has a fixed order, and results are
 //   bit-reproducible.  The four waves' partials are added in wave order into
 //   one partial per (b, query head, chunk), merged by combine_kernel.
-// GKT: most head slots a key group may have (16: the (wave, slot) partials
-// then fill half of the queues' 32 KB at d = 64 and all of it at d = 128).
+// GKT: most head slots a key group may have (8 or 16; at 16 the (wave, slot)
+// partials fill half of the queues' 32 KB at d = 64 and all of it at d = 128).
 // V8: an fp8 E4M3 value cache (d bytes per row, one scale per (b, value
 // head)): each lane loads 16 codes and widens them exactly, and a head slot's
 // partial is multiplied by its value head's scale once.
@@ -74,12 +74,15 @@ __device__ __forceinline__ void tail_gather(const SelectStreamArgs& a, unsigned 
     // load covers twice the rows; the fp8 count keeps the kernel within the
     // 128 VGPRs that the four workgroups per CU of the fp8 K launch need.
     constexpr int NB = V8 ? SAGA_TAIL_NB_V8 : (D == 128 ? SAGA_TAIL_NB128 : SAGA_TAIL_NB);
-    constexpr int CAPL = 2048;                // entries staged per round
-    constexpr int EPT = CAPL / kBlock;
     constexpr uint32_t kNoRow = 0x80000000u;  // past the value heads (< 2^31 bytes, host-checked)
     constexpr size_t kPartFloats = (size_t)kWavesPerBlock * GKT * D;
     constexpr size_t kPartBytes = kPartFloats * 4;
     constexpr size_t kQueueBytes = sizeof(uint2) * kWavesPerBlock * 4 * kQueueCap;
+    // Entries staged per round: the queues' LDS left after the partials (3072
+    // at d = 64 with 8 head slots, 2048 with 16), else 2048 in LDS of their own.
+    constexpr int kLeft = (int)((kQueueBytes - kPartBytes) / 8 / kBlock * kBlock);
+    constexpr int CAPL = kLeft >= 2048 ? kLeft : 2048;
+    constexpr int EPT = CAPL / kBlock;
     static_assert(kPartBytes <= kQueueBytes, "the (wave, slot) partials live in the queues' LDS");
     __shared__ int32_t tcnt[kWavesPerBlock][16];
     __shared__ float tmx[kWavesPerBlock][16];
@@ -989,24 +992,28 @@ hipError_t launch_select_stream(int D, const SelectStreamArgs& a, hipStream_t s)
 #define SAGA_LAUNCH_STREAM(DD, DBG, PG, F8)                                                      \
     hipLaunchKernelGGL((select_stream_kernel<DD, F8 ? decode_unroll_k8(DD) : decode_unroll(DD),  \
                                              DBG, PG, F8, 0, false>), grid, dim3(kBlock), 0, s, a)
-#define SAGA_LAUNCH_TAIL(DD, DBG, F8)                                                            \
+#define SAGA_LAUNCH_TAIL(DD, DBG, F8, GG)                                                        \
     if (a.v_scale) hipLaunchKernelGGL((select_stream_kernel<DD, F8 ? decode_unroll_k8(DD) :       \
-                                                            decode_unroll(DD), DBG, false, F8, 16, F8>), \
+                                                            decode_unroll(DD), DBG, false, F8, GG, F8>), \
                                       grid, dim3(kBlock), 0, s, a);                              \
     else hipLaunchKernelGGL((select_stream_kernel<DD, F8 ? decode_unroll_k8(DD) : decode_unroll(DD), \
-                                                  DBG, false, F8, 16, false>),                   \
+                                                  DBG, false, F8, GG, false>),                   \
                             grid, dim3(kBlock), 0, s, a)
     if (a.v) {
         // The tail gather: contiguous caches, d = 64 or 128, at most 16 head
-        // slots; an fp8 V cache comes with an fp8 K cache.
+        // slots; an fp8 V cache comes with an fp8 K cache.  With bf16 K at
+        // d = 64, key groups of at most 8 query heads get 8 slots and the
+        // larger stage that leaves (128 VGPRs, three workgroups per CU, which
+        // the bf16 launch of 768 has); the fp8 K launch needs four per CU.
         if (a.pg.block_table || (D != 64 && D != 128) || a.Gk > 16 || (a.v_scale && kind != 2))
             return hipErrorInvalidValue;
         if (D == 64) {
-            if (kind == 2) { if (dbg) SAGA_LAUNCH_TAIL(64, true, true); else SAGA_LAUNCH_TAIL(64, false, true); }
-            else { if (dbg) SAGA_LAUNCH_TAIL(64, true, false); else SAGA_LAUNCH_TAIL(64, false, false); }
+            if (kind == 2) { if (dbg) SAGA_LAUNCH_TAIL(64, true, true, 16); else SAGA_LAUNCH_TAIL(64, false, true, 16); }
+            else if (a.Gk <= 8) { if (dbg) SAGA_LAUNCH_TAIL(64, true, false, 8); else SAGA_LAUNCH_TAIL(64, false, false, 8); }
+            else { if (dbg) SAGA_LAUNCH_TAIL(64, true, false, 16); else SAGA_LAUNCH_TAIL(64, false, false, 16); }
         } else {
-            if (kind == 2) { if (dbg) SAGA_LAUNCH_TAIL(128, true, true); else SAGA_LAUNCH_TAIL(128, false, true); }
-            else { if (dbg) SAGA_LAUNCH_TAIL(128, true, false); else SAGA_LAUNCH_TAIL(128, false, false); }
+            if (kind == 2) { if (dbg) SAGA_LAUNCH_TAIL(128, true, true, 16); else SAGA_LAUNCH_TAIL(128, false, true, 16); }
+            else { if (dbg) SAGA_LAUNCH_TAIL(128, true, false, 16); else SAGA_LAUNCH_TAIL(128, false, false, 16); }
         }
 #undef SAGA_LAUNCH_TAIL
         return hipGetLastError();
