@@ -151,10 +151,11 @@ def sweep(path):
 
 def util(d):
     names = ["MfmaUtil", "VALUBusy", "MfmaFlopsBF16"]
-    kinds = ["select_stream", "gather_kernel", "combine_kernel"]
     per = {nm: _decode_calls(_counter(d, nm)) for nm in names}
     n = min(len(c) for c in per.values())
-    mean = lambda nm, k: sum(c[k] for c in per[nm][:n]) / n
+    kinds = [k for k in ("select_stream", "gather_kernel", "combine_kernel")
+             if any(k in c for c in per[names[0]][:n])]
+    mean = lambda nm, k: sum(c.get(k, 0.0) for c in per[nm][:n]) / n
     lines = [f"Plain decode calls measured: {n}.", "",
              "| kernel | MFMA busy (% of SIMD cycles) | VALU busy (%) | bf16 MFMA GFLOP per launch |",
              "|---|---|---|---|"]
