@@ -192,6 +192,54 @@ def test_per_sequence_lengths_match_each_sequence_alone(fused):
             assert err <= OUT_TOL, f"b={b} t={t}: {err:.3e}"
 
 
+# Larger batches of mixed lengths (many K-stream workgroups per call): (B, hq,
+# hk, hv, d, P, pages per sequence, N, n, T, sequences checked).
+LARGE_PAGED = {
+    "llama_like_d64": (8, 32, 4, 8, 64, 256, 12, 100, 2, 3, None),
+    "qwen_like_d128": (64, 12, 1, 2, 128, 256, 66, 300, 2, 2, [0, 1, 17, 40, 63]),
+}
+
+
+@pytest.mark.parametrize("name", list(LARGE_PAGED))
+def test_large_batch_paged_per_sequence_lengths(name):
+    """Paged calls with mixed lengths at larger batches: per sequence,
+    thresholds and counts bit-equal to that sequence's own contiguous calls,
+    and outputs within the bar of the oracle on that step's selection (the
+    single-sequence calls take another path, so the summation order differs)."""
+    B, hq, hk, hv, d, P, maxp, N, n, T, check = LARGE_PAGED[name]
+    rows = maxp * P
+    q, K, V = make_inputs(B, hq, hk, hv, d, rows, T, seed=95 + len(name))
+    rng = np.random.default_rng(7)
+    base = rng.integers(rows // 8, rows - T, size=B)
+    base[0], base[-1] = rows - T, 40                             # the longest; N >= ctx
+    lens = [[int(x) + t for x in base] for t in range(T)]
+    kp, vp, table, npages = to_pages(K, V, P, seed=4)
+    got = run_paged(q, kp, vp, table, npages, P, rows, lens, N, n)
+    for b in (check if check is not None else range(B)):
+        ctx_b = [lens[t][b] for t in range(T)]
+        qb = q[:, b:b + 1].contiguous()
+        Kb, Vb = K[b:b + 1].contiguous(), V[b:b + 1].contiguous()
+        ref = run_contiguous(qb, Kb, Vb, ctx_b, N, n)
+        print(f"[paged large {name} b={b}] ctx={ctx_b}", flush=True)
+        for t in range(T):
+            tau_r, cnt_r, _ = ref[t]
+            tau_g, cnt_g, out_g = got[t]
+            assert np.array_equal(bits(tau_r[0]), bits(tau_g[b])), (b, t)
+            assert np.array_equal(cnt_r[0].cpu().numpy(), cnt_g[b].cpu().numpy()), (b, t)
+            dm = saga.dims(1, hq, hk, hv, d, ctx_b[t], rows)
+            ws = saga.alloc_workspace(dm, 1)
+            bm = torch.empty(1, hq, (rows + 31) // 32, dtype=torch.int32, device="cuda")
+            o1 = torch.empty(1, hq, d, dtype=torch.bfloat16, device="cuda")
+            saga.saga_decode_step(dm, qb[t], Kb, Vb, tau_g[b:b + 1].contiguous(), o1, ws,
+                                  sel_bitmap_debug=bm)
+            torch.cuda.synchronize()
+            ref_o, cnt_o = oracle.masked(to_np_bits(qb[t]), to_np_bits(Kb), to_np_bits(Vb),
+                                         ctx_b[t], bm.cpu().numpy().view(np.uint32))
+            assert (cnt_o[0] == cnt_g[b].cpu().numpy()).all(), (b, t)
+            err = np.abs(out_g[b].float().cpu().numpy() - ref_o[0]).max()
+            assert err <= OUT_TOL, f"b={b} t={t}: {err:.3e}"
+
+
 @pytest.mark.parametrize("B", [80, 264])
 def test_many_sequences_work_split(B):
     """More sequences than one wave (80) and than one workgroup (264) holds:
