@@ -147,6 +147,7 @@ void plan_choices()
         {{"qwen_like_128k_b1", 1, 12, 1, 2, 128, 0, 131104, 1024}, 131104, true},
         {{"tiny_8k_b1", 1, 4, 1, 2, 64, 0, 8200, 64}, 8192, true},               // smoke(): 64
         {{"tiny_b1", 1, 4, 1, 2, 64, 0, 1032, 64}, 1024, false},                // smoke(): 8
+        {{"tiny_b64", 64, 4, 1, 2, 64, 0, 1032, 64}, 1024, false, false, true}, // smoke(): 512
         {{"qwen_like_4k_b1", 1, 12, 1, 2, 128, 0, 4111, 1024}, 4111, false},     // 33 workgroups
         {{"qwen_like_8k_b1", 1, 12, 1, 2, 128, 0, 8207, 1024}, 8207, true},      // 65
         {{"qwen_like_16k_b1", 1, 12, 1, 2, 128, 0, 16399, 1024}, 16399, true},   // 129
