@@ -190,11 +190,14 @@ def test_n_covering_context_is_full_attention():
         assert np.abs(out.float().cpu().numpy() - ref).max() <= OUT_TOL
 
 
-def test_tail_gather_every_row_selected():
+@pytest.mark.parametrize("shape", [(32, 32, 2, 8, 128, 16384), (16, 32, 4, 8, 64, 6144)])
+def test_tail_gather_every_row_selected(shape):
     """N >= ctx on a launch that gathers in the K stream's tail: every row of a
-    chunk is selected for all 16 head slots (16 x 2048 entries per workgroup,
-    16 staging rounds), so the call is full attention."""
-    B, hq, hk, hv, d, rows = 32, 32, 2, 8, 128, 16384
+    chunk is selected for every head slot, so the queues flush during the
+    stream and the entries take several staging rounds read back from the lists
+    (d = 128: 16 slots x 2048 rows per chunk, 16 rounds of 2048; d = 64: 8 slots
+    x 512 rows, two rounds of 3072), and the call is full attention."""
+    B, hq, hk, hv, d, rows = shape
     q, K, V = make_inputs(B, hq, hk, hv, d, rows, 1, seed=46)
     gpu = run_atopn(q, K, V, [rows], rows + 5, 1, logits_every_step=False)
     assert np.isneginf(gpu["tau"][0]).all() and (gpu["counts"][0] == rows).all()
