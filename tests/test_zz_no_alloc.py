@@ -48,6 +48,14 @@ def test_no_alloc_matches_workspace_call_twice():
     compare(q[0], K, V, 3000, 100)
 
 
+def test_no_alloc_on_the_tail_gather():
+    """Four sequences of Llama-like heads at 8K rows: 768 K-stream workgroups,
+    which gather the value rows in their tails, on the library's scratch."""
+    q, K, V = make_inputs(4, 32, 4, 8, 64, 8200, 1, seed=62)
+    print("[no-alloc] llama-like heads, B=4, 8K rows (tail gather)", flush=True)
+    compare(q[0], K, V, 8192, 512)
+
+
 @pytest.mark.parametrize("name", ["qwen_like_128k_b1", "sweep_llama_L131072_N2048_B1"])
 def test_no_alloc_at_long_context(name):
     """Batch 1 at 128K context: Qwen-like heads (27 MiB of scratch) and
