@@ -1,6 +1,8 @@
 // decode.hip -- SAGA Atop-N decode step: (1) K stream with the threshold
 // mask and wave-ballot compaction, (2) masked softmax with the sparse value
-// gather, (3) split-sequence combine (shared with the full-attention path).
+// gather, either in the K stream's tail (large batches) or as a kernel of its
+// own over the selection lists, (3) split-sequence combine (shared with the
+// full-attention path).
 //
 // Method: "More Value per Key: Asymmetric Sparse Attention for Faster LLM
 // Decoding" (ai.info AI summary): entries are selected by comparing each
@@ -13,17 +15,19 @@
 // select_stream_kernel: grid.y = (b, key head g), grid.x = a chunk of rows.
 //   Each wave streams 16*U-row K tiles once for all h_q/h_k query heads of the
 //   group (MFMA QK tile from device.hpp), compares every logit with its head's
-//   threshold, and compacts the hits with ballot + popcount straight into a
-//   per-(b, query head, chunk, wave) list of (row, logit) in the workspace,
-//   together with the list length and the list's largest logit.  No LDS, no
-//   waiting on anything but the K stream.
+//   threshold, and compacts the hits with ballot + mbcnt into wave-private
+//   LDS queues, flushed when full to per-(b, query head, chunk, wave) lists
+//   of (row, logit) in the workspace.  The list path then writes each list's
+//   length and largest logit for gather_kernel; with GKT > 0 the workgroup
+//   instead gathers its own chunk's value rows in its tail (tail_gather) and
+//   writes one partial per (b, query head, chunk).
 // gather_kernel: one workgroup per (b, query head, segment of its entries).
 //   Reads its lists' lengths and maxima, stages the entries in LDS with their
 //   softmax weights exp(s - M) (M = the segment's largest selected logit),
 //   then gathers the selected rows of the query head's value head with
 //   16-byte loads, many rows in flight per lane, accumulating in fp32.
 //   One (M, l, count, o) partial per (b, query head, segment).
-// combine_kernel merges the partials in segment order.
+// combine_kernel merges the partials in segment (or chunk) order.
 // Every sum runs in a fixed order and no float atomics are used, so results
 // are bit-identical run to run.
 #include "kernels.hpp"

@@ -425,9 +425,10 @@ struct SelectStreamArgs {
     int32_t lq;              // query tokens per query head and step (1: one)
     const float* k_scale;    // non-null: fp8 e4m3 K, one scale per (b, key head)
     PagedKV pg;              // paged caches (block_table != nullptr)
-    // Value gather in the stream's tail (v non-null; contiguous bf16 V with
-    // d_v = d_k of 64 or 128): each workgroup gathers its own chunk's selected value rows
-    // and writes one partial per (b*h_q + i, chunk) instead of list lengths.
+    // Value gather in the stream's tail (v non-null; contiguous V, bf16 or fp8
+    // with v_scale, d_v = d_k of 64 or 128): each workgroup gathers its own
+    // chunk's selected value rows and writes one partial per (b*h_q + i, chunk)
+    // instead of list lengths.
     const uint16_t* v;
     Partials part;
     int32_t hv, Gv;
